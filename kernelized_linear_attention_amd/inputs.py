@@ -1,0 +1,66 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds no attention arithmetic: it only draws random numbers.
+Both the HIP path and the fp64 oracle receive exactly the arrays produced
+here (cast to the compute dtype by the caller), so neither side re-draws.
+
+Seeding: every tensor comes from numpy's PCG64 seeded by
+``SeedSequence([workload_id, tensor_id, rep])``; tensor ids are fixed below.
+
+The random-feature matrix omega is the one random draw the method itself
+makes.  It is drawn here and handed to both sides as an input:
+
+* ``orf_omega`` -- orthogonal random features as the Performer page (sec. 2,
+  step 4) describes them: rows of independent random orthogonal d x d blocks,
+  each row rescaled to a Gaussian-distributed length, i.e. the length of an
+  independent N(0, I_d) vector (chi distribution with d degrees of freedom).
+  The Kernel Zoo (sec. 5.1, 5.3) builds the orthogonal directions by
+  Gram-Schmidt; ``orthonormal_rows`` is that Gram-Schmidt, computed through a
+  QR factorisation whose signs are fixed so that it returns the same vectors.
+* ``iid_omega`` -- independent N(0, I_d) rows (Kernel Zoo sec. 4.2).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+T_Q, T_K, T_V, T_OMEGA, T_PREFIX = 0, 1, 2, 3, 4
+
+
+def rng(workload: int, tensor: int, rep: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([workload, tensor, rep])))
+
+
+def normal(shape, workload: int, tensor: int, rep: int = 0) -> np.ndarray:
+    """i.i.d. N(0, 1) float32 array of the given shape."""
+    return rng(workload, tensor, rep).standard_normal(size=tuple(shape), dtype=np.float32)
+
+
+def orthonormal_rows(m: np.ndarray) -> np.ndarray:
+    """Gram-Schmidt on the rows of m (rows in order), in float64.
+
+    Uses the QR factorisation of m^T: Gram-Schmidt on the columns of m^T is
+    Q with each column's sign chosen so that diag(R) > 0.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    q, r = np.linalg.qr(m.T)
+    signs = np.sign(np.diag(r))
+    signs[signs == 0] = 1.0
+    return (q * signs).T
+
+
+def orf_omega(r: int, d: int, workload: int, rep: int = 0) -> np.ndarray:
+    """[r, d] float64: ceil(r/d) independent orthogonal blocks, rows scaled to
+    chi(d)-distributed lengths; the last block is truncated when d does not
+    divide r."""
+    g = rng(workload, T_OMEGA, rep)
+    blocks = []
+    for _ in range((r + d - 1) // d):
+        directions = orthonormal_rows(g.standard_normal((d, d)))
+        lengths = np.linalg.norm(g.standard_normal((d, d)), axis=1)
+        blocks.append(directions * lengths[:, None])
+    return np.concatenate(blocks, axis=0)[:r]
+
+
+def iid_omega(r: int, d: int, workload: int, rep: int = 0) -> np.ndarray:
+    """[r, d] float64 with i.i.d. N(0, 1) entries."""
+    return rng(workload, T_OMEGA, rep).standard_normal((r, d))

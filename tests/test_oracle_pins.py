@@ -1,0 +1,376 @@
+"""Pins of the fp64 oracle to what the pages and the mathematics fix.
+
+Each test names the passage it checks.  Together they are chosen so that a
+plausible slip in the oracle (a dropped 1/sqrt(m), a wrong sign on the norm
+term, S stored transposed, exclusive instead of inclusive causality, the DPFP
+roll in the wrong direction, a missing eps clamp, misplaced temperature) fails
+at least one of them.  CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from kernelized_linear_attention_amd import inputs
+from tests.conftest import golden
+
+A = np.asarray
+
+
+# --------------------------------------------------------------------------
+# Worked examples printed on the pages
+# --------------------------------------------------------------------------
+
+def test_rescan_example_identity_map():
+    """Interactive chapter: s=(9,10), z=(2,5), 9/2 = 4.5 by both routes."""
+    g = golden("rescan_identity.json")
+    K = A(g["keys"], float)[None]
+    V = A(g["values"], float)[None]
+    q = A(g["query"], float)[None, None]
+    Q = np.repeat(q, K.shape[1], axis=1)  # one query per key row; all equal q0
+    out, S, z = oracle.bidir(Q, K, V, "identity")
+    np.testing.assert_array_equal(S[0][:, 0], g["s"])
+    np.testing.assert_array_equal(z[0], g["z"])
+    assert out[0, 0, 0] == g["output"]
+    # the naive route: per-key scores, weighted sum, normaliser
+    explicit = oracle.explicit(Q, K, V, "identity", causal_mask=False)
+    assert explicit[0, 0, 0] == g["output"]
+    scores = K[0] @ A(g["query"], float)
+    np.testing.assert_array_equal(scores, g["scores"])
+    assert scores @ V[0][:, 0] == g["numerator"] and scores.sum() == g["normaliser"]
+
+
+def test_fwp_trace_identity_unnormalised():
+    """Kernel Zoo sec. 1.4: y = (0,0),(1,0),(3,3),(2,4); state after step i is W(i)^T."""
+    g = golden("running_example.json")
+    Q, K, V = (A(g[n], float)[None] for n in ("Q", "K", "V"))
+    out, S, z = oracle.causal(Q, K, V, "identity", norm="none")
+    np.testing.assert_array_equal(out[0], g["fwp_y"])
+    for i in range(4):
+        _, Si, _ = oracle.causal(Q[:, : i + 1], K[:, : i + 1], V[:, : i + 1], "identity",
+                                 norm="none")
+        np.testing.assert_array_equal(Si[0], A(g["fwp_W"][i]).T)
+    np.testing.assert_array_equal(S[0], A(g["fwp_W"][3]).T)
+
+
+def test_identity_attn_first_token_hits_eps_clamp():
+    """Running example with normalisation: at t=1 the denominator q1.k1 is 0, so
+    the eps clamp (the Reassociate page asks for it to be explicit) gives
+    0 / eps = 0; the later denominators are q_t . z_t = 1, 4, 4."""
+    g = golden("running_example.json")
+    Q, K, V = (A(g[n], float)[None] for n in ("Q", "K", "V"))
+    out, _, _ = oracle.causal(Q, K, V, "identity", norm="attn", eps=1e-6)
+    np.testing.assert_array_equal(out[0, 0], [0.0, 0.0])
+    y = A(g["fwp_y"], float)
+    np.testing.assert_allclose(out[0, 1:], y[1:] / A([1.0, 4.0, 4.0])[:, None], rtol=1e-15)
+
+
+def test_elu1_maps_of_running_example():
+    """Kernel Zoo, running example: phi_elu(Q) and phi_elu(K) as printed."""
+    g = golden("running_example.json")
+    np.testing.assert_array_equal(oracle.featuremap(A(g["Q"]), "elu1"), g["phi_elu_Q"])
+    np.testing.assert_array_equal(oracle.featuremap(A(g["K"]), "elu1"), g["phi_elu_K"])
+
+
+def test_elu1_negative_branch_matches_library_elu():
+    """ELU (alpha = 1) + 1 on negative inputs: no printed value covers x < 0,
+    so pin against torch's ELU, and check continuity at 0."""
+    import torch
+
+    x = np.linspace(-6.0, 3.0, 181).reshape(1, 181, 1)
+    ref = torch.nn.functional.elu(torch.from_numpy(x), alpha=1.0).numpy() + 1.0
+    np.testing.assert_allclose(oracle.featuremap(x, "elu1"), ref, rtol=1e-14, atol=0)
+    tiny = A([[[-1e-12], [0.0], [1e-12]]])
+    np.testing.assert_allclose(oracle.featuremap(tiny, "elu1")[0, :, 0], 1.0, atol=2e-12)
+
+
+def test_elu1_causal_output_and_state():
+    """Kernel Zoo sec. 1.4 (o4 = (0.962, 0.577), from the earlier post) and
+    sec. 2.3 (S2).  Exactly o4 = (25, 15)/26: S4 = [[5,4],[10,3]], z4 = (6,8),
+    phi(q4) = (3,1)."""
+    g = golden("running_example.json")
+    Q, K, V = (A(g[n], float)[None] for n in ("Q", "K", "V"))
+    out, S, z = oracle.causal(Q, K, V, "elu1")
+    np.testing.assert_allclose(out[0, 3], g["elu_causal_o4_printed"], atol=5e-4)
+    np.testing.assert_allclose(out[0, 3], [25 / 26, 15 / 26], rtol=1e-15)
+    np.testing.assert_array_equal(S[0], [[5, 4], [10, 3]])
+    np.testing.assert_array_equal(z[0], [6, 8])
+    _, S2, _ = oracle.causal(Q[:, :2], K[:, :2], V[:, :2], "elu1")
+    np.testing.assert_array_equal(S2[0], g["elu_S2"])
+    # the other causal rows, worked by hand from the same data
+    np.testing.assert_allclose(out[0, :3], [[1, 0], [5 / 9, 4 / 9], [0.7, 0.7]], rtol=1e-15)
+
+
+def test_crosstalk_retrieval():
+    """Kernel Zoo sec. 2.3: querying S2 with phi_elu(k1) returns (5, 4); with
+    normalisation (5,4)/9 = (0.556, 0.444)."""
+    g = golden("running_example.json")
+    Q, K, V = (A(g[n], float)[None] for n in ("Q", "K", "V"))
+    Qx = Q[:, :2].copy()
+    Qx[0, 1] = K[0, 0]  # the second query is key 1
+    out_none, _, _ = oracle.causal(Qx, K[:, :2], V[:, :2], "elu1", norm="none")
+    np.testing.assert_array_equal(out_none[0, 1], g["crosstalk_retrieval"])
+    out_attn, _, _ = oracle.causal(Qx, K[:, :2], V[:, :2], "elu1", norm="attn")
+    np.testing.assert_allclose(out_attn[0, 1], g["crosstalk_normalised_printed"], atol=5e-4)
+
+
+def test_orthonormal_keys_retrieve_exactly():
+    """Kernel Zoo sec. 2.4: orthonormal mapped keys give S2 = I and retrieve v1."""
+    g = golden("running_example.json")
+    K = A(g["orthonormal_phi_k"], float)[None]
+    V = A(g["V"], float)[None, :2]
+    out, S, _ = oracle.causal(K, K, V, "identity", norm="none")
+    np.testing.assert_array_equal(S[0], g["orthonormal_S2"])
+    full, _, _ = oracle.bidir(K, K, V, "identity", norm="none")
+    np.testing.assert_array_equal(full[0, 0], V[0, 0])
+
+
+def test_favor_m4_worked_example():
+    """Kernel Zoo sec. 4.3: phi+(q1), phi+(k1) and the two kernel estimates."""
+    g = golden("favor_m4.json")
+    om = A(g["omega"])
+    tol = g["tolerance_abs"]
+    pq1 = oracle.featuremap(A([[g["q1"]]]), "favor", omega=om)[0, 0]
+    pk1 = oracle.featuremap(A([[g["k1"]]]), "favor", omega=om)[0, 0]
+    pk2 = oracle.featuremap(A([[g["k2"]]]), "favor", omega=om)[0, 0]
+    np.testing.assert_allclose(pq1, g["phi_q1"], atol=tol)
+    np.testing.assert_allclose(pk1, g["phi_k1"], atol=tol)
+    assert abs(pq1 @ pk1 - g["estimate_q1_k1"]) < tol
+    assert abs(pq1 @ pk2 - g["estimate_q1_k2"]) < tol
+    # closed form of the first component: exp(0.5 - 1/2) / sqrt(4) = 1/2
+    assert abs(pq1[0] - 0.5) < 1e-15
+
+
+def test_orf_gram_schmidt_worked_example():
+    """Kernel Zoo sec. 5.3: Gram-Schmidt of omega_1, omega_2, scaled to sqrt(2);
+    orthogonality; phi_ort(q1) = (1.442, 0.889)."""
+    g = golden("orf_2d.json")
+    tol = g["tolerance_abs"]
+    om = inputs.orthonormal_rows(A(g["omega"])) * g["row_length"]
+    np.testing.assert_allclose(om, g["omega_ort"], atol=tol)
+    assert abs(om[0] @ om[1]) < 1e-15
+    p = oracle.featuremap(A([[g["q1"]]]), "favor", omega=om)[0, 0]
+    np.testing.assert_allclose(p, g["phi_ort_q1"], atol=tol)
+
+
+def test_dpfp_nu1_worked_example():
+    """Kernel Zoo sec. 6.5-6.6: DPFP-1 of the running keys, of k_A, k_B, and
+    the orthogonality of phi(k_A), phi(k_B)."""
+    g = golden("dpfp_nu1.json")
+    np.testing.assert_array_equal(oracle.featuremap(A([g["keys"]]), "dpfp", nu=1)[0],
+                                  g["phi_keys"])
+    pa = oracle.featuremap(A([[g["k_A"]]]), "dpfp", nu=1)[0, 0]
+    pb = oracle.featuremap(A([[g["k_B"]]]), "dpfp", nu=1)[0, 0]
+    np.testing.assert_allclose(pa, g["phi_k_A"], rtol=1e-15)
+    np.testing.assert_allclose(pb, g["phi_k_B"], rtol=1e-15)
+    assert pa @ pb == 0.0
+    assert oracle.feature_dim("dpfp", d=2, nu=1) == 4
+    assert oracle.feature_dim("dpfp", d=64, nu=2) == 256
+
+
+def test_dpfp_nu2_block_order_and_roll():
+    """Kernel Zoo sec. 6.3: block s holds kt_i * kt_{(i+s) mod 2d}, blocks in
+    ascending s.  With kt = (2,0,3,0,0,0) the only nonzero product is
+    kt_0 * kt_2: the forward roll puts it in block s=2 at i=0 (index 6); the
+    backward roll would put it at i=2 (index 8), block-major order elsewhere."""
+    x = A([[[2.0, 0.0, 3.0]]])  # kt = (2, 0, 3, 0, 0, 0)
+    p = oracle.featuremap(x, "dpfp", nu=2)[0, 0]
+    expect = np.zeros(12)
+    expect[6 + 0] = 2.0 * 3.0   # s=2, i=0: kt_0 * kt_2
+    np.testing.assert_array_equal(p, expect)
+
+
+def test_sum_normalisation_worked_example():
+    """Kernel Zoo sec. 7.3: phi'(q1) = (2/3, 1/3), phi'(k1) = (1/3, 2/3), 4/9."""
+    g = golden("sum_norm.json")
+    pq = oracle.featuremap(A([[g["q1"]]]), "elu1", sum_norm=True)[0, 0]
+    pk = oracle.featuremap(A([[g["k1"]]]), "elu1", sum_norm=True)[0, 0]
+    np.testing.assert_allclose(pq, g["phi_q1"], rtol=1e-15)
+    np.testing.assert_allclose(pk, g["phi_k1"], rtol=1e-15)
+    assert abs(pq @ pk - g["similarity"]) < 1e-15
+    assert abs(pq @ pk - g["similarity_printed"]) < 5e-4
+
+
+def test_sum_norm_of_all_zero_features_stays_zero():
+    """Kernel Zoo sec. 6.6: most running keys map to zero under DPFP-1; with
+    sum normalisation the eps clamp keeps them zero instead of 0/0."""
+    g = golden("dpfp_nu1.json")
+    p = oracle.featuremap(A([g["keys"]]), "dpfp", nu=1, sum_norm=True)[0]
+    assert np.all(np.isfinite(p))
+    np.testing.assert_array_equal(p[[0, 1, 3]], 0.0)
+    np.testing.assert_array_equal(p[2], [1, 0, 0, 0])
+
+
+# --------------------------------------------------------------------------
+# Identities and invariants (random tiny inputs)
+# --------------------------------------------------------------------------
+
+KIND_CASES = [
+    ("identity", {}, False),
+    ("elu1", {}, False),
+    ("elu1", {}, True),
+    ("favor", {"r": 24}, False),
+    ("dpfp", {"nu": 2}, False),
+    ("dpfp", {"nu": 3}, True),
+]
+
+
+def _tiny(seed, BH=3, N=9, d=6, dv=5, r=None):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((BH, N, d))
+    k = g.standard_normal((BH, N, d))
+    v = g.standard_normal((BH, N, dv))
+    om = g.standard_normal((r, d)) if r else None
+    return q, k, v, om
+
+
+@pytest.mark.parametrize("kind,extra,sum_norm", KIND_CASES)
+@pytest.mark.parametrize("norm", ["attn", "none"])
+def test_reassociated_equals_explicit(kind, extra, sum_norm, norm):
+    """Associativity (Kernel Zoo opening paragraph; interactive chapter): the
+    state forms equal the N x N forms, bidirectional and causally masked."""
+    q, k, v, om = _tiny(11, r=extra.get("r"))
+    kw = dict(omega=om, nu=extra.get("nu", 1), sum_norm=sum_norm, norm=norm, scale=0.8)
+    if kind == "identity" and norm == "attn":
+        q, k = np.abs(q), np.abs(k)  # keep denominators away from the clamp
+    out_b, _, _ = oracle.bidir(q, k, v, kind, **kw)
+    ref_b = oracle.explicit(q, k, v, kind, causal_mask=False, **kw)
+    np.testing.assert_allclose(out_b, ref_b, rtol=1e-12, atol=1e-12)
+    out_c, S, z = oracle.causal(q, k, v, kind, **kw)
+    ref_c = oracle.explicit(q, k, v, kind, causal_mask=True, **kw)
+    np.testing.assert_allclose(out_c, ref_c, rtol=1e-12, atol=1e-12)
+    # carried-in state: continue from (S, z) on fresh tokens
+    q2, k2, v2, _ = _tiny(12, r=None)
+    out_c2, _, _ = oracle.causal(q2, k2, v2, kind, S0=S, z0=z, **kw)
+    ref_c2 = oracle.explicit(q2, k2, v2, kind, causal_mask=True, S0=S, z0=z, **kw)
+    np.testing.assert_allclose(out_c2, ref_c2, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind,extra,sum_norm", KIND_CASES)
+def test_last_causal_row_equals_bidirectional(kind, extra, sum_norm):
+    """The causal state after the last token is the bidirectional summary
+    (Kernel Zoo sec. 5.4 with i = N; Performer page sec. 2 step 5)."""
+    q, k, v, om = _tiny(21, r=extra.get("r"))
+    kw = dict(omega=om, nu=extra.get("nu", 1), sum_norm=sum_norm, norm="none")
+    out_c, S_c, z_c = oracle.causal(q, k, v, kind, **kw)
+    out_b, S_b, z_b = oracle.bidir(q, k, v, kind, **kw)
+    np.testing.assert_allclose(out_c[:, -1], out_b[:, -1], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S_c, S_b, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z_c, z_b, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind,extra", [("elu1", {}), ("favor", {"r": 32}), ("dpfp", {"nu": 2})])
+def test_attention_output_is_convex_combination(kind, extra):
+    """Non-negative weights and a positive denominator make each output a
+    weighted average of the visible values (Reassociate page, 2nd paragraph)."""
+    q, k, v, om = _tiny(31, N=12, r=extra.get("r"))
+    out, _, _ = oracle.causal(q, k, v, kind, omega=om, nu=extra.get("nu", 1))
+    den_ok = oracle.causal(q, k, np.ones_like(v[..., :1]), kind, omega=om,
+                           nu=extra.get("nu", 1), norm="none")[0][..., 0] > 1e-6
+    for t in range(q.shape[1]):
+        lo = v[:, : t + 1].min(axis=1)
+        hi = v[:, : t + 1].max(axis=1)
+        m = den_ok[:, t]
+        assert np.all(out[m, t] >= lo[m] - 1e-12) and np.all(out[m, t] <= hi[m] + 1e-12)
+
+
+def test_split_call_carries_state():
+    """Carrying the fast-weight memory from one segment to the next (Kernel Zoo
+    sec. 9.3) gives the same outputs and final state as one call."""
+    q, k, v, om = _tiny(41, N=14, r=16)
+    kw = dict(omega=om, scale=0.7)
+    out, S, z = oracle.causal(q, k, v, "favor", **kw)
+    o1, S1, z1 = oracle.causal(q[:, :5], k[:, :5], v[:, :5], "favor", **kw)
+    o2, S2, z2 = oracle.causal(q[:, 5:], k[:, 5:], v[:, 5:], "favor", S0=S1, z0=z1, **kw)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=1), out, rtol=1e-13)
+    np.testing.assert_allclose(S2, S, rtol=1e-13)
+    np.testing.assert_allclose(z2, z, rtol=1e-13)
+
+
+def test_decode_step_equals_next_causal_row():
+    """Kernel Zoo sec. 1.2: one decode step (update, then read) is the next row
+    of the causal recurrence."""
+    q, k, v, om = _tiny(51, N=10, r=16)
+    kw = dict(omega=om)
+    out, S, z = oracle.causal(q, k, v, "favor", **kw)
+    _, S9, z9 = oracle.causal(q[:, :9], k[:, :9], v[:, :9], "favor", **kw)
+    o, S10, z10 = oracle.decode(q[:, 9], k[:, 9], v[:, 9], S9, z9, "favor", **kw)
+    np.testing.assert_allclose(o, out[:, 9], rtol=1e-13)
+    np.testing.assert_allclose(S10, S, rtol=1e-13)
+    np.testing.assert_allclose(z10, z, rtol=1e-13)
+
+
+def test_favor_features_are_positive():
+    """Kernel Zoo sec. 4.2: every component of phi+ is positive."""
+    g = np.random.default_rng(61)
+    x = 3.0 * g.standard_normal((2, 50, 16))
+    om = g.standard_normal((64, 16))
+    assert np.all(oracle.featuremap(x, "favor", omega=om, scale=0.5) > 0.0)
+
+
+# --------------------------------------------------------------------------
+# Lemma 1: unbiasedness of positive random features (statistical)
+# --------------------------------------------------------------------------
+
+def _lemma1_estimates(x, y, sampler, r, seeds, scale=1.0):
+    d = x.shape[-1]
+    est = np.empty(seeds)
+    xy = np.stack([x, y])[:, None, :]
+    for s in range(seeds):
+        om = sampler(r, d, 900, s)
+        p = oracle.featuremap(xy, "favor", omega=om, scale=scale)
+        est[s] = p[0, 0] @ p[1, 0]
+    return est
+
+
+@pytest.mark.parametrize("sampler", [inputs.iid_omega, inputs.orf_omega], ids=["iid", "orf"])
+def test_lemma1_positive_features_unbiased(sampler):
+    """Kernel Zoo sec. 4.1 (Lemma 1): E[phi+(x) . phi+(y)] = exp(x . y), for
+    i.i.d. Gaussian rows and for orthogonal rows with chi-distributed lengths
+    (Performer page sec. 2 step 4).  Mean over seeds within 5 standard errors."""
+    g = np.random.default_rng(71)
+    d = 8
+    x = g.standard_normal(d)
+    y = g.standard_normal(d)
+    x *= 0.6 / np.linalg.norm(x)
+    y *= 0.7 / np.linalg.norm(y)
+    est = _lemma1_estimates(x, y, sampler, r=16, seeds=3000)
+    target = math.exp(x @ y)
+    se = est.std(ddof=1) / math.sqrt(est.size)
+    assert abs(est.mean() - target) < 5 * se
+    # the same estimator is biased for a wrong kernel, e.g. exp(x.y/2): the
+    # test has the power to see a misplaced factor
+    assert abs(est.mean() - math.exp(0.5 * (x @ y))) > 5 * se or abs(x @ y) < 0.05
+
+
+def test_lemma1_with_temperature_scale():
+    """With x, y scaled by d^-1/4 inside phi the estimator targets
+    exp(x . y / sqrt(d)) (Kernel Zoo sec. 3.3: the sqrt(d) can be absorbed)."""
+    g = np.random.default_rng(81)
+    d = 16
+    x = g.standard_normal(d)
+    y = g.standard_normal(d)
+    x *= 1.2 / np.linalg.norm(x)
+    y *= 1.4 / np.linalg.norm(y)
+    s = d ** -0.25
+    est = _lemma1_estimates(x, y, inputs.orf_omega, r=32, seeds=2000, scale=s)
+    se = est.std(ddof=1) / math.sqrt(est.size)
+    assert abs(est.mean() - math.exp(x @ y / math.sqrt(d))) < 5 * se
+
+
+def test_orthogonal_rows_have_chi_lengths():
+    """The omega sampler: rows orthogonal within each d x d block, lengths with
+    the chi(d) mean sqrt(2) Gamma((d+1)/2) / Gamma(d/2)."""
+    d, r = 16, 64
+    om = inputs.orf_omega(r, d, 5)
+    for b in range(r // d):
+        blk = om[b * d:(b + 1) * d]
+        gram = blk @ blk.T
+        off = gram - np.diag(np.diag(gram))
+        assert np.max(np.abs(off)) < 1e-12
+    lengths = np.concatenate([np.linalg.norm(inputs.orf_omega(r, d, 5, s), axis=1)
+                              for s in range(200)])
+    chi_mean = math.sqrt(2) * math.exp(math.lgamma((d + 1) / 2) - math.lgamma(d / 2))
+    chi_var = d - chi_mean ** 2
+    assert abs(lengths.mean() - chi_mean) < 5 * math.sqrt(chi_var / lengths.size)

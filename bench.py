@@ -1,0 +1,271 @@
+"""Benchmark of the kernelized linear attention hot path on one MI355X.
+
+One step = one causal FAVOR+ prefill of the headline workload (B=1, H=8,
+N=65536, d=64, r=256, bf16 inputs, float32 state): feature map, masked
+intra-chunk block, inter-chunk readout and state update, segment carry.
+The same run also times the 12-layer batched decode (B=256, H=8, fp32 state
+read-modify-written in HBM) and the bidirectional FAVOR+ pass (B=4, H=8,
+N=4096), and reports each against its roofline.  Inputs are synthetic
+(seeded N(0,1)), resident in HBM before timing starts; two input sets
+alternate so that the 256 MB last-level cache cannot hold a step's inputs.
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
+[--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal FAVOR+ prefill tokens/s + % MFMA peak (r=256,d=64); decode GB/s % HBM"
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # HBM3E
+
+
+def favor_alg_flops_per_tok_head(r=256, d=64, dv=64):
+    """Algorithmic flops of one token of one head: q and k projections
+    (2 * 2rd), phi(K)^T V and phi(Q) S (2 * 2 r dv), z / den / sum (~3r)."""
+    return 4 * r * d + 4 * r * dv + 3 * r
+
+
+def decode_alg_bytes_per_head(r=256, dv=64, in_bytes=2):
+    """Read and write S [r, dv] and z [r] in float32, read q, k, v and write
+    the output (bf16)."""
+    return 2 * (r * dv + r) * 4 + 4 * 64 * in_bytes
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "bidir"], default=None,
+                    help="run one section only (for profiling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kernelized_linear_attention_amd import binding, inputs, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a, dtype=torch.bfloat16):
+        return torch.from_numpy(np.asarray(a, np.float32)).to(dev).to(dtype)
+
+    result = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+
+    def timed(fn, steps, warmup):
+        """Runs fn() warmup + steps times; returns (total ms of the timed steps,
+        list of per-call event ms)."""
+        for _ in range(warmup):
+            fn(0)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            evs[i][0].record()
+            fn(i)
+            evs[i][1].record()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in evs]
+
+    # ------------------------------------------------------------------ prefill
+    w = workloads.FAVOR_CAUSAL
+    scale = workloads.scale_of(w)
+    if args.only in (None, "prefill"):
+        sets = []
+        for rep in range(2):
+            q = to_dev(inputs.normal((w.B, w.H, w.N, w.d), w.wid, inputs.T_Q, rep))
+            k = to_dev(inputs.normal((w.B, w.H, w.N, w.d), w.wid, inputs.T_K, rep))
+            v = to_dev(inputs.normal((w.B, w.H, w.N, w.dv), w.wid, inputs.T_V, rep))
+            sets.append((q, k, v))
+        om = to_dev(inputs.orf_omega(w.r, w.d, w.wid))
+        S = torch.empty((w.B, w.H, w.r, w.dv), device=dev)
+        z = torch.empty((w.B, w.H, w.r), device=dev)
+        out = torch.empty((w.B, w.H, w.N, w.dv), device=dev, dtype=torch.bfloat16)
+        p = binding.make_params("favor", w.r, dtype=torch.bfloat16, scale=scale, eps=w.eps)
+        wsb = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, w.B, w.H, w.N, w.d, w.dv, 64)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def step(i):
+            q, k, v = sets[i % 2]
+            binding.lin_attn_causal_chunked(q, k, v, "favor", omega=om, scale=scale, eps=w.eps,
+                                            chunk=64, S=S, z=z, out=out, workspace=ws)
+
+        total_ms, per = timed(step, args.steps, args.warmup)
+        ms = total_ms / args.steps
+        call_ms = float(np.mean(per))
+        toks = w.B * w.N
+        flops = favor_alg_flops_per_tok_head(w.r, w.d, w.dv) * w.B * w.H * w.N
+        achieved = flops / (call_ms * 1e-3) / 1e12
+        result.update(value=toks / (ms * 1e-3), ms_per_step=ms)
+        result["config"] = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                            "dv": w.dv, "r": w.r, "phi": "favor", "chunk": 64,
+                            "inputs": "bf16 N(0,1)", "state": "fp32", "eps": w.eps,
+                            "scale": scale}
+        result["roofline"] = {
+            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": stored_traffic("prefill"),
+            "kernel": "lin_attn_causal_chunked (whole call)",
+            "alg_flops_per_launch": flops, "avg_launch_ms": call_ms,
+        }
+        del sets, out, ws
+
+    # ------------------------------------------------------------------ decode
+    wd = workloads.FAVOR_DECODE
+    if args.only in (None, "decode"):
+        sd = workloads.scale_of(wd)
+        layers = []
+        pre_q = to_dev(inputs.normal((wd.B, wd.H, wd.prefix, wd.d), wd.wid, inputs.T_PREFIX, 0))
+        pre_k = to_dev(inputs.normal((wd.B, wd.H, wd.prefix, wd.d), wd.wid, inputs.T_PREFIX, 1))
+        pre_v = to_dev(inputs.normal((wd.B, wd.H, wd.prefix, wd.dv), wd.wid, inputs.T_PREFIX, 2))
+        for l in range(wd.layers):
+            om = to_dev(inputs.orf_omega(wd.r, wd.d, wd.wid, 100 + l))
+            # the state: a causal prefill of a 64-token prefix (not timed)
+            _, S, z = binding.lin_attn_causal_chunked(pre_q, pre_k, pre_v, "favor", omega=om,
+                                                      scale=sd)
+            q, k, v = (to_dev(inputs.normal((wd.B, wd.H, wd.d), wd.wid, t, 200 + l))
+                       for t in (inputs.T_Q, inputs.T_K, inputs.T_V))
+            o = torch.empty((wd.B, wd.H, wd.dv), device=dev, dtype=torch.bfloat16)
+            layers.append((q, k, v, om, S, z, o))
+        torch.cuda.synchronize()
+        lev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(wd.layers)] for _ in range(args.steps)]
+
+        def dstep(i, record=False):
+            for l, (q, k, v, om, S, z, o) in enumerate(layers):
+                if record:
+                    lev[i][l][0].record()
+                binding.lin_attn_decode_step(q, k, v, S, z, "favor", omega=om, scale=sd,
+                                             eps=wd.eps, out=o)
+                if record:
+                    lev[i][l][1].record()
+
+        total_ms, _ = timed(lambda i: dstep(i, record=True), args.steps, args.warmup)
+        dms = total_ms / args.steps
+        launch_ms = float(np.mean([a.elapsed_time(b) for row in lev for a, b in row]))
+        heads = wd.B * wd.H
+        bytes_layer = decode_alg_bytes_per_head(wd.r, wd.dv, 2) * heads
+        gbps_step = bytes_layer * wd.layers / (dms * 1e-3) / 1e9
+        gbps_launch = bytes_layer / (launch_ms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": wd.name, "B": wd.B, "H": wd.H, "layers": wd.layers, "r": wd.r,
+            "ms_per_step": dms, "seq_tokens_per_s": wd.B / (dms * 1e-3),
+            "GBps_step": gbps_step,
+            "roofline": {"bound": "hbm", "achieved": gbps_launch, "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": gbps_launch / PEAK_HBM_GBPS,
+                         "traffic": stored_traffic("decode"), "kernel": "k_decode",
+                         "alg_bytes_per_launch": bytes_layer, "avg_launch_ms": launch_ms},
+        }
+        del layers
+
+    # ------------------------------------------------------------------ bidir
+    wb = workloads.FAVOR_BIDIR
+    if args.only in (None, "bidir"):
+        sb = workloads.scale_of(wb)
+        bsets = []
+        for rep in range(2):
+            q, k, v = (to_dev(inputs.normal((wb.B, wb.H, wb.N, wb.d), wb.wid, t, rep))
+                       for t in (inputs.T_Q, inputs.T_K, inputs.T_V))
+            bsets.append((q, k, v))
+        om = to_dev(inputs.orf_omega(wb.r, wb.d, wb.wid))
+        bout = torch.empty((wb.B, wb.H, wb.N, wb.dv), device=dev, dtype=torch.bfloat16)
+        pb = binding.make_params("favor", wb.r, dtype=torch.bfloat16, scale=sb, eps=wb.eps)
+        wsb = binding.lin_attn_workspace_bytes(binding.OP_BIDIR, pb, wb.B, wb.H, wb.N, wb.d, wb.dv)
+        bws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def bstep(i):
+            q, k, v = bsets[i % 2]
+            binding.lin_attn_bidir(q, k, v, "favor", omega=om, scale=sb, eps=wb.eps, out=bout,
+                                   workspace=bws)
+
+        total_ms, per = timed(bstep, args.steps, args.warmup)
+        bms = total_ms / args.steps
+        bflops = favor_alg_flops_per_tok_head(wb.r, wb.d, wb.dv) * wb.B * wb.H * wb.N
+        bach = bflops / (float(np.mean(per)) * 1e-3) / 1e12
+        result["bidir"] = {"workload": wb.name, "B": wb.B, "H": wb.H, "N": wb.N, "r": wb.r,
+                           "ms_per_step": bms, "tokens_per_s": wb.B * wb.N / (bms * 1e-3),
+                           "tflops_alg": bach, "frac_mfma": bach / PEAK_BF16_TFLOPS}
+        del bsets
+
+    if args.only in (None, "prefill") and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, scale)
+    print(json.dumps(result), flush=True)
+
+
+def stored_traffic(section):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, when it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{section}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kernelized_linear_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(w, scale):
+    """The fp64 oracle as it stands, on a bounded sample of the prefill
+    workload: all heads, the first `n` tokens (same seeded inputs)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from kernelized_linear_attention_amd import inputs
+
+    n = int(os.environ.get("LINATTN_CPU_SAMPLE_TOKENS", "65536"))
+    q, k, v = (torch.from_numpy(inputs.normal((w.B, w.H, w.N, w.d), w.wid, t, 0)[:, :, :n].copy())
+               .to(torch.bfloat16).to(torch.float64).numpy() for t in (inputs.T_Q, inputs.T_K,
+                                                                        inputs.T_V))
+    om = torch.from_numpy(inputs.orf_omega(w.r, w.d, w.wid).astype(np.float32)).to(
+        torch.bfloat16).to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    oracle.causal(q, k, v, "favor", omega=om, scale=scale, eps=w.eps)
+    dt = time.perf_counter() - t0
+    cores = min(oracle.threads(), w.B * w.H)
+    return {"value": w.B * n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"causal FAVOR+ oracle (fp64), B={w.B} H={w.H}, first {n} of {w.N} tokens; "
+                      f"{dt:.1f} s on {cores} threads (OpenMP over heads)"}
+
+
+if __name__ == "__main__":
+    main()

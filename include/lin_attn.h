@@ -1,0 +1,200 @@
+/*
+ * lin_attn.h -- C ABI of liblinattn.so: kernelized linear attention on
+ * AMD MI355X (gfx950), forward pass.
+ *
+ * Sources of the operations (the pages the method is taken from):
+ *   [KZ] "The Kernel Zoo: Performers, Fast Weight Programmers, and the
+ *        Capacity-Approximation Tradeoff in Linear Attention" (prathamp.com)
+ *   [RF] "Reassociate a feature-map kernel without claiming exact softmax"
+ *        (study.greatitself.com)
+ *   [LA] "Linear attention & kernelized approximations" (interactive chapter)
+ *   [PF] "Performer -- Random Feature Softmax Approximation" (lizeman.github.io)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Buffers.  Every tensor argument is a DEVICE pointer to contiguous,
+ *   row-major memory, 16-byte aligned.  Shapes use B (batch), H (heads),
+ *   N (tokens), d (query/key width), dv (value width), r (feature width):
+ *     q, k, x    [B, H, N, d]        v, out   [B, H, N, dv]
+ *     omega      [r, d]              phi      [B, H, N, r]   (float32)
+ *     S          [B, H, r, dv]       z        [B, H, r]      (float32)
+ *   q, k, v, omega and out share the element type lin_attn_params.dtype
+ *   (float32 or bfloat16).  S and z are always float32.  Heads are
+ *   independent; one omega is shared by all heads of a call ([PF] sec. 2,
+ *   "sampled once and frozen").
+ * Ownership.  The caller allocates and owns every buffer, including the
+ *   workspace (size from lin_attn_workspace_bytes).  The library never
+ *   allocates, frees or keeps a pointer after returning, holds no global
+ *   state and is reentrant.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *   stream).  All work is enqueued asynchronously on it; nothing
+ *   synchronises.  Buffers must stay valid until that work completes.
+ *   Device faults surface at the caller's next synchronisation.
+ * Errors.  Every int-returning entry point returns LIN_ATTN_OK (0) or a
+ *   negative code, checks its arguments before enqueueing anything, and on
+ *   error enqueues nothing and leaves every buffer untouched.  It never
+ *   prints, throws or aborts.  N == 0 or B*H == 0 is a successful no-op.
+ * GPU coverage.  d == dv == 64; r a multiple of 32 in [32, 256]; feature
+ *   maps identity, ELU+1, FAVOR+, DPFP; float32 and bfloat16.  Other
+ *   combinations return LIN_ATTN_ERR_UNSUPPORTED.
+ */
+#ifndef LIN_ATTN_H
+#define LIN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LIN_ATTN_ABI_VERSION 1
+
+/* Feature maps phi: R^d -> R^r. */
+#define LIN_ATTN_PHI_IDENTITY 0 /* phi(x) = x, r = d ([KZ] sec. 1.3; [LA])         */
+#define LIN_ATTN_PHI_ELU1 1     /* elu(x) + 1 (alpha = 1), r = d ([KZ] running     */
+                                /* example; [PF] sec. 1)                           */
+#define LIN_ATTN_PHI_FAVOR 2    /* exp(omega_i . x - |x|^2 / 2) / sqrt(r), r rows  */
+                                /* of omega ([KZ] sec. 4.2, 5.4; [PF] sec. 2-3)    */
+#define LIN_ATTN_PHI_DPFP 3     /* relu([x,-x]) products with rolled copies,      */
+                                /* r = 2 d nu ([KZ] sec. 6.3)                      */
+
+/* Readout. */
+#define LIN_ATTN_NORM_ATTN 0 /* out = num / max(den, eps) ([RF] par. 1-2; [PF] sketch) */
+#define LIN_ATTN_NORM_NONE 1 /* out = num (unnormalised fast-weight read, [KZ] 1.2)   */
+
+/* Element types of q, k, v, omega, out. */
+#define LIN_ATTN_F32 0
+#define LIN_ATTN_BF16 1 /* bfloat16; float32 accumulation everywhere */
+
+/* Return codes. */
+#define LIN_ATTN_OK 0
+#define LIN_ATTN_ERR_INVALID (-1)     /* null required pointer, negative size, bad enum,  */
+                                      /* eps <= 0, r inconsistent with phi / nu / omega    */
+#define LIN_ATTN_ERR_UNSUPPORTED (-2) /* valid, but outside the GPU coverage above         */
+#define LIN_ATTN_ERR_WORKSPACE (-3)   /* ws_bytes smaller than lin_attn_workspace_bytes   */
+#define LIN_ATTN_ERR_HIP (-4)         /* a kernel launch failed (hipGetLastError)          */
+
+/* Operation ids for lin_attn_workspace_bytes. */
+#define LIN_ATTN_OP_BIDIR 1
+#define LIN_ATTN_OP_CAUSAL 2
+
+/*
+ * Method parameters, shared by every call.
+ *   phi       LIN_ATTN_PHI_*.
+ *   r         feature width: must equal d for IDENTITY and ELU1, the number of
+ *             rows of omega for FAVOR, 2*d*nu for DPFP ([KZ] sec. 6.3).
+ *   nu        DPFP shift count, 1 <= nu <= 2d-1 ([KZ] sec. 6.3); ignored otherwise.
+ *   sum_norm  0 or 1: replace phi(x) by phi(x) / max(sum_i phi(x)_i, eps), for
+ *             queries and keys ([KZ] sec. 7.2).
+ *   norm      LIN_ATTN_NORM_ATTN or LIN_ATTN_NORM_NONE.
+ *   dtype     LIN_ATTN_F32 or LIN_ATTN_BF16.
+ *   scale     x <- scale * x for q and k before phi.  d^-1/4 places the
+ *             softmax temperature 1/sqrt(d) inside FAVOR+ ([KZ] sec. 3.3: it
+ *             can be absorbed into the inputs); 1 reproduces the pages'
+ *             worked examples.
+ *   eps       > 0.  Lower clamp of the attention denominator
+ *             (max(den, eps), the [PF] sketch's clamp) and of the sum in sum
+ *             normalisation.  [RF] par. 2 asks that it be stated, not hidden.
+ *   n_seg     sequence segments per head for the parallel scan; 0 = choose
+ *             automatically.  Changes rounding only, never the result.
+ *   reserved  must be 0.
+ */
+typedef struct lin_attn_params {
+    int32_t phi;
+    int32_t r;
+    int32_t nu;
+    int32_t sum_norm;
+    int32_t norm;
+    int32_t dtype;
+    float scale;
+    float eps;
+    int32_t n_seg;
+    int32_t reserved;
+} lin_attn_params;
+
+/*
+ * Feature map alone: phi = phi(scale * x) for every token, float32 output
+ * [B, H, N, r].  omega [r, d] is required for FAVOR and ignored otherwise
+ * (may be NULL).  Definitions: [KZ] running example (ELU+1), sec. 4.2 boxed
+ * map and sec. 5.4 (FAVOR+), sec. 6.3 (DPFP), sec. 7.2 (sum normalisation).
+ */
+int lin_attn_featuremap(const lin_attn_params* p, const void* x, int64_t B, int64_t H,
+                        int64_t N, int64_t d, const void* omega, float* phi, void* stream);
+
+/*
+ * Bidirectional (encoder) attention in the reassociated form
+ * ([RF] par. 1; [PF] sec. 2 step 5 and sec. 3 sketch; [LA]):
+ *   S = sum_j phi(k_j) v_j^T,  z = sum_j phi(k_j),
+ *   out_i = phi(q_i)^T S / max(phi(q_i) . z, eps)   (NORM_ATTN)
+ *         = phi(q_i)^T S                            (NORM_NONE)
+ * out [B, H, N, dv] has the input dtype.  S_out [B, H, r, dv] and
+ * z_out [B, H, r] (float32) receive the summaries when non-NULL.
+ * ws: device workspace of at least
+ * lin_attn_workspace_bytes(LIN_ATTN_OP_BIDIR, ...) bytes (may be NULL when
+ * that is 0); its contents on entry do not matter.
+ */
+int lin_attn_bidir(const lin_attn_params* p, const void* q, const void* k, const void* v,
+                   int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, const void* omega,
+                   void* out, float* S_out, float* z_out, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/*
+ * Causal prefill by the prefix-sum recurrence ([KZ] sec. 1.3 and sec. 5.4;
+ * [RF] par. 4; [PF] sec. 2 step 5 and the sketch's last line):
+ *   (S, z) <- (0, 0) when state_in == 0, else the caller's (S, z);
+ *   for t = 1..N:  S += phi(k_t) v_t^T;  z += phi(k_t);      (write first)
+ *                  out_t = readout of phi(q_t) against (S, z) (then read)
+ * so query t sees keys up to and including t.  Computed as a chunked scan:
+ * each chunk of `chunk` tokens combines its masked intra-chunk block with
+ * the state carried in from earlier chunks, and sequence segments are
+ * combined by a prefix sum of their state increments; all of these are
+ * exact re-associations of the recurrence.
+ *   chunk     0, 32, 64 or 128: intra-chunk block length hint.  Each kernel
+ *             family has one native block length (64 on the MFMA path, 32
+ *             on the float32 path) and uses it; the value never changes the
+ *             result beyond rounding.
+ *   S, z      float32 [B, H, r, dv] / [B, H, r], required, in/out: read
+ *             when state_in == 1, always overwritten with the state after
+ *             token N (the carried fast-weight memory of [KZ] sec. 9.3; a
+ *             packing boundary is a call with state_in == 0, [RF] par. 4).
+ *   out       [B, H, N, dv], input dtype.
+ *   ws        at least lin_attn_workspace_bytes(LIN_ATTN_OP_CAUSAL, ...) bytes.
+ */
+int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void* k,
+                            const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
+                            int64_t dv, const void* omega, int32_t chunk, float* S, float* z,
+                            int32_t state_in, void* out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
+ * One decode step for B*H single tokens ([KZ] sec. 1.2 steps 2-3; [RF]
+ * par. 3 "streaming causal calculation"):
+ *   S += phi(k) v^T;  z += phi(k);  out = readout of phi(q) against (S, z).
+ * q, k [B, H, d], v [B, H, dv], out [B, H, dv] (input dtype); S, z are
+ * updated in place (float32).  Needs no workspace.
+ */
+int lin_attn_decode_step(const lin_attn_params* p, const void* q, const void* k,
+                         const void* v, int64_t B, int64_t H, int64_t d, int64_t dv,
+                         const void* omega, float* S, float* z, void* out, void* stream);
+
+/*
+ * Workspace bytes needed by lin_attn_bidir (op = LIN_ATTN_OP_BIDIR) or
+ * lin_attn_causal_chunked (op = LIN_ATTN_OP_CAUSAL) for these arguments.
+ * Host-only, deterministic in its arguments (independent of the device).
+ * Returns 0 for invalid arguments.
+ */
+size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B, int64_t H,
+                                int64_t N, int64_t d, int64_t dv, int32_t chunk);
+
+/* Static, NUL-terminated description of a return code. */
+const char* lin_attn_strerror(int32_t code);
+
+/* LIN_ATTN_ABI_VERSION of the built library. */
+int32_t lin_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIN_ATTN_H */

@@ -1,0 +1,226 @@
+// abi.hip -- the extern "C" entry points of liblinattn.so (include/lin_attn.h):
+// argument validation, segmentation plan, workspace layout and dispatch.
+// Validation happens entirely on the host, before anything is enqueued.
+#include <math.h>
+
+#include "../../include/lin_attn.h"
+#include "launch.hpp"
+
+using namespace linattn;
+
+namespace {
+
+bool ptr_ok(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool opt_ptr_ok(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// INVALID checks, then GPU-coverage checks (UNSUPPORTED).
+int check_params(const lin_attn_params* p, int64_t d, int64_t dv, const void* omega) {
+    if (!p) return LIN_ATTN_ERR_INVALID;
+    if (p->reserved != 0) return LIN_ATTN_ERR_INVALID;
+    if (p->phi < LIN_ATTN_PHI_IDENTITY || p->phi > LIN_ATTN_PHI_DPFP) return LIN_ATTN_ERR_INVALID;
+    if (p->norm != LIN_ATTN_NORM_ATTN && p->norm != LIN_ATTN_NORM_NONE) return LIN_ATTN_ERR_INVALID;
+    if (p->dtype != LIN_ATTN_F32 && p->dtype != LIN_ATTN_BF16) return LIN_ATTN_ERR_INVALID;
+    if (p->sum_norm != 0 && p->sum_norm != 1) return LIN_ATTN_ERR_INVALID;
+    if (!(p->eps > 0.f) || !isfinite(p->eps) || !isfinite(p->scale)) return LIN_ATTN_ERR_INVALID;
+    if (p->n_seg < 0) return LIN_ATTN_ERR_INVALID;
+    if (d <= 0 || dv <= 0 || p->r <= 0) return LIN_ATTN_ERR_INVALID;
+    switch (p->phi) {
+    case LIN_ATTN_PHI_IDENTITY:
+    case LIN_ATTN_PHI_ELU1:
+        if (p->r != d) return LIN_ATTN_ERR_INVALID;
+        break;
+    case LIN_ATTN_PHI_DPFP:
+        if (p->nu < 1 || p->nu > 2 * d - 1) return LIN_ATTN_ERR_INVALID;
+        if ((int64_t)p->r != 2 * d * p->nu) return LIN_ATTN_ERR_INVALID;
+        break;
+    case LIN_ATTN_PHI_FAVOR:
+        if (!ptr_ok(omega)) return LIN_ATTN_ERR_INVALID;
+        break;
+    }
+    if (d != D || dv != DV) return LIN_ATTN_ERR_UNSUPPORTED;
+    if (p->r % 32 != 0 || p->r > RMAX) return LIN_ATTN_ERR_UNSUPPORTED;
+    return LIN_ATTN_OK;
+}
+
+Cfg make_cfg(const lin_attn_params* p) {
+    Cfg c;
+    c.phi = p->phi;
+    c.r = p->r;
+    c.nu = p->nu;
+    c.sum_norm = p->sum_norm;
+    c.norm = p->norm;
+    c.scale = p->scale;
+    c.eps = p->eps;
+    c.favor_log2_bias = -0.5f * log2f((float)p->r);
+    return c;
+}
+
+int check_sizes(int64_t B, int64_t H, int64_t N) {
+    if (B < 0 || H < 0 || N < 0) return LIN_ATTN_ERR_INVALID;
+    // grid sizes are unsigned 32-bit; keep every flattened grid in range
+    if (B > 0 && H > (((int64_t)1 << 31) / B)) return LIN_ATTN_ERR_UNSUPPORTED;
+    if (B * H > ((int64_t)1 << 24) || N > ((int64_t)1 << 40)) return LIN_ATTN_ERR_UNSUPPORTED;
+    return LIN_ATTN_OK;
+}
+
+// Workspace layout (float32):
+//   [0, BH*G*E)            per-segment state increments, then carried-in states
+//   [BH*G*E, +BH*E)        bidirectional only: the full summary per head
+size_t ws_floats(int32_t op, int64_t BH, SegPlan sp, int r) {
+    const int64_t E = state_elems(r);
+    size_t n = (size_t)(BH * sp.G * E);
+    if (op == LIN_ATTN_OP_BIDIR) n += (size_t)(BH * E);
+    return n;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? LIN_ATTN_OK : LIN_ATTN_ERR_HIP; }
+
+} // namespace
+
+extern "C" {
+
+int32_t lin_attn_abi_version(void) { return LIN_ATTN_ABI_VERSION; }
+
+const char* lin_attn_strerror(int32_t code) {
+    switch (code) {
+    case LIN_ATTN_OK: return "success";
+    case LIN_ATTN_ERR_INVALID: return "invalid argument";
+    case LIN_ATTN_ERR_UNSUPPORTED: return "valid but unsupported on this GPU path";
+    case LIN_ATTN_ERR_WORKSPACE: return "workspace too small";
+    case LIN_ATTN_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown error code";
+    }
+}
+
+size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B, int64_t H,
+                                int64_t N, int64_t d, int64_t dv, int32_t chunk) {
+    (void)chunk;
+    if (op != LIN_ATTN_OP_BIDIR && op != LIN_ATTN_OP_CAUSAL) return 0;
+    if (!p || check_sizes(B, H, N) != LIN_ATTN_OK) return 0;
+    // omega is not needed to size the workspace: check the rest with a dummy
+    const int rc = check_params(p, d, dv, reinterpret_cast<const void*>(uintptr_t(16)));
+    if (rc != LIN_ATTN_OK) return 0;
+    const int64_t BH = B * H;
+    if (BH == 0 || N == 0) return 0;
+    return ws_floats(op, BH, plan_segments(BH, N, p->n_seg), p->r) * sizeof(float);
+}
+
+int lin_attn_featuremap(const lin_attn_params* p, const void* x, int64_t B, int64_t H, int64_t N,
+                        int64_t d, const void* omega, float* phi, void* stream) {
+    int rc = check_params(p, d, DV, omega);
+    if (rc == LIN_ATTN_ERR_INVALID) return rc;
+    const int rs = check_sizes(B, H, N);
+    if (rs == LIN_ATTN_ERR_INVALID) return rs;
+    const bool empty = B * H == 0 || N == 0;
+    if (!empty && (!ptr_ok(x) || !ptr_ok(phi))) return LIN_ATTN_ERR_INVALID;
+    if (rc != LIN_ATTN_OK) return rc;
+    if (rs != LIN_ATTN_OK) return rs;
+    if (empty) return LIN_ATTN_OK;
+    return launch_status(launch_featuremap(make_cfg(p), p->dtype, x, omega, Shape{B * H, N}, phi,
+                                           (hipStream_t)stream));
+}
+
+int lin_attn_bidir(const lin_attn_params* p, const void* q, const void* k, const void* v,
+                   int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, const void* omega,
+                   void* out, float* S_out, float* z_out, void* ws, size_t ws_bytes,
+                   void* stream) {
+    int rc = check_params(p, d, dv, omega);
+    if (rc == LIN_ATTN_ERR_INVALID) return rc;
+    const int rs = check_sizes(B, H, N);
+    if (rs == LIN_ATTN_ERR_INVALID) return rs;
+    if (!opt_ptr_ok(S_out) || !opt_ptr_ok(z_out) || !opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
+    const bool empty = B * H == 0 || N == 0;
+    if (!empty && (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out)))
+        return LIN_ATTN_ERR_INVALID;
+    if (rc != LIN_ATTN_OK) return rc;
+    if (rs != LIN_ATTN_OK) return rs;
+    if (empty) {
+        // no key: the summaries are zero
+        hipError_t e = hipSuccess;
+        if (S_out) e = launch_fill_zero(S_out, B * H * (int64_t)p->r * DV, (hipStream_t)stream);
+        if (e == hipSuccess && z_out) e = launch_fill_zero(z_out, B * H * (int64_t)p->r, (hipStream_t)stream);
+        return launch_status(e);
+    }
+    const int64_t BH = B * H;
+    const SegPlan sp = plan_segments(BH, N, p->n_seg);
+    const size_t need = ws_floats(LIN_ATTN_OP_BIDIR, BH, sp, p->r) * sizeof(float);
+    if (ws_bytes < need || !ws) return LIN_ATTN_ERR_WORKSPACE;
+
+    const Cfg c = make_cfg(p);
+    const Shape s{BH, N};
+    hipStream_t st = (hipStream_t)stream;
+    float* inc = (float*)ws;
+    float* fin = inc + BH * sp.G * state_elems(p->r);
+    hipError_t e = launch_segment_sums(c, p->dtype, k, v, omega, s, sp, inc, st);
+    if (e == hipSuccess)
+        e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc, 0, S_out, z_out, fin, st);
+    if (e == hipSuccess)
+        e = launch_segment_outputs(c, p->dtype, 0, q, k, v, omega, s, sp, fin, state_elems(p->r),
+                                   0, out, st);
+    return launch_status(e);
+}
+
+int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void* k,
+                            const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
+                            int64_t dv, const void* omega, int32_t chunk, float* S, float* z,
+                            int32_t state_in, void* out, void* ws, size_t ws_bytes,
+                            void* stream) {
+    int rc = check_params(p, d, dv, omega);
+    if (rc == LIN_ATTN_ERR_INVALID) return rc;
+    const int rs = check_sizes(B, H, N);
+    if (rs == LIN_ATTN_ERR_INVALID) return rs;
+    if (chunk != 0 && chunk != 32 && chunk != 64 && chunk != 128) return LIN_ATTN_ERR_INVALID;
+    if (state_in != 0 && state_in != 1) return LIN_ATTN_ERR_INVALID;
+    if (!opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
+    if (B * H > 0 && (!ptr_ok(S) || !ptr_ok(z))) return LIN_ATTN_ERR_INVALID;
+    if (B * H > 0 && N > 0 && (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out)))
+        return LIN_ATTN_ERR_INVALID;
+    if (rc != LIN_ATTN_OK) return rc;
+    if (rs != LIN_ATTN_OK) return rs;
+    if (B * H == 0) return LIN_ATTN_OK;
+    if (N == 0) {
+        // no token: the state after token N is the starting state
+        if (state_in) return LIN_ATTN_OK;
+        hipStream_t st = (hipStream_t)stream;
+        hipError_t e = launch_fill_zero(S, B * H * (int64_t)p->r * DV, st);
+        if (e == hipSuccess) e = launch_fill_zero(z, B * H * (int64_t)p->r, st);
+        return launch_status(e);
+    }
+    const int64_t BH = B * H;
+    const SegPlan sp = plan_segments(BH, N, p->n_seg);
+    const size_t need = ws_floats(LIN_ATTN_OP_CAUSAL, BH, sp, p->r) * sizeof(float);
+    if (ws_bytes < need || !ws) return LIN_ATTN_ERR_WORKSPACE;
+
+    const Cfg c = make_cfg(p);
+    const Shape s{BH, N};
+    hipStream_t st = (hipStream_t)stream;
+    float* inc = (float*)ws;
+    const int64_t E = state_elems(p->r);
+    hipError_t e = launch_segment_sums(c, p->dtype, k, v, omega, s, sp, inc, st);
+    if (e == hipSuccess)
+        e = launch_segment_scan(p->r, s, sp, state_in ? S : nullptr, state_in ? z : nullptr, inc,
+                                1, S, z, nullptr, st);
+    if (e == hipSuccess)
+        e = launch_segment_outputs(c, p->dtype, 1, q, k, v, omega, s, sp, inc, sp.G * E, E, out,
+                                   st);
+    return launch_status(e);
+}
+
+int lin_attn_decode_step(const lin_attn_params* p, const void* q, const void* k, const void* v,
+                         int64_t B, int64_t H, int64_t d, int64_t dv, const void* omega, float* S,
+                         float* z, void* out, void* stream) {
+    int rc = check_params(p, d, dv, omega);
+    if (rc == LIN_ATTN_ERR_INVALID) return rc;
+    const int rs = check_sizes(B, H, 1);
+    if (rs == LIN_ATTN_ERR_INVALID) return rs;
+    if (B * H > 0 &&
+        (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out) || !ptr_ok(S) || !ptr_ok(z)))
+        return LIN_ATTN_ERR_INVALID;
+    if (rc != LIN_ATTN_OK) return rc;
+    if (rs != LIN_ATTN_OK) return rs;
+    if (B * H == 0) return LIN_ATTN_OK;
+    return launch_status(
+        launch_decode(make_cfg(p), p->dtype, q, k, v, omega, B * H, S, z, out, (hipStream_t)stream));
+}
+
+} // extern "C"

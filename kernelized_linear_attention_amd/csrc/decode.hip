@@ -1,0 +1,166 @@
+// decode.hip -- one decode step for B*H independent heads (Kernel Zoo sec. 1.2
+// steps 2-3, "update, then read"):
+//   S <- S + phi(k) v^T,  z <- z + phi(k),
+//   out = phi(q)^T S / max(phi(q) . z, eps)     (or phi(q)^T S, NORM_NONE)
+//
+// The step is a streaming read-modify-write of the float32 state: per head
+// r*dv*4 bytes of S (64 KiB at r = 256) are read and written once, against
+// ~2 flops per byte, so the kernel is bound by HBM bandwidth.  One workgroup
+// per head: every thread issues all of its S loads (16-byte, non-temporal)
+// before it computes its share of phi(q), phi(k), so the feature map runs
+// under the load latency; the new S goes straight back with non-temporal
+// stores and the readout is accumulated from registers.
+#include "launch.hpp"
+
+namespace linattn {
+namespace {
+
+constexpr int NT = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int MAXM = RMAX * DV / 4 / NT; // float4 chunks of S per thread at r = RMAX
+
+template <typename T>
+__global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
+                                               const T* __restrict__ k,
+                                               const T* __restrict__ v,
+                                               const T* __restrict__ omega,
+                                               float* __restrict__ S, float* __restrict__ z,
+                                               T* __restrict__ out) {
+    __shared__ float uq_s[D], uk_s[D], v_s[DV];
+    __shared__ float pq_s[RMAX], pk_s[RMAX];
+    __shared__ float red_s[NT / 64][DV];
+    __shared__ float scal_s[8];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t bh = blockIdx.x;
+    const int r = c.r;
+    const int m_count = r * DV / 4 / NT; // rows of S per thread: r / 16
+
+    // 1. issue every S load of this thread: float4 e = tid + NT*m is row
+    //    e / 16 = tid/16 + 16m, columns 4*(tid%16) .. +3.
+    f32x4* S4 = reinterpret_cast<f32x4*>(S + bh * (int64_t)r * DV);
+    f32x4 s[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m)
+        if (m < m_count) s[m] = __builtin_nontemporal_load(S4 + tid + NT * m);
+    float zold = 0.f;
+    if (tid < r) zold = z[bh * r + tid];
+
+    // 2. inputs of this head
+    if (tid < D) {
+        uq_s[tid] = c.scale * Elem<T>::load(q, bh * D + tid);
+        uk_s[tid] = c.scale * Elem<T>::load(k, bh * D + tid);
+        v_s[tid] = Elem<T>::load(v, bh * DV + tid);
+    }
+    __syncthreads();
+    if (c.phi == PHI_FAVOR && w < 2) {
+        const float a = (w == 0 ? uq_s : uk_s)[lane];
+        const float n = wave_sum(a * a);
+        if (lane == 0) scal_s[w] = n;
+    }
+    __syncthreads();
+
+    // 3. one feature of phi(q) and phi(k) per thread
+    float pq = 0.f, pk = 0.f;
+    if (tid < r) {
+        pq = phi_feature<T>(c, uq_s, scal_s[0], tid, omega);
+        pk = phi_feature<T>(c, uk_s, scal_s[1], tid, omega);
+    }
+    if (c.sum_norm) {
+        const float a = wave_sum(pq), b = wave_sum(pk);
+        if (lane == 0) {
+            red_s[w][0] = a;
+            red_s[w][1] = b;
+        }
+        __syncthreads();
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int i = 0; i < NT / 64; ++i) {
+            sq += red_s[i][0];
+            sk += red_s[i][1];
+        }
+        pq *= 1.f / fmaxf(sq, c.eps);
+        pk *= 1.f / fmaxf(sk, c.eps);
+        __syncthreads(); // red_s is reused below
+    }
+    if (tid < r) {
+        pq_s[tid] = pq;
+        pk_s[tid] = pk;
+    }
+
+    // 4. z <- z + phi(k); den = phi(q) . z
+    float den_part = 0.f;
+    if (tid < r) {
+        const float zn = zold + pk;
+        z[bh * r + tid] = zn;
+        den_part = pq * zn;
+    }
+    den_part = wave_sum(den_part);
+    if (lane == 0) scal_s[2 + w] = den_part;
+    __syncthreads();
+
+    // 5. S rows: S <- S + phi(k)_row v^T, o += phi(q)_row S_row
+    const int c4 = (tid % 16) * 4;
+    const float4 vv = make_float4(v_s[c4], v_s[c4 + 1], v_s[c4 + 2], v_s[c4 + 3]);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        if (m < m_count) {
+            const int row = tid / 16 + 16 * m;
+            const float a = pk_s[row], b = pq_s[row];
+            f32x4 x = s[m];
+            x.x = fmaf(a, vv.x, x.x);
+            x.y = fmaf(a, vv.y, x.y);
+            x.z = fmaf(a, vv.z, x.z);
+            x.w = fmaf(a, vv.w, x.w);
+            __builtin_nontemporal_store(x, S4 + tid + NT * m);
+            o.x = fmaf(b, x.x, o.x);
+            o.y = fmaf(b, x.y, o.y);
+            o.z = fmaf(b, x.z, o.z);
+            o.w = fmaf(b, x.w, o.w);
+        }
+    }
+    // 6. reduce o over the 16 threads sharing columns c4..c4+3: lanes l^16,
+    //    l^32 within the wave, then the NT/64 waves through LDS.
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
+        o.x += __shfl_xor(o.x, off, 64);
+        o.y += __shfl_xor(o.y, off, 64);
+        o.z += __shfl_xor(o.z, off, 64);
+        o.w += __shfl_xor(o.w, off, 64);
+    }
+    if (lane < 16) {
+        red_s[w][c4] = o.x;
+        red_s[w][c4 + 1] = o.y;
+        red_s[w][c4 + 2] = o.z;
+        red_s[w][c4 + 3] = o.w;
+    }
+    __syncthreads();
+    if (tid < DV) {
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int i = 0; i < NT / 64; ++i) {
+            num += red_s[i][tid];
+            den += scal_s[2 + i];
+        }
+        const float y = c.norm == NORM_ATTN ? num / fmaxf(den, c.eps) : num;
+        Elem<T>::store(out, bh * DV + tid, y);
+    }
+}
+
+} // namespace
+
+hipError_t launch_decode(const Cfg& c, int dtype, const void* q, const void* k, const void* v,
+                         const void* omega, int64_t BH, float* S, float* z, void* out,
+                         hipStream_t st) {
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_decode<float>, dim3((unsigned)BH), dim3(NT), 0, st, c,
+                           (const float*)q, (const float*)k, (const float*)v,
+                           (const float*)omega, S, z, (float*)out);
+    else
+        hipLaunchKernelGGL(k_decode<bf16_raw>, dim3((unsigned)BH), dim3(NT), 0, st, c,
+                           (const bf16_raw*)q, (const bf16_raw*)k, (const bf16_raw*)v,
+                           (const bf16_raw*)omega, S, z, (bf16_raw*)out);
+    return hipGetLastError();
+}
+
+} // namespace linattn

@@ -1,0 +1,468 @@
+// generic.hip -- LDS-tiled kernels with float32 vector arithmetic, for every
+// feature map, float32 and bfloat16 inputs, r a multiple of 32 up to 256.
+//
+// The chunked scan follows the causal recurrence of the Kernel Zoo (sec. 1.3,
+// sec. 5.4): S_t = S_{t-1} + phi(k_t) v_t^T, z_t = z_{t-1} + phi(k_t),
+// out_t = phi(q_t)^T S_t / max(phi(q_t) . z_t, eps).  It is evaluated as
+//   segments (workgroups) -> chunks of L tokens -> tokens,
+// where for a chunk c with carried-in state (S_{c-1}, z_{c-1})
+//   num_t = phi(q_t)^T S_{c-1} + sum_{j<=t in c} (phi(q_t) . phi(k_j)) v_j
+//   den_t = phi(q_t) . z_{c-1} + sum_{j<=t in c}  phi(q_t) . phi(k_j)
+// and S_c = S_{c-1} + phi(K_c)^T V_c, z_c = z_{c-1} + phi(K_c)^T 1: the same
+// sums, re-associated.  Segment starting states come from an exclusive prefix
+// sum of per-segment increments (launch_segment_scan), summed in a fixed
+// order, so results are bitwise reproducible.
+#include <algorithm>
+
+#include "launch.hpp"
+
+namespace linattn {
+namespace {
+
+constexpr int NT = 256; // threads per workgroup in this file
+
+// Copies `rows` rows of a [*, 64] matrix (zero rows after `rows`, up to L)
+// into dst[L][64] as scale * x.
+template <typename T, int L>
+__device__ void load_rows(const T* __restrict__ src, int rows, float scale, float* dst) {
+    for (int g = threadIdx.x; g < L * (D / 4); g += NT) {
+        const int row = g / (D / 4), c4 = (g % (D / 4)) * 4;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row < rows) x = Elem<T>::load4(src, (long)row * D + c4);
+        float* o = dst + row * D + c4;
+        o[0] = scale * x.x;
+        o[1] = scale * x.y;
+        o[2] = scale * x.z;
+        o[3] = scale * x.w;
+    }
+}
+
+// nrm[t] = |u_t|^2 for the L rows of u[L][64] (one wave per row).
+template <int L>
+__device__ void row_norms(const float* u, float* nrm) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int t = w; t < L; t += NT / 64) {
+        float a = u[t * D + lane];
+        float s = wave_sum(a * a);
+        if (lane == 0) nrm[t] = s;
+    }
+}
+
+// out[t][f] = phi_f(u_t) for t < L, f < r (rows >= `rows` are zero), then the
+// optional sum normalisation.  u, nrm must be complete (caller synchronised).
+// Ends with a barrier.
+template <typename T, int L>
+__device__ void phi_tile(const Cfg& c, const float* u, const float* nrm,
+                         const T* __restrict__ omega, int rows, float* out, int ol, float* rs) {
+    const int tid = threadIdx.x;
+    if (c.phi == PHI_FAVOR) {
+        for (int f = tid; f < c.r; f += NT) {
+            float w[D];
+#pragma unroll
+            for (int i = 0; i < D; i += 4) {
+                float4 x = Elem<T>::load4(omega, (long)f * D + i);
+                w[i] = x.x;
+                w[i + 1] = x.y;
+                w[i + 2] = x.z;
+                w[i + 3] = x.w;
+            }
+            for (int t = 0; t < L; ++t) {
+                float dot = 0.f;
+#pragma unroll
+                for (int i = 0; i < D; ++i) dot = fmaf(w[i], u[t * D + i], dot);
+                out[t * ol + f] = t < rows ? favor_feature(c, dot, nrm[t]) : 0.f;
+            }
+        }
+    } else {
+        for (int idx = tid; idx < L * c.r; idx += NT) {
+            const int t = idx / c.r, f = idx - t * c.r;
+            float y = 0.f;
+            if (t < rows) y = phi_feature<T>(c, u + t * D, 0.f, f, omega);
+            out[t * ol + f] = y;
+        }
+    }
+    __syncthreads();
+    if (c.sum_norm) {
+        const int lane = tid & 63, w = tid >> 6;
+        for (int t = w; t < L; t += NT / 64) {
+            float s = 0.f;
+            for (int f = lane; f < c.r; f += 64) s += out[t * ol + f];
+            s = wave_sum(s);
+            if (lane == 0) rs[t] = 1.f / fmaxf(s, c.eps);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < L * c.r; idx += NT) {
+            const int t = idx / c.r, f = idx - t * c.r;
+            out[t * ol + f] *= rs[t];
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Feature map alone: phi [BH, N, r] float32.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(NT) void k_featuremap(Cfg c, const T* __restrict__ x,
+                                                   const T* __restrict__ omega, int64_t N,
+                                                   int64_t tiles, float* __restrict__ phi) {
+    constexpr int L = 32;
+    __shared__ float u_s[L * D];
+    __shared__ float p_s[L * (RMAX + 4)];
+    __shared__ float nrm_s[L], rs_s[L];
+    const int64_t bh = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int64_t t0 = tile * L;
+    const int rows = (int)min<int64_t>(L, N - t0);
+    const int ol = c.r + 4;
+    load_rows<T, L>(x + (bh * N + t0) * D, rows, c.scale, u_s);
+    __syncthreads();
+    row_norms<L>(u_s, nrm_s);
+    __syncthreads();
+    phi_tile<T, L>(c, u_s, nrm_s, omega, rows, p_s, ol, rs_s);
+    float* dst = phi + (bh * N + t0) * c.r;
+    for (int idx = threadIdx.x; idx < rows * c.r; idx += NT) {
+        const int t = idx / c.r, f = idx - t * c.r;
+        dst[(long)t * c.r + f] = p_s[t * ol + f];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Segment state increments: ws[bh][g] = (sum phi(k_j) v_j^T, sum phi(k_j)).
+// Thread (fb = tid/8, nb = tid%8) owns S[fb*FPT + i][nb*8 + j], i < FPT, j < 8.
+// ---------------------------------------------------------------------------
+template <typename T, int FPT>
+__global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict__ k,
+                                                     const T* __restrict__ v,
+                                                     const T* __restrict__ omega, int64_t N,
+                                                     int64_t G, int64_t seg_len,
+                                                     float* __restrict__ ws) {
+    constexpr int L = 64;
+    constexpr int R = 32 * FPT;
+    constexpr int OL = R + 4;
+    __shared__ float u_s[L * D];
+    __shared__ float v_s[L * DV];
+    __shared__ float p_s[L * OL];
+    __shared__ float nrm_s[L], rs_s[L];
+    const int tid = threadIdx.x;
+    const int fb = tid / 8, nb = tid % 8;
+    const int64_t bh = blockIdx.x / G, g = blockIdx.x % G;
+    const int64_t t0 = g * seg_len, t1 = min<int64_t>(N, t0 + seg_len);
+
+    float acc[FPT][8];
+    float zacc[FPT];
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) {
+        zacc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    }
+    for (int64_t c0 = t0; c0 < t1; c0 += L) {
+        const int rows = (int)min<int64_t>(L, t1 - c0);
+        load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, u_s);
+        load_rows<T, L>(v + (bh * N + c0) * DV, rows, 1.f, v_s);
+        __syncthreads();
+        row_norms<L>(u_s, nrm_s);
+        __syncthreads();
+        phi_tile<T, L>(c, u_s, nrm_s, omega, rows, p_s, OL, rs_s);
+        for (int t = 0; t < rows; ++t) {
+            float vv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vv[j] = v_s[t * DV + nb * 8 + j];
+#pragma unroll
+            for (int i = 0; i < FPT; ++i) {
+                const float p = p_s[t * OL + fb * FPT + i];
+                zacc[i] += p;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(p, vv[j], acc[i][j]);
+            }
+        }
+        __syncthreads();
+    }
+    float* dst = ws + (bh * G + g) * state_elems(R);
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) {
+        const int f = fb * FPT + i;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[(long)f * DV + nb * 8 + j] = acc[i][j];
+        if (nb == 0) dst[(long)R * DV + f] = zacc[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prefix over segments, one thread per state element, fixed order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const float* __restrict__ S0,
+                                                     const float* __restrict__ z0,
+                                                     float* __restrict__ ws, int write_prefix,
+                                                     float* __restrict__ S_fin,
+                                                     float* __restrict__ z_fin,
+                                                     float* __restrict__ fin) {
+    const int64_t E = state_elems(r);
+    const int64_t blocks_per_head = (E + NT - 1) / NT;
+    const int64_t bh = blockIdx.x / blocks_per_head;
+    const int64_t e = (blockIdx.x % blocks_per_head) * NT + threadIdx.x;
+    if (e >= E) return;
+    const int64_t rdv = (int64_t)r * DV;
+    float run = 0.f;
+    if (S0) run = e < rdv ? S0[bh * rdv + e] : z0[bh * r + (e - rdv)];
+    float* p = ws + bh * G * E + e;
+    for (int64_t g = 0; g < G; ++g) {
+        const float a = p[g * E];
+        if (write_prefix) p[g * E] = run;
+        run += a;
+    }
+    if (e < rdv) {
+        if (S_fin) S_fin[bh * rdv + e] = run;
+    } else {
+        if (z_fin) z_fin[bh * r + (e - rdv)] = run;
+    }
+    if (fin) fin[bh * E + e] = run;
+}
+
+// ---------------------------------------------------------------------------
+// Segment outputs.  CAUSAL: chunked recurrence from the carried-in state;
+// otherwise: readout of every token against the full summary.
+// ---------------------------------------------------------------------------
+template <typename T, int FPT, bool CAUSAL>
+__global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restrict__ q,
+                                                        const T* __restrict__ k,
+                                                        const T* __restrict__ v,
+                                                        const T* __restrict__ omega, int64_t N,
+                                                        int64_t G, int64_t seg_len,
+                                                        const float* __restrict__ state,
+                                                        int64_t st_bh, int64_t st_g,
+                                                        T* __restrict__ out) {
+    constexpr int L = 32;
+    constexpr int R = 32 * FPT;
+    constexpr int OL = R + 4;
+    constexpr int LC = CAUSAL ? L : 1;
+    __shared__ float S_s[R * DV];
+    __shared__ float z_s[R];
+    __shared__ float pq_s[L * OL];
+    __shared__ float pk_s[LC * OL];
+    __shared__ float v_s[LC * DV];
+    __shared__ float a_s[LC * (L + 1)];
+    __shared__ float u_s[L * D];
+    __shared__ float nrm_s[L], rs_s[L];
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x / G, g = blockIdx.x % G;
+    const int64_t t0 = g * seg_len, t1 = min<int64_t>(N, t0 + seg_len);
+
+    const float* sin = state + bh * st_bh + g * st_g;
+    for (int e = tid; e < R * DV; e += NT) S_s[e] = sin[e];
+    for (int f = tid; f < R; f += NT) z_s[f] = sin[R * DV + f];
+
+    // readout thread mapping: token t = tid / 8, value columns nb*8 .. nb*8+7
+    const int rt = tid / 8, nb = tid % 8;
+    // update thread mapping: features fb*FPT + i, value columns nb*8 + j
+    const int fb = tid / 8;
+
+    for (int64_t c0 = t0; c0 < t1; c0 += L) {
+        const int rows = (int)min<int64_t>(L, t1 - c0);
+        if (CAUSAL) {
+            load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, u_s);
+            load_rows<T, L>(v + (bh * N + c0) * DV, rows, 1.f, v_s);
+            __syncthreads();
+            row_norms<L>(u_s, nrm_s);
+            __syncthreads();
+            phi_tile<T, L>(c, u_s, nrm_s, omega, rows, pk_s, OL, rs_s);
+        }
+        load_rows<T, L>(q + (bh * N + c0) * D, rows, c.scale, u_s);
+        __syncthreads();
+        row_norms<L>(u_s, nrm_s);
+        __syncthreads();
+        phi_tile<T, L>(c, u_s, nrm_s, omega, rows, pq_s, OL, rs_s);
+
+        if (CAUSAL) {
+            // masked intra-chunk block a[t][j] = phi(q_t) . phi(k_j), j <= t
+            for (int p = tid; p < L * L; p += NT) {
+                const int t = p % L, j = p / L;
+                float a = 0.f;
+                if (j <= t) {
+                    const float* x = pq_s + t * OL;
+                    const float* y = pk_s + j * OL;
+                    for (int f = 0; f < R; f += 4) {
+                        a = fmaf(x[f], y[f], a);
+                        a = fmaf(x[f + 1], y[f + 1], a);
+                        a = fmaf(x[f + 2], y[f + 2], a);
+                        a = fmaf(x[f + 3], y[f + 3], a);
+                    }
+                }
+                a_s[t * (L + 1) + j] = a;
+            }
+            __syncthreads();
+        }
+
+        // readout against the carried-in state, plus the intra-chunk block
+        {
+            float num[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) num[j] = 0.f;
+            float den = 0.f;
+            const float* x = pq_s + rt * OL;
+            for (int f = 0; f < R; ++f) {
+                const float pf = x[f];
+                den = fmaf(pf, z_s[f], den);
+                const float* srow = S_s + f * DV + nb * 8;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) num[j] = fmaf(pf, srow[j], num[j]);
+            }
+            if (CAUSAL) {
+                for (int jj = 0; jj <= rt; ++jj) {
+                    const float a = a_s[rt * (L + 1) + jj];
+                    den += a;
+                    const float* vrow = v_s + jj * DV + nb * 8;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) num[j] = fmaf(a, vrow[j], num[j]);
+                }
+            }
+            if (rt < rows) {
+                T* o = out + (bh * N + c0 + rt) * DV + nb * 8;
+                const float inv = c.norm == NORM_ATTN ? 1.f / fmaxf(den, c.eps) : 1.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float y = c.norm == NORM_ATTN ? num[j] * inv : num[j];
+                    Elem<T>::store(o, j, y);
+                }
+            }
+        }
+
+        if (CAUSAL) {
+            __syncthreads(); // every read of S_s / z_s for this chunk is done
+#pragma unroll
+            for (int i = 0; i < FPT; ++i) {
+                const int f = fb * FPT + i;
+                float s[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s[j] = S_s[f * DV + nb * 8 + j];
+                float zf = 0.f;
+                for (int t = 0; t < rows; ++t) {
+                    const float p = pk_s[t * OL + f];
+                    zf += p;
+                    const float* vrow = v_s + t * DV + nb * 8;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) s[j] = fmaf(p, vrow[j], s[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) S_s[f * DV + nb * 8 + j] = s[j];
+                if (nb == 0) z_s[f] += zf;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <typename T>
+hipError_t featuremap_t(const Cfg& c, const void* x, const void* omega, Shape s, float* phi,
+                        hipStream_t st) {
+    const int64_t tiles = (s.N + 31) / 32;
+    hipLaunchKernelGGL(k_featuremap<T>, dim3((unsigned)(tiles * s.BH)), dim3(NT), 0, st, c,
+                       (const T*)x, (const T*)omega, s.N, tiles, phi);
+    return hipGetLastError();
+}
+
+template <typename T, int FPT>
+void sums_fpt(const Cfg& c, const void* k, const void* v, const void* omega, Shape s, SegPlan sp,
+              float* ws, hipStream_t st) {
+    hipLaunchKernelGGL((k_segment_sums<T, FPT>), dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0, st,
+                       c, (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G, sp.seg_len, ws);
+}
+
+template <typename T>
+hipError_t segment_sums_t(const Cfg& c, const void* k, const void* v, const void* omega, Shape s,
+                          SegPlan sp, float* ws, hipStream_t st) {
+    switch (c.r / 32) {
+    case 1: sums_fpt<T, 1>(c, k, v, omega, s, sp, ws, st); break;
+    case 2: sums_fpt<T, 2>(c, k, v, omega, s, sp, ws, st); break;
+    case 3: sums_fpt<T, 3>(c, k, v, omega, s, sp, ws, st); break;
+    case 4: sums_fpt<T, 4>(c, k, v, omega, s, sp, ws, st); break;
+    case 5: sums_fpt<T, 5>(c, k, v, omega, s, sp, ws, st); break;
+    case 6: sums_fpt<T, 6>(c, k, v, omega, s, sp, ws, st); break;
+    case 7: sums_fpt<T, 7>(c, k, v, omega, s, sp, ws, st); break;
+    case 8: sums_fpt<T, 8>(c, k, v, omega, s, sp, ws, st); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int FPT>
+void outputs_fpt(const Cfg& c, int causal, const void* q, const void* k, const void* v,
+                 const void* omega, Shape s, SegPlan sp, const float* state, int64_t sbh,
+                 int64_t sg, void* out, hipStream_t st) {
+    const dim3 grid((unsigned)(sp.G * s.BH)), block(NT);
+    if (causal)
+        hipLaunchKernelGGL((k_segment_outputs<T, FPT, true>), grid, block, 0, st, c, (const T*)q,
+                           (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G, sp.seg_len,
+                           state, sbh, sg, (T*)out);
+    else
+        hipLaunchKernelGGL((k_segment_outputs<T, FPT, false>), grid, block, 0, st, c,
+                           (const T*)q, (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G,
+                           sp.seg_len, state, sbh, sg, (T*)out);
+}
+
+template <typename T>
+hipError_t segment_outputs_t(const Cfg& c, int causal, const void* q, const void* k,
+                             const void* v, const void* omega, Shape s, SegPlan sp,
+                             const float* state, int64_t sbh, int64_t sg, void* out,
+                             hipStream_t st) {
+    switch (c.r / 32) {
+    case 1: outputs_fpt<T, 1>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
+    case 2: outputs_fpt<T, 2>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
+    case 3: outputs_fpt<T, 3>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
+    case 4: outputs_fpt<T, 4>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
+    case 5: outputs_fpt<T, 5>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
+    case 6: outputs_fpt<T, 6>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
+    case 7: outputs_fpt<T, 7>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
+    case 8: outputs_fpt<T, 8>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(NT) void k_fill_zero(float* __restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT)
+        p[i] = 0.f;
+}
+
+} // namespace
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + NT - 1) / NT, 4096);
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(NT), 0, st, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_featuremap(const Cfg& c, int dtype, const void* x, const void* omega, Shape s,
+                             float* phi, hipStream_t st) {
+    return dtype == 0 ? featuremap_t<float>(c, x, omega, s, phi, st)
+                      : featuremap_t<bf16_raw>(c, x, omega, s, phi, st);
+}
+
+hipError_t launch_segment_sums(const Cfg& c, int dtype, const void* k, const void* v,
+                               const void* omega, Shape s, SegPlan sp, float* ws, hipStream_t st) {
+    return dtype == 0 ? segment_sums_t<float>(c, k, v, omega, s, sp, ws, st)
+                      : segment_sums_t<bf16_raw>(c, k, v, omega, s, sp, ws, st);
+}
+
+hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, const float* z0,
+                               float* ws, int write_prefix, float* S_fin, float* z_fin,
+                               float* fin, hipStream_t st) {
+    const int64_t E = state_elems(r);
+    const dim3 grid((unsigned)(((E + NT - 1) / NT) * s.BH));
+    hipLaunchKernelGGL(k_segment_scan, grid, dim3(NT), 0, st, r, sp.G, S0, z0, ws, write_prefix,
+                       S_fin, z_fin, fin);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_outputs(const Cfg& c, int dtype, int causal, const void* q,
+                                  const void* k, const void* v, const void* omega, Shape s,
+                                  SegPlan sp, const float* state, int64_t sbh, int64_t sg,
+                                  void* out, hipStream_t st) {
+    return dtype == 0
+               ? segment_outputs_t<float>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st)
+               : segment_outputs_t<bf16_raw>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out,
+                                             st);
+}
+
+} // namespace linattn

@@ -1,0 +1,77 @@
+// launch.hpp -- host-side launchers of the kernels, called by the C ABI layer
+// after it has validated every argument.  All sizes are already known to be
+// in range; each launcher only enqueues work on `st` and reports the launch
+// status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace linattn {
+
+// Sequence segmentation used by the parallel scan: G segments of seg_len
+// tokens per head (the last may be shorter); every segment boundary is a
+// multiple of SEG_UNIT tokens.
+constexpr int64_t SEG_UNIT = 64;
+constexpr int64_t TARGET_BLOCKS = 512; // aim for about two workgroups per CU
+
+struct SegPlan {
+    int64_t G;
+    int64_t seg_len;
+};
+
+inline SegPlan plan_segments(int64_t BH, int64_t N, int32_t n_seg_req) {
+    SegPlan p{1, N};
+    if (N <= 0 || BH <= 0) return p;
+    const int64_t units = (N + SEG_UNIT - 1) / SEG_UNIT;
+    int64_t G = n_seg_req > 0 ? n_seg_req : (TARGET_BLOCKS + BH - 1) / BH;
+    if (G < 1) G = 1;
+    if (G > units) G = units;
+    const int64_t per = (units + G - 1) / G;
+    p.G = (units + per - 1) / per;
+    p.seg_len = per * SEG_UNIT;
+    return p;
+}
+
+// Elements of one (S | z) state block: r*dv floats of S followed by r of z.
+__host__ __device__ inline int64_t state_elems(int r) { return (int64_t)r * DV + r; }
+
+struct Shape {
+    int64_t BH; // batch * heads
+    int64_t N;  // tokens per head
+};
+
+// dtype-erased launchers (T is float or bf16_raw inside)
+hipError_t launch_featuremap(const Cfg& c, int dtype, const void* x, const void* omega, Shape s,
+                             float* phi, hipStream_t st);
+
+// State increments of every segment: ws[bh][g] = sum over the segment of
+// phi(k_j) v_j^T (then z).
+hipError_t launch_segment_sums(const Cfg& c, int dtype, const void* k, const void* v,
+                               const void* omega, Shape s, SegPlan sp, float* ws, hipStream_t st);
+
+// Prefix over segments.  Reads S0/z0 (may be NULL = zero), turns ws[bh][g]
+// into the exclusive prefix when write_prefix, and writes the total to
+// S_fin / z_fin / fin (each may be NULL).
+hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, const float* z0,
+                               float* ws, int write_prefix, float* S_fin, float* z_fin,
+                               float* fin, hipStream_t st);
+
+// Outputs of every segment.  causal: chunked recurrence from the segment's
+// carried-in state ws[bh][g]; bidirectional: readout against the full
+// summary fin[bh].
+hipError_t launch_segment_outputs(const Cfg& c, int dtype, int causal, const void* q,
+                                  const void* k, const void* v, const void* omega, Shape s,
+                                  SegPlan sp, const float* state, int64_t state_bh_stride,
+                                  int64_t state_g_stride, void* out, hipStream_t st);
+
+// p[0, n) = 0 with a plain kernel (capturable into a graph).
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+hipError_t launch_decode(const Cfg& c, int dtype, const void* q, const void* k, const void* v,
+                         const void* omega, int64_t BH, float* S, float* z, void* out,
+                         hipStream_t st);
+
+} // namespace linattn

@@ -1,0 +1,91 @@
+"""Helpers of the GPU parity tests: seeded inputs on the device, their exact
+values for the oracle, and the comparison metric.
+
+Tolerance (relative, per (batch, head) slice, both must hold):
+    max|gpu - ref| / max|ref|  <= tol   and   ||gpu - ref||_F / ||ref||_F <= tol
+with tol = 1e-4 for float32 inputs and 2e-2 for bfloat16 inputs (float32
+accumulation).  The oracle always receives the inputs the GPU received,
+after rounding to the compute dtype, upcast exactly to float64.
+"""
+import numpy as np
+import torch
+
+import oracle
+from kernelized_linear_attention_amd import inputs
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(dtype)
+
+
+def host(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def slice_errors(gpu, ref, lead_dims):
+    """Worst (max-abs ratio, Frobenius ratio) over the leading slices."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    n = int(np.prod(g.shape[:lead_dims])) if lead_dims else 1
+    g = g.reshape(n, -1)
+    r = r.reshape(n, -1)
+    worst_max = worst_fro = 0.0
+    for i in range(n):
+        d = g[i] - r[i]
+        ra = np.max(np.abs(r[i])) if r[i].size else 0.0
+        if ra == 0.0:
+            # an all-zero reference slice must come back exactly zero
+            assert np.all(g[i] == 0.0), f"slice {i}: expected zeros"
+            continue
+        worst_max = max(worst_max, np.max(np.abs(d)) / ra)
+        worst_fro = max(worst_fro, np.linalg.norm(d) / np.linalg.norm(r[i]))
+    return worst_max, worst_fro
+
+
+def assert_parity(gpu, ref, tol, what, lead_dims=2):
+    assert np.all(np.isfinite(host(gpu) if isinstance(gpu, torch.Tensor) else gpu)), what
+    g = host(gpu) if isinstance(gpu, torch.Tensor) else gpu
+    e_max, e_fro = slice_errors(g, ref, lead_dims)
+    assert e_max <= tol and e_fro <= tol, f"{what}: max-rel {e_max:.3e}, fro-rel {e_fro:.3e} > {tol}"
+    return e_max, e_fro
+
+
+class Case:
+    """Seeded q, k, v (and omega) for one shape; device tensors + oracle arrays."""
+
+    def __init__(self, wid, B, H, N, kind, dtype, *, r=None, nu=1, d=64, dv=64, rep=0,
+                 omega_kind="orf"):
+        self.dtype = dtype
+        self.kind = kind
+        self.nu = nu
+        self.q = dev(inputs.normal((B, H, N, d), wid, inputs.T_Q, rep), dtype)
+        self.k = dev(inputs.normal((B, H, N, d), wid, inputs.T_K, rep), dtype)
+        self.v = dev(inputs.normal((B, H, N, dv), wid, inputs.T_V, rep), dtype)
+        self.omega = None
+        self.omega_h = None
+        if kind == "favor":
+            sampler = inputs.orf_omega if omega_kind == "orf" else inputs.iid_omega
+            self.omega = dev(sampler(r, d, wid, rep), dtype)
+            self.omega_h = host(self.omega)
+        self.qh, self.kh, self.vh = host(self.q), host(self.k), host(self.v)
+
+    def okw(self, **kw):
+        """keyword arguments shared by the oracle and the binding"""
+        out = dict(omega=self.omega_h, nu=self.nu)
+        out.update(kw)
+        return out
+
+    def gkw(self, **kw):
+        out = dict(omega=self.omega, nu=self.nu)
+        out.update(kw)
+        return out
+
+
+def oracle_prefix_state(case_q, case_k, case_v, kind, **kw):
+    """State after a causal prefix, from the oracle, rounded to float32."""
+    _, S, z = oracle.causal(case_q, case_k, case_v, kind, **kw)
+    return S.astype(np.float32), z.astype(np.float32)

@@ -1,0 +1,190 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, agrees with the header on constants and struct layout, and rejects
+bad arguments before enqueueing anything.  No call here reaches a kernel
+launch: each one fails validation (or is an empty no-op) first.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "lin_attn.h")
+
+binding = pytest.importorskip("kernelized_linear_attention_amd.binding")
+lib = binding.raw()
+P = binding.LinAttnParams
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def header_defines():
+    out = {}
+    for m in re.finditer(r"#define\s+(LIN_ATTN_\w+)\s+\(?(-?\d+)\)?", header_text()):
+        out[m.group(1)] = int(m.group(2))
+    return out
+
+
+def test_every_declared_symbol_is_exported():
+    declared = set(re.findall(r"^\s*(?:int|size_t|const char\*|int32_t)\s+(lin_attn_\w+)\s*\(",
+                              header_text(), flags=re.M))
+    assert declared == set(binding.EXPORTS)
+    nm = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(lin_attn_\w+)", nm))
+    assert declared <= exported
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_constants_match_header():
+    d = header_defines()
+    assert d["LIN_ATTN_ABI_VERSION"] == binding.lin_attn_abi_version() == binding.ABI_VERSION
+    assert {k: d["LIN_ATTN_PHI_" + k.upper().replace("ELU1", "ELU1")] for k in binding.PHI} == \
+        binding.PHI
+    assert d["LIN_ATTN_NORM_ATTN"] == binding.NORM["attn"]
+    assert d["LIN_ATTN_NORM_NONE"] == binding.NORM["none"]
+    assert d["LIN_ATTN_F32"] == 0 and d["LIN_ATTN_BF16"] == 1
+    assert d["LIN_ATTN_OP_BIDIR"] == binding.OP_BIDIR
+    assert d["LIN_ATTN_OP_CAUSAL"] == binding.OP_CAUSAL
+    assert (d["LIN_ATTN_OK"], d["LIN_ATTN_ERR_INVALID"], d["LIN_ATTN_ERR_UNSUPPORTED"],
+            d["LIN_ATTN_ERR_WORKSPACE"], d["LIN_ATTN_ERR_HIP"]) == (0, -1, -2, -3, -4)
+
+
+def test_params_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    fields = [f for f, _ in P._fields_]
+    body = "".join(f'printf("%zu ", offsetof(lin_attn_params, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lin_attn.h"\n'
+                   f'int main(void){{ {body} printf("%zu\\n", sizeof(lin_attn_params)); return 0; }}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True,
+                                       check=True).stdout.split()))
+    assert got[:-1] == [getattr(P, f).offset for f in fields]
+    assert got[-1] == ctypes.sizeof(P)
+
+
+def test_strerror_covers_every_code():
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert binding.lin_attn_strerror(code) != "unknown error code"
+    assert binding.lin_attn_strerror(7) == "unknown error code"
+
+
+def params(kind="favor", r=256, **kw):
+    base = dict(nu=1, sum_norm=0, norm=0, dtype=1, scale=0.35, eps=1e-6, n_seg=0, reserved=0)
+    base.update(kw)
+    return P(binding.PHI[kind], r, base["nu"], base["sum_norm"], base["norm"], base["dtype"],
+             base["scale"], base["eps"], base["n_seg"], base["reserved"])
+
+
+def bidir(p, B=1, H=2, N=100, d=64, dv=64, ptr=FAKE, omega=FAKE, ws=FAKE, ws_bytes=1 << 40,
+          S_out=None, z_out=None):
+    pp = None if p is None else ctypes.byref(p)
+    return lib.lin_attn_bidir(pp, ptr, ptr, ptr, B, H, N, d, dv, omega, ptr, S_out, z_out, ws,
+                              ws_bytes, None)
+
+
+def causal(p, B=1, H=2, N=100, d=64, dv=64, ptr=FAKE, omega=FAKE, chunk=0, state_in=0, ws=FAKE,
+           ws_bytes=1 << 40, S=FAKE, z=FAKE):
+    return lib.lin_attn_causal_chunked(ctypes.byref(p), ptr, ptr, ptr, B, H, N, d, dv, omega, chunk,
+                                       S, z, state_in, ptr, ws, ws_bytes, None)
+
+
+def decode(p, B=4, H=2, d=64, dv=64, ptr=FAKE, omega=FAKE):
+    return lib.lin_attn_decode_step(ctypes.byref(p), ptr, ptr, ptr, B, H, d, dv, omega, ptr, ptr,
+                                    ptr, None)
+
+
+def featuremap(p, B=1, H=1, N=10, d=64, ptr=FAKE, omega=FAKE):
+    return lib.lin_attn_featuremap(ctypes.byref(p), ptr, B, H, N, d, omega, ptr, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(phi=7), dict(norm=3), dict(dtype=5), dict(sum_norm=2), dict(reserved=1), dict(eps=0.0),
+    dict(eps=-1e-6), dict(eps=float("nan")), dict(scale=float("inf")), dict(n_seg=-1),
+])
+def test_bad_parameters_are_invalid(bad):
+    p = params()
+    for k, v in bad.items():
+        setattr(p, k, v)
+    for call in (bidir, causal, decode, featuremap):
+        assert call(p) == INVALID
+
+
+def test_feature_width_must_match_the_map():
+    assert bidir(params("elu1", r=32)) == INVALID        # r must equal d
+    assert bidir(params("identity", r=128)) == INVALID
+    assert bidir(params("dpfp", r=256, nu=0)) == INVALID  # 1 <= nu <= 2d - 1
+    assert bidir(params("dpfp", r=256, nu=128)) == INVALID
+    assert bidir(params("dpfp", r=128, nu=2)) == INVALID  # r = 2 d nu
+    assert bidir(params("favor", r=256), omega=None) == INVALID
+    assert bidir(params("favor", r=0)) == INVALID
+
+
+def test_pointers_sizes_and_enums():
+    p = params()
+    assert bidir(None) == INVALID
+    assert bidir(p, ptr=None) == INVALID
+    assert bidir(p, ptr=FAKE + 4) == INVALID             # 16-byte alignment
+    assert bidir(p, N=-1) == INVALID
+    assert bidir(p, B=-2) == INVALID
+    assert causal(p, chunk=16) == INVALID
+    assert causal(p, state_in=2) == INVALID
+    assert causal(p, S=None) == INVALID
+    assert decode(p, ptr=None) == INVALID
+    assert featuremap(p, ptr=None) == INVALID
+
+
+def test_outside_gpu_coverage_is_unsupported():
+    assert bidir(params("elu1", r=32), d=32, dv=64) == UNSUPPORTED
+    assert bidir(params(), dv=32) == UNSUPPORTED
+    assert bidir(params("favor", r=512)) == UNSUPPORTED
+    assert bidir(params("favor", r=48)) == UNSUPPORTED
+    assert causal(params("dpfp", r=384, nu=3)) == UNSUPPORTED
+    assert decode(params("favor", r=272)) == UNSUPPORTED
+
+
+def test_small_workspace_is_rejected():
+    p = params()
+    need = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 1, 2, 100, 64, 64)
+    assert need > 0
+    assert causal(p, ws_bytes=need - 4) == WORKSPACE
+    assert causal(p, ws=None, ws_bytes=0) == WORKSPACE
+    need_b = binding.lin_attn_workspace_bytes(binding.OP_BIDIR, p, 1, 2, 100, 64, 64)
+    assert bidir(p, ws_bytes=need_b - 4) == WORKSPACE
+
+
+def test_empty_inputs_are_noops():
+    p = params()
+    assert bidir(p, B=0) == OK
+    assert bidir(p, N=0, S_out=None, z_out=None) == OK
+    assert causal(p, H=0) == OK
+    assert causal(p, N=0, state_in=1) == OK   # the state after no token is the input state
+    assert decode(p, B=0) == OK
+    assert featuremap(p, N=0) == OK
+
+
+def test_workspace_size_formula():
+    """One (S | z) block of r*dv + r floats per head and sequence segment;
+    bidirectional adds one per head for the full summary.  The causal
+    FAVOR+ prefill at B=1, H=8, N=65536 uses 64 segments of 1024 tokens."""
+    p = params()
+    E = 256 * 64 + 256
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 1, 8, 65536, 64, 64) == \
+        8 * 64 * E * 4
+    assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR, p, 1, 8, 65536, 64, 64) == \
+        (8 * 64 + 8) * E * 4
+    p1 = params(n_seg=1)
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p1, 2, 3, 1000, 64, 64) == 6 * E * 4
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 2, 3, 0, 64, 64) == 0
+    assert binding.lin_attn_workspace_bytes(9, p, 2, 3, 10, 64, 64) == 0

@@ -70,7 +70,7 @@ def main():
     torch.cuda.set_device(dev)
 
     def to_dev(a, dtype=torch.bfloat16):
-        return torch.from_numpy(np.asarray(a, np.float32)).to(dev).to(dtype)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(dtype)
 
     result = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",

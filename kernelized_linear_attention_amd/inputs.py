@@ -45,7 +45,7 @@ def orthonormal_rows(m: np.ndarray) -> np.ndarray:
     q, r = np.linalg.qr(m.T)
     signs = np.sign(np.diag(r))
     signs[signs == 0] = 1.0
-    return (q * signs).T
+    return np.ascontiguousarray((q * signs).T)
 
 
 def orf_omega(r: int, d: int, workload: int, rep: int = 0) -> np.ndarray:
@@ -58,7 +58,7 @@ def orf_omega(r: int, d: int, workload: int, rep: int = 0) -> np.ndarray:
         directions = orthonormal_rows(g.standard_normal((d, d)))
         lengths = np.linalg.norm(g.standard_normal((d, d)), axis=1)
         blocks.append(directions * lengths[:, None])
-    return np.concatenate(blocks, axis=0)[:r]
+    return np.ascontiguousarray(np.concatenate(blocks, axis=0)[:r])
 
 
 def iid_omega(r: int, d: int, workload: int, rep: int = 0) -> np.ndarray:

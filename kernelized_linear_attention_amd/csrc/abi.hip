@@ -75,6 +75,28 @@ size_t ws_floats(int32_t op, int64_t BH, SegPlan sp, int r) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? LIN_ATTN_OK : LIN_ATTN_ERR_HIP; }
 
+// The kernel family a validated call runs on, and its segmentation.
+bool use_mfma(const lin_attn_params* p) { return favor_mfma_supported(make_cfg(p), p->dtype); }
+
+SegPlan plan_for(const lin_attn_params* p, int64_t BH, int64_t N) {
+    return plan_segments(BH, N, p->n_seg, use_mfma(p) ? TARGET_BLOCKS_MFMA : TARGET_BLOCKS_VALU);
+}
+
+hipError_t segment_sums(const lin_attn_params* p, const Cfg& c, const void* k, const void* v,
+                        const void* omega, Shape s, SegPlan sp, float* ws, hipStream_t st) {
+    return use_mfma(p) ? launch_favor_sums(c, k, v, omega, s, sp, ws, st)
+                       : launch_segment_sums(c, p->dtype, k, v, omega, s, sp, ws, st);
+}
+
+hipError_t segment_outputs(const lin_attn_params* p, const Cfg& c, int causal, const void* q,
+                           const void* k, const void* v, const void* omega, Shape s, SegPlan sp,
+                           const float* state, int64_t sbh, int64_t sg, void* out,
+                           hipStream_t st) {
+    return use_mfma(p) ? launch_favor_outputs(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st)
+                       : launch_segment_outputs(c, p->dtype, causal, q, k, v, omega, s, sp, state,
+                                                sbh, sg, out, st);
+}
+
 } // namespace
 
 extern "C" {
@@ -102,7 +124,7 @@ size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B,
     if (rc != LIN_ATTN_OK) return 0;
     const int64_t BH = B * H;
     if (BH == 0 || N == 0) return 0;
-    return ws_floats(op, BH, plan_segments(BH, N, p->n_seg), p->r) * sizeof(float);
+    return ws_floats(op, BH, plan_for(p, BH, N), p->r) * sizeof(float);
 }
 
 int lin_attn_featuremap(const lin_attn_params* p, const void* x, int64_t B, int64_t H, int64_t N,
@@ -142,7 +164,7 @@ int lin_attn_bidir(const lin_attn_params* p, const void* q, const void* k, const
         return launch_status(e);
     }
     const int64_t BH = B * H;
-    const SegPlan sp = plan_segments(BH, N, p->n_seg);
+    const SegPlan sp = plan_for(p, BH, N);
     const size_t need = ws_floats(LIN_ATTN_OP_BIDIR, BH, sp, p->r) * sizeof(float);
     if (ws_bytes < need || !ws) return LIN_ATTN_ERR_WORKSPACE;
 
@@ -151,12 +173,11 @@ int lin_attn_bidir(const lin_attn_params* p, const void* q, const void* k, const
     hipStream_t st = (hipStream_t)stream;
     float* inc = (float*)ws;
     float* fin = inc + BH * sp.G * state_elems(p->r);
-    hipError_t e = launch_segment_sums(c, p->dtype, k, v, omega, s, sp, inc, st);
+    hipError_t e = segment_sums(p, c, k, v, omega, s, sp, inc, st);
     if (e == hipSuccess)
         e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc, 0, S_out, z_out, fin, st);
     if (e == hipSuccess)
-        e = launch_segment_outputs(c, p->dtype, 0, q, k, v, omega, s, sp, fin, state_elems(p->r),
-                                   0, out, st);
+        e = segment_outputs(p, c, 0, q, k, v, omega, s, sp, fin, state_elems(p->r), 0, out, st);
     return launch_status(e);
 }
 
@@ -187,7 +208,7 @@ int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void*
         return launch_status(e);
     }
     const int64_t BH = B * H;
-    const SegPlan sp = plan_segments(BH, N, p->n_seg);
+    const SegPlan sp = plan_for(p, BH, N);
     const size_t need = ws_floats(LIN_ATTN_OP_CAUSAL, BH, sp, p->r) * sizeof(float);
     if (ws_bytes < need || !ws) return LIN_ATTN_ERR_WORKSPACE;
 
@@ -196,13 +217,12 @@ int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void*
     hipStream_t st = (hipStream_t)stream;
     float* inc = (float*)ws;
     const int64_t E = state_elems(p->r);
-    hipError_t e = launch_segment_sums(c, p->dtype, k, v, omega, s, sp, inc, st);
+    hipError_t e = segment_sums(p, c, k, v, omega, s, sp, inc, st);
     if (e == hipSuccess)
         e = launch_segment_scan(p->r, s, sp, state_in ? S : nullptr, state_in ? z : nullptr, inc,
                                 1, S, z, nullptr, st);
     if (e == hipSuccess)
-        e = launch_segment_outputs(c, p->dtype, 1, q, k, v, omega, s, sp, inc, sp.G * E, E, out,
-                                   st);
+        e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, sp.G * E, E, out, st);
     return launch_status(e);
 }
 

@@ -1,0 +1,551 @@
+// favor_mfma.hip -- FAVOR+ attention on the matrix cores (bfloat16 inputs,
+// r = 256 features, d = dv = 64, float32 accumulation and state).
+//
+// One workgroup of four waves handles one sequence segment of one head.
+// Wave w owns the features F_w = [64w, 64w + 64): the rows of omega for F_w
+// stay in its registers for the whole segment, and so does its slice
+// S[F_w, :] of the state (float32 MFMA accumulators).  Per chunk of 64
+// tokens (Kernel Zoo sec. 4.2 / 5.4 map; causal recurrence of sec. 1.3 in
+// chunked form, see generic.hip):
+//   P_Q^T = omega_w Q_c^T           -> phi(Q_c)[:, F_w]  (tokens on lanes)
+//   P_K   = K_c omega_w^T           -> phi(K_c)[:, F_w]  (features on lanes)
+//   phi   = exp2(P * s*log2(e) + per-token bias), the bias holding
+//           -s^2 |x|^2 / 2 and -log2(sqrt(r)) (x unscaled, s = scale)
+//   num_w = phi(Q_c) S_{c-1}[F_w]                         (inter-chunk readout)
+//         + ((phi(Q_c) phi(K_c)^T)|_{F_w} o causal mask) V_c (intra-chunk block)
+//   den_w = phi(Q_c) z_{c-1}[F_w] + row sums of the masked block
+//   S[F_w] += phi(K_c)[:, F_w]^T V_c,  z[F_w] += column sums of phi(K_c)
+// and the partial num_w, den_w of the four waves are summed through LDS.
+// Every contraction is a v_mfma_f32_32x32x16_bf16; the MFMA accumulator
+// layout of one product is reused as an operand of the next where the
+// contraction index allows it (a k-slot permutation applied to both
+// operands), so only phi(K) (for the intra block) and V (transposed) pass
+// through LDS.
+//
+// Modes: SUMS     -- per-segment state increments (no outputs);
+//        CAUSAL   -- chunked recurrence from the carried-in state;
+//        READOUT  -- bidirectional readout against the full summary.
+#include "launch.hpp"
+
+namespace linattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NT = 256;       // four waves
+constexpr int NW = 4;
+constexpr int R = 256;        // features: 64 per wave
+constexpr int L = 64;         // chunk length
+constexpr int LD = 68;        // LDS row stride (bf16) of the V^T and phi(K) tiles
+
+enum { MODE_SUMS = 0, MODE_CAUSAL = 1, MODE_READOUT = 2 };
+
+struct FavorArgs {
+    const u16* q;
+    const u16* k;
+    const u16* v;
+    const u16* omega;
+    int64_t N;
+    int64_t G;
+    int64_t seg_len;
+    float a_scale;  // scale * log2(e)
+    float b_norm;   // -scale^2 * log2(e) / 2
+    float b_const;  // log2(1 / sqrt(r))
+    float eps;
+    int norm;
+    float* state;   // SUMS: increments out; CAUSAL: carried-in states; READOUT: summaries
+    int64_t st_bh;
+    int64_t st_g;
+    u16* out;
+};
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int base) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)c[base + e];
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)0.f;
+    return r;
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = 0.f;
+    return r;
+}
+
+// Raw bits of element e of a bfloat16 vector (through 32-bit words: a bit
+// cast of a single __bf16 vector element does not lower reliably).
+__device__ __forceinline__ u16 bf16_bits(const bf16x8& v, int e) {
+    const u32x4 u = __builtin_bit_cast(u32x4, v);
+    const uint32_t word = u[e >> 1];
+    return (e & 1) ? (u16)(word >> 16) : (u16)(word & 0xffffu);
+}
+
+// Two 4-element runs of a bf16 row in LDS, as one MFMA operand.
+__device__ __forceinline__ bf16x8 lds_pair(const u16* row, int c0, int c1) {
+    bf16x4 a = *reinterpret_cast<const bf16x4*>(row + c0);
+    bf16x4 b = *reinterpret_cast<const bf16x4*>(row + c1);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = a[e];
+        r[4 + e] = b[e];
+    }
+    return r;
+}
+
+// frag[tile][ks] = X[32 tile + lo][16 ks + 8 h .. +7] of the chunk at X
+// (rows >= `rows` read as zero).  This is the A operand (tokens as M) and the
+// B operand (tokens as N) of a contraction over d.
+__device__ __forceinline__ void load_x(const u16* __restrict__ X, int rows, int lo, int h,
+                                       bf16x8 (&f)[2][4]) {
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+        const int t = 32 * tile + lo;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            f[tile][ks] = t < rows ? *reinterpret_cast<const bf16x8*>(X + (int64_t)t * D + 16 * ks + 8 * h)
+                                   : zero8();
+    }
+}
+
+// One token tile of load_x.
+__device__ __forceinline__ void load_x_tile(const u16* __restrict__ X, int rows, int lo, int h,
+                                            int tile, bf16x8 (&f)[2][4]) {
+    const int t = 32 * tile + lo;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        f[tile][ks] = t < rows ? *reinterpret_cast<const bf16x8*>(X + (int64_t)t * D + 16 * ks + 8 * h)
+                               : zero8();
+}
+
+// |x_t|^2 for t = 32 tile + lo from its fragments (the two lane halves hold
+// complementary halves of the row); bf16 products are exact in float32.
+__device__ __forceinline__ float sq_norm(const bf16x8 (&f)[2][4], int tile) {
+    float s = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 x = {f[tile][ks][e], f[tile][ks][e + 1]};
+            s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
+        }
+    return s + __shfl_xor(s, 32, 64);
+}
+
+// Raw V rows of the chunk for the transposed LDS copy: thread th holds
+// V[th/4][16 (th%4) .. +15].
+__device__ __forceinline__ void load_v(const u16* __restrict__ V, int rows, int tid,
+                                       bf16x8 (&vr)[2]) {
+    const int t = tid >> 2, n0 = (tid & 3) * 16;
+    vr[0] = t < rows ? *reinterpret_cast<const bf16x8*>(V + (int64_t)t * DV + n0) : zero8();
+    vr[1] = t < rows ? *reinterpret_cast<const bf16x8*>(V + (int64_t)t * DV + n0 + 8) : zero8();
+}
+
+__device__ __forceinline__ void store_vt(u16* vt, int tid, const bf16x8 (&vr)[2]) {
+    const int t = tid >> 2, n0 = (tid & 3) * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        vt[(n0 + e) * LD + t] = bf16_bits(vr[e >> 3], e & 7);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
+    __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LD];       // V^T, double buffered
+    __shared__ __attribute__((aligned(16))) u16 pk_s[NW][L * LD];       // phi(K)[:, F_w], bf16
+    __shared__ __attribute__((aligned(16))) float red_s[4][NW][4][64][4]; // partial num tiles
+    __shared__ __attribute__((aligned(16))) float z_s[R];
+    __shared__ __attribute__((aligned(16))) float den_s[NW][L];
+    __shared__ __attribute__((aligned(16))) float kb_s[NW][L];          // key biases by token
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lo = lane & 31, h = lane >> 5;
+    const int f0 = 64 * w;
+    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
+    const int64_t t0 = g * a.seg_len;
+    const int64_t t1 = min<int64_t>(a.N, t0 + a.seg_len);
+    constexpr bool HAS_K = MODE != MODE_READOUT;
+    constexpr bool HAS_Q = MODE != MODE_SUMS;
+
+    // omega rows of F_w: om[mt][ks] = omega[f0 + 32 mt + lo][16 ks + 8 h ..].
+    // A operand of omega X^T and B operand of X omega^T at once.
+    bf16x8 om[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            om[mt][ks] = *reinterpret_cast<const bf16x8*>(a.omega + (int64_t)(f0 + 32 * mt + lo) * D +
+                                                         16 * ks + 8 * h);
+
+    // State slice S[F_w, :] in accumulator layout: element i of S[mt][nt]
+    // is S[f0 + 32 mt + 8 (i/4) + 4 h + i%4][32 nt + lo].
+    f32x16 S[2][2];
+    float zreg[2] = {0.f, 0.f}; // z[f0 + 32 nt + lo]
+    const float* st = a.state + bh * a.st_bh + g * a.st_g;
+    if (MODE == MODE_SUMS) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) S[mt][nt] = zero16();
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int f = f0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+                    S[mt][nt][i] = st[(int64_t)f * DV + 32 * nt + lo];
+                }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) zreg[nt] = st[(int64_t)R * DV + f0 + 32 * nt + lo];
+        if (h == 0) {
+            z_s[f0 + lo] = zreg[0];
+            z_s[f0 + 32 + lo] = zreg[1];
+        }
+    }
+
+    const u16* qb = a.q + bh * a.N * D;
+    const u16* kb = a.k + bh * a.N * D;
+    const u16* vb = a.v + bh * a.N * DV;
+
+    bf16x8 qf[2][4], kf[2][4], vr[2];
+    int rows = (int)min<int64_t>(L, t1 - t0);
+    if (HAS_Q) load_x(qb + t0 * D, rows, lo, h, qf);
+    if (HAS_K) {
+        load_x(kb + t0 * D, rows, lo, h, kf);
+        load_v(vb + t0 * DV, rows, tid, vr);
+        store_vt(vt_s[0], tid, vr);
+    }
+
+    int buf = 0;
+    for (int64_t c0 = t0; c0 < t1; c0 += L, buf ^= 1) {
+        rows = (int)min<int64_t>(L, t1 - c0);
+        const int64_t cn = c0 + L;
+        const int rows_next = cn < t1 ? (int)min<int64_t>(L, t1 - cn) : 0;
+        __syncthreads(); // (A) vt_s[buf] complete; last chunk's red_s reads done
+
+        // ---- phi(K) = exp(K omega_w^T ...), features on lanes -------------------
+        bf16x8 fk[2][2][2]; // [tt][nt][kk]: A operand of the update
+        float zpart[2] = {0.f, 0.f};
+        if (HAS_K) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const float bk = fmaf(a.b_norm, sq_norm(kf, tt), a.b_const);
+                if (h == 0) kb_s[w][32 * tt + lo] = bk;
+            }
+            f32x16 PK[2][2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x16 c = zero16();
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) c = mfma(kf[tt][ks], om[nt][ks], c);
+                    PK[tt][nt] = c; // token 32 tt + 8(i/4) + 4h + i%4, feature f0 + 32 nt + lo
+                }
+            // the next chunk's keys and values load while this one is computed
+            if (rows_next > 0) {
+                load_x(kb + cn * D, rows_next, lo, h, kf);
+                load_v(vb + cn * DV, rows_next, tid, vr);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                f32x4 kbias[4]; // biases of the tokens 32 tt + 8 j + 4 h + (0..3)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    kbias[j] = *reinterpret_cast<const f32x4*>(&kb_s[w][32 * tt + 8 * j + 4 * h]);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x16& c = PK[tt][nt];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
+                    if (rows < L) { // keys past the end of the segment contribute nothing
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int t = 32 * tt + 8 * (i >> 2) + 4 * h + (i & 3);
+                            c[i] = t < rows ? c[i] : 0.f;
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) zpart[nt] += c[i];
+                    fk[tt][nt][0] = pack8(c, 0);
+                    fk[tt][nt][1] = pack8(c, 8);
+                }
+            }
+            if (MODE == MODE_CAUSAL) {
+                // phi(K) rows to LDS for the intra-chunk block
+                u16* pk = pk_s[w];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int t = 32 * tt + 8 * (i >> 2) + 4 * h + (i & 3);
+                            pk[t * LD + 32 * nt + lo] = bf16_bits(fk[tt][nt][i >> 3], i & 7);
+                        }
+            }
+        }
+
+        // ---- V fragments: vf[tt][kk][nt], k-slot e <-> token
+        //      32 tt + 16 kk + 8 (e/4) + 4 h + e%4, lane <-> column 32 nt + lo
+        bf16x8 vf[2][2][2];
+        if (HAS_K) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const u16* row = vt_s[buf] + (32 * nt + lo) * LD;
+                        const int tb = 32 * tt + 16 * kk + 4 * h;
+                        vf[tt][kk][nt] = lds_pair(row, tb, tb + 8);
+                    }
+        }
+
+        // ---- queries, in two halves of 32 tokens: phi(Q), readout against
+        //      S_{c-1}, intra-chunk block; partial sums of other waves' tiles to LDS
+        f32x16 own = zero16(); // this wave's output tile (w / 2, w % 2)
+        if (HAS_Q) {
+            bf16x8 sb[2][2][2]; // [mt][nt][kk]: S_{c-1} as the B operand of the readout
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    sb[mt][nt][0] = pack8(S[mt][nt], 0);
+                    sb[mt][nt][1] = pack8(S[mt][nt], 8);
+                }
+#pragma unroll
+            for (int tq = 0; tq < 2; ++tq) {
+                const float bq = fmaf(a.b_norm, sq_norm(qf, tq), a.b_const);
+                bf16x8 fq[2][2]; // [mt][kk]
+                float den = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    f32x16 c = zero16();
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) c = mfma(om[mt][ks], qf[tq][ks], c);
+                    // c[i]: feature f0 + 32 mt + 8(i/4) + 4h + i%4, token 32 tq + lo
+                    f32x4 zq[4]; // z of the features f0 + 32 mt + 8 j + 4 h + (0..3)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        zq[j] = *reinterpret_cast<const f32x4*>(&z_s[f0 + 32 * mt + 8 * j + 4 * h]);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float y = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
+                        c[i] = y;
+                        den = fmaf(y, zq[i >> 2][i & 3], den);
+                    }
+                    fq[mt][0] = pack8(c, 0);
+                    fq[mt][1] = pack8(c, 8);
+                }
+                // this half of the queries is consumed: load the next chunk's
+                if (rows_next > 0) load_x_tile(qb + cn * D, rows_next, lo, h, tq, qf);
+
+                f32x16 num[2]; // [nt]: row 32 tq + 8(i/4) + 4h + i%4, column 32 nt + lo
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x16 c = zero16();
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) c = mfma(fq[mt][kk], sb[mt][nt][kk], c);
+                    num[nt] = c;
+                }
+                if (MODE == MODE_CAUSAL) {
+                    // masked block, transposed: c[i] = A[32 tq + lo][32 jt + 8(i/4) + 4h + i%4]
+                    const u16* pk = pk_s[w];
+#pragma unroll
+                    for (int jt = 0; jt <= tq; ++jt) {
+                        f32x16 c = zero16();
+#pragma unroll
+                        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                            for (int kk = 0; kk < 2; ++kk) {
+                                const int fb = 32 * mt + 16 * kk + 4 * h;
+                                c = mfma(lds_pair(pk + (32 * jt + lo) * LD, fb, fb + 8), fq[mt][kk], c);
+                            }
+                        if (jt == tq) {
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+                                const int j = 8 * (i >> 2) + 4 * h + (i & 3);
+                                c[i] = j <= lo ? c[i] : 0.f;
+                            }
+                        }
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) den += c[i];
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) {
+                            const bf16x8 at = pack8(c, 8 * kk);
+#pragma unroll
+                            for (int nt = 0; nt < 2; ++nt) num[nt] = mfma(at, vf[jt][kk][nt], num[nt]);
+                        }
+                    }
+                }
+                den += __shfl_xor(den, 32, 64);
+                if (h == 0) den_s[w][32 * tq + lo] = den;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int tile = 2 * tq + nt;
+                    if (tile == w) {
+                        own = num[nt];
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const f32x4 x = {num[nt][4 * j], num[nt][4 * j + 1], num[nt][4 * j + 2],
+                                             num[nt][4 * j + 3]};
+                            *reinterpret_cast<f32x4*>(&red_s[tile][w][j][lane][0]) = x;
+                        }
+                    }
+                }
+            }
+        }
+
+        // ---- state update: S[F_w] += phi(K)^T V, z[F_w] += column sums ---------------
+        if (HAS_K) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk)
+                            S[mt][nt] = mfma(fk[tt][mt][kk], vf[tt][kk][nt], S[mt][nt]);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                zreg[nt] += zpart[nt] + __shfl_xor(zpart[nt], 32, 64);
+                if (MODE == MODE_CAUSAL && h == 0) z_s[f0 + 32 * nt + lo] = zreg[nt];
+            }
+        }
+
+        if (HAS_Q) {
+            __syncthreads(); // (B) partial tiles and denominators of all waves in LDS
+            // wave w finishes output tile (tq, nt) = (w / 2, w % 2)
+            const int tq = w >> 1, nt = w & 1;
+            f32x16 c = own;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) {
+                if (w2 == w) continue;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(&red_s[w][w2][j][lane][0]);
+                    c[4 * j] += x[0];
+                    c[4 * j + 1] += x[1];
+                    c[4 * j + 2] += x[2];
+                    c[4 * j + 3] += x[3];
+                }
+            }
+            u16* ob = a.out + (bh * a.N + c0) * DV + 32 * nt + lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tb = 32 * tq + 8 * j + 4 * h;
+                f32x4 dsum = *reinterpret_cast<const f32x4*>(&den_s[0][tb]);
+#pragma unroll
+                for (int w2 = 1; w2 < NW; ++w2) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(&den_s[w2][tb]);
+                    dsum[0] += x[0];
+                    dsum[1] += x[1];
+                    dsum[2] += x[2];
+                    dsum[3] += x[3];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = tb + e;
+                    float y = c[4 * j + e];
+                    if (a.norm == NORM_ATTN) y = y / fmaxf(dsum[e], a.eps);
+                    if (t < rows) ob[(int64_t)t * DV] = __builtin_bit_cast(u16, (__bf16)y);
+                }
+            }
+        }
+
+        // next chunk's V^T (its loads were issued above)
+        if (HAS_K && rows_next > 0) store_vt(vt_s[buf ^ 1], tid, vr);
+    }
+
+    if (MODE == MODE_SUMS) {
+        float* dst = a.state + bh * a.st_bh + g * a.st_g;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int f = f0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+                    dst[(int64_t)f * DV + 32 * nt + lo] = S[mt][nt][i];
+                }
+        if (h == 0) {
+            dst[(int64_t)R * DV + f0 + lo] = zreg[0];
+            dst[(int64_t)R * DV + f0 + 32 + lo] = zreg[1];
+        }
+    }
+}
+
+FavorArgs make_args(const Cfg& c, const void* q, const void* k, const void* v, const void* omega,
+                    Shape s, SegPlan sp, float* state, int64_t sbh, int64_t sg, void* out) {
+    FavorArgs a;
+    a.q = (const u16*)q;
+    a.k = (const u16*)k;
+    a.v = (const u16*)v;
+    a.omega = (const u16*)omega;
+    a.N = s.N;
+    a.G = sp.G;
+    a.seg_len = sp.seg_len;
+    a.a_scale = c.scale * LOG2E;
+    a.b_norm = -0.5f * c.scale * c.scale * LOG2E;
+    a.b_const = c.favor_log2_bias;
+    a.eps = c.eps;
+    a.norm = c.norm;
+    a.state = state;
+    a.st_bh = sbh;
+    a.st_g = sg;
+    a.out = (u16*)out;
+    return a;
+}
+
+} // namespace
+
+bool favor_mfma_supported(const Cfg& c, int dtype) {
+    return c.phi == PHI_FAVOR && dtype == 1 && c.r == R && c.sum_norm == 0;
+}
+
+hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const void* omega,
+                             Shape s, SegPlan sp, float* ws, hipStream_t st) {
+    const FavorArgs a = make_args(c, nullptr, k, v, omega, s, sp, ws, sp.G * state_elems(R),
+                                  state_elems(R), nullptr);
+    hipLaunchKernelGGL(k_favor_mfma<MODE_SUMS>, dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_favor_outputs(const Cfg& c, int causal, const void* q, const void* k,
+                                const void* v, const void* omega, Shape s, SegPlan sp,
+                                const float* state, int64_t sbh, int64_t sg, void* out,
+                                hipStream_t st) {
+    const FavorArgs a = make_args(c, q, k, v, omega, s, sp, const_cast<float*>(state), sbh, sg, out);
+    if (causal)
+        hipLaunchKernelGGL(k_favor_mfma<MODE_CAUSAL>, dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_favor_mfma<MODE_READOUT>, dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0, st, a);
+    return hipGetLastError();
+}
+
+} // namespace linattn

@@ -15,18 +15,19 @@ namespace linattn {
 // tokens per head (the last may be shorter); every segment boundary is a
 // multiple of SEG_UNIT tokens.
 constexpr int64_t SEG_UNIT = 64;
-constexpr int64_t TARGET_BLOCKS = 512; // aim for about two workgroups per CU
+constexpr int64_t TARGET_BLOCKS_VALU = 512; // vector kernels: about two workgroups per CU
+constexpr int64_t TARGET_BLOCKS_MFMA = 256; // matrix-core kernels: one workgroup per CU
 
 struct SegPlan {
     int64_t G;
     int64_t seg_len;
 };
 
-inline SegPlan plan_segments(int64_t BH, int64_t N, int32_t n_seg_req) {
+inline SegPlan plan_segments(int64_t BH, int64_t N, int32_t n_seg_req, int64_t target_blocks) {
     SegPlan p{1, N};
     if (N <= 0 || BH <= 0) return p;
     const int64_t units = (N + SEG_UNIT - 1) / SEG_UNIT;
-    int64_t G = n_seg_req > 0 ? n_seg_req : (TARGET_BLOCKS + BH - 1) / BH;
+    int64_t G = n_seg_req > 0 ? n_seg_req : (target_blocks + BH - 1) / BH;
     if (G < 1) G = 1;
     if (G > units) G = units;
     const int64_t per = (units + G - 1) / G;
@@ -69,6 +70,16 @@ hipError_t launch_segment_outputs(const Cfg& c, int dtype, int causal, const voi
 
 // p[0, n) = 0 with a plain kernel (capturable into a graph).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+// Matrix-core path for FAVOR+ with bfloat16 inputs and r = 256 (favor_mfma.hip);
+// same workspace layout and segment scan as the vector path.
+bool favor_mfma_supported(const Cfg& c, int dtype);
+hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const void* omega,
+                             Shape s, SegPlan sp, float* ws, hipStream_t st);
+hipError_t launch_favor_outputs(const Cfg& c, int causal, const void* q, const void* k,
+                                const void* v, const void* omega, Shape s, SegPlan sp,
+                                const float* state, int64_t sbh, int64_t sg, void* out,
+                                hipStream_t st);
 
 hipError_t launch_decode(const Cfg& c, int dtype, const void* q, const void* k, const void* v,
                          const void* omega, int64_t BH, float* S, float* z, void* out,

@@ -1,11 +1,12 @@
 // favor_mfma.hip -- FAVOR+ attention on the matrix cores (bfloat16 inputs,
 // r = 256 features, d = dv = 64, float32 accumulation and state).
 //
-// One workgroup of four waves handles one sequence segment of one head.
+// One workgroup of four waves handles one sequence segment of one head, in
+// chunks of 32 tokens (one MFMA tile: the intra-chunk block is a single
+// masked 32 x 32 tile).
 // Wave w owns the features F_w = [64w, 64w + 64): the rows of omega for F_w
 // stay in its registers for the whole segment, and so does its slice
-// S[F_w, :] of the state (float32 MFMA accumulators).  Per chunk of 64
-// tokens (Kernel Zoo sec. 4.2 / 5.4 map; causal recurrence of sec. 1.3 in
+// S[F_w, :] of the state (float32 MFMA accumulators).  Per chunk (Kernel Zoo sec. 4.2 / 5.4 map; causal recurrence of sec. 1.3 in
 // chunked form, see generic.hip):
 //   P_Q^T = omega_w Q_c^T           -> phi(Q_c)[:, F_w]  (tokens on lanes)
 //   P_K   = K_c omega_w^T           -> phi(K_c)[:, F_w]  (features on lanes)
@@ -41,8 +42,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int NT = 256;       // four waves
 constexpr int NW = 4;
 constexpr int R = 256;        // features: 64 per wave
-constexpr int L = 64;         // chunk length
-constexpr int LD = 68;        // LDS row stride (bf16) of the V^T and phi(K) tiles
+constexpr int L = 32;         // chunk length: one 32-token MFMA tile
+constexpr int LDK = 68;       // LDS row stride (bf16) of a wave's phi(K) tile [32 t][64 f]
+constexpr int LDV = 36;       // LDS row stride (bf16) of the V^T tile [64 n][32 t]
 
 enum { MODE_SUMS = 0, MODE_CAUSAL = 1, MODE_READOUT = 2 };
 
@@ -64,6 +66,13 @@ struct FavorArgs {
     int64_t st_g;
     u16* out;
 };
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
+// every outstanding global load, which would stall on the next chunk's
+// prefetch; here all communication between waves goes through LDS.
+__device__ __forceinline__ void sync_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -111,69 +120,56 @@ __device__ __forceinline__ bf16x8 lds_pair(const u16* row, int c0, int c1) {
     return r;
 }
 
-// frag[tile][ks] = X[32 tile + lo][16 ks + 8 h .. +7] of the chunk at X
-// (rows >= `rows` read as zero).  This is the A operand (tokens as M) and the
-// B operand (tokens as N) of a contraction over d.
+// f[ks] = X[lo][16 ks + 8 h .. +7] of the chunk at X: the A operand
+// (tokens as M) and the B operand (tokens as N) of a contraction over d.
+// Rows past `rows` repeat row rows-1: every load stays in bounds without
+// per-lane branches (which would make the compiler wait for the loads right
+// away); the kernel zeroes phi(K) of those rows and never stores their
+// outputs.
 __device__ __forceinline__ void load_x(const u16* __restrict__ X, int rows, int lo, int h,
-                                       bf16x8 (&f)[2][4]) {
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-        const int t = 32 * tile + lo;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            f[tile][ks] = t < rows ? *reinterpret_cast<const bf16x8*>(X + (int64_t)t * D + 16 * ks + 8 * h)
-                                   : zero8();
-    }
-}
-
-// One token tile of load_x.
-__device__ __forceinline__ void load_x_tile(const u16* __restrict__ X, int rows, int lo, int h,
-                                            int tile, bf16x8 (&f)[2][4]) {
-    const int t = 32 * tile + lo;
+                                       bf16x8 (&f)[4]) {
+    const int t = min(lo, rows - 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-        f[tile][ks] = t < rows ? *reinterpret_cast<const bf16x8*>(X + (int64_t)t * D + 16 * ks + 8 * h)
-                               : zero8();
+        f[ks] = *reinterpret_cast<const bf16x8*>(X + (int64_t)t * D + 16 * ks + 8 * h);
 }
 
-// |x_t|^2 for t = 32 tile + lo from its fragments (the two lane halves hold
+// |x_t|^2 for t = lo from its fragments (the two lane halves hold
 // complementary halves of the row); bf16 products are exact in float32.
-__device__ __forceinline__ float sq_norm(const bf16x8 (&f)[2][4], int tile) {
+__device__ __forceinline__ float sq_norm(const bf16x8 (&f)[4]) {
     float s = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            const bf16x2 x = {f[tile][ks][e], f[tile][ks][e + 1]};
+            const bf16x2 x = {f[ks][e], f[ks][e + 1]};
             s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
         }
     return s + __shfl_xor(s, 32, 64);
 }
 
 // Raw V rows of the chunk for the transposed LDS copy: thread th holds
-// V[th/4][16 (th%4) .. +15].
-__device__ __forceinline__ void load_v(const u16* __restrict__ V, int rows, int tid,
-                                       bf16x8 (&vr)[2]) {
-    const int t = tid >> 2, n0 = (tid & 3) * 16;
-    vr[0] = t < rows ? *reinterpret_cast<const bf16x8*>(V + (int64_t)t * DV + n0) : zero8();
-    vr[1] = t < rows ? *reinterpret_cast<const bf16x8*>(V + (int64_t)t * DV + n0 + 8) : zero8();
+// V[th/8][8 (th%8) .. +7] (rows past `rows` repeat row rows-1; they only
+// ever meet zero weights).
+__device__ __forceinline__ bf16x8 load_v(const u16* __restrict__ V, int rows, int tid) {
+    const int t = min(tid >> 3, rows - 1), n0 = (tid & 7) * 8;
+    return *reinterpret_cast<const bf16x8*>(V + (int64_t)t * DV + n0);
 }
 
-__device__ __forceinline__ void store_vt(u16* vt, int tid, const bf16x8 (&vr)[2]) {
-    const int t = tid >> 2, n0 = (tid & 3) * 16;
+__device__ __forceinline__ void store_vt(u16* vt, int tid, const bf16x8& vr) {
+    const int t = tid >> 3, n0 = (tid & 7) * 8;
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-        vt[(n0 + e) * LD + t] = bf16_bits(vr[e >> 3], e & 7);
+    for (int e = 0; e < 8; ++e) vt[(n0 + e) * LDV + t] = bf16_bits(vr, e);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
-    __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LD];       // V^T, double buffered
-    __shared__ __attribute__((aligned(16))) u16 pk_s[NW][L * LD];       // phi(K)[:, F_w], bf16
-    __shared__ __attribute__((aligned(16))) float red_s[4][NW][4][64][4]; // partial num tiles
+    __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LDV];        // V^T, double buffered
+    __shared__ __attribute__((aligned(16))) u16 pk_s[NW][L * LDK];        // phi(K)[:, F_w], bf16
+    __shared__ __attribute__((aligned(16))) float red_s[2][2][NW][2][64][4]; // partial num blocks
     __shared__ __attribute__((aligned(16))) float z_s[R];
     __shared__ __attribute__((aligned(16))) float den_s[NW][L];
-    __shared__ __attribute__((aligned(16))) float kb_s[NW][L];          // key biases by token
+    __shared__ __attribute__((aligned(16))) float kb_s[NW][L];            // key biases by token
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lo = lane & 31, h = lane >> 5;
@@ -183,6 +179,8 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
     const int64_t t1 = min<int64_t>(a.N, t0 + a.seg_len);
     constexpr bool HAS_K = MODE != MODE_READOUT;
     constexpr bool HAS_Q = MODE != MODE_SUMS;
+    // this wave finishes rows [16 oq, 16 oq + 16) of output tile on (columns 32 on + ..)
+    const int on = w & 1, oq = w >> 1;
 
     // omega rows of F_w: om[mt][ks] = omega[f0 + 32 mt + lo][16 ks + 8 h ..].
     // A operand of omega X^T and B operand of X omega^T at once.
@@ -226,12 +224,12 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
     const u16* kb = a.k + bh * a.N * D;
     const u16* vb = a.v + bh * a.N * DV;
 
-    bf16x8 qf[2][4], kf[2][4], vr[2];
+    bf16x8 qf[4], kf[4], vr;
     int rows = (int)min<int64_t>(L, t1 - t0);
     if (HAS_Q) load_x(qb + t0 * D, rows, lo, h, qf);
     if (HAS_K) {
         load_x(kb + t0 * D, rows, lo, h, kf);
-        load_v(vb + t0 * DV, rows, tid, vr);
+        vr = load_v(vb + t0 * DV, rows, tid);
         store_vt(vt_s[0], tid, vr);
     }
 
@@ -240,91 +238,77 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
         rows = (int)min<int64_t>(L, t1 - c0);
         const int64_t cn = c0 + L;
         const int rows_next = cn < t1 ? (int)min<int64_t>(L, t1 - cn) : 0;
-        __syncthreads(); // (A) vt_s[buf] complete; last chunk's red_s reads done
+        sync_lds(); // (A) vt_s[buf] complete; last chunk's red_s / den_s reads done
 
         // ---- phi(K) = exp(K omega_w^T ...), features on lanes -------------------
-        bf16x8 fk[2][2][2]; // [tt][nt][kk]: A operand of the update
+        bf16x8 fk[2][2]; // [nt][kk]: A operand of the update
         float zpart[2] = {0.f, 0.f};
         if (HAS_K) {
+            const float bk = fmaf(a.b_norm, sq_norm(kf), a.b_const);
+            kb_s[w][lo] = bk; // both lane halves write the same value
+            f32x16 PK[2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const float bk = fmaf(a.b_norm, sq_norm(kf, tt), a.b_const);
-                if (h == 0) kb_s[w][32 * tt + lo] = bk;
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x16 c = zero16();
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) c = mfma(kf[ks], om[nt][ks], c);
+                PK[nt] = c; // token 8(i/4) + 4h + i%4, feature f0 + 32 nt + lo
             }
-            f32x16 PK[2][2];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x16 c = zero16();
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) c = mfma(kf[tt][ks], om[nt][ks], c);
-                    PK[tt][nt] = c; // token 32 tt + 8(i/4) + 4h + i%4, feature f0 + 32 nt + lo
-                }
             // the next chunk's keys and values load while this one is computed
             if (rows_next > 0) {
                 load_x(kb + cn * D, rows_next, lo, h, kf);
-                load_v(vb + cn * DV, rows_next, tid, vr);
+                vr = load_v(vb + cn * DV, rows_next, tid);
             }
+            f32x4 kbias[4]; // biases of the tokens 8 j + 4 h + (0..3)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f32x4 kbias[4]; // biases of the tokens 32 tt + 8 j + 4 h + (0..3)
+            for (int j = 0; j < 4; ++j)
+                kbias[j] = *reinterpret_cast<const f32x4*>(&kb_s[w][8 * j + 4 * h]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    kbias[j] = *reinterpret_cast<const f32x4*>(&kb_s[w][32 * tt + 8 * j + 4 * h]);
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x16& c = PK[nt];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x16& c = PK[tt][nt];
+                for (int i = 0; i < 16; ++i)
+                    c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
+                if (rows < L) { // keys past the end of the segment contribute nothing
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
-                    if (rows < L) { // keys past the end of the segment contribute nothing
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int t = 32 * tt + 8 * (i >> 2) + 4 * h + (i & 3);
-                            c[i] = t < rows ? c[i] : 0.f;
-                        }
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = 8 * (i >> 2) + 4 * h + (i & 3);
+                        c[i] = t < rows ? c[i] : 0.f;
                     }
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) zpart[nt] += c[i];
-                    fk[tt][nt][0] = pack8(c, 0);
-                    fk[tt][nt][1] = pack8(c, 8);
                 }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) zpart[nt] += c[i];
+                fk[nt][0] = pack8(c, 0);
+                fk[nt][1] = pack8(c, 8);
             }
             if (MODE == MODE_CAUSAL) {
                 // phi(K) rows to LDS for the intra-chunk block
                 u16* pk = pk_s[w];
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
+                for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int t = 32 * tt + 8 * (i >> 2) + 4 * h + (i & 3);
-                            pk[t * LD + 32 * nt + lo] = bf16_bits(fk[tt][nt][i >> 3], i & 7);
-                        }
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = 8 * (i >> 2) + 4 * h + (i & 3);
+                        pk[t * LDK + 32 * nt + lo] = bf16_bits(fk[nt][i >> 3], i & 7);
+                    }
             }
         }
 
-        // ---- V fragments: vf[tt][kk][nt], k-slot e <-> token
-        //      32 tt + 16 kk + 8 (e/4) + 4 h + e%4, lane <-> column 32 nt + lo
-        bf16x8 vf[2][2][2];
+        // ---- V fragments vf[kk][nt]: k-slot e <-> token 16 kk + 8 (e/4) + 4 h + e%4,
+        //      lane <-> column 32 nt + lo
+        bf16x8 vf[2][2];
         if (HAS_K) {
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const u16* row = vt_s[buf] + (32 * nt + lo) * LD;
-                        const int tb = 32 * tt + 16 * kk + 4 * h;
-                        vf[tt][kk][nt] = lds_pair(row, tb, tb + 8);
-                    }
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int tb = 16 * kk + 4 * h;
+                    vf[kk][nt] = lds_pair(vt_s[buf] + (32 * nt + lo) * LDV, tb, tb + 8);
+                }
         }
 
-        // ---- queries, in two halves of 32 tokens: phi(Q), readout against
-        //      S_{c-1}, intra-chunk block; partial sums of other waves' tiles to LDS
-        f32x16 own = zero16(); // this wave's output tile (w / 2, w % 2)
+        // ---- queries: phi(Q), readout against S_{c-1}, intra-chunk block ---------
+        f32x16 own = zero16(); // rows 16 oq .. of output tile on, in regs 8 oq .. 8 oq + 7
         if (HAS_Q) {
             bf16x8 sb[2][2][2]; // [mt][nt][kk]: S_{c-1} as the B operand of the readout
 #pragma unroll
@@ -334,90 +318,87 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
                     sb[mt][nt][0] = pack8(S[mt][nt], 0);
                     sb[mt][nt][1] = pack8(S[mt][nt], 8);
                 }
+            const float bq = fmaf(a.b_norm, sq_norm(qf), a.b_const);
+            f32x16 PQ[2];
 #pragma unroll
-            for (int tq = 0; tq < 2; ++tq) {
-                const float bq = fmaf(a.b_norm, sq_norm(qf, tq), a.b_const);
-                bf16x8 fq[2][2]; // [mt][kk]
-                float den = 0.f;
+            for (int mt = 0; mt < 2; ++mt) {
+                f32x16 c = zero16();
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    f32x16 c = zero16();
+                for (int ks = 0; ks < 4; ++ks) c = mfma(om[mt][ks], qf[ks], c);
+                PQ[mt] = c; // feature f0 + 32 mt + 8(i/4) + 4h + i%4, token lo
+            }
+            if (rows_next > 0) load_x(qb + cn * D, rows_next, lo, h, qf);
+            bf16x8 fq[2][2]; // [mt][kk]
+            float den = 0.f;
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) c = mfma(om[mt][ks], qf[tq][ks], c);
-                    // c[i]: feature f0 + 32 mt + 8(i/4) + 4h + i%4, token 32 tq + lo
-                    f32x4 zq[4]; // z of the features f0 + 32 mt + 8 j + 4 h + (0..3)
+            for (int mt = 0; mt < 2; ++mt) {
+                f32x4 zq[4]; // z_{c-1} of the features f0 + 32 mt + 8 j + 4 h + (0..3)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        zq[j] = *reinterpret_cast<const f32x4*>(&z_s[f0 + 32 * mt + 8 * j + 4 * h]);
+                for (int j = 0; j < 4; ++j)
+                    zq[j] = *reinterpret_cast<const f32x4*>(&z_s[f0 + 32 * mt + 8 * j + 4 * h]);
+                f32x16& c = PQ[mt];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float y = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
-                        c[i] = y;
-                        den = fmaf(y, zq[i >> 2][i & 3], den);
-                    }
-                    fq[mt][0] = pack8(c, 0);
-                    fq[mt][1] = pack8(c, 8);
+                for (int i = 0; i < 16; ++i) {
+                    const float y = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
+                    c[i] = y;
+                    den = fmaf(y, zq[i >> 2][i & 3], den);
                 }
-                // this half of the queries is consumed: load the next chunk's
-                if (rows_next > 0) load_x_tile(qb + cn * D, rows_next, lo, h, tq, qf);
-
-                f32x16 num[2]; // [nt]: row 32 tq + 8(i/4) + 4h + i%4, column 32 nt + lo
+                fq[mt][0] = pack8(c, 0);
+                fq[mt][1] = pack8(c, 8);
+            }
+            f32x16 num[2]; // [nt]: row 8(i/4) + 4h + i%4, column 32 nt + lo
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x16 c = zero16();
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x16 c = zero16();
 #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) c = mfma(fq[mt][kk], sb[mt][nt][kk], c);
-                    num[nt] = c;
-                }
-                if (MODE == MODE_CAUSAL) {
-                    // masked block, transposed: c[i] = A[32 tq + lo][32 jt + 8(i/4) + 4h + i%4]
-                    const u16* pk = pk_s[w];
+                    for (int kk = 0; kk < 2; ++kk) c = mfma(fq[mt][kk], sb[mt][nt][kk], c);
+                num[nt] = c;
+            }
+            if (MODE == MODE_CAUSAL) {
+                // masked block, transposed: c[i] = A[lo][j], j = 8(i/4) + 4h + i%4, over F_w
+                const u16* pk = pk_s[w] + lo * LDK;
+                f32x16 c = zero16();
 #pragma unroll
-                    for (int jt = 0; jt <= tq; ++jt) {
-                        f32x16 c = zero16();
+                for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                            for (int kk = 0; kk < 2; ++kk) {
-                                const int fb = 32 * mt + 16 * kk + 4 * h;
-                                c = mfma(lds_pair(pk + (32 * jt + lo) * LD, fb, fb + 8), fq[mt][kk], c);
-                            }
-                        if (jt == tq) {
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) {
-                                const int j = 8 * (i >> 2) + 4 * h + (i & 3);
-                                c[i] = j <= lo ? c[i] : 0.f;
-                            }
-                        }
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) den += c[i];
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) {
-                            const bf16x8 at = pack8(c, 8 * kk);
-#pragma unroll
-                            for (int nt = 0; nt < 2; ++nt) num[nt] = mfma(at, vf[jt][kk][nt], num[nt]);
-                        }
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const int fb = 32 * mt + 16 * kk + 4 * h;
+                        c = mfma(lds_pair(pk, fb, fb + 8), fq[mt][kk], c);
                     }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int j = 8 * (i >> 2) + 4 * h + (i & 3);
+                    c[i] = j <= lo ? c[i] : 0.f;
+                    den += c[i];
                 }
-                den += __shfl_xor(den, 32, 64);
-                if (h == 0) den_s[w][32 * tq + lo] = den;
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const int tile = 2 * tq + nt;
-                    if (tile == w) {
-                        own = num[nt];
-                    } else {
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 at = pack8(c, 8 * kk);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const f32x4 x = {num[nt][4 * j], num[nt][4 * j + 1], num[nt][4 * j + 2],
-                                             num[nt][4 * j + 3]};
-                            *reinterpret_cast<f32x4*>(&red_s[tile][w][j][lane][0]) = x;
-                        }
-                    }
+                    for (int nt = 0; nt < 2; ++nt) num[nt] = mfma(at, vf[kk][nt], num[nt]);
                 }
             }
+            den += __shfl_xor(den, 32, 64);
+            den_s[w][lo] = den; // both lane halves hold the full sum
+            // blocks (nt, q) of the other waves go to LDS; this wave keeps (on, oq)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    if (nt == on && q == oq) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) own[i] = num[nt][8 * q + i];
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const f32x4 x = {num[nt][8 * q + 4 * j], num[nt][8 * q + 4 * j + 1],
+                                             num[nt][8 * q + 4 * j + 2], num[nt][8 * q + 4 * j + 3]};
+                            *reinterpret_cast<f32x4*>(&red_s[nt][q][w][j][lane][0]) = x;
+                        }
+                    }
+                }
         }
 
         // ---- state update: S[F_w] += phi(K)^T V, z[F_w] += column sums ---------------
@@ -427,38 +408,32 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk)
-                            S[mt][nt] = mfma(fk[tt][mt][kk], vf[tt][kk][nt], S[mt][nt]);
+                    for (int kk = 0; kk < 2; ++kk) S[mt][nt] = mfma(fk[mt][kk], vf[kk][nt], S[mt][nt]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 zreg[nt] += zpart[nt] + __shfl_xor(zpart[nt], 32, 64);
-                if (MODE == MODE_CAUSAL && h == 0) z_s[f0 + 32 * nt + lo] = zreg[nt];
+                if (MODE == MODE_CAUSAL) z_s[f0 + 32 * nt + lo] = zreg[nt];
             }
         }
 
         if (HAS_Q) {
-            __syncthreads(); // (B) partial tiles and denominators of all waves in LDS
-            // wave w finishes output tile (tq, nt) = (w / 2, w % 2)
-            const int tq = w >> 1, nt = w & 1;
-            f32x16 c = own;
+            sync_lds(); // (B) partial blocks and denominators of all waves in LDS
 #pragma unroll
             for (int w2 = 0; w2 < NW; ++w2) {
                 if (w2 == w) continue;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(&red_s[w][w2][j][lane][0]);
-                    c[4 * j] += x[0];
-                    c[4 * j + 1] += x[1];
-                    c[4 * j + 2] += x[2];
-                    c[4 * j + 3] += x[3];
+                for (int j = 0; j < 2; ++j) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(&red_s[on][oq][w2][j][lane][0]);
+                    own[4 * j] += x[0];
+                    own[4 * j + 1] += x[1];
+                    own[4 * j + 2] += x[2];
+                    own[4 * j + 3] += x[3];
                 }
             }
-            u16* ob = a.out + (bh * a.N + c0) * DV + 32 * nt + lo;
+            u16* ob = a.out + (bh * a.N + c0) * DV + 32 * on + lo;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tb = 32 * tq + 8 * j + 4 * h;
+            for (int j = 0; j < 2; ++j) {
+                const int tb = 16 * oq + 8 * j + 4 * h; // rows of regs 8 oq + 4 j .. + 3
                 f32x4 dsum = *reinterpret_cast<const f32x4*>(&den_s[0][tb]);
 #pragma unroll
                 for (int w2 = 1; w2 < NW; ++w2) {
@@ -470,10 +445,22 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = tb + e;
-                    float y = c[4 * j + e];
-                    if (a.norm == NORM_ATTN) y = y / fmaxf(dsum[e], a.eps);
-                    if (t < rows) ob[(int64_t)t * DV] = __builtin_bit_cast(u16, (__bf16)y);
+                    float y = own[4 * j + e];
+                    if (a.norm == NORM_ATTN) y *= __builtin_amdgcn_rcpf(fmaxf(dsum[e], a.eps));
+                    own[4 * j + e] = y;
+                }
+            }
+            if (rows == L) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int t = 16 * oq + 8 * (i >> 2) + 4 * h + (i & 3);
+                    ob[(int64_t)t * DV] = __builtin_bit_cast(u16, (__bf16)own[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int t = 16 * oq + 8 * (i >> 2) + 4 * h + (i & 3);
+                    if (t < rows) ob[(int64_t)t * DV] = __builtin_bit_cast(u16, (__bf16)own[i]);
                 }
             }
         }

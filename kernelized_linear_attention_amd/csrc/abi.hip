@@ -68,7 +68,7 @@ int check_sizes(int64_t B, int64_t H, int64_t N) {
 //   [BH*G*E, +BH*E)        bidirectional only: the full summary per head
 size_t ws_floats(int32_t op, int64_t BH, SegPlan sp, int r) {
     const int64_t E = state_elems(r);
-    size_t n = (size_t)(BH * sp.G * E);
+    size_t n = (size_t)(BH * sp.G * sp.sub * E);
     if (op == LIN_ATTN_OP_BIDIR) n += (size_t)(BH * E);
     return n;
 }
@@ -78,8 +78,12 @@ int launch_status(hipError_t e) { return e == hipSuccess ? LIN_ATTN_OK : LIN_ATT
 // The kernel family a validated call runs on, and its segmentation.
 bool use_mfma(const lin_attn_params* p) { return favor_mfma_supported(make_cfg(p), p->dtype); }
 
+// The matrix-core increment kernel fits two workgroups per CU while the
+// output kernel fits one: it sums over half segments (32-token multiples).
 SegPlan plan_for(const lin_attn_params* p, int64_t BH, int64_t N) {
-    return plan_segments(BH, N, p->n_seg, use_mfma(p) ? TARGET_BLOCKS_MFMA : TARGET_BLOCKS_VALU);
+    SegPlan sp = plan_segments(BH, N, p->n_seg, use_mfma(p) ? TARGET_BLOCKS_MFMA : TARGET_BLOCKS_VALU);
+    if (use_mfma(p)) sp.sub = 2;
+    return sp;
 }
 
 hipError_t segment_sums(const lin_attn_params* p, const Cfg& c, const void* k, const void* v,
@@ -171,11 +175,12 @@ int lin_attn_bidir(const lin_attn_params* p, const void* q, const void* k, const
     const Cfg c = make_cfg(p);
     const Shape s{BH, N};
     hipStream_t st = (hipStream_t)stream;
+    const SegPlan ss = sums_plan(sp);
     float* inc = (float*)ws;
-    float* fin = inc + BH * sp.G * state_elems(p->r);
-    hipError_t e = segment_sums(p, c, k, v, omega, s, sp, inc, st);
+    float* fin = inc + BH * ss.G * state_elems(p->r);
+    hipError_t e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
     if (e == hipSuccess)
-        e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc, 0, S_out, z_out, fin, st);
+        e = launch_segment_scan(p->r, s, ss, nullptr, nullptr, inc, 0, S_out, z_out, fin, st);
     if (e == hipSuccess)
         e = segment_outputs(p, c, 0, q, k, v, omega, s, sp, fin, state_elems(p->r), 0, out, st);
     return launch_status(e);
@@ -215,14 +220,16 @@ int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void*
     const Cfg c = make_cfg(p);
     const Shape s{BH, N};
     hipStream_t st = (hipStream_t)stream;
+    const SegPlan ss = sums_plan(sp);
     float* inc = (float*)ws;
     const int64_t E = state_elems(p->r);
-    hipError_t e = segment_sums(p, c, k, v, omega, s, sp, inc, st);
+    hipError_t e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
     if (e == hipSuccess)
-        e = launch_segment_scan(p->r, s, sp, state_in ? S : nullptr, state_in ? z : nullptr, inc,
+        e = launch_segment_scan(p->r, s, ss, state_in ? S : nullptr, state_in ? z : nullptr, inc,
                                 1, S, z, nullptr, st);
+    // segment g starts at sub-segment g * sub: its carried-in state is that prefix
     if (e == hipSuccess)
-        e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, sp.G * E, E, out, st);
+        e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, ss.G * E, sp.sub * E, out, st);
     return launch_status(e);
 }
 

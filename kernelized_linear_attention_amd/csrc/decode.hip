@@ -19,6 +19,52 @@ constexpr int NT = 256;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int MAXM = RMAX * DV / 4 / NT; // float4 chunks of S per thread at r = RMAX
 
+// Row f of omega, raw (bfloat16 pairs or float32), loaded early and
+// unpacked only when the feature is computed.
+template <typename T> struct OmegaRow;
+template <> struct OmegaRow<bf16_raw> {
+    uint4 w[D / 8];
+    __device__ __forceinline__ void load(const bf16_raw* om, int f) {
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) w[i] = reinterpret_cast<const uint4*>(om + (int64_t)f * D)[i];
+    }
+    __device__ __forceinline__ float dot(const float* u) const {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+            const uint32_t x[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s = fmaf(__uint_as_float(x[j] << 16), u[8 * i + 2 * j], s);
+                s = fmaf(__uint_as_float(x[j] & 0xffff0000u), u[8 * i + 2 * j + 1], s);
+            }
+        }
+        return s;
+    }
+};
+template <> struct OmegaRow<float> {
+    float4 w[D / 4];
+    __device__ __forceinline__ void load(const float* om, int f) {
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) w[i] = reinterpret_cast<const float4*>(om + (int64_t)f * D)[i];
+    }
+    __device__ __forceinline__ float dot(const float* u) const {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) {
+            s = fmaf(w[i].x, u[4 * i], s);
+            s = fmaf(w[i].y, u[4 * i + 1], s);
+            s = fmaf(w[i].z, u[4 * i + 2], s);
+            s = fmaf(w[i].w, u[4 * i + 3], s);
+        }
+        return s;
+    }
+};
+
+// Barrier for LDS traffic only: __syncthreads() would also wait for the S
+// loads still in flight.
+__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <typename T>
 __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
                                                const T* __restrict__ k,
@@ -34,36 +80,56 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
     const int64_t bh = blockIdx.x;
     const int r = c.r;
     const int m_count = r * DV / 4 / NT; // rows of S per thread: r / 16
+    const bool favor = c.phi == PHI_FAVOR;
 
-    // 1. issue every S load of this thread: float4 e = tid + NT*m is row
-    //    e / 16 = tid/16 + 16m, columns 4*(tid%16) .. +3.
+    // 1. the feature map's inputs first: vector-memory counters retire in
+    //    order, so anything issued after the S stream would wait for all of it
+    float xq = 0.f, xk = 0.f, xv = 0.f;
+    if (tid < D) {
+        xq = Elem<T>::load(q, bh * D + tid);
+        xk = Elem<T>::load(k, bh * D + tid);
+        xv = Elem<T>::load(v, bh * DV + tid);
+    }
+    OmegaRow<T> om;
+    if (favor && tid < r) om.load(omega, tid);
+
+    // 2. the state stream: float4 e = tid + NT*m is row tid/16 + 16m,
+    //    columns 4*(tid%16) .. +3
     f32x4* S4 = reinterpret_cast<f32x4*>(S + bh * (int64_t)r * DV);
     f32x4 s[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m)
         if (m < m_count) s[m] = __builtin_nontemporal_load(S4 + tid + NT * m);
     float zold = 0.f;
-    if (tid < r) zold = z[bh * r + tid];
+    if (tid < r) zold = __builtin_nontemporal_load(z + bh * r + tid);
 
-    // 2. inputs of this head
     if (tid < D) {
-        uq_s[tid] = c.scale * Elem<T>::load(q, bh * D + tid);
-        uk_s[tid] = c.scale * Elem<T>::load(k, bh * D + tid);
-        v_s[tid] = Elem<T>::load(v, bh * DV + tid);
+        uq_s[tid] = c.scale * xq;
+        uk_s[tid] = c.scale * xk;
+        v_s[tid] = xv;
+        if (favor) {
+            // |scale x|^2 of q (wave 0 holds all 64 components)
+            const float nq = wave_sum(uq_s[tid] * uq_s[tid]);
+            const float nk = wave_sum(uk_s[tid] * uk_s[tid]);
+            if (lane == 0) {
+                scal_s[0] = nq;
+                scal_s[1] = nk;
+            }
+        }
     }
-    __syncthreads();
-    if (c.phi == PHI_FAVOR && w < 2) {
-        const float a = (w == 0 ? uq_s : uk_s)[lane];
-        const float n = wave_sum(a * a);
-        if (lane == 0) scal_s[w] = n;
-    }
-    __syncthreads();
+    sync_lds();
 
     // 3. one feature of phi(q) and phi(k) per thread
     float pq = 0.f, pk = 0.f;
     if (tid < r) {
-        pq = phi_feature<T>(c, uq_s, scal_s[0], tid, omega);
-        pk = phi_feature<T>(c, uk_s, scal_s[1], tid, omega);
+        if (favor) {
+            // omega . (scale x), from the unscaled row and the scaled input
+            pq = favor_feature(c, om.dot(uq_s), scal_s[0]);
+            pk = favor_feature(c, om.dot(uk_s), scal_s[1]);
+        } else {
+            pq = phi_feature<T>(c, uq_s, 0.f, tid, omega);
+            pk = phi_feature<T>(c, uk_s, 0.f, tid, omega);
+        }
     }
     if (c.sum_norm) {
         const float a = wave_sum(pq), b = wave_sum(pk);
@@ -71,7 +137,7 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
             red_s[w][0] = a;
             red_s[w][1] = b;
         }
-        __syncthreads();
+        sync_lds();
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int i = 0; i < NT / 64; ++i) {
@@ -80,7 +146,7 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
         }
         pq *= 1.f / fmaxf(sq, c.eps);
         pk *= 1.f / fmaxf(sk, c.eps);
-        __syncthreads(); // red_s is reused below
+        sync_lds(); // red_s is reused below
     }
     if (tid < r) {
         pq_s[tid] = pq;
@@ -91,12 +157,12 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
     float den_part = 0.f;
     if (tid < r) {
         const float zn = zold + pk;
-        z[bh * r + tid] = zn;
+        __builtin_nontemporal_store(zn, z + bh * r + tid);
         den_part = pq * zn;
     }
     den_part = wave_sum(den_part);
     if (lane == 0) scal_s[2 + w] = den_part;
-    __syncthreads();
+    sync_lds();
 
     // 5. S rows: S <- S + phi(k)_row v^T, o += phi(q)_row S_row
     const int c4 = (tid % 16) * 4;
@@ -134,7 +200,7 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
         red_s[w][c4 + 2] = o.z;
         red_s[w][c4 + 3] = o.w;
     }
-    __syncthreads();
+    sync_lds();
     if (tid < DV) {
         float num = 0.f, den = 0.f;
 #pragma unroll

@@ -226,8 +226,8 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
 
     bf16x8 qf[4], kf[4], vr;
     int rows = (int)min<int64_t>(L, t1 - t0);
-    if (HAS_Q) load_x(qb + t0 * D, rows, lo, h, qf);
-    if (HAS_K) {
+    if (HAS_Q && rows > 0) load_x(qb + t0 * D, rows, lo, h, qf);
+    if (HAS_K && rows > 0) {
         load_x(kb + t0 * D, rows, lo, h, kf);
         vr = load_v(vb + t0 * DV, rows, tid);
         store_vt(vt_s[0], tid, vr);

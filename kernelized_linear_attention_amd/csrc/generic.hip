@@ -206,10 +206,19 @@ __global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const flo
     float run = 0.f;
     if (S0) run = e < rdv ? S0[bh * rdv + e] : z0[bh * r + (e - rdv)];
     float* p = ws + bh * G * E + e;
-    for (int64_t g = 0; g < G; ++g) {
-        const float a = p[g * E];
-        if (write_prefix) p[g * E] = run;
-        run += a;
+    // batches of 8 independent loads, then the fixed-order running sum
+    for (int64_t g0 = 0; g0 < G; g0 += 8) {
+        const int n = (int)min<int64_t>(8, G - g0);
+        float a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = i < n ? p[(g0 + i) * E] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < n) {
+                if (write_prefix) p[(g0 + i) * E] = run;
+                run += a[i];
+            }
+        }
     }
     if (e < rdv) {
         if (S_fin) S_fin[bh * rdv + e] = run;

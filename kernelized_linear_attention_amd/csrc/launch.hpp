@@ -19,12 +19,16 @@ constexpr int64_t TARGET_BLOCKS_VALU = 512; // vector kernels: about two workgro
 constexpr int64_t TARGET_BLOCKS_MFMA = 256; // matrix-core kernels: one workgroup per CU
 
 struct SegPlan {
-    int64_t G;
-    int64_t seg_len;
+    int64_t G;       // segments per head (one workgroup each for the outputs)
+    int64_t seg_len; // tokens per segment
+    int64_t sub;     // the state increments are summed over seg_len / sub tokens
 };
 
+// The plan of the increment and prefix kernels: sub-segments as segments.
+inline SegPlan sums_plan(SegPlan p) { return SegPlan{p.G * p.sub, p.seg_len / p.sub, 1}; }
+
 inline SegPlan plan_segments(int64_t BH, int64_t N, int32_t n_seg_req, int64_t target_blocks) {
-    SegPlan p{1, N};
+    SegPlan p{1, N, 1};
     if (N <= 0 || BH <= 0) return p;
     const int64_t units = (N + SEG_UNIT - 1) / SEG_UNIT;
     int64_t G = n_seg_req > 0 ? n_seg_req : (target_blocks + BH - 1) / BH;

@@ -179,17 +179,18 @@ def test_workspace_size_formula():
     bidirectional adds one per head for the full summary.  FAVOR+ with
     bfloat16 inputs and r = 256 runs on the matrix-core kernels, one
     workgroup per CU: at B=1, H=8, N=65536 that is 32 segments of 2048
-    tokens; the float32 vector kernels aim at two per CU (64 segments)."""
+    tokens, whose increments are summed over half segments (64 blocks per
+    head); the float32 vector kernels aim at two per CU (64 segments)."""
     p = params()
     E = 256 * 64 + 256
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 1, 8, 65536, 64, 64) == \
-        8 * 32 * E * 4
+        8 * 64 * E * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR, p, 1, 8, 65536, 64, 64) == \
-        (8 * 32 + 8) * E * 4
+        (8 * 64 + 8) * E * 4
     pf = params(dtype=0)
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, pf, 1, 8, 65536, 64, 64) == \
         8 * 64 * E * 4
     p1 = params(n_seg=1)
-    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p1, 2, 3, 1000, 64, 64) == 6 * E * 4
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p1, 2, 3, 1000, 64, 64) == 6 * 2 * E * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 2, 3, 0, 64, 64) == 0
     assert binding.lin_attn_workspace_bytes(9, p, 2, 3, 10, 64, 64) == 0

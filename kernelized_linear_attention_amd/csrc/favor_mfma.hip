@@ -43,10 +43,19 @@ constexpr int NT = 256;       // four waves
 constexpr int NW = 4;
 constexpr int R = 256;        // features: 64 per wave
 constexpr int L = 32;         // chunk length: one 32-token MFMA tile
-constexpr int LDK = 68;       // LDS row stride (bf16) of a wave's phi(K) tile [32 t][64 f]
-constexpr int LDV = 36;       // LDS row stride (bf16) of the V^T tile [64 n][32 t]
+constexpr int LDK = 72;       // LDS row stride (bf16) of a wave's phi(K) tile [32 t][64 f]: 144 B
+constexpr int LDV = 40;       // LDS row stride (bf16) of the V^T tile [64 n][32 t]: 80 B
 
 enum { MODE_SUMS = 0, MODE_CAUSAL = 1, MODE_READOUT = 2 };
+
+// Register budget.  omega's fragments stay in registers (re-reading them per
+// projection doubles the L1 traffic of a chunk) and each chunk's inputs are
+// loaded one chunk ahead; that takes more than the 256 registers per lane of
+// two workgroups per CU, so the kernel runs one workgroup per CU and hides
+// latency with the prefetch.
+constexpr bool OMEGA_IN_REGS = true;
+constexpr bool PREFETCH = true;
+constexpr int MIN_WG_PER_CU = 1;
 
 struct FavorArgs {
     const u16* q;
@@ -85,13 +94,6 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int base) {
     return r;
 }
 
-__device__ __forceinline__ bf16x8 zero8() {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (__bf16)0.f;
-    return r;
-}
-
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 r;
 #pragma unroll
@@ -107,18 +109,16 @@ __device__ __forceinline__ u16 bf16_bits(const bf16x8& v, int e) {
     return (e & 1) ? (u16)(word >> 16) : (u16)(word & 0xffffu);
 }
 
-// Two 4-element runs of a bf16 row in LDS, as one MFMA operand.
-__device__ __forceinline__ bf16x8 lds_pair(const u16* row, int c0, int c1) {
-    bf16x4 a = *reinterpret_cast<const bf16x4*>(row + c0);
-    bf16x4 b = *reinterpret_cast<const bf16x4*>(row + c1);
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r[e] = a[e];
-        r[4 + e] = b[e];
-    }
-    return r;
-}
+// Column order of the LDS tiles that feed MFMA operands.  An accumulator
+// element i of lane half h belongs to index 8(i/4) + 4h + i%4 within a
+// 16-block; the operand built from it holds, in k-slot e, index
+// 8(e/4) + 4h + e%4.  Storing index x at column swap23(x) (bits 2 and 3
+// exchanged) makes those eight indices the contiguous columns 8h .. 8h + 7,
+// so each operand is one 16-byte LDS read.
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+// One MFMA operand: 8 contiguous bf16 of an LDS row.
+__device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // f[ks] = X[lo][16 ks + 8 h .. +7] of the chunk at X: the A operand
 // (tokens as M) and the B operand (tokens as N) of a contraction over d.
@@ -156,14 +156,26 @@ __device__ __forceinline__ bf16x8 load_v(const u16* __restrict__ V, int rows, in
     return *reinterpret_cast<const bf16x8*>(V + (int64_t)t * DV + n0);
 }
 
+// V^T in LDS: row n holds V[t][n] at column vt_col(n, swap23(t)); the
+// 16-byte chunks of a row are rotated by (n / 8) % 4 so that the transposing
+// stores (eight rows 8 apart at a time) fall on different banks.
+__device__ __forceinline__ int vt_col(int n, int c) { return (((c >> 3) ^ ((n >> 3) & 3)) << 3) | (c & 7); }
+
 __device__ __forceinline__ void store_vt(u16* vt, int tid, const bf16x8& vr) {
-    const int t = tid >> 3, n0 = (tid & 7) * 8;
+    const int t = swap23(tid >> 3), n0 = (tid & 7) * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vt[(n0 + e) * LDV + t] = bf16_bits(vr, e);
+    for (int e = 0; e < 8; ++e) vt[(n0 + e) * LDV + vt_col(n0 + e, t)] = bf16_bits(vr, e);
+}
+
+// omega[f0 + 32 t + lo][16 ks + 8 h ..]: A operand of omega X^T (t = feature
+// tile as M) and B operand of X omega^T (t = feature tile as N) at once.
+__device__ __forceinline__ bf16x8 omega_frag(const u16* __restrict__ omega, int f0, int t, int ks,
+                                             int lo, int h) {
+    return *reinterpret_cast<const bf16x8*>(omega + (int64_t)(f0 + 32 * t + lo) * D + 16 * ks + 8 * h);
 }
 
 template <int MODE>
-__global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
+__global__ __launch_bounds__(NT, MIN_WG_PER_CU) void k_favor_mfma(FavorArgs a) {
     __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LDV];        // V^T, double buffered
     __shared__ __attribute__((aligned(16))) u16 pk_s[NW][L * LDK];        // phi(K)[:, F_w], bf16
     __shared__ __attribute__((aligned(16))) float red_s[2][2][NW][2][64][4]; // partial num blocks
@@ -171,7 +183,8 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
     __shared__ __attribute__((aligned(16))) float den_s[NW][L];
     __shared__ __attribute__((aligned(16))) float kb_s[NW][L];            // key biases by token
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
     const int lo = lane & 31, h = lane >> 5;
     const int f0 = 64 * w;
     const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
@@ -182,15 +195,13 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
     // this wave finishes rows [16 oq, 16 oq + 16) of output tile on (columns 32 on + ..)
     const int on = w & 1, oq = w >> 1;
 
-    // omega rows of F_w: om[mt][ks] = omega[f0 + 32 mt + lo][16 ks + 8 h ..].
-    // A operand of omega X^T and B operand of X omega^T at once.
-    bf16x8 om[2][4];
+    bf16x8 om[2][4]; // omega rows of F_w, when they stay in registers
+    if (OMEGA_IN_REGS) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            om[mt][ks] = *reinterpret_cast<const bf16x8*>(a.omega + (int64_t)(f0 + 32 * mt + lo) * D +
-                                                         16 * ks + 8 * h);
+            for (int ks = 0; ks < 4; ++ks) om[mt][ks] = omega_frag(a.omega, f0, mt, ks, lo, h);
+    }
 
     // State slice S[F_w, :] in accumulator layout: element i of S[mt][nt]
     // is S[f0 + 32 mt + 8 (i/4) + 4 h + i%4][32 nt + lo].
@@ -226,12 +237,16 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
 
     bf16x8 qf[4], kf[4], vr;
     int rows = (int)min<int64_t>(L, t1 - t0);
-    if (HAS_Q && rows > 0) load_x(qb + t0 * D, rows, lo, h, qf);
+    if (PREFETCH && HAS_Q && rows > 0) load_x(qb + t0 * D, rows, lo, h, qf);
+    if (PREFETCH && HAS_K && rows > 0) load_x(kb + t0 * D, rows, lo, h, kf);
     if (HAS_K && rows > 0) {
-        load_x(kb + t0 * D, rows, lo, h, kf);
         vr = load_v(vb + t0 * DV, rows, tid);
         store_vt(vt_s[0], tid, vr);
     }
+
+    // causal mask of the diagonal tile: element i of lane (lo, h) pairs query
+    // lo with key 8(i/4) + 4h + i%4, kept when 8(i/4) + i%4 <= lo - 4h
+    const int keep_thr = lo - 4 * h;
 
     int buf = 0;
     for (int64_t c0 = t0; c0 < t1; c0 += L, buf ^= 1) {
@@ -244,18 +259,22 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
         bf16x8 fk[2][2]; // [nt][kk]: A operand of the update
         float zpart[2] = {0.f, 0.f};
         if (HAS_K) {
-            const float bk = fmaf(a.b_norm, sq_norm(kf), a.b_const);
+            if (!PREFETCH) load_x(kb + c0 * D, rows, lo, h, kf);
+            // keys past the end of the segment get bias -inf: exp2 gives exactly 0,
+            // so they add nothing to S, z or the intra-chunk block
+            const float bk = lo < rows ? fmaf(a.b_norm, sq_norm(kf), a.b_const) : -INFINITY;
             kb_s[w][lo] = bk; // both lane halves write the same value
             f32x16 PK[2];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 f32x16 c = zero16();
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) c = mfma(kf[ks], om[nt][ks], c);
+                for (int ks = 0; ks < 4; ++ks)
+                    c = mfma(kf[ks], OMEGA_IN_REGS ? om[nt][ks] : omega_frag(a.omega, f0, nt, ks, lo, h), c);
                 PK[nt] = c; // token 8(i/4) + 4h + i%4, feature f0 + 32 nt + lo
             }
             // the next chunk's keys and values load while this one is computed
-            if (rows_next > 0) {
+            if (PREFETCH && rows_next > 0) {
                 load_x(kb + cn * D, rows_next, lo, h, kf);
                 vr = load_v(vb + cn * DV, rows_next, tid);
             }
@@ -269,74 +288,54 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
-                if (rows < L) { // keys past the end of the segment contribute nothing
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int t = 8 * (i >> 2) + 4 * h + (i & 3);
-                        c[i] = t < rows ? c[i] : 0.f;
-                    }
-                }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) zpart[nt] += c[i];
                 fk[nt][0] = pack8(c, 0);
                 fk[nt][1] = pack8(c, 8);
             }
             if (MODE == MODE_CAUSAL) {
-                // phi(K) rows to LDS for the intra-chunk block
-                u16* pk = pk_s[w];
+                // phi(K) rows to LDS for the intra-chunk block: row t, column swap23(f)
+                u16* pk = pk_s[w] + swap23(lo);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int t = 8 * (i >> 2) + 4 * h + (i & 3);
-                        pk[t * LDK + 32 * nt + lo] = bf16_bits(fk[nt][i >> 3], i & 7);
+                        pk[t * LDK + 32 * nt] = bf16_bits(fk[nt][i >> 3], i & 7);
                     }
             }
         }
 
-        // ---- V fragments vf[kk][nt]: k-slot e <-> token 16 kk + 8 (e/4) + 4 h + e%4,
-        //      lane <-> column 32 nt + lo
-        bf16x8 vf[2][2];
-        if (HAS_K) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const int tb = 16 * kk + 4 * h;
-                    vf[kk][nt] = lds_pair(vt_s[buf] + (32 * nt + lo) * LDV, tb, tb + 8);
-                }
-        }
+        // keep the query side's loads (omega, q) from being hoisted into the key
+        // side: that would hold both phases' operands at once
+        asm volatile("" ::: "memory");
+
+        // V fragment (kk, nt): k-slot e <-> token 16 kk + 8 (e/4) + 4 h + e%4,
+        // lane <-> column 32 nt + lo (re-read from LDS where needed: cheaper
+        // than keeping it in registers)
+        const u16* vt = vt_s[buf];
+        auto vfrag = [&](int kk, int nt) {
+            return lds8(vt + (32 * nt + lo) * LDV + vt_col(32 * nt + lo, 16 * kk + 8 * h));
+        };
 
         // ---- queries: phi(Q), readout against S_{c-1}, intra-chunk block ---------
         f32x16 own = zero16(); // rows 16 oq .. of output tile on, in regs 8 oq .. 8 oq + 7
         if (HAS_Q) {
-            bf16x8 sb[2][2][2]; // [mt][nt][kk]: S_{c-1} as the B operand of the readout
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    sb[mt][nt][0] = pack8(S[mt][nt], 0);
-                    sb[mt][nt][1] = pack8(S[mt][nt], 8);
-                }
+            if (!PREFETCH) load_x(qb + c0 * D, rows, lo, h, qf);
             const float bq = fmaf(a.b_norm, sq_norm(qf), a.b_const);
-            f32x16 PQ[2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                f32x16 c = zero16();
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) c = mfma(om[mt][ks], qf[ks], c);
-                PQ[mt] = c; // feature f0 + 32 mt + 8(i/4) + 4h + i%4, token lo
-            }
-            if (rows_next > 0) load_x(qb + cn * D, rows_next, lo, h, qf);
             bf16x8 fq[2][2]; // [mt][kk]
             float den = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
+                // P_Q^T tile mt: feature f0 + 32 mt + 8(i/4) + 4h + i%4, token lo
+                f32x16 c = zero16();
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    c = mfma(OMEGA_IN_REGS ? om[mt][ks] : omega_frag(a.omega, f0, mt, ks, lo, h), qf[ks], c);
                 f32x4 zq[4]; // z_{c-1} of the features f0 + 32 mt + 8 j + 4 h + (0..3)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     zq[j] = *reinterpret_cast<const f32x4*>(&z_s[f0 + 32 * mt + 8 * j + 4 * h]);
-                f32x16& c = PQ[mt];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float y = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
@@ -346,60 +345,58 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
                 fq[mt][0] = pack8(c, 0);
                 fq[mt][1] = pack8(c, 8);
             }
-            f32x16 num[2]; // [nt]: row 8(i/4) + 4h + i%4, column 32 nt + lo
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f32x16 c = zero16();
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) c = mfma(fq[mt][kk], sb[mt][nt][kk], c);
-                num[nt] = c;
-            }
+            // this chunk's queries are consumed: load the next chunk's
+            if (PREFETCH && rows_next > 0) load_x(qb + cn * D, rows_next, lo, h, qf);
+            bf16x8 at[2]; // masked intra-chunk block A[lo][j] as the A operand of A V
             if (MODE == MODE_CAUSAL) {
                 // masked block, transposed: c[i] = A[lo][j], j = 8(i/4) + 4h + i%4, over F_w
-                const u16* pk = pk_s[w] + lo * LDK;
+                const u16* pk = pk_s[w] + lo * LDK + 8 * h;
                 f32x16 c = zero16();
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const int fb = 32 * mt + 16 * kk + 4 * h;
-                        c = mfma(lds_pair(pk, fb, fb + 8), fq[mt][kk], c);
-                    }
+                    for (int kk = 0; kk < 2; ++kk) c = mfma(lds8(pk + 32 * mt + 16 * kk), fq[mt][kk], c);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int j = 8 * (i >> 2) + 4 * h + (i & 3);
-                    c[i] = j <= lo ? c[i] : 0.f;
+                    c[i] = 8 * (i >> 2) + (i & 3) <= keep_thr ? c[i] : 0.f;
                     den += c[i];
                 }
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 at = pack8(c, 8 * kk);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) num[nt] = mfma(at, vf[kk][nt], num[nt]);
-                }
+                at[0] = pack8(c, 0);
+                at[1] = pack8(c, 8);
             }
             den += __shfl_xor(den, 32, 64);
             den_s[w][lo] = den; // both lane halves hold the full sum
-            // blocks (nt, q) of the other waves go to LDS; this wave keeps (on, oq)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt) {
+                // num tile nt: row 8(i/4) + 4h + i%4, column 32 nt + lo
+                f32x16 c = zero16();
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) c = mfma(fq[mt][kk], pack8(S[mt][nt], 8 * kk), c);
+                if (MODE == MODE_CAUSAL) {
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) c = mfma(at[kk], vfrag(kk, nt), c);
+                }
+                // blocks (nt, q) of the other waves go to LDS; this wave keeps (on, oq)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     if (nt == on && q == oq) {
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) own[i] = num[nt][8 * q + i];
+                        for (int i = 0; i < 8; ++i) own[i] = c[8 * q + i];
                     } else {
 #pragma unroll
                         for (int j = 0; j < 2; ++j) {
-                            const f32x4 x = {num[nt][8 * q + 4 * j], num[nt][8 * q + 4 * j + 1],
-                                             num[nt][8 * q + 4 * j + 2], num[nt][8 * q + 4 * j + 3]};
+                            const f32x4 x = {c[8 * q + 4 * j], c[8 * q + 4 * j + 1], c[8 * q + 4 * j + 2],
+                                             c[8 * q + 4 * j + 3]};
                             *reinterpret_cast<f32x4*>(&red_s[nt][q][w][j][lane][0]) = x;
                         }
                     }
                 }
+            }
         }
+
+        asm volatile("" ::: "memory");
 
         // ---- state update: S[F_w] += phi(K)^T V, z[F_w] += column sums ---------------
         if (HAS_K) {
@@ -408,7 +405,7 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) S[mt][nt] = mfma(fk[mt][kk], vf[kk][nt], S[mt][nt]);
+                    for (int kk = 0; kk < 2; ++kk) S[mt][nt] = mfma(fk[mt][kk], vfrag(kk, nt), S[mt][nt]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 zreg[nt] += zpart[nt] + __shfl_xor(zpart[nt], 32, 64);
@@ -466,7 +463,10 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
         }
 
         // next chunk's V^T (its loads were issued above)
-        if (HAS_K && rows_next > 0) store_vt(vt_s[buf ^ 1], tid, vr);
+        if (HAS_K && rows_next > 0) {
+            if (!PREFETCH) vr = load_v(vb + cn * DV, rows_next, tid);
+            store_vt(vt_s[buf ^ 1], tid, vr);
+        }
     }
 
     if (MODE == MODE_SUMS) {

@@ -1,27 +1,34 @@
 // favor_mfma.hip -- FAVOR+ attention on the matrix cores (bfloat16 inputs,
 // r = 256 features, d = dv = 64, float32 accumulation and state).
 //
-// One workgroup of four waves handles one sequence segment of one head, in
-// chunks of 32 tokens (one MFMA tile: the intra-chunk block is a single
-// masked 32 x 32 tile).
-// Wave w owns the features F_w = [64w, 64w + 64): the rows of omega for F_w
-// stay in its registers for the whole segment, and so does its slice
-// S[F_w, :] of the state (float32 MFMA accumulators).  Per chunk (Kernel Zoo sec. 4.2 / 5.4 map; causal recurrence of sec. 1.3 in
-// chunked form, see generic.hip):
-//   P_Q^T = omega_w Q_c^T           -> phi(Q_c)[:, F_w]  (tokens on lanes)
-//   P_K   = K_c omega_w^T           -> phi(K_c)[:, F_w]  (features on lanes)
-//   phi   = exp2(P * s*log2(e) + per-token bias), the bias holding
-//           -s^2 |x|^2 / 2 and -log2(sqrt(r)) (x unscaled, s = scale)
-//   num_w = phi(Q_c) S_{c-1}[F_w]                         (inter-chunk readout)
-//         + ((phi(Q_c) phi(K_c)^T)|_{F_w} o causal mask) V_c (intra-chunk block)
-//   den_w = phi(Q_c) z_{c-1}[F_w] + row sums of the masked block
-//   S[F_w] += phi(K_c)[:, F_w]^T V_c,  z[F_w] += column sums of phi(K_c)
-// and the partial num_w, den_w of the four waves are summed through LDS.
+// One workgroup handles one sequence segment of one head, in chunks of 32
+// tokens (one MFMA tile: the intra-chunk block is a single masked 32 x 32
+// tile).  The 256 features are split into four groups F_g = [64g, 64g + 64),
+// and each group has two waves on the same SIMD:
+//   producer g  (waves 4..7) keeps the rows of omega for F_g in registers and
+//               turns chunk c into its random features, one chunk ahead of
+//               the consumer: the projections and the exponentials
+//                 P_Q^T = omega_g Q_c^T,  P_K = K_c omega_g^T,
+//                 phi   = exp2(P * s*log2(e) + per-token bias)
+//               (the bias holds -s^2 |x|^2 / 2 and -log2(sqrt(r)); x unscaled,
+//               s = scale), the partial denominators phi(Q_c) z_{c-1}[F_g] and
+//               the masked intra-chunk block (phi(Q_c) phi(K_c)^T)|_{F_g};
+//               it also keeps z[F_g] and stages V_c^T in LDS;
+//   consumer g  (waves 0..3) keeps its state slice S[F_g, :] in float32
+//               accumulators and, for chunk c - 1, forms the partial numerator
+//                 phi(Q) S_{c-1}[F_g] + (masked block) V
+//               and the update S[F_g] += phi(K)^T V; the four partial
+//               numerators are summed through LDS and divided by the summed
+//               denominators.
+// Producers are VALU-heavy (two exponentials per token and feature) and
+// consumers MFMA-heavy, so the pair on a SIMD keeps both units busy.  The
+// hand-off buffers in LDS are double-buffered by chunk, which leaves one
+// workgroup barrier per chunk (Kernel Zoo sec. 4.2 / 5.4 map; causal
+// recurrence of sec. 1.3 in chunked form, see generic.hip).
 // Every contraction is a v_mfma_f32_32x32x16_bf16; the MFMA accumulator
 // layout of one product is reused as an operand of the next where the
 // contraction index allows it (a k-slot permutation applied to both
-// operands), so only phi(K) (for the intra block) and V (transposed) pass
-// through LDS.
+// operands).
 //
 // Modes: SUMS     -- per-segment state increments (no outputs);
 //        CAUSAL   -- chunked recurrence from the carried-in state;
@@ -39,23 +46,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 256;       // four waves
-constexpr int NW = 4;
-constexpr int R = 256;        // features: 64 per wave
+constexpr int NW = 4;         // feature groups of 64: one producer and one consumer wave each
+constexpr int NT = 2 * 64 * NW;
+constexpr int R = 256;
 constexpr int L = 32;         // chunk length: one 32-token MFMA tile
-constexpr int LDK = 72;       // LDS row stride (bf16) of a wave's phi(K) tile [32 t][64 f]: 144 B
 constexpr int LDV = 40;       // LDS row stride (bf16) of the V^T tile [64 n][32 t]: 80 B
 
 enum { MODE_SUMS = 0, MODE_CAUSAL = 1, MODE_READOUT = 2 };
-
-// Register budget.  omega's fragments stay in registers (re-reading them per
-// projection doubles the L1 traffic of a chunk) and each chunk's inputs are
-// loaded one chunk ahead; that takes more than the 256 registers per lane of
-// two workgroups per CU, so the kernel runs one workgroup per CU and hides
-// latency with the prefetch.
-constexpr bool OMEGA_IN_REGS = true;
-constexpr bool PREFETCH = true;
-constexpr int MIN_WG_PER_CU = 1;
 
 struct FavorArgs {
     const u16* q;
@@ -134,18 +131,25 @@ __device__ __forceinline__ void load_x(const u16* __restrict__ X, int rows, int 
         f[ks] = *reinterpret_cast<const bf16x8*>(X + (int64_t)t * D + 16 * ks + 8 * h);
 }
 
+// x[lane] + x[lane ^ 32]: the two lane halves exchanged by one
+// v_permlane32_swap (no LDS round trip).
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // |x_t|^2 for t = lo from its fragments (the two lane halves hold
 // complementary halves of the row); bf16 products are exact in float32.
 __device__ __forceinline__ float sq_norm(const bf16x8 (&f)[4]) {
-    float s = 0.f;
+    float s[2] = {0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
             const bf16x2 x = {f[ks][e], f[ks][e + 1]};
-            s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
+            s[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(x, x, s[(e >> 1) & 1], false);
         }
-    return s + __shfl_xor(s, 32, 64);
+    return half_sum(s[0] + s[1]);
 }
 
 // Raw V rows of the chunk for the transposed LDS copy: thread th holds
@@ -174,46 +178,249 @@ __device__ __forceinline__ bf16x8 omega_frag(const u16* __restrict__ omega, int 
     return *reinterpret_cast<const bf16x8*>(omega + (int64_t)(f0 + 32 * t + lo) * D + 16 * ks + 8 * h);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(NT, MIN_WG_PER_CU) void k_favor_mfma(FavorArgs a) {
-    __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LDV];        // V^T, double buffered
-    __shared__ __attribute__((aligned(16))) u16 pk_s[NW][L * LDK];        // phi(K)[:, F_w], bf16
-    __shared__ __attribute__((aligned(16))) float red_s[2][2][NW][2][64][4]; // partial num blocks
-    __shared__ __attribute__((aligned(16))) float z_s[R];
-    __shared__ __attribute__((aligned(16))) float den_s[NW][L];
-    __shared__ __attribute__((aligned(16))) float kb_s[NW][L];            // key biases by token
+// One chunk's hand-off from the producers to the consumers, per feature
+// group g; every operand is stored lane-linear, so each side moves it with one
+// 16-byte LDS access per lane.
+struct XBuf {
+    bf16x8 fq[NW][2][2][64]; // phi(Q) as the A operand of the readout [g][feature tile][kk][lane]
+    bf16x8 fk[NW][2][2][64]; // phi(K) as the A operand of the update  [g][feature tile][kk][lane]
+    bf16x8 at[NW][2][64];    // masked intra-chunk block over F_g, A operand of A V [g][kk][lane]
+    float den[NW][L];        // denominators over F_g, by token
+};
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
-    const int lo = lane & 31, h = lane >> 5;
-    const int f0 = 64 * w;
-    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
-    const int64_t t0 = g * a.seg_len;
-    const int64_t t1 = min<int64_t>(a.N, t0 + a.seg_len);
+struct Smem {
+    XBuf xb[2];                    // double-buffered by chunk
+    u16 vt[2][DV * LDV];           // V^T of the chunk, double-buffered
+    float red[2][NW][NW - 1][2][64][4]; // partial numerator blocks [buf][owner][sender slot][j][lane]
+    float z[R];                    // producer-private: z_{c-1}, by feature
+    float kb[NW][L];               // producer-private: key biases by token
+    u16 ot[NW][16 * 32];           // consumer-private: finished output block, bf16 rows
+};
+
+// B operand of a transposition through the matrix core: k-slot e of lane
+// (n, h) is 1 where token 16 kk + 8(e/4) + 4h + e%4 equals n.  With an
+// operand X whose lanes are features and whose k-slots are those tokens,
+// sum_kk mfma(X_kk, eye_kk) is X transposed (tokens on lanes), exactly:
+// every output is one bfloat16 product by 1 plus zeros.
+__device__ __forceinline__ bf16x8 eye_frag(int kk, int lo, int h) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)(16 * kk + 8 * (e >> 2) + 4 * h + (e & 3) == lo ? 1.f : 0.f);
+    return r;
+}
+
+template <int MODE>
+__device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, int lane, int64_t bh,
+                                         int64_t g, int64_t t0, int64_t t1, int nck) {
     constexpr bool HAS_K = MODE != MODE_READOUT;
     constexpr bool HAS_Q = MODE != MODE_SUMS;
+    const int lo = lane & 31, h = lane >> 5;
+    const int f0 = 64 * p;
+    const int ptid = 64 * p + lane; // 0 .. 255 over the producers: V^T staging
+
+    bf16x8 om[2][4]; // omega[f0 + 32 t + lo][16 ks + 8 h ..]
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) om[t][ks] = omega_frag(a.omega, f0, t, ks, lo, h);
+
+    float zreg[2] = {0.f, 0.f}; // z[f0 + 32 nt + lo]
+    if (MODE != MODE_SUMS) {
+        const float* st = a.state + bh * a.st_bh + g * a.st_g;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) zreg[nt] = st[(int64_t)R * DV + f0 + 32 * nt + lo];
+        if (h == 0) {
+            sm.z[f0 + lo] = zreg[0];
+            sm.z[f0 + 32 + lo] = zreg[1];
+        }
+    }
+
+    const u16* qb = a.q + bh * a.N * D;
+    const u16* kb = a.k + bh * a.N * D;
+    const u16* vb = a.v + bh * a.N * DV;
+
+    // each chunk's inputs are loaded one chunk ahead
+    bf16x8 qf[4], kf[4], vr;
+    if (nck > 0) {
+        const int rows = (int)min<int64_t>(L, t1 - t0);
+        if (HAS_Q) load_x(qb + t0 * D, rows, lo, h, qf);
+        if (HAS_K) {
+            load_x(kb + t0 * D, rows, lo, h, kf);
+            vr = load_v(vb + t0 * DV, rows, ptid);
+        }
+    }
+
+    // causal mask of the diagonal tile: element i of lane (lo, h) pairs query
+    // lo with key 8(i/4) + 4h + i%4, kept when 8(i/4) + i%4 <= lo - 4h
+    const int keep_thr = lo - 4 * h;
+
+    bf16x8 eye[2]; // transposition operands (causal intra-chunk block)
+    if (MODE == MODE_CAUSAL) {
+        eye[0] = eye_frag(0, lo, h);
+        eye[1] = eye_frag(1, lo, h);
+    }
+
+    for (int ci = 0; ci <= nck; ++ci) {
+        if (ci < nck) {
+            const int64_t c0 = t0 + (int64_t)L * ci;
+            const int rows = (int)min<int64_t>(L, t1 - c0);
+            const int64_t cn = c0 + L;
+            const int rows_next = cn < t1 ? (int)min<int64_t>(L, t1 - cn) : 0;
+            XBuf& X = sm.xb[ci & 1];
+
+            // ---- projections: both sides' MFMAs first, so that the matrix core
+            // works while the exponentials of the key side run ---------------------
+            f32x16 PK[2], PQ[2];
+            float bq = 0.f;
+            if (HAS_K) {
+                // keys past the end of the segment get bias -inf: exp2 gives exactly 0,
+                // so they add nothing to S, z or the intra-chunk block
+                const float bk = lo < rows ? fmaf(a.b_norm, sq_norm(kf), a.b_const) : -INFINITY;
+                sm.kb[p][lo] = bk; // both lane halves write the same value
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x16 c = zero16();
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) c = mfma(kf[ks], om[nt][ks], c);
+                    PK[nt] = c; // token 8(i/4) + 4h + i%4, feature f0 + 32 nt + lo
+                }
+            }
+            if (HAS_Q) {
+                bq = fmaf(a.b_norm, sq_norm(qf), a.b_const);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    f32x16 c = zero16();
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) c = mfma(om[mt][ks], qf[ks], c);
+                    PQ[mt] = c; // feature f0 + 32 mt + 8(i/4) + 4h + i%4, token lo
+                }
+            }
+            // the next chunk's inputs load while this one is computed
+            if (HAS_K) {
+                store_vt(sm.vt[ci & 1], ptid, vr);
+                if (rows_next > 0) {
+                    load_x(kb + cn * D, rows_next, lo, h, kf);
+                    vr = load_v(vb + cn * DV, rows_next, ptid);
+                }
+            }
+            if (HAS_Q && rows_next > 0) load_x(qb + cn * D, rows_next, lo, h, qf);
+
+            // ---- phi(K): exponentials, column sums, hand-off -----------------------
+            float zpart[2] = {0.f, 0.f};
+            bf16x8 fk[2][2];
+            if (HAS_K) {
+                f32x4 kbias[4]; // biases of the tokens 8 j + 4 h + (0..3)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    kbias[j] = *reinterpret_cast<const f32x4*>(&sm.kb[p][8 * j + 4 * h]);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x16& c = PK[nt];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
+                    float zs[2] = {0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) zs[i & 1] += c[i];
+                    zpart[nt] = zs[0] + zs[1];
+                    fk[nt][0] = pack8(c, 0);
+                    fk[nt][1] = pack8(c, 8);
+                    X.fk[p][nt][0][lane] = fk[nt][0];
+                    X.fk[p][nt][1][lane] = fk[nt][1];
+                }
+            }
+
+            // ---- phi(Q), its denominators against z_{c-1}, the intra-chunk block ----
+            if (HAS_Q) {
+                bf16x8 fq[2][2]; // [feature tile][kk]
+                float den[2] = {0.f, 0.f};
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    f32x16& c = PQ[mt];
+                    f32x4 zq[4]; // z_{c-1} of the features f0 + 32 mt + 8 j + 4 h + (0..3)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        zq[j] = *reinterpret_cast<const f32x4*>(&sm.z[f0 + 32 * mt + 8 * j + 4 * h]);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float y = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
+                        c[i] = y;
+                        den[i & 1] = fmaf(y, zq[i >> 2][i & 3], den[i & 1]);
+                    }
+                    fq[mt][0] = pack8(c, 0);
+                    fq[mt][1] = pack8(c, 8);
+                    X.fq[p][mt][0][lane] = fq[mt][0];
+                    X.fq[p][mt][1][lane] = fq[mt][1];
+                }
+                if (MODE == MODE_CAUSAL) {
+                    // phi(K) with tokens on lanes: the transposition of fk through the
+                    // matrix core; lane (j, h), k-slot e <-> feature
+                    // f0 + 32 mt + 16 kk + 8(e/4) + 4h + e%4, as in fq
+                    bf16x8 kt[2][2];
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        f32x16 c = zero16();
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) c = mfma(fk[nt][kk], eye[kk], c);
+                        kt[nt][0] = pack8(c, 0);
+                        kt[nt][1] = pack8(c, 8);
+                    }
+                    // masked block, transposed: c[i] = A[lo][j], j = 8(i/4) + 4h + i%4, over F_g
+                    f32x16 c = zero16();
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) c = mfma(kt[mt][kk], fq[mt][kk], c);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        c[i] = 8 * (i >> 2) + (i & 3) <= keep_thr ? c[i] : 0.f;
+                        den[i & 1] += c[i];
+                    }
+                    X.at[p][0][lane] = pack8(c, 0);
+                    X.at[p][1][lane] = pack8(c, 8);
+                }
+                X.den[p][lo] = half_sum(den[0] + den[1]); // both lane halves hold the full sum
+            }
+
+            // ---- z[F_g] += column sums of phi(K_c), after the queries read z_{c-1} ----
+            if (HAS_K) {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    zreg[nt] += half_sum(zpart[nt]);
+                    if (MODE == MODE_CAUSAL) sm.z[f0 + 32 * nt + lo] = zreg[nt];
+                }
+            }
+        }
+        sync_lds(); // chunk ci handed over; the consumers are done with chunk ci - 1
+    }
+
+    if (MODE == MODE_SUMS && h == 0) {
+        float* dst = a.state + bh * a.st_bh + g * a.st_g;
+        dst[(int64_t)R * DV + f0 + lo] = zreg[0];
+        dst[(int64_t)R * DV + f0 + 32 + lo] = zreg[1];
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ void consumer(const FavorArgs& a, Smem& sm, int w, int lane, int64_t bh,
+                                         int64_t g, int64_t t0, int64_t t1, int nck) {
+    constexpr bool HAS_K = MODE != MODE_READOUT;
+    constexpr bool HAS_Q = MODE != MODE_SUMS;
+    const int lo = lane & 31, h = lane >> 5;
+    const int f0 = 64 * w;
     // this wave finishes rows [16 oq, 16 oq + 16) of output tile on (columns 32 on + ..)
     const int on = w & 1, oq = w >> 1;
 
-    bf16x8 om[2][4]; // omega rows of F_w, when they stay in registers
-    if (OMEGA_IN_REGS) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) om[mt][ks] = omega_frag(a.omega, f0, mt, ks, lo, h);
-    }
-
-    // State slice S[F_w, :] in accumulator layout: element i of S[mt][nt]
+    // State slice S[F_g, :] in accumulator layout: element i of S[mt][nt]
     // is S[f0 + 32 mt + 8 (i/4) + 4 h + i%4][32 nt + lo].
     f32x16 S[2][2];
-    float zreg[2] = {0.f, 0.f}; // z[f0 + 32 nt + lo]
-    const float* st = a.state + bh * a.st_bh + g * a.st_g;
     if (MODE == MODE_SUMS) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) S[mt][nt] = zero16();
     } else {
+        const float* st = a.state + bh * a.st_bh + g * a.st_g;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -223,249 +430,125 @@ __global__ __launch_bounds__(NT, MIN_WG_PER_CU) void k_favor_mfma(FavorArgs a) {
                     const int f = f0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
                     S[mt][nt][i] = st[(int64_t)f * DV + 32 * nt + lo];
                 }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) zreg[nt] = st[(int64_t)R * DV + f0 + 32 * nt + lo];
-        if (h == 0) {
-            z_s[f0 + lo] = zreg[0];
-            z_s[f0 + 32 + lo] = zreg[1];
-        }
     }
 
-    const u16* qb = a.q + bh * a.N * D;
-    const u16* kb = a.k + bh * a.N * D;
-    const u16* vb = a.v + bh * a.N * DV;
-
-    bf16x8 qf[4], kf[4], vr;
-    int rows = (int)min<int64_t>(L, t1 - t0);
-    if (PREFETCH && HAS_Q && rows > 0) load_x(qb + t0 * D, rows, lo, h, qf);
-    if (PREFETCH && HAS_K && rows > 0) load_x(kb + t0 * D, rows, lo, h, kf);
-    if (HAS_K && rows > 0) {
-        vr = load_v(vb + t0 * DV, rows, tid);
-        store_vt(vt_s[0], tid, vr);
-    }
-
-    // causal mask of the diagonal tile: element i of lane (lo, h) pairs query
-    // lo with key 8(i/4) + 4h + i%4, kept when 8(i/4) + i%4 <= lo - 4h
-    const int keep_thr = lo - 4 * h;
-
-    int buf = 0;
-    for (int64_t c0 = t0; c0 < t1; c0 += L, buf ^= 1) {
-        rows = (int)min<int64_t>(L, t1 - c0);
-        const int64_t cn = c0 + L;
-        const int rows_next = cn < t1 ? (int)min<int64_t>(L, t1 - cn) : 0;
-        sync_lds(); // (A) vt_s[buf] complete; last chunk's red_s / den_s reads done
-
-        // ---- phi(K) = exp(K omega_w^T ...), features on lanes -------------------
-        bf16x8 fk[2][2]; // [nt][kk]: A operand of the update
-        float zpart[2] = {0.f, 0.f};
-        if (HAS_K) {
-            if (!PREFETCH) load_x(kb + c0 * D, rows, lo, h, kf);
-            // keys past the end of the segment get bias -inf: exp2 gives exactly 0,
-            // so they add nothing to S, z or the intra-chunk block
-            const float bk = lo < rows ? fmaf(a.b_norm, sq_norm(kf), a.b_const) : -INFINITY;
-            kb_s[w][lo] = bk; // both lane halves write the same value
-            f32x16 PK[2];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f32x16 c = zero16();
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    c = mfma(kf[ks], OMEGA_IN_REGS ? om[nt][ks] : omega_frag(a.omega, f0, nt, ks, lo, h), c);
-                PK[nt] = c; // token 8(i/4) + 4h + i%4, feature f0 + 32 nt + lo
-            }
-            // the next chunk's keys and values load while this one is computed
-            if (PREFETCH && rows_next > 0) {
-                load_x(kb + cn * D, rows_next, lo, h, kf);
-                vr = load_v(vb + cn * DV, rows_next, tid);
-            }
-            f32x4 kbias[4]; // biases of the tokens 8 j + 4 h + (0..3)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                kbias[j] = *reinterpret_cast<const f32x4*>(&kb_s[w][8 * j + 4 * h]);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f32x16& c = PK[nt];
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
-#pragma unroll
-                for (int i = 0; i < 16; ++i) zpart[nt] += c[i];
-                fk[nt][0] = pack8(c, 0);
-                fk[nt][1] = pack8(c, 8);
-            }
-            if (MODE == MODE_CAUSAL) {
-                // phi(K) rows to LDS for the intra-chunk block: row t, column swap23(f)
-                u16* pk = pk_s[w] + swap23(lo);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int t = 8 * (i >> 2) + 4 * h + (i & 3);
-                        pk[t * LDK + 32 * nt] = bf16_bits(fk[nt][i >> 3], i & 7);
-                    }
-            }
-        }
-
-        // keep the query side's loads (omega, q) from being hoisted into the key
-        // side: that would hold both phases' operands at once
-        asm volatile("" ::: "memory");
-
-        // V fragment (kk, nt): k-slot e <-> token 16 kk + 8 (e/4) + 4 h + e%4,
-        // lane <-> column 32 nt + lo (re-read from LDS where needed: cheaper
-        // than keeping it in registers)
-        const u16* vt = vt_s[buf];
-        auto vfrag = [&](int kk, int nt) {
-            return lds8(vt + (32 * nt + lo) * LDV + vt_col(32 * nt + lo, 16 * kk + 8 * h));
-        };
-
-        // ---- queries: phi(Q), readout against S_{c-1}, intra-chunk block ---------
-        f32x16 own = zero16(); // rows 16 oq .. of output tile on, in regs 8 oq .. 8 oq + 7
-        if (HAS_Q) {
-            if (!PREFETCH) load_x(qb + c0 * D, rows, lo, h, qf);
-            const float bq = fmaf(a.b_norm, sq_norm(qf), a.b_const);
-            bf16x8 fq[2][2]; // [mt][kk]
-            float den = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                // P_Q^T tile mt: feature f0 + 32 mt + 8(i/4) + 4h + i%4, token lo
-                f32x16 c = zero16();
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    c = mfma(OMEGA_IN_REGS ? om[mt][ks] : omega_frag(a.omega, f0, mt, ks, lo, h), qf[ks], c);
-                f32x4 zq[4]; // z_{c-1} of the features f0 + 32 mt + 8 j + 4 h + (0..3)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    zq[j] = *reinterpret_cast<const f32x4*>(&z_s[f0 + 32 * mt + 8 * j + 4 * h]);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float y = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
-                    c[i] = y;
-                    den = fmaf(y, zq[i >> 2][i & 3], den);
-                }
-                fq[mt][0] = pack8(c, 0);
-                fq[mt][1] = pack8(c, 8);
-            }
-            // this chunk's queries are consumed: load the next chunk's
-            if (PREFETCH && rows_next > 0) load_x(qb + cn * D, rows_next, lo, h, qf);
-            bf16x8 at[2]; // masked intra-chunk block A[lo][j] as the A operand of A V
-            if (MODE == MODE_CAUSAL) {
-                // masked block, transposed: c[i] = A[lo][j], j = 8(i/4) + 4h + i%4, over F_w
-                const u16* pk = pk_s[w] + lo * LDK + 8 * h;
-                f32x16 c = zero16();
+    for (int ci = 0; ci <= nck; ++ci) {
+        f32x16 own;       // rows 16 oq .. of output tile on, in regs 8 oq .. 8 oq + 7
+        f32x4 dsum[2];    // denominators of the rows 16 oq + 8 j + 4 h + (0..3)
+        if (ci > 0) {
+            const int c = ci - 1;
+            const XBuf& X = sm.xb[c & 1];
+            const u16* vt = sm.vt[c & 1];
+            // V fragment (kk, nt): k-slot e <-> token 16 kk + 8 (e/4) + 4 h + e%4,
+            // lane <-> column 32 nt + lo
+            auto vfrag = [&](int kk, int nt) {
+                return lds8(vt + (32 * nt + lo) * LDV + vt_col(32 * nt + lo, 16 * kk + 8 * h));
+            };
+            if (HAS_Q) {
+                bf16x8 fq[2][2], at[2];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) c = mfma(lds8(pk + 32 * mt + 16 * kk), fq[mt][kk], c);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    c[i] = 8 * (i >> 2) + (i & 3) <= keep_thr ? c[i] : 0.f;
-                    den += c[i];
-                }
-                at[0] = pack8(c, 0);
-                at[1] = pack8(c, 8);
-            }
-            den += __shfl_xor(den, 32, 64);
-            den_s[w][lo] = den; // both lane halves hold the full sum
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                // num tile nt: row 8(i/4) + 4h + i%4, column 32 nt + lo
-                f32x16 c = zero16();
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) c = mfma(fq[mt][kk], pack8(S[mt][nt], 8 * kk), c);
+                    for (int kk = 0; kk < 2; ++kk) fq[mt][kk] = X.fq[w][mt][kk][lane];
                 if (MODE == MODE_CAUSAL) {
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) c = mfma(at[kk], vfrag(kk, nt), c);
+                    at[0] = X.at[w][0][lane];
+                    at[1] = X.at[w][1][lane];
                 }
-                // blocks (nt, q) of the other waves go to LDS; this wave keeps (on, oq)
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    if (nt == on && q == oq) {
+                for (int j = 0; j < 2; ++j) {
+                    const int tb = 16 * oq + 8 * j + 4 * h;
+                    dsum[j] = *reinterpret_cast<const f32x4*>(&X.den[0][tb]);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) own[i] = c[8 * q + i];
-                    } else {
+                    for (int w2 = 1; w2 < NW; ++w2) {
+                        const f32x4 x = *reinterpret_cast<const f32x4*>(&X.den[w2][tb]);
+                        dsum[j][0] += x[0];
+                        dsum[j][1] += x[1];
+                        dsum[j][2] += x[2];
+                        dsum[j][3] += x[3];
+                    }
+                }
+                float(&red)[NW][NW - 1][2][64][4] = sm.red[c & 1];
 #pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const f32x4 x = {c[8 * q + 4 * j], c[8 * q + 4 * j + 1], c[8 * q + 4 * j + 2],
-                                             c[8 * q + 4 * j + 3]};
-                            *reinterpret_cast<f32x4*>(&red_s[nt][q][w][j][lane][0]) = x;
+                for (int nt = 0; nt < 2; ++nt) {
+                    // num tile nt: row 8(i/4) + 4h + i%4, column 32 nt + lo
+                    f32x16 acc = zero16();
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) acc = mfma(fq[mt][kk], pack8(S[mt][nt], 8 * kk), acc);
+                    if (MODE == MODE_CAUSAL) {
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) acc = mfma(at[kk], vfrag(kk, nt), acc);
+                    }
+                    // block (nt, q) belongs to consumer nt + 2 q; this wave keeps its own
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int owner = nt + 2 * q;
+                        if (owner == w) {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) own[i] = acc[8 * q + i];
+                        } else {
+                            const int slot = w < owner ? w : w - 1;
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                const f32x4 x = {acc[8 * q + 4 * j], acc[8 * q + 4 * j + 1],
+                                                 acc[8 * q + 4 * j + 2], acc[8 * q + 4 * j + 3]};
+                                *reinterpret_cast<f32x4*>(&red[owner][slot][j][lane][0]) = x;
+                            }
                         }
                     }
                 }
             }
-        }
-
-        asm volatile("" ::: "memory");
-
-        // ---- state update: S[F_w] += phi(K)^T V, z[F_w] += column sums ---------------
-        if (HAS_K) {
+            // ---- state update: S[F_g] += phi(K)^T V ----------------------------------
+            if (HAS_K) {
+                bf16x8 fk[2][2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+                    for (int kk = 0; kk < 2; ++kk) fk[mt][kk] = X.fk[w][mt][kk][lane];
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) S[mt][nt] = mfma(fk[mt][kk], vfrag(kk, nt), S[mt][nt]);
+                for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                zreg[nt] += zpart[nt] + __shfl_xor(zpart[nt], 32, 64);
-                if (MODE == MODE_CAUSAL) z_s[f0 + 32 * nt + lo] = zreg[nt];
+                    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) S[mt][nt] = mfma(fk[mt][kk], vfrag(kk, nt), S[mt][nt]);
             }
         }
+        sync_lds(); // partial blocks of all consumers in LDS; chunk ci handed over
 
-        if (HAS_Q) {
-            sync_lds(); // (B) partial blocks and denominators of all waves in LDS
+        if (HAS_Q && ci > 0) {
+            const int c = ci - 1;
+            const int64_t c0 = t0 + (int64_t)L * c;
+            const int rows = (int)min<int64_t>(L, t1 - c0);
+            const float(&red)[NW][NW - 1][2][64][4] = sm.red[c & 1];
 #pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) {
-                if (w2 == w) continue;
+            for (int s = 0; s < NW - 1; ++s)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(&red_s[on][oq][w2][j][lane][0]);
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(&red[w][s][j][lane][0]);
                     own[4 * j] += x[0];
                     own[4 * j + 1] += x[1];
                     own[4 * j + 2] += x[2];
                     own[4 * j + 3] += x[3];
                 }
+            if (a.norm == NORM_ATTN) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        own[4 * j + e] *= __builtin_amdgcn_rcpf(fmaxf(dsum[j][e], a.eps));
             }
-            u16* ob = a.out + (bh * a.N + c0) * DV + 32 * on + lo;
+            // the block (16 rows x 32 columns) goes out through LDS so that each lane
+            // stores 16 contiguous bytes of one row
+            u16* ot = sm.ot[w];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int tb = 16 * oq + 8 * j + 4 * h; // rows of regs 8 oq + 4 j .. + 3
-                f32x4 dsum = *reinterpret_cast<const f32x4*>(&den_s[0][tb]);
-#pragma unroll
-                for (int w2 = 1; w2 < NW; ++w2) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(&den_s[w2][tb]);
-                    dsum[0] += x[0];
-                    dsum[1] += x[1];
-                    dsum[2] += x[2];
-                    dsum[3] += x[3];
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float y = own[4 * j + e];
-                    if (a.norm == NORM_ATTN) y *= __builtin_amdgcn_rcpf(fmaxf(dsum[e], a.eps));
-                    own[4 * j + e] = y;
-                }
-            }
-            if (rows == L) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int t = 16 * oq + 8 * (i >> 2) + 4 * h + (i & 3);
-                    ob[(int64_t)t * DV] = __builtin_bit_cast(u16, (__bf16)own[i]);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int t = 16 * oq + 8 * (i >> 2) + 4 * h + (i & 3);
-                    if (t < rows) ob[(int64_t)t * DV] = __builtin_bit_cast(u16, (__bf16)own[i]);
-                }
-            }
-        }
-
-        // next chunk's V^T (its loads were issued above)
-        if (HAS_K && rows_next > 0) {
-            if (!PREFETCH) vr = load_v(vb + cn * DV, rows_next, tid);
-            store_vt(vt_s[buf ^ 1], tid, vr);
+            for (int i = 0; i < 8; ++i)
+                ot[(8 * (i >> 2) + 4 * h + (i & 3)) * 32 + lo] = __builtin_bit_cast(u16, (__bf16)own[i]);
+            const int orow = lane >> 2, ocol = 8 * (lane & 3); // same wave: LDS keeps its order
+            const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&ot[orow * 32 + ocol]);
+            const int t = 16 * oq + orow;
+            if (t < rows)
+                *reinterpret_cast<bf16x8*>(a.out + (bh * a.N + c0 + t) * DV + 32 * on + ocol) = ov;
         }
     }
 
@@ -480,11 +563,24 @@ __global__ __launch_bounds__(NT, MIN_WG_PER_CU) void k_favor_mfma(FavorArgs a) {
                     const int f = f0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
                     dst[(int64_t)f * DV + 32 * nt + lo] = S[mt][nt][i];
                 }
-        if (h == 0) {
-            dst[(int64_t)R * DV + f0 + lo] = zreg[0];
-            dst[(int64_t)R * DV + f0 + 32 + lo] = zreg[1];
-        }
     }
+}
+
+// Every wave of the workgroup runs nck + 1 iterations with one barrier each
+// (nck is uniform over the workgroup), whichever role it has.
+template <int MODE>
+__global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
+    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
+    const int64_t t0 = g * a.seg_len;
+    const int64_t t1 = min<int64_t>(a.N, t0 + a.seg_len);
+    const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
+    if (wv >= NW)
+        producer<MODE>(a, sm, wv - NW, lane, bh, g, t0, t1, nck);
+    else
+        consumer<MODE>(a, sm, wv, lane, bh, g, t0, t1, nck);
 }
 
 FavorArgs make_args(const Cfg& c, const void* q, const void* k, const void* v, const void* omega,

@@ -131,6 +131,17 @@ __device__ __forceinline__ void load_x(const u16* __restrict__ X, int rows, int 
         f[ks] = *reinterpret_cast<const bf16x8*>(X + (int64_t)t * D + 16 * ks + 8 * h);
 }
 
+// Sum of the eight bfloat16 elements, two per v_dot2 against (1, 1).
+__device__ __forceinline__ float sum8(const bf16x8& v) {
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    float s0 = 0.f, s1 = 0.f;
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[0], v[1]}, one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2], v[3]}, one, s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[4], v[5]}, one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[6], v[7]}, one, s1, false);
+    return s0 + s1;
+}
+
 // x[lane] + x[lane ^ 32]: the two lane halves exchanged by one
 // v_permlane32_swap (no LDS round trip).
 __device__ __forceinline__ float half_sum(float x) {
@@ -184,14 +195,14 @@ __device__ __forceinline__ bf16x8 omega_frag(const u16* __restrict__ omega, int 
 struct XBuf {
     bf16x8 fq[NW][2][2][64]; // phi(Q) as the A operand of the readout [g][feature tile][kk][lane]
     bf16x8 fk[NW][2][2][64]; // phi(K) as the A operand of the update  [g][feature tile][kk][lane]
-    bf16x8 at[NW][2][64];    // masked intra-chunk block over F_g, A operand of A V [g][kk][lane]
-    float den[NW][L];        // denominators over F_g, by token
+    float den[NW][L];        // phi(Q) z_{c-1} over F_g, by token
 };
 
 struct Smem {
     XBuf xb[2];                    // double-buffered by chunk
     u16 vt[2][DV * LDV];           // V^T of the chunk, double-buffered
     float red[2][NW][NW - 1][2][64][4]; // partial numerator blocks [buf][owner][sender slot][j][lane]
+    float dint[2][NW][L];          // denominators over F_g (readout + intra block) [buf][g][token]
     float z[R];                    // producer-private: z_{c-1}, by feature
     float kb[NW][L];               // producer-private: key biases by token
     u16 ot[NW][16 * 32];           // consumer-private: finished output block, bf16 rows
@@ -209,6 +220,15 @@ __device__ __forceinline__ bf16x8 eye_frag(int kk, int lo, int h) {
     return r;
 }
 
+// Producer of feature group p.  The projections of chunk c + 1 are issued
+// during iteration c, tile by tile between the exponentials of chunk c, so
+// that the exponentials of chunk c + 1 start as soon as the next iteration
+// does; inputs are loaded two chunks ahead of their exponentials (one chunk
+// ahead of their projection).  Every load in the loop
+// is issued unconditionally (past the last chunk it repeats the last one), so
+// the number of loads in flight is the same on every path and each wait
+// covers exactly the loads it needs: a data-dependent load count makes the
+// compiler drain all of them at the top of the loop.
 template <int MODE>
 __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, int lane, int64_t bh,
                                          int64_t g, int64_t t0, int64_t t1, int nck) {
@@ -238,101 +258,93 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
     const u16* qb = a.q + bh * a.N * D;
     const u16* kb = a.k + bh * a.N * D;
     const u16* vb = a.v + bh * a.N * DV;
+    auto rows_of = [&](int c) { return (int)min<int64_t>(L, t1 - t0 - (int64_t)L * c); };
 
-    // each chunk's inputs are loaded one chunk ahead
+    // projections of one chunk: P_K (token 8(i/4) + 4h + i%4, feature
+    // f0 + 32 nt + lo) with the key biases in LDS, P_Q^T (feature
+    // f0 + 32 mt + 8(i/4) + 4h + i%4, token lo) with the query bias in bq.
+    // Each tile of the next chunk is projected right after this chunk's
+    // exponentials have consumed the same tile, so the matrix core runs
+    // under the next tile's exponentials.
     bf16x8 qf[4], kf[4], vr;
+    f32x16 PK[2], PQ[2];
+    float bq = 0.f;
+    // keys past the end of the segment get bias -inf: exp2 gives exactly 0,
+    // so they add nothing to S, z or the intra-chunk block
+    auto key_bias = [&](int rows) {
+        const float bk = lo < rows ? fmaf(a.b_norm, sq_norm(kf), a.b_const) : -INFINITY;
+        sm.kb[p][lo] = bk; // both lane halves write the same value
+    };
+    auto project_k = [&](int nt) {
+        f32x16 c = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) c = mfma(kf[ks], om[nt][ks], c);
+        PK[nt] = c;
+    };
+    auto project_q = [&](int mt) {
+        f32x16 c = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) c = mfma(om[mt][ks], qf[ks], c);
+        PQ[mt] = c;
+    };
+    auto load_qk = [&](int c) {
+        const int rows = rows_of(c);
+        const int64_t c0 = t0 + (int64_t)L * c;
+        if (HAS_Q) load_x(qb + c0 * D, rows, lo, h, qf);
+        if (HAS_K) load_x(kb + c0 * D, rows, lo, h, kf);
+    };
+
     if (nck > 0) {
-        const int rows = (int)min<int64_t>(L, t1 - t0);
-        if (HAS_Q) load_x(qb + t0 * D, rows, lo, h, qf);
+        load_qk(0);
+        if (HAS_K) vr = load_v(vb + t0 * DV, rows_of(0), ptid);
         if (HAS_K) {
-            load_x(kb + t0 * D, rows, lo, h, kf);
-            vr = load_v(vb + t0 * DV, rows, ptid);
+            key_bias(rows_of(0));
+            project_k(0);
+            project_k(1);
         }
+        if (HAS_Q) {
+            bq = fmaf(a.b_norm, sq_norm(qf), a.b_const);
+            project_q(0);
+            project_q(1);
+        }
+        load_qk(min(1, nck - 1));
     }
 
-    // causal mask of the diagonal tile: element i of lane (lo, h) pairs query
-    // lo with key 8(i/4) + 4h + i%4, kept when 8(i/4) + i%4 <= lo - 4h
-    const int keep_thr = lo - 4 * h;
-
-    bf16x8 eye[2]; // transposition operands (causal intra-chunk block)
-    if (MODE == MODE_CAUSAL) {
-        eye[0] = eye_frag(0, lo, h);
-        eye[1] = eye_frag(1, lo, h);
-    }
-
-    for (int ci = 0; ci <= nck; ++ci) {
-        if (ci < nck) {
-            const int64_t c0 = t0 + (int64_t)L * ci;
-            const int rows = (int)min<int64_t>(L, t1 - c0);
-            const int64_t cn = c0 + L;
-            const int rows_next = cn < t1 ? (int)min<int64_t>(L, t1 - cn) : 0;
+    for (int ci = 0; ci < nck; ++ci) {
+        {
             XBuf& X = sm.xb[ci & 1];
-
-            // ---- projections: both sides' MFMAs first, so that the matrix core
-            // works while the exponentials of the key side run ---------------------
-            f32x16 PK[2], PQ[2];
-            float bq = 0.f;
-            if (HAS_K) {
-                // keys past the end of the segment get bias -inf: exp2 gives exactly 0,
-                // so they add nothing to S, z or the intra-chunk block
-                const float bk = lo < rows ? fmaf(a.b_norm, sq_norm(kf), a.b_const) : -INFINITY;
-                sm.kb[p][lo] = bk; // both lane halves write the same value
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x16 c = zero16();
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) c = mfma(kf[ks], om[nt][ks], c);
-                    PK[nt] = c; // token 8(i/4) + 4h + i%4, feature f0 + 32 nt + lo
-                }
-            }
-            if (HAS_Q) {
-                bq = fmaf(a.b_norm, sq_norm(qf), a.b_const);
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    f32x16 c = zero16();
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) c = mfma(om[mt][ks], qf[ks], c);
-                    PQ[mt] = c; // feature f0 + 32 mt + 8(i/4) + 4h + i%4, token lo
-                }
-            }
-            // the next chunk's inputs load while this one is computed
-            if (HAS_K) {
-                store_vt(sm.vt[ci & 1], ptid, vr);
-                if (rows_next > 0) {
-                    load_x(kb + cn * D, rows_next, lo, h, kf);
-                    vr = load_v(vb + cn * DV, rows_next, ptid);
-                }
-            }
-            if (HAS_Q && rows_next > 0) load_x(qb + cn * D, rows_next, lo, h, qf);
+            // the next chunk (the last one again after the end: its projections
+            // are then unused, and every iteration keeps the same shape)
+            const int cn = min(ci + 1, nck - 1);
 
             // ---- phi(K): exponentials, column sums, hand-off -----------------------
             float zpart[2] = {0.f, 0.f};
-            bf16x8 fk[2][2];
             if (HAS_K) {
+                store_vt(sm.vt[ci & 1], ptid, vr);
+                vr = load_v(vb + (t0 + (int64_t)L * cn) * DV, rows_of(cn), ptid);
                 f32x4 kbias[4]; // biases of the tokens 8 j + 4 h + (0..3)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     kbias[j] = *reinterpret_cast<const f32x4*>(&sm.kb[p][8 * j + 4 * h]);
+                key_bias(rows_of(cn)); // after this chunk's biases are read
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     f32x16& c = PK[nt];
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
                         c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
-                    float zs[2] = {0.f, 0.f};
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) zs[i & 1] += c[i];
-                    zpart[nt] = zs[0] + zs[1];
-                    fk[nt][0] = pack8(c, 0);
-                    fk[nt][1] = pack8(c, 8);
-                    X.fk[p][nt][0][lane] = fk[nt][0];
-                    X.fk[p][nt][1][lane] = fk[nt][1];
+                    const bf16x8 k0 = pack8(c, 0), k1 = pack8(c, 8);
+                    X.fk[p][nt][0][lane] = k0;
+                    X.fk[p][nt][1][lane] = k1;
+                    // z sums the bfloat16 features that also enter S
+                    zpart[nt] = sum8(k0) + sum8(k1);
+                    project_k(nt);
                 }
             }
 
-            // ---- phi(Q), its denominators against z_{c-1}, the intra-chunk block ----
+            // ---- phi(Q) and its denominators against z_{c-1} ------------------------
             if (HAS_Q) {
-                bf16x8 fq[2][2]; // [feature tile][kk]
+                const float bq_next = fmaf(a.b_norm, sq_norm(qf), a.b_const);
                 float den[2] = {0.f, 0.f};
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
@@ -347,39 +359,12 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
                         c[i] = y;
                         den[i & 1] = fmaf(y, zq[i >> 2][i & 3], den[i & 1]);
                     }
-                    fq[mt][0] = pack8(c, 0);
-                    fq[mt][1] = pack8(c, 8);
-                    X.fq[p][mt][0][lane] = fq[mt][0];
-                    X.fq[p][mt][1][lane] = fq[mt][1];
-                }
-                if (MODE == MODE_CAUSAL) {
-                    // phi(K) with tokens on lanes: the transposition of fk through the
-                    // matrix core; lane (j, h), k-slot e <-> feature
-                    // f0 + 32 mt + 16 kk + 8(e/4) + 4h + e%4, as in fq
-                    bf16x8 kt[2][2];
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        f32x16 c = zero16();
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) c = mfma(fk[nt][kk], eye[kk], c);
-                        kt[nt][0] = pack8(c, 0);
-                        kt[nt][1] = pack8(c, 8);
-                    }
-                    // masked block, transposed: c[i] = A[lo][j], j = 8(i/4) + 4h + i%4, over F_g
-                    f32x16 c = zero16();
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) c = mfma(kt[mt][kk], fq[mt][kk], c);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        c[i] = 8 * (i >> 2) + (i & 3) <= keep_thr ? c[i] : 0.f;
-                        den[i & 1] += c[i];
-                    }
-                    X.at[p][0][lane] = pack8(c, 0);
-                    X.at[p][1][lane] = pack8(c, 8);
+                    X.fq[p][mt][0][lane] = pack8(c, 0);
+                    X.fq[p][mt][1][lane] = pack8(c, 8);
+                    project_q(mt);
                 }
                 X.den[p][lo] = half_sum(den[0] + den[1]); // both lane halves hold the full sum
+                bq = bq_next;
             }
 
             // ---- z[F_g] += column sums of phi(K_c), after the queries read z_{c-1} ----
@@ -390,9 +375,14 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
                     if (MODE == MODE_CAUSAL) sm.z[f0 + 32 * nt + lo] = zreg[nt];
                 }
             }
+
+            // the chunk after the next starts loading
+            load_qk(min(ci + 2, nck - 1));
+
         }
         sync_lds(); // chunk ci handed over; the consumers are done with chunk ci - 1
     }
+    sync_lds(); // the consumers' last chunk
 
     if (MODE == MODE_SUMS && h == 0) {
         float* dst = a.state + bh * a.st_bh + g * a.st_g;
@@ -401,15 +391,73 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
     }
 }
 
+// Output block (ON, OQ) of chunk c -- rows [16 OQ, 16 OQ + 16), columns
+// [32 ON, 32 ON + 32) -- finished by consumer ON + 2 OQ: its own partial
+// (registers 8 OQ .. 8 OQ + 7 of tile ON) plus the other three groups'
+// partials from LDS, divided by the summed denominators, then stored as
+// bfloat16 rows through LDS so that each lane writes 16 contiguous bytes.
+template <int ON, int OQ>
+__device__ __forceinline__ void finish_block(const FavorArgs& a, Smem& sm, const f32x16 (&acc)[2],
+                                             int lane, int c, int64_t bh, int64_t c0, int rows) {
+    constexpr int W = ON + 2 * OQ;
+    const int lo = lane & 31, h = lane >> 5;
+    // every LDS read first, then one wait: the partials and denominators were
+    // all written before the barrier
+    const float(&red)[NW][NW - 1][2][64][4] = sm.red[c & 1];
+    f32x4 part[NW - 1][2], dpart[2][NW];
+#pragma unroll
+    for (int s = 0; s < NW - 1; ++s)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) part[s][j] = *reinterpret_cast<const f32x4*>(&red[W][s][j][lane][0]);
+    if (a.norm == NORM_ATTN) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) // rows 16 OQ + 8 j + 4 h + (0..3)
+                dpart[j][w2] = *reinterpret_cast<const f32x4*>(&sm.dint[c & 1][w2][16 * OQ + 8 * j + 4 * h]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float own[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        own[i] = acc[ON][8 * OQ + i];
+#pragma unroll
+        for (int s = 0; s < NW - 1; ++s) own[i] += part[s][i >> 2][i & 3];
+    }
+    if (a.norm == NORM_ATTN) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float dsum = (dpart[i >> 2][0][i & 3] + dpart[i >> 2][1][i & 3]) +
+                               (dpart[i >> 2][2][i & 3] + dpart[i >> 2][3][i & 3]);
+            own[i] *= __builtin_amdgcn_rcpf(fmaxf(dsum, a.eps));
+        }
+    }
+    u16* ot = sm.ot[W];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const bf16x2 pr = {(__bf16)own[i], (__bf16)own[i + 1]};
+        const uint32_t u = __builtin_bit_cast(uint32_t, pr);
+        const int r = 8 * (i >> 2) + 4 * h + (i & 3); // rows r and r + 1
+        ot[r * 32 + lo] = (u16)(u & 0xffffu);
+        ot[(r + 1) * 32 + lo] = (u16)(u >> 16);
+    }
+    const int orow = lane >> 2, ocol = 8 * (lane & 3); // same wave: LDS keeps its order
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&ot[orow * 32 + ocol]);
+    const int t = 16 * OQ + orow;
+    if (t < rows) *reinterpret_cast<bf16x8*>(a.out + (bh * a.N + c0 + t) * DV + 32 * ON + ocol) = ov;
+}
+
+// Consumer of feature group w: owns S[F_w, :]; for chunk c (one behind the
+// producers) it forms the group's masked intra-chunk block, the partial
+// numerator and the state update, then finishes one quarter of the output.
 template <int MODE>
 __device__ __forceinline__ void consumer(const FavorArgs& a, Smem& sm, int w, int lane, int64_t bh,
                                          int64_t g, int64_t t0, int64_t t1, int nck) {
     constexpr bool HAS_K = MODE != MODE_READOUT;
     constexpr bool HAS_Q = MODE != MODE_SUMS;
+    constexpr bool CAUSAL = MODE == MODE_CAUSAL;
     const int lo = lane & 31, h = lane >> 5;
     const int f0 = 64 * w;
-    // this wave finishes rows [16 oq, 16 oq + 16) of output tile on (columns 32 on + ..)
-    const int on = w & 1, oq = w >> 1;
 
     // State slice S[F_g, :] in accumulator layout: element i of S[mt][nt]
     // is S[f0 + 32 mt + 8 (i/4) + 4 h + i%4][32 nt + lo].
@@ -431,10 +479,17 @@ __device__ __forceinline__ void consumer(const FavorArgs& a, Smem& sm, int w, in
                     S[mt][nt][i] = st[(int64_t)f * DV + 32 * nt + lo];
                 }
     }
+    bf16x8 eye[2];
+    if (CAUSAL) {
+        eye[0] = eye_frag(0, lo, h);
+        eye[1] = eye_frag(1, lo, h);
+    }
+    // causal mask of the diagonal tile: element i of lane (lo, h) pairs query
+    // lo with key 8(i/4) + 4h + i%4, kept when 8(i/4) + i%4 <= lo - 4h
+    const int keep_thr = lo - 4 * h;
 
     for (int ci = 0; ci <= nck; ++ci) {
-        f32x16 own;       // rows 16 oq .. of output tile on, in regs 8 oq .. 8 oq + 7
-        f32x4 dsum[2];    // denominators of the rows 16 oq + 8 j + 4 h + (0..3)
+        f32x16 acc[2];    // partial numerator tiles: row 8(i/4) + 4h + i%4, column 32 nt + lo
         if (ci > 0) {
             const int c = ci - 1;
             const XBuf& X = sm.xb[c & 1];
@@ -444,68 +499,84 @@ __device__ __forceinline__ void consumer(const FavorArgs& a, Smem& sm, int w, in
             auto vfrag = [&](int kk, int nt) {
                 return lds8(vt + (32 * nt + lo) * LDV + vt_col(32 * nt + lo, 16 * kk + 8 * h));
             };
-            if (HAS_Q) {
-                bf16x8 fq[2][2], at[2];
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) fq[mt][kk] = X.fq[w][mt][kk][lane];
-                if (MODE == MODE_CAUSAL) {
-                    at[0] = X.at[w][0][lane];
-                    at[1] = X.at[w][1][lane];
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int tb = 16 * oq + 8 * j + 4 * h;
-                    dsum[j] = *reinterpret_cast<const f32x4*>(&X.den[0][tb]);
-#pragma unroll
-                    for (int w2 = 1; w2 < NW; ++w2) {
-                        const f32x4 x = *reinterpret_cast<const f32x4*>(&X.den[w2][tb]);
-                        dsum[j][0] += x[0];
-                        dsum[j][1] += x[1];
-                        dsum[j][2] += x[2];
-                        dsum[j][3] += x[3];
-                    }
-                }
-                float(&red)[NW][NW - 1][2][64][4] = sm.red[c & 1];
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    // num tile nt: row 8(i/4) + 4h + i%4, column 32 nt + lo
-                    f32x16 acc = zero16();
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) acc = mfma(fq[mt][kk], pack8(S[mt][nt], 8 * kk), acc);
-                    if (MODE == MODE_CAUSAL) {
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) acc = mfma(at[kk], vfrag(kk, nt), acc);
-                    }
-                    // block (nt, q) belongs to consumer nt + 2 q; this wave keeps its own
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int owner = nt + 2 * q;
-                        if (owner == w) {
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) own[i] = acc[8 * q + i];
-                        } else {
-                            const int slot = w < owner ? w : w - 1;
-#pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                const f32x4 x = {acc[8 * q + 4 * j], acc[8 * q + 4 * j + 1],
-                                                 acc[8 * q + 4 * j + 2], acc[8 * q + 4 * j + 3]};
-                                *reinterpret_cast<f32x4*>(&red[owner][slot][j][lane][0]) = x;
-                            }
-                        }
-                    }
-                }
-            }
-            // ---- state update: S[F_g] += phi(K)^T V ----------------------------------
+            bf16x8 fk[2][2];
             if (HAS_K) {
-                bf16x8 fk[2][2];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) fk[mt][kk] = X.fk[w][mt][kk][lane];
+            }
+            if (HAS_Q) {
+                bf16x8 fq[2][2];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) fq[mt][kk] = X.fq[w][mt][kk][lane];
+                float den = X.den[w][lo]; // phi(Q) z_{c-1} over F_g of query lo
+                bf16x8 at[2];
+                if (CAUSAL) {
+                    // phi(K) with tokens on lanes (transposed through the matrix core):
+                    // lane (j, h), k-slot e <-> feature f0 + 32 mt + 16 kk + 8(e/4) + 4h + e%4,
+                    // as in fq
+                    bf16x8 kt[2][2];
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        f32x16 t = zero16();
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) t = mfma(fk[mt][kk], eye[kk], t);
+                        kt[mt][0] = pack8(t, 0);
+                        kt[mt][1] = pack8(t, 8);
+                    }
+                    // masked block over F_g, transposed: m[i] = A[lo][j], j = 8(i/4) + 4h + i%4
+                    f32x16 m = zero16();
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) m = mfma(kt[mt][kk], fq[mt][kk], m);
+                    float rs[2] = {0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        m[i] = 8 * (i >> 2) + (i & 3) <= keep_thr ? m[i] : 0.f;
+                        rs[i & 1] += m[i];
+                    }
+                    den += half_sum(rs[0] + rs[1]);
+                    at[0] = pack8(m, 0);
+                    at[1] = pack8(m, 8);
+                }
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    acc[nt] = zero16();
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) acc[nt] = mfma(fq[mt][kk], pack8(S[mt][nt], 8 * kk), acc[nt]);
+                }
+                if (CAUSAL) {
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) acc[nt] = mfma(at[kk], vfrag(kk, nt), acc[nt]);
+                }
+                sm.dint[c & 1][w][lo] = den; // both lane halves hold the full sum
+                // block (nt, q) belongs to consumer nt + 2 q; this wave keeps its own
+                float(&red)[NW][NW - 1][2][64][4] = sm.red[c & 1];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int owner = nt + 2 * q;
+                        if (owner == w) continue;
+                        const int slot = w < owner ? w : w - 1;
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const f32x4 x = {acc[nt][8 * q + 4 * j], acc[nt][8 * q + 4 * j + 1],
+                                             acc[nt][8 * q + 4 * j + 2], acc[nt][8 * q + 4 * j + 3]};
+                            *reinterpret_cast<f32x4*>(&red[owner][slot][j][lane][0]) = x;
+                        }
+                    }
+            }
+            // ---- state update: S[F_g] += phi(K)^T V ----------------------------------
+            if (HAS_K) {
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -520,35 +591,13 @@ __device__ __forceinline__ void consumer(const FavorArgs& a, Smem& sm, int w, in
             const int c = ci - 1;
             const int64_t c0 = t0 + (int64_t)L * c;
             const int rows = (int)min<int64_t>(L, t1 - c0);
-            const float(&red)[NW][NW - 1][2][64][4] = sm.red[c & 1];
-#pragma unroll
-            for (int s = 0; s < NW - 1; ++s)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(&red[w][s][j][lane][0]);
-                    own[4 * j] += x[0];
-                    own[4 * j + 1] += x[1];
-                    own[4 * j + 2] += x[2];
-                    own[4 * j + 3] += x[3];
-                }
-            if (a.norm == NORM_ATTN) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        own[4 * j + e] *= __builtin_amdgcn_rcpf(fmaxf(dsum[j][e], a.eps));
+            // block indices as constants: the block's registers are then fixed
+            switch (w) {
+            case 0: finish_block<0, 0>(a, sm, acc, lane, c, bh, c0, rows); break;
+            case 1: finish_block<1, 0>(a, sm, acc, lane, c, bh, c0, rows); break;
+            case 2: finish_block<0, 1>(a, sm, acc, lane, c, bh, c0, rows); break;
+            default: finish_block<1, 1>(a, sm, acc, lane, c, bh, c0, rows); break;
             }
-            // the block (16 rows x 32 columns) goes out through LDS so that each lane
-            // stores 16 contiguous bytes of one row
-            u16* ot = sm.ot[w];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                ot[(8 * (i >> 2) + 4 * h + (i & 3)) * 32 + lo] = __builtin_bit_cast(u16, (__bf16)own[i]);
-            const int orow = lane >> 2, ocol = 8 * (lane & 3); // same wave: LDS keeps its order
-            const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&ot[orow * 32 + ocol]);
-            const int t = 16 * oq + orow;
-            if (t < rows)
-                *reinterpret_cast<bf16x8*>(a.out + (bh * a.N + c0 + t) * DV + 32 * on + ocol) = ov;
         }
     }
 

@@ -189,6 +189,25 @@ __device__ __forceinline__ bf16x8 omega_frag(const u16* __restrict__ omega, int 
     return *reinterpret_cast<const bf16x8*>(omega + (int64_t)(f0 + 32 * t + lo) * D + 16 * ks + 8 * h);
 }
 
+// Swizzled LDS copy of one chunk of 32 rows x 64 bfloat16 (4 KB): row t,
+// 16-byte column block j is stored at block index 8t + (j ^ (t & 7)), so that
+// the MFMA operand reads (row = lane, one block per lane) hit all banks.
+__device__ __forceinline__ int xs_index(int t, int j) { return 8 * t + (j ^ (t & 7)); }
+
+// Thread th (of 256) loads block th of the chunk: row th / 8, block
+// (th % 8) ^ (row % 8), i.e. the block it will store at index th.  Rows past
+// `rows` repeat row rows-1.
+__device__ __forceinline__ bf16x8 load_block(const u16* __restrict__ X, int rows, int th) {
+    const int t = th >> 3, j = (th & 7) ^ (t & 7);
+    return *reinterpret_cast<const bf16x8*>(X + (int64_t)min(t, rows - 1) * D + 8 * j);
+}
+
+// f[ks] = X[lo][16 ks + 8 h .. +7] from the swizzled copy (as load_x).
+__device__ __forceinline__ void lds_x(const bf16x8* xs, int lo, int h, bf16x8 (&f)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) f[ks] = xs[xs_index(lo, 2 * ks + h)];
+}
+
 // One chunk's hand-off from the producers to the consumers, per feature
 // group g; every operand is stored lane-linear, so each side moves it with one
 // 16-byte LDS access per lane.
@@ -200,6 +219,8 @@ struct XBuf {
 
 struct Smem {
     XBuf xb[2];                    // double-buffered by chunk
+    bf16x8 xq[3][256];             // producer-shared: swizzled q chunks, three in flight
+    bf16x8 xk[3][256];             // producer-shared: swizzled k chunks
     u16 vt[2][DV * LDV];           // V^T of the chunk, double-buffered
     float red[2][NW][NW - 1][2][64][4]; // partial numerator blocks [buf][owner][sender slot][j][lane]
     float dint[2][NW][L];          // denominators over F_g (readout + intra block) [buf][g][token]
@@ -223,12 +244,12 @@ __device__ __forceinline__ bf16x8 eye_frag(int kk, int lo, int h) {
 // Producer of feature group p.  The projections of chunk c + 1 are issued
 // during iteration c, tile by tile between the exponentials of chunk c, so
 // that the exponentials of chunk c + 1 start as soon as the next iteration
-// does; inputs are loaded two chunks ahead of their exponentials (one chunk
-// ahead of their projection).  Every load in the loop
-// is issued unconditionally (past the last chunk it repeats the last one), so
-// the number of loads in flight is the same on every path and each wait
-// covers exactly the loads it needs: a data-dependent load count makes the
-// compiler drain all of them at the top of the loop.
+// does.  q and k reach the producers through LDS (loaded once per
+// workgroup, three chunks ahead of their exponentials).  Every global load
+// in the loop is issued unconditionally (past the last chunk it repeats the
+// last one), so the number of loads in flight is the same on every path and
+// each wait covers exactly the loads it needs: a data-dependent load count
+// makes the compiler drain all of them at the top of the loop.
 template <int MODE>
 __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, int lane, int64_t bh,
                                          int64_t g, int64_t t0, int64_t t1, int nck) {
@@ -287,16 +308,38 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
         for (int ks = 0; ks < 4; ++ks) c = mfma(om[mt][ks], qf[ks], c);
         PQ[mt] = c;
     };
-    auto load_qk = [&](int c) {
-        const int rows = rows_of(c);
-        const int64_t c0 = t0 + (int64_t)L * c;
-        if (HAS_Q) load_x(qb + c0 * D, rows, lo, h, qf);
-        if (HAS_K) load_x(kb + c0 * D, rows, lo, h, kf);
+    // q and k chunks are loaded once for the four producers (one 16-byte
+    // block per thread) into a ring of three swizzled LDS copies: chunk c + 2
+    // is stored during iteration c from registers loaded one iteration
+    // earlier, and the projections of chunk c + 1 read their fragments
+    auto chunk_ptr = [&](const u16* base, int c) { return base + (t0 + (int64_t)L * c) * D; };
+    bf16x8 qr, kr; // staged blocks
+    auto stage_load = [&](int c) {
+        if (HAS_Q) qr = load_block(chunk_ptr(qb, c), rows_of(c), ptid);
+        if (HAS_K) kr = load_block(chunk_ptr(kb, c), rows_of(c), ptid);
+    };
+    auto stage_store = [&](int c) {
+        if (HAS_Q) sm.xq[c % 3][ptid] = qr;
+        if (HAS_K) sm.xk[c % 3][ptid] = kr;
+    };
+    auto frags = [&](int c) {
+        if (HAS_Q) lds_x(sm.xq[c % 3], lo, h, qf);
+        if (HAS_K) lds_x(sm.xk[c % 3], lo, h, kf);
     };
 
     if (nck > 0) {
-        load_qk(0);
+        stage_load(0);
+        stage_store(0);
+        if (nck > 1) {
+            stage_load(1);
+            stage_store(1);
+        }
+        stage_load(min(2, nck - 1));
         if (HAS_K) vr = load_v(vb + t0 * DV, rows_of(0), ptid);
+    }
+    sync_lds(); // chunks 0 and 1 staged (the consumers wait here once as well)
+    if (nck > 0) {
+        frags(0);
         if (HAS_K) {
             key_bias(rows_of(0));
             project_k(0);
@@ -307,7 +350,6 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
             project_q(0);
             project_q(1);
         }
-        load_qk(min(1, nck - 1));
     }
 
     for (int ci = 0; ci < nck; ++ci) {
@@ -316,6 +358,9 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
             // the next chunk (the last one again after the end: its projections
             // are then unused, and every iteration keeps the same shape)
             const int cn = min(ci + 1, nck - 1);
+            frags(cn);
+            if (ci + 2 < nck) stage_store(ci + 2);
+            stage_load(min(ci + 3, nck - 1));
 
             // ---- phi(K): exponentials, column sums, hand-off -----------------------
             float zpart[2] = {0.f, 0.f};
@@ -376,8 +421,6 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
                 }
             }
 
-            // the chunk after the next starts loading
-            load_qk(min(ci + 2, nck - 1));
 
         }
         sync_lds(); // chunk ci handed over; the consumers are done with chunk ci - 1
@@ -488,6 +531,7 @@ __device__ __forceinline__ void consumer(const FavorArgs& a, Smem& sm, int w, in
     // lo with key 8(i/4) + 4h + i%4, kept when 8(i/4) + i%4 <= lo - 4h
     const int keep_thr = lo - 4 * h;
 
+    sync_lds(); // matches the producers' staging barrier
     for (int ci = 0; ci <= nck; ++ci) {
         f32x16 acc[2];    // partial numerator tiles: row 8(i/4) + 4h + i%4, column 32 nt + lo
         if (ci > 0) {
@@ -632,6 +676,95 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
         consumer<MODE>(a, sm, wv, lane, bh, g, t0, t1, nck);
 }
 
+// Segment sums (increments of S and z) with eight symmetric waves: wave w
+// owns the 32 features F_w = [32w, 32w + 32) and, per chunk, projects the
+// keys on its rows of omega, takes the exponentials and adds
+// phi(K)[:, F_w]^T V to its slice of S in MFMA accumulators.  Nothing is
+// reduced across waves; the chunk's keys and V^T are loaded once per
+// workgroup by waves 0..3 and staged in LDS (one barrier per chunk), and
+// every wave has the same mix of matrix-core and vector work.
+constexpr int NT8 = 512;
+__global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
+    __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LDV];
+    __shared__ bf16x8 ks_s[2][256];
+    __shared__ __attribute__((aligned(16))) float kb_s[8][L];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lo = lane & 31, h = lane >> 5;
+    const int f0 = 32 * w;
+    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
+    const int64_t t0 = g * a.seg_len;
+    const int64_t t1 = min<int64_t>(a.N, t0 + a.seg_len);
+    const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
+    auto rows_of = [&](int c) { return (int)min<int64_t>(L, t1 - t0 - (int64_t)L * c); };
+    const bool stager = w < 4; // waves 0..3 (threads 0..255) stage K and V^T
+
+    bf16x8 om[4]; // omega[f0 + lo][16 ks + 8 h ..]
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) om[ks] = omega_frag(a.omega, f0, 0, ks, lo, h);
+    f32x16 S[2] = {zero16(), zero16()}; // S[f0 + 8(i/4) + 4h + i%4][32 nt + lo]
+    float zacc = 0.f;                   // z[f0 + lo]
+
+    const u16* kb = a.k + bh * a.N * D;
+    const u16* vb = a.v + bh * a.N * DV;
+    auto kchunk = [&](int c) { return kb + (t0 + (int64_t)L * c) * D; };
+    auto vchunk = [&](int c) { return vb + (t0 + (int64_t)L * c) * DV; };
+    // stagers hold the keys of chunk c + 1 and the values of chunk c in
+    // registers at the top of iteration c
+    bf16x8 kr, vr;
+    if (nck > 0 && stager) {
+        ks_s[0][tid] = load_block(kchunk(0), rows_of(0), tid);
+        const int c1 = min(1, nck - 1);
+        kr = load_block(kchunk(c1), rows_of(c1), tid);
+        vr = load_v(vchunk(0), rows_of(0), tid);
+    }
+    sync_lds(); // keys of chunk 0 staged
+
+    for (int ci = 0; ci < nck; ++ci) {
+        const int rows = rows_of(ci);
+        if (stager) {
+            // past the end: the last chunk again, so every iteration has the same loads
+            const int c1 = min(ci + 1, nck - 1), c2 = min(ci + 2, nck - 1);
+            ks_s[(ci + 1) & 1][tid] = kr;
+            store_vt(vt_s[ci & 1], tid, vr);
+            kr = load_block(kchunk(c2), rows_of(c2), tid);
+            vr = load_v(vchunk(c1), rows_of(c1), tid);
+        }
+        bf16x8 kf[4];
+        lds_x(ks_s[ci & 1], lo, h, kf);
+        // keys past the end of the segment get bias -inf (exp2 gives 0)
+        kb_s[w][lo] = lo < rows ? fmaf(a.b_norm, sq_norm(kf), a.b_const) : -INFINITY;
+        f32x16 c = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) c = mfma(kf[ks], om[ks], c); // token 8(i/4)+4h+i%4, feature f0+lo
+        f32x4 kbias[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kbias[j] = *reinterpret_cast<const f32x4*>(&kb_s[w][8 * j + 4 * h]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
+        const bf16x8 fk0 = pack8(c, 0), fk1 = pack8(c, 8);
+        zacc += sum8(fk0) + sum8(fk1); // the bfloat16 features that also enter S
+        sync_lds(); // V^T of this chunk and the keys of the next staged
+        const u16* vt = vt_s[ci & 1];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int n = 32 * nt + lo;
+            S[nt] = mfma(fk0, lds8(vt + n * LDV + vt_col(n, 8 * h)), S[nt]);
+            S[nt] = mfma(fk1, lds8(vt + n * LDV + vt_col(n, 16 + 8 * h)), S[nt]);
+        }
+    }
+    float* dst = a.state + bh * a.st_bh + g * a.st_g;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int f = f0 + 8 * (i >> 2) + 4 * h + (i & 3);
+            dst[(int64_t)f * DV + 32 * nt + lo] = S[nt][i];
+        }
+    const float zt = half_sum(zacc);
+    if (h == 0) dst[(int64_t)R * DV + f0 + lo] = zt;
+}
+
 FavorArgs make_args(const Cfg& c, const void* q, const void* k, const void* v, const void* omega,
                     Shape s, SegPlan sp, float* state, int64_t sbh, int64_t sg, void* out) {
     FavorArgs a;
@@ -664,7 +797,7 @@ hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const v
                              Shape s, SegPlan sp, float* ws, hipStream_t st) {
     const FavorArgs a = make_args(c, nullptr, k, v, omega, s, sp, ws, sp.G * state_elems(R),
                                   state_elems(R), nullptr);
-    hipLaunchKernelGGL(k_favor_mfma<MODE_SUMS>, dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(k_favor_sums8, dim3((unsigned)(sp.G * s.BH)), dim3(NT8), 0, st, a);
     return hipGetLastError();
 }
 

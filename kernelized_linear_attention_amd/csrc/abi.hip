@@ -226,7 +226,7 @@ int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void*
     hipError_t e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
     if (e == hipSuccess)
         e = launch_segment_scan(p->r, s, ss, state_in ? S : nullptr, state_in ? z : nullptr, inc,
-                                1, S, z, nullptr, st);
+                                (int)sp.sub, S, z, nullptr, st);
     // segment g starts at sub-segment g * sub: its carried-in state is that prefix
     if (e == hipSuccess)
         e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, ss.G * E, sp.sub * E, out, st);

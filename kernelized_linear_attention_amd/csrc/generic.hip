@@ -193,10 +193,11 @@ __global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict_
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const float* __restrict__ S0,
                                                      const float* __restrict__ z0,
-                                                     float* __restrict__ ws, int write_prefix,
+                                                     float* __restrict__ ws, int prefix_stride,
                                                      float* __restrict__ S_fin,
                                                      float* __restrict__ z_fin,
                                                      float* __restrict__ fin) {
+    constexpr int BATCH = 16;
     const int64_t E = state_elems(r);
     const int64_t blocks_per_head = (E + NT - 1) / NT;
     const int64_t bh = blockIdx.x / blocks_per_head;
@@ -206,16 +207,20 @@ __global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const flo
     float run = 0.f;
     if (S0) run = e < rdv ? S0[bh * rdv + e] : z0[bh * r + (e - rdv)];
     float* p = ws + bh * G * E + e;
-    // batches of 8 independent loads, then the fixed-order running sum
-    for (int64_t g0 = 0; g0 < G; g0 += 8) {
-        const int n = (int)min<int64_t>(8, G - g0);
-        float a[8];
+    // batches of independent loads (the scan is latency-bound: one element per
+    // thread), then the fixed-order running sum; the exclusive prefix is
+    // written back only for the segments that read it (every prefix_stride-th;
+    // the stride is a power of two)
+    const int64_t pmask = prefix_stride - 1;
+    for (int64_t g0 = 0; g0 < G; g0 += BATCH) {
+        const int n = (int)min<int64_t>(BATCH, G - g0);
+        float a[BATCH];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = i < n ? p[(g0 + i) * E] : 0.f;
+        for (int i = 0; i < BATCH; ++i) a[i] = i < n ? p[(g0 + i) * E] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < BATCH; ++i) {
             if (i < n) {
-                if (write_prefix) p[(g0 + i) * E] = run;
+                if (prefix_stride > 0 && ((g0 + i) & pmask) == 0) p[(g0 + i) * E] = run;
                 run += a[i];
             }
         }
@@ -455,11 +460,11 @@ hipError_t launch_segment_sums(const Cfg& c, int dtype, const void* k, const voi
 }
 
 hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, const float* z0,
-                               float* ws, int write_prefix, float* S_fin, float* z_fin,
+                               float* ws, int prefix_stride, float* S_fin, float* z_fin,
                                float* fin, hipStream_t st) {
     const int64_t E = state_elems(r);
     const dim3 grid((unsigned)(((E + NT - 1) / NT) * s.BH));
-    hipLaunchKernelGGL(k_segment_scan, grid, dim3(NT), 0, st, r, sp.G, S0, z0, ws, write_prefix,
+    hipLaunchKernelGGL(k_segment_scan, grid, dim3(NT), 0, st, r, sp.G, S0, z0, ws, prefix_stride,
                        S_fin, z_fin, fin);
     return hipGetLastError();
 }

@@ -57,11 +57,12 @@ hipError_t launch_featuremap(const Cfg& c, int dtype, const void* x, const void*
 hipError_t launch_segment_sums(const Cfg& c, int dtype, const void* k, const void* v,
                                const void* omega, Shape s, SegPlan sp, float* ws, hipStream_t st);
 
-// Prefix over segments.  Reads S0/z0 (may be NULL = zero), turns ws[bh][g]
-// into the exclusive prefix when write_prefix, and writes the total to
+// Prefix over segments.  Reads S0/z0 (may be NULL = zero), overwrites
+// ws[bh][g] with the exclusive prefix for every g that is a multiple of
+// prefix_stride (a power of two; none when 0), and writes the total to
 // S_fin / z_fin / fin (each may be NULL).
 hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, const float* z0,
-                               float* ws, int write_prefix, float* S_fin, float* z_fin,
+                               float* ws, int prefix_stride, float* S_fin, float* z_fin,
                                float* fin, hipStream_t st);
 
 // Outputs of every segment.  causal: chunked recurrence from the segment's

@@ -78,6 +78,7 @@ extern "C" {
 /* Operation ids for lin_attn_workspace_bytes. */
 #define LIN_ATTN_OP_BIDIR 1
 #define LIN_ATTN_OP_CAUSAL 2
+#define LIN_ATTN_OP_CAUSAL_VARLEN 3
 
 /*
  * Method parameters, shared by every call.
@@ -168,6 +169,35 @@ int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void*
                             void* stream);
 
 /*
+ * Causal prefill of a packed batch: num_seqs independent sequences laid end
+ * to end along the token axis, the state reset at every sequence boundary
+ * ([RF] par. 4: packing must reset the state at the logical boundary).
+ * Sequence i is tokens [cu_seqlens[i], cu_seqlens[i+1]) of every head and
+ * runs the recurrence of lin_attn_causal_chunked from its own state.
+ *   q, k        [H, total, d]; v, out [H, total, dv] (head-major, tokens of
+ *               all sequences packed), input dtype.
+ *   cu_seqlens  device int32 [num_seqs + 1]: nondecreasing, cu_seqlens[0] = 0,
+ *               cu_seqlens[num_seqs] = total (4-byte aligned).  It is read on
+ *               the device only, so the call stays asynchronous and is not
+ *               checked on the host: values are clamped to [0, total] there,
+ *               and malformed boundaries give unspecified results but no
+ *               access out of bounds.  Empty sequences are allowed.
+ *   S, z        float32 [num_seqs, H, r, dv] / [num_seqs, H, r], required,
+ *               in/out: each sequence's initial state when state_in == 1
+ *               (else zero), its final state after the call (the carry into
+ *               a following call).
+ *   ws          at least lin_attn_workspace_bytes(LIN_ATTN_OP_CAUSAL_VARLEN,
+ *               p, num_seqs, H, total, d, dv, 0) bytes; the library plans the
+ *               segments into it on the device.
+ * Errors as lin_attn_causal_chunked; tokens with num_seqs == 0 are invalid.
+ */
+int lin_attn_causal_varlen(const lin_attn_params* p, const void* q, const void* k,
+                           const void* v, const int32_t* cu_seqlens, int64_t num_seqs,
+                           int64_t H, int64_t total, int64_t d, int64_t dv, const void* omega,
+                           float* S, float* z, int32_t state_in, void* out, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
  * One decode step for B*H single tokens ([KZ] sec. 1.2 steps 2-3; [RF]
  * par. 3 "streaming causal calculation"):
  *   S += phi(k) v^T;  z += phi(k);  out = readout of phi(q) against (S, z).
@@ -179,8 +209,9 @@ int lin_attn_decode_step(const lin_attn_params* p, const void* q, const void* k,
                          const void* omega, float* S, float* z, void* out, void* stream);
 
 /*
- * Workspace bytes needed by lin_attn_bidir (op = LIN_ATTN_OP_BIDIR) or
- * lin_attn_causal_chunked (op = LIN_ATTN_OP_CAUSAL) for these arguments.
+ * Workspace bytes needed by lin_attn_bidir (op = LIN_ATTN_OP_BIDIR),
+ * lin_attn_causal_chunked (op = LIN_ATTN_OP_CAUSAL) or, with B = num_seqs and
+ * N = total, lin_attn_causal_varlen (op = LIN_ATTN_OP_CAUSAL_VARLEN).
  * Host-only, deterministic in its arguments (independent of the device).
  * Returns 0 for invalid arguments.
  */

@@ -27,10 +27,12 @@ NORM = {"attn": 0, "none": 1}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 OP_BIDIR = 1
 OP_CAUSAL = 2
+OP_CAUSAL_VARLEN = 3
 ABI_VERSION = 1
 
 # Every symbol include/lin_attn.h declares.
 EXPORTS = ("lin_attn_featuremap", "lin_attn_bidir", "lin_attn_causal_chunked",
+           "lin_attn_causal_varlen",
            "lin_attn_decode_step", "lin_attn_workspace_bytes", "lin_attn_strerror",
            "lin_attn_abi_version")
 
@@ -54,6 +56,9 @@ _lib.lin_attn_bidir.restype = ctypes.c_int
 _lib.lin_attn_causal_chunked.argtypes = [_PP, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I32,
                                          _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]
 _lib.lin_attn_causal_chunked.restype = ctypes.c_int
+_lib.lin_attn_causal_varlen.argtypes = [_PP, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
+                                        _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]
+_lib.lin_attn_causal_varlen.restype = ctypes.c_int
 _lib.lin_attn_decode_step.argtypes = [_PP, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.lin_attn_decode_step.restype = ctypes.c_int
 _lib.lin_attn_workspace_bytes.argtypes = [_I32, _PP, _I64, _I64, _I64, _I64, _I64, _I32]
@@ -212,6 +217,43 @@ def lin_attn_causal_chunked(q, k, v, kind, *, omega=None, nu=1, sum_norm=False, 
                                       _ptr(om), int(chunk), _ptr(S), _ptr(z), int(bool(state_in)),
                                       _ptr(out), _ptr(ws), ws_bytes, _stream(q.device, stream))
     _check("lin_attn_causal_chunked", rc)
+    return out, S, z
+
+
+def lin_attn_causal_varlen(q, k, v, cu_seqlens, kind, *, omega=None, nu=1, sum_norm=False,
+                           norm="attn", scale=1.0, eps=1e-6, n_seg=0, S=None, z=None,
+                           state_in=False, out=None, workspace=None, stream=None):
+    """Causal prefill of packed sequences.  q, k [H, total, d], v [H, total, dv];
+    cu_seqlens int32 [num_seqs + 1] on the device.  Returns (out, S, z) with
+    S [num_seqs, H, r, dv], z [num_seqs, H, r] (updated in place when given,
+    read first when state_in)."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t, q.dtype)
+    _dev_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    H, total, d = q.shape
+    dv = v.shape[-1]
+    num_seqs = cu_seqlens.numel() - 1
+    om = _omega(kind, omega, q.dtype)
+    r = feature_width(kind, d, nu, om)
+    p = make_params(kind, r, nu=nu, sum_norm=sum_norm, norm=norm, dtype=q.dtype, scale=scale,
+                    eps=eps, n_seg=n_seg)
+    if S is None:
+        if state_in:
+            raise ValueError("state_in needs S and z")
+        S = torch.empty((num_seqs, H, r, dv), dtype=torch.float32, device=q.device)
+        z = torch.empty((num_seqs, H, r), dtype=torch.float32, device=q.device)
+    _dev_tensor("S", S, torch.float32)
+    _dev_tensor("z", z, torch.float32)
+    if out is None:
+        out = torch.empty((H, total, dv), dtype=q.dtype, device=q.device)
+    _dev_tensor("out", out, q.dtype)
+    ws, ws_bytes = _workspace(OP_CAUSAL_VARLEN, p, num_seqs, H, total, d, dv, 0, q.device,
+                              workspace)
+    rc = _lib.lin_attn_causal_varlen(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
+                                     num_seqs, H, total, d, dv, _ptr(om), _ptr(S), _ptr(z),
+                                     int(bool(state_in)), _ptr(out), _ptr(ws), ws_bytes,
+                                     _stream(q.device, stream))
+    _check("lin_attn_causal_varlen", rc)
     return out, S, z
 
 

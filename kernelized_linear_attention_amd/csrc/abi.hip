@@ -101,6 +101,32 @@ hipError_t segment_outputs(const lin_attn_params* p, const Cfg& c, int causal, c
                                                 sbh, sg, out, st);
 }
 
+// Packed batch (lin_attn_causal_varlen): the uniform planner over all tokens
+// of a head fixes the segment length; every sequence adds at most one
+// partial segment, which bounds the segment table.  Workspace: increments
+// (float32) [H][parts][E], then the table int64 [parts][2], then the first
+// part of every sequence int64 [num_seqs + 1].
+struct VarlenLayout {
+    SegPlan sp;        // G = segment capacity per head, seg_len, sub
+    int64_t parts;     // table capacity (segments x sub)
+    size_t tab_off, first_off, bytes;
+};
+
+VarlenLayout varlen_layout(const lin_attn_params* p, int64_t num_seqs, int64_t H, int64_t total) {
+    VarlenLayout L;
+    L.sp = plan_for(p, H, total);
+    L.sp.G = (total + L.sp.seg_len - 1) / L.sp.seg_len + num_seqs;
+    L.parts = L.sp.G * L.sp.sub;
+    size_t off = (size_t)(H * L.parts * state_elems(p->r)) * sizeof(float);
+    off = (off + 255) & ~(size_t)255;
+    L.tab_off = off;
+    off += (size_t)L.parts * 2 * sizeof(int64_t);
+    L.first_off = off;
+    off += (size_t)(num_seqs + 1) * sizeof(int64_t);
+    L.bytes = off;
+    return L;
+}
+
 } // namespace
 
 extern "C" {
@@ -121,13 +147,15 @@ const char* lin_attn_strerror(int32_t code) {
 size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B, int64_t H,
                                 int64_t N, int64_t d, int64_t dv, int32_t chunk) {
     (void)chunk;
-    if (op != LIN_ATTN_OP_BIDIR && op != LIN_ATTN_OP_CAUSAL) return 0;
+    if (op != LIN_ATTN_OP_BIDIR && op != LIN_ATTN_OP_CAUSAL && op != LIN_ATTN_OP_CAUSAL_VARLEN)
+        return 0;
     if (!p || check_sizes(B, H, N) != LIN_ATTN_OK) return 0;
     // omega is not needed to size the workspace: check the rest with a dummy
     const int rc = check_params(p, d, dv, reinterpret_cast<const void*>(uintptr_t(16)));
     if (rc != LIN_ATTN_OK) return 0;
     const int64_t BH = B * H;
     if (BH == 0 || N == 0) return 0;
+    if (op == LIN_ATTN_OP_CAUSAL_VARLEN) return varlen_layout(p, B, H, N).bytes;
     return ws_floats(op, BH, plan_for(p, BH, N), p->r) * sizeof(float);
 }
 
@@ -228,6 +256,58 @@ int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void*
         e = launch_segment_scan(p->r, s, ss, state_in ? S : nullptr, state_in ? z : nullptr, inc,
                                 (int)sp.sub, S, z, nullptr, st);
     // segment g starts at sub-segment g * sub: its carried-in state is that prefix
+    if (e == hipSuccess)
+        e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, ss.G * E, sp.sub * E, out, st);
+    return launch_status(e);
+}
+
+int lin_attn_causal_varlen(const lin_attn_params* p, const void* q, const void* k,
+                           const void* v, const int32_t* cu_seqlens, int64_t num_seqs,
+                           int64_t H, int64_t total, int64_t d, int64_t dv, const void* omega,
+                           float* S, float* z, int32_t state_in, void* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+    int rc = check_params(p, d, dv, omega);
+    if (rc == LIN_ATTN_ERR_INVALID) return rc;
+    const int rs = check_sizes(num_seqs, H, total);
+    if (rs == LIN_ATTN_ERR_INVALID) return rs;
+    if (state_in != 0 && state_in != 1) return LIN_ATTN_ERR_INVALID;
+    if (num_seqs == 0 && total > 0) return LIN_ATTN_ERR_INVALID; // tokens of no sequence
+    if (!opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
+    if (num_seqs * H > 0 && (!ptr_ok(S) || !ptr_ok(z))) return LIN_ATTN_ERR_INVALID;
+    if (num_seqs > 0 && (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3)))
+        return LIN_ATTN_ERR_INVALID;
+    if (H > 0 && total > 0 && (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out)))
+        return LIN_ATTN_ERR_INVALID;
+    if (rc != LIN_ATTN_OK) return rc;
+    if (rs != LIN_ATTN_OK) return rs;
+    if (num_seqs * H == 0) return LIN_ATTN_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (total == 0) {
+        // no token in any sequence: every final state is the starting state
+        if (state_in) return LIN_ATTN_OK;
+        hipError_t e = launch_fill_zero(S, num_seqs * H * (int64_t)p->r * DV, st);
+        if (e == hipSuccess) e = launch_fill_zero(z, num_seqs * H * (int64_t)p->r, st);
+        return launch_status(e);
+    }
+    const VarlenLayout L = varlen_layout(p, num_seqs, H, total);
+    if (ws_bytes < L.bytes || !ws) return LIN_ATTN_ERR_WORKSPACE;
+
+    const Cfg c = make_cfg(p);
+    const Shape s{H, total};
+    float* inc = (float*)ws;
+    int64_t* tab = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + L.tab_off);
+    int64_t* first = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + L.first_off);
+    SegPlan sp = L.sp;
+    sp.tab = tab;
+    const SegPlan ss = sums_plan(sp);
+    const int64_t E = state_elems(p->r);
+    hipError_t e = launch_varlen_plan(cu_seqlens, num_seqs, total, sp.seg_len, sp.sub, L.parts, tab,
+                                      first, st);
+    if (e == hipSuccess) e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
+    if (e == hipSuccess)
+        e = launch_segment_scan_varlen(p->r, H, num_seqs, L.parts, first, state_in ? S : nullptr,
+                                       state_in ? z : nullptr, inc, (int)sp.sub, S, z, st);
+    // segment g starts at part g * sub: its carried-in state is that prefix
     if (e == hipSuccess)
         e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, ss.G * E, sp.sub * E, out, st);
     return launch_status(e);

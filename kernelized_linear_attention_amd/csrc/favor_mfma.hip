@@ -71,6 +71,8 @@ struct FavorArgs {
     int64_t st_bh;
     int64_t st_g;
     u16* out;
+    const int64_t* tab; // segment table (packed sequences) or NULL
+    int64_t tsub;       // parts per segment in the table
 };
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
@@ -667,8 +669,8 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
     const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
-    const int64_t t0 = g * a.seg_len;
-    const int64_t t1 = min<int64_t>(a.N, t0 + a.seg_len);
+    int64_t t0, t1;
+    seg_range(a.tab, a.tsub, g, a.seg_len, a.N, t0, t1);
     const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
     if (wv >= NW)
         producer<MODE>(a, sm, wv - NW, lane, bh, g, t0, t1, nck);
@@ -693,8 +695,8 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
     const int lo = lane & 31, h = lane >> 5;
     const int f0 = 32 * w;
     const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
-    const int64_t t0 = g * a.seg_len;
-    const int64_t t1 = min<int64_t>(a.N, t0 + a.seg_len);
+    int64_t t0, t1;
+    seg_range(a.tab, a.tsub, g, a.seg_len, a.N, t0, t1);
     const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
     auto rows_of = [&](int c) { return (int)min<int64_t>(L, t1 - t0 - (int64_t)L * c); };
     const bool stager = w < 4; // waves 0..3 (threads 0..255) stage K and V^T
@@ -784,6 +786,8 @@ FavorArgs make_args(const Cfg& c, const void* q, const void* k, const void* v, c
     a.st_bh = sbh;
     a.st_g = sg;
     a.out = (u16*)out;
+    a.tab = sp.tab;
+    a.tsub = sp.sub;
     return a;
 }
 

@@ -135,6 +135,7 @@ __global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict_
                                                      const T* __restrict__ v,
                                                      const T* __restrict__ omega, int64_t N,
                                                      int64_t G, int64_t seg_len,
+                                                     const int64_t* __restrict__ tab,
                                                      float* __restrict__ ws) {
     constexpr int L = 64;
     constexpr int R = 32 * FPT;
@@ -146,7 +147,8 @@ __global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict_
     const int tid = threadIdx.x;
     const int fb = tid / 8, nb = tid % 8;
     const int64_t bh = blockIdx.x / G, g = blockIdx.x % G;
-    const int64_t t0 = g * seg_len, t1 = min<int64_t>(N, t0 + seg_len);
+    int64_t t0, t1;
+    seg_range(tab, 1, g, seg_len, N, t0, t1);
 
     float acc[FPT][8];
     float zacc[FPT];
@@ -234,6 +236,104 @@ __global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const flo
 }
 
 // ---------------------------------------------------------------------------
+// Packed sequences: the segment table and the per-sequence prefix.
+// ---------------------------------------------------------------------------
+// One workgroup walks the sequences NT at a time: each thread counts its
+// sequence's parts, a workgroup scan turns the counts into offsets, and the
+// thread writes its parts.  Every range is clamped to [0, total] and every
+// index to cap, whatever cu_seqlens holds.
+__global__ __launch_bounds__(NT) void k_varlen_plan(const int32_t* __restrict__ cu, int64_t num_seqs,
+                                                    int64_t total, int64_t seg_len, int64_t sub,
+                                                    int64_t cap, int64_t* __restrict__ tab,
+                                                    int64_t* __restrict__ first) {
+    __shared__ int64_t cnt_s[NT];
+    __shared__ int64_t base_s;
+    const int tid = threadIdx.x;
+    const int64_t part_len = seg_len / sub;
+    if (tid == 0) base_s = 0;
+    __syncthreads();
+    for (int64_t i0 = 0; i0 < num_seqs; i0 += NT) {
+        const int64_t i = i0 + tid;
+        int64_t s0 = 0, s1 = 0, n = 0;
+        if (i < num_seqs) {
+            s0 = min<int64_t>(max<int64_t>(cu[i], 0), total);
+            s1 = min<int64_t>(max<int64_t>(cu[i + 1], s0), total);
+            n = (s1 - s0 + seg_len - 1) / seg_len * sub;
+        }
+        cnt_s[tid] = n;
+        __syncthreads();
+        for (int off = 1; off < NT; off <<= 1) { // inclusive scan of the counts
+            const int64_t x = tid >= off ? cnt_s[tid - off] : 0;
+            __syncthreads();
+            cnt_s[tid] += x;
+            __syncthreads();
+        }
+        const int64_t base = base_s;
+        const int64_t e0 = base + cnt_s[tid] - n;
+        if (i < num_seqs) {
+            first[i] = min<int64_t>(e0, cap);
+            for (int64_t j = 0; j < n && e0 + j < cap; ++j) {
+                const int64_t a = s0 + j * part_len;
+                tab[2 * (e0 + j)] = min<int64_t>(a, s1);
+                tab[2 * (e0 + j) + 1] = min<int64_t>(a + part_len, s1);
+            }
+        }
+        __syncthreads();
+        if (tid == NT - 1) base_s = base + cnt_s[NT - 1];
+        __syncthreads();
+    }
+    const int64_t used = min<int64_t>(base_s, cap);
+    if (tid == 0) first[num_seqs] = used;
+    for (int64_t e = used + tid; e < cap; e += NT) {
+        tab[2 * e] = 0;
+        tab[2 * e + 1] = 0;
+    }
+}
+
+// Like k_segment_scan, over the parts of one sequence of one head: a
+// sequence starts from its own state, so the carry resets at every sequence
+// boundary.  Block (element block, h, i).
+__global__ __launch_bounds__(NT) void k_segment_scan_varlen(int r, int64_t H, int64_t parts,
+                                                            const int64_t* __restrict__ first,
+                                                            const float* __restrict__ S0,
+                                                            const float* __restrict__ z0,
+                                                            float* __restrict__ ws, int prefix_stride,
+                                                            float* __restrict__ S_fin,
+                                                            float* __restrict__ z_fin) {
+    constexpr int BATCH = 16;
+    const int64_t E = state_elems(r);
+    const int64_t bpe = (E + NT - 1) / NT;
+    const int64_t rest = blockIdx.x / bpe;
+    const int64_t h = rest % H, i = rest / H;
+    const int64_t e = (blockIdx.x % bpe) * NT + threadIdx.x;
+    if (e >= E) return;
+    const int64_t rdv = (int64_t)r * DV;
+    const int64_t sh = i * H + h;
+    float run = 0.f;
+    if (S0) run = e < rdv ? S0[sh * rdv + e] : z0[sh * r + (e - rdv)];
+    const int64_t g0 = first[i], g1 = first[i + 1];
+    float* p = ws + h * parts * E + e;
+    const int64_t pmask = prefix_stride - 1;
+    for (int64_t gb = g0; gb < g1; gb += BATCH) {
+        const int n = (int)min<int64_t>(BATCH, g1 - gb);
+        float a[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) a[j] = j < n ? p[(gb + j) * E] : 0.f;
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            if (j < n) {
+                if (prefix_stride > 0 && ((gb + j - g0) & pmask) == 0) p[(gb + j) * E] = run;
+                run += a[j];
+            }
+        }
+    }
+    if (e < rdv)
+        S_fin[sh * rdv + e] = run;
+    else
+        z_fin[sh * r + (e - rdv)] = run;
+}
+
+// ---------------------------------------------------------------------------
 // Segment outputs.  CAUSAL: chunked recurrence from the carried-in state;
 // otherwise: readout of every token against the full summary.
 // ---------------------------------------------------------------------------
@@ -243,6 +343,7 @@ __global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restri
                                                         const T* __restrict__ v,
                                                         const T* __restrict__ omega, int64_t N,
                                                         int64_t G, int64_t seg_len,
+                                                        const int64_t* __restrict__ tab, int64_t sub,
                                                         const float* __restrict__ state,
                                                         int64_t st_bh, int64_t st_g,
                                                         T* __restrict__ out) {
@@ -260,7 +361,8 @@ __global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restri
     __shared__ float nrm_s[L], rs_s[L];
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x / G, g = blockIdx.x % G;
-    const int64_t t0 = g * seg_len, t1 = min<int64_t>(N, t0 + seg_len);
+    int64_t t0, t1;
+    seg_range(tab, sub, g, seg_len, N, t0, t1);
 
     const float* sin = state + bh * st_bh + g * st_g;
     for (int e = tid; e < R * DV; e += NT) S_s[e] = sin[e];
@@ -379,7 +481,8 @@ template <typename T, int FPT>
 void sums_fpt(const Cfg& c, const void* k, const void* v, const void* omega, Shape s, SegPlan sp,
               float* ws, hipStream_t st) {
     hipLaunchKernelGGL((k_segment_sums<T, FPT>), dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0, st,
-                       c, (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G, sp.seg_len, ws);
+                       c, (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G, sp.seg_len, sp.tab,
+                       ws);
 }
 
 template <typename T>
@@ -407,11 +510,11 @@ void outputs_fpt(const Cfg& c, int causal, const void* q, const void* k, const v
     if (causal)
         hipLaunchKernelGGL((k_segment_outputs<T, FPT, true>), grid, block, 0, st, c, (const T*)q,
                            (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G, sp.seg_len,
-                           state, sbh, sg, (T*)out);
+                           sp.tab, sp.sub, state, sbh, sg, (T*)out);
     else
         hipLaunchKernelGGL((k_segment_outputs<T, FPT, false>), grid, block, 0, st, c,
                            (const T*)q, (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G,
-                           sp.seg_len, state, sbh, sg, (T*)out);
+                           sp.seg_len, sp.tab, sp.sub, state, sbh, sg, (T*)out);
 }
 
 template <typename T>
@@ -466,6 +569,25 @@ hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, cons
     const dim3 grid((unsigned)(((E + NT - 1) / NT) * s.BH));
     hipLaunchKernelGGL(k_segment_scan, grid, dim3(NT), 0, st, r, sp.G, S0, z0, ws, prefix_stride,
                        S_fin, z_fin, fin);
+    return hipGetLastError();
+}
+
+hipError_t launch_varlen_plan(const int32_t* cu_seqlens, int64_t num_seqs, int64_t total,
+                              int64_t seg_len, int64_t sub, int64_t cap, int64_t* tab,
+                              int64_t* first, hipStream_t st) {
+    hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(NT), 0, st, cu_seqlens, num_seqs, total,
+                       seg_len, sub, cap, tab, first);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_scan_varlen(int r, int64_t H, int64_t num_seqs, int64_t parts,
+                                      const int64_t* first, const float* S0, const float* z0,
+                                      float* ws, int prefix_stride, float* S_fin, float* z_fin,
+                                      hipStream_t st) {
+    const int64_t E = state_elems(r);
+    const dim3 grid((unsigned)(((E + NT - 1) / NT) * H * num_seqs));
+    hipLaunchKernelGGL(k_segment_scan_varlen, grid, dim3(NT), 0, st, r, H, parts, first, S0, z0, ws,
+                       prefix_stride, S_fin, z_fin);
     return hipGetLastError();
 }
 

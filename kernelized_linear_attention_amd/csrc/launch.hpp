@@ -22,10 +22,14 @@ struct SegPlan {
     int64_t G;       // segments per head (one workgroup each for the outputs)
     int64_t seg_len; // tokens per segment
     int64_t sub;     // the state increments are summed over seg_len / sub tokens
+    // Segment table (device), or NULL for uniform segments: part e covers
+    // tokens [tab[2e], tab[2e+1]) of every head and segment g is parts
+    // g*sub .. g*sub + sub - 1 (packed sequences, see launch_varlen_plan).
+    const int64_t* tab = nullptr;
 };
 
 // The plan of the increment and prefix kernels: sub-segments as segments.
-inline SegPlan sums_plan(SegPlan p) { return SegPlan{p.G * p.sub, p.seg_len / p.sub, 1}; }
+inline SegPlan sums_plan(SegPlan p) { return SegPlan{p.G * p.sub, p.seg_len / p.sub, 1, p.tab}; }
 
 inline SegPlan plan_segments(int64_t BH, int64_t N, int32_t n_seg_req, int64_t target_blocks) {
     SegPlan p{1, N, 1};
@@ -42,6 +46,18 @@ inline SegPlan plan_segments(int64_t BH, int64_t N, int32_t n_seg_req, int64_t t
 
 // Elements of one (S | z) state block: r*dv floats of S followed by r of z.
 __host__ __device__ inline int64_t state_elems(int r) { return (int64_t)r * DV + r; }
+
+// Token range [t0, t1) of segment g of a head with N tokens (see SegPlan).
+__device__ __forceinline__ void seg_range(const int64_t* tab, int64_t sub, int64_t g,
+                                          int64_t seg_len, int64_t N, int64_t& t0, int64_t& t1) {
+    if (tab) {
+        t0 = tab[2 * g * sub];
+        t1 = tab[2 * (g * sub + sub - 1) + 1];
+    } else {
+        t0 = g * seg_len;
+        t1 = t0 + seg_len < N ? t0 + seg_len : N;
+    }
+}
 
 struct Shape {
     int64_t BH; // batch * heads
@@ -72,6 +88,26 @@ hipError_t launch_segment_outputs(const Cfg& c, int dtype, int causal, const voi
                                   const void* k, const void* v, const void* omega, Shape s,
                                   SegPlan sp, const float* state, int64_t state_bh_stride,
                                   int64_t state_g_stride, void* out, hipStream_t st);
+
+// Segment table of a packed batch: sequence i covers tokens
+// [cu_seqlens[i], cu_seqlens[i+1]) of every head and is cut into
+// ceil(len / seg_len) segments of `sub` parts of seg_len / sub tokens (tail
+// parts may be empty).  Writes tab[2e], tab[2e+1] for the cap parts (unused
+// ones empty) and first[i] = first part of sequence i (first[num_seqs] = parts
+// used).  Ranges are clamped to [0, total] and the count to cap, so malformed
+// boundaries cannot send a later kernel out of bounds.  One workgroup.
+hipError_t launch_varlen_plan(const int32_t* cu_seqlens, int64_t num_seqs, int64_t total,
+                              int64_t seg_len, int64_t sub, int64_t cap, int64_t* tab,
+                              int64_t* first, hipStream_t st);
+
+// Prefix over the parts of every (sequence, head): parts first[i] ..
+// first[i+1]-1 of head h in ws[h][.], starting from S0/z0[(i*H + h)] (or
+// zero), exclusive prefix written at every prefix_stride-th part of the
+// sequence, final state to S_fin/z_fin[(i*H + h)].
+hipError_t launch_segment_scan_varlen(int r, int64_t H, int64_t num_seqs, int64_t parts,
+                                      const int64_t* first, const float* S0, const float* z0,
+                                      float* ws, int prefix_stride, float* S_fin, float* z_fin,
+                                      hipStream_t st);
 
 // p[0, n) = 0 with a plain kernel (capturable into a graph).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);

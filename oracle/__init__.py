@@ -15,6 +15,8 @@ Definitions followed (see the header of oracle.c for the passages):
   * bidirectional form: "Reassociate a feature-map kernel..." first paragraph,
     Performer page sec. 2 step 5;
   * causal recurrence and decode: Kernel Zoo sec. 1.2-1.3 and 5.4;
+  * packed sequences: the causal recurrence per sequence, the state reset at
+    each boundary ("Reassociate a feature-map kernel..." par. 4);
   * explicit N x N form: the interactive chapter's "rescan every key".
 """
 import ctypes
@@ -151,6 +153,37 @@ def causal(q, k, v, kind, *, omega=None, nu=1, sum_norm=False, norm="attn",
                             int(state_in), _ptr(S), _ptr(z), _ptr(out))
     if rc:
         raise ValueError("oracle causal: invalid argument")
+    return out, S, z
+
+
+def causal_varlen(q, k, v, cu_seqlens, kind, *, omega=None, nu=1, sum_norm=False,
+                  norm="attn", scale=1.0, eps=1e-6, S0=None, z0=None):
+    """Causal recurrence over sequences packed along the token axis: q, k
+    [H, total, d], v [H, total, dv], cu_seqlens [num_seqs + 1].  Sequence i
+    (tokens cu_seqlens[i] .. cu_seqlens[i+1] - 1 of every head) runs the
+    recurrence of causal() from zero, or from (S0[i], z0[i]), and nothing
+    carries from one sequence to the next (packing resets the state at the
+    boundary, "Reassociate a feature-map kernel..." par. 4).
+    Returns out [H, total, dv], S [num_seqs, H, r, dv], z [num_seqs, H, r]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = [int(x) for x in cu_seqlens]
+    n = len(cu) - 1
+    H, total, d = q.shape
+    dv = v.shape[-1]
+    r = feature_dim(kind, d, nu, omega)
+    if cu[0] != 0 or cu[-1] != total or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must rise from 0 to total")
+    if (S0 is None) != (z0 is None):
+        raise ValueError("give both S0 and z0, or neither")
+    out = np.zeros((H, total, dv))
+    S = np.zeros((n, H, r, dv))
+    z = np.zeros((n, H, r))
+    for i in range(n):
+        a, b = cu[i], cu[i + 1]
+        kw = {} if S0 is None else dict(S0=_f64(S0)[i], z0=_f64(z0)[i])
+        o, S[i], z[i] = causal(q[:, a:b], k[:, a:b], v[:, a:b], kind, omega=omega, nu=nu,
+                               sum_norm=sum_norm, norm=norm, scale=scale, eps=eps, **kw)
+        out[:, a:b] = o
     return out, S, z
 
 

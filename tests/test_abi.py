@@ -56,6 +56,7 @@ def test_constants_match_header():
     assert d["LIN_ATTN_F32"] == 0 and d["LIN_ATTN_BF16"] == 1
     assert d["LIN_ATTN_OP_BIDIR"] == binding.OP_BIDIR
     assert d["LIN_ATTN_OP_CAUSAL"] == binding.OP_CAUSAL
+    assert d["LIN_ATTN_OP_CAUSAL_VARLEN"] == binding.OP_CAUSAL_VARLEN
     assert (d["LIN_ATTN_OK"], d["LIN_ATTN_ERR_INVALID"], d["LIN_ATTN_ERR_UNSUPPORTED"],
             d["LIN_ATTN_ERR_WORKSPACE"], d["LIN_ATTN_ERR_HIP"]) == (0, -1, -2, -3, -4)
 
@@ -98,6 +99,12 @@ def causal(p, B=1, H=2, N=100, d=64, dv=64, ptr=FAKE, omega=FAKE, chunk=0, state
            ws_bytes=1 << 40, S=FAKE, z=FAKE):
     return lib.lin_attn_causal_chunked(ctypes.byref(p), ptr, ptr, ptr, B, H, N, d, dv, omega, chunk,
                                        S, z, state_in, ptr, ws, ws_bytes, None)
+
+
+def varlen(p, num_seqs=2, H=2, total=100, d=64, dv=64, ptr=FAKE, cu=FAKE, omega=FAKE, state_in=0,
+           ws=FAKE, ws_bytes=1 << 40, S=FAKE, z=FAKE):
+    return lib.lin_attn_causal_varlen(ctypes.byref(p), ptr, ptr, ptr, cu, num_seqs, H, total, d, dv,
+                                      omega, S, z, state_in, ptr, ws, ws_bytes, None)
 
 
 def decode(p, B=4, H=2, d=64, dv=64, ptr=FAKE, omega=FAKE):
@@ -194,3 +201,38 @@ def test_workspace_size_formula():
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p1, 2, 3, 1000, 64, 64) == 6 * 2 * E * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 2, 3, 0, 64, 64) == 0
     assert binding.lin_attn_workspace_bytes(9, p, 2, 3, 10, 64, 64) == 0
+
+
+def test_varlen_arguments():
+    p = params()
+    assert varlen(p, num_seqs=-1) == INVALID
+    assert varlen(p, total=-1) == INVALID
+    assert varlen(p, num_seqs=0, total=10) == INVALID   # tokens of no sequence
+    assert varlen(p, cu=None) == INVALID
+    assert varlen(p, cu=FAKE + 2) == INVALID            # int32 array: 4-byte alignment
+    assert varlen(p, state_in=2) == INVALID
+    assert varlen(p, S=None) == INVALID
+    assert varlen(p, ptr=None) == INVALID
+    assert varlen(params("favor", r=512)) == UNSUPPORTED
+    need = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 2, 2, 100, 64, 64)
+    assert need > 0
+    assert varlen(p, ws_bytes=need - 8) == WORKSPACE
+    assert varlen(p, ws=None, ws_bytes=0) == WORKSPACE
+    assert varlen(p, num_seqs=0, total=0) == OK
+    assert varlen(p, H=0) == OK
+
+
+def test_varlen_workspace_formula():
+    """Increments of every part of every head -- the segments of the uniform
+    plan over all tokens plus one partial segment per sequence, two parts each
+    on the matrix-core path -- then the segment table (two int64 per part,
+    after 256-byte alignment) and the first part of every sequence."""
+    p = params()
+    E = 256 * 64 + 256
+    # H = 8, total = 65536: 32 segments of 2048 tokens per head, + 4 sequences
+    parts = (32 + 4) * 2
+    inc = 8 * parts * E * 4
+    assert inc % 256 == 0
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 4, 8, 65536, 64, 64) == \
+        inc + parts * 16 + 5 * 8
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 4, 8, 0, 64, 64) == 0

@@ -282,3 +282,71 @@ def test_workload_favor_decode_layers(gpu_lib):
         assert_parity(out, ro, 2e-2, f"C5 layer {layer} out")
         assert_parity(S, rS, 2e-2, f"C5 layer {layer} S")
         assert_parity(z, rz, 2e-2, f"C5 layer {layer} z")
+
+
+# ---------------------------------------------------------------- packed sequences
+VARLEN_LENS = [70, 0, 1, 33, 150, 64]   # empty, one-token, ragged and multi-segment sequences
+
+
+def _packed(wid, lens, kind, dtype, r, nu, H=2, rep=0):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    c = Case(wid, 1, H, int(cu[-1]), kind, dtype, r=r, nu=nu, rep=rep)
+    q, k, v = c.q[0], c.k[0], c.v[0]                       # [H, total, d]
+    return c, q, k, v, cu, torch.from_numpy(cu).to("cuda")
+
+
+@pytest.mark.parametrize("kind,dtype,r,nu,sum_norm,scale", MAPS, ids=MAP_IDS)
+def test_causal_varlen(gpu_lib, kind, dtype, r, nu, sum_norm, scale):
+    norm = "none" if kind == "identity" else "attn"
+    c, q, k, v, cu, cu_d = _packed(105, VARLEN_LENS, kind, dtype, r, nu)
+    kw = dict(sum_norm=sum_norm, scale=scale, norm=norm)
+    out, S, z = gpu_lib.lin_attn_causal_varlen(q, k, v, cu_d, kind, **c.gkw(**kw))
+    ro, rS, rz = oracle.causal_varlen(c.qh[0], c.kh[0], c.vh[0], cu, kind, **c.okw(**kw))
+    tol = TOL[dtype]
+    assert_parity(out, ro, tol, "varlen out", lead_dims=1)
+    assert_parity(S, rS, tol, "varlen S")
+    assert_parity(z, rz, tol, "varlen z")
+
+
+@pytest.mark.parametrize("kind,dtype,r", [("favor", torch.bfloat16, 256), ("elu1", torch.float32, 64)])
+def test_causal_varlen_from_carried_states(gpu_lib, kind, dtype, r):
+    """Each sequence continues from its own state (carry across calls)."""
+    c, q, k, v, cu, cu_d = _packed(106, [40, 0, 97], kind, dtype, r, 1)
+    g = np.random.default_rng(107)
+    S0 = np.abs(g.standard_normal((3, 2, r, 64))).astype(np.float32)
+    z0 = np.abs(g.standard_normal((3, 2, r))).astype(np.float32) + 1.0
+    S = torch.from_numpy(S0).to("cuda")
+    z = torch.from_numpy(z0).to("cuda")
+    scale = 64 ** -0.25 if kind == "favor" else 1.0
+    out, S, z = gpu_lib.lin_attn_causal_varlen(q, k, v, cu_d, kind, S=S, z=z, state_in=True,
+                                               **c.gkw(scale=scale))
+    ro, rS, rz = oracle.causal_varlen(c.qh[0], c.kh[0], c.vh[0], cu, kind, S0=S0, z0=z0,
+                                      **c.okw(scale=scale))
+    tol = TOL[dtype]
+    assert_parity(out, ro, tol, "varlen carried out", lead_dims=1)
+    assert_parity(S, rS, tol, "varlen carried S")
+    assert_parity(z, rz, tol, "varlen carried z")
+
+
+def test_causal_varlen_one_sequence_matches_chunked(gpu_lib):
+    c, q, k, v, cu, cu_d = _packed(108, [1000], "favor", torch.bfloat16, 256, 1, H=3)
+    kw = c.gkw(scale=64 ** -0.25)
+    out, S, z = gpu_lib.lin_attn_causal_varlen(q, k, v, cu_d, "favor", **kw)
+    o2, S2, z2 = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, "favor", **kw)
+    assert_parity(out, host(o2[0]), 2e-2, "varlen vs chunked out", lead_dims=1)
+    assert_parity(S[0], host(S2[0]), 1e-5, "varlen vs chunked S", lead_dims=1)
+
+
+def test_causal_varlen_many_sequences_at_scale(gpu_lib):
+    """16 ragged sequences (~16k tokens), 8 heads: the matrix-core path with
+    several segments per sequence and partial segments at every boundary."""
+    g = np.random.default_rng(109)
+    lens = g.integers(1, 2048, size=16)
+    lens[3] = 0
+    c, q, k, v, cu, cu_d = _packed(109, list(lens), "favor", torch.bfloat16, 256, 1, H=8)
+    kw = dict(scale=64 ** -0.25)
+    out, S, z = gpu_lib.lin_attn_causal_varlen(q, k, v, cu_d, "favor", **c.gkw(**kw))
+    ro, rS, rz = oracle.causal_varlen(c.qh[0], c.kh[0], c.vh[0], cu, "favor", **c.okw(**kw))
+    assert_parity(out, ro, 2e-2, "varlen at scale out", lead_dims=1)
+    assert_parity(S, rS, 2e-2, "varlen at scale S")
+    assert_parity(z, rz, 2e-2, "varlen at scale z")

@@ -374,3 +374,80 @@ def test_orthogonal_rows_have_chi_lengths():
     chi_mean = math.sqrt(2) * math.exp(math.lgamma((d + 1) / 2) - math.lgamma(d / 2))
     chi_var = d - chi_mean ** 2
     assert abs(lengths.mean() - chi_mean) < 5 * math.sqrt(chi_var / lengths.size)
+
+
+# --------------------------------------------------------------------------
+# Packed sequences ("Reassociate a feature-map kernel..." par. 4: packing
+# resets the state at the logical boundary)
+# --------------------------------------------------------------------------
+
+def _block_diagonal_reference(q, k, v, cu, kind, S0=None, z0=None, eps=1e-6, **kw):
+    """The explicit form with a block-diagonal causal mask, written directly
+    in numpy from the feature maps: query i of sequence s sees keys j <= i of
+    sequence s only, plus that sequence's carried-in state."""
+    pq = oracle.featuremap(q, kind, **kw)
+    pk = oracle.featuremap(k, kind, **kw)
+    H, total, _ = q.shape
+    out = np.zeros((H, total, v.shape[-1]))
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        for h in range(H):
+            for i in range(a, b):
+                w = pk[h, a:i + 1] @ pq[h, i]          # weights of the visible keys
+                num = w @ v[h, a:i + 1]
+                den = w.sum()
+                if S0 is not None:
+                    num = num + pq[h, i] @ S0[s, h]
+                    den = den + pq[h, i] @ z0[s, h]
+                out[h, i] = num / max(den, eps)
+    return out
+
+
+@pytest.mark.parametrize("kind,extra", [("elu1", {}), ("favor", {"r": 16}), ("dpfp", {"nu": 1})])
+def test_varlen_equals_block_diagonal_explicit_form(kind, extra):
+    cu = [0, 4, 4, 11, 12, 17]                   # includes an empty and a one-token sequence
+    q, k, v, om = _tiny(61, BH=2, N=17, r=extra.get("r"))
+    kw = dict(omega=om, nu=extra.get("nu", 1), scale=0.9)
+    out, S, z = oracle.causal_varlen(q, k, v, cu, kind, **kw)
+    ref = _block_diagonal_reference(q, k, v, cu, kind, **kw)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    # each sequence's final state is its own keys' sum, and the empty one is zero
+    pk = oracle.featuremap(k, kind, **kw)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        np.testing.assert_allclose(z[s], pk[:, a:b].sum(axis=1), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(S[s], np.einsum("hjr,hjv->hrv", pk[:, a:b], v[:, a:b]),
+                                   rtol=1e-12, atol=1e-14)
+    assert not S[1].any() and not z[1].any()
+
+
+def test_varlen_with_carried_states():
+    cu = [0, 6, 9]
+    q, k, v, om = _tiny(62, BH=2, N=9, r=12)
+    g = np.random.default_rng(63)
+    S0 = np.abs(g.standard_normal((2, 2, 12, 5)))
+    z0 = np.abs(g.standard_normal((2, 2, 12)))
+    kw = dict(omega=om, scale=0.6)
+    out, S, z = oracle.causal_varlen(q, k, v, cu, "favor", S0=S0, z0=z0, **kw)
+    ref = _block_diagonal_reference(q, k, v, cu, "favor", S0=S0, z0=z0, **kw)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    pk = oracle.featuremap(k, "favor", **kw)
+    np.testing.assert_allclose(z[1], z0[1] + pk[:, 6:9].sum(axis=1), rtol=1e-12)
+
+
+def test_varlen_sequences_do_not_see_each_other():
+    """Changing every token of one sequence leaves the other sequences'
+    outputs and states bit-for-bit unchanged."""
+    cu = [0, 5, 13, 20]
+    q, k, v, om = _tiny(64, BH=2, N=20, r=16)
+    kw = dict(omega=om)
+    out, S, z = oracle.causal_varlen(q, k, v, cu, "favor", **kw)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[:, 5:13] += 1.0
+    k2[:, 5:13] -= 0.5
+    v2[:, 5:13] *= 3.0
+    out2, S2, z2 = oracle.causal_varlen(q2, k2, v2, cu, "favor", **kw)
+    for a, b in ((0, 5), (13, 20)):
+        assert np.array_equal(out[:, a:b], out2[:, a:b])
+    assert np.array_equal(S[[0, 2]], S2[[0, 2]]) and np.array_equal(z[[0, 2]], z2[[0, 2]])
+    assert not np.array_equal(out[:, 5:13], out2[:, 5:13])

@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "bidir"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "bidir", "varlen"], default=None,
                     help="run one section only (for profiling)")
     return ap.parse_args()
 
@@ -221,6 +221,41 @@ def main():
                            "ms_per_step": bms, "tokens_per_s": wb.B * wb.N / (bms * 1e-3),
                            "tflops_alg": bach, "frac_mfma": bach / PEAK_BF16_TFLOPS}
         del bsets
+
+    # ------------------------------------------------------------------ packed sequences
+    wv = workloads.FAVOR_VARLEN
+    if args.only in (None, "varlen"):
+        sv = workloads.scale_of(wv)
+        lens = inputs.packed_lengths(wv.B, wv.N, wv.wid)
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+        vsets = []
+        for rep in range(2):
+            q, k, v = (to_dev(inputs.normal((wv.H, wv.N, wv.d), wv.wid, t, rep))
+                       for t in (inputs.T_Q, inputs.T_K, inputs.T_V))
+            vsets.append((q, k, v))
+        om = to_dev(inputs.orf_omega(wv.r, wv.d, wv.wid))
+        vout = torch.empty((wv.H, wv.N, wv.dv), device=dev, dtype=torch.bfloat16)
+        vS = torch.empty((wv.B, wv.H, wv.r, wv.dv), device=dev, dtype=torch.float32)
+        vz = torch.empty((wv.B, wv.H, wv.r), device=dev, dtype=torch.float32)
+        pv = binding.make_params("favor", wv.r, dtype=torch.bfloat16, scale=sv, eps=wv.eps)
+        wsv = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, pv, wv.B, wv.H, wv.N,
+                                               wv.d, wv.dv)
+        vws = torch.empty(wsv, dtype=torch.uint8, device=dev)
+
+        def vstep(i):
+            q, k, v = vsets[i % 2]
+            binding.lin_attn_causal_varlen(q, k, v, cu, "favor", omega=om, scale=sv, eps=wv.eps,
+                                           S=vS, z=vz, out=vout, workspace=vws)
+
+        total_ms, per = timed(vstep, args.steps, args.warmup)
+        vms = total_ms / args.steps
+        vflops = favor_alg_flops_per_tok_head(wv.r, wv.d, wv.dv) * wv.H * wv.N
+        vach = vflops / (float(np.mean(per)) * 1e-3) / 1e12
+        result["varlen"] = {"workload": wv.name, "sequences": wv.B, "H": wv.H,
+                            "tokens": wv.N, "min_len": int(lens.min()), "max_len": int(lens.max()),
+                            "ms_per_step": vms, "tokens_per_s": wv.N / (vms * 1e-3),
+                            "tflops_alg": vach, "frac_mfma": vach / PEAK_BF16_TFLOPS}
+        del vsets
 
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, scale)

@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-T_Q, T_K, T_V, T_OMEGA, T_PREFIX = 0, 1, 2, 3, 4
+T_Q, T_K, T_V, T_OMEGA, T_PREFIX, T_LENGTHS = 0, 1, 2, 3, 4, 5
 
 
 def rng(workload: int, tensor: int, rep: int = 0) -> np.random.Generator:
@@ -64,3 +64,15 @@ def orf_omega(r: int, d: int, workload: int, rep: int = 0) -> np.ndarray:
 def iid_omega(r: int, d: int, workload: int, rep: int = 0) -> np.ndarray:
     """[r, d] float64 with i.i.d. N(0, 1) entries."""
     return rng(workload, T_OMEGA, rep).standard_normal((r, d))
+
+
+def packed_lengths(num_seqs: int, total: int, workload: int, rep: int = 0,
+                   lo: int = 256, hi: int = 8192) -> np.ndarray:
+    """Lengths of num_seqs packed sequences that sum to total: log-uniform
+    draws in [lo, hi] (a mix of short and long documents), scaled to the
+    total and rounded, the rounding remainder added to the last one."""
+    g = rng(workload, T_LENGTHS, rep)
+    w = np.exp(g.uniform(np.log(lo), np.log(hi), size=num_seqs))
+    lens = np.floor(w / w.sum() * total).astype(np.int64)
+    lens[-1] += total - lens.sum()
+    return lens

@@ -1,4 +1,4 @@
-"""The five synthetic workloads the path is tested and measured on.
+"""The six synthetic workloads the path is tested and measured on.
 
 Plain data, no arithmetic.  Shapes follow the pages' settings: head size
 d_h = d_v = 64 and h = 8 heads (Kernel Zoo "The Running Example" model
@@ -15,12 +15,12 @@ from dataclasses import dataclass
 class Workload:
     wid: int            # workload id, first word of every seed
     name: str
-    mode: str           # "bidir" | "causal" | "decode" | "bidir+causal"
+    mode: str           # "bidir" | "causal" | "decode" | "bidir+causal" | "causal_varlen"
     kind: str           # "elu1" | "favor" | "dpfp"
     dtype: str          # "f32" | "bf16"
     B: int
     H: int
-    N: int              # tokens per sequence (1 for decode)
+    N: int              # tokens per sequence (1 for decode; all packed tokens for causal_varlen)
     d: int = 64
     dv: int = 64
     r: int = 64
@@ -43,7 +43,12 @@ DPFP_CAUSAL = Workload(3, "dpfp_causal", "causal", "dpfp", "f32", B=8, H=8, N=20
 FAVOR_DECODE = Workload(4, "favor_decode", "decode", "favor", "bf16", B=256, H=8, N=1, r=256,
                         favor_scale=True, layers=12, prefix=64)
 
-ALL = (ELU_SMALL, FAVOR_BIDIR, FAVOR_CAUSAL, DPFP_CAUSAL, FAVOR_DECODE)
+# the causal prefill's 65,536 tokens per head as 32 packed documents of mixed
+# length (lengths from inputs.packed_lengths), each starting from zero state
+FAVOR_VARLEN = Workload(5, "favor_causal_packed", "causal_varlen", "favor", "bf16", B=32, H=8,
+                        N=65536, r=256, favor_scale=True)
+
+ALL = (ELU_SMALL, FAVOR_BIDIR, FAVOR_CAUSAL, DPFP_CAUSAL, FAVOR_DECODE, FAVOR_VARLEN)
 
 
 def scale_of(w: Workload) -> float:

@@ -350,3 +350,21 @@ def test_causal_varlen_many_sequences_at_scale(gpu_lib):
     assert_parity(out, ro, 2e-2, "varlen at scale out", lead_dims=1)
     assert_parity(S, rS, 2e-2, "varlen at scale S")
     assert_parity(z, rz, 2e-2, "varlen at scale z")
+
+
+def test_workload_favor_causal_packed(gpu_lib):
+    """The benchmark's packed workload at full size: 32 documents of mixed
+    length over 65,536 tokens, 8 heads."""
+    w = workloads.FAVOR_VARLEN
+    lens = inputs.packed_lengths(w.B, w.N, w.wid)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q, k, v = (dev(inputs.normal((w.H, w.N, w.d), w.wid, t, 0), DT[w.dtype])
+               for t in (inputs.T_Q, inputs.T_K, inputs.T_V))
+    om = dev(inputs.orf_omega(w.r, w.d, w.wid), DT[w.dtype])
+    kw = dict(scale=workloads.scale_of(w), eps=w.eps)
+    o, S, z = gpu_lib.lin_attn_causal_varlen(q, k, v, torch.from_numpy(cu).to("cuda"), w.kind,
+                                             omega=om, **kw)
+    ro, rS, rz = oracle.causal_varlen(host(q), host(k), host(v), cu, w.kind, omega=host(om), **kw)
+    assert_parity(o, ro, 2e-2, "packed out", lead_dims=1)
+    assert_parity(S, rS, 2e-2, "packed S")
+    assert_parity(z, rz, 2e-2, "packed z")

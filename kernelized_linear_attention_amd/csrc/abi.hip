@@ -104,12 +104,13 @@ hipError_t segment_outputs(const lin_attn_params* p, const Cfg& c, int causal, c
 // Packed batch (lin_attn_causal_varlen): the uniform planner over all tokens
 // of a head fixes the segment length; every sequence adds at most one
 // partial segment, which bounds the segment table.  Workspace: increments
-// (float32) [H][parts][E], then the table int64 [parts][2], then the first
-// part of every sequence int64 [num_seqs + 1].
+// (float32) [H][parts][E], then the table int64 [parts][2], the first part of
+// every sequence int64 [num_seqs + 1] and the dispatch order of the segments
+// int64 [segments].
 struct VarlenLayout {
     SegPlan sp;        // G = segment capacity per head, seg_len, sub
     int64_t parts;     // table capacity (segments x sub)
-    size_t tab_off, first_off, bytes;
+    size_t tab_off, first_off, order_off, bytes;
 };
 
 VarlenLayout varlen_layout(const lin_attn_params* p, int64_t num_seqs, int64_t H, int64_t total) {
@@ -123,6 +124,8 @@ VarlenLayout varlen_layout(const lin_attn_params* p, int64_t num_seqs, int64_t H
     off += (size_t)L.parts * 2 * sizeof(int64_t);
     L.first_off = off;
     off += (size_t)(num_seqs + 1) * sizeof(int64_t);
+    L.order_off = off;
+    off += (size_t)L.sp.G * sizeof(int64_t);
     L.bytes = off;
     return L;
 }
@@ -297,12 +300,16 @@ int lin_attn_causal_varlen(const lin_attn_params* p, const void* q, const void* 
     float* inc = (float*)ws;
     int64_t* tab = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + L.tab_off);
     int64_t* first = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + L.first_off);
+    int64_t* order = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + L.order_off);
     SegPlan sp = L.sp;
     sp.tab = tab;
+    // the matrix-core kernels run the segments longest first; the vector
+    // kernels keep head-major order
+    if (use_mfma(p)) sp.order = order;
     const SegPlan ss = sums_plan(sp);
     const int64_t E = state_elems(p->r);
     hipError_t e = launch_varlen_plan(cu_seqlens, num_seqs, total, sp.seg_len, sp.sub, L.parts, tab,
-                                      first, st);
+                                      first, order, st);
     if (e == hipSuccess) e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
     if (e == hipSuccess)
         e = launch_segment_scan_varlen(p->r, H, num_seqs, L.parts, first, state_in ? S : nullptr,

@@ -73,7 +73,24 @@ struct FavorArgs {
     u16* out;
     const int64_t* tab; // segment table (packed sequences) or NULL
     int64_t tsub;       // parts per segment in the table
+    const int64_t* order; // segment-major dispatch order or NULL (see SegPlan)
+    int64_t osub;
+    int64_t BH;
 };
+
+// The (head, segment) this workgroup runs; false when it runs nothing.
+__device__ __forceinline__ bool block_segment(const FavorArgs& a, int64_t& bh, int64_t& g) {
+    if (!a.order) {
+        bh = blockIdx.x / a.G;
+        g = blockIdx.x % a.G;
+        return true;
+    }
+    const int64_t s = blockIdx.x / a.BH;
+    bh = blockIdx.x % a.BH;
+    const int64_t seg = a.order[s / a.osub];
+    g = seg * a.osub + s % a.osub;
+    return seg >= 0 && g < a.G;
+}
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
 // every outstanding global load, which would stall on the next chunk's
@@ -668,7 +685,8 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
-    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
+    int64_t bh, g;
+    if (!block_segment(a, bh, g)) return; // uniform over the workgroup
     int64_t t0, t1;
     seg_range(a.tab, a.tsub, g, a.seg_len, a.N, t0, t1);
     const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
@@ -694,7 +712,8 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lo = lane & 31, h = lane >> 5;
     const int f0 = 32 * w;
-    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
+    int64_t bh, g;
+    if (!block_segment(a, bh, g)) return; // uniform over the workgroup
     int64_t t0, t1;
     seg_range(a.tab, a.tsub, g, a.seg_len, a.N, t0, t1);
     const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
@@ -788,6 +807,9 @@ FavorArgs make_args(const Cfg& c, const void* q, const void* k, const void* v, c
     a.out = (u16*)out;
     a.tab = sp.tab;
     a.tsub = sp.sub;
+    a.order = sp.order;
+    a.osub = sp.osub;
+    a.BH = s.BH;
     return a;
 }
 

@@ -241,52 +241,112 @@ __global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const flo
 // One workgroup walks the sequences NT at a time: each thread counts its
 // sequence's parts, a workgroup scan turns the counts into offsets, and the
 // thread writes its parts.  Every range is clamped to [0, total] and every
-// index to cap, whatever cu_seqlens holds.
+// index to cap, whatever cu_seqlens holds.  A second walk writes the
+// dispatch order: all full segments (seg_len tokens) first, then each
+// sequence's partial last segment, in buckets of 64 tokens from the longest
+// down (list scheduling, longest first, as the hardware dispatches
+// workgroups in order).
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int64_t i, int64_t total, int64_t& s0,
+                                           int64_t& s1) {
+    s0 = min<int64_t>(max<int64_t>(cu[i], 0), total);
+    s1 = min<int64_t>(max<int64_t>(cu[i + 1], s0), total);
+}
+
+// Exclusive scan of one value per thread over the workgroup (all threads
+// call it); returns this thread's offset and sets *sum to the total.
+__device__ int64_t block_exclusive_scan(int64_t x, int64_t* buf, int64_t* sum) {
+    const int tid = threadIdx.x;
+    buf[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+        const int64_t y = tid >= off ? buf[tid - off] : 0;
+        __syncthreads();
+        buf[tid] += y;
+        __syncthreads();
+    }
+    const int64_t incl = buf[tid];
+    *sum = buf[NT - 1];
+    __syncthreads();
+    return incl - x;
+}
+
 __global__ __launch_bounds__(NT) void k_varlen_plan(const int32_t* __restrict__ cu, int64_t num_seqs,
                                                     int64_t total, int64_t seg_len, int64_t sub,
                                                     int64_t cap, int64_t* __restrict__ tab,
-                                                    int64_t* __restrict__ first) {
-    __shared__ int64_t cnt_s[NT];
-    __shared__ int64_t base_s;
+                                                    int64_t* __restrict__ first,
+                                                    int64_t* __restrict__ order) {
+    constexpr int NB = 128; // partial-segment buckets of 64 tokens (seg_len <= 8192)
+    __shared__ int64_t buf[NT];
+    __shared__ int bucket_n[NB], bucket_at[NB];
     const int tid = threadIdx.x;
     const int64_t part_len = seg_len / sub;
-    if (tid == 0) base_s = 0;
+    const int64_t seg_cap = cap / sub;
+    const int nb = (int)min<int64_t>(NB, (seg_len + 63) / 64);
+    for (int j = tid; j < NB; j += NT) bucket_n[j] = 0;
+    for (int64_t e = tid; e < seg_cap; e += NT) order[e] = -1; // every entry defined
     __syncthreads();
+    int64_t base = 0, full_base = 0;
     for (int64_t i0 = 0; i0 < num_seqs; i0 += NT) {
         const int64_t i = i0 + tid;
-        int64_t s0 = 0, s1 = 0, n = 0;
+        int64_t s0 = 0, s1 = 0, n = 0, nf = 0;
         if (i < num_seqs) {
-            s0 = min<int64_t>(max<int64_t>(cu[i], 0), total);
-            s1 = min<int64_t>(max<int64_t>(cu[i + 1], s0), total);
+            seq_bounds(cu, i, total, s0, s1);
             n = (s1 - s0 + seg_len - 1) / seg_len * sub;
+            nf = (s1 - s0) / seg_len;
         }
-        cnt_s[tid] = n;
-        __syncthreads();
-        for (int off = 1; off < NT; off <<= 1) { // inclusive scan of the counts
-            const int64_t x = tid >= off ? cnt_s[tid - off] : 0;
-            __syncthreads();
-            cnt_s[tid] += x;
-            __syncthreads();
-        }
-        const int64_t base = base_s;
-        const int64_t e0 = base + cnt_s[tid] - n;
+        int64_t sum, fsum;
+        const int64_t e0 = base + block_exclusive_scan(n, buf, &sum);
+        block_exclusive_scan(nf, buf, &fsum);
         if (i < num_seqs) {
             first[i] = min<int64_t>(e0, cap);
             for (int64_t j = 0; j < n && e0 + j < cap; ++j) {
-                const int64_t a = s0 + j * part_len;
-                tab[2 * (e0 + j)] = min<int64_t>(a, s1);
-                tab[2 * (e0 + j) + 1] = min<int64_t>(a + part_len, s1);
+                const int64_t x = s0 + j * part_len;
+                tab[2 * (e0 + j)] = min<int64_t>(x, s1);
+                tab[2 * (e0 + j) + 1] = min<int64_t>(x + part_len, s1);
             }
+            const int64_t rem = (s1 - s0) % seg_len;
+            if (rem > 0) atomicAdd(&bucket_n[min<int64_t>(nb - 1, (rem - 1) / 64)], 1);
         }
-        __syncthreads();
-        if (tid == NT - 1) base_s = base + cnt_s[NT - 1];
-        __syncthreads();
+        base += sum;
+        full_base += fsum;
     }
-    const int64_t used = min<int64_t>(base_s, cap);
+    const int64_t used = min<int64_t>(base, cap);
     if (tid == 0) first[num_seqs] = used;
     for (int64_t e = used + tid; e < cap; e += NT) {
         tab[2 * e] = 0;
         tab[2 * e + 1] = 0;
+    }
+    // bucket offsets, longest partials first (nb <= NB <= NT: one thread each)
+    __syncthreads();
+    {
+        const int j = nb - 1 - tid; // descending bucket index
+        int64_t c = (tid < nb) ? bucket_n[j] : 0, sum;
+        const int64_t off = block_exclusive_scan(c, buf, &sum);
+        if (tid < nb) bucket_at[j] = (int)min<int64_t>(full_base + off, seg_cap);
+    }
+    __syncthreads();
+    // second walk: full segments in sequence order, partials into their bucket
+    int64_t fbase = 0;
+    for (int64_t i0 = 0; i0 < num_seqs; i0 += NT) {
+        const int64_t i = i0 + tid;
+        int64_t s0 = 0, s1 = 0, nf = 0;
+        if (i < num_seqs) {
+            seq_bounds(cu, i, total, s0, s1);
+            nf = (s1 - s0) / seg_len;
+        }
+        int64_t fsum;
+        const int64_t f0 = fbase + block_exclusive_scan(nf, buf, &fsum);
+        if (i < num_seqs) {
+            const int64_t g0 = first[i] / sub; // the sequence's first segment
+            for (int64_t j = 0; j < nf && f0 + j < seg_cap && g0 + j < seg_cap; ++j)
+                order[f0 + j] = g0 + j;
+            const int64_t rem = (s1 - s0) % seg_len;
+            if (rem > 0) {
+                const int pos = atomicAdd(&bucket_at[min<int64_t>(nb - 1, (rem - 1) / 64)], 1);
+                if (pos < seg_cap) order[pos] = g0 + nf < seg_cap ? g0 + nf : -1;
+            }
+        }
+        fbase += fsum;
     }
 }
 
@@ -574,9 +634,9 @@ hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, cons
 
 hipError_t launch_varlen_plan(const int32_t* cu_seqlens, int64_t num_seqs, int64_t total,
                               int64_t seg_len, int64_t sub, int64_t cap, int64_t* tab,
-                              int64_t* first, hipStream_t st) {
+                              int64_t* first, int64_t* order, hipStream_t st) {
     hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(NT), 0, st, cu_seqlens, num_seqs, total,
-                       seg_len, sub, cap, tab, first);
+                       seg_len, sub, cap, tab, first, order);
     return hipGetLastError();
 }
 

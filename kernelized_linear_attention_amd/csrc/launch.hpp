@@ -26,10 +26,17 @@ struct SegPlan {
     // tokens [tab[2e], tab[2e+1]) of every head and segment g is parts
     // g*sub .. g*sub + sub - 1 (packed sequences, see launch_varlen_plan).
     const int64_t* tab = nullptr;
+    // Dispatch order of the segments (matrix-core kernels, packed sequences):
+    // workgroup b runs segment order[b / heads] of head b % heads (-1: none),
+    // longest segments first.  NULL: head-major, segment g = b % G.
+    const int64_t* order = nullptr;
+    int64_t osub = 1; // parts per entry of `order` (the increment kernels run parts)
 };
 
 // The plan of the increment and prefix kernels: sub-segments as segments.
-inline SegPlan sums_plan(SegPlan p) { return SegPlan{p.G * p.sub, p.seg_len / p.sub, 1, p.tab}; }
+inline SegPlan sums_plan(SegPlan p) {
+    return SegPlan{p.G * p.sub, p.seg_len / p.sub, 1, p.tab, p.order, p.sub};
+}
 
 inline SegPlan plan_segments(int64_t BH, int64_t N, int32_t n_seg_req, int64_t target_blocks) {
     SegPlan p{1, N, 1};
@@ -93,12 +100,13 @@ hipError_t launch_segment_outputs(const Cfg& c, int dtype, int causal, const voi
 // [cu_seqlens[i], cu_seqlens[i+1]) of every head and is cut into
 // ceil(len / seg_len) segments of `sub` parts of seg_len / sub tokens (tail
 // parts may be empty).  Writes tab[2e], tab[2e+1] for the cap parts (unused
-// ones empty) and first[i] = first part of sequence i (first[num_seqs] = parts
-// used).  Ranges are clamped to [0, total] and the count to cap, so malformed
+// ones empty), first[i] = first part of sequence i (first[num_seqs] = parts
+// used) and the dispatch order of the cap / sub segments (see SegPlan).
+// Ranges are clamped to [0, total] and the count to cap, so malformed
 // boundaries cannot send a later kernel out of bounds.  One workgroup.
 hipError_t launch_varlen_plan(const int32_t* cu_seqlens, int64_t num_seqs, int64_t total,
                               int64_t seg_len, int64_t sub, int64_t cap, int64_t* tab,
-                              int64_t* first, hipStream_t st);
+                              int64_t* first, int64_t* order, hipStream_t st);
 
 // Prefix over the parts of every (sequence, head): parts first[i] ..
 // first[i+1]-1 of head h in ws[h][.], starting from S0/z0[(i*H + h)] (or

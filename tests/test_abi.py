@@ -226,7 +226,8 @@ def test_varlen_workspace_formula():
     """Increments of every part of every head -- the segments of the uniform
     plan over all tokens plus one partial segment per sequence, two parts each
     on the matrix-core path -- then the segment table (two int64 per part,
-    after 256-byte alignment) and the first part of every sequence."""
+    after 256-byte alignment), the first part of every sequence and the
+    dispatch order (one int64 per segment)."""
     p = params()
     E = 256 * 64 + 256
     # H = 8, total = 65536: 32 segments of 2048 tokens per head, + 4 sequences
@@ -234,5 +235,5 @@ def test_varlen_workspace_formula():
     inc = 8 * parts * E * 4
     assert inc % 256 == 0
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 4, 8, 65536, 64, 64) == \
-        inc + parts * 16 + 5 * 8
+        inc + parts * 16 + 5 * 8 + (32 + 4) * 8
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 4, 8, 0, 64, 64) == 0

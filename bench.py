@@ -182,7 +182,16 @@ def main():
         bytes_layer = decode_alg_bytes_per_head(wd.r, wd.dv, 2) * heads
         gbps_step = bytes_layer * wd.layers / (dms * 1e-3) / 1e9
         gbps_launch = bytes_layer / (launch_ms * 1e-3) / 1e9
+        # omega redraw for all layers on the device (orthogonal random features
+        # from Gaussian draws): one launch building 12 [r, d] matrices
+        draws = [inputs.orf_draws(wd.r, wd.d, wd.wid, 300 + l) for l in range(wd.layers)]
+        og = torch.from_numpy(np.stack([g for g, _ in draws])).to(dev)
+        ol = torch.from_numpy(np.stack([x for _, x in draws])).to(dev)
+        oom = torch.empty((wd.layers, wd.r, wd.d), device=dev, dtype=torch.bfloat16)
+        orf_ms, orf_per = timed(lambda i: binding.lin_attn_orf_omega(og, ol, out=oom), args.steps,
+                                args.warmup)
         result["decode"] = {
+            "omega_redraw_us": float(np.median(orf_per)) * 1e3,
             "workload": wd.name, "B": wd.B, "H": wd.H, "layers": wd.layers, "r": wd.r,
             "ms_per_step": dms, "seq_tokens_per_s": wd.B / (dms * 1e-3),
             "GBps_step": gbps_step,

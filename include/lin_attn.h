@@ -209,6 +209,26 @@ int lin_attn_decode_step(const lin_attn_params* p, const void* q, const void* k,
                          const void* omega, float* S, float* z, void* out, void* stream);
 
 /*
+ * Orthogonal random features built on the device ([PF] sec. 2 step 4;
+ * [KZ] sec. 5.1-5.3): n_mat independent omega matrices [r, d], each from
+ * ceil(r/d) blocks; block b is Gram-Schmidt of the rows of the d x d
+ * Gaussian matrix gauss[m][b] taken in order, and row f is then scaled to the
+ * norm of len_gauss[m][f] (a chi(d)-distributed length), or to sqrt(d) when
+ * len_gauss is NULL.  The last block is cut at r rows.  The random draws are
+ * the caller's (any generator); this call only does the arithmetic, in
+ * float64 (classical Gram-Schmidt with one reorthogonalisation pass, equal
+ * to the pages' procedure in exact arithmetic), then rounds to the output
+ * dtype through float32 (nearest-even at each step).
+ *   gauss      float32 [n_mat, ceil(r/d), d, d]
+ *   len_gauss  float32 [n_mat, ceil(r/d) * d, d] or NULL
+ *   omega      [n_mat, r, d], dtype LIN_ATTN_F32 or LIN_ATTN_BF16
+ * Returns -1 for a null or misaligned pointer, a negative size or a bad
+ * dtype, -2 for d > 64; r = 0 or n_mat = 0 is a no-op.  No workspace.
+ */
+int lin_attn_orf_omega(const float* gauss, const float* len_gauss, int64_t n_mat, int64_t r,
+                       int64_t d, int32_t dtype, void* omega, void* stream);
+
+/*
  * Workspace bytes needed by lin_attn_bidir (op = LIN_ATTN_OP_BIDIR),
  * lin_attn_causal_chunked (op = LIN_ATTN_OP_CAUSAL) or, with B = num_seqs and
  * N = total, lin_attn_causal_varlen (op = LIN_ATTN_OP_CAUSAL_VARLEN).

@@ -32,7 +32,7 @@ ABI_VERSION = 1
 
 # Every symbol include/lin_attn.h declares.
 EXPORTS = ("lin_attn_featuremap", "lin_attn_bidir", "lin_attn_causal_chunked",
-           "lin_attn_causal_varlen",
+           "lin_attn_causal_varlen", "lin_attn_orf_omega",
            "lin_attn_decode_step", "lin_attn_workspace_bytes", "lin_attn_strerror",
            "lin_attn_abi_version")
 
@@ -59,6 +59,8 @@ _lib.lin_attn_causal_chunked.restype = ctypes.c_int
 _lib.lin_attn_causal_varlen.argtypes = [_PP, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
                                         _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]
 _lib.lin_attn_causal_varlen.restype = ctypes.c_int
+_lib.lin_attn_orf_omega.argtypes = [_P, _P, _I64, _I64, _I64, _I32, _P, _P]
+_lib.lin_attn_orf_omega.restype = ctypes.c_int
 _lib.lin_attn_decode_step.argtypes = [_PP, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.lin_attn_decode_step.restype = ctypes.c_int
 _lib.lin_attn_workspace_bytes.argtypes = [_I32, _PP, _I64, _I64, _I64, _I64, _I64, _I32]
@@ -255,6 +257,28 @@ def lin_attn_causal_varlen(q, k, v, cu_seqlens, kind, *, omega=None, nu=1, sum_n
                                      _stream(q.device, stream))
     _check("lin_attn_causal_varlen", rc)
     return out, S, z
+
+
+def lin_attn_orf_omega(gauss, len_gauss=None, *, r=None, dtype=torch.bfloat16, out=None,
+                       stream=None):
+    """Orthogonal random features from Gaussian draws on the device: gauss
+    float32 [n_mat, nblk, d, d] (or [nblk, d, d]), len_gauss float32
+    [n_mat, nblk*d, d] or None (rows scaled to sqrt(d)).  Returns omega
+    [n_mat, r, d] (or [r, d]) in dtype; r defaults to nblk * d."""
+    _dev_tensor("gauss", gauss, torch.float32)
+    single = gauss.dim() == 3
+    g = gauss.unsqueeze(0) if single else gauss
+    n_mat, nblk, d, _ = g.shape
+    r = nblk * d if r is None else int(r)
+    if len_gauss is not None:
+        _dev_tensor("len_gauss", len_gauss, torch.float32)
+    if out is None:
+        out = torch.empty((n_mat, r, d), dtype=dtype, device=gauss.device)
+    _dev_tensor("out", out, dtype)
+    rc = _lib.lin_attn_orf_omega(_ptr(g), _ptr(len_gauss), n_mat, r, d, DTYPE[dtype], _ptr(out),
+                                 _stream(gauss.device, stream))
+    _check("lin_attn_orf_omega", rc)
+    return out[0] if single else out
 
 
 def lin_attn_decode_step(q, k, v, S, z, kind, *, omega=None, nu=1, sum_norm=False, norm="attn",

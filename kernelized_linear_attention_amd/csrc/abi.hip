@@ -320,6 +320,20 @@ int lin_attn_causal_varlen(const lin_attn_params* p, const void* q, const void* 
     return launch_status(e);
 }
 
+int lin_attn_orf_omega(const float* gauss, const float* len_gauss, int64_t n_mat, int64_t r,
+                       int64_t d, int32_t dtype, void* omega, void* stream) {
+    if (n_mat < 0 || r < 0 || d < 1) return LIN_ATTN_ERR_INVALID;
+    if (dtype != LIN_ATTN_F32 && dtype != LIN_ATTN_BF16) return LIN_ATTN_ERR_INVALID;
+    if (n_mat > 0 && r > 0 && (!ptr_ok(gauss) || !ptr_ok(omega) || !opt_ptr_ok(len_gauss)))
+        return LIN_ATTN_ERR_INVALID;
+    if (d > 64) return LIN_ATTN_ERR_UNSUPPORTED;
+    if (n_mat == 0 || r == 0) return LIN_ATTN_OK;
+    const int64_t nblk = (r + d - 1) / d;
+    if (n_mat > ((int64_t)1 << 24) || nblk > ((int64_t)1 << 24) / n_mat) return LIN_ATTN_ERR_UNSUPPORTED;
+    return launch_status(launch_orf(gauss, len_gauss, n_mat, r, (int)d, dtype, omega,
+                                    (hipStream_t)stream));
+}
+
 int lin_attn_decode_step(const lin_attn_params* p, const void* q, const void* k, const void* v,
                          int64_t B, int64_t H, int64_t d, int64_t dv, const void* omega, float* S,
                          float* z, void* out, void* stream) {

@@ -130,6 +130,10 @@ hipError_t launch_favor_outputs(const Cfg& c, int causal, const void* q, const v
                                 const float* state, int64_t sbh, int64_t sg, void* out,
                                 hipStream_t st);
 
+// Orthogonal random features (orf.hip): n_mat matrices [r, d], d <= 64.
+hipError_t launch_orf(const float* gauss, const float* len_gauss, int64_t n_mat, int64_t r, int d,
+                      int dtype, void* omega, hipStream_t st);
+
 hipError_t launch_decode(const Cfg& c, int dtype, const void* q, const void* k, const void* v,
                          const void* omega, int64_t BH, float* S, float* z, void* out,
                          hipStream_t st);

@@ -1,0 +1,93 @@
+// orf.hip -- orthogonal random features built on the device (Performer page
+// sec. 2 step 4; Kernel Zoo sec. 5.1-5.3): every block of d rows of omega is
+// Gram-Schmidt of the rows of a d x d Gaussian matrix, each row then scaled
+// to the length of an independent Gaussian vector (or to sqrt(d)).  The
+// Gaussian draws are inputs: the caller's generator makes them.
+//
+// One workgroup per (matrix, block), d <= 64.  The block is orthogonalised
+// in float64 in LDS, row by row in order; each row has its projections on
+// the earlier rows removed twice (classical Gram-Schmidt with one
+// reorthogonalisation pass: the pages' procedure in exact arithmetic, and
+// orthogonal to float64 precision in floating point).  The dot products of
+// one pass run in parallel, one wave per earlier row.
+#include "launch.hpp"
+
+namespace linattn {
+namespace {
+
+constexpr int NT = 256;
+constexpr int DMAX = 64;
+constexpr int LD = DMAX + 1; // LDS row stride (doubles)
+
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+template <typename T>
+__global__ __launch_bounds__(NT) void k_orf(const float* __restrict__ gauss,
+                                            const float* __restrict__ len_gauss, int64_t r, int d,
+                                            int64_t nblk, T* __restrict__ omega) {
+    __shared__ double e_s[DMAX * LD];
+    __shared__ double c_s[DMAX];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t m = blockIdx.x / nblk, b = blockIdx.x % nblk;
+    const float* g = gauss + (m * nblk + b) * d * d;
+
+    for (int x = tid; x < d * d; x += NT) e_s[(x / d) * LD + x % d] = (double)g[x];
+    __syncthreads();
+
+    for (int i = 0; i < d; ++i) {
+        double* ei = e_s + i * LD;
+        for (int pass = 0; pass < 2; ++pass) {
+            // c_j = e_j . e_i for the earlier rows j, one wave per row
+            for (int j = w; j < i; j += NT / 64) {
+                const double p = lane < d ? e_s[j * LD + lane] * ei[lane] : 0.0;
+                const double s = wave_sum_d(p);
+                if (lane == 0) c_s[j] = s;
+            }
+            __syncthreads();
+            if (tid < d) {
+                double x = ei[tid];
+                for (int j = 0; j < i; ++j) x -= c_s[j] * e_s[j * LD + tid];
+                ei[tid] = x;
+            }
+            __syncthreads();
+        }
+        if (w == 0) {
+            const double n2 = wave_sum_d(lane < d ? ei[lane] * ei[lane] : 0.0);
+            if (lane < d) ei[lane] = ei[lane] / sqrt(n2);
+        }
+        __syncthreads();
+    }
+
+    // rows of this block that exist (the last block may be cut at r)
+    const int rows = (int)min<int64_t>(d, r - b * d);
+    for (int i = w; i < rows; i += NT / 64) {
+        const int64_t f = b * d + i;
+        double len = sqrt((double)d);
+        if (len_gauss) {
+            const float* lg = len_gauss + (m * nblk * d + f) * d;
+            len = sqrt(wave_sum_d(lane < d ? (double)lg[lane] * (double)lg[lane] : 0.0));
+        }
+        if (lane < d) Elem<T>::store(omega, (m * r + f) * d + lane, (float)(e_s[i * LD + lane] * len));
+    }
+}
+
+} // namespace
+
+hipError_t launch_orf(const float* gauss, const float* len_gauss, int64_t n_mat, int64_t r, int d,
+                      int dtype, void* omega, hipStream_t st) {
+    const int64_t nblk = (r + d - 1) / d;
+    const dim3 grid((unsigned)(n_mat * nblk)), block(NT);
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_orf<float>, grid, block, 0, st, gauss, len_gauss, r, d, nblk,
+                           (float*)omega);
+    else
+        hipLaunchKernelGGL(k_orf<bf16_raw>, grid, block, 0, st, gauss, len_gauss, r, d, nblk,
+                           (bf16_raw*)omega);
+    return hipGetLastError();
+}
+
+} // namespace linattn

@@ -48,6 +48,21 @@ def orthonormal_rows(m: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray((q * signs).T)
 
 
+def orf_draws(r: int, d: int, workload: int, rep: int = 0):
+    """The Gaussian draws behind orf_omega, in the same order: per block of d
+    rows, a d x d matrix for the directions, then a d x d matrix whose row
+    norms are the lengths.  Returns (gauss [nblk, d, d], len_gauss
+    [nblk * d, d]) as float32 -- the inputs of an on-device ORF build."""
+    g = rng(workload, T_OMEGA, rep)
+    nblk = (r + d - 1) // d
+    gauss = np.empty((nblk, d, d), dtype=np.float64)
+    lens = np.empty((nblk * d, d), dtype=np.float64)
+    for b in range(nblk):
+        gauss[b] = g.standard_normal((d, d))
+        lens[b * d:(b + 1) * d] = g.standard_normal((d, d))
+    return gauss.astype(np.float32), lens.astype(np.float32)
+
+
 def orf_omega(r: int, d: int, workload: int, rep: int = 0) -> np.ndarray:
     """[r, d] float64: ceil(r/d) independent orthogonal blocks, rows scaled to
     chi(d)-distributed lengths; the last block is truncated when d does not

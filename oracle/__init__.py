@@ -17,7 +17,9 @@ Definitions followed (see the header of oracle.c for the passages):
   * causal recurrence and decode: Kernel Zoo sec. 1.2-1.3 and 5.4;
   * packed sequences: the causal recurrence per sequence, the state reset at
     each boundary ("Reassociate a feature-map kernel..." par. 4);
-  * explicit N x N form: the interactive chapter's "rescan every key".
+  * explicit N x N form: the interactive chapter's "rescan every key";
+  * orthogonal random features: Performer page sec. 2 step 4, Kernel Zoo
+    sec. 5.1-5.3 (Gram-Schmidt of Gaussian rows, chi or sqrt(d) lengths).
 """
 import ctypes
 import os
@@ -59,6 +61,8 @@ def _load():
     lib.orc_decode.restype = I
     lib.orc_explicit.argtypes = [I, I, I, I, I, D, D, I, P, P, P, L, L, L, L, P, I, P, P, P]
     lib.orc_explicit.restype = I
+    lib.orc_orf.argtypes = [P, P, L, L, P]
+    lib.orc_orf.restype = I
     _lib = lib
     return lib
 
@@ -229,4 +233,18 @@ def explicit(q, k, v, kind, *, causal_mask, omega=None, nu=1, sum_norm=False,
                               _ptr(z0), _ptr(out))
     if rc:
         raise ValueError("oracle explicit: invalid argument")
+    return out
+
+
+def orf(gauss, r, len_gauss=None):
+    """Orthogonal random features [r, d] from the Gaussian draws gauss
+    [ceil(r/d), d, d] (Gram-Schmidt on each block's rows, in order) and
+    len_gauss [ceil(r/d)*d, d] (each row scaled to the norm of its row of
+    len_gauss; sqrt(d) when None)."""
+    g = _f64(gauss)
+    d = g.shape[-1]
+    lg = _f64(len_gauss)
+    out = np.zeros((r, d))
+    if _load().orc_orf(_ptr(g), _ptr(lg), r, d, _ptr(out)):
+        raise ValueError("oracle orf: invalid argument")
     return out

@@ -369,3 +369,60 @@ int orc_explicit(int phi, int r, int nu, int sum_norm, int norm, double scale,
     }
     return 0;
 }
+
+/*
+ * Orthogonal random features ([PF] sec. 2 step 4; [KZ] sec. 5.1-5.3):
+ * omega [r, d] from ceil(r/d) independent blocks.  Block b takes the rows of
+ * the d x d Gaussian matrix gauss[b] in order and applies Gram-Schmidt:
+ * subtract from each row its projections on the earlier (orthonormal) rows,
+ * then divide by its norm.  Row f of the block is then scaled to the length
+ * of the independent Gaussian vector len_gauss[f] (chi(d)-distributed,
+ * [PF] sec. 2 step 4), or to sqrt(d) when len_gauss is NULL (the fixed
+ * length of [KZ] sec. 5.3).  The last block keeps its first r - (b*d) rows.
+ *   gauss      [ceil(r/d), d, d]     len_gauss  [ceil(r/d) * d, d] or NULL
+ */
+int orc_orf(const double *gauss, const double *len_gauss, long r, long d, double *omega)
+{
+    if (!gauss || !omega || r < 0 || d < 1)
+        return -1;
+    const long nblk = (r + d - 1) / d;
+    double *e = (double *)malloc((size_t)(d * d) * sizeof(double));
+    if (!e)
+        return -1;
+    for (long b = 0; b < nblk; ++b) {
+        const double *g = gauss + b * d * d;
+        for (long i = 0; i < d; ++i) {
+            double *ei = e + i * d;
+            for (long k = 0; k < d; ++k)
+                ei[k] = g[i * d + k];
+            for (long j = 0; j < i; ++j) {
+                const double *ej = e + j * d;
+                double dot = 0.0;
+                for (long k = 0; k < d; ++k)
+                    dot += g[i * d + k] * ej[k];
+                for (long k = 0; k < d; ++k)
+                    ei[k] -= dot * ej[k];
+            }
+            double nrm = 0.0;
+            for (long k = 0; k < d; ++k)
+                nrm += ei[k] * ei[k];
+            nrm = sqrt(nrm);
+            for (long k = 0; k < d; ++k)
+                ei[k] /= nrm;
+        }
+        for (long i = 0; i < d && b * d + i < r; ++i) {
+            const long f = b * d + i;
+            double len = sqrt((double)d);
+            if (len_gauss) {
+                double s = 0.0;
+                for (long k = 0; k < d; ++k)
+                    s += len_gauss[f * d + k] * len_gauss[f * d + k];
+                len = sqrt(s);
+            }
+            for (long k = 0; k < d; ++k)
+                omega[f * d + k] = e[i * d + k] * len;
+        }
+    }
+    free(e);
+    return 0;
+}

@@ -237,3 +237,18 @@ def test_varlen_workspace_formula():
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 4, 8, 65536, 64, 64) == \
         inc + parts * 16 + 5 * 8 + (32 + 4) * 8
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 4, 8, 0, 64, 64) == 0
+
+
+def test_orf_arguments():
+    orf = lib.lin_attn_orf_omega
+    assert orf(None, None, 1, 256, 64, 1, FAKE, None) == INVALID
+    assert orf(FAKE, None, 1, 256, 64, 1, None, None) == INVALID
+    assert orf(FAKE + 4, None, 1, 256, 64, 1, FAKE, None) == INVALID
+    assert orf(FAKE, FAKE + 8, 1, 256, 64, 1, FAKE, None) == INVALID
+    assert orf(FAKE, None, -1, 256, 64, 1, FAKE, None) == INVALID
+    assert orf(FAKE, None, 1, -2, 64, 1, FAKE, None) == INVALID
+    assert orf(FAKE, None, 1, 256, 0, 1, FAKE, None) == INVALID
+    assert orf(FAKE, None, 1, 256, 64, 2, FAKE, None) == INVALID
+    assert orf(FAKE, None, 1, 256, 65, 1, FAKE, None) == UNSUPPORTED
+    assert orf(FAKE, None, 0, 256, 64, 1, FAKE, None) == OK
+    assert orf(FAKE, None, 1, 0, 64, 1, FAKE, None) == OK

@@ -368,3 +368,60 @@ def test_workload_favor_causal_packed(gpu_lib):
     assert_parity(o, ro, 2e-2, "packed out", lead_dims=1)
     assert_parity(S, rS, 2e-2, "packed S")
     assert_parity(z, rz, 2e-2, "packed z")
+
+
+# ---------------------------------------------------------------- on-device ORF
+def _orf_case(n_mat, r, d, wid, with_lengths=True):
+    draws = [inputs.orf_draws(r, d, wid, rep) for rep in range(n_mat)]
+    gauss = np.stack([g for g, _ in draws])
+    lens = np.stack([l for _, l in draws]) if with_lengths else None
+    ref = np.stack([oracle.orf(gauss[m], r, None if lens is None else lens[m]) for m in range(n_mat)])
+    g_d = torch.from_numpy(gauss).to("cuda")
+    l_d = None if lens is None else torch.from_numpy(lens).to("cuda")
+    return g_d, l_d, ref
+
+
+@pytest.mark.parametrize("n_mat,r,d,lengths", [(3, 256, 64, True), (2, 100, 48, True),
+                                               (1, 64, 64, False), (4, 33, 7, True)])
+def test_orf_omega_float32(gpu_lib, n_mat, r, d, lengths):
+    g, l, ref = _orf_case(n_mat, r, d, 110, lengths)
+    om = gpu_lib.lin_attn_orf_omega(g, l, r=r, dtype=torch.float32)
+    got = host(om)
+    want = ref.astype(np.float32).astype(np.float64)
+    # float64 arithmetic on both sides, rounded once to float32: equal up to
+    # a rounding-boundary ulp
+    assert np.max(np.abs(got - want) / np.maximum(np.abs(want), 1e-30)) <= 2.0 ** -22
+    # rows orthogonal within each block
+    for m in range(n_mat):
+        for b in range(0, r, d):
+            blk = got[m, b:b + d]
+            gram = blk @ blk.T
+            off = gram - np.diag(np.diag(gram))
+            assert np.max(np.abs(off)) < 1e-5 * np.max(np.diag(gram))
+
+
+def test_orf_omega_bfloat16(gpu_lib):
+    g, l, ref = _orf_case(12, 256, 64, 111)
+    om = gpu_lib.lin_attn_orf_omega(g, l, dtype=torch.bfloat16)
+    want = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16)
+    got = om.cpu()
+    # the same rounding (float64 -> float32 -> bfloat16, nearest-even) on both
+    # sides: bit-equal except at a rounding boundary, where one ulp apart
+    bits_got = got.view(torch.int16).to(torch.int32)
+    bits_want = want.view(torch.int16).to(torch.int32)
+    diff = (bits_got - bits_want).abs()
+    assert int(diff.max()) <= 1
+    assert int((diff > 0).sum()) <= got.numel() // 1000
+
+
+def test_orf_omega_drives_favor_like_the_host_sampler(gpu_lib):
+    """Attention with the device-built omega matches the oracle run with the
+    oracle-built omega (bfloat16 inputs, r = 256: the matrix-core path)."""
+    g, l, ref = _orf_case(1, 256, 64, 112)
+    om = gpu_lib.lin_attn_orf_omega(g[0], l[0], dtype=torch.bfloat16)
+    c = Case(112, 1, 2, 300, "favor", torch.bfloat16, r=256)
+    kw = dict(scale=64 ** -0.25)
+    out, S, z = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, "favor", omega=om, **kw)
+    ro, rS, rz = oracle.causal(c.qh, c.kh, c.vh, "favor", omega=host(om), **kw)
+    assert_parity(out, ro, 2e-2, "orf causal out")
+    np.testing.assert_allclose(host(om), ref[0], rtol=2 ** -8, atol=1e-6)

@@ -451,3 +451,38 @@ def test_varlen_sequences_do_not_see_each_other():
         assert np.array_equal(out[:, a:b], out2[:, a:b])
     assert np.array_equal(S[[0, 2]], S2[[0, 2]]) and np.array_equal(z[[0, 2]], z2[[0, 2]])
     assert not np.array_equal(out[:, 5:13], out2[:, 5:13])
+
+
+# --------------------------------------------------------------------------
+# Orthogonal random features (Performer page sec. 2 step 4; Kernel Zoo
+# sec. 5.1-5.3), the oracle's own Gram-Schmidt
+# --------------------------------------------------------------------------
+
+def test_orf_oracle_reproduces_the_worked_example():
+    """Kernel Zoo sec. 5.3: Gram-Schmidt of (0.5, -0.3), (-0.8, 1.2), rows
+    scaled to sqrt(d) = sqrt(2)."""
+    g = golden("orf_2d.json")
+    om = oracle.orf(A(g["omega"])[None], 2)
+    np.testing.assert_allclose(om, g["omega_ort"], atol=g["tolerance_abs"])
+    assert abs(om[0] @ om[1]) < 1e-14  # rows of squared length 2
+
+
+def test_orf_oracle_equals_sign_fixed_qr_and_chi_lengths():
+    """Gram-Schmidt on the rows of a block is Q^T of the QR factorisation of
+    the block's transpose with diag(R) > 0 (a library routine as the
+    reference); each row's length is the norm of its len_gauss row; the last
+    block is cut at r rows."""
+    g = np.random.default_rng(71)
+    d, r = 12, 30
+    gauss = g.standard_normal((3, d, d))
+    lens = g.standard_normal((3 * d, d))
+    om = oracle.orf(gauss, r, lens)
+    for b in range(3):
+        q, rr = np.linalg.qr(gauss[b].T)
+        rows = (q * np.sign(np.diag(rr))).T
+        n = min(d, r - b * d)
+        want = rows[:n] * np.linalg.norm(lens[b * d:b * d + n], axis=1)[:, None]
+        np.testing.assert_allclose(om[b * d:b * d + n], want, rtol=1e-10, atol=1e-12)
+    blk = om[:d]
+    gram = blk @ blk.T
+    np.testing.assert_allclose(gram - np.diag(np.diag(gram)), 0.0, atol=1e-12)

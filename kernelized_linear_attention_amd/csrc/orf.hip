@@ -4,18 +4,20 @@
 // to the length of an independent Gaussian vector (or to sqrt(d)).  The
 // Gaussian draws are inputs: the caller's generator makes them.
 //
-// One workgroup per (matrix, block), d <= 64.  The block is orthogonalised
-// in float64 in LDS, row by row in order; each row has its projections on
-// the earlier rows removed twice (classical Gram-Schmidt with one
+// One wave per (matrix, block), d <= 64.  The block is orthogonalised in
+// float64 in LDS, row by row in order; each row has its projections on the
+// earlier rows removed twice (classical Gram-Schmidt with one
 // reorthogonalisation pass: the pages' procedure in exact arithmetic, and
-// orthogonal to float64 precision in floating point).  The dot products of
-// one pass run in parallel, one wave per earlier row.
+// orthogonal to float64 precision in floating point).  Lane j forms the dot
+// product with earlier row j by a loop over the columns and lane k updates
+// column k, so no step needs a cross-lane reduction except the row norm;
+// a single wave needs no barrier (its LDS accesses complete in order).
 #include "launch.hpp"
 
 namespace linattn {
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 64;
 constexpr int DMAX = 64;
 constexpr int LD = DMAX + 1; // LDS row stride (doubles)
 
@@ -25,46 +27,45 @@ __device__ __forceinline__ double wave_sum_d(double x) {
     return x;
 }
 
-template <typename T>
+// DC: the row length as a constant (64: every loop unrolls, so the LDS reads
+// of a dot product are issued together), or 0 for any d <= 64.
+template <typename T, int DC>
 __global__ __launch_bounds__(NT) void k_orf(const float* __restrict__ gauss,
-                                            const float* __restrict__ len_gauss, int64_t r, int d,
+                                            const float* __restrict__ len_gauss, int64_t r, int d_,
                                             int64_t nblk, T* __restrict__ omega) {
+    const int d = DC ? DC : d_;
     __shared__ double e_s[DMAX * LD];
     __shared__ double c_s[DMAX];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lane = threadIdx.x;
     const int64_t m = blockIdx.x / nblk, b = blockIdx.x % nblk;
     const float* g = gauss + (m * nblk + b) * d * d;
 
-    for (int x = tid; x < d * d; x += NT) e_s[(x / d) * LD + x % d] = (double)g[x];
-    __syncthreads();
+    for (int x = lane; x < d * d; x += NT) e_s[(x / d) * LD + x % d] = (double)g[x];
 
     for (int i = 0; i < d; ++i) {
         double* ei = e_s + i * LD;
         for (int pass = 0; pass < 2; ++pass) {
-            // c_j = e_j . e_i for the earlier rows j, one wave per row
-            for (int j = w; j < i; j += NT / 64) {
-                const double p = lane < d ? e_s[j * LD + lane] * ei[lane] : 0.0;
-                const double s = wave_sum_d(p);
-                if (lane == 0) c_s[j] = s;
+            if (lane < i) { // c_j = e_j . e_i
+                const double* ej = e_s + lane * LD;
+                double c[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll(DC ? DC : 1)
+                for (int k = 0; k < d; ++k) c[k & 3] = fma(ej[k], ei[k], c[k & 3]);
+                c_s[lane] = (c[0] + c[1]) + (c[2] + c[3]);
             }
-            __syncthreads();
-            if (tid < d) {
-                double x = ei[tid];
-                for (int j = 0; j < i; ++j) x -= c_s[j] * e_s[j * LD + tid];
-                ei[tid] = x;
+            if (lane < d) { // e_i -= sum_j c_j e_j
+                double x = ei[lane];
+                for (int j = 0; j < i; ++j) x = fma(-c_s[j], e_s[j * LD + lane], x);
+                ei[lane] = x;
             }
-            __syncthreads();
         }
-        if (w == 0) {
-            const double n2 = wave_sum_d(lane < d ? ei[lane] * ei[lane] : 0.0);
-            if (lane < d) ei[lane] = ei[lane] / sqrt(n2);
-        }
-        __syncthreads();
+        const double x = lane < d ? ei[lane] : 0.0;
+        const double n2 = wave_sum_d(x * x);
+        if (lane < d) ei[lane] = x / sqrt(n2);
     }
 
     // rows of this block that exist (the last block may be cut at r)
     const int rows = (int)min<int64_t>(d, r - b * d);
-    for (int i = w; i < rows; i += NT / 64) {
+    for (int i = 0; i < rows; ++i) {
         const int64_t f = b * d + i;
         double len = sqrt((double)d);
         if (len_gauss) {
@@ -81,12 +82,21 @@ hipError_t launch_orf(const float* gauss, const float* len_gauss, int64_t n_mat,
                       int dtype, void* omega, hipStream_t st) {
     const int64_t nblk = (r + d - 1) / d;
     const dim3 grid((unsigned)(n_mat * nblk)), block(NT);
-    if (dtype == 0)
-        hipLaunchKernelGGL(k_orf<float>, grid, block, 0, st, gauss, len_gauss, r, d, nblk,
-                           (float*)omega);
-    else
-        hipLaunchKernelGGL(k_orf<bf16_raw>, grid, block, 0, st, gauss, len_gauss, r, d, nblk,
-                           (bf16_raw*)omega);
+    if (dtype == 0) {
+        if (d == DMAX)
+            hipLaunchKernelGGL((k_orf<float, DMAX>), grid, block, 0, st, gauss, len_gauss, r, d,
+                               nblk, (float*)omega);
+        else
+            hipLaunchKernelGGL((k_orf<float, 0>), grid, block, 0, st, gauss, len_gauss, r, d, nblk,
+                               (float*)omega);
+    } else {
+        if (d == DMAX)
+            hipLaunchKernelGGL((k_orf<bf16_raw, DMAX>), grid, block, 0, st, gauss, len_gauss, r, d,
+                               nblk, (bf16_raw*)omega);
+        else
+            hipLaunchKernelGGL((k_orf<bf16_raw, 0>), grid, block, 0, st, gauss, len_gauss, r, d,
+                               nblk, (bf16_raw*)omega);
+    }
     return hipGetLastError();
 }
 

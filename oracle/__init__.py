@@ -19,7 +19,10 @@ Definitions followed (see the header of oracle.c for the passages):
     each boundary ("Reassociate a feature-map kernel..." par. 4);
   * explicit N x N form: the interactive chapter's "rescan every key";
   * orthogonal random features: Performer page sec. 2 step 4, Kernel Zoo
-    sec. 5.1-5.3 (Gram-Schmidt of Gaussian rows, chi or sqrt(d) lengths).
+    sec. 5.1-5.3 (Gram-Schmidt of Gaussian rows, chi or sqrt(d) lengths);
+  * backward pass: the chain rule through the readout, the summaries and
+    the feature map ("Reassociate a feature-map kernel..." par. 6 asks for
+    gradient error to be evaluated).
 """
 import ctypes
 import os
@@ -63,6 +66,10 @@ def _load():
     lib.orc_explicit.restype = I
     lib.orc_orf.argtypes = [P, P, L, L, P]
     lib.orc_orf.restype = I
+    for name in ("orc_bidir_backward", "orc_causal_backward"):
+        fn = getattr(lib, name)
+        fn.argtypes = [I, I, I, I, I, D, D, P, P, P, P, L, L, L, L, P, P, P, P]
+        fn.restype = I
     _lib = lib
     return lib
 
@@ -248,3 +255,37 @@ def orf(gauss, r, len_gauss=None):
     if _load().orc_orf(_ptr(g), _ptr(lg), r, d, _ptr(out)):
         raise ValueError("oracle orf: invalid argument")
     return out
+
+
+def _backward(fname, q, k, v, dout, kind, omega, nu, sum_norm, norm, scale, eps):
+    q, lead, BH, N, d = _split(q)
+    k = _f64(k)
+    v = _f64(v)
+    dout = _f64(dout)
+    dv = v.shape[-1]
+    om = _f64(omega)
+    kk, r = _cfg(kind, d, nu, om)
+    dq = np.zeros(lead + (N, d))
+    dk = np.zeros(lead + (N, d))
+    dvv = np.zeros(lead + (N, dv))
+    rc = getattr(_load(), fname)(kk, r, nu, int(bool(sum_norm)), _NORMS[norm], float(scale),
+                                 float(eps), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), BH, N, d, dv,
+                                 _ptr(om), _ptr(dq), _ptr(dk), _ptr(dvv))
+    if rc:
+        raise ValueError(f"oracle {fname}: invalid argument")
+    return dq, dk, dvv
+
+
+def bidir_backward(q, k, v, dout, kind, *, omega=None, nu=1, sum_norm=False, norm="attn",
+                   scale=1.0, eps=1e-6):
+    """Gradients (dq, dk, dv) of sum(out * dout) for the bidirectional form."""
+    return _backward("orc_bidir_backward", q, k, v, dout, kind, omega, nu, sum_norm, norm,
+                     scale, eps)
+
+
+def causal_backward(q, k, v, dout, kind, *, omega=None, nu=1, sum_norm=False, norm="attn",
+                    scale=1.0, eps=1e-6):
+    """Gradients (dq, dk, dv) of sum(out * dout) for the causal recurrence
+    from zero state."""
+    return _backward("orc_causal_backward", q, k, v, dout, kind, omega, nu, sum_norm, norm,
+                     scale, eps)

@@ -426,3 +426,255 @@ int orc_orf(const double *gauss, const double *len_gauss, long r, long d, double
     free(e);
     return 0;
 }
+
+/*
+ * Backward pass: the gradients of a loss L with respect to q, k and v given
+ * dL/dout ([RF] par. 6 asks for gradient error to be evaluated; the
+ * derivatives are the chain rule through the definitions above).  With
+ * D_i = max(den_i, eps):
+ *   ATTN: dnum_i = dout_i / D_i,  dden_i = -(dout_i . out_i) / D_i when
+ *         den_i > eps (0 where the clamp holds D_i fixed)
+ *   NONE: dnum_i = dout_i,        dden_i = 0
+ *   dphi(q_i) = S_i dnum_i + z_i dden_i      (S_i, z_i: what query i read)
+ *   dphi(k_j) = sum over the queries i that see key j of
+ *               phi(q_i) (dnum_i . v_j + dden_i)
+ *   dv_j      = sum over the same i of dnum_i (phi(q_i) . phi(k_j))
+ * and dx = scale * J_phi(u)^T dphi at u = scale * x, J_phi from the map's
+ * definition (orc_phi_backward).
+ */
+
+/* dx = scale * J_phi(u)^T dphi for one vector x (u = scale * x).
+ * work must hold at least 3d + 2r doubles. */
+static void orc_phi_backward(const orc_cfg *c, const double *x, long d, const double *omega,
+                             const double *dphi, double *dx, double *work)
+{
+    double *u = work;                 /* d */
+    double *kt = work + d;            /* 2d (DPFP) */
+    double *p = work + 3 * d;         /* r: the map before sum normalisation */
+    double *dp = work + 3 * d + c->r; /* r */
+    for (long i = 0; i < d; ++i) u[i] = c->scale * x[i];
+    long r = c->r;
+
+    /* the map before normalisation */
+    if (c->phi == ORC_PHI_IDENTITY) {
+        for (long i = 0; i < d; ++i) p[i] = u[i];
+    } else if (c->phi == ORC_PHI_ELU1) {
+        for (long i = 0; i < d; ++i) p[i] = (u[i] > 0.0 ? u[i] : expm1(u[i])) + 1.0;
+    } else if (c->phi == ORC_PHI_FAVOR) {
+        double sq = 0.0;
+        for (long i = 0; i < d; ++i) sq += u[i] * u[i];
+        for (long f = 0; f < r; ++f) {
+            double dot = 0.0;
+            for (long i = 0; i < d; ++i) dot += omega[f * d + i] * u[i];
+            p[f] = exp(dot - 0.5 * sq) / sqrt((double)r);
+        }
+    } else {
+        for (long i = 0; i < d; ++i) {
+            kt[i] = u[i] > 0.0 ? u[i] : 0.0;
+            kt[d + i] = -u[i] > 0.0 ? -u[i] : 0.0;
+        }
+        long two_d = 2 * d;
+        for (long s = 1; s <= c->nu; ++s)
+            for (long i = 0; i < two_d; ++i)
+                p[(s - 1) * two_d + i] = kt[i] * kt[(i + s) % two_d];
+    }
+
+    /* through the sum normalisation phi = p / max(sum p, eps) */
+    if (c->sum_norm) {
+        double sum = 0.0;
+        for (long f = 0; f < r; ++f) sum += p[f];
+        double den = sum > c->eps ? sum : c->eps;
+        double dot = 0.0; /* dphi . phi */
+        for (long f = 0; f < r; ++f) dot += dphi[f] * (p[f] / den);
+        for (long f = 0; f < r; ++f)
+            dp[f] = (dphi[f] - (sum > c->eps ? dot : 0.0)) / den;
+    } else {
+        for (long f = 0; f < r; ++f) dp[f] = dphi[f];
+    }
+
+    /* through the map */
+    double *du = dx;
+    if (c->phi == ORC_PHI_IDENTITY) {
+        for (long i = 0; i < d; ++i) du[i] = dp[i];
+    } else if (c->phi == ORC_PHI_ELU1) {
+        for (long i = 0; i < d; ++i) du[i] = dp[i] * (u[i] > 0.0 ? 1.0 : exp(u[i]));
+    } else if (c->phi == ORC_PHI_FAVOR) {
+        /* d p_f / d u = p_f (omega_f - u) */
+        double w = 0.0;
+        for (long f = 0; f < r; ++f) w += dp[f] * p[f];
+        for (long i = 0; i < d; ++i) {
+            double s = 0.0;
+            for (long f = 0; f < r; ++f) s += dp[f] * p[f] * omega[f * d + i];
+            du[i] = s - w * u[i];
+        }
+    } else {
+        long two_d = 2 * d;
+        double *dkt = p; /* p is no longer needed */
+        for (long m = 0; m < two_d; ++m) dkt[m] = 0.0;
+        for (long s = 1; s <= c->nu; ++s)
+            for (long i = 0; i < two_d; ++i) {
+                double g = dp[(s - 1) * two_d + i];
+                dkt[i] += g * kt[(i + s) % two_d];
+                dkt[(i + s) % two_d] += g * kt[i];
+            }
+        for (long i = 0; i < d; ++i)
+            du[i] = (u[i] > 0.0 ? dkt[i] : 0.0) - (-u[i] > 0.0 ? dkt[d + i] : 0.0);
+    }
+    for (long i = 0; i < d; ++i) dx[i] = c->scale * du[i];
+}
+
+/* dnum, dden of one query from its readout inputs and dout. */
+static void orc_readout_backward(const orc_cfg *c, const double *pq, const double *S,
+                                 const double *z, long dv, const double *dout, double *dnum,
+                                 double *dden)
+{
+    double den = 0.0;
+    for (long f = 0; f < c->r; ++f) den += pq[f] * z[f];
+    if (c->norm == ORC_NORM_ATTN) {
+        double D = den > c->eps ? den : c->eps;
+        double go = 0.0; /* dout . out */
+        for (long n = 0; n < dv; ++n) {
+            double num = 0.0;
+            for (long f = 0; f < c->r; ++f) num += pq[f] * S[f * dv + n];
+            go += dout[n] * (num / D);
+            dnum[n] = dout[n] / D;
+        }
+        *dden = den > c->eps ? -go / D : 0.0;
+    } else {
+        for (long n = 0; n < dv; ++n) dnum[n] = dout[n];
+        *dden = 0.0;
+    }
+}
+
+/* dphi(q) = S dnum + z dden */
+static void orc_dphi_q(const orc_cfg *c, const double *S, const double *z, long dv,
+                       const double *dnum, double dden, double *dpq)
+{
+    for (long f = 0; f < c->r; ++f) {
+        double s = z[f] * dden;
+        for (long n = 0; n < dv; ++n) s += S[f * dv + n] * dnum[n];
+        dpq[f] = s;
+    }
+}
+
+/* key side from the accumulated G = sum phi(q_i) dnum_i^T, g = sum phi(q_i) dden_i */
+static void orc_key_grads(const orc_cfg *c, const double *G, const double *g, const double *pk,
+                          const double *v, long dv, double *dpk, double *dvj)
+{
+    for (long f = 0; f < c->r; ++f) {
+        double s = g[f];
+        for (long n = 0; n < dv; ++n) s += G[f * dv + n] * v[n];
+        dpk[f] = s;
+    }
+    for (long n = 0; n < dv; ++n) {
+        double s = 0.0;
+        for (long f = 0; f < c->r; ++f) s += G[f * dv + n] * pk[f];
+        dvj[n] = s;
+    }
+}
+
+/* Gradients of the bidirectional form (every query sees every key). */
+int orc_bidir_backward(int phi, int r, int nu, int sum_norm, int norm, double scale, double eps,
+                       const double *q, const double *k, const double *v, const double *dout,
+                       long BH, long N, long d, long dv, const double *omega, double *dq,
+                       double *dk, double *dvo)
+{
+    orc_cfg c = {phi, r, nu, sum_norm, norm, scale, eps};
+    if (orc_check(&c, d) || BH < 0 || N < 0 || dv <= 0) return -1;
+    if (phi == ORC_PHI_FAVOR && !omega) return -1;
+#pragma omp parallel
+    {
+        double *work = (double *)malloc(sizeof(double) * (3 * (size_t)d + 2 * (size_t)r));
+        double *pk = (double *)malloc(sizeof(double) * (size_t)r);
+        double *pq = (double *)malloc(sizeof(double) * (size_t)r);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)r);
+        double *S = (double *)malloc(sizeof(double) * (size_t)r * dv);
+        double *z = (double *)malloc(sizeof(double) * (size_t)r);
+        double *G = (double *)malloc(sizeof(double) * (size_t)r * dv);
+        double *g = (double *)malloc(sizeof(double) * (size_t)r);
+        double *dnum = (double *)malloc(sizeof(double) * (size_t)dv);
+#pragma omp for schedule(dynamic, 1)
+        for (long bh = 0; bh < BH; ++bh) {
+            memset(S, 0, sizeof(double) * (size_t)r * dv);
+            memset(z, 0, sizeof(double) * (size_t)r);
+            memset(G, 0, sizeof(double) * (size_t)r * dv);
+            memset(g, 0, sizeof(double) * (size_t)r);
+            for (long j = 0; j < N; ++j) {
+                orc_phi(&c, k + (bh * N + j) * d, d, omega, pk, work);
+                orc_write(&c, pk, v + (bh * N + j) * dv, dv, S, z);
+            }
+            for (long i = 0; i < N; ++i) {
+                double dden;
+                orc_phi(&c, q + (bh * N + i) * d, d, omega, pq, work);
+                orc_readout_backward(&c, pq, S, z, dv, dout + (bh * N + i) * dv, dnum, &dden);
+                orc_dphi_q(&c, S, z, dv, dnum, dden, dp);
+                orc_phi_backward(&c, q + (bh * N + i) * d, d, omega, dp, dq + (bh * N + i) * d, work);
+                for (long f = 0; f < r; ++f) {
+                    for (long n = 0; n < dv; ++n) G[f * dv + n] += pq[f] * dnum[n];
+                    g[f] += pq[f] * dden;
+                }
+            }
+            for (long j = 0; j < N; ++j) {
+                orc_phi(&c, k + (bh * N + j) * d, d, omega, pk, work);
+                orc_key_grads(&c, G, g, pk, v + (bh * N + j) * dv, dv, dp, dvo + (bh * N + j) * dv);
+                orc_phi_backward(&c, k + (bh * N + j) * d, d, omega, dp, dk + (bh * N + j) * d, work);
+            }
+        }
+        free(work); free(pk); free(pq); free(dp); free(S); free(z); free(G); free(g); free(dnum);
+    }
+    return 0;
+}
+
+/* Gradients of the causal recurrence from zero state: a forward sweep
+ * (query i reads the state after key i) gives dq and stores phi(q_i),
+ * dnum_i, dden_i; a backward sweep accumulates G, g over the queries
+ * i >= j that see key j. */
+int orc_causal_backward(int phi, int r, int nu, int sum_norm, int norm, double scale, double eps,
+                        const double *q, const double *k, const double *v, const double *dout,
+                        long BH, long N, long d, long dv, const double *omega, double *dq,
+                        double *dk, double *dvo)
+{
+    orc_cfg c = {phi, r, nu, sum_norm, norm, scale, eps};
+    if (orc_check(&c, d) || BH < 0 || N < 0 || dv <= 0) return -1;
+    if (phi == ORC_PHI_FAVOR && !omega) return -1;
+#pragma omp parallel
+    {
+        double *work = (double *)malloc(sizeof(double) * (3 * (size_t)d + 2 * (size_t)r));
+        double *pk = (double *)malloc(sizeof(double) * (size_t)r);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)r);
+        double *S = (double *)malloc(sizeof(double) * (size_t)r * dv);
+        double *z = (double *)malloc(sizeof(double) * (size_t)r);
+        double *PQ = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * r);
+        double *DN = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * dv);
+        double *DD = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (long bh = 0; bh < BH; ++bh) {
+            memset(S, 0, sizeof(double) * (size_t)r * dv);
+            memset(z, 0, sizeof(double) * (size_t)r);
+            for (long t = 0; t < N; ++t) {
+                orc_phi(&c, k + (bh * N + t) * d, d, omega, pk, work);
+                orc_write(&c, pk, v + (bh * N + t) * dv, dv, S, z);
+                double *pq = PQ + t * r;
+                orc_phi(&c, q + (bh * N + t) * d, d, omega, pq, work);
+                orc_readout_backward(&c, pq, S, z, dv, dout + (bh * N + t) * dv, DN + t * dv, DD + t);
+                orc_dphi_q(&c, S, z, dv, DN + t * dv, DD[t], dp);
+                orc_phi_backward(&c, q + (bh * N + t) * d, d, omega, dp, dq + (bh * N + t) * d, work);
+            }
+            /* S, z reused as G, g */
+            memset(S, 0, sizeof(double) * (size_t)r * dv);
+            memset(z, 0, sizeof(double) * (size_t)r);
+            for (long t = N - 1; t >= 0; --t) {
+                const double *pq = PQ + t * r;
+                for (long f = 0; f < r; ++f) {
+                    for (long n = 0; n < dv; ++n) S[f * dv + n] += pq[f] * DN[t * dv + n];
+                    z[f] += pq[f] * DD[t];
+                }
+                orc_phi(&c, k + (bh * N + t) * d, d, omega, pk, work);
+                orc_key_grads(&c, S, z, pk, v + (bh * N + t) * dv, dv, dp, dvo + (bh * N + t) * dv);
+                orc_phi_backward(&c, k + (bh * N + t) * d, d, omega, dp, dk + (bh * N + t) * d, work);
+            }
+        }
+        free(work); free(pk); free(dp); free(S); free(z); free(PQ); free(DN); free(DD);
+    }
+    return 0;
+}

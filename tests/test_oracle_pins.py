@@ -486,3 +486,77 @@ def test_orf_oracle_equals_sign_fixed_qr_and_chi_lengths():
     blk = om[:d]
     gram = blk @ blk.T
     np.testing.assert_allclose(gram - np.diag(np.diag(gram)), 0.0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Backward pass: the oracle's analytic gradients against central finite
+# differences of the pinned forward oracle (the chain rule through the
+# readout, the summaries and every feature map; "Reassociate a feature-map
+# kernel..." par. 6 asks for gradient error to be evaluated)
+# --------------------------------------------------------------------------
+
+def _finite_difference(fwd, args, dout, h=1e-5):
+    """d sum(fwd(*args) * dout) / d args[a], for a in 0..2, by central
+    differences on every element."""
+    grads = []
+    for a in range(3):
+        x = args[a]
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = float(np.sum(fwd(*args) * dout))
+            x[idx] = old - h
+            lm = float(np.sum(fwd(*args) * dout))
+            x[idx] = old
+            g[idx] = (lp - lm) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("form", ["bidir", "causal"])
+@pytest.mark.parametrize("kind,extra,sum_norm", KIND_CASES)
+@pytest.mark.parametrize("norm", ["attn", "none"])
+def test_backward_equals_finite_differences(form, kind, extra, sum_norm, norm):
+    q, k, v, om = _tiny(31, BH=2, N=5, d=4, dv=3, r=extra.get("r") and 12)
+    if kind == "identity" and norm == "attn":
+        q, k = np.abs(q) + 0.1, np.abs(k) + 0.1  # denominators far from the clamp
+    dout = np.random.default_rng(32).standard_normal(v.shape)
+    kw = dict(omega=om, nu=extra.get("nu", 1), sum_norm=sum_norm, norm=norm, scale=0.8)
+    fwd_fn = oracle.bidir if form == "bidir" else oracle.causal
+    bwd_fn = oracle.bidir_backward if form == "bidir" else oracle.causal_backward
+    got = bwd_fn(q, k, v, dout, kind, **kw)
+    want = _finite_difference(lambda a, b, c: fwd_fn(a, b, c, kind, **kw)[0], [q, k, v], dout)
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("form", ["bidir", "causal"])
+def test_backward_through_the_eps_clamp(form):
+    """Where every denominator is below eps the clamp holds D = eps, so the
+    output is num / eps and the denominator carries no gradient."""
+    q, k, v, _ = _tiny(33, BH=2, N=5, d=4, dv=3)
+    dout = np.random.default_rng(34).standard_normal(v.shape)
+    kw = dict(norm="attn", eps=1e3)
+    fwd_fn = oracle.bidir if form == "bidir" else oracle.causal
+    bwd_fn = oracle.bidir_backward if form == "bidir" else oracle.causal_backward
+    got = bwd_fn(q, k, v, dout, "elu1", **kw)
+    want = _finite_difference(lambda a, b, c: fwd_fn(a, b, c, "elu1", **kw)[0], [q, k, v], dout)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-6, atol=1e-9)
+    # and it is the unnormalised gradient scaled by 1/eps
+    ref = bwd_fn(q, k, v, dout / 1e3, "elu1", norm="none")
+    for g, w in zip(got, ref):
+        np.testing.assert_allclose(g, w, rtol=1e-12, atol=1e-15)
+
+
+def test_causal_backward_of_last_row_equals_bidirectional():
+    """The last query sees every key in both forms (Kernel Zoo sec. 5.4 with
+    i = N): a loss on that row alone has the same gradients."""
+    q, k, v, om = _tiny(35, BH=2, N=7, d=4, dv=3, r=16)
+    dout = np.zeros(v.shape)
+    dout[:, -1] = np.random.default_rng(36).standard_normal((2, 3))
+    kw = dict(omega=om, scale=0.7)
+    for a, b in zip(oracle.causal_backward(q, k, v, dout, "favor", **kw),
+                    oracle.bidir_backward(q, k, v, dout, "favor", **kw)):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)

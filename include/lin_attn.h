@@ -1,6 +1,7 @@
 /*
  * lin_attn.h -- C ABI of liblinattn.so: kernelized linear attention on
- * AMD MI355X (gfx950), forward pass.
+ * AMD MI355X (gfx950): forward pass, decode, orthogonal random features and
+ * the backward pass.
  *
  * Sources of the operations (the pages the method is taken from):
  *   [KZ] "The Kernel Zoo: Performers, Fast Weight Programmers, and the
@@ -79,6 +80,8 @@ extern "C" {
 #define LIN_ATTN_OP_BIDIR 1
 #define LIN_ATTN_OP_CAUSAL 2
 #define LIN_ATTN_OP_CAUSAL_VARLEN 3
+#define LIN_ATTN_OP_BIDIR_BACKWARD 4
+#define LIN_ATTN_OP_CAUSAL_BACKWARD 5
 
 /*
  * Method parameters, shared by every call.
@@ -229,9 +232,41 @@ int lin_attn_orf_omega(const float* gauss, const float* len_gauss, int64_t n_mat
                        int64_t d, int32_t dtype, void* omega, void* stream);
 
 /*
+ * Backward pass: the gradients dq, dk, dv of a loss L given dout = dL/dout
+ * for the outputs of lin_attn_bidir (lin_attn_bidir_backward) or of
+ * lin_attn_causal_chunked from zero state (lin_attn_causal_backward), same
+ * parameters and inputs.  [RF] par. 6 asks for gradient error to be
+ * evaluated; the derivatives are the chain rule through the definitions of
+ * those calls.  With D_i = max(den_i, eps):
+ *   dnum_i = dout_i / D_i, dden_i = -(dout_i . out_i) / D_i where den_i > eps,
+ *   0 where the clamp holds (NORM_NONE: dnum_i = dout_i, dden_i = 0);
+ *   dphi(q_i) = S_i dnum_i + z_i dden_i, with (S_i, z_i) the state query i reads;
+ *   dphi(k_j) = G_j v_j + g_j and dv_j = G_j^T phi(k_j), with (G_j, g_j) the
+ *   sum of (phi(q_i) dnum_i^T, phi(q_i) dden_i) over the queries that see
+ *   key j (every query; causal: i >= j);
+ *   dx = scale * J_phi(scale * x)^T dphi(x) for x = q_i, k_j, through the
+ *   sum normalisation when it is on.
+ * omega is a constant ([PF] sec. 2: sampled once and frozen): no gradient.
+ *   q, k, dq, dk [B, H, N, d]; v, dout, dv [B, H, N, dv]; all of the input
+ *   dtype (float32 arithmetic inside).  dq, dk, dv are overwritten.
+ *   ws  at least lin_attn_workspace_bytes(LIN_ATTN_OP_BIDIR_BACKWARD or
+ *       LIN_ATTN_OP_CAUSAL_BACKWARD, ...) bytes; contents on entry ignored.
+ * Errors as lin_attn_bidir.
+ */
+int lin_attn_bidir_backward(const lin_attn_params* p, const void* q, const void* k,
+                            const void* v, const void* dout, int64_t B, int64_t H, int64_t N,
+                            int64_t d, int64_t dv, const void* omega, void* dq, void* dk,
+                            void* dv_out, void* ws, size_t ws_bytes, void* stream);
+int lin_attn_causal_backward(const lin_attn_params* p, const void* q, const void* k,
+                             const void* v, const void* dout, int64_t B, int64_t H, int64_t N,
+                             int64_t d, int64_t dv, const void* omega, void* dq, void* dk,
+                             void* dv_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Workspace bytes needed by lin_attn_bidir (op = LIN_ATTN_OP_BIDIR),
  * lin_attn_causal_chunked (op = LIN_ATTN_OP_CAUSAL) or, with B = num_seqs and
- * N = total, lin_attn_causal_varlen (op = LIN_ATTN_OP_CAUSAL_VARLEN).
+ * N = total, lin_attn_causal_varlen (op = LIN_ATTN_OP_CAUSAL_VARLEN), and
+ * the backward calls (LIN_ATTN_OP_BIDIR_BACKWARD, LIN_ATTN_OP_CAUSAL_BACKWARD).
  * Host-only, deterministic in its arguments (independent of the device).
  * Returns 0 for invalid arguments.
  */

@@ -28,11 +28,14 @@ DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 OP_BIDIR = 1
 OP_CAUSAL = 2
 OP_CAUSAL_VARLEN = 3
+OP_BIDIR_BACKWARD = 4
+OP_CAUSAL_BACKWARD = 5
 ABI_VERSION = 1
 
 # Every symbol include/lin_attn.h declares.
 EXPORTS = ("lin_attn_featuremap", "lin_attn_bidir", "lin_attn_causal_chunked",
-           "lin_attn_causal_varlen", "lin_attn_orf_omega",
+           "lin_attn_causal_varlen", "lin_attn_orf_omega", "lin_attn_bidir_backward",
+           "lin_attn_causal_backward",
            "lin_attn_decode_step", "lin_attn_workspace_bytes", "lin_attn_strerror",
            "lin_attn_abi_version")
 
@@ -61,6 +64,10 @@ _lib.lin_attn_causal_varlen.argtypes = [_PP, _P, _P, _P, _P, _I64, _I64, _I64, _
 _lib.lin_attn_causal_varlen.restype = ctypes.c_int
 _lib.lin_attn_orf_omega.argtypes = [_P, _P, _I64, _I64, _I64, _I32, _P, _P]
 _lib.lin_attn_orf_omega.restype = ctypes.c_int
+for _fn in (_lib.lin_attn_bidir_backward, _lib.lin_attn_causal_backward):
+    _fn.argtypes = [_PP, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P,
+                    ctypes.c_size_t, _P]
+    _fn.restype = ctypes.c_int
 _lib.lin_attn_decode_step.argtypes = [_PP, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.lin_attn_decode_step.restype = ctypes.c_int
 _lib.lin_attn_workspace_bytes.argtypes = [_I32, _PP, _I64, _I64, _I64, _I64, _I64, _I32]
@@ -303,6 +310,45 @@ def lin_attn_decode_step(q, k, v, S, z, kind, *, omega=None, nu=1, sum_norm=Fals
                                    _stream(q.device, stream))
     _check("lin_attn_decode_step", rc)
     return out
+
+
+def _backward(name, op, q, k, v, dout, kind, omega, nu, sum_norm, norm, scale, eps, n_seg,
+              workspace, stream):
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _dev_tensor(n, t, q.dtype)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    om = _omega(kind, omega, q.dtype)
+    r = feature_width(kind, d, nu, om)
+    p = make_params(kind, r, nu=nu, sum_norm=sum_norm, norm=norm, dtype=q.dtype, scale=scale,
+                    eps=eps, n_seg=n_seg)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    ws, ws_bytes = _workspace(op, p, B, H, N, d, dv, 0, q.device, workspace)
+    rc = getattr(_lib, name)(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d,
+                             dv, _ptr(om), _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(ws), ws_bytes,
+                             _stream(q.device, stream))
+    _check(name, rc)
+    return dq, dk, dvv
+
+
+def lin_attn_bidir_backward(q, k, v, dout, kind, *, omega=None, nu=1, sum_norm=False,
+                            norm="attn", scale=1.0, eps=1e-6, n_seg=0, workspace=None,
+                            stream=None):
+    """Gradients (dq, dk, dv) of sum(lin_attn_bidir(q, k, v) * dout), each of
+    the input dtype and shape."""
+    return _backward("lin_attn_bidir_backward", OP_BIDIR_BACKWARD, q, k, v, dout, kind, omega, nu,
+                     sum_norm, norm, scale, eps, n_seg, workspace, stream)
+
+
+def lin_attn_causal_backward(q, k, v, dout, kind, *, omega=None, nu=1, sum_norm=False,
+                             norm="attn", scale=1.0, eps=1e-6, n_seg=0, workspace=None,
+                             stream=None):
+    """Gradients (dq, dk, dv) of sum(out * dout) for the causal recurrence from
+    zero state (lin_attn_causal_chunked with state_in = 0)."""
+    return _backward("lin_attn_causal_backward", OP_CAUSAL_BACKWARD, q, k, v, dout, kind, omega,
+                     nu, sum_norm, norm, scale, eps, n_seg, workspace, stream)
 
 
 def raw():

@@ -130,6 +130,85 @@ VarlenLayout varlen_layout(const lin_attn_params* p, int64_t num_seqs, int64_t H
     return L;
 }
 
+// Backward pass (vector kernels, no increment halving).  Workspace (float32):
+//   [0, BH*G*E)          forward increments, then prefixes (causal)
+//   [BH*G*E, 2*BH*G*E)   backward increments, then suffixes (causal)
+//   bidirectional: the forward and the backward totals, BH*E each;
+//   causal: (1/D_t, dden_t) per token, BH*N*2.
+struct BackwardLayout {
+    SegPlan sp;
+    size_t inc_b, extra, floats;
+};
+
+BackwardLayout backward_layout(const lin_attn_params* p, bool causal, int64_t BH, int64_t N) {
+    BackwardLayout L;
+    L.sp = plan_segments(BH, N, p->n_seg, TARGET_BLOCKS_VALU);
+    const size_t inc = (size_t)(BH * L.sp.G * state_elems(p->r));
+    L.inc_b = inc;
+    L.extra = 2 * inc;
+    L.floats = L.extra + (causal ? (size_t)(BH * N * 2) : (size_t)(2 * BH * state_elems(p->r)));
+    return L;
+}
+
+int backward_call(bool causal, const lin_attn_params* p, const void* q, const void* k,
+                  const void* v, const void* dout, int64_t B, int64_t H, int64_t N, int64_t d,
+                  int64_t dv, const void* omega, void* dq, void* dk, void* dvv, void* ws,
+                  size_t ws_bytes, void* stream) {
+    int rc = check_params(p, d, dv, omega);
+    if (rc == LIN_ATTN_ERR_INVALID) return rc;
+    const int rs = check_sizes(B, H, N);
+    if (rs == LIN_ATTN_ERR_INVALID) return rs;
+    if (!opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
+    if (B * H > 0 && N > 0 &&
+        (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(dout) || !ptr_ok(dq) || !ptr_ok(dk) ||
+         !ptr_ok(dvv)))
+        return LIN_ATTN_ERR_INVALID;
+    if (rc != LIN_ATTN_OK) return rc;
+    if (rs != LIN_ATTN_OK) return rs;
+    if (B * H == 0 || N == 0) return LIN_ATTN_OK; // no element to write
+    const int64_t BH = B * H;
+    const BackwardLayout L = backward_layout(p, causal, BH, N);
+    if (ws_bytes < L.floats * sizeof(float) || !ws) return LIN_ATTN_ERR_WORKSPACE;
+
+    const Cfg c = make_cfg(p);
+    const Shape s{BH, N};
+    const SegPlan sp = L.sp;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t E = state_elems(p->r);
+    float* inc_f = (float*)ws;
+    float* inc_b = inc_f + L.inc_b;
+    float* extra = inc_f + L.extra;
+    hipError_t e = segment_sums(p, c, k, v, omega, s, sp, inc_f, st);
+    if (causal) {
+        if (e == hipSuccess)
+            e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_f, 1, nullptr, nullptr,
+                                    nullptr, st);
+        if (e == hipSuccess)
+            e = launch_backward_query(c, p->dtype, 1, q, k, v, dout, omega, s, sp, inc_f, sp.G * E,
+                                      E, inc_b, extra, dq, st);
+        if (e == hipSuccess) e = launch_segment_suffix_scan(p->r, s, sp, inc_b, st);
+        if (e == hipSuccess)
+            e = launch_backward_key(c, p->dtype, 1, q, k, v, dout, omega, s, sp, inc_b, sp.G * E, E,
+                                    extra, dk, dvv, st);
+    } else {
+        float* fin_f = extra;
+        float* fin_b = extra + BH * E;
+        if (e == hipSuccess)
+            e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_f, 0, nullptr, nullptr,
+                                    fin_f, st);
+        if (e == hipSuccess)
+            e = launch_backward_query(c, p->dtype, 0, q, k, v, dout, omega, s, sp, fin_f, E, 0,
+                                      inc_b, nullptr, dq, st);
+        if (e == hipSuccess)
+            e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_b, 0, nullptr, nullptr,
+                                    fin_b, st);
+        if (e == hipSuccess)
+            e = launch_backward_key(c, p->dtype, 0, q, k, v, dout, omega, s, sp, fin_b, E, 0,
+                                    nullptr, dk, dvv, st);
+    }
+    return launch_status(e);
+}
+
 } // namespace
 
 extern "C" {
@@ -150,8 +229,7 @@ const char* lin_attn_strerror(int32_t code) {
 size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B, int64_t H,
                                 int64_t N, int64_t d, int64_t dv, int32_t chunk) {
     (void)chunk;
-    if (op != LIN_ATTN_OP_BIDIR && op != LIN_ATTN_OP_CAUSAL && op != LIN_ATTN_OP_CAUSAL_VARLEN)
-        return 0;
+    if (op < LIN_ATTN_OP_BIDIR || op > LIN_ATTN_OP_CAUSAL_BACKWARD) return 0;
     if (!p || check_sizes(B, H, N) != LIN_ATTN_OK) return 0;
     // omega is not needed to size the workspace: check the rest with a dummy
     const int rc = check_params(p, d, dv, reinterpret_cast<const void*>(uintptr_t(16)));
@@ -159,6 +237,8 @@ size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B,
     const int64_t BH = B * H;
     if (BH == 0 || N == 0) return 0;
     if (op == LIN_ATTN_OP_CAUSAL_VARLEN) return varlen_layout(p, B, H, N).bytes;
+    if (op == LIN_ATTN_OP_BIDIR_BACKWARD || op == LIN_ATTN_OP_CAUSAL_BACKWARD)
+        return backward_layout(p, op == LIN_ATTN_OP_CAUSAL_BACKWARD, BH, N).floats * sizeof(float);
     return ws_floats(op, BH, plan_for(p, BH, N), p->r) * sizeof(float);
 }
 
@@ -332,6 +412,22 @@ int lin_attn_orf_omega(const float* gauss, const float* len_gauss, int64_t n_mat
     if (n_mat > ((int64_t)1 << 24) || nblk > ((int64_t)1 << 24) / n_mat) return LIN_ATTN_ERR_UNSUPPORTED;
     return launch_status(launch_orf(gauss, len_gauss, n_mat, r, (int)d, dtype, omega,
                                     (hipStream_t)stream));
+}
+
+int lin_attn_bidir_backward(const lin_attn_params* p, const void* q, const void* k,
+                            const void* v, const void* dout, int64_t B, int64_t H, int64_t N,
+                            int64_t d, int64_t dv, const void* omega, void* dq, void* dk,
+                            void* dv_out, void* ws, size_t ws_bytes, void* stream) {
+    return backward_call(false, p, q, k, v, dout, B, H, N, d, dv, omega, dq, dk, dv_out, ws,
+                         ws_bytes, stream);
+}
+
+int lin_attn_causal_backward(const lin_attn_params* p, const void* q, const void* k,
+                             const void* v, const void* dout, int64_t B, int64_t H, int64_t N,
+                             int64_t d, int64_t dv, const void* omega, void* dq, void* dk,
+                             void* dv_out, void* ws, size_t ws_bytes, void* stream) {
+    return backward_call(true, p, q, k, v, dout, B, H, N, d, dv, omega, dq, dk, dv_out, ws,
+                         ws_bytes, stream);
 }
 
 int lin_attn_decode_step(const lin_attn_params* p, const void* q, const void* k, const void* v,

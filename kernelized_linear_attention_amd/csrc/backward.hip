@@ -1,0 +1,561 @@
+// backward.hip -- gradients of the bidirectional form and of the causal
+// recurrence (from zero state) with respect to q, k and v: the chain rule
+// through the readout, the summaries and the feature map (Kernel Zoo sec.
+// 1.3 and 5.4 for the forward definitions; "Reassociate a feature-map
+// kernel..." par. 6 asks for the gradients to be evaluated).  Vector kernels,
+// float32 arithmetic, every feature map, float32 and bfloat16 inputs.
+//
+// With D_i = max(den_i, eps), query i read against the state (S_i, z_i) it
+// sees, and dout_i = dL/dout_i:
+//   dnum_i = dout_i / D_i,  dden_i = -(dout_i . out_i) / D_i where den_i > eps
+//   (0 where the clamp holds D_i fixed); NORM_NONE: dnum_i = dout_i, dden_i = 0
+//   dphi(q_i) = S_i dnum_i + z_i dden_i
+//   dphi(k_j) = G_j v_j + g_j,   dv_j = G_j^T phi(k_j)
+// where (G_j, g_j) sums (phi(q_i) dnum_i^T, phi(q_i) dden_i) over the queries
+// i that see key j: all of them in the bidirectional form, i >= j in the
+// causal one.  The causal G_j is a suffix sum and is evaluated like the
+// forward prefix, mirrored: segments -> chunks walked last to first ->
+// tokens, with an exclusive suffix over per-segment increments.  Through the
+// map, dx = scale * J_phi(u)^T dphi at u = scale * x.
+//
+// Launch order (abi.hip): forward increments, forward scan, query pass (dq,
+// backward increments, per-token (1/D, dden) for the causal form), backward
+// scan (suffix for causal), key pass (dk, dv).
+#include "launch.hpp"
+#include "tiles.hpp"
+
+namespace linattn {
+namespace {
+
+constexpr int NT = VNT;
+constexpr int L = 16;       // tokens per chunk
+constexpr int SL = DV + 4;  // LDS row stride of a state matrix [R][DV]
+
+// Loads state block src = (M [R][DV], m [R]) into M_s (row stride SL), m_s.
+template <int R>
+__device__ void load_state(const float* __restrict__ src, float* M_s, float* m_s) {
+    for (int e = threadIdx.x; e < R * (DV / 4); e += NT) {
+        const int f = e / (DV / 4), n4 = (e % (DV / 4)) * 4;
+        *reinterpret_cast<float4*>(M_s + f * SL + n4) =
+            *reinterpret_cast<const float4*>(src + (long)f * DV + n4);
+    }
+    for (int f = threadIdx.x; f < R; f += NT) m_s[f] = src[(long)R * DV + f];
+}
+
+// Outer-product sums over the rows of a chunk, for the items of this thread:
+// feature f = tid/16 + 16*it, value columns n4 = 4*(tid % 16) .. n4+3:
+//   acc[it][j] += sum_t x[t][f] y[t][n4+j],   macc[it] += sum_t x[t][f] s[t]
+// (s == NULL: s[t] = 1).  x has row stride ol, y row stride DV.
+template <int FPT>
+__device__ void outer_accum(const float* x, int ol, const float* y, const float* s, int rows,
+                            float (&acc)[2 * FPT][4], float (&macc)[2 * FPT]) {
+    const int f0 = threadIdx.x / 16, n4 = (threadIdx.x % 16) * 4;
+    for (int t = 0; t < rows; ++t) {
+        const float4 yv = *reinterpret_cast<const float4*>(y + t * DV + n4);
+        const float st = s ? s[t] : 1.f;
+#pragma unroll
+        for (int it = 0; it < 2 * FPT; ++it) {
+            const float xf = x[t * ol + f0 + 16 * it];
+            acc[it][0] = fmaf(xf, yv.x, acc[it][0]);
+            acc[it][1] = fmaf(xf, yv.y, acc[it][1]);
+            acc[it][2] = fmaf(xf, yv.z, acc[it][2]);
+            acc[it][3] = fmaf(xf, yv.w, acc[it][3]);
+            macc[it] = fmaf(xf, st, macc[it]);
+        }
+    }
+}
+
+// In-LDS state update M += x^T y, m += x^T s over the rows of a chunk.
+// Caller synchronises before (readers of M done) and after.
+template <int FPT>
+__device__ void state_update(float* M_s, float* m_s, const float* x, int ol, const float* y,
+                             const float* s, int rows) {
+    const int f0 = threadIdx.x / 16, n4 = (threadIdx.x % 16) * 4;
+    float acc[2 * FPT][4], macc[2 * FPT];
+#pragma unroll
+    for (int it = 0; it < 2 * FPT; ++it) {
+        const float4 a = *reinterpret_cast<const float4*>(M_s + (f0 + 16 * it) * SL + n4);
+        acc[it][0] = a.x;
+        acc[it][1] = a.y;
+        acc[it][2] = a.z;
+        acc[it][3] = a.w;
+        macc[it] = 0.f;
+    }
+    outer_accum<FPT>(x, ol, y, s, rows, acc, macc);
+#pragma unroll
+    for (int it = 0; it < 2 * FPT; ++it) {
+        *reinterpret_cast<float4*>(M_s + (f0 + 16 * it) * SL + n4) =
+            make_float4(acc[it][0], acc[it][1], acc[it][2], acc[it][3]);
+        if (n4 == 0) m_s[f0 + 16 * it] += macc[it];
+    }
+}
+
+// dp[t][f] = sum_n M[f][n] y[t][n] + m[f] s[t] + sum_j cm[t][j] x[j][f] for
+// the L rows of a chunk (s == NULL: s[t] = 1; cm == NULL: no third term; cm
+// row stride L+1, already zero outside the mask).  Item (feature f, token
+// group of 8 rows).
+template <int FPT>
+__device__ void dphi_rows(const float* M_s, const float* m_s, const float* y, const float* s,
+                          const float* cm, const float* x, int ol, float* dp) {
+    constexpr int R = 32 * FPT;
+    for (int p = threadIdx.x; p < 2 * R; p += NT) {
+        const int f = p % R, t0 = (p / R) * 8;
+        float acc[8];
+        const float mf = m_s[f];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] = s ? mf * s[t0 + t] : mf;
+        for (int n = 0; n < DV; n += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(M_s + f * SL + n);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float4 yv = *reinterpret_cast<const float4*>(y + (t0 + t) * DV + n);
+                acc[t] = fmaf(w.x, yv.x, acc[t]);
+                acc[t] = fmaf(w.y, yv.y, acc[t]);
+                acc[t] = fmaf(w.z, yv.z, acc[t]);
+                acc[t] = fmaf(w.w, yv.w, acc[t]);
+            }
+        }
+        if (cm) {
+            for (int j = 0; j < L; ++j) {
+                const float xv = x[j * ol + f];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc[t] = fmaf(cm[(t0 + t) * (L + 1) + j], xv, acc[t]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dp[(t0 + t) * ol + f] = acc[t];
+    }
+}
+
+// cm[t][j] = (j <= t) ? a[t] . b[j] : 0 (LOWER) or (j >= t) ? ... (upper),
+// plus add[t] (may be NULL) inside the mask; a, b row stride `ld`, length n.
+template <bool LOWER>
+__device__ void masked_products(const float* a, const float* b, int ld, int n, const float* add,
+                                float* cm) {
+    for (int p = threadIdx.x; p < L * L; p += NT) {
+        const int t = p / L, j = p % L;
+        float acc = 0.f;
+        if (LOWER ? j <= t : j >= t) {
+            const float* x = a + t * ld;
+            const float* y = b + j * ld;
+            for (int e = 0; e < n; e += 4) {
+                acc = fmaf(x[e], y[e], acc);
+                acc = fmaf(x[e + 1], y[e + 1], acc);
+                acc = fmaf(x[e + 2], y[e + 2], acc);
+                acc = fmaf(x[e + 3], y[e + 3], acc);
+            }
+            if (add) acc += add[j];
+        }
+        cm[t * (L + 1) + j] = acc;
+    }
+}
+
+// out[t] = scale * J_phi(u_t)^T dp_t for the rows t < rows of a chunk.
+// phi: the map's output tile (after sum normalisation), rs / live from
+// phi_tile; dp (dphi, row stride ol) is overwritten.  Starts after a barrier
+// (dp, phi, u complete); ends without one.
+template <typename T, int FPT>
+__device__ void phi_backward_tile(const Cfg& c, const float* u, const float* phi, int ol,
+                                  const float* rs, const float* live, float* dp, float* cc,
+                                  const T* __restrict__ omega, int rows, T* __restrict__ out) {
+    constexpr int R = 32 * FPT;
+    const int tid = threadIdx.x;
+    if (c.sum_norm) {
+        // through phi = p / max(sum p, eps): dp = (dphi - [sum > eps] dphi . phi) / max(sum, eps)
+        const int lane = tid & 63, w = tid >> 6;
+        for (int t = w; t < L; t += NT / 64) {
+            float s = 0.f;
+            for (int f = lane; f < R; f += 64) s = fmaf(dp[t * ol + f], phi[t * ol + f], s);
+            s = wave_sum(s);
+            if (lane == 0) cc[t] = live[t] != 0.f ? s : 0.f;
+        }
+        __syncthreads();
+    }
+    if (c.sum_norm || c.phi == PHI_FAVOR) {
+        // FAVOR+ keeps dp_f * p_f = (dphi_f - c) * phi_f (d p_f / d u = p_f (omega_f - u))
+        for (int idx = tid; idx < L * R; idx += NT) {
+            const int t = idx / R, f = idx - t * R;
+            float g = dp[t * ol + f];
+            if (c.sum_norm) g -= cc[t];
+            if (c.phi == PHI_FAVOR) g *= phi[t * ol + f];
+            else g *= rs[t];
+            dp[t * ol + f] = g;
+        }
+        __syncthreads();
+    }
+    const int i = tid & 63, t0 = (tid >> 6) * (L / 4);
+    float du[L / 4];
+    if (c.phi == PHI_FAVOR) {
+        float a[L / 4], wsum[L / 4];
+#pragma unroll
+        for (int m = 0; m < L / 4; ++m) a[m] = wsum[m] = 0.f;
+        for (int f = 0; f < R; ++f) {
+            const float om = Elem<T>::load(omega, (long)f * D + i);
+#pragma unroll
+            for (int m = 0; m < L / 4; ++m) {
+                const float wv = dp[(t0 + m) * ol + f];
+                a[m] = fmaf(wv, om, a[m]);
+                wsum[m] += wv;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < L / 4; ++m) du[m] = a[m] - wsum[m] * u[(t0 + m) * D + i];
+    } else if (c.phi == PHI_ELU1) {
+#pragma unroll
+        for (int m = 0; m < L / 4; ++m) {
+            const float x = u[(t0 + m) * D + i];
+            du[m] = dp[(t0 + m) * ol + i] * (x > 0.f ? 1.f : expf(x));
+        }
+    } else if (c.phi == PHI_IDENTITY) {
+#pragma unroll
+        for (int m = 0; m < L / 4; ++m) du[m] = dp[(t0 + m) * ol + i];
+    } else {
+        // DPFP: feature (s-1)*2D + j = kt_j * kt_{(j+s) mod 2D}; kt = relu([u, -u])
+        constexpr int M2 = 2 * D - 1;
+#pragma unroll
+        for (int m = 0; m < L / 4; ++m) {
+            const float* ut = u + (t0 + m) * D;
+            const float* g = dp + (t0 + m) * ol;
+            float dpos = 0.f, dneg = 0.f; // d/d kt_i, d/d kt_{D+i}
+            for (int s = 1; s <= c.nu; ++s) {
+                const float* gs = g + (s - 1) * 2 * D;
+                dpos = fmaf(gs[i], dpfp_kt(ut, (i + s) & M2), dpos);
+                dpos = fmaf(gs[(i - s) & M2], dpfp_kt(ut, (i - s) & M2), dpos);
+                dneg = fmaf(gs[D + i], dpfp_kt(ut, (D + i + s) & M2), dneg);
+                dneg = fmaf(gs[(D + i - s) & M2], dpfp_kt(ut, (D + i - s) & M2), dneg);
+            }
+            const float x = ut[i];
+            du[m] = (x > 0.f ? dpos : 0.f) - (x < 0.f ? dneg : 0.f);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < L / 4; ++m)
+        if (t0 + m < rows) Elem<T>::store(out, (long)(t0 + m) * D + i, c.scale * du[m]);
+}
+
+// ---------------------------------------------------------------------------
+// Query pass.  One workgroup per (head, segment).
+// ---------------------------------------------------------------------------
+template <typename T, int FPT, bool CAUSAL>
+__global__ __launch_bounds__(NT) void k_bwd_query(Cfg c, const T* __restrict__ q,
+                                                  const T* __restrict__ k, const T* __restrict__ v,
+                                                  const T* __restrict__ dout,
+                                                  const T* __restrict__ omega, int64_t N, int64_t G,
+                                                  int64_t seg_len, const float* __restrict__ state,
+                                                  int64_t st_bh, int64_t st_g,
+                                                  float* __restrict__ inc, float* __restrict__ tok,
+                                                  T* __restrict__ dq) {
+    constexpr int R = 32 * FPT;
+    constexpr int OL = R + 4;
+    constexpr int LC = CAUSAL ? L : 1;
+    __shared__ __align__(16) float S_s[R * SL];
+    __shared__ float z_s[R];
+    __shared__ __align__(16) float u_s[L * D];
+    __shared__ __align__(16) float pq_s[L * OL];
+    __shared__ __align__(16) float pk_s[LC * OL];
+    __shared__ __align__(16) float dp_s[L * OL];
+    __shared__ __align__(16) float v_s[LC * DV];
+    __shared__ __align__(16) float dn_s[L * DV];
+    __shared__ float dd_s[L], a_s[LC * (L + 1)];
+    __shared__ float nrm_s[L], rs_s[L], live_s[L], cc_s[L];
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x / G, g = blockIdx.x % G;
+    const int64_t t0 = g * seg_len, t1 = t0 + seg_len < N ? t0 + seg_len : N;
+
+    load_state<R>(state + bh * st_bh + g * st_g, S_s, z_s);
+    float acc[2 * FPT][4], macc[2 * FPT];
+#pragma unroll
+    for (int it = 0; it < 2 * FPT; ++it) {
+        macc[it] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[it][j] = 0.f;
+    }
+    const int rt = tid / 16, cb = (tid % 16) * 4; // readout: token, 4 value columns
+
+    for (int64_t c0 = t0; c0 < t1; c0 += L) {
+        const int rows = (int)min<int64_t>(L, t1 - c0);
+        if (CAUSAL) {
+            load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, u_s);
+            load_rows<T, L>(v + (bh * N + c0) * DV, rows, 1.f, v_s);
+            __syncthreads();
+            row_norms<L>(u_s, nrm_s);
+            __syncthreads();
+            phi_tile<T, L>(c, u_s, nrm_s, omega, rows, pk_s, OL, rs_s);
+        }
+        load_rows<T, L>(q + (bh * N + c0) * D, rows, c.scale, u_s);
+        __syncthreads();
+        row_norms<L>(u_s, nrm_s);
+        __syncthreads();
+        phi_tile<T, L>(c, u_s, nrm_s, omega, rows, pq_s, OL, rs_s, live_s);
+        if (CAUSAL) {
+            masked_products<true>(pq_s, pk_s, OL, R, nullptr, a_s);
+            __syncthreads();
+        }
+
+        // forward readout of token rt, then dnum, dden
+        {
+            float num[4] = {0.f, 0.f, 0.f, 0.f};
+            float den = 0.f;
+            const float* x = pq_s + rt * OL;
+            for (int f = 0; f < R; ++f) {
+                const float pf = x[f];
+                den = fmaf(pf, z_s[f], den);
+                const float4 sv = *reinterpret_cast<const float4*>(S_s + f * SL + cb);
+                num[0] = fmaf(pf, sv.x, num[0]);
+                num[1] = fmaf(pf, sv.y, num[1]);
+                num[2] = fmaf(pf, sv.z, num[2]);
+                num[3] = fmaf(pf, sv.w, num[3]);
+            }
+            if (CAUSAL) {
+                for (int j = 0; j <= rt; ++j) {
+                    const float a = a_s[rt * (L + 1) + j];
+                    den += a;
+                    const float4 vv = *reinterpret_cast<const float4*>(v_s + j * DV + cb);
+                    num[0] = fmaf(a, vv.x, num[0]);
+                    num[1] = fmaf(a, vv.y, num[1]);
+                    num[2] = fmaf(a, vv.z, num[2]);
+                    num[3] = fmaf(a, vv.w, num[3]);
+                }
+            }
+            const bool attn = c.norm == NORM_ATTN;
+            const float inv = attn ? 1.f / fmaxf(den, c.eps) : 1.f;
+            float4 go = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (rt < rows) go = Elem<T>::load4(dout, (bh * N + c0 + rt) * DV + cb);
+            // dout . out over the 16 lanes of this token
+            float dot = go.x * num[0] + go.y * num[1] + go.z * num[2] + go.w * num[3];
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+            const float dden = (attn && den > c.eps) ? -dot * inv * inv : 0.f;
+            *reinterpret_cast<float4*>(dn_s + rt * DV + cb) =
+                make_float4(go.x * inv, go.y * inv, go.z * inv, go.w * inv);
+            if (cb == 0) {
+                dd_s[rt] = dden;
+                if (CAUSAL && rt < rows) {
+                    tok[2 * (bh * N + c0 + rt)] = inv;
+                    tok[2 * (bh * N + c0 + rt) + 1] = dden;
+                }
+            }
+        }
+        __syncthreads();
+        if (CAUSAL) {
+            // coefficient of phi(k_j) in dphi(q_t): v_j . dnum_t + dden_t, j <= t
+            masked_products<true>(dn_s, v_s, DV, DV, nullptr, a_s);
+            __syncthreads();
+            for (int p = tid; p < L * L; p += NT) {
+                const int t = p / L, j = p % L;
+                if (j <= t) a_s[t * (L + 1) + j] += dd_s[t];
+            }
+            __syncthreads();
+        }
+        dphi_rows<FPT>(S_s, z_s, dn_s, dd_s, CAUSAL ? a_s : nullptr, pk_s, OL, dp_s);
+        outer_accum<FPT>(pq_s, OL, dn_s, dd_s, rows, acc, macc);
+        __syncthreads();
+        phi_backward_tile<T, FPT>(c, u_s, pq_s, OL, rs_s, live_s, dp_s, cc_s, omega, rows,
+                                  dq + (bh * N + c0) * D);
+        if (CAUSAL) state_update<FPT>(S_s, z_s, pk_s, OL, v_s, nullptr, rows);
+        __syncthreads();
+    }
+
+    float* dst = inc + (bh * G + g) * state_elems(R);
+    const int f0 = tid / 16;
+#pragma unroll
+    for (int it = 0; it < 2 * FPT; ++it) {
+        const int f = f0 + 16 * it;
+        *reinterpret_cast<float4*>(dst + (long)f * DV + cb) =
+            make_float4(acc[it][0], acc[it][1], acc[it][2], acc[it][3]);
+        if (cb == 0) dst[(long)R * DV + f] = macc[it];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Key pass.  One workgroup per (head, segment); causal chunks last to first.
+// ---------------------------------------------------------------------------
+template <typename T, int FPT, bool CAUSAL>
+__global__ __launch_bounds__(NT) void k_bwd_key(Cfg c, const T* __restrict__ q,
+                                                const T* __restrict__ k, const T* __restrict__ v,
+                                                const T* __restrict__ dout,
+                                                const T* __restrict__ omega, int64_t N, int64_t G,
+                                                int64_t seg_len, const float* __restrict__ state,
+                                                int64_t st_bh, int64_t st_g,
+                                                const float* __restrict__ tok, T* __restrict__ dk,
+                                                T* __restrict__ dv) {
+    constexpr int R = 32 * FPT;
+    constexpr int OL = R + 4;
+    constexpr int LC = CAUSAL ? L : 1;
+    __shared__ __align__(16) float G_s[R * SL];
+    __shared__ float g_s[R];
+    __shared__ __align__(16) float uk_s[L * D];
+    __shared__ __align__(16) float uq_s[LC * D];
+    __shared__ __align__(16) float pk_s[L * OL];
+    __shared__ __align__(16) float pq_s[LC * OL];
+    __shared__ __align__(16) float dp_s[L * OL];
+    __shared__ __align__(16) float v_s[L * DV];
+    __shared__ __align__(16) float dn_s[LC * DV];
+    __shared__ float dd_s[LC], a_s[LC * (L + 1)], b_s[LC * (L + 1)];
+    __shared__ float nrm_s[L], rs_s[L], live_s[L], cc_s[L], rsq_s[L];
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x / G, g = blockIdx.x % G;
+    const int64_t t0 = g * seg_len, t1 = t0 + seg_len < N ? t0 + seg_len : N;
+    const int64_t nch = (t1 - t0 + L - 1) / L;
+
+    load_state<R>(state + bh * st_bh + g * st_g, G_s, g_s);
+    const int rt = tid / 16, cb = (tid % 16) * 4; // dv: key, 4 value columns
+
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        const int64_t c0 = t0 + (CAUSAL ? nch - 1 - ci : ci) * L;
+        const int rows = (int)min<int64_t>(L, t1 - c0);
+        if (CAUSAL) {
+            // the chunk's queries: phi(q_i), dnum_i = dout_i / D_i, dden_i
+            load_rows<T, L>(q + (bh * N + c0) * D, rows, c.scale, uq_s);
+            for (int e = tid; e < L * (DV / 4); e += NT) {
+                const int t = e / (DV / 4), n4 = (e % (DV / 4)) * 4;
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+                float inv = 0.f;
+                if (t < rows) {
+                    x = Elem<T>::load4(dout, (bh * N + c0 + t) * DV + n4);
+                    inv = tok[2 * (bh * N + c0 + t)];
+                }
+                *reinterpret_cast<float4*>(dn_s + t * DV + n4) =
+                    make_float4(x.x * inv, x.y * inv, x.z * inv, x.w * inv);
+            }
+            for (int t = tid; t < L; t += NT) dd_s[t] = t < rows ? tok[2 * (bh * N + c0 + t) + 1] : 0.f;
+            __syncthreads();
+            row_norms<L>(uq_s, nrm_s);
+            __syncthreads();
+            phi_tile<T, L>(c, uq_s, nrm_s, omega, rows, pq_s, OL, rsq_s);
+        }
+        load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, uk_s);
+        load_rows<T, L>(v + (bh * N + c0) * DV, rows, 1.f, v_s);
+        __syncthreads();
+        row_norms<L>(uk_s, nrm_s);
+        __syncthreads();
+        phi_tile<T, L>(c, uk_s, nrm_s, omega, rows, pk_s, OL, rs_s, live_s);
+        if (CAUSAL) {
+            // b[j][i] = phi(k_j) . phi(q_i); a[j][i] = v_j . dnum_i + dden_i; i >= j
+            masked_products<false>(pk_s, pq_s, OL, R, nullptr, b_s);
+            masked_products<false>(v_s, dn_s, DV, DV, dd_s, a_s);
+            __syncthreads();
+        }
+        dphi_rows<FPT>(G_s, g_s, v_s, nullptr, CAUSAL ? a_s : nullptr, pq_s, OL, dp_s);
+        {
+            // dv_j = G^T phi(k_j) + sum_{i >= j} b[j][i] dnum_i
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            const float* x = pk_s + rt * OL;
+            for (int f = 0; f < R; ++f) {
+                const float pf = x[f];
+                const float4 gv = *reinterpret_cast<const float4*>(G_s + f * SL + cb);
+                acc[0] = fmaf(pf, gv.x, acc[0]);
+                acc[1] = fmaf(pf, gv.y, acc[1]);
+                acc[2] = fmaf(pf, gv.z, acc[2]);
+                acc[3] = fmaf(pf, gv.w, acc[3]);
+            }
+            if (CAUSAL) {
+                for (int i = rt; i < L; ++i) {
+                    const float b = b_s[rt * (L + 1) + i];
+                    const float4 dn = *reinterpret_cast<const float4*>(dn_s + i * DV + cb);
+                    acc[0] = fmaf(b, dn.x, acc[0]);
+                    acc[1] = fmaf(b, dn.y, acc[1]);
+                    acc[2] = fmaf(b, dn.z, acc[2]);
+                    acc[3] = fmaf(b, dn.w, acc[3]);
+                }
+            }
+            if (rt < rows) {
+                T* o = dv + (bh * N + c0 + rt) * DV + cb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Elem<T>::store(o, j, acc[j]);
+            }
+        }
+        __syncthreads();
+        phi_backward_tile<T, FPT>(c, uk_s, pk_s, OL, rs_s, live_s, dp_s, cc_s, omega, rows,
+                                  dk + (bh * N + c0) * D);
+        if (CAUSAL) state_update<FPT>(G_s, g_s, pq_s, OL, dn_s, dd_s, rows);
+        __syncthreads();
+    }
+}
+
+template <typename T, int FPT>
+void query_fpt(const Cfg& c, int causal, const void* q, const void* k, const void* v,
+               const void* dout, const void* omega, Shape s, SegPlan sp, const float* state,
+               int64_t sbh, int64_t sg, float* inc, float* tok, void* dq, hipStream_t st) {
+    const dim3 grid((unsigned)(sp.G * s.BH)), block(NT);
+    if (causal)
+        hipLaunchKernelGGL((k_bwd_query<T, FPT, true>), grid, block, 0, st, c, (const T*)q,
+                           (const T*)k, (const T*)v, (const T*)dout, (const T*)omega, s.N, sp.G,
+                           sp.seg_len, state, sbh, sg, inc, tok, (T*)dq);
+    else
+        hipLaunchKernelGGL((k_bwd_query<T, FPT, false>), grid, block, 0, st, c, (const T*)q,
+                           (const T*)k, (const T*)v, (const T*)dout, (const T*)omega, s.N, sp.G,
+                           sp.seg_len, state, sbh, sg, inc, tok, (T*)dq);
+}
+
+template <typename T, int FPT>
+void key_fpt(const Cfg& c, int causal, const void* q, const void* k, const void* v,
+             const void* dout, const void* omega, Shape s, SegPlan sp, const float* state,
+             int64_t sbh, int64_t sg, const float* tok, void* dk, void* dv, hipStream_t st) {
+    const dim3 grid((unsigned)(sp.G * s.BH)), block(NT);
+    if (causal)
+        hipLaunchKernelGGL((k_bwd_key<T, FPT, true>), grid, block, 0, st, c, (const T*)q,
+                           (const T*)k, (const T*)v, (const T*)dout, (const T*)omega, s.N, sp.G,
+                           sp.seg_len, state, sbh, sg, tok, (T*)dk, (T*)dv);
+    else
+        hipLaunchKernelGGL((k_bwd_key<T, FPT, false>), grid, block, 0, st, c, (const T*)q,
+                           (const T*)k, (const T*)v, (const T*)dout, (const T*)omega, s.N, sp.G,
+                           sp.seg_len, state, sbh, sg, tok, (T*)dk, (T*)dv);
+}
+
+template <typename T>
+hipError_t query_t(const Cfg& c, int causal, const void* q, const void* k, const void* v,
+                   const void* dout, const void* omega, Shape s, SegPlan sp, const float* state,
+                   int64_t sbh, int64_t sg, float* inc, float* tok, void* dq, hipStream_t st) {
+#define LINATTN_QUERY(F)                                                                         \
+    case F: query_fpt<T, F>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, inc, tok, dq, \
+                            st);                                                                 \
+        break;
+    switch (c.r / 32) {
+        LINATTN_QUERY(1) LINATTN_QUERY(2) LINATTN_QUERY(3) LINATTN_QUERY(4)
+        LINATTN_QUERY(5) LINATTN_QUERY(6) LINATTN_QUERY(7) LINATTN_QUERY(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef LINATTN_QUERY
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t key_t(const Cfg& c, int causal, const void* q, const void* k, const void* v,
+                 const void* dout, const void* omega, Shape s, SegPlan sp, const float* state,
+                 int64_t sbh, int64_t sg, const float* tok, void* dk, void* dv, hipStream_t st) {
+#define LINATTN_KEY(F)                                                                            \
+    case F: key_fpt<T, F>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, tok, dk, dv, st); \
+        break;
+    switch (c.r / 32) {
+        LINATTN_KEY(1) LINATTN_KEY(2) LINATTN_KEY(3) LINATTN_KEY(4)
+        LINATTN_KEY(5) LINATTN_KEY(6) LINATTN_KEY(7) LINATTN_KEY(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef LINATTN_KEY
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_backward_query(const Cfg& c, int dtype, int causal, const void* q,
+                                 const void* k, const void* v, const void* dout, const void* omega,
+                                 Shape s, SegPlan sp, const float* state, int64_t sbh, int64_t sg,
+                                 float* inc, float* tok, void* dq, hipStream_t st) {
+    return dtype == 0 ? query_t<float>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, inc,
+                                       tok, dq, st)
+                      : query_t<bf16_raw>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg,
+                                          inc, tok, dq, st);
+}
+
+hipError_t launch_backward_key(const Cfg& c, int dtype, int causal, const void* q, const void* k,
+                               const void* v, const void* dout, const void* omega, Shape s,
+                               SegPlan sp, const float* state, int64_t sbh, int64_t sg,
+                               const float* tok, void* dk, void* dv, hipStream_t st) {
+    return dtype == 0 ? key_t<float>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, tok,
+                                     dk, dv, st)
+                      : key_t<bf16_raw>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg,
+                                        tok, dk, dv, st);
+}
+
+} // namespace linattn

@@ -15,89 +15,12 @@
 #include <algorithm>
 
 #include "launch.hpp"
+#include "tiles.hpp"
 
 namespace linattn {
 namespace {
 
-constexpr int NT = 256; // threads per workgroup in this file
-
-// Copies `rows` rows of a [*, 64] matrix (zero rows after `rows`, up to L)
-// into dst[L][64] as scale * x.
-template <typename T, int L>
-__device__ void load_rows(const T* __restrict__ src, int rows, float scale, float* dst) {
-    for (int g = threadIdx.x; g < L * (D / 4); g += NT) {
-        const int row = g / (D / 4), c4 = (g % (D / 4)) * 4;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row < rows) x = Elem<T>::load4(src, (long)row * D + c4);
-        float* o = dst + row * D + c4;
-        o[0] = scale * x.x;
-        o[1] = scale * x.y;
-        o[2] = scale * x.z;
-        o[3] = scale * x.w;
-    }
-}
-
-// nrm[t] = |u_t|^2 for the L rows of u[L][64] (one wave per row).
-template <int L>
-__device__ void row_norms(const float* u, float* nrm) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int t = w; t < L; t += NT / 64) {
-        float a = u[t * D + lane];
-        float s = wave_sum(a * a);
-        if (lane == 0) nrm[t] = s;
-    }
-}
-
-// out[t][f] = phi_f(u_t) for t < L, f < r (rows >= `rows` are zero), then the
-// optional sum normalisation.  u, nrm must be complete (caller synchronised).
-// Ends with a barrier.
-template <typename T, int L>
-__device__ void phi_tile(const Cfg& c, const float* u, const float* nrm,
-                         const T* __restrict__ omega, int rows, float* out, int ol, float* rs) {
-    const int tid = threadIdx.x;
-    if (c.phi == PHI_FAVOR) {
-        for (int f = tid; f < c.r; f += NT) {
-            float w[D];
-#pragma unroll
-            for (int i = 0; i < D; i += 4) {
-                float4 x = Elem<T>::load4(omega, (long)f * D + i);
-                w[i] = x.x;
-                w[i + 1] = x.y;
-                w[i + 2] = x.z;
-                w[i + 3] = x.w;
-            }
-            for (int t = 0; t < L; ++t) {
-                float dot = 0.f;
-#pragma unroll
-                for (int i = 0; i < D; ++i) dot = fmaf(w[i], u[t * D + i], dot);
-                out[t * ol + f] = t < rows ? favor_feature(c, dot, nrm[t]) : 0.f;
-            }
-        }
-    } else {
-        for (int idx = tid; idx < L * c.r; idx += NT) {
-            const int t = idx / c.r, f = idx - t * c.r;
-            float y = 0.f;
-            if (t < rows) y = phi_feature<T>(c, u + t * D, 0.f, f, omega);
-            out[t * ol + f] = y;
-        }
-    }
-    __syncthreads();
-    if (c.sum_norm) {
-        const int lane = tid & 63, w = tid >> 6;
-        for (int t = w; t < L; t += NT / 64) {
-            float s = 0.f;
-            for (int f = lane; f < c.r; f += 64) s += out[t * ol + f];
-            s = wave_sum(s);
-            if (lane == 0) rs[t] = 1.f / fmaxf(s, c.eps);
-        }
-        __syncthreads();
-        for (int idx = tid; idx < L * c.r; idx += NT) {
-            const int t = idx / c.r, f = idx - t * c.r;
-            out[t * ol + f] *= rs[t];
-        }
-        __syncthreads();
-    }
-}
+constexpr int NT = VNT; // threads per workgroup in this file
 
 // ---------------------------------------------------------------------------
 // Feature map alone: phi [BH, N, r] float32.
@@ -191,8 +114,10 @@ __global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Prefix over segments, one thread per state element, fixed order.
+// Prefix over segments, one thread per state element, fixed order.  REV: the
+// same over the segments in reverse order (exclusive suffix sums).
 // ---------------------------------------------------------------------------
+template <bool REV>
 __global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const float* __restrict__ S0,
                                                      const float* __restrict__ z0,
                                                      float* __restrict__ ws, int prefix_stride,
@@ -208,7 +133,9 @@ __global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const flo
     const int64_t rdv = (int64_t)r * DV;
     float run = 0.f;
     if (S0) run = e < rdv ? S0[bh * rdv + e] : z0[bh * r + (e - rdv)];
-    float* p = ws + bh * G * E + e;
+    // REV walks the segments from the last: segment index G-1-i at step i
+    float* p = REV ? ws + (bh * G + G - 1) * E + e : ws + bh * G * E + e;
+    const int64_t step = REV ? -E : E;
     // batches of independent loads (the scan is latency-bound: one element per
     // thread), then the fixed-order running sum; the exclusive prefix is
     // written back only for the segments that read it (every prefix_stride-th;
@@ -218,11 +145,11 @@ __global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const flo
         const int n = (int)min<int64_t>(BATCH, G - g0);
         float a[BATCH];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) a[i] = i < n ? p[(g0 + i) * E] : 0.f;
+        for (int i = 0; i < BATCH; ++i) a[i] = i < n ? p[(g0 + i) * step] : 0.f;
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
             if (i < n) {
-                if (prefix_stride > 0 && ((g0 + i) & pmask) == 0) p[(g0 + i) * E] = run;
+                if (prefix_stride > 0 && ((g0 + i) & pmask) == 0) p[(g0 + i) * step] = run;
                 run += a[i];
             }
         }
@@ -627,8 +554,16 @@ hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, cons
                                float* fin, hipStream_t st) {
     const int64_t E = state_elems(r);
     const dim3 grid((unsigned)(((E + NT - 1) / NT) * s.BH));
-    hipLaunchKernelGGL(k_segment_scan, grid, dim3(NT), 0, st, r, sp.G, S0, z0, ws, prefix_stride,
-                       S_fin, z_fin, fin);
+    hipLaunchKernelGGL(k_segment_scan<false>, grid, dim3(NT), 0, st, r, sp.G, S0, z0, ws,
+                       prefix_stride, S_fin, z_fin, fin);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_suffix_scan(int r, Shape s, SegPlan sp, float* ws, hipStream_t st) {
+    const int64_t E = state_elems(r);
+    const dim3 grid((unsigned)(((E + NT - 1) / NT) * s.BH));
+    hipLaunchKernelGGL(k_segment_scan<true>, grid, dim3(NT), 0, st, r, sp.G, nullptr, nullptr, ws,
+                       1, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 

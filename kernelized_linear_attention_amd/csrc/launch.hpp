@@ -88,6 +88,10 @@ hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, cons
                                float* ws, int prefix_stride, float* S_fin, float* z_fin,
                                float* fin, hipStream_t st);
 
+// Exclusive suffix over segments: overwrites ws[bh][g] with the sum of
+// ws[bh][g+1 ..] (zero for the last segment), in a fixed order.
+hipError_t launch_segment_suffix_scan(int r, Shape s, SegPlan sp, float* ws, hipStream_t st);
+
 // Outputs of every segment.  causal: chunked recurrence from the segment's
 // carried-in state ws[bh][g]; bidirectional: readout against the full
 // summary fin[bh].
@@ -116,6 +120,23 @@ hipError_t launch_segment_scan_varlen(int r, int64_t H, int64_t num_seqs, int64_
                                       const int64_t* first, const float* S0, const float* z0,
                                       float* ws, int prefix_stride, float* S_fin, float* z_fin,
                                       hipStream_t st);
+
+// Backward pass (backward.hip), vector kernels, every feature map.
+// Query pass: from the forward state of each segment (causal: carried-in
+// prefix ws_f[bh][g]; bidirectional: total fin_f[bh]) it writes dq and the
+// segment increments ws_b[bh][g] = (sum phi(q_i) dnum_i^T, sum phi(q_i) dden_i);
+// causal also writes tok[bh][t] = (1 / max(den_t, eps) or 1, dden_t).
+// Key pass: from the backward state of each segment (causal: exclusive
+// suffix ws_b[bh][g], chunks walked last to first; bidirectional: total
+// fin_b[bh]) it writes dk and dv.
+hipError_t launch_backward_query(const Cfg& c, int dtype, int causal, const void* q,
+                                 const void* k, const void* v, const void* dout, const void* omega,
+                                 Shape s, SegPlan sp, const float* state, int64_t sbh, int64_t sg,
+                                 float* inc, float* tok, void* dq, hipStream_t st);
+hipError_t launch_backward_key(const Cfg& c, int dtype, int causal, const void* q, const void* k,
+                               const void* v, const void* dout, const void* omega, Shape s,
+                               SegPlan sp, const float* state, int64_t sbh, int64_t sg,
+                               const float* tok, void* dk, void* dv, hipStream_t st);
 
 // p[0, n) = 0 with a plain kernel (capturable into a graph).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);

@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-T_Q, T_K, T_V, T_OMEGA, T_PREFIX, T_LENGTHS = 0, 1, 2, 3, 4, 5
+T_Q, T_K, T_V, T_OMEGA, T_PREFIX, T_LENGTHS, T_DOUT = 0, 1, 2, 3, 4, 5, 6
 
 
 def rng(workload: int, tensor: int, rep: int = 0) -> np.random.Generator:

@@ -57,6 +57,8 @@ def test_constants_match_header():
     assert d["LIN_ATTN_OP_BIDIR"] == binding.OP_BIDIR
     assert d["LIN_ATTN_OP_CAUSAL"] == binding.OP_CAUSAL
     assert d["LIN_ATTN_OP_CAUSAL_VARLEN"] == binding.OP_CAUSAL_VARLEN
+    assert d["LIN_ATTN_OP_BIDIR_BACKWARD"] == binding.OP_BIDIR_BACKWARD
+    assert d["LIN_ATTN_OP_CAUSAL_BACKWARD"] == binding.OP_CAUSAL_BACKWARD
     assert (d["LIN_ATTN_OK"], d["LIN_ATTN_ERR_INVALID"], d["LIN_ATTN_ERR_UNSUPPORTED"],
             d["LIN_ATTN_ERR_WORKSPACE"], d["LIN_ATTN_ERR_HIP"]) == (0, -1, -2, -3, -4)
 
@@ -252,3 +254,48 @@ def test_orf_arguments():
     assert orf(FAKE, None, 1, 256, 65, 1, FAKE, None) == UNSUPPORTED
     assert orf(FAKE, None, 0, 256, 64, 1, FAKE, None) == OK
     assert orf(FAKE, None, 1, 0, 64, 1, FAKE, None) == OK
+
+
+def backward(p, fn="lin_attn_causal_backward", B=1, H=2, N=100, d=64, dv=64, ptr=FAKE,
+             dout=FAKE, grads=FAKE, omega=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return getattr(lib, fn)(ctypes.byref(p), ptr, ptr, ptr, dout, B, H, N, d, dv, omega, grads,
+                            grads, grads, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["lin_attn_bidir_backward", "lin_attn_causal_backward"])
+def test_backward_arguments(fn):
+    p = params()
+    assert backward(p, fn, B=-1) == INVALID
+    assert backward(p, fn, N=-1) == INVALID
+    assert backward(p, fn, ptr=None) == INVALID
+    assert backward(p, fn, dout=None) == INVALID
+    assert backward(p, fn, dout=FAKE + 2) == INVALID
+    assert backward(p, fn, grads=None) == INVALID
+    assert backward(p, fn, omega=None) == INVALID
+    assert backward(p, fn, ws=FAKE + 4) == INVALID
+    assert backward(params(eps=0.0), fn) == INVALID
+    assert backward(params("favor", r=512), fn) == UNSUPPORTED
+    assert backward(p, fn, d=32) == UNSUPPORTED
+    op = binding.OP_BIDIR_BACKWARD if "bidir" in fn else binding.OP_CAUSAL_BACKWARD
+    need = binding.lin_attn_workspace_bytes(op, p, 1, 2, 100, 64, 64)
+    assert need > 0
+    assert backward(p, fn, ws_bytes=need - 4) == WORKSPACE
+    assert backward(p, fn, ws=None, ws_bytes=0) == WORKSPACE
+    assert backward(p, fn, N=0, ptr=None, dout=None, grads=None) == OK
+    assert backward(p, fn, H=0) == OK
+
+
+def test_backward_workspace_formula():
+    """Forward and backward increments of every segment (the vector kernels'
+    plan: two workgroups per CU, 64 segments of 1024 tokens per head at H = 8,
+    N = 65536), then the two full summaries per head (bidirectional) or two
+    floats per token (causal: 1 / max(den, eps) and the denominator's
+    gradient)."""
+    p = params()
+    E = 256 * 64 + 256
+    inc = 2 * 8 * 64 * E * 4
+    assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR_BACKWARD, p, 1, 8, 65536, 64, 64) == \
+        inc + 2 * 8 * E * 4
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 65536, 64, 64) == \
+        inc + 8 * 65536 * 2 * 4
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 0, 64, 64) == 0

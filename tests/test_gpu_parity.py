@@ -425,3 +425,112 @@ def test_orf_omega_drives_favor_like_the_host_sampler(gpu_lib):
     ro, rS, rz = oracle.causal(c.qh, c.kh, c.vh, "favor", omega=host(om), **kw)
     assert_parity(out, ro, 2e-2, "orf causal out")
     np.testing.assert_allclose(host(om), ref[0], rtol=2 ** -8, atol=1e-6)
+
+
+# ---------------------------------------------------------------- backward pass
+def _bwd(gpu_lib, oracle_too, form, c, do, kind, **kw):
+    fn = gpu_lib.lin_attn_bidir_backward if form == "bidir" else gpu_lib.lin_attn_causal_backward
+    got = fn(c.q, c.k, c.v, do, kind, **c.gkw(**kw))
+    if not oracle_too:
+        return got, None
+    ofn = oracle.bidir_backward if form == "bidir" else oracle.causal_backward
+    return got, ofn(c.qh, c.kh, c.vh, host(do), kind, **c.okw(**kw))
+
+
+def _assert_grads(got, ref, tol, what):
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert g.dtype == got[0].dtype
+        assert_parity(g, r, tol, f"{what} {name}")
+
+
+@pytest.mark.parametrize("form", ["bidir", "causal"])
+@pytest.mark.parametrize("norm", ["attn", "none"])
+@pytest.mark.parametrize("kind,dtype,r,nu,sum_norm,scale", MAPS, ids=MAP_IDS)
+def test_backward(gpu_lib, form, kind, dtype, r, nu, sum_norm, scale, norm):
+    """dq, dk, dv over several segments, chunks and a ragged tail (300
+    tokens: segments of 64, chunks of 16, a last segment of 44)."""
+    if not _norm_ok(kind, norm):
+        pytest.skip("identity map with attention normalisation has no positive denominator")
+    B, H, N = 2, 2, 300
+    c = Case(120, B, H, N, kind, dtype, r=r, nu=nu)
+    do = dev(inputs.normal((B, H, N, 64), 120, inputs.T_DOUT), dtype)
+    got, ref = _bwd(gpu_lib, True, form, c, do, kind, sum_norm=sum_norm, scale=scale, norm=norm)
+    _assert_grads(got, ref, TOL[dtype], f"{form} backward")
+
+
+@pytest.mark.parametrize("form", ["bidir", "causal"])
+@pytest.mark.parametrize("N", [1, 15, 16, 17, 64, 65])
+def test_backward_short_sequences(gpu_lib, form, N):
+    c = Case(121, 1, 3, N, "favor", torch.float32, r=96)
+    do = dev(inputs.normal((1, 3, N, 64), 121, inputs.T_DOUT), torch.float32)
+    got, ref = _bwd(gpu_lib, True, form, c, do, "favor", scale=0.4)
+    if N == 1:
+        # one token: out = v whatever q and k are, so dv = dout and dq = dk = 0
+        # exactly; only rounding is left in them
+        assert_parity(got[2], host(do), 1e-6, "N=1 dv")
+        for g in got[:2]:
+            assert float(g.abs().max()) <= 1e-5 * float(do.abs().max())
+        return
+    _assert_grads(got, ref, 1e-4, f"{form} N={N}")
+
+
+@pytest.mark.parametrize("form", ["bidir", "causal"])
+def test_backward_segment_count_changes_rounding_only(gpu_lib, form):
+    c = Case(122, 1, 2, 1000, "elu1", torch.float32, r=64)
+    do = dev(inputs.normal((1, 2, 1000, 64), 122, inputs.T_DOUT), torch.float32)
+    ofn = oracle.bidir_backward if form == "bidir" else oracle.causal_backward
+    ref = ofn(c.qh, c.kh, c.vh, host(do), "elu1", **c.okw())
+    fn = gpu_lib.lin_attn_bidir_backward if form == "bidir" else gpu_lib.lin_attn_causal_backward
+    first = None
+    for n_seg in (1, 3, 16):
+        got = fn(c.q, c.k, c.v, do, "elu1", n_seg=n_seg, **c.gkw())
+        _assert_grads(got, ref, 1e-4, f"{form} n_seg={n_seg}")
+        again = fn(c.q, c.k, c.v, do, "elu1", n_seg=n_seg, **c.gkw())
+        assert all(torch.equal(a, b) for a, b in zip(got, again)), "not bitwise reproducible"
+
+
+def test_backward_zero_features_stay_finite(gpu_lib):
+    """DPFP of vectors with one positive component has no nonzero feature
+    (Kernel Zoo sec. 6.6): every denominator is clamped and every gradient
+    is exactly zero, never NaN, with and without sum normalisation."""
+    B, H, N = 1, 1, 70
+    x = np.zeros((B, H, N, 64), np.float32)
+    x[..., 0] = 1.0
+    q = dev(x, torch.float32)
+    v = dev(inputs.normal((B, H, N, 64), 123, inputs.T_V), torch.float32)
+    do = dev(inputs.normal((B, H, N, 64), 123, inputs.T_DOUT), torch.float32)
+    for sn in (False, True):
+        for fn in (gpu_lib.lin_attn_bidir_backward, gpu_lib.lin_attn_causal_backward):
+            for g in fn(q, q, v, do, "dpfp", nu=1, sum_norm=sn):
+                assert bool(torch.isfinite(g).all()) and torch.count_nonzero(g) == 0
+
+
+def test_causal_backward_of_last_row_equals_bidirectional(gpu_lib):
+    """A loss on the last row alone: both forms give the same gradients
+    (that query sees every key in both)."""
+    B, H, N = 1, 2, 777
+    c = Case(124, B, H, N, "favor", torch.float32, r=256)
+    do_np = np.zeros((B, H, N, 64), np.float32)
+    do_np[:, :, -1] = inputs.normal((B, H, 64), 124, inputs.T_DOUT)
+    do = dev(do_np, torch.float32)
+    kw = c.gkw(scale=64 ** -0.25)
+    a = gpu_lib.lin_attn_causal_backward(c.q, c.k, c.v, do, "favor", **kw)
+    b = gpu_lib.lin_attn_bidir_backward(c.q, c.k, c.v, do, "favor", **kw)
+    for x, y in zip(a, b):
+        assert_parity(x, host(y), 1e-4, "last-row gradients")  # two summation orders
+
+
+def test_workload_favor_bidir_backward(gpu_lib):
+    w = workloads.FAVOR_BIDIR
+    c = _wl_case(w)
+    do = dev(inputs.normal((w.B, w.H, w.N, w.dv), w.wid, inputs.T_DOUT), DT[w.dtype])
+    got, ref = _bwd(gpu_lib, True, "bidir", c, do, w.kind, **_wl_kw(w))
+    _assert_grads(got, ref, 2e-2, "bidir workload backward")
+
+
+def test_workload_favor_causal_backward(gpu_lib):
+    w = workloads.FAVOR_CAUSAL
+    c = _wl_case(w)
+    do = dev(inputs.normal((w.B, w.H, w.N, w.dv), w.wid, inputs.T_DOUT), DT[w.dtype])
+    got, ref = _bwd(gpu_lib, True, "causal", c, do, w.kind, **_wl_kw(w))
+    _assert_grads(got, ref, 2e-2, "causal prefill backward")

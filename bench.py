@@ -4,8 +4,9 @@ One step = one causal FAVOR+ prefill of the headline workload (B=1, H=8,
 N=65536, d=64, r=256, bf16 inputs, float32 state): feature map, masked
 intra-chunk block, inter-chunk readout and state update, segment carry.
 The same run also times the 12-layer batched decode (B=256, H=8, fp32 state
-read-modify-written in HBM) and the bidirectional FAVOR+ pass (B=4, H=8,
-N=4096), and reports each against its roofline.  Inputs are synthetic
+read-modify-written in HBM), the bidirectional FAVOR+ pass (B=4, H=8,
+N=4096), the packed prefill and the backward passes of the causal and
+bidirectional workloads, and reports each against its roofline.  Inputs are synthetic
 (seeded N(0,1)), resident in HBM before timing starts; two input sets
 alternate so that the 256 MB last-level cache cannot hold a step's inputs.
 
@@ -28,12 +29,22 @@ METRIC = "causal FAVOR+ prefill tokens/s + % MFMA peak (r=256,d=64); decode GB/s
 # MI355X published peaks
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # HBM3E
+PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector ALU
 
 
 def favor_alg_flops_per_tok_head(r=256, d=64, dv=64):
     """Algorithmic flops of one token of one head: q and k projections
     (2 * 2rd), phi(K)^T V and phi(Q) S (2 * 2 r dv), z / den / sum (~3r)."""
     return 4 * r * d + 4 * r * dv + 3 * r
+
+
+def backward_alg_flops_per_tok_head(r=256, d=64, dv=64):
+    """Algorithmic flops of the backward pass for one token of one head,
+    counting each product once (no recomputation): q and k projections
+    (2 * 2rd), the forward state and readout (2 * 2 r dv), dphi(q) and the
+    backward state (2 * 2 r dv), dphi(k) and dv (2 * 2 r dv), and dq, dk
+    through the map (2 * 2rd)."""
+    return 8 * r * d + 12 * r * dv
 
 
 def decode_alg_bytes_per_head(r=256, dv=64, in_bytes=2):
@@ -48,7 +59,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "bidir", "varlen"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "bidir", "varlen", "backward"],
+                    default=None,
                     help="run one section only (for profiling)")
     return ap.parse_args()
 
@@ -265,6 +277,44 @@ def main():
                             "ms_per_step": vms, "tokens_per_s": wv.N / (vms * 1e-3),
                             "tflops_alg": vach, "frac_mfma": vach / PEAK_BF16_TFLOPS}
         del vsets
+
+    # ------------------------------------------------------------------ backward
+    if args.only in (None, "backward"):
+        bw = {}
+        for form, wk in (("causal", workloads.FAVOR_CAUSAL), ("bidir", workloads.FAVOR_BIDIR)):
+            sk = workloads.scale_of(wk)
+            shape = (wk.B, wk.H, wk.N, wk.d)
+            ksets = []
+            for rep in range(2):
+                ksets.append(tuple(to_dev(inputs.normal(shape, wk.wid, t, rep))
+                                   for t in (inputs.T_Q, inputs.T_K, inputs.T_V, inputs.T_DOUT)))
+            om = to_dev(inputs.orf_omega(wk.r, wk.d, wk.wid))
+            op = binding.OP_CAUSAL_BACKWARD if form == "causal" else binding.OP_BIDIR_BACKWARD
+            pk = binding.make_params("favor", wk.r, dtype=torch.bfloat16, scale=sk, eps=wk.eps)
+            kws = torch.empty(binding.lin_attn_workspace_bytes(op, pk, wk.B, wk.H, wk.N, wk.d,
+                                                               wk.dv),
+                              dtype=torch.uint8, device=dev)
+            fn = (binding.lin_attn_causal_backward if form == "causal"
+                  else binding.lin_attn_bidir_backward)
+
+            def kstep(i, fn=fn, ksets=ksets, om=om, sk=sk, wk=wk, kws=kws):
+                q, k, v, do = ksets[i % 2]
+                fn(q, k, v, do, "favor", omega=om, scale=sk, eps=wk.eps, workspace=kws)
+
+            total_ms, per = timed(kstep, args.steps, args.warmup)
+            kms = total_ms / args.steps
+            kflops = backward_alg_flops_per_tok_head(wk.r, wk.d, wk.dv) * wk.B * wk.H * wk.N
+            kach = kflops / (float(np.mean(per)) * 1e-3) / 1e12
+            bw[form] = {"workload": wk.name, "B": wk.B, "H": wk.H, "N": wk.N, "r": wk.r,
+                        "ms_per_step": kms, "tokens_per_s": wk.B * wk.N / (kms * 1e-3),
+                        "roofline": {"bound": "alu", "achieved": kach,
+                                     "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": kach / PEAK_FP32_VALU_TFLOPS,
+                                     "kernel": "whole call (fp32 vector kernels)",
+                                     "alg_flops_per_launch": kflops,
+                                     "avg_launch_ms": float(np.mean(per))}}
+            del ksets
+        result["backward"] = bw
 
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, scale)

@@ -20,6 +20,8 @@ Definitions followed (see the header of oracle.c for the passages):
   * explicit N x N form: the interactive chapter's "rescan every key";
   * orthogonal random features: Performer page sec. 2 step 4, Kernel Zoo
     sec. 5.1-5.3 (Gram-Schmidt of Gaussian rows, chi or sqrt(d) lengths);
+  * input projection: q, k, v = W_q x, W_k x, W_v x per token (Kernel Zoo
+    sec. 1.2 step 1), a float64 matmul ahead of the calls above;
   * backward pass: the chain rule through the readout, the summaries and
     the feature map ("Reassociate a feature-map kernel..." par. 6 asks for
     gradient error to be evaluated).
@@ -289,3 +291,27 @@ def causal_backward(q, k, v, dout, kind, *, omega=None, nu=1, sum_norm=False, no
     from zero state."""
     return _backward("orc_causal_backward", q, k, v, dout, kind, omega, nu, sum_norm, norm,
                      scale, eps)
+
+
+def project(x, w, heads):
+    """Per-token projection W x (Kernel Zoo sec. 1.2 step 1) of x [B, N, dm]
+    by w [heads * d, dm] (output row h*d + i is feature i of head h):
+    returns [B, heads, N, d] in float64."""
+    x = _f64(x)
+    w = _f64(w)
+    B, N, _ = x.shape
+    d = w.shape[0] // heads
+    y = np.matmul(x, w.T)                                  # [B, N, heads * d]
+    return np.ascontiguousarray(y.reshape(B, N, heads, d).transpose(0, 2, 1, 3))
+
+
+def causal_proj(x, w_q, w_k, w_v, heads, kind, **kw):
+    """The causal recurrence on q, k, v projected from x."""
+    return causal(project(x, w_q, heads), project(x, w_k, heads), project(x, w_v, heads), kind,
+                  **kw)
+
+
+def bidir_proj(x, w_q, w_k, w_v, heads, kind, **kw):
+    """The bidirectional form on q, k, v projected from x."""
+    return bidir(project(x, w_q, heads), project(x, w_k, heads), project(x, w_v, heads), kind,
+                 **kw)

@@ -560,3 +560,41 @@ def test_causal_backward_of_last_row_equals_bidirectional():
     for a, b in zip(oracle.causal_backward(q, k, v, dout, "favor", **kw),
                     oracle.bidir_backward(q, k, v, dout, "favor", **kw)):
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Input projection (Kernel Zoo sec. 1.2 step 1: k, v, q = W_k x, W_v x, W_q x)
+# --------------------------------------------------------------------------
+
+def test_projection_reproduces_the_fwp_trace():
+    """Tokens x = [q, k, v] of the running example with selector weights
+    give back the printed FWP outputs (Kernel Zoo sec. 1.4)."""
+    g = golden("running_example.json")
+    Q, K, V = (A(g[n], float) for n in ("Q", "K", "V"))
+    x = np.concatenate([Q, K, V], axis=1)[None]            # [1, 4, 6]
+    eye = np.eye(6)
+    w_q, w_k, w_v = eye[0:2], eye[2:4], eye[4:6]
+    out, S, _ = oracle.causal_proj(x, w_q, w_k, w_v, 1, "identity", norm="none")
+    np.testing.assert_array_equal(out[0, 0], g["fwp_y"])
+    np.testing.assert_array_equal(S[0, 0], A(g["fwp_W"][3]).T)
+
+
+@pytest.mark.parametrize("form", ["bidir", "causal"])
+def test_projection_by_permuted_selectors_equals_the_plain_call(form):
+    """W rows that pick permuted coordinates of x: head h of the projected
+    call equals the plain call on those coordinates (fixes which rows of W
+    belong to which head, and that x is multiplied by W, not by W^T)."""
+    g = np.random.default_rng(41)
+    B, N, H, d, dm = 2, 7, 3, 4, 16
+    x = g.standard_normal((B, N, dm))
+    perms = [g.permutation(dm)[: H * d] for _ in range(3)]
+    ws = [np.eye(dm)[p] for p in perms]                     # [H*d, dm] selectors
+    om = g.standard_normal((8, d))
+    kw = dict(omega=om, scale=0.6)
+    fwd = oracle.causal_proj if form == "causal" else oracle.bidir_proj
+    plain = oracle.causal if form == "causal" else oracle.bidir
+    got = fwd(x, *ws, H, "favor", **kw)
+    q, k, v = (np.stack([x[:, :, p[h * d:(h + 1) * d]] for h in range(H)], axis=1) for p in perms)
+    want = plain(q, k, v, "favor", **kw)
+    for a, b in zip(got, want):
+        np.testing.assert_array_equal(a, b)

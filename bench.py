@@ -5,8 +5,9 @@ N=65536, d=64, r=256, bf16 inputs, float32 state): feature map, masked
 intra-chunk block, inter-chunk readout and state update, segment carry.
 The same run also times the 12-layer batched decode (B=256, H=8, fp32 state
 read-modify-written in HBM), the bidirectional FAVOR+ pass (B=4, H=8,
-N=4096), the packed prefill and the backward passes of the causal and
-bidirectional workloads, and reports each against its roofline.  Inputs are synthetic
+N=4096), the packed prefill, the prefill from 512-wide tokens with the q/k/v
+projection fused in, and the backward passes of the causal and bidirectional
+workloads, and reports each against its roofline.  Inputs are synthetic
 (seeded N(0,1)), resident in HBM before timing starts; two input sets
 alternate so that the 256 MB last-level cache cannot hold a step's inputs.
 
@@ -59,7 +60,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "bidir", "varlen", "backward"],
+    ap.add_argument("--only", choices=["prefill", "decode", "bidir", "varlen", "backward",
+                                       "proj"],
                     default=None,
                     help="run one section only (for profiling)")
     return ap.parse_args()
@@ -315,6 +317,62 @@ def main():
                                      "avg_launch_ms": float(np.mean(per))}}
             del ksets
         result["backward"] = bw
+
+    # ------------------------------------------------------------------ from tokens
+    if args.only in (None, "proj"):
+        wp = workloads.FAVOR_CAUSAL
+        dm = 512
+        sp_ = workloads.scale_of(wp)
+        psets = []
+        for rep in range(2):
+            x = to_dev(inputs.normal((wp.B, wp.N, dm), wp.wid, inputs.T_X, rep))
+            psets.append(x)
+        wq, wk, wv = (to_dev(a) for a in inputs.projection_weights(wp.H, wp.d, dm, wp.wid))
+        om = to_dev(inputs.orf_omega(wp.r, wp.d, wp.wid))
+        pS = torch.empty((wp.B, wp.H, wp.r, wp.dv), device=dev)
+        pz = torch.empty((wp.B, wp.H, wp.r), device=dev)
+        pout = torch.empty((wp.B, wp.H, wp.N, wp.dv), device=dev, dtype=torch.bfloat16)
+        pp = binding.make_params("favor", wp.r, dtype=torch.bfloat16, scale=sp_, eps=wp.eps)
+        pws = torch.empty(binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_PROJ, pp, wp.B, wp.H,
+                                                           wp.N, wp.d, wp.dv),
+                          dtype=torch.uint8, device=dev)
+
+        def pstep(i):
+            binding.lin_attn_causal_proj(psets[i % 2], wq, wk, wv, wp.H, "favor", omega=om,
+                                         scale=sp_, eps=wp.eps, S=pS, z=pz, out=pout,
+                                         workspace=pws)
+
+        total_ms, per = timed(pstep, args.steps, args.warmup)
+        pms = total_ms / args.steps
+        proj_flops = 3 * 2 * dm * wp.d * wp.H * wp.B * wp.N
+        att_flops = favor_alg_flops_per_tok_head(wp.r, wp.d, wp.dv) * wp.B * wp.H * wp.N
+        pach = (proj_flops + att_flops) / (float(np.mean(per)) * 1e-3) / 1e12
+
+        # the unfused route for comparison: torch's matmul writes q, k, v, then
+        # the matrix-core prefill reads them
+        wcat = torch.cat([wq, wk, wv], dim=0)
+        uws = torch.empty(binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, pp, wp.B, wp.H,
+                                                           wp.N, wp.d, wp.dv, 64),
+                          dtype=torch.uint8, device=dev)
+
+        def ustep(i):
+            y = torch.matmul(psets[i % 2], wcat.t())                 # [B, N, 3 * H * d]
+            y = y.view(wp.B, wp.N, 3, wp.H, wp.d).permute(2, 0, 3, 1, 4).contiguous()
+            binding.lin_attn_causal_chunked(y[0], y[1], y[2], "favor", omega=om, scale=sp_,
+                                            eps=wp.eps, chunk=64, S=pS, z=pz, out=pout,
+                                            workspace=uws)
+
+        u_total, _ = timed(ustep, args.steps, args.warmup)
+        result["proj"] = {
+            "workload": wp.name + "_from_tokens", "B": wp.B, "H": wp.H, "N": wp.N, "d_model": dm,
+            "r": wp.r, "ms_per_step": pms, "tokens_per_s": wp.B * wp.N / (pms * 1e-3),
+            "unfused_torch_matmul_then_prefill_ms": u_total / args.steps,
+            "roofline": {"bound": "alu", "achieved": pach, "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": pach / PEAK_FP32_VALU_TFLOPS,
+                         "kernel": "whole call (vector kernels, projection on MFMA)",
+                         "alg_flops_per_launch": proj_flops + att_flops,
+                         "avg_launch_ms": float(np.mean(per))}}
+        del psets
 
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, scale)

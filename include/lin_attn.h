@@ -1,7 +1,8 @@
 /*
  * lin_attn.h -- C ABI of liblinattn.so: kernelized linear attention on
- * AMD MI355X (gfx950): forward pass, decode, orthogonal random features and
- * the backward pass.
+ * AMD MI355X (gfx950): forward pass (also from the tokens, with the q/k/v
+ * projection fused in), decode, orthogonal random features and the backward
+ * pass.
  *
  * Sources of the operations (the pages the method is taken from):
  *   [KZ] "The Kernel Zoo: Performers, Fast Weight Programmers, and the
@@ -82,6 +83,8 @@ extern "C" {
 #define LIN_ATTN_OP_CAUSAL_VARLEN 3
 #define LIN_ATTN_OP_BIDIR_BACKWARD 4
 #define LIN_ATTN_OP_CAUSAL_BACKWARD 5
+#define LIN_ATTN_OP_CAUSAL_PROJ 6
+#define LIN_ATTN_OP_BIDIR_PROJ 7
 
 /*
  * Method parameters, shared by every call.
@@ -232,6 +235,36 @@ int lin_attn_orf_omega(const float* gauss, const float* len_gauss, int64_t n_mat
                        int64_t d, int32_t dtype, void* omega, void* stream);
 
 /*
+ * Causal prefill and bidirectional attention from the tokens, with the
+ * input projection fused into the loads of the kernels ([KZ] sec. 1.2 step
+ * 1: k, v, q = W_k x, W_v x, W_q x for every token x): q, k and v are
+ * computed in float32 from bfloat16 x and W inside the kernels, chunk by
+ * chunk, and never written to memory.  Then exactly lin_attn_causal_chunked
+ * (state_in, S, z as there) or lin_attn_bidir (S_out, z_out as there).
+ *   x              [B, N, d_model] bfloat16 tokens.
+ *   w_q, w_k, w_v  [H * d, d_model] bfloat16 each (out = W x, the layout of a
+ *                  linear layer's weight): row h*d + i gives feature i of
+ *                  head h.
+ *   out            [B, H, N, dv] bfloat16.
+ *   d_model        a multiple of 16, at most 65536 (else -2).
+ * lin_attn_params.dtype must be LIN_ATTN_BF16 (float32 returns -2).  The
+ * float32 vector kernels run these calls for every feature map.
+ *   ws   at least lin_attn_workspace_bytes(LIN_ATTN_OP_CAUSAL_PROJ or
+ *        LIN_ATTN_OP_BIDIR_PROJ, p, B, H, N, d, dv, 0) bytes.
+ * Errors as lin_attn_causal_chunked / lin_attn_bidir; x, w_q, w_k, w_v must
+ * be 16-byte aligned.
+ */
+int lin_attn_causal_proj(const lin_attn_params* p, const void* x, const void* w_q,
+                         const void* w_k, const void* w_v, int64_t B, int64_t H, int64_t N,
+                         int64_t d_model, int64_t d, int64_t dv, const void* omega, float* S,
+                         float* z, int32_t state_in, void* out, void* ws, size_t ws_bytes,
+                         void* stream);
+int lin_attn_bidir_proj(const lin_attn_params* p, const void* x, const void* w_q,
+                        const void* w_k, const void* w_v, int64_t B, int64_t H, int64_t N,
+                        int64_t d_model, int64_t d, int64_t dv, const void* omega, void* out,
+                        float* S_out, float* z_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Backward pass: the gradients dq, dk, dv of a loss L given dout = dL/dout
  * for the outputs of lin_attn_bidir (lin_attn_bidir_backward) or of
  * lin_attn_causal_chunked from zero state (lin_attn_causal_backward), same
@@ -266,7 +299,8 @@ int lin_attn_causal_backward(const lin_attn_params* p, const void* q, const void
  * Workspace bytes needed by lin_attn_bidir (op = LIN_ATTN_OP_BIDIR),
  * lin_attn_causal_chunked (op = LIN_ATTN_OP_CAUSAL) or, with B = num_seqs and
  * N = total, lin_attn_causal_varlen (op = LIN_ATTN_OP_CAUSAL_VARLEN), and
- * the backward calls (LIN_ATTN_OP_BIDIR_BACKWARD, LIN_ATTN_OP_CAUSAL_BACKWARD).
+ * the backward calls (LIN_ATTN_OP_BIDIR_BACKWARD, LIN_ATTN_OP_CAUSAL_BACKWARD) and
+ * the projected calls (LIN_ATTN_OP_CAUSAL_PROJ, LIN_ATTN_OP_BIDIR_PROJ).
  * Host-only, deterministic in its arguments (independent of the device).
  * Returns 0 for invalid arguments.
  */

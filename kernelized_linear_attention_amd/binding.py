@@ -30,12 +30,14 @@ OP_CAUSAL = 2
 OP_CAUSAL_VARLEN = 3
 OP_BIDIR_BACKWARD = 4
 OP_CAUSAL_BACKWARD = 5
+OP_CAUSAL_PROJ = 6
+OP_BIDIR_PROJ = 7
 ABI_VERSION = 1
 
 # Every symbol include/lin_attn.h declares.
 EXPORTS = ("lin_attn_featuremap", "lin_attn_bidir", "lin_attn_causal_chunked",
            "lin_attn_causal_varlen", "lin_attn_orf_omega", "lin_attn_bidir_backward",
-           "lin_attn_causal_backward",
+           "lin_attn_causal_backward", "lin_attn_causal_proj", "lin_attn_bidir_proj",
            "lin_attn_decode_step", "lin_attn_workspace_bytes", "lin_attn_strerror",
            "lin_attn_abi_version")
 
@@ -68,6 +70,12 @@ for _fn in (_lib.lin_attn_bidir_backward, _lib.lin_attn_causal_backward):
     _fn.argtypes = [_PP, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P,
                     ctypes.c_size_t, _P]
     _fn.restype = ctypes.c_int
+_lib.lin_attn_causal_proj.argtypes = [_PP, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
+                                      _P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]
+_lib.lin_attn_causal_proj.restype = ctypes.c_int
+_lib.lin_attn_bidir_proj.argtypes = [_PP, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P,
+                                     _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.lin_attn_bidir_proj.restype = ctypes.c_int
 _lib.lin_attn_decode_step.argtypes = [_PP, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.lin_attn_decode_step.restype = ctypes.c_int
 _lib.lin_attn_workspace_bytes.argtypes = [_I32, _PP, _I64, _I64, _I64, _I64, _I64, _I32]
@@ -309,6 +317,68 @@ def lin_attn_decode_step(q, k, v, S, z, kind, *, omega=None, nu=1, sum_norm=Fals
                                    _ptr(om), _ptr(S), _ptr(z), _ptr(out),
                                    _stream(q.device, stream))
     _check("lin_attn_decode_step", rc)
+    return out
+
+
+def _proj_args(x, w_q, w_k, w_v, heads, kind, omega, nu):
+    _dev_tensor("x", x, torch.bfloat16)
+    for n, t in (("w_q", w_q), ("w_k", w_k), ("w_v", w_v)):
+        _dev_tensor(n, t, torch.bfloat16)
+    B, N, dm = x.shape
+    d = w_q.shape[0] // heads
+    dv = w_v.shape[0] // heads
+    om = _omega(kind, omega, torch.bfloat16)
+    return B, N, dm, d, dv, om, feature_width(kind, d, nu, om)
+
+
+def lin_attn_causal_proj(x, w_q, w_k, w_v, heads, kind, *, omega=None, nu=1, sum_norm=False,
+                         norm="attn", scale=1.0, eps=1e-6, n_seg=0, S=None, z=None,
+                         state_in=False, out=None, workspace=None, stream=None):
+    """Causal prefill from tokens x [B, N, d_model] (bf16) with the q/k/v
+    projection w_* [heads * 64, d_model] fused into the kernels.  Returns
+    (out [B, heads, N, 64], S, z)."""
+    B, N, dm, d, dv, om, r = _proj_args(x, w_q, w_k, w_v, heads, kind, omega, nu)
+    H = heads
+    p = make_params(kind, r, nu=nu, sum_norm=sum_norm, norm=norm, dtype=torch.bfloat16,
+                    scale=scale, eps=eps, n_seg=n_seg)
+    if S is None:
+        if state_in:
+            raise ValueError("state_in needs S and z")
+        S = torch.empty((B, H, r, dv), dtype=torch.float32, device=x.device)
+        z = torch.empty((B, H, r), dtype=torch.float32, device=x.device)
+    _dev_tensor("S", S, torch.float32)
+    _dev_tensor("z", z, torch.float32)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=torch.bfloat16, device=x.device)
+    _dev_tensor("out", out, torch.bfloat16)
+    ws, ws_bytes = _workspace(OP_CAUSAL_PROJ, p, B, H, N, d, dv, 0, x.device, workspace)
+    rc = _lib.lin_attn_causal_proj(ctypes.byref(p), _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), B, H,
+                                   N, dm, d, dv, _ptr(om), _ptr(S), _ptr(z), int(bool(state_in)),
+                                   _ptr(out), _ptr(ws), ws_bytes, _stream(x.device, stream))
+    _check("lin_attn_causal_proj", rc)
+    return out, S, z
+
+
+def lin_attn_bidir_proj(x, w_q, w_k, w_v, heads, kind, *, omega=None, nu=1, sum_norm=False,
+                        norm="attn", scale=1.0, eps=1e-6, n_seg=0, out=None, S_out=None,
+                        z_out=None, workspace=None, stream=None):
+    """Bidirectional attention from tokens x [B, N, d_model] (bf16) with the
+    q/k/v projection fused into the kernels.  Returns out [B, heads, N, 64]."""
+    B, N, dm, d, dv, om, r = _proj_args(x, w_q, w_k, w_v, heads, kind, omega, nu)
+    H = heads
+    p = make_params(kind, r, nu=nu, sum_norm=sum_norm, norm=norm, dtype=torch.bfloat16,
+                    scale=scale, eps=eps, n_seg=n_seg)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=torch.bfloat16, device=x.device)
+    _dev_tensor("out", out, torch.bfloat16)
+    for n, t in (("S_out", S_out), ("z_out", z_out)):
+        if t is not None:
+            _dev_tensor(n, t, torch.float32)
+    ws, ws_bytes = _workspace(OP_BIDIR_PROJ, p, B, H, N, d, dv, 0, x.device, workspace)
+    rc = _lib.lin_attn_bidir_proj(ctypes.byref(p), _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), B, H,
+                                  N, dm, d, dv, _ptr(om), _ptr(out), _ptr(S_out), _ptr(z_out),
+                                  _ptr(ws), ws_bytes, _stream(x.device, stream))
+    _check("lin_attn_bidir_proj", rc)
     return out
 
 

@@ -209,6 +209,31 @@ int backward_call(bool causal, const lin_attn_params* p, const void* q, const vo
     return launch_status(e);
 }
 
+// Fused input projection: the vector kernels with q, k, v projected from the
+// tokens in their loads.  Workspace as lin_attn_causal_chunked / lin_attn_bidir
+// on the vector plan (no increment halving).
+SegPlan proj_plan(const lin_attn_params* p, int64_t BH, int64_t N) {
+    return plan_segments(BH, N, p->n_seg, TARGET_BLOCKS_VALU);
+}
+
+size_t proj_ws_floats(bool causal, const lin_attn_params* p, int64_t BH, int64_t N) {
+    const SegPlan sp = proj_plan(p, BH, N);
+    const int64_t E = state_elems(p->r);
+    return (size_t)(BH * sp.G * E) + (causal ? 0 : (size_t)(BH * E));
+}
+
+// Checks shared by the two projected calls (beyond check_params / check_sizes).
+int proj_checks(const lin_attn_params* p, const void* x, const void* w_q, const void* w_k,
+                const void* w_v, int64_t B, int64_t H, int64_t N, int64_t d_model, bool any) {
+    if (d_model <= 0) return LIN_ATTN_ERR_INVALID;
+    if (any && B * N > 0 && !ptr_ok(x)) return LIN_ATTN_ERR_INVALID;
+    if (any && (!ptr_ok(w_q) || !ptr_ok(w_k) || !ptr_ok(w_v))) return LIN_ATTN_ERR_INVALID;
+    (void)H;
+    if (p->dtype != LIN_ATTN_BF16) return LIN_ATTN_ERR_UNSUPPORTED;
+    if (d_model % 16 != 0 || d_model > 65536) return LIN_ATTN_ERR_UNSUPPORTED;
+    return LIN_ATTN_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -229,7 +254,7 @@ const char* lin_attn_strerror(int32_t code) {
 size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B, int64_t H,
                                 int64_t N, int64_t d, int64_t dv, int32_t chunk) {
     (void)chunk;
-    if (op < LIN_ATTN_OP_BIDIR || op > LIN_ATTN_OP_CAUSAL_BACKWARD) return 0;
+    if (op < LIN_ATTN_OP_BIDIR || op > LIN_ATTN_OP_BIDIR_PROJ) return 0;
     if (!p || check_sizes(B, H, N) != LIN_ATTN_OK) return 0;
     // omega is not needed to size the workspace: check the rest with a dummy
     const int rc = check_params(p, d, dv, reinterpret_cast<const void*>(uintptr_t(16)));
@@ -237,6 +262,8 @@ size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B,
     const int64_t BH = B * H;
     if (BH == 0 || N == 0) return 0;
     if (op == LIN_ATTN_OP_CAUSAL_VARLEN) return varlen_layout(p, B, H, N).bytes;
+    if (op == LIN_ATTN_OP_CAUSAL_PROJ || op == LIN_ATTN_OP_BIDIR_PROJ)
+        return proj_ws_floats(op == LIN_ATTN_OP_CAUSAL_PROJ, p, BH, N) * sizeof(float);
     if (op == LIN_ATTN_OP_BIDIR_BACKWARD || op == LIN_ATTN_OP_CAUSAL_BACKWARD)
         return backward_layout(p, op == LIN_ATTN_OP_CAUSAL_BACKWARD, BH, N).floats * sizeof(float);
     return ws_floats(op, BH, plan_for(p, BH, N), p->r) * sizeof(float);
@@ -428,6 +455,97 @@ int lin_attn_causal_backward(const lin_attn_params* p, const void* q, const void
                              void* dv_out, void* ws, size_t ws_bytes, void* stream) {
     return backward_call(true, p, q, k, v, dout, B, H, N, d, dv, omega, dq, dk, dv_out, ws,
                          ws_bytes, stream);
+}
+
+int lin_attn_causal_proj(const lin_attn_params* p, const void* x, const void* w_q,
+                         const void* w_k, const void* w_v, int64_t B, int64_t H, int64_t N,
+                         int64_t d_model, int64_t d, int64_t dv, const void* omega, float* S,
+                         float* z, int32_t state_in, void* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+    int rc = check_params(p, d, dv, omega);
+    if (rc == LIN_ATTN_ERR_INVALID) return rc;
+    const int rs = check_sizes(B, H, N);
+    if (rs == LIN_ATTN_ERR_INVALID) return rs;
+    if (state_in != 0 && state_in != 1) return LIN_ATTN_ERR_INVALID;
+    if (!opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
+    if (B * H > 0 && (!ptr_ok(S) || !ptr_ok(z))) return LIN_ATTN_ERR_INVALID;
+    if (B * H > 0 && N > 0 && !ptr_ok(out)) return LIN_ATTN_ERR_INVALID;
+    const int pc = proj_checks(p, x, w_q, w_k, w_v, B, H, N, d_model, B * H > 0 && N > 0);
+    if (pc == LIN_ATTN_ERR_INVALID) return pc;
+    if (rc != LIN_ATTN_OK) return rc;
+    if (rs != LIN_ATTN_OK) return rs;
+    if (pc != LIN_ATTN_OK) return pc;
+    if (B * H == 0) return LIN_ATTN_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (N == 0) {
+        // no token: the state after token N is the starting state
+        if (state_in) return LIN_ATTN_OK;
+        hipError_t e = launch_fill_zero(S, B * H * (int64_t)p->r * DV, st);
+        if (e == hipSuccess) e = launch_fill_zero(z, B * H * (int64_t)p->r, st);
+        return launch_status(e);
+    }
+    const int64_t BH = B * H;
+    if (ws_bytes < proj_ws_floats(true, p, BH, N) * sizeof(float) || !ws)
+        return LIN_ATTN_ERR_WORKSPACE;
+    const Cfg c = make_cfg(p);
+    const Shape s{BH, N};
+    const SegPlan sp = proj_plan(p, BH, N);
+    const Proj P{(const bf16_raw*)x,
+                 {(const bf16_raw*)w_q, (const bf16_raw*)w_k, (const bf16_raw*)w_v},
+                 d_model,
+                 H};
+    float* inc = (float*)ws;
+    const int64_t E = state_elems(p->r);
+    hipError_t e = launch_segment_sums_proj(c, P, omega, s, sp, inc, st);
+    if (e == hipSuccess)
+        e = launch_segment_scan(p->r, s, sp, state_in ? S : nullptr, state_in ? z : nullptr, inc,
+                                1, S, z, nullptr, st);
+    if (e == hipSuccess)
+        e = launch_segment_outputs_proj(c, 1, P, omega, s, sp, inc, sp.G * E, E, out, st);
+    return launch_status(e);
+}
+
+int lin_attn_bidir_proj(const lin_attn_params* p, const void* x, const void* w_q,
+                        const void* w_k, const void* w_v, int64_t B, int64_t H, int64_t N,
+                        int64_t d_model, int64_t d, int64_t dv, const void* omega, void* out,
+                        float* S_out, float* z_out, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_params(p, d, dv, omega);
+    if (rc == LIN_ATTN_ERR_INVALID) return rc;
+    const int rs = check_sizes(B, H, N);
+    if (rs == LIN_ATTN_ERR_INVALID) return rs;
+    if (!opt_ptr_ok(S_out) || !opt_ptr_ok(z_out) || !opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
+    const bool empty = B * H == 0 || N == 0;
+    if (!empty && !ptr_ok(out)) return LIN_ATTN_ERR_INVALID;
+    const int pc = proj_checks(p, x, w_q, w_k, w_v, B, H, N, d_model, !empty);
+    if (pc == LIN_ATTN_ERR_INVALID) return pc;
+    if (rc != LIN_ATTN_OK) return rc;
+    if (rs != LIN_ATTN_OK) return rs;
+    if (pc != LIN_ATTN_OK) return pc;
+    hipStream_t st = (hipStream_t)stream;
+    if (empty) {
+        hipError_t e = hipSuccess;
+        if (S_out) e = launch_fill_zero(S_out, B * H * (int64_t)p->r * DV, st);
+        if (e == hipSuccess && z_out) e = launch_fill_zero(z_out, B * H * (int64_t)p->r, st);
+        return launch_status(e);
+    }
+    const int64_t BH = B * H;
+    if (ws_bytes < proj_ws_floats(false, p, BH, N) * sizeof(float) || !ws)
+        return LIN_ATTN_ERR_WORKSPACE;
+    const Cfg c = make_cfg(p);
+    const Shape s{BH, N};
+    const SegPlan sp = proj_plan(p, BH, N);
+    const Proj P{(const bf16_raw*)x,
+                 {(const bf16_raw*)w_q, (const bf16_raw*)w_k, (const bf16_raw*)w_v},
+                 d_model,
+                 H};
+    const int64_t E = state_elems(p->r);
+    float* inc = (float*)ws;
+    float* fin = inc + BH * sp.G * E;
+    hipError_t e = launch_segment_sums_proj(c, P, omega, s, sp, inc, st);
+    if (e == hipSuccess)
+        e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc, 0, S_out, z_out, fin, st);
+    if (e == hipSuccess) e = launch_segment_outputs_proj(c, 0, P, omega, s, sp, fin, E, 0, out, st);
+    return launch_status(e);
 }
 
 int lin_attn_decode_step(const lin_attn_params* p, const void* q, const void* k, const void* v,

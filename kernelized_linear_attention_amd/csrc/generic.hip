@@ -15,6 +15,7 @@
 #include <algorithm>
 
 #include "launch.hpp"
+#include "proj.hpp"
 #include "tiles.hpp"
 
 namespace linattn {
@@ -53,13 +54,14 @@ __global__ __launch_bounds__(NT) void k_featuremap(Cfg c, const T* __restrict__ 
 // Segment state increments: ws[bh][g] = (sum phi(k_j) v_j^T, sum phi(k_j)).
 // Thread (fb = tid/8, nb = tid%8) owns S[fb*FPT + i][nb*8 + j], i < FPT, j < 8.
 // ---------------------------------------------------------------------------
-template <typename T, int FPT>
+// PROJ: k and v are projected from the tokens x (proj.hpp) instead of read.
+template <typename T, int FPT, bool PROJ>
 __global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict__ k,
                                                      const T* __restrict__ v,
                                                      const T* __restrict__ omega, int64_t N,
                                                      int64_t G, int64_t seg_len,
                                                      const int64_t* __restrict__ tab,
-                                                     float* __restrict__ ws) {
+                                                     float* __restrict__ ws, Proj P) {
     constexpr int L = 64;
     constexpr int R = 32 * FPT;
     constexpr int OL = R + 4;
@@ -83,8 +85,12 @@ __global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict_
     }
     for (int64_t c0 = t0; c0 < t1; c0 += L) {
         const int rows = (int)min<int64_t>(L, t1 - c0);
-        load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, u_s);
-        load_rows<T, L>(v + (bh * N + c0) * DV, rows, 1.f, v_s);
+        if (PROJ) {
+            project_chunk<L>(P, bh, N, c0, rows, PROJ_K, u_s, c.scale, PROJ_V, v_s, 1.f);
+        } else {
+            load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, u_s);
+            load_rows<T, L>(v + (bh * N + c0) * DV, rows, 1.f, v_s);
+        }
         __syncthreads();
         row_norms<L>(u_s, nrm_s);
         __syncthreads();
@@ -324,7 +330,8 @@ __global__ __launch_bounds__(NT) void k_segment_scan_varlen(int r, int64_t H, in
 // Segment outputs.  CAUSAL: chunked recurrence from the carried-in state;
 // otherwise: readout of every token against the full summary.
 // ---------------------------------------------------------------------------
-template <typename T, int FPT, bool CAUSAL>
+// PROJ: q, k and v are projected from the tokens x (proj.hpp) instead of read.
+template <typename T, int FPT, bool CAUSAL, bool PROJ>
 __global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restrict__ q,
                                                         const T* __restrict__ k,
                                                         const T* __restrict__ v,
@@ -333,7 +340,7 @@ __global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restri
                                                         const int64_t* __restrict__ tab, int64_t sub,
                                                         const float* __restrict__ state,
                                                         int64_t st_bh, int64_t st_g,
-                                                        T* __restrict__ out) {
+                                                        T* __restrict__ out, Proj P) {
     constexpr int L = 32;
     constexpr int R = 32 * FPT;
     constexpr int OL = R + 4;
@@ -363,14 +370,21 @@ __global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restri
     for (int64_t c0 = t0; c0 < t1; c0 += L) {
         const int rows = (int)min<int64_t>(L, t1 - c0);
         if (CAUSAL) {
-            load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, u_s);
-            load_rows<T, L>(v + (bh * N + c0) * DV, rows, 1.f, v_s);
+            if (PROJ) {
+                project_chunk<L>(P, bh, N, c0, rows, PROJ_K, u_s, c.scale, PROJ_V, v_s, 1.f);
+            } else {
+                load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, u_s);
+                load_rows<T, L>(v + (bh * N + c0) * DV, rows, 1.f, v_s);
+            }
             __syncthreads();
             row_norms<L>(u_s, nrm_s);
             __syncthreads();
             phi_tile<T, L>(c, u_s, nrm_s, omega, rows, pk_s, OL, rs_s);
         }
-        load_rows<T, L>(q + (bh * N + c0) * D, rows, c.scale, u_s);
+        if (PROJ)
+            project_chunk<L>(P, bh, N, c0, rows, PROJ_Q, u_s, c.scale, -1, nullptr, 0.f);
+        else
+            load_rows<T, L>(q + (bh * N + c0) * D, rows, c.scale, u_s);
         __syncthreads();
         row_norms<L>(u_s, nrm_s);
         __syncthreads();
@@ -464,62 +478,60 @@ hipError_t featuremap_t(const Cfg& c, const void* x, const void* omega, Shape s,
     return hipGetLastError();
 }
 
-template <typename T, int FPT>
+template <typename T, int FPT, bool PROJ>
 void sums_fpt(const Cfg& c, const void* k, const void* v, const void* omega, Shape s, SegPlan sp,
-              float* ws, hipStream_t st) {
-    hipLaunchKernelGGL((k_segment_sums<T, FPT>), dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0, st,
-                       c, (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G, sp.seg_len, sp.tab,
-                       ws);
+              float* ws, const Proj& P, hipStream_t st) {
+    hipLaunchKernelGGL((k_segment_sums<T, FPT, PROJ>), dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0,
+                       st, c, (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G, sp.seg_len,
+                       sp.tab, ws, P);
 }
 
-template <typename T>
+template <typename T, bool PROJ>
 hipError_t segment_sums_t(const Cfg& c, const void* k, const void* v, const void* omega, Shape s,
-                          SegPlan sp, float* ws, hipStream_t st) {
+                          SegPlan sp, float* ws, const Proj& P, hipStream_t st) {
     switch (c.r / 32) {
-    case 1: sums_fpt<T, 1>(c, k, v, omega, s, sp, ws, st); break;
-    case 2: sums_fpt<T, 2>(c, k, v, omega, s, sp, ws, st); break;
-    case 3: sums_fpt<T, 3>(c, k, v, omega, s, sp, ws, st); break;
-    case 4: sums_fpt<T, 4>(c, k, v, omega, s, sp, ws, st); break;
-    case 5: sums_fpt<T, 5>(c, k, v, omega, s, sp, ws, st); break;
-    case 6: sums_fpt<T, 6>(c, k, v, omega, s, sp, ws, st); break;
-    case 7: sums_fpt<T, 7>(c, k, v, omega, s, sp, ws, st); break;
-    case 8: sums_fpt<T, 8>(c, k, v, omega, s, sp, ws, st); break;
+    case 1: sums_fpt<T, 1, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
+    case 2: sums_fpt<T, 2, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
+    case 3: sums_fpt<T, 3, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
+    case 4: sums_fpt<T, 4, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
+    case 5: sums_fpt<T, 5, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
+    case 6: sums_fpt<T, 6, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
+    case 7: sums_fpt<T, 7, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
+    case 8: sums_fpt<T, 8, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <typename T, int FPT>
+template <typename T, int FPT, bool PROJ>
 void outputs_fpt(const Cfg& c, int causal, const void* q, const void* k, const void* v,
                  const void* omega, Shape s, SegPlan sp, const float* state, int64_t sbh,
-                 int64_t sg, void* out, hipStream_t st) {
+                 int64_t sg, void* out, const Proj& P, hipStream_t st) {
     const dim3 grid((unsigned)(sp.G * s.BH)), block(NT);
     if (causal)
-        hipLaunchKernelGGL((k_segment_outputs<T, FPT, true>), grid, block, 0, st, c, (const T*)q,
-                           (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G, sp.seg_len,
-                           sp.tab, sp.sub, state, sbh, sg, (T*)out);
-    else
-        hipLaunchKernelGGL((k_segment_outputs<T, FPT, false>), grid, block, 0, st, c,
+        hipLaunchKernelGGL((k_segment_outputs<T, FPT, true, PROJ>), grid, block, 0, st, c,
                            (const T*)q, (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G,
-                           sp.seg_len, sp.tab, sp.sub, state, sbh, sg, (T*)out);
+                           sp.seg_len, sp.tab, sp.sub, state, sbh, sg, (T*)out, P);
+    else
+        hipLaunchKernelGGL((k_segment_outputs<T, FPT, false, PROJ>), grid, block, 0, st, c,
+                           (const T*)q, (const T*)k, (const T*)v, (const T*)omega, s.N, sp.G,
+                           sp.seg_len, sp.tab, sp.sub, state, sbh, sg, (T*)out, P);
 }
 
-template <typename T>
+template <typename T, bool PROJ>
 hipError_t segment_outputs_t(const Cfg& c, int causal, const void* q, const void* k,
                              const void* v, const void* omega, Shape s, SegPlan sp,
                              const float* state, int64_t sbh, int64_t sg, void* out,
-                             hipStream_t st) {
+                             const Proj& P, hipStream_t st) {
+#define LINATTN_OUTPUTS(F)                                                                        \
+    case F: outputs_fpt<T, F, PROJ>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, P, st); \
+        break;
     switch (c.r / 32) {
-    case 1: outputs_fpt<T, 1>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
-    case 2: outputs_fpt<T, 2>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
-    case 3: outputs_fpt<T, 3>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
-    case 4: outputs_fpt<T, 4>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
-    case 5: outputs_fpt<T, 5>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
-    case 6: outputs_fpt<T, 6>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
-    case 7: outputs_fpt<T, 7>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
-    case 8: outputs_fpt<T, 8>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st); break;
+        LINATTN_OUTPUTS(1) LINATTN_OUTPUTS(2) LINATTN_OUTPUTS(3) LINATTN_OUTPUTS(4)
+        LINATTN_OUTPUTS(5) LINATTN_OUTPUTS(6) LINATTN_OUTPUTS(7) LINATTN_OUTPUTS(8)
     default: return hipErrorInvalidValue;
     }
+#undef LINATTN_OUTPUTS
     return hipGetLastError();
 }
 
@@ -545,8 +557,14 @@ hipError_t launch_featuremap(const Cfg& c, int dtype, const void* x, const void*
 
 hipError_t launch_segment_sums(const Cfg& c, int dtype, const void* k, const void* v,
                                const void* omega, Shape s, SegPlan sp, float* ws, hipStream_t st) {
-    return dtype == 0 ? segment_sums_t<float>(c, k, v, omega, s, sp, ws, st)
-                      : segment_sums_t<bf16_raw>(c, k, v, omega, s, sp, ws, st);
+    const Proj none{};
+    return dtype == 0 ? segment_sums_t<float, false>(c, k, v, omega, s, sp, ws, none, st)
+                      : segment_sums_t<bf16_raw, false>(c, k, v, omega, s, sp, ws, none, st);
+}
+
+hipError_t launch_segment_sums_proj(const Cfg& c, const Proj& P, const void* omega, Shape s,
+                                    SegPlan sp, float* ws, hipStream_t st) {
+    return segment_sums_t<bf16_raw, true>(c, nullptr, nullptr, omega, s, sp, ws, P, st);
 }
 
 hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, const float* z0,
@@ -590,10 +608,18 @@ hipError_t launch_segment_outputs(const Cfg& c, int dtype, int causal, const voi
                                   const void* k, const void* v, const void* omega, Shape s,
                                   SegPlan sp, const float* state, int64_t sbh, int64_t sg,
                                   void* out, hipStream_t st) {
-    return dtype == 0
-               ? segment_outputs_t<float>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st)
-               : segment_outputs_t<bf16_raw>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out,
-                                             st);
+    const Proj none{};
+    return dtype == 0 ? segment_outputs_t<float, false>(c, causal, q, k, v, omega, s, sp, state,
+                                                        sbh, sg, out, none, st)
+                      : segment_outputs_t<bf16_raw, false>(c, causal, q, k, v, omega, s, sp,
+                                                           state, sbh, sg, out, none, st);
+}
+
+hipError_t launch_segment_outputs_proj(const Cfg& c, int causal, const Proj& P, const void* omega,
+                                       Shape s, SegPlan sp, const float* state, int64_t sbh,
+                                       int64_t sg, void* out, hipStream_t st) {
+    return segment_outputs_t<bf16_raw, true>(c, causal, nullptr, nullptr, nullptr, omega, s, sp,
+                                             state, sbh, sg, out, P, st);
 }
 
 } // namespace linattn

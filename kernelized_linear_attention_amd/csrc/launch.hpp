@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "proj.hpp"
 
 namespace linattn {
 
@@ -99,6 +100,14 @@ hipError_t launch_segment_outputs(const Cfg& c, int dtype, int causal, const voi
                                   const void* k, const void* v, const void* omega, Shape s,
                                   SegPlan sp, const float* state, int64_t state_bh_stride,
                                   int64_t state_g_stride, void* out, hipStream_t st);
+
+// The same two kernels with q, k, v projected from the tokens P.x through
+// P.w (proj.hpp) inside their loads; bfloat16 only.
+hipError_t launch_segment_sums_proj(const Cfg& c, const Proj& P, const void* omega, Shape s,
+                                    SegPlan sp, float* ws, hipStream_t st);
+hipError_t launch_segment_outputs_proj(const Cfg& c, int causal, const Proj& P, const void* omega,
+                                       Shape s, SegPlan sp, const float* state, int64_t sbh,
+                                       int64_t sg, void* out, hipStream_t st);
 
 // Segment table of a packed batch: sequence i covers tokens
 // [cu_seqlens[i], cu_seqlens[i+1]) of every head and is cut into

@@ -24,6 +24,7 @@ from __future__ import annotations
 import numpy as np
 
 T_Q, T_K, T_V, T_OMEGA, T_PREFIX, T_LENGTHS, T_DOUT = 0, 1, 2, 3, 4, 5, 6
+T_X, T_WQ, T_WK, T_WV = 7, 8, 9, 10
 
 
 def rng(workload: int, tensor: int, rep: int = 0) -> np.random.Generator:
@@ -91,3 +92,11 @@ def packed_lengths(num_seqs: int, total: int, workload: int, rep: int = 0,
     lens = np.floor(w / w.sum() * total).astype(np.int64)
     lens[-1] += total - lens.sum()
     return lens
+
+
+def projection_weights(heads: int, d: int, d_model: int, workload: int, rep: int = 0):
+    """W_q, W_k, W_v [heads * d, d_model]: i.i.d. N(0, 1/d_model) float32, so
+    that W x has unit-variance entries for x ~ N(0, I)."""
+    std = np.float32(1.0 / np.sqrt(d_model))
+    return tuple(normal((heads * d, d_model), workload, t, rep) * std
+                 for t in (T_WQ, T_WK, T_WV))

@@ -59,6 +59,8 @@ def test_constants_match_header():
     assert d["LIN_ATTN_OP_CAUSAL_VARLEN"] == binding.OP_CAUSAL_VARLEN
     assert d["LIN_ATTN_OP_BIDIR_BACKWARD"] == binding.OP_BIDIR_BACKWARD
     assert d["LIN_ATTN_OP_CAUSAL_BACKWARD"] == binding.OP_CAUSAL_BACKWARD
+    assert d["LIN_ATTN_OP_CAUSAL_PROJ"] == binding.OP_CAUSAL_PROJ
+    assert d["LIN_ATTN_OP_BIDIR_PROJ"] == binding.OP_BIDIR_PROJ
     assert (d["LIN_ATTN_OK"], d["LIN_ATTN_ERR_INVALID"], d["LIN_ATTN_ERR_UNSUPPORTED"],
             d["LIN_ATTN_ERR_WORKSPACE"], d["LIN_ATTN_ERR_HIP"]) == (0, -1, -2, -3, -4)
 
@@ -299,3 +301,51 @@ def test_backward_workspace_formula():
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 65536, 64, 64) == \
         inc + 8 * 65536 * 2 * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 0, 64, 64) == 0
+
+
+def causal_proj(p, B=1, H=2, N=100, dm=512, d=64, dv=64, x=FAKE, w=FAKE, omega=FAKE, state_in=0,
+                out=FAKE, ws=FAKE, ws_bytes=1 << 40, S=FAKE, z=FAKE):
+    return lib.lin_attn_causal_proj(ctypes.byref(p), x, w, w, w, B, H, N, dm, d, dv, omega, S, z,
+                                    state_in, out, ws, ws_bytes, None)
+
+
+def bidir_proj(p, B=1, H=2, N=100, dm=512, d=64, dv=64, x=FAKE, w=FAKE, omega=FAKE, out=FAKE,
+               ws=FAKE, ws_bytes=1 << 40):
+    return lib.lin_attn_bidir_proj(ctypes.byref(p), x, w, w, w, B, H, N, dm, d, dv, omega, out,
+                                   None, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("call", [causal_proj, bidir_proj])
+def test_projected_call_arguments(call):
+    p = params()
+    assert call(p, dm=0) == INVALID
+    assert call(p, dm=-16) == INVALID
+    assert call(p, x=None) == INVALID
+    assert call(p, x=FAKE + 8) == INVALID
+    assert call(p, w=None) == INVALID
+    assert call(p, out=None) == INVALID
+    assert call(p, omega=None) == INVALID
+    assert call(p, N=-1) == INVALID
+    assert call(p, dm=520) == UNSUPPORTED               # not a multiple of 16
+    assert call(params(dtype=0)) == UNSUPPORTED          # bfloat16 tokens and weights only
+    assert call(p, d=32) == UNSUPPORTED
+    op = binding.OP_CAUSAL_PROJ if call is causal_proj else binding.OP_BIDIR_PROJ
+    need = binding.lin_attn_workspace_bytes(op, p, 1, 2, 100, 64, 64)
+    assert need > 0
+    assert call(p, ws_bytes=need - 4) == WORKSPACE
+    assert call(p, B=0) == OK
+    if call is causal_proj:
+        assert call(p, state_in=3) == INVALID
+        assert call(p, S=None) == INVALID
+
+
+def test_projected_workspace_formula():
+    """The vector kernels' plan (64 segments per head at H = 8, N = 65536),
+    one (S | z) block per segment, plus the summary per head when
+    bidirectional."""
+    p = params()
+    E = 256 * 64 + 256
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_PROJ, p, 1, 8, 65536, 64, 64) == \
+        8 * 64 * E * 4
+    assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR_PROJ, p, 1, 8, 65536, 64, 64) == \
+        (8 * 64 + 8) * E * 4

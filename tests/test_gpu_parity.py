@@ -534,3 +534,91 @@ def test_workload_favor_causal_backward(gpu_lib):
     do = dev(inputs.normal((w.B, w.H, w.N, w.dv), w.wid, inputs.T_DOUT), DT[w.dtype])
     got, ref = _bwd(gpu_lib, True, "causal", c, do, w.kind, **_wl_kw(w))
     _assert_grads(got, ref, 2e-2, "causal prefill backward")
+
+
+# ---------------------------------------------------------------- fused input projection
+# (kind, r, nu, sum_norm, scale, norm): bfloat16 tokens and weights only
+PROJ_MAPS = [
+    ("favor", 256, 1, False, 64 ** -0.25, "attn"),
+    ("favor", 96, 1, False, 64 ** -0.25, "none"),
+    ("elu1", 64, 1, True, 1.0, "attn"),
+    ("dpfp", 256, 2, True, 1.0, "none"),
+    ("identity", 64, 1, False, 0.5, "none"),
+]
+PROJ_IDS = [f"{k}-r{r}{'-sn' if sn else ''}-{nm}" for k, r, _, sn, _, nm in PROJ_MAPS]
+
+
+class ProjCase:
+    """Seeded tokens x [B, N, dm] and weights W_q, W_k, W_v [H*64, dm] on the
+    device (bf16), their exact values for the oracle, and omega."""
+
+    def __init__(self, wid, B, H, N, dm, kind, r, rep=0):
+        self.H = H
+        self.x = dev(inputs.normal((B, N, dm), wid, inputs.T_X, rep), torch.bfloat16)
+        self.w = [dev(w, torch.bfloat16) for w in inputs.projection_weights(H, 64, dm, wid, rep)]
+        self.xh = host(self.x)
+        self.wh = [host(w) for w in self.w]
+        self.omega = self.omega_h = None
+        if kind == "favor":
+            self.omega = dev(inputs.orf_omega(r, 64, wid, rep), torch.bfloat16)
+            self.omega_h = host(self.omega)
+
+
+@pytest.mark.parametrize("kind,r,nu,sum_norm,scale,norm", PROJ_MAPS, ids=PROJ_IDS)
+@pytest.mark.parametrize("B,H,N,dm", [(2, 2, 300, 128), (1, 8, 200, 512)])
+def test_causal_proj(gpu_lib, kind, r, nu, sum_norm, scale, norm, B, H, N, dm):
+    c = ProjCase(130, B, H, N, dm, kind, r)
+    kw = dict(nu=nu, sum_norm=sum_norm, scale=scale, norm=norm)
+    out, S, z = gpu_lib.lin_attn_causal_proj(c.x, *c.w, H, kind, omega=c.omega, **kw)
+    ro, rS, rz = oracle.causal_proj(c.xh, *c.wh, H, kind, omega=c.omega_h, **kw)
+    assert_parity(out, ro, 2e-2, "causal_proj out")
+    assert_parity(S, rS, 2e-2, "causal_proj S")
+    assert_parity(z, rz, 2e-2, "causal_proj z")
+
+
+@pytest.mark.parametrize("kind,r,nu,sum_norm,scale,norm", PROJ_MAPS, ids=PROJ_IDS)
+def test_bidir_proj(gpu_lib, kind, r, nu, sum_norm, scale, norm):
+    B, H, N, dm = 2, 2, 300, 128
+    c = ProjCase(131, B, H, N, dm, kind, r)
+    kw = dict(nu=nu, sum_norm=sum_norm, scale=scale, norm=norm)
+    r_ = oracle.feature_dim(kind, 64, nu, c.omega_h)
+    S = torch.empty((B, H, r_, 64), device="cuda")
+    z = torch.empty((B, H, r_), device="cuda")
+    out = gpu_lib.lin_attn_bidir_proj(c.x, *c.w, H, kind, omega=c.omega, S_out=S, z_out=z, **kw)
+    ro, rS, rz = oracle.bidir_proj(c.xh, *c.wh, H, kind, omega=c.omega_h, **kw)
+    assert_parity(out, ro, 2e-2, "bidir_proj out")
+    assert_parity(S, rS, 2e-2, "bidir_proj S")
+    assert_parity(z, rz, 2e-2, "bidir_proj z")
+
+
+def test_causal_proj_carried_state_and_short_inputs(gpu_lib):
+    """A split call carrying (S, z) equals one call; N in {1, 31, 33}."""
+    H, dm = 2, 64
+    c = ProjCase(132, 1, H, 400, dm, "favor", 128)
+    kw = dict(omega=c.omega, scale=64 ** -0.25)
+    out, S, z = gpu_lib.lin_attn_causal_proj(c.x, *c.w, H, "favor", **kw)
+    m = 157
+    o1, S1, z1 = gpu_lib.lin_attn_causal_proj(c.x[:, :m].contiguous(), *c.w, H, "favor", **kw)
+    o2, _, _ = gpu_lib.lin_attn_causal_proj(c.x[:, m:].contiguous(), *c.w, H, "favor", S=S1,
+                                            z=z1, state_in=True, **kw)
+    assert_parity(torch.cat([o1, o2], dim=2), host(out), 1e-2, "split out")
+    assert_parity(S1, host(S), 1e-2, "split S")  # S1 was updated in place by the second call
+    for n in (1, 31, 33):
+        o, Sn, _ = gpu_lib.lin_attn_causal_proj(c.x[:, :n].contiguous(), *c.w, H, "favor", **kw)
+        ro, rS, _ = oracle.causal_proj(c.xh[:, :n], *c.wh, H, "favor", omega=c.omega_h,
+                                       scale=64 ** -0.25)
+        assert_parity(o, ro, 2e-2, f"N={n} out")
+        assert_parity(Sn, rS, 2e-2, f"N={n} S")
+
+
+def test_workload_favor_causal_prefill_from_tokens(gpu_lib):
+    """The causal prefill workload (B=1, H=8, N=65536, r=256) from tokens of
+    the pages' model width d_model = 512."""
+    w = workloads.FAVOR_CAUSAL
+    c = ProjCase(w.wid, w.B, w.H, w.N, 512, w.kind, w.r)
+    kw = _wl_kw(w)
+    out, S, z = gpu_lib.lin_attn_causal_proj(c.x, *c.w, w.H, w.kind, omega=c.omega, **kw)
+    ro, rS, rz = oracle.causal_proj(c.xh, *c.wh, w.H, w.kind, omega=c.omega_h, **kw)
+    assert_parity(out, ro, 2e-2, "prefill from tokens out")
+    assert_parity(S, rS, 2e-2, "prefill from tokens S")
+    assert_parity(z, rz, 2e-2, "prefill from tokens z")

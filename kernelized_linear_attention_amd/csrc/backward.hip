@@ -42,25 +42,35 @@ __device__ void load_state(const float* __restrict__ src, float* M_s, float* m_s
     for (int f = threadIdx.x; f < R; f += NT) m_s[f] = src[(long)R * DV + f];
 }
 
+// First of the 2*FPT contiguous features a thread owns in the state updates.
+template <int FPT>
+__device__ __forceinline__ int feat0() { return (threadIdx.x / 16) * 2 * FPT; }
+
 // Outer-product sums over the rows of a chunk, for the items of this thread:
-// feature f = tid/16 + 16*it, value columns n4 = 4*(tid % 16) .. n4+3:
+// features f = feat0() + it, value columns n4 = 4*(tid % 16) .. n4+3:
 //   acc[it][j] += sum_t x[t][f] y[t][n4+j],   macc[it] += sum_t x[t][f] s[t]
 // (s == NULL: s[t] = 1).  x has row stride ol, y row stride DV.
 template <int FPT>
 __device__ void outer_accum(const float* x, int ol, const float* y, const float* s, int rows,
                             float (&acc)[2 * FPT][4], float (&macc)[2 * FPT]) {
-    const int f0 = threadIdx.x / 16, n4 = (threadIdx.x % 16) * 4;
+    const int f0 = feat0<FPT>(), n4 = (threadIdx.x % 16) * 4;
     for (int t = 0; t < rows; ++t) {
         const float4 yv = *reinterpret_cast<const float4*>(y + t * DV + n4);
         const float st = s ? s[t] : 1.f;
+        float xf[2 * FPT];
+#pragma unroll
+        for (int it = 0; it < 2 * FPT; it += 2) {
+            const float2 x2 = *reinterpret_cast<const float2*>(x + t * ol + f0 + it);
+            xf[it] = x2.x;
+            xf[it + 1] = x2.y;
+        }
 #pragma unroll
         for (int it = 0; it < 2 * FPT; ++it) {
-            const float xf = x[t * ol + f0 + 16 * it];
-            acc[it][0] = fmaf(xf, yv.x, acc[it][0]);
-            acc[it][1] = fmaf(xf, yv.y, acc[it][1]);
-            acc[it][2] = fmaf(xf, yv.z, acc[it][2]);
-            acc[it][3] = fmaf(xf, yv.w, acc[it][3]);
-            macc[it] = fmaf(xf, st, macc[it]);
+            acc[it][0] = fmaf(xf[it], yv.x, acc[it][0]);
+            acc[it][1] = fmaf(xf[it], yv.y, acc[it][1]);
+            acc[it][2] = fmaf(xf[it], yv.z, acc[it][2]);
+            acc[it][3] = fmaf(xf[it], yv.w, acc[it][3]);
+            macc[it] = fmaf(xf[it], st, macc[it]);
         }
     }
 }
@@ -70,11 +80,11 @@ __device__ void outer_accum(const float* x, int ol, const float* y, const float*
 template <int FPT>
 __device__ void state_update(float* M_s, float* m_s, const float* x, int ol, const float* y,
                              const float* s, int rows) {
-    const int f0 = threadIdx.x / 16, n4 = (threadIdx.x % 16) * 4;
+    const int f0 = feat0<FPT>(), n4 = (threadIdx.x % 16) * 4;
     float acc[2 * FPT][4], macc[2 * FPT];
 #pragma unroll
     for (int it = 0; it < 2 * FPT; ++it) {
-        const float4 a = *reinterpret_cast<const float4*>(M_s + (f0 + 16 * it) * SL + n4);
+        const float4 a = *reinterpret_cast<const float4*>(M_s + (f0 + it) * SL + n4);
         acc[it][0] = a.x;
         acc[it][1] = a.y;
         acc[it][2] = a.z;
@@ -84,9 +94,9 @@ __device__ void state_update(float* M_s, float* m_s, const float* x, int ol, con
     outer_accum<FPT>(x, ol, y, s, rows, acc, macc);
 #pragma unroll
     for (int it = 0; it < 2 * FPT; ++it) {
-        *reinterpret_cast<float4*>(M_s + (f0 + 16 * it) * SL + n4) =
+        *reinterpret_cast<float4*>(M_s + (f0 + it) * SL + n4) =
             make_float4(acc[it][0], acc[it][1], acc[it][2], acc[it][3]);
-        if (n4 == 0) m_s[f0 + 16 * it] += macc[it];
+        if (n4 == 0) m_s[f0 + it] += macc[it];
     }
 }
 
@@ -139,10 +149,12 @@ __device__ void masked_products(const float* a, const float* b, int ld, int n, c
             const float* x = a + t * ld;
             const float* y = b + j * ld;
             for (int e = 0; e < n; e += 4) {
-                acc = fmaf(x[e], y[e], acc);
-                acc = fmaf(x[e + 1], y[e + 1], acc);
-                acc = fmaf(x[e + 2], y[e + 2], acc);
-                acc = fmaf(x[e + 3], y[e + 3], acc);
+                const float4 a4 = *reinterpret_cast<const float4*>(x + e);
+                const float4 b4 = *reinterpret_cast<const float4*>(y + e);
+                acc = fmaf(a4.x, b4.x, acc);
+                acc = fmaf(a4.y, b4.y, acc);
+                acc = fmaf(a4.z, b4.z, acc);
+                acc = fmaf(a4.w, b4.w, acc);
             }
             if (add) acc += add[j];
         }
@@ -189,13 +201,19 @@ __device__ void phi_backward_tile(const Cfg& c, const float* u, const float* phi
         float a[L / 4], wsum[L / 4];
 #pragma unroll
         for (int m = 0; m < L / 4; ++m) a[m] = wsum[m] = 0.f;
-        for (int f = 0; f < R; ++f) {
-            const float om = Elem<T>::load(omega, (long)f * D + i);
+        // omega column i, 4 rows at a time; the dp rows as 16-byte reads
+        for (int f = 0; f < R; f += 4) {
+            float om[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) om[j] = Elem<T>::load(omega, (long)(f + j) * D + i);
 #pragma unroll
             for (int m = 0; m < L / 4; ++m) {
-                const float wv = dp[(t0 + m) * ol + f];
-                a[m] = fmaf(wv, om, a[m]);
-                wsum[m] += wv;
+                const float4 wv = *reinterpret_cast<const float4*>(dp + (t0 + m) * ol + f);
+                a[m] = fmaf(wv.x, om[0], a[m]);
+                a[m] = fmaf(wv.y, om[1], a[m]);
+                a[m] = fmaf(wv.z, om[2], a[m]);
+                a[m] = fmaf(wv.w, om[3], a[m]);
+                wsum[m] += (wv.x + wv.y) + (wv.z + wv.w);
             }
         }
 #pragma unroll
@@ -249,7 +267,7 @@ __global__ __launch_bounds__(NT) void k_bwd_query(Cfg c, const T* __restrict__ q
     constexpr int OL = R + 4;
     constexpr int LC = CAUSAL ? L : 1;
     __shared__ __align__(16) float S_s[R * SL];
-    __shared__ float z_s[R];
+    __shared__ __align__(16) float z_s[R];
     __shared__ __align__(16) float u_s[L * D];
     __shared__ __align__(16) float pq_s[L * OL];
     __shared__ __align__(16) float pk_s[LC * OL];
@@ -297,14 +315,22 @@ __global__ __launch_bounds__(NT) void k_bwd_query(Cfg c, const T* __restrict__ q
             float num[4] = {0.f, 0.f, 0.f, 0.f};
             float den = 0.f;
             const float* x = pq_s + rt * OL;
-            for (int f = 0; f < R; ++f) {
-                const float pf = x[f];
-                den = fmaf(pf, z_s[f], den);
-                const float4 sv = *reinterpret_cast<const float4*>(S_s + f * SL + cb);
-                num[0] = fmaf(pf, sv.x, num[0]);
-                num[1] = fmaf(pf, sv.y, num[1]);
-                num[2] = fmaf(pf, sv.z, num[2]);
-                num[3] = fmaf(pf, sv.w, num[3]);
+            for (int f = 0; f < R; f += 4) {
+                const float4 p4 = *reinterpret_cast<const float4*>(x + f);
+                const float4 z4 = *reinterpret_cast<const float4*>(z_s + f);
+                const float pf[4] = {p4.x, p4.y, p4.z, p4.w};
+                den = fmaf(p4.x, z4.x, den);
+                den = fmaf(p4.y, z4.y, den);
+                den = fmaf(p4.z, z4.z, den);
+                den = fmaf(p4.w, z4.w, den);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 sv = *reinterpret_cast<const float4*>(S_s + (f + j) * SL + cb);
+                    num[0] = fmaf(pf[j], sv.x, num[0]);
+                    num[1] = fmaf(pf[j], sv.y, num[1]);
+                    num[2] = fmaf(pf[j], sv.z, num[2]);
+                    num[3] = fmaf(pf[j], sv.w, num[3]);
+                }
             }
             if (CAUSAL) {
                 for (int j = 0; j <= rt; ++j) {
@@ -357,10 +383,10 @@ __global__ __launch_bounds__(NT) void k_bwd_query(Cfg c, const T* __restrict__ q
     }
 
     float* dst = inc + (bh * G + g) * state_elems(R);
-    const int f0 = tid / 16;
+    const int f0 = feat0<FPT>();
 #pragma unroll
     for (int it = 0; it < 2 * FPT; ++it) {
-        const int f = f0 + 16 * it;
+        const int f = f0 + it;
         *reinterpret_cast<float4*>(dst + (long)f * DV + cb) =
             make_float4(acc[it][0], acc[it][1], acc[it][2], acc[it][3]);
         if (cb == 0) dst[(long)R * DV + f] = macc[it];
@@ -383,7 +409,7 @@ __global__ __launch_bounds__(NT) void k_bwd_key(Cfg c, const T* __restrict__ q,
     constexpr int OL = R + 4;
     constexpr int LC = CAUSAL ? L : 1;
     __shared__ __align__(16) float G_s[R * SL];
-    __shared__ float g_s[R];
+    __shared__ __align__(16) float g_s[R];
     __shared__ __align__(16) float uk_s[L * D];
     __shared__ __align__(16) float uq_s[LC * D];
     __shared__ __align__(16) float pk_s[L * OL];
@@ -441,13 +467,17 @@ __global__ __launch_bounds__(NT) void k_bwd_key(Cfg c, const T* __restrict__ q,
             // dv_j = G^T phi(k_j) + sum_{i >= j} b[j][i] dnum_i
             float acc[4] = {0.f, 0.f, 0.f, 0.f};
             const float* x = pk_s + rt * OL;
-            for (int f = 0; f < R; ++f) {
-                const float pf = x[f];
-                const float4 gv = *reinterpret_cast<const float4*>(G_s + f * SL + cb);
-                acc[0] = fmaf(pf, gv.x, acc[0]);
-                acc[1] = fmaf(pf, gv.y, acc[1]);
-                acc[2] = fmaf(pf, gv.z, acc[2]);
-                acc[3] = fmaf(pf, gv.w, acc[3]);
+            for (int f = 0; f < R; f += 4) {
+                const float4 p4 = *reinterpret_cast<const float4*>(x + f);
+                const float pf[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 gv = *reinterpret_cast<const float4*>(G_s + (f + j) * SL + cb);
+                    acc[0] = fmaf(pf[j], gv.x, acc[0]);
+                    acc[1] = fmaf(pf[j], gv.y, acc[1]);
+                    acc[2] = fmaf(pf[j], gv.z, acc[2]);
+                    acc[3] = fmaf(pf[j], gv.w, acc[3]);
+                }
             }
             if (CAUSAL) {
                 for (int i = rt; i < L; ++i) {

@@ -265,6 +265,24 @@ int lin_attn_bidir_proj(const lin_attn_params* p, const void* x, const void* w_q
                         float* S_out, float* z_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The q/k/v input projection alone ([KZ] sec. 1.2 step 1), written in the
+ * head-major layout the other calls read: for every token x of x
+ * [B, N, d_model] (bfloat16),
+ *   q[b, h, t, :] = W_q[h*d : h*d + d, :] x[b, t, :]   (likewise k with w_k, v with w_v),
+ * one matrix-core GEMM with float32 accumulation, results rounded to
+ * bfloat16 (nearest-even).  w_q, w_k, w_v [H * d, d_model] bfloat16; q, k, v
+ * [B, H, N, d] bfloat16, overwritten.  Followed by lin_attn_causal_chunked or
+ * lin_attn_bidir this is the unfused route from tokens: q, k, v make one
+ * round trip through memory, in the layout the attention kernels read, with
+ * no transpose between.  d must be 64 and d_model a multiple of 16 (at most
+ * 65536), else -2; -1 for a null or misaligned pointer or a negative size.
+ * No workspace.
+ */
+int lin_attn_qkv_project(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                         int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t d, void* q,
+                         void* k, void* v, void* stream);
+
+/*
  * Backward pass: the gradients dq, dk, dv of a loss L given dout = dL/dout
  * for the outputs of lin_attn_bidir (lin_attn_bidir_backward) or of
  * lin_attn_causal_chunked from zero state (lin_attn_causal_backward), same

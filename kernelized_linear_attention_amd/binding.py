@@ -38,6 +38,7 @@ ABI_VERSION = 1
 EXPORTS = ("lin_attn_featuremap", "lin_attn_bidir", "lin_attn_causal_chunked",
            "lin_attn_causal_varlen", "lin_attn_orf_omega", "lin_attn_bidir_backward",
            "lin_attn_causal_backward", "lin_attn_causal_proj", "lin_attn_bidir_proj",
+           "lin_attn_qkv_project",
            "lin_attn_decode_step", "lin_attn_workspace_bytes", "lin_attn_strerror",
            "lin_attn_abi_version")
 
@@ -76,6 +77,9 @@ _lib.lin_attn_causal_proj.restype = ctypes.c_int
 _lib.lin_attn_bidir_proj.argtypes = [_PP, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P,
                                      _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.lin_attn_bidir_proj.restype = ctypes.c_int
+_lib.lin_attn_qkv_project.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
+                                      _P]
+_lib.lin_attn_qkv_project.restype = ctypes.c_int
 _lib.lin_attn_decode_step.argtypes = [_PP, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.lin_attn_decode_step.restype = ctypes.c_int
 _lib.lin_attn_workspace_bytes.argtypes = [_I32, _PP, _I64, _I64, _I64, _I64, _I64, _I32]
@@ -380,6 +384,26 @@ def lin_attn_bidir_proj(x, w_q, w_k, w_v, heads, kind, *, omega=None, nu=1, sum_
                                   _ptr(ws), ws_bytes, _stream(x.device, stream))
     _check("lin_attn_bidir_proj", rc)
     return out
+
+
+def lin_attn_qkv_project(x, w_q, w_k, w_v, heads, *, q=None, k=None, v=None, stream=None):
+    """q, k, v [B, heads, N, 64] (bf16, head-major) projected from tokens
+    x [B, N, d_model] by w_* [heads * 64, d_model]."""
+    _dev_tensor("x", x, torch.bfloat16)
+    for n, t in (("w_q", w_q), ("w_k", w_k), ("w_v", w_v)):
+        _dev_tensor(n, t, torch.bfloat16)
+    B, N, dm = x.shape
+    d = w_q.shape[0] // heads
+    outs = []
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if t is None:
+            t = torch.empty((B, heads, N, d), dtype=torch.bfloat16, device=x.device)
+        outs.append(_dev_tensor(n, t, torch.bfloat16))
+    rc = _lib.lin_attn_qkv_project(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), B, N, dm, heads, d,
+                                   _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                                   _stream(x.device, stream))
+    _check("lin_attn_qkv_project", rc)
+    return tuple(outs)
 
 
 def _backward(name, op, q, k, v, dout, kind, omega, nu, sum_norm, norm, scale, eps, n_seg,

@@ -548,6 +548,24 @@ int lin_attn_bidir_proj(const lin_attn_params* p, const void* x, const void* w_q
     return launch_status(e);
 }
 
+int lin_attn_qkv_project(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                         int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t d, void* q,
+                         void* k, void* v, void* stream) {
+    if (B < 0 || N < 0 || H < 0 || d <= 0 || d_model <= 0) return LIN_ATTN_ERR_INVALID;
+    const bool empty = B * N == 0 || H == 0;
+    if (!empty && (!ptr_ok(x) || !ptr_ok(w_q) || !ptr_ok(w_k) || !ptr_ok(w_v) || !ptr_ok(q) ||
+                   !ptr_ok(k) || !ptr_ok(v)))
+        return LIN_ATTN_ERR_INVALID;
+    if (d != D || d_model % 16 != 0 || d_model > 65536) return LIN_ATTN_ERR_UNSUPPORTED;
+    if (check_sizes(B, H, N) != LIN_ATTN_OK) return LIN_ATTN_ERR_UNSUPPORTED;
+    if (empty) return LIN_ATTN_OK;
+    // grid: one block per 128 tokens x 128 output columns
+    const int64_t tiles = ((B * N + 127) / 128) * ((3 * H * D + 127) / 128);
+    if (tiles > ((int64_t)1 << 31)) return LIN_ATTN_ERR_UNSUPPORTED;
+    return launch_status(
+        launch_qkv_project(x, w_q, w_k, w_v, B, N, d_model, H, q, k, v, (hipStream_t)stream));
+}
+
 int lin_attn_decode_step(const lin_attn_params* p, const void* q, const void* k, const void* v,
                          int64_t B, int64_t H, int64_t d, int64_t dv, const void* omega, float* S,
                          float* z, void* out, void* stream) {

@@ -109,6 +109,12 @@ hipError_t launch_segment_outputs_proj(const Cfg& c, int causal, const Proj& P, 
                                        Shape s, SegPlan sp, const float* state, int64_t sbh,
                                        int64_t sg, void* out, hipStream_t st);
 
+// q, k, v [B, H, N, 64] (bf16) = the tokens x [B, N, dm] times W_q, W_k, W_v
+// [H*64, dm] transposed: one matrix-core GEMM (project.hip).
+hipError_t launch_qkv_project(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                              int64_t B, int64_t N, int64_t dm, int64_t H, void* q, void* k,
+                              void* v, hipStream_t st);
+
 // Segment table of a packed batch: sequence i covers tokens
 // [cu_seqlens[i], cu_seqlens[i+1]) of every head and is cut into
 // ceil(len / seg_len) segments of `sub` parts of seg_len / sub tokens (tail

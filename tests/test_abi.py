@@ -349,3 +349,20 @@ def test_projected_workspace_formula():
         8 * 64 * E * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR_PROJ, p, 1, 8, 65536, 64, 64) == \
         (8 * 64 + 8) * E * 4
+
+
+def test_qkv_project_arguments():
+    f = lib.lin_attn_qkv_project
+
+    def call(x=FAKE, w=FAKE, B=1, N=100, dm=512, H=8, d=64, out=FAKE):
+        return f(x, w, w, w, B, N, dm, H, d, out, out, out, None)
+
+    assert call(x=None) == INVALID
+    assert call(w=FAKE + 4) == INVALID
+    assert call(out=None) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(dm=0) == INVALID
+    assert call(d=32) == UNSUPPORTED
+    assert call(dm=520) == UNSUPPORTED
+    assert call(N=0, x=None, w=None, out=None) == OK
+    assert call(H=0) == OK

@@ -622,3 +622,31 @@ def test_workload_favor_causal_prefill_from_tokens(gpu_lib):
     assert_parity(out, ro, 2e-2, "prefill from tokens out")
     assert_parity(S, rS, 2e-2, "prefill from tokens S")
     assert_parity(z, rz, 2e-2, "prefill from tokens z")
+
+
+@pytest.mark.parametrize("B,H,N,dm", [(2, 3, 300, 48), (1, 8, 200, 512), (3, 1, 1, 16),
+                                      (1, 2, 128, 128)])
+def test_qkv_project(gpu_lib, B, H, N, dm):
+    """One GEMM for all three projections, head-major outputs: ragged token
+    count, an odd number of heads (half-empty column tile), K not a multiple
+    of the 32-wide step.  Rounding to bf16 bounds the error by 2^-9
+    relative."""
+    c = ProjCase(133, B, H, N, dm, "elu1", 64)
+    q, k, v = gpu_lib.lin_attn_qkv_project(c.x, *c.w, H)
+    for name, got, w in zip("qkv", (q, k, v), c.wh):
+        ref = oracle.project(c.xh, w, H)
+        assert_parity(got, ref, 4e-3, f"projection {name}")
+
+
+def test_workload_favor_causal_prefill_from_projected_tokens(gpu_lib):
+    """The unfused route from tokens: the projection GEMM, then the
+    matrix-core prefill, at the prefill workload with d_model = 512."""
+    w = workloads.FAVOR_CAUSAL
+    c = ProjCase(w.wid, w.B, w.H, w.N, 512, w.kind, w.r)
+    kw = _wl_kw(w)
+    q, k, v = gpu_lib.lin_attn_qkv_project(c.x, *c.w, w.H)
+    out, S, z = gpu_lib.lin_attn_causal_chunked(q, k, v, w.kind, omega=c.omega, chunk=64, **kw)
+    ro, rS, rz = oracle.causal_proj(c.xh, *c.wh, w.H, w.kind, omega=c.omega_h, **kw)
+    assert_parity(out, ro, 2e-2, "projected route out")
+    assert_parity(S, rS, 2e-2, "projected route S")
+    assert_parity(z, rz, 2e-2, "projected route z")

@@ -134,10 +134,12 @@ VarlenLayout varlen_layout(const lin_attn_params* p, int64_t num_seqs, int64_t H
 //   [0, BH*G*E)          forward increments, then prefixes (causal)
 //   [BH*G*E, 2*BH*G*E)   backward increments, then suffixes (causal)
 //   bidirectional: the forward and the backward totals, BH*E each;
-//   causal: (1/D_t, dden_t) per token, BH*N*2.
+//   causal: (1/D_t, dden_t) per token, BH*N*2;
+//   then, 256-byte aligned, r*64 floats holding omega^T in bfloat16
+//   (bfloat16 FAVOR+ only).
 struct BackwardLayout {
     SegPlan sp;
-    size_t inc_b, extra, floats;
+    size_t inc_b, extra, omega_t, floats;
 };
 
 BackwardLayout backward_layout(const lin_attn_params* p, bool causal, int64_t BH, int64_t N) {
@@ -146,7 +148,9 @@ BackwardLayout backward_layout(const lin_attn_params* p, bool causal, int64_t BH
     const size_t inc = (size_t)(BH * L.sp.G * state_elems(p->r));
     L.inc_b = inc;
     L.extra = 2 * inc;
-    L.floats = L.extra + (causal ? (size_t)(BH * N * 2) : (size_t)(2 * BH * state_elems(p->r)));
+    L.omega_t = L.extra + (causal ? (size_t)(BH * N * 2) : (size_t)(2 * BH * state_elems(p->r)));
+    L.omega_t = (L.omega_t + 63) & ~(size_t)63; // 256-byte aligned (read as 16-byte pieces)
+    L.floats = L.omega_t + (size_t)p->r * D;
     return L;
 }
 
@@ -178,18 +182,23 @@ int backward_call(bool causal, const lin_attn_params* p, const void* q, const vo
     float* inc_f = (float*)ws;
     float* inc_b = inc_f + L.inc_b;
     float* extra = inc_f + L.extra;
+    void* omega_t = nullptr;
     hipError_t e = segment_sums(p, c, k, v, omega, s, sp, inc_f, st);
+    if (e == hipSuccess && p->phi == LIN_ATTN_PHI_FAVOR && p->dtype == LIN_ATTN_BF16) {
+        omega_t = inc_f + L.omega_t;
+        e = launch_transpose_omega(omega, p->r, omega_t, st);
+    }
     if (causal) {
         if (e == hipSuccess)
             e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_f, 1, nullptr, nullptr,
                                     nullptr, st);
         if (e == hipSuccess)
             e = launch_backward_query(c, p->dtype, 1, q, k, v, dout, omega, s, sp, inc_f, sp.G * E,
-                                      E, inc_b, extra, dq, st);
+                                      E, omega_t, inc_b, extra, dq, st);
         if (e == hipSuccess) e = launch_segment_suffix_scan(p->r, s, sp, inc_b, st);
         if (e == hipSuccess)
             e = launch_backward_key(c, p->dtype, 1, q, k, v, dout, omega, s, sp, inc_b, sp.G * E, E,
-                                    extra, dk, dvv, st);
+                                    omega_t, extra, dk, dvv, st);
     } else {
         float* fin_f = extra;
         float* fin_b = extra + BH * E;
@@ -198,13 +207,13 @@ int backward_call(bool causal, const lin_attn_params* p, const void* q, const vo
                                     fin_f, st);
         if (e == hipSuccess)
             e = launch_backward_query(c, p->dtype, 0, q, k, v, dout, omega, s, sp, fin_f, E, 0,
-                                      inc_b, nullptr, dq, st);
+                                      omega_t, inc_b, nullptr, dq, st);
         if (e == hipSuccess)
             e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_b, 0, nullptr, nullptr,
                                     fin_b, st);
         if (e == hipSuccess)
             e = launch_backward_key(c, p->dtype, 0, q, k, v, dout, omega, s, sp, fin_b, E, 0,
-                                    nullptr, dk, dvv, st);
+                                    omega_t, nullptr, dk, dvv, st);
     }
     return launch_status(e);
 }

@@ -18,9 +18,15 @@
 // tokens, with an exclusive suffix over per-segment increments.  Through the
 // map, dx = scale * J_phi(u)^T dphi at u = scale * x.
 //
-// Launch order (abi.hip): forward increments, forward scan, query pass (dq,
-// backward increments, per-token (1/D, dden) for the causal form), backward
-// scan (suffix for causal), key pass (dk, dv).
+// With bfloat16 inputs and FAVOR+, the two contractions with omega run on
+// the matrix cores (32x32x16 bf16, float32 accumulation): the projections
+// omega . x of the feature map (exact bf16 products, as in the forward
+// kernels) and du = sum_f w_f omega_f of the map's backward (w rounded to
+// bf16, against omega^T prepared once per call).
+//
+// Launch order (abi.hip): forward increments, forward scan, omega^T (bf16
+// FAVOR+ only), query pass (dq, backward increments, per-token (1/D, dden)
+// for the causal form), backward scan (suffix for causal), key pass (dk, dv).
 #include "launch.hpp"
 #include "tiles.hpp"
 
@@ -30,6 +36,81 @@ namespace {
 constexpr int NT = VNT;
 constexpr int L = 16;       // tokens per chunk
 constexpr int SL = DV + 4;  // LDS row stride of a state matrix [R][DV]
+
+typedef __bf16 bw_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float bw_f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename T> constexpr bool is_bf16() { return false; }
+template <> constexpr bool is_bf16<bf16_raw>() { return true; }
+
+__device__ __forceinline__ bw_f32x16 mfma32(uint4 a, uint4 b, bw_f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bw_bf16x8, a),
+                                                   __builtin_bit_cast(bw_bf16x8, b), c, 0, 0, 0);
+}
+
+// FAVOR+ features of the chunk's rows x (bfloat16, [rows][D] in global
+// memory) with the projections on the matrix cores: C[f][t] = omega_f . x_t
+// for 32-feature blocks, the waves taking blocks in turn.  Lane l holds token
+// t = l % 32 (rows at or past `rows` are zero, t < 32 covers L = 16), and
+// accumulator i feature 8(i/4) + 4(l/32) + i%4 of the block.  Then
+// out[t][f] = exp(scale (omega_f . x_t) - |u_t|^2 / 2) / sqrt(r) (u = scale x,
+// nrm[t] = |u_t|^2).  Ends without a barrier.
+template <int FPT>
+__device__ void favor_tile_mfma(const Cfg& c, const bf16_raw* __restrict__ x, int rows,
+                                const bf16_raw* __restrict__ omega, const float* nrm, float* out,
+                                int ol) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int tok = lane & 31, kq = 8 * (lane >> 5);
+    uint4 bx[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        bx[ks] = make_uint4(0u, 0u, 0u, 0u);
+        if (tok < rows) bx[ks] = *reinterpret_cast<const uint4*>(x + tok * D + 16 * ks + kq);
+    }
+    for (int fb = wv; fb < FPT; fb += NT / 64) {
+        bw_f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        const bf16_raw* wa = omega + (int64_t)(fb * 32 + (lane & 31)) * D + kq;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            acc = mfma32(*reinterpret_cast<const uint4*>(wa + 16 * ks), bx[ks], acc);
+        if (tok < L) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int f = fb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                out[tok * ol + f] = tok < rows ? favor_feature(c, c.scale * acc[i], nrm[tok]) : 0.f;
+            }
+        }
+    }
+}
+
+// The feature tile of the chunk: matrix-core projections for bfloat16
+// FAVOR+, else phi_tile.  x: the chunk's raw rows; u, nrm as phi_tile.
+// Ends with a barrier.
+template <typename T, int FPT>
+__device__ void bwd_phi_tile(const Cfg& c, const float* u, const float* nrm,
+                             const T* __restrict__ omega, const T* __restrict__ x, int rows,
+                             float* out, int ol, float* rs, float* live = nullptr) {
+    if constexpr (is_bf16<T>()) {
+        if (c.phi == PHI_FAVOR) {
+            favor_tile_mfma<FPT>(c, x, rows, omega, nrm, out, ol);
+            __syncthreads();
+            if (c.sum_norm) sum_normalize<L>(c, out, ol, rs, live);
+            return;
+        }
+    }
+    phi_tile<T, L>(c, u, nrm, omega, rows, out, ol, rs, live);
+}
+
+// omega^T [D][r] (bfloat16) for the matrix-core du contraction.
+__global__ __launch_bounds__(NT) void k_transpose_omega(const bf16_raw* __restrict__ omega, int r,
+                                                        bf16_raw* __restrict__ omega_t) {
+    const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
+    if (idx >= (int64_t)r * D) return;
+    const int d = (int)(idx / r), f = (int)(idx % r);
+    omega_t[idx] = omega[(int64_t)f * D + d];
+}
 
 // Loads state block src = (M [R][DV], m [R]) into M_s (row stride SL), m_s.
 template <int R>
@@ -169,7 +250,9 @@ __device__ void masked_products(const float* a, const float* b, int ld, int n, c
 template <typename T, int FPT>
 __device__ void phi_backward_tile(const Cfg& c, const float* u, const float* phi, int ol,
                                   const float* rs, const float* live, float* dp, float* cc,
-                                  const T* __restrict__ omega, int rows, T* __restrict__ out) {
+                                  const T* __restrict__ omega,
+                                  const bf16_raw* __restrict__ omega_t, int rows,
+                                  T* __restrict__ out) {
     constexpr int R = 32 * FPT;
     const int tid = threadIdx.x;
     if (c.sum_norm) {
@@ -194,6 +277,51 @@ __device__ void phi_backward_tile(const Cfg& c, const float* u, const float* phi
             dp[t * ol + f] = g;
         }
         __syncthreads();
+    }
+    if constexpr (is_bf16<T>()) {
+        if (c.phi == PHI_FAVOR && omega_t) {
+            // cc[t] = sum_f w[t][f] (cc is free after the transform above)
+            const int lane = tid & 63, w = tid >> 6;
+            for (int t = w; t < L; t += NT / 64) {
+                float sacc = 0.f;
+                for (int f = lane; f < R; f += 64) sacc += dp[t * ol + f];
+                sacc = wave_sum(sacc);
+                if (lane == 0) cc[t] = sacc;
+            }
+            __syncthreads();
+            // du as C[t][d] = sum_f w[t][f] omega[f][d]: waves 0 and 1 take
+            // the two 32-column halves of d; A = w rows (bf16), B = omega^T rows
+            if (w < 2) {
+                const int tok = lane & 31, kq = 8 * (lane >> 5);
+                const int dcol = 32 * w + (lane & 31);
+                bw_f32x16 acc;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+                const bf16_raw* wb = omega_t + (int64_t)dcol * R + kq;
+#pragma unroll 4
+                for (int f0 = 0; f0 < R; f0 += 16) {
+                    uint4 a = make_uint4(0u, 0u, 0u, 0u);
+                    if (tok < L) {
+                        const float4 x0 = *reinterpret_cast<const float4*>(dp + tok * ol + f0 + kq);
+                        const float4 x1 = *reinterpret_cast<const float4*>(dp + tok * ol + f0 + kq + 4);
+                        bw_bf16x8 h;
+                        h[0] = (__bf16)x0.x; h[1] = (__bf16)x0.y; h[2] = (__bf16)x0.z; h[3] = (__bf16)x0.w;
+                        h[4] = (__bf16)x1.x; h[5] = (__bf16)x1.y; h[6] = (__bf16)x1.z; h[7] = (__bf16)x1.w;
+                        a = __builtin_bit_cast(uint4, h);
+                    }
+                    acc = mfma32(a, *reinterpret_cast<const uint4*>(wb + f0), acc);
+                }
+                // accumulator e: token 8(e/4) + 4(l/32) + e%4, column dcol
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    if (t < rows)
+                        Elem<T>::store(out, (long)t * D + dcol,
+                                       c.scale * (acc[e] - cc[t] * u[t * D + dcol]));
+                }
+            }
+            return;
+        }
     }
     const int i = tid & 63, t0 = (tid >> 6) * (L / 4);
     float du[L / 4];
@@ -261,6 +389,7 @@ __global__ __launch_bounds__(NT) void k_bwd_query(Cfg c, const T* __restrict__ q
                                                   const T* __restrict__ omega, int64_t N, int64_t G,
                                                   int64_t seg_len, const float* __restrict__ state,
                                                   int64_t st_bh, int64_t st_g,
+                                                  const bf16_raw* __restrict__ omega_t,
                                                   float* __restrict__ inc, float* __restrict__ tok,
                                                   T* __restrict__ dq) {
     constexpr int R = 32 * FPT;
@@ -298,13 +427,15 @@ __global__ __launch_bounds__(NT) void k_bwd_query(Cfg c, const T* __restrict__ q
             __syncthreads();
             row_norms<L>(u_s, nrm_s);
             __syncthreads();
-            phi_tile<T, L>(c, u_s, nrm_s, omega, rows, pk_s, OL, rs_s);
+            bwd_phi_tile<T, FPT>(c, u_s, nrm_s, omega, k + (bh * N + c0) * D, rows, pk_s, OL,
+                                 rs_s);
         }
         load_rows<T, L>(q + (bh * N + c0) * D, rows, c.scale, u_s);
         __syncthreads();
         row_norms<L>(u_s, nrm_s);
         __syncthreads();
-        phi_tile<T, L>(c, u_s, nrm_s, omega, rows, pq_s, OL, rs_s, live_s);
+        bwd_phi_tile<T, FPT>(c, u_s, nrm_s, omega, q + (bh * N + c0) * D, rows, pq_s, OL, rs_s,
+                             live_s);
         if (CAUSAL) {
             masked_products<true>(pq_s, pk_s, OL, R, nullptr, a_s);
             __syncthreads();
@@ -376,7 +507,7 @@ __global__ __launch_bounds__(NT) void k_bwd_query(Cfg c, const T* __restrict__ q
         dphi_rows<FPT>(S_s, z_s, dn_s, dd_s, CAUSAL ? a_s : nullptr, pk_s, OL, dp_s);
         outer_accum<FPT>(pq_s, OL, dn_s, dd_s, rows, acc, macc);
         __syncthreads();
-        phi_backward_tile<T, FPT>(c, u_s, pq_s, OL, rs_s, live_s, dp_s, cc_s, omega, rows,
+        phi_backward_tile<T, FPT>(c, u_s, pq_s, OL, rs_s, live_s, dp_s, cc_s, omega, omega_t, rows,
                                   dq + (bh * N + c0) * D);
         if (CAUSAL) state_update<FPT>(S_s, z_s, pk_s, OL, v_s, nullptr, rows);
         __syncthreads();
@@ -403,6 +534,7 @@ __global__ __launch_bounds__(NT) void k_bwd_key(Cfg c, const T* __restrict__ q,
                                                 const T* __restrict__ omega, int64_t N, int64_t G,
                                                 int64_t seg_len, const float* __restrict__ state,
                                                 int64_t st_bh, int64_t st_g,
+                                                const bf16_raw* __restrict__ omega_t,
                                                 const float* __restrict__ tok, T* __restrict__ dk,
                                                 T* __restrict__ dv) {
     constexpr int R = 32 * FPT;
@@ -448,14 +580,16 @@ __global__ __launch_bounds__(NT) void k_bwd_key(Cfg c, const T* __restrict__ q,
             __syncthreads();
             row_norms<L>(uq_s, nrm_s);
             __syncthreads();
-            phi_tile<T, L>(c, uq_s, nrm_s, omega, rows, pq_s, OL, rsq_s);
+            bwd_phi_tile<T, FPT>(c, uq_s, nrm_s, omega, q + (bh * N + c0) * D, rows, pq_s, OL,
+                                 rsq_s);
         }
         load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, uk_s);
         load_rows<T, L>(v + (bh * N + c0) * DV, rows, 1.f, v_s);
         __syncthreads();
         row_norms<L>(uk_s, nrm_s);
         __syncthreads();
-        phi_tile<T, L>(c, uk_s, nrm_s, omega, rows, pk_s, OL, rs_s, live_s);
+        bwd_phi_tile<T, FPT>(c, uk_s, nrm_s, omega, k + (bh * N + c0) * D, rows, pk_s, OL, rs_s,
+                             live_s);
         if (CAUSAL) {
             // b[j][i] = phi(k_j) . phi(q_i); a[j][i] = v_j . dnum_i + dden_i; i >= j
             masked_products<false>(pk_s, pq_s, OL, R, nullptr, b_s);
@@ -496,7 +630,7 @@ __global__ __launch_bounds__(NT) void k_bwd_key(Cfg c, const T* __restrict__ q,
             }
         }
         __syncthreads();
-        phi_backward_tile<T, FPT>(c, uk_s, pk_s, OL, rs_s, live_s, dp_s, cc_s, omega, rows,
+        phi_backward_tile<T, FPT>(c, uk_s, pk_s, OL, rs_s, live_s, dp_s, cc_s, omega, omega_t, rows,
                                   dk + (bh * N + c0) * D);
         if (CAUSAL) state_update<FPT>(G_s, g_s, pq_s, OL, dn_s, dd_s, rows);
         __syncthreads();
@@ -506,40 +640,43 @@ __global__ __launch_bounds__(NT) void k_bwd_key(Cfg c, const T* __restrict__ q,
 template <typename T, int FPT>
 void query_fpt(const Cfg& c, int causal, const void* q, const void* k, const void* v,
                const void* dout, const void* omega, Shape s, SegPlan sp, const float* state,
-               int64_t sbh, int64_t sg, float* inc, float* tok, void* dq, hipStream_t st) {
+               int64_t sbh, int64_t sg, const bf16_raw* omega_t, float* inc, float* tok, void* dq,
+               hipStream_t st) {
     const dim3 grid((unsigned)(sp.G * s.BH)), block(NT);
     if (causal)
         hipLaunchKernelGGL((k_bwd_query<T, FPT, true>), grid, block, 0, st, c, (const T*)q,
                            (const T*)k, (const T*)v, (const T*)dout, (const T*)omega, s.N, sp.G,
-                           sp.seg_len, state, sbh, sg, inc, tok, (T*)dq);
+                           sp.seg_len, state, sbh, sg, omega_t, inc, tok, (T*)dq);
     else
         hipLaunchKernelGGL((k_bwd_query<T, FPT, false>), grid, block, 0, st, c, (const T*)q,
                            (const T*)k, (const T*)v, (const T*)dout, (const T*)omega, s.N, sp.G,
-                           sp.seg_len, state, sbh, sg, inc, tok, (T*)dq);
+                           sp.seg_len, state, sbh, sg, omega_t, inc, tok, (T*)dq);
 }
 
 template <typename T, int FPT>
 void key_fpt(const Cfg& c, int causal, const void* q, const void* k, const void* v,
              const void* dout, const void* omega, Shape s, SegPlan sp, const float* state,
-             int64_t sbh, int64_t sg, const float* tok, void* dk, void* dv, hipStream_t st) {
+             int64_t sbh, int64_t sg, const bf16_raw* omega_t, const float* tok, void* dk,
+             void* dv, hipStream_t st) {
     const dim3 grid((unsigned)(sp.G * s.BH)), block(NT);
     if (causal)
         hipLaunchKernelGGL((k_bwd_key<T, FPT, true>), grid, block, 0, st, c, (const T*)q,
                            (const T*)k, (const T*)v, (const T*)dout, (const T*)omega, s.N, sp.G,
-                           sp.seg_len, state, sbh, sg, tok, (T*)dk, (T*)dv);
+                           sp.seg_len, state, sbh, sg, omega_t, tok, (T*)dk, (T*)dv);
     else
         hipLaunchKernelGGL((k_bwd_key<T, FPT, false>), grid, block, 0, st, c, (const T*)q,
                            (const T*)k, (const T*)v, (const T*)dout, (const T*)omega, s.N, sp.G,
-                           sp.seg_len, state, sbh, sg, tok, (T*)dk, (T*)dv);
+                           sp.seg_len, state, sbh, sg, omega_t, tok, (T*)dk, (T*)dv);
 }
 
 template <typename T>
 hipError_t query_t(const Cfg& c, int causal, const void* q, const void* k, const void* v,
                    const void* dout, const void* omega, Shape s, SegPlan sp, const float* state,
-                   int64_t sbh, int64_t sg, float* inc, float* tok, void* dq, hipStream_t st) {
+                   int64_t sbh, int64_t sg, const bf16_raw* omega_t, float* inc, float* tok,
+                   void* dq, hipStream_t st) {
 #define LINATTN_QUERY(F)                                                                         \
-    case F: query_fpt<T, F>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, inc, tok, dq, \
-                            st);                                                                 \
+    case F: query_fpt<T, F>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, omega_t, inc,  \
+                            tok, dq, st);                                                        \
         break;
     switch (c.r / 32) {
         LINATTN_QUERY(1) LINATTN_QUERY(2) LINATTN_QUERY(3) LINATTN_QUERY(4)
@@ -553,9 +690,11 @@ hipError_t query_t(const Cfg& c, int causal, const void* q, const void* k, const
 template <typename T>
 hipError_t key_t(const Cfg& c, int causal, const void* q, const void* k, const void* v,
                  const void* dout, const void* omega, Shape s, SegPlan sp, const float* state,
-                 int64_t sbh, int64_t sg, const float* tok, void* dk, void* dv, hipStream_t st) {
+                 int64_t sbh, int64_t sg, const bf16_raw* omega_t, const float* tok, void* dk,
+                 void* dv, hipStream_t st) {
 #define LINATTN_KEY(F)                                                                            \
-    case F: key_fpt<T, F>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, tok, dk, dv, st); \
+    case F: key_fpt<T, F>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, omega_t, tok, dk, \
+                          dv, st);                                                               \
         break;
     switch (c.r / 32) {
         LINATTN_KEY(1) LINATTN_KEY(2) LINATTN_KEY(3) LINATTN_KEY(4)
@@ -568,23 +707,34 @@ hipError_t key_t(const Cfg& c, int causal, const void* q, const void* k, const v
 
 } // namespace
 
+hipError_t launch_transpose_omega(const void* omega, int r, void* omega_t, hipStream_t st) {
+    const int64_t n = (int64_t)r * D;
+    hipLaunchKernelGGL(k_transpose_omega, dim3((unsigned)((n + NT - 1) / NT)), dim3(NT), 0, st,
+                       (const bf16_raw*)omega, r, (bf16_raw*)omega_t);
+    return hipGetLastError();
+}
+
 hipError_t launch_backward_query(const Cfg& c, int dtype, int causal, const void* q,
                                  const void* k, const void* v, const void* dout, const void* omega,
                                  Shape s, SegPlan sp, const float* state, int64_t sbh, int64_t sg,
-                                 float* inc, float* tok, void* dq, hipStream_t st) {
-    return dtype == 0 ? query_t<float>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, inc,
-                                       tok, dq, st)
+                                 const void* omega_t, float* inc, float* tok, void* dq,
+                                 hipStream_t st) {
+    const bf16_raw* ot = (const bf16_raw*)omega_t;
+    return dtype == 0 ? query_t<float>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, ot,
+                                       inc, tok, dq, st)
                       : query_t<bf16_raw>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg,
-                                          inc, tok, dq, st);
+                                          ot, inc, tok, dq, st);
 }
 
 hipError_t launch_backward_key(const Cfg& c, int dtype, int causal, const void* q, const void* k,
                                const void* v, const void* dout, const void* omega, Shape s,
                                SegPlan sp, const float* state, int64_t sbh, int64_t sg,
-                               const float* tok, void* dk, void* dv, hipStream_t st) {
-    return dtype == 0 ? key_t<float>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, tok,
-                                     dk, dv, st)
-                      : key_t<bf16_raw>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg,
+                               const void* omega_t, const float* tok, void* dk, void* dv,
+                               hipStream_t st) {
+    const bf16_raw* ot = (const bf16_raw*)omega_t;
+    return dtype == 0 ? key_t<float>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, ot,
+                                     tok, dk, dv, st)
+                      : key_t<bf16_raw>(c, causal, q, k, v, dout, omega, s, sp, state, sbh, sg, ot,
                                         tok, dk, dv, st);
 }
 

@@ -144,14 +144,19 @@ hipError_t launch_segment_scan_varlen(int r, int64_t H, int64_t num_seqs, int64_
 // Key pass: from the backward state of each segment (causal: exclusive
 // suffix ws_b[bh][g], chunks walked last to first; bidirectional: total
 // fin_b[bh]) it writes dk and dv.
+// omega_t: omega^T [64][r] in bfloat16 (launch_transpose_omega) for bfloat16
+// FAVOR+ inputs, which then use the matrix-core contractions; else NULL.
+hipError_t launch_transpose_omega(const void* omega, int r, void* omega_t, hipStream_t st);
 hipError_t launch_backward_query(const Cfg& c, int dtype, int causal, const void* q,
                                  const void* k, const void* v, const void* dout, const void* omega,
                                  Shape s, SegPlan sp, const float* state, int64_t sbh, int64_t sg,
-                                 float* inc, float* tok, void* dq, hipStream_t st);
+                                 const void* omega_t, float* inc, float* tok, void* dq,
+                                 hipStream_t st);
 hipError_t launch_backward_key(const Cfg& c, int dtype, int causal, const void* q, const void* k,
                                const void* v, const void* dout, const void* omega, Shape s,
                                SegPlan sp, const float* state, int64_t sbh, int64_t sg,
-                               const float* tok, void* dk, void* dv, hipStream_t st);
+                               const void* omega_t, const float* tok, void* dk, void* dv,
+                               hipStream_t st);
 
 // p[0, n) = 0 with a plain kernel (capturable into a graph).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);

@@ -35,10 +35,34 @@ __device__ void row_norms(const float* u, float* nrm) {
     }
 }
 
+// Optional sum normalisation of a feature tile out[L][r] (row stride ol):
+// rs[t] = 1 / max(sum_f, eps) and, when `live` is given, live[t] = 1 where
+// the sum exceeds eps (the clamp does not hold); rows are scaled by rs.
+// The tile must be complete (caller synchronised).  Ends with a barrier.
+template <int L>
+__device__ void sum_normalize(const Cfg& c, float* out, int ol, float* rs, float* live) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    for (int t = w; t < L; t += VNT / 64) {
+        float s = 0.f;
+        for (int f = lane; f < c.r; f += 64) s += out[t * ol + f];
+        s = wave_sum(s);
+        if (lane == 0) {
+            rs[t] = 1.f / fmaxf(s, c.eps);
+            if (live) live[t] = s > c.eps ? 1.f : 0.f;
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < L * c.r; idx += VNT) {
+        const int t = idx / c.r, f = idx - t * c.r;
+        out[t * ol + f] *= rs[t];
+    }
+    __syncthreads();
+}
+
 // out[t][f] = phi_f(u_t) for t < L, f < r (rows >= `rows` are zero), then the
-// optional sum normalisation: rs[t] = 1 / max(sum_f, eps) and, when `live` is
-// given, live[t] = 1 where the sum exceeds eps (the clamp does not hold).
-// u, nrm must be complete (caller synchronised).  Ends with a barrier.
+// optional sum normalisation (sum_normalize).  u, nrm must be complete
+// (caller synchronised).  Ends with a barrier.
 template <typename T, int L>
 __device__ void phi_tile(const Cfg& c, const float* u, const float* nrm,
                          const T* __restrict__ omega, int rows, float* out, int ol, float* rs,
@@ -71,24 +95,7 @@ __device__ void phi_tile(const Cfg& c, const float* u, const float* nrm,
         }
     }
     __syncthreads();
-    if (c.sum_norm) {
-        const int lane = tid & 63, w = tid >> 6;
-        for (int t = w; t < L; t += VNT / 64) {
-            float s = 0.f;
-            for (int f = lane; f < c.r; f += 64) s += out[t * ol + f];
-            s = wave_sum(s);
-            if (lane == 0) {
-                rs[t] = 1.f / fmaxf(s, c.eps);
-                if (live) live[t] = s > c.eps ? 1.f : 0.f;
-            }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < L * c.r; idx += VNT) {
-            const int t = idx / c.r, f = idx - t * c.r;
-            out[t * ol + f] *= rs[t];
-        }
-        __syncthreads();
-    }
+    if (c.sum_norm) sum_normalize<L>(c, out, ol, rs, live);
 }
 
 } // namespace linattn

@@ -439,13 +439,16 @@ def cpu_baseline(w, scale):
                                                                         inputs.T_V))
     om = torch.from_numpy(inputs.orf_omega(w.r, w.d, w.wid).astype(np.float32)).to(
         torch.bfloat16).to(torch.float64).numpy()
-    t0 = time.perf_counter()
-    oracle.causal(q, k, v, "favor", omega=om, scale=scale, eps=w.eps)
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.causal(q, k, v, "favor", omega=om, scale=scale, eps=w.eps)
+        runs.append(time.perf_counter() - t0)
+    dt = sorted(runs)[1]
     cores = min(oracle.threads(), w.B * w.H)
     return {"value": w.B * n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"causal FAVOR+ oracle (fp64), B={w.B} H={w.H}, first {n} of {w.N} tokens; "
-                      f"{dt:.1f} s on {cores} threads (OpenMP over heads)"}
+                      f"median of 3 runs {dt:.2f} s on {cores} threads (OpenMP over heads)"}
 
 
 if __name__ == "__main__":

@@ -70,8 +70,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(heads shard across GPUs with no communication; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU; the library has no multi-GPU path (heads would "
+              "shard across GPUs with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -19,6 +19,7 @@ MAPS = [
     ("elu1", torch.bfloat16, 64, 1, True, 1.0),
     ("favor", torch.float32, 128, 1, False, 64 ** -0.25),
     ("favor", torch.bfloat16, 256, 1, False, 64 ** -0.25),
+    ("favor", torch.bfloat16, 128, 1, True, 64 ** -0.25),
     ("dpfp", torch.float32, 256, 2, True, 1.0),
     ("dpfp", torch.bfloat16, 128, 1, False, 1.0),
 ]

@@ -130,13 +130,14 @@ VarlenLayout varlen_layout(const lin_attn_params* p, int64_t num_seqs, int64_t H
     return L;
 }
 
-// Backward pass (vector kernels, no increment halving).  Workspace (float32):
+// Backward pass (no increment halving).  Workspace (float32):
 //   [0, BH*G*E)          forward increments, then prefixes (causal)
 //   [BH*G*E, 2*BH*G*E)   backward increments, then suffixes (causal)
-//   bidirectional: the forward and the backward totals, BH*E each;
+//   bidirectional: the forward and the backward totals, BH*E each, then
+//     dnum (bf16, BH*N*DV) and dden (BH*N) for the matrix-core route;
 //   causal: (1/D_t, dden_t) per token, BH*N*2;
 //   then, 256-byte aligned, r*64 floats holding omega^T in bfloat16
-//   (bfloat16 FAVOR+ only).
+//   (bfloat16 FAVOR+ on the vector kernels only).
 struct BackwardLayout {
     SegPlan sp;
     size_t inc_b, extra, omega_t, floats;
@@ -148,7 +149,9 @@ BackwardLayout backward_layout(const lin_attn_params* p, bool causal, int64_t BH
     const size_t inc = (size_t)(BH * L.sp.G * state_elems(p->r));
     L.inc_b = inc;
     L.extra = 2 * inc;
-    L.omega_t = L.extra + (causal ? (size_t)(BH * N * 2) : (size_t)(2 * BH * state_elems(p->r)));
+    L.omega_t = L.extra + (causal ? (size_t)(BH * N * 2)
+                                  : (size_t)(2 * BH * state_elems(p->r)) +
+                                        (size_t)(BH * N) * (DV / 2 + 1));
     L.omega_t = (L.omega_t + 63) & ~(size_t)63; // 256-byte aligned (read as 16-byte pieces)
     L.floats = L.omega_t + (size_t)p->r * D;
     return L;
@@ -184,7 +187,8 @@ int backward_call(bool causal, const lin_attn_params* p, const void* q, const vo
     float* extra = inc_f + L.extra;
     void* omega_t = nullptr;
     hipError_t e = segment_sums(p, c, k, v, omega, s, sp, inc_f, st);
-    if (e == hipSuccess && p->phi == LIN_ATTN_PHI_FAVOR && p->dtype == LIN_ATTN_BF16) {
+    if (e == hipSuccess && p->phi == LIN_ATTN_PHI_FAVOR && p->dtype == LIN_ATTN_BF16 &&
+        (causal || !use_mfma(p))) {
         omega_t = inc_f + L.omega_t;
         e = launch_transpose_omega(omega, p->r, omega_t, st);
     }
@@ -199,6 +203,23 @@ int backward_call(bool causal, const lin_attn_params* p, const void* q, const vo
         if (e == hipSuccess)
             e = launch_backward_key(c, p->dtype, 1, q, k, v, dout, omega, s, sp, inc_b, sp.G * E, E,
                                     omega_t, extra, dk, dvv, st);
+    } else if (use_mfma(p)) {
+        // matrix-core route: every wave its own chunks against the totals
+        float* fin_f = extra;
+        float* fin_b = extra + BH * E;
+        void* dnum = fin_b + BH * E;                        // bf16 [BH, N, DV]
+        float* dden = (float*)dnum + (size_t)BH * N * (DV / 2); // [BH, N]
+        if (e == hipSuccess)
+            e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_f, 0, nullptr, nullptr,
+                                    fin_f, st);
+        if (e == hipSuccess)
+            e = launch_favor_bwd_query(c, q, dout, omega, s, sp, fin_f, dq, dnum, dden, st);
+        // (G | g) = sum_t phi(q_t) (dnum_t, dden_t): the increment kernel on (q, dnum), z weighted
+        if (e == hipSuccess) e = launch_favor_sums(c, q, dnum, omega, s, sp, inc_b, st, dden);
+        if (e == hipSuccess)
+            e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_b, 0, nullptr, nullptr,
+                                    fin_b, st);
+        if (e == hipSuccess) e = launch_favor_bwd_key(c, k, v, omega, s, sp, fin_b, dk, dvv, st);
     } else {
         float* fin_f = extra;
         float* fin_b = extra + BH * E;

@@ -76,6 +76,7 @@ struct FavorArgs {
     const int64_t* order; // segment-major dispatch order or NULL (see SegPlan)
     int64_t osub;
     int64_t BH;
+    const float* zw;      // SUMS: per-token weights of the z sum [BH, N], or NULL (weight 1)
 };
 
 // The (head, segment) this workgroup runs; false when it runs nothing.
@@ -704,6 +705,9 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
 // workgroup by waves 0..3 and staged in LDS (one barrier per chunk), and
 // every wave has the same mix of matrix-core and vector work.
 constexpr int NT8 = 512;
+// ZW: the z sum weighted per token by a.zw (a separate instantiation, so the
+// plain one keeps its registers).
+template <bool ZW>
 __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
     __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LDV];
     __shared__ bf16x8 ks_s[2][256];
@@ -764,7 +768,18 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
         const bf16x8 fk0 = pack8(c, 0), fk1 = pack8(c, 8);
-        zacc += sum8(fk0) + sum8(fk1); // the bfloat16 features that also enter S
+        if (!ZW) {
+            zacc += sum8(fk0) + sum8(fk1); // the bfloat16 features that also enter S
+        } else {
+            // weighted: element i is token 8(i/4) + 4h + i%4 of the chunk
+            const float* wt = a.zw + bh * a.N + t0 + (int64_t)L * ci;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int t = 8 * (i >> 2) + 4 * h + (i & 3);
+                const float x = (float)(i < 8 ? fk0[i] : fk1[i - 8]);
+                if (t < rows) zacc = fmaf(x, wt[t], zacc);
+            }
+        }
         sync_lds(); // V^T of this chunk and the keys of the next staged
         const u16* vt = vt_s[ci & 1];
 #pragma unroll
@@ -784,6 +799,293 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
         }
     const float zt = half_sum(zacc);
     if (h == 0) dst[(int64_t)R * DV + f0 + lo] = zt;
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the bidirectional form on the matrix cores (see backward.hip
+// for the derivatives).  The state is one total per head, so every wave
+// takes its own 32-token chunks and nothing is exchanged between waves:
+// the workgroup first builds bf16 operand tables of the state and of
+// omega^T in LDS, then each wave walks its chunks over the 8 feature tiles.
+//   query pass:  phi(Q)^T per tile (omega Q^T, exp), num^T += S^T phi(Q)^T,
+//                den; then dnum, dden; then per tile
+//                dphi(Q)^T = S dnum^T + z dden^T, w = dphi o phi,
+//                du^T += omega^T w^T; dq = scale (du - (sum_f w) u).
+//                dnum (bf16) and dden go to memory for the backward state.
+//   key pass:    per tile phi(K)^T, dphi(K)^T = G V^T + g, dv^T += G^T phi(K)^T,
+//                w, du^T; dk = scale (du - (sum_f w) u).
+// Tables store the 16-blocks of their contraction index in swap23 order, so
+// an accumulator tile of the previous product is the other operand as is.
+// ---------------------------------------------------------------------------
+constexpr int NTB = 256;          // 4 waves, one chunk each at a time
+constexpr int LDF = R + 8;        // row length of the [64][R] tables (bank spread)
+constexpr int LDN = DV + 8;       // row length of the [R][64] table
+
+struct BwdArgs {
+    const u16* x;      // q (query pass) or k (key pass) [BH, N, D]
+    const u16* y;      // dout (query pass) or v (key pass) [BH, N, DV]
+    const u16* omega;  // [R, D]
+    const float* st;   // per head: (S | z) total (query pass) or (G | g) total (key pass)
+    int64_t N, G, seg_len;
+    float a_scale, b_norm, b_const, scale, eps;
+    int norm;
+    u16* dx;           // dq or dk [BH, N, D]
+    u16* dy;           // key pass: dv [BH, N, DV]; query pass: dnum (bf16) [BH, N, DV]
+    float* dden;       // query pass: dden [BH, N]
+};
+
+struct BwdTables {
+    u16 mt[DV * LDF];   // M^T [n][f']: M[16b + swap23(j)][n] at column 16b + j
+    u16 mn[R * LDN];    // query pass: S [f][n'] (n in swap23 order); key pass: G [f][n] natural
+    u16 wt[D * LDF];    // omega^T [d][f']: omega[16b + swap23(j)][d] at column 16b + j
+    float m1[R];        // z or g
+};
+
+__device__ __forceinline__ u16 f2bf(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
+
+// Build the tables from the head's state total (float32 [R][DV] then [R])
+// and omega; `swap_n`: store the n index of mn in swap23 order.
+__device__ void build_tables(BwdTables& tb, const float* __restrict__ st,
+                             const u16* __restrict__ omega, bool swap_n) {
+    for (int e = threadIdx.x; e < R * DV; e += NTB) {
+        const int f = e / DV, n = e % DV;
+        const u16 v = f2bf(st[e]);
+        tb.mt[n * LDF + (f & ~15) + swap23(f & 15)] = v;
+        tb.mn[f * LDN + (swap_n ? (n & ~15) + swap23(n & 15) : n)] = v;
+    }
+    for (int e = threadIdx.x; e < R * D; e += NTB) {
+        const int f = e / D, d = e % D;
+        tb.wt[d * LDF + (f & ~15) + swap23(f & 15)] = omega[e];
+    }
+    for (int f = threadIdx.x; f < R; f += NTB) tb.m1[f] = st[R * DV + f];
+}
+
+// Loads 4 consecutive bf16 of row `row` of X at column c0 as floats (0 past `rows`).
+__device__ __forceinline__ void load4(const u16* __restrict__ X, int ld, int row, int rows, int c0,
+                                      float (&o)[4]) {
+    uint2 w = make_uint2(0u, 0u);
+    if (row < rows) w = *reinterpret_cast<const uint2*>(X + (int64_t)row * ld + c0);
+    o[0] = __uint_as_float(w.x << 16);
+    o[1] = __uint_as_float(w.x & 0xffff0000u);
+    o[2] = __uint_as_float(w.y << 16);
+    o[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void store4(u16* __restrict__ X, int ld, int row, int c0, const float* v) {
+    uint2 w;
+    w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    *reinterpret_cast<uint2*>(X + (int64_t)row * ld + c0) = w;
+}
+
+// phi(X)^T for feature tile b of the chunk: C[f][t] = omega_f . x_t, then
+// exp2(C a_scale + bias_t); tokens past `rows` are zero.
+__device__ __forceinline__ f32x16 feature_tile(const BwdArgs& a, const bf16x8 (&xf)[4], int b,
+                                               float bias, bool live, int lo, int h) {
+    f32x16 c = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) c = mfma(omega_frag(a.omega, 0, b, ks, lo, h), xf[ks], c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = live ? __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bias)) : 0.f;
+    return c;
+}
+
+// dx[t][d] = scale (du[d][t] - wsum_t u[t][d]), u = scale x, for the lane's
+// token; du in accumulator layout (d = 32 dt + 8(i/4) + 4h + i%4).
+__device__ __forceinline__ void store_dx(const BwdArgs& a, const u16* xrow0, u16* dxrow0,
+                                         const f32x16 (&du)[2], float wsum, int lo, int h,
+                                         int rows) {
+    if (lo >= rows) return;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int c0 = 32 * dt + 8 * m + 4 * h;
+            float xv[4], o[4];
+            load4(xrow0, D, lo, rows, c0, xv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = a.scale * (du[dt][4 * m + j] - wsum * a.scale * xv[j]);
+            store4(dxrow0, D, lo, c0, o);
+        }
+}
+
+__global__ __launch_bounds__(NTB) void k_bwd_query_favor(BwdArgs a) {
+    __shared__ BwdTables tb;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lo = lane & 31, h = lane >> 5;
+    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
+    build_tables(tb, a.st + bh * state_elems(R), a.omega, true);
+    __syncthreads();
+    const int64_t t0 = g * a.seg_len, t1 = min<int64_t>(t0 + a.seg_len, a.N);
+    const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
+    const bool attn = a.norm == NORM_ATTN;
+    for (int ci = wv; ci < nck; ci += NTB / 64) {
+        const int64_t c0 = t0 + (int64_t)L * ci;
+        const int rows = (int)min<int64_t>(L, t1 - c0);
+        const bool live = lo < rows;
+        const u16* xr = a.x + (bh * a.N + c0) * D;
+        const u16* yr = a.y + (bh * a.N + c0) * DV;
+        bf16x8 xf[4];
+        load_x(xr, rows, lo, h, xf);
+        const float bias = fmaf(a.b_norm, sq_norm(xf), a.b_const);
+
+        // pass 1: features and the readout against the total
+        bf16x8 ph[8][2];
+        f32x16 num[2] = {zero16(), zero16()};
+        float den = 0.f;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const f32x16 c = feature_tile(a, xf, b, bias, live, lo, h);
+            ph[b][0] = pack8(c, 0);
+            ph[b][1] = pack8(c, 8);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                den = fmaf((float)ph[b][i >> 3][i & 7], tb.m1[32 * b + 8 * (i >> 2) + 4 * h + (i & 3)], den);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    num[nt] = mfma(lds8(tb.mt + (32 * nt + lo) * LDF + 32 * b + 16 * s2 + 8 * h),
+                                   ph[b][s2], num[nt]);
+            // one tile at a time: keeps the scheduler from hoisting every
+            // tile's operand loads (which spills)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        den = half_sum(den);
+
+        // dnum, dden of the lane's token (num in accumulator layout: n = 32 nt + 8(i/4) + 4h + i%4)
+        const float inv = attn ? 1.f / fmaxf(den, a.eps) : 1.f;
+        float dn[2][16], dot = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                float o[4];
+                load4(yr, DV, lo, rows, 32 * nt + 8 * m + 4 * h, o);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    dot = fmaf(o[j], num[nt][4 * m + j], dot);
+                    dn[nt][4 * m + j] = o[j] * inv;
+                }
+            }
+        dot = half_sum(dot);
+        const float dden = (attn && den > a.eps) ? -dot * inv * inv : 0.f;
+        if (live) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    store4(a.dy + (bh * a.N + c0) * DV, DV, lo, 32 * nt + 8 * m + 4 * h, &dn[nt][4 * m]);
+            if (h == 0) a.dden[bh * a.N + c0 + lo] = dden;
+        }
+        bf16x8 dnf[2][2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                bf16x8 r;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) r[e] = (__bf16)dn[nt][8 * s2 + e];
+                dnf[nt][s2] = r;
+            }
+
+        // pass 2: dphi(Q) = S dnum + z dden per tile, w, du
+        f32x16 du[2] = {zero16(), zero16()};
+        float wsum = 0.f;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            f32x16 gq = zero16();
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    gq = mfma(lds8(tb.mn + (32 * b + lo) * LDN + 32 * nt + 16 * s2 + 8 * h),
+                              dnf[nt][s2], gq);
+            f32x16 w;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float gi = fmaf(tb.m1[32 * b + 8 * (i >> 2) + 4 * h + (i & 3)], dden, gq[i]);
+                w[i] = gi * (float)ph[b][i >> 3][i & 7];
+                wsum += w[i];
+            }
+            const bf16x8 w0 = pack8(w, 0), w1 = pack8(w, 8);
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                du[dt] = mfma(lds8(tb.wt + (32 * dt + lo) * LDF + 32 * b + 8 * h), w0, du[dt]);
+                du[dt] = mfma(lds8(tb.wt + (32 * dt + lo) * LDF + 32 * b + 16 + 8 * h), w1, du[dt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wsum = half_sum(wsum);
+        store_dx(a, xr, a.dx + (bh * a.N + c0) * D, du, wsum, lo, h, rows);
+    }
+}
+
+__global__ __launch_bounds__(NTB) void k_bwd_key_favor(BwdArgs a) {
+    __shared__ BwdTables tb;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lo = lane & 31, h = lane >> 5;
+    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
+    build_tables(tb, a.st + bh * state_elems(R), a.omega, false);
+    __syncthreads();
+    const int64_t t0 = g * a.seg_len, t1 = min<int64_t>(t0 + a.seg_len, a.N);
+    const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
+    for (int ci = wv; ci < nck; ci += NTB / 64) {
+        const int64_t c0 = t0 + (int64_t)L * ci;
+        const int rows = (int)min<int64_t>(L, t1 - c0);
+        const bool live = lo < rows;
+        const u16* xr = a.x + (bh * a.N + c0) * D;
+        const u16* yr = a.y + (bh * a.N + c0) * DV;
+        bf16x8 xf[4], vf[4];
+        load_x(xr, rows, lo, h, xf);
+        load_x(yr, rows, lo, h, vf); // V^T as the B operand (n natural: 16 ks + 8h + e)
+        const float bias = fmaf(a.b_norm, sq_norm(xf), a.b_const);
+        f32x16 dv[2] = {zero16(), zero16()}, du[2] = {zero16(), zero16()};
+        float wsum = 0.f;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const f32x16 c = feature_tile(a, xf, b, bias, live, lo, h);
+            const bf16x8 p0 = pack8(c, 0), p1 = pack8(c, 8);
+            // dphi(K)^T = G V^T + g
+            f32x16 gk = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                gk = mfma(lds8(tb.mn + (32 * b + lo) * LDN + 16 * ks + 8 * h), vf[ks], gk);
+            // dv^T += G^T phi(K)^T
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                dv[nt] = mfma(lds8(tb.mt + (32 * nt + lo) * LDF + 32 * b + 8 * h), p0, dv[nt]);
+                dv[nt] = mfma(lds8(tb.mt + (32 * nt + lo) * LDF + 32 * b + 16 + 8 * h), p1, dv[nt]);
+            }
+            f32x16 w;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float gi = gk[i] + tb.m1[32 * b + 8 * (i >> 2) + 4 * h + (i & 3)];
+                w[i] = live ? gi * c[i] : 0.f;
+                wsum += w[i];
+            }
+            const bf16x8 w0 = pack8(w, 0), w1 = pack8(w, 8);
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                du[dt] = mfma(lds8(tb.wt + (32 * dt + lo) * LDF + 32 * b + 8 * h), w0, du[dt]);
+                du[dt] = mfma(lds8(tb.wt + (32 * dt + lo) * LDF + 32 * b + 16 + 8 * h), w1, du[dt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wsum = half_sum(wsum);
+        if (live) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                {
+                    const float o[4] = {dv[nt][4 * m], dv[nt][4 * m + 1], dv[nt][4 * m + 2],
+                                        dv[nt][4 * m + 3]};
+                    store4(a.dy + (bh * a.N + c0) * DV, DV, lo, 32 * nt + 8 * m + 4 * h, o);
+                }
+        }
+        store_dx(a, xr, a.dx + (bh * a.N + c0) * D, du, wsum, lo, h, rows);
+    }
 }
 
 FavorArgs make_args(const Cfg& c, const void* q, const void* k, const void* v, const void* omega,
@@ -810,6 +1112,7 @@ FavorArgs make_args(const Cfg& c, const void* q, const void* k, const void* v, c
     a.order = sp.order;
     a.osub = sp.osub;
     a.BH = s.BH;
+    a.zw = nullptr;
     return a;
 }
 
@@ -820,10 +1123,53 @@ bool favor_mfma_supported(const Cfg& c, int dtype) {
 }
 
 hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const void* omega,
-                             Shape s, SegPlan sp, float* ws, hipStream_t st) {
-    const FavorArgs a = make_args(c, nullptr, k, v, omega, s, sp, ws, sp.G * state_elems(R),
-                                  state_elems(R), nullptr);
-    hipLaunchKernelGGL(k_favor_sums8, dim3((unsigned)(sp.G * s.BH)), dim3(NT8), 0, st, a);
+                             Shape s, SegPlan sp, float* ws, hipStream_t st, const float* zw) {
+    FavorArgs a = make_args(c, nullptr, k, v, omega, s, sp, ws, sp.G * state_elems(R),
+                            state_elems(R), nullptr);
+    a.zw = zw;
+    if (zw)
+        hipLaunchKernelGGL(k_favor_sums8<true>, dim3((unsigned)(sp.G * s.BH)), dim3(NT8), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_favor_sums8<false>, dim3((unsigned)(sp.G * s.BH)), dim3(NT8), 0, st,
+                           a);
+    return hipGetLastError();
+}
+
+static BwdArgs bwd_args(const Cfg& c, const void* x, const void* y, const void* omega, Shape s,
+                        SegPlan sp, const float* st, void* dx, void* dy, float* dden) {
+    BwdArgs a;
+    a.x = (const u16*)x;
+    a.y = (const u16*)y;
+    a.omega = (const u16*)omega;
+    a.st = st;
+    a.N = s.N;
+    a.G = sp.G;
+    a.seg_len = sp.seg_len;
+    a.a_scale = c.scale * LOG2E;
+    a.b_norm = -0.5f * c.scale * c.scale * LOG2E;
+    a.b_const = c.favor_log2_bias;
+    a.scale = c.scale;
+    a.eps = c.eps;
+    a.norm = c.norm;
+    a.dx = (u16*)dx;
+    a.dy = (u16*)dy;
+    a.dden = dden;
+    return a;
+}
+
+hipError_t launch_favor_bwd_query(const Cfg& c, const void* q, const void* dout, const void* omega,
+                                  Shape s, SegPlan sp, const float* total, void* dq, void* dnum,
+                                  float* dden, hipStream_t st) {
+    const BwdArgs a = bwd_args(c, q, dout, omega, s, sp, total, dq, dnum, dden);
+    hipLaunchKernelGGL(k_bwd_query_favor, dim3((unsigned)(sp.G * s.BH)), dim3(NTB), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_favor_bwd_key(const Cfg& c, const void* k, const void* v, const void* omega,
+                                Shape s, SegPlan sp, const float* total, void* dk, void* dv,
+                                hipStream_t st) {
+    const BwdArgs a = bwd_args(c, k, v, omega, s, sp, total, dk, dv, nullptr);
+    hipLaunchKernelGGL(k_bwd_key_favor, dim3((unsigned)(sp.G * s.BH)), dim3(NTB), 0, st, a);
     return hipGetLastError();
 }
 

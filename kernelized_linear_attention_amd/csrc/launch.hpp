@@ -164,11 +164,26 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 // Matrix-core path for FAVOR+ with bfloat16 inputs and r = 256 (favor_mfma.hip);
 // same workspace layout and segment scan as the vector path.
 bool favor_mfma_supported(const Cfg& c, int dtype);
+// zw: optional per-token weights [BH, N] of the z sum (z = sum_t w_t phi(k_t));
+// NULL gives the plain sum.
 hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const void* omega,
-                             Shape s, SegPlan sp, float* ws, hipStream_t st);
+                             Shape s, SegPlan sp, float* ws, hipStream_t st,
+                             const float* zw = nullptr);
 hipError_t launch_favor_outputs(const Cfg& c, int causal, const void* q, const void* k,
                                 const void* v, const void* omega, Shape s, SegPlan sp,
                                 const float* state, int64_t sbh, int64_t sg, void* out,
+                                hipStream_t st);
+
+// Backward of the bidirectional form on the matrix cores (FAVOR+, bfloat16,
+// r = 256): total = the head's (S | z) for the query pass, (G | g) for the key
+// pass.  The query pass also writes dnum (bf16 [BH, N, DV]) and dden
+// (float [BH, N]), from which the increment kernel (with z weights dden)
+// forms (G | g).
+hipError_t launch_favor_bwd_query(const Cfg& c, const void* q, const void* dout, const void* omega,
+                                  Shape s, SegPlan sp, const float* total, void* dq, void* dnum,
+                                  float* dden, hipStream_t st);
+hipError_t launch_favor_bwd_key(const Cfg& c, const void* k, const void* v, const void* omega,
+                                Shape s, SegPlan sp, const float* total, void* dk, void* dv,
                                 hipStream_t st);
 
 // Orthogonal random features (orf.hip): n_mat matrices [r, d], d <= 64.

@@ -292,13 +292,16 @@ def test_backward_workspace_formula():
     plan: two workgroups per CU, 64 segments of 1024 tokens per head at H = 8,
     N = 65536), then the two full summaries per head (bidirectional) or two
     floats per token (causal: 1 / max(den, eps) and the denominator's
-    gradient), then r * 64 floats for omega^T (used in bfloat16 by FAVOR+)."""
+    gradient), or the dnum (bf16) and dden of every token (bidirectional),
+    then r * 64 floats for omega^T (used in bfloat16 by FAVOR+)."""
     p = params()
     E = 256 * 64 + 256
     inc = 2 * 8 * 64 * E * 4
     om_t = 256 * 64 * 4
+    # bidirectional: + dnum (bf16) and dden per token for the matrix-core route
+    tokens = 8 * 65536 * (32 + 1) * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR_BACKWARD, p, 1, 8, 65536, 64, 64) == \
-        inc + 2 * 8 * E * 4 + om_t
+        inc + 2 * 8 * E * 4 + tokens + om_t
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 65536, 64, 64) == \
         inc + 8 * 65536 * 2 * 4 + om_t
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 0, 64, 64) == 0

@@ -651,3 +651,27 @@ def test_workload_favor_causal_prefill_from_projected_tokens(gpu_lib):
     assert_parity(out, ro, 2e-2, "projected route out")
     assert_parity(S, rS, 2e-2, "projected route S")
     assert_parity(z, rz, 2e-2, "projected route z")
+
+
+@pytest.mark.parametrize("N,n_seg", [(1, 0), (31, 0), (33, 1), (300, 0), (300, 5), (1000, 3)])
+@pytest.mark.parametrize("norm", ["attn", "none"])
+def test_bidir_backward_matrix_core_route(gpu_lib, N, n_seg, norm):
+    """bf16 FAVOR+ with r = 256 runs the bidirectional backward on the matrix
+    cores: ragged chunks (each wave owns 32-token chunks), segment counts,
+    both readouts, and bitwise repeatability."""
+    B, H = 2, 2
+    c = Case(125, B, H, N, "favor", torch.bfloat16, r=256)
+    do = dev(inputs.normal((B, H, N, 64), 125, inputs.T_DOUT), torch.bfloat16)
+    kw = dict(scale=64 ** -0.25, norm=norm)
+    got = gpu_lib.lin_attn_bidir_backward(c.q, c.k, c.v, do, "favor", n_seg=n_seg, **c.gkw(**kw))
+    again = gpu_lib.lin_attn_bidir_backward(c.q, c.k, c.v, do, "favor", n_seg=n_seg,
+                                            **c.gkw(**kw))
+    assert all(torch.equal(a, b) for a, b in zip(got, again)), "not bitwise reproducible"
+    if N == 1 and norm == "attn":
+        # one token: dv = dout, dq = dk = 0 up to rounding (out = v)
+        assert_parity(got[2], host(do), 1e-2, "N=1 dv")
+        for g in got[:2]:
+            assert float(g.abs().max()) <= 1e-2 * float(do.abs().max())
+        return
+    ref = oracle.bidir_backward(c.qh, c.kh, c.vh, host(do), "favor", **c.okw(**kw))
+    _assert_grads(got, ref, 2e-2, f"bidir backward N={N} n_seg={n_seg} {norm}")

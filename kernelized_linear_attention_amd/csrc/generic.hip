@@ -326,6 +326,79 @@ __global__ __launch_bounds__(NT) void k_segment_scan_varlen(int r, int64_t H, in
         z_fin[sh * r + (e - rdv)] = run;
 }
 
+// The same scan with one block per (element block, head) instead of per
+// (element block, head, sequence): the sequence starts first[] are staged in
+// LDS once, and each thread walks all parts of its head in batches of
+// independent loads that span sequences (the carry restarts at every
+// sequence's first part).  For batches of at most MAXS_LDS sequences.
+constexpr int MAXS_LDS = 1024;
+__global__ __launch_bounds__(NT) void k_segment_scan_varlen_heads(
+    int r, int64_t H, int64_t num_seqs, int64_t parts, const int64_t* __restrict__ first,
+    const float* __restrict__ S0, const float* __restrict__ z0, float* __restrict__ ws,
+    int prefix_stride, float* __restrict__ S_fin, float* __restrict__ z_fin) {
+    constexpr int BATCH = 16;
+    __shared__ int64_t first_s[MAXS_LDS + 1];
+    for (int64_t i = threadIdx.x; i <= num_seqs; i += NT) first_s[i] = first[i];
+    __syncthreads();
+    const int64_t E = state_elems(r);
+    const int64_t bpe = (E + NT - 1) / NT;
+    const int64_t h = blockIdx.x / bpe;
+    const int64_t e = (blockIdx.x % bpe) * NT + threadIdx.x;
+    if (e >= E) return;
+    const int64_t rdv = (int64_t)r * DV;
+    auto start = [&](int64_t i) -> float {
+        if (!S0) return 0.f;
+        const int64_t sh = i * H + h;
+        return e < rdv ? S0[sh * rdv + e] : z0[sh * r + (e - rdv)];
+    };
+    auto finish = [&](int64_t i, float v) {
+        const int64_t sh = i * H + h;
+        if (e < rdv)
+            S_fin[sh * rdv + e] = v;
+        else
+            z_fin[sh * r + (e - rdv)] = v;
+    };
+    const int64_t P = min<int64_t>(first_s[num_seqs], parts);
+    float* p = ws + h * parts * E + e;
+    const int64_t pmask = prefix_stride - 1;
+    // sequence i owns parts first[i] .. first[i+1]-1 (empty ones end where they start)
+    int64_t i = 0, seq_first = 0, seq_end = 0;
+    float run = 0.f;
+    auto next_sequence = [&]() {
+        while (i < num_seqs && first_s[i + 1] <= first_s[i]) {
+            finish(i, start(i));
+            ++i;
+        }
+        if (i < num_seqs) {
+            run = start(i);
+            seq_first = first_s[i];
+            seq_end = first_s[i + 1];
+        }
+    };
+    next_sequence();
+    for (int64_t gb = 0; gb < P; gb += BATCH) {
+        const int n = (int)min<int64_t>(BATCH, P - gb);
+        float a[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) a[j] = j < n ? p[(gb + j) * E] : 0.f;
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            if (j < n && i < num_seqs) {
+                const int64_t g = gb + j;
+                if (prefix_stride > 0 && ((g - seq_first) & pmask) == 0) p[g * E] = run;
+                run += a[j];
+                if (g + 1 >= seq_end) { // last part of sequence i
+                    finish(i, run);
+                    ++i;
+                    next_sequence();
+                }
+            }
+        }
+    }
+    // sequences with parts past the capacity (malformed boundaries only)
+    for (; i < num_seqs; ++i) finish(i, start(i));
+}
+
 // ---------------------------------------------------------------------------
 // Segment outputs.  CAUSAL: chunked recurrence from the carried-in state;
 // otherwise: readout of every token against the full summary.
@@ -598,6 +671,12 @@ hipError_t launch_segment_scan_varlen(int r, int64_t H, int64_t num_seqs, int64_
                                       float* ws, int prefix_stride, float* S_fin, float* z_fin,
                                       hipStream_t st) {
     const int64_t E = state_elems(r);
+    if (num_seqs <= MAXS_LDS) {
+        const dim3 grid((unsigned)(((E + NT - 1) / NT) * H));
+        hipLaunchKernelGGL(k_segment_scan_varlen_heads, grid, dim3(NT), 0, st, r, H, num_seqs,
+                           parts, first, S0, z0, ws, prefix_stride, S_fin, z_fin);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)(((E + NT - 1) / NT) * H * num_seqs));
     hipLaunchKernelGGL(k_segment_scan_varlen, grid, dim3(NT), 0, st, r, H, parts, first, S0, z0, ws,
                        prefix_stride, S_fin, z_fin);

@@ -675,3 +675,25 @@ def test_bidir_backward_matrix_core_route(gpu_lib, N, n_seg, norm):
         return
     ref = oracle.bidir_backward(c.qh, c.kh, c.vh, host(do), "favor", **c.okw(**kw))
     _assert_grads(got, ref, 2e-2, f"bidir backward N={N} n_seg={n_seg} {norm}")
+
+
+@pytest.mark.parametrize("num_seqs", [1000, 1100])
+def test_causal_varlen_thousand_documents(gpu_lib, num_seqs):
+    """Many short documents (empty ones included), on both sides of the
+    1024-document limit of the per-head scan (above it the per-document scan
+    runs)."""
+    g = np.random.default_rng(126 + num_seqs)
+    lens = g.integers(0, 40, size=num_seqs)
+    lens[::97] = 0
+    c, q, k, v, cu, cu_d = _packed(126, list(lens), "elu1", torch.float32, 64, 1, H=2)
+    S0 = inputs.normal((num_seqs, 2, 64, 64), 126, inputs.T_PREFIX).astype(np.float32) * 0.1
+    z0 = np.abs(inputs.normal((num_seqs, 2, 64), 126, inputs.T_PREFIX, 1)).astype(np.float32)
+    S = torch.from_numpy(S0).cuda()
+    z = torch.from_numpy(z0).cuda()
+    out, S, z = gpu_lib.lin_attn_causal_varlen(q, k, v, cu_d, "elu1", S=S, z=z, state_in=True,
+                                               **c.gkw())
+    ro, rS, rz = oracle.causal_varlen(c.qh[0], c.kh[0], c.vh[0], cu, "elu1", S0=S0, z0=z0,
+                                      **c.okw())
+    assert_parity(out, ro, 1e-4, "many documents out", lead_dims=1)
+    assert_parity(S, rS, 1e-4, "many documents S")
+    assert_parity(z, rz, 1e-4, "many documents z")

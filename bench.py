@@ -307,9 +307,8 @@ def main():
             kms = total_ms / args.steps
             kflops = backward_alg_flops_per_tok_head(wk.r, wk.d, wk.dv) * wk.B * wk.H * wk.N
             kach = kflops / (float(np.mean(per)) * 1e-3) / 1e12
-            # bf16 FAVOR+ with r = 256: the bidirectional backward runs on the
-            # matrix cores, the causal one on the fp32 vector kernels
-            mfma = form == "bidir"
+            # bf16 FAVOR+ with r = 256: both backward forms run on the matrix cores
+            mfma = True
             peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
             bw[form] = {"workload": wk.name, "B": wk.B, "H": wk.H, "N": wk.N, "r": wk.r,
                         "ms_per_step": kms, "tokens_per_s": wk.B * wk.N / (kms * 1e-3),

@@ -188,11 +188,24 @@ int backward_call(bool causal, const lin_attn_params* p, const void* q, const vo
     void* omega_t = nullptr;
     hipError_t e = segment_sums(p, c, k, v, omega, s, sp, inc_f, st);
     if (e == hipSuccess && p->phi == LIN_ATTN_PHI_FAVOR && p->dtype == LIN_ATTN_BF16 &&
-        (causal || !use_mfma(p))) {
+        !use_mfma(p)) {
         omega_t = inc_f + L.omega_t;
         e = launch_transpose_omega(omega, p->r, omega_t, st);
     }
-    if (causal) {
+    if (causal && use_mfma(p)) {
+        // matrix-core route: each workgroup walks its segment's chunks with the
+        // evolving state in accumulators (forward order, then reverse)
+        if (e == hipSuccess)
+            e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_f, 1, nullptr, nullptr,
+                                    nullptr, st);
+        if (e == hipSuccess)
+            e = launch_favor_causal_bwd_query(c, q, k, v, dout, omega, s, sp, inc_f, sp.G * E, E,
+                                              extra, inc_b, dq, st);
+        if (e == hipSuccess) e = launch_segment_suffix_scan(p->r, s, sp, inc_b, st);
+        if (e == hipSuccess)
+            e = launch_favor_causal_bwd_key(c, q, k, v, dout, omega, s, sp, inc_b, sp.G * E, E,
+                                            extra, dk, dvv, st);
+    } else if (causal) {
         if (e == hipSuccess)
             e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_f, 1, nullptr, nullptr,
                                     nullptr, st);

@@ -1135,6 +1135,530 @@ hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const v
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Causal backward on the matrix cores (FAVOR+, bf16, r = 256).  One workgroup
+// per (head, segment) walks its chunks in order (query pass) or in reverse
+// (key pass); wave w keeps the 64 features F_w = [64w, 64w + 64) of the
+// evolving state in float32 accumulators, as the forward kernel's consumers
+// do.  Products over all features (readout, the masked intra-chunk block,
+// du) are summed across the four waves through LDS, two workgroup barriers
+// per chunk.  Tiles are 32 x 32 accumulator tiles; T as an operand is
+// pack8(T, 8 kk) (k-slots in swap23 order): the B operand of a product over
+// T's rows, or the A operand of T^T.  transpose32 turns a tile into its
+// transpose with the identity operand (exact: one bf16 product by 1 each).
+// ---------------------------------------------------------------------------
+constexpr int NTC = 256; // 4 waves
+constexpr int LDT = 40;  // row length of the per-chunk V tables (bank spread)
+
+__device__ __forceinline__ f32x16 transpose32(const f32x16& t, const bf16x8 (&eye)[2]) {
+    return mfma(pack8(t, 8), eye[1], mfma(pack8(t, 0), eye[0], zero16()));
+}
+
+struct CausalArgs {
+    const u16* q;
+    const u16* k;
+    const u16* v;
+    const u16* dout;
+    const u16* omega;
+    int64_t N, G, seg_len;
+    float a_scale, b_norm, b_const, scale, eps;
+    int norm;
+    const float* state; // query: forward prefix per segment; key: backward suffix per segment
+    int64_t st_bh, st_g;
+    float* tok;         // (1 / D_t, dden_t) per token: written by the query pass, read by the key pass
+    float* inc;         // query pass: backward increments per segment [BH][G][E]
+    u16* dx;            // dq or dk
+    u16* dv;            // key pass: dv
+};
+
+struct CausalSmem {
+    u16 wt[D * LDF];                 // omega^T [d][f'] (swap23 columns)
+    u16 vt[2][DV * LDT];             // V^T [n][j'] of the chunk (j in swap23 order)
+    u16 vs[2][L * LDN];              // V [j][n'] of the chunk (n in swap23 order)
+    float part[4][3][16][64];        // per wave: partial readout (two tiles) + intra block
+    float dpart[4][2][16][64];       // per wave: partial du^T or dv^T tiles (a second buffer, so
+                                     // no wave can overwrite partials another is still reading)
+    float tokv[4][3][L];             // per wave, per token: [0] den / B1 partial sums, [1] dden
+                                     // (own copy), [2] sum_f w partial
+    float z[R];                      // z (query pass) or g (key pass)
+    float dd[L];                     // dden of the chunk's tokens (key pass)
+};
+
+// V of chunk rows [rows] (bf16 [L][DV] at vp) into the two LDS tables.
+__device__ __forceinline__ void stage_v(u16* vt, u16* vs, const u16* __restrict__ vp, int rows) {
+    for (int e = threadIdx.x; e < L * DV; e += NTC) {
+        const int j = e / DV, n = e % DV;
+        const u16 x = j < rows ? vp[(int64_t)j * DV + n] : (u16)0;
+        vt[n * LDT + (j & ~15) + swap23(j & 15)] = x;
+        vs[j * LDN + (n & ~15) + swap23(n & 15)] = x;
+    }
+}
+
+// phi(X)^T tiles of this wave's two feature tiles: C[f][t], token t = lo.
+__device__ __forceinline__ void features2(const CausalArgs& a, const bf16x8 (&xf)[4], int w,
+                                          float bias, bool live, int lo, int h, f32x16 (&p)[2]) {
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+        f32x16 c = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) c = mfma(omega_frag(a.omega, 64 * w, ft, ks, lo, h), xf[ks], c);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] = live ? __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bias)) : 0.f;
+        p[ft] = c;
+    }
+}
+
+__global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
+    __shared__ CausalSmem sm;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lo = lane & 31, h = lane >> 5;
+    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
+    const int64_t t0 = g * a.seg_len, t1 = min<int64_t>(t0 + a.seg_len, a.N);
+    const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
+    const bool attn = a.norm == NORM_ATTN;
+    const bf16x8 eye[2] = {eye_frag(0, lo, h), eye_frag(1, lo, h)};
+    // element i of a [row x token] tile pairs token lo with row 8(i/4) + 4h + i%4
+    const int keep_thr = lo - 4 * h; // row <= token  <=>  8(i/4) + i%4 <= keep_thr
+
+    for (int e = threadIdx.x; e < R * D; e += NTC) {
+        const int f = e / D, d = e % D;
+        sm.wt[d * LDF + (f & ~15) + swap23(f & 15)] = a.omega[e];
+    }
+    // the forward state carried into the segment: S[F_w] in accumulators, z in LDS
+    const float* st = a.state + bh * a.st_bh + g * a.st_g;
+    f32x16 S[2][2], Gi[2][2];
+    float gacc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            Gi[ft][nt] = zero16();
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                S[ft][nt][i] = st[(int64_t)(64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)) * DV + 32 * nt + lo];
+        }
+    for (int f = threadIdx.x; f < R; f += NTC) sm.z[f] = st[(int64_t)R * DV + f];
+    __syncthreads(); // omega^T table and z
+
+    for (int ci = 0; ci < nck; ++ci) {
+        const int64_t c0 = t0 + (int64_t)L * ci;
+        const int rows = (int)min<int64_t>(L, t1 - c0);
+        const bool live = lo < rows;
+        const int buf = ci & 1;
+        stage_v(sm.vt[buf], sm.vs[buf], a.v + (bh * a.N + c0) * DV, rows);
+        const u16* qr = a.q + (bh * a.N + c0) * D;
+        bf16x8 qf[4], kf[4];
+        load_x(qr, rows, lo, h, qf);
+        load_x(a.k + (bh * a.N + c0) * D, rows, lo, h, kf);
+        f32x16 PQ[2], PK[2];
+        features2(a, qf, w, fmaf(a.b_norm, sq_norm(qf), a.b_const), live, lo, h, PQ);
+        features2(a, kf, w, fmaf(a.b_norm, sq_norm(kf), a.b_const), live, lo, h, PK);
+
+        // partial readout num^T [n x t] = S^T phi(Q)^T, den, and A1^T [j x t] = phi(K) phi(Q)^T over F_w
+        f32x16 num[2] = {zero16(), zero16()}, a1 = zero16();
+        float den = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 pq = pack8(PQ[ft], 8 * kk);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) num[nt] = mfma(pack8(S[ft][nt], 8 * kk), pq, num[nt]);
+                a1 = mfma(pack8(PK[ft], 8 * kk), pq, a1);
+            }
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                den = fmaf(PQ[ft][i], sm.z[64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)], den);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sm.part[w][0][i][lane] = num[0][i];
+            sm.part[w][1][i][lane] = num[1][i];
+            sm.part[w][2][i][lane] = a1[i];
+        }
+        den = half_sum(den);
+        if (h == 0) sm.tokv[w][0][lo] = den;
+        __syncthreads(); // B1: partials and V tables of the chunk
+
+        // full sums (every wave, redundantly)
+        den = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) num[0][i] = num[1][i] = a1[i] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                num[0][i] += sm.part[u][0][i][lane];
+                num[1][i] += sm.part[u][1][i][lane];
+                a1[i] += sm.part[u][2][i][lane];
+            }
+            den += sm.tokv[u][0][lo];
+        }
+        // masked intra-chunk block: keys j <= query t
+        float aden = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            a1[i] = (8 * (i >> 2) + (i & 3) <= keep_thr) ? a1[i] : 0.f;
+            aden += a1[i];
+        }
+        den += half_sum(aden);
+        const u16* vt = sm.vt[buf];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 af = pack8(a1, 8 * kk);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                num[nt] = mfma(lds8(vt + (32 * nt + lo) * LDT + 16 * kk + 8 * h), af, num[nt]);
+        }
+
+        // dnum^T [n x t], dden
+        const float inv = attn ? 1.f / fmaxf(den, a.eps) : 1.f;
+        const u16* dor = a.dout + (bh * a.N + c0) * DV;
+        f32x16 dn[2];
+        float dot = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                float o[4];
+                load4(dor, DV, lo, rows, 32 * nt + 8 * m + 4 * h, o);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    dot = fmaf(o[j], num[nt][4 * m + j], dot);
+                    dn[nt][4 * m + j] = o[j] * inv;
+                }
+            }
+        dot = half_sum(dot);
+        const float dden = (attn && den > a.eps) ? -dot * inv * inv : 0.f;
+        if (w == 0 && h == 0 && live) {
+            a.tok[2 * (bh * a.N + c0 + lo)] = inv;
+            a.tok[2 * (bh * a.N + c0 + lo) + 1] = dden;
+        }
+        if (h == 0) sm.tokv[w][1][lo] = dden; // this wave's copy, read back below
+
+        // A2^T [j x t] = V dnum^T + dden_t, masked
+        f32x16 a2 = zero16();
+        const u16* vs = sm.vs[buf];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                a2 = mfma(lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), pack8(dn[nt], 8 * kk), a2);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a2[i] = (8 * (i >> 2) + (i & 3) <= keep_thr) ? a2[i] + dden : 0.f;
+
+        // dphi(Q)^T [f x t] = S dnum^T + z dden + phi(K)^T A2^T, w = dphi o phi, du^T
+        f32x16 du[2] = {zero16(), zero16()}, PKt[2];
+        float wsum = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+            PKt[ft] = transpose32(PK[ft], eye);
+            f32x16 gq = zero16();
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const f32x16 St = transpose32(S[ft][nt], eye); // [n x f]
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) gq = mfma(pack8(St, 8 * kk), pack8(dn[nt], 8 * kk), gq);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) gq = mfma(pack8(PKt[ft], 8 * kk), pack8(a2, 8 * kk), gq);
+            f32x16 wq;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float gi = fmaf(sm.z[64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)], dden, gq[i]);
+                wq[i] = gi * PQ[ft][i];
+                wsum += wq[i];
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 wf = pack8(wq, 8 * kk);
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt)
+                    du[dt] = mfma(lds8(sm.wt + (32 * dt + lo) * LDF + 64 * w + 32 * ft + 16 * kk + 8 * h),
+                                  wf, du[dt]);
+            }
+        }
+        wsum = half_sum(wsum);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sm.dpart[w][0][i][lane] = du[0][i];
+            sm.dpart[w][1][i][lane] = du[1][i];
+        }
+        if (h == 0) sm.tokv[w][2][lo] = wsum;
+        __syncthreads(); // B2: du partials
+        if (w < 2) {
+            // wave dt sums d-tile dt and stores dq = scale (du - wsum u)
+            f32x16 s = zero16();
+            float ws = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[i] += sm.dpart[u][w][i][lane];
+                ws += sm.tokv[u][2][lo];
+            }
+            if (live) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int c0d = 32 * w + 8 * m + 4 * h;
+                    float xv[4], o[4];
+                    load4(qr, D, lo, rows, c0d, xv);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = a.scale * (s[4 * m + j] - ws * a.scale * xv[j]);
+                    store4(a.dx + (bh * a.N + c0) * D, D, lo, c0d, o);
+                }
+            }
+        }
+
+        // backward increments: G[F_w] += phi(Q)^T dnum, g[F_w] += phi(Q)^T dden
+        f32x16 dnr[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) dnr[nt] = transpose32(dn[nt], eye); // [t x n]
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+            const f32x16 PQt = transpose32(PQ[ft], eye); // [t x f]
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 pf = pack8(PQt, 8 * kk);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) Gi[ft][nt] = mfma(pf, pack8(dnr[nt], 8 * kk), Gi[ft][nt]);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                gacc[ft] = fmaf(PQt[i], sm.tokv[w][1][8 * (i >> 2) + 4 * h + (i & 3)], gacc[ft]);
+        }
+        // state update: S[F_w] += phi(K)^T V, z[F_w] += phi(K)^T 1
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 pk = pack8(PKt[ft], 8 * kk);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    S[ft][nt] = mfma(pk, lds8(vt + (32 * nt + lo) * LDT + 16 * kk + 8 * h), S[ft][nt]);
+            }
+            float zs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) zs += PKt[ft][i];
+            zs = half_sum(zs);
+            if (h == 0) sm.z[64 * w + 32 * ft + lo] += zs;
+        }
+    }
+    // the segment's backward increments
+    float* dst = a.inc + (bh * a.G + g) * state_elems(R);
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                dst[(int64_t)(64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)) * DV + 32 * nt + lo] = Gi[ft][nt][i];
+        const float gs = half_sum(gacc[ft]);
+        if (h == 0) dst[(int64_t)R * DV + 64 * w + 32 * ft + lo] = gs;
+    }
+}
+
+__global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
+    __shared__ CausalSmem sm;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lo = lane & 31, h = lane >> 5;
+    const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
+    const int64_t t0 = g * a.seg_len, t1 = min<int64_t>(t0 + a.seg_len, a.N);
+    const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
+    const bf16x8 eye[2] = {eye_frag(0, lo, h), eye_frag(1, lo, h)};
+    // element i of a [row x key] tile pairs key lo with row (query) 8(i/4) + 4h + i%4
+    const int keep_thr = lo - 4 * h; // query >= key  <=>  8(i/4) + i%4 >= keep_thr
+
+    for (int e = threadIdx.x; e < R * D; e += NTC) {
+        const int f = e / D, d = e % D;
+        sm.wt[d * LDF + (f & ~15) + swap23(f & 15)] = a.omega[e];
+    }
+    // the backward state after the segment (suffix): G[F_w] in accumulators, g in LDS
+    const float* st = a.state + bh * a.st_bh + g * a.st_g;
+    f32x16 Gs[2][2];
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                Gs[ft][nt][i] = st[(int64_t)(64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)) * DV + 32 * nt + lo];
+    for (int f = threadIdx.x; f < R; f += NTC) sm.z[f] = st[(int64_t)R * DV + f];
+    __syncthreads(); // omega^T table and g
+
+    for (int cr = 0; cr < nck; ++cr) {
+        const int ci = nck - 1 - cr; // chunks last to first
+        const int64_t c0 = t0 + (int64_t)L * ci;
+        const int rows = (int)min<int64_t>(L, t1 - c0);
+        const bool live = lo < rows;
+        const int buf = cr & 1;
+        stage_v(sm.vt[buf], sm.vs[buf], a.v + (bh * a.N + c0) * DV, rows);
+        const u16* kr = a.k + (bh * a.N + c0) * D;
+        bf16x8 qf[4], kf[4];
+        load_x(a.q + (bh * a.N + c0) * D, rows, lo, h, qf);
+        load_x(kr, rows, lo, h, kf);
+        f32x16 PQ[2], PK[2];
+        features2(a, qf, w, fmaf(a.b_norm, sq_norm(qf), a.b_const), live, lo, h, PQ);
+        features2(a, kf, w, fmaf(a.b_norm, sq_norm(kf), a.b_const), live, lo, h, PK);
+        // dnum^T [n x i] = dout^T / D_i and dden_i of the lane's query i = lo
+        float inv = 0.f, dden = 0.f;
+        if (live) {
+            inv = a.tok[2 * (bh * a.N + c0 + lo)];
+            dden = a.tok[2 * (bh * a.N + c0 + lo) + 1];
+        }
+        const u16* dor = a.dout + (bh * a.N + c0) * DV;
+        f32x16 dn[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                float o[4];
+                load4(dor, DV, lo, rows, 32 * nt + 8 * m + 4 * h, o);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dn[nt][4 * m + j] = o[j] * inv;
+            }
+        if (h == 0) sm.tokv[w][1][lo] = dden; // this wave's copy, by query
+
+        // partials over F_w: dv^T [n x j] = G^T phi(K)^T, B1 [i x j] = phi(Q) phi(K)^T
+        f32x16 dvp[2] = {zero16(), zero16()}, b1 = zero16();
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 pk = pack8(PK[ft], 8 * kk);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) dvp[nt] = mfma(pack8(Gs[ft][nt], 8 * kk), pk, dvp[nt]);
+                b1 = mfma(pack8(PQ[ft], 8 * kk), pk, b1);
+            }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sm.part[w][0][i][lane] = dvp[0][i];
+            sm.part[w][1][i][lane] = dvp[1][i];
+            sm.part[w][2][i][lane] = b1[i];
+        }
+        __syncthreads(); // B1: partials, dden copies and V tables of the chunk
+
+        const u16* vs = sm.vs[buf];
+        f32x16 dnr[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) dnr[nt] = transpose32(dn[nt], eye); // [i x n]
+        if (w < 2) {
+            // wave nt: dv^T tile nt = sum of partials + dnum^T B1 (masked: query i >= key j)
+            f32x16 s = zero16();
+            f32x16 bm = zero16();
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    s[i] += sm.part[u][w][i][lane];
+                    bm[i] += sm.part[u][2][i][lane];
+                }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) bm[i] = (8 * (i >> 2) + (i & 3) >= keep_thr) ? bm[i] : 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) s = mfma(pack8(dnr[w], 8 * kk), pack8(bm, 8 * kk), s);
+            if (live) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float o[4] = {s[4 * m], s[4 * m + 1], s[4 * m + 2], s[4 * m + 3]};
+                    store4(a.dv + (bh * a.N + c0) * DV, DV, lo, 32 * w + 8 * m + 4 * h, o);
+                }
+            }
+        }
+        // A3 [i x j] = dnum_i . v_j + dden_i, masked (i >= j)
+        f32x16 a3 = zero16();
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                a3 = mfma(pack8(dn[nt], 8 * kk), lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), a3);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            a3[i] = (8 * (i >> 2) + (i & 3) >= keep_thr)
+                        ? a3[i] + sm.tokv[w][1][8 * (i >> 2) + 4 * h + (i & 3)]
+                        : 0.f;
+        // dphi(K)^T [f x j] = G V^T + g + phi(Q)^T A3, w = dphi o phi, du^T
+        f32x16 du[2] = {zero16(), zero16()}, PQt[2];
+        float wsum = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+            PQt[ft] = transpose32(PQ[ft], eye); // [i x f]
+            f32x16 gk = zero16();
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const f32x16 Gt = transpose32(Gs[ft][nt], eye); // [n x f]
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    gk = mfma(pack8(Gt, 8 * kk), lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), gk);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) gk = mfma(pack8(PQt[ft], 8 * kk), pack8(a3, 8 * kk), gk);
+            f32x16 wk;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float gi = gk[i] + sm.z[64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)];
+                wk[i] = gi * PK[ft][i];
+                wsum += wk[i];
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 wf = pack8(wk, 8 * kk);
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt)
+                    du[dt] = mfma(lds8(sm.wt + (32 * dt + lo) * LDF + 64 * w + 32 * ft + 16 * kk + 8 * h),
+                                  wf, du[dt]);
+            }
+        }
+        wsum = half_sum(wsum);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sm.dpart[w][0][i][lane] = du[0][i];
+            sm.dpart[w][1][i][lane] = du[1][i];
+        }
+        if (h == 0) sm.tokv[w][2][lo] = wsum;
+        __syncthreads(); // B2: du partials
+        if (w >= 2) {
+            // wave 2 + dt: dk tile dt = scale (du - wsum u)
+            const int dt = w - 2;
+            f32x16 s = zero16();
+            float ws = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[i] += sm.dpart[u][dt][i][lane];
+                ws += sm.tokv[u][2][lo];
+            }
+            if (live) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int c0d = 32 * dt + 8 * m + 4 * h;
+                    float xv[4], o[4];
+                    load4(kr, D, lo, rows, c0d, xv);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = a.scale * (s[4 * m + j] - ws * a.scale * xv[j]);
+                    store4(a.dx + (bh * a.N + c0) * D, D, lo, c0d, o);
+                }
+            }
+        }
+        // suffix update for the earlier chunks: G[F_w] += phi(Q)^T dnum, g += phi(Q)^T dden
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 pf = pack8(PQt[ft], 8 * kk);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) Gs[ft][nt] = mfma(pf, pack8(dnr[nt], 8 * kk), Gs[ft][nt]);
+            }
+            float gsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                gsum = fmaf(PQt[ft][i], sm.tokv[w][1][8 * (i >> 2) + 4 * h + (i & 3)], gsum);
+            gsum = half_sum(gsum);
+            if (h == 0) sm.z[64 * w + 32 * ft + lo] += gsum;
+        }
+    }
+}
+
 static BwdArgs bwd_args(const Cfg& c, const void* x, const void* y, const void* omega, Shape s,
                         SegPlan sp, const float* st, void* dx, void* dy, float* dden) {
     BwdArgs a;
@@ -1170,6 +1694,55 @@ hipError_t launch_favor_bwd_key(const Cfg& c, const void* k, const void* v, cons
                                 hipStream_t st) {
     const BwdArgs a = bwd_args(c, k, v, omega, s, sp, total, dk, dv, nullptr);
     hipLaunchKernelGGL(k_bwd_key_favor, dim3((unsigned)(sp.G * s.BH)), dim3(NTB), 0, st, a);
+    return hipGetLastError();
+}
+
+static CausalArgs causal_args(const Cfg& c, const void* q, const void* k, const void* v,
+                              const void* dout, const void* omega, Shape s, SegPlan sp,
+                              const float* state, int64_t sbh, int64_t sg, float* tok, float* inc,
+                              void* dx, void* dv) {
+    CausalArgs a;
+    a.q = (const u16*)q;
+    a.k = (const u16*)k;
+    a.v = (const u16*)v;
+    a.dout = (const u16*)dout;
+    a.omega = (const u16*)omega;
+    a.N = s.N;
+    a.G = sp.G;
+    a.seg_len = sp.seg_len;
+    a.a_scale = c.scale * LOG2E;
+    a.b_norm = -0.5f * c.scale * c.scale * LOG2E;
+    a.b_const = c.favor_log2_bias;
+    a.scale = c.scale;
+    a.eps = c.eps;
+    a.norm = c.norm;
+    a.state = state;
+    a.st_bh = sbh;
+    a.st_g = sg;
+    a.tok = tok;
+    a.inc = inc;
+    a.dx = (u16*)dx;
+    a.dv = (u16*)dv;
+    return a;
+}
+
+hipError_t launch_favor_causal_bwd_query(const Cfg& c, const void* q, const void* k, const void* v,
+                                         const void* dout, const void* omega, Shape s, SegPlan sp,
+                                         const float* prefix, int64_t sbh, int64_t sg, float* tok,
+                                         float* inc, void* dq, hipStream_t st) {
+    const CausalArgs a =
+        causal_args(c, q, k, v, dout, omega, s, sp, prefix, sbh, sg, tok, inc, dq, nullptr);
+    hipLaunchKernelGGL(k_bwd_causal_query_favor, dim3((unsigned)(sp.G * s.BH)), dim3(NTC), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_favor_causal_bwd_key(const Cfg& c, const void* q, const void* k, const void* v,
+                                       const void* dout, const void* omega, Shape s, SegPlan sp,
+                                       const float* suffix, int64_t sbh, int64_t sg,
+                                       const float* tok, void* dk, void* dv, hipStream_t st) {
+    const CausalArgs a = causal_args(c, q, k, v, dout, omega, s, sp, suffix, sbh, sg,
+                                     const_cast<float*>(tok), nullptr, dk, dv);
+    hipLaunchKernelGGL(k_bwd_causal_key_favor, dim3((unsigned)(sp.G * s.BH)), dim3(NTC), 0, st, a);
     return hipGetLastError();
 }
 

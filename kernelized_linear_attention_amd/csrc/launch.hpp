@@ -186,6 +186,19 @@ hipError_t launch_favor_bwd_key(const Cfg& c, const void* k, const void* v, cons
                                 Shape s, SegPlan sp, const float* total, void* dk, void* dv,
                                 hipStream_t st);
 
+// Causal backward on the matrix cores (same configuration): the query pass
+// from each segment's forward prefix writes dq, (1/D, dden) per token and the
+// segment's backward increments; the key pass from each segment's backward
+// suffix writes dk and dv.
+hipError_t launch_favor_causal_bwd_query(const Cfg& c, const void* q, const void* k, const void* v,
+                                         const void* dout, const void* omega, Shape s, SegPlan sp,
+                                         const float* prefix, int64_t sbh, int64_t sg, float* tok,
+                                         float* inc, void* dq, hipStream_t st);
+hipError_t launch_favor_causal_bwd_key(const Cfg& c, const void* q, const void* k, const void* v,
+                                       const void* dout, const void* omega, Shape s, SegPlan sp,
+                                       const float* suffix, int64_t sbh, int64_t sg,
+                                       const float* tok, void* dk, void* dv, hipStream_t st);
+
 // Orthogonal random features (orf.hip): n_mat matrices [r, d], d <= 64.
 hipError_t launch_orf(const float* gauss, const float* len_gauss, int64_t n_mat, int64_t r, int d,
                       int dtype, void* omega, hipStream_t st);

@@ -697,3 +697,26 @@ def test_causal_varlen_thousand_documents(gpu_lib, num_seqs):
     assert_parity(out, ro, 1e-4, "many documents out", lead_dims=1)
     assert_parity(S, rS, 1e-4, "many documents S")
     assert_parity(z, rz, 1e-4, "many documents z")
+
+
+@pytest.mark.parametrize("N,n_seg", [(1, 0), (31, 0), (33, 1), (100, 2), (300, 0), (1000, 3)])
+@pytest.mark.parametrize("norm", ["attn", "none"])
+def test_causal_backward_matrix_core_route(gpu_lib, N, n_seg, norm):
+    """bf16 FAVOR+ with r = 256 runs the causal backward on the matrix cores:
+    ragged chunks, several segments (carried prefix and suffix states), both
+    readouts, bitwise repeatability."""
+    B, H = 2, 2
+    c = Case(127, B, H, N, "favor", torch.bfloat16, r=256)
+    do = dev(inputs.normal((B, H, N, 64), 127, inputs.T_DOUT), torch.bfloat16)
+    kw = dict(scale=64 ** -0.25, norm=norm)
+    got = gpu_lib.lin_attn_causal_backward(c.q, c.k, c.v, do, "favor", n_seg=n_seg, **c.gkw(**kw))
+    again = gpu_lib.lin_attn_causal_backward(c.q, c.k, c.v, do, "favor", n_seg=n_seg,
+                                             **c.gkw(**kw))
+    assert all(torch.equal(a, b) for a, b in zip(got, again)), "not bitwise reproducible"
+    if N == 1 and norm == "attn":
+        assert_parity(got[2], host(do), 1e-2, "N=1 dv")
+        for g in got[:2]:
+            assert float(g.abs().max()) <= 1e-2 * float(do.abs().max())
+        return
+    ref = oracle.causal_backward(c.qh, c.kh, c.vh, host(do), "favor", **c.okw(**kw))
+    _assert_grads(got, ref, 2e-2, f"causal backward N={N} n_seg={n_seg} {norm}")

@@ -1184,14 +1184,57 @@ struct CausalSmem {
     float dd[L];                     // dden of the chunk's tokens (key pass)
 };
 
-// V of chunk rows [rows] (bf16 [L][DV] at vp) into the two LDS tables.
-__device__ __forceinline__ void stage_v(u16* vt, u16* vs, const u16* __restrict__ vp, int rows) {
-    for (int e = threadIdx.x; e < L * DV; e += NTC) {
-        const int j = e / DV, n = e % DV;
-        const u16 x = j < rows ? vp[(int64_t)j * DV + n] : (u16)0;
-        vt[n * LDT + (j & ~15) + swap23(j & 15)] = x;
-        vs[j * LDN + (n & ~15) + swap23(n & 15)] = x;
+// V of the chunk: thread t fetches row t/8, columns 8 (t%8) .. +7 (zero past
+// `rows`) with one 16-byte load, then writes them to the two LDS tables.
+__device__ __forceinline__ uint4 fetch_v(const u16* __restrict__ vp, int rows) {
+    const int j = threadIdx.x >> 3, n0 = (threadIdx.x & 7) * 8;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (j < rows) x = *reinterpret_cast<const uint4*>(vp + (int64_t)j * DV + n0);
+    return x;
+}
+
+__device__ __forceinline__ void stash_v(u16* vt, u16* vs, uint4 x) {
+    const int j = threadIdx.x >> 3, n0 = (threadIdx.x & 7) * 8;
+    const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int n = n0 + e;
+        const u16 val = (e & 1) ? (u16)(wd[e >> 1] >> 16) : (u16)(wd[e >> 1] & 0xffffu);
+        vt[n * LDT + (j & ~15) + swap23(j & 15)] = val;
+        vs[j * LDN + (n & ~15) + swap23(n & 15)] = val;
     }
+}
+
+// The lane's dout values of a [n x t] tile pair: dout[lo][32 nt + 8 m + 4h .. +3]
+// as raw bf16 pairs (zero past `rows`).
+__device__ __forceinline__ void fetch_dout(const u16* __restrict__ dor, int rows, int lo, int h,
+                                           uint2 (&r)[2][4]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            r[nt][m] = make_uint2(0u, 0u);
+            if (lo < rows)
+                r[nt][m] = *reinterpret_cast<const uint2*>(dor + (int64_t)lo * DV + 32 * nt + 8 * m + 4 * h);
+        }
+}
+
+// Row lo of X at columns 32 dt + 8m + 4h .. +3 (the epilogue's u = scale x).
+__device__ __forceinline__ void fetch_row(const u16* __restrict__ xr, int rows, int lo, int h,
+                                          int dt, uint2 (&r)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        r[m] = make_uint2(0u, 0u);
+        if (lo < rows)
+            r[m] = *reinterpret_cast<const uint2*>(xr + (int64_t)lo * D + 32 * dt + 8 * m + 4 * h);
+    }
+}
+
+__device__ __forceinline__ void unpack4(uint2 w, float (&o)[4]) {
+    o[0] = __uint_as_float(w.x << 16);
+    o[1] = __uint_as_float(w.x & 0xffff0000u);
+    o[2] = __uint_as_float(w.y << 16);
+    o[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
 // phi(X)^T tiles of this wave's two feature tiles: C[f][t], token t = lo.
@@ -1245,11 +1288,16 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         const int rows = (int)min<int64_t>(L, t1 - c0);
         const bool live = lo < rows;
         const int buf = ci & 1;
-        stage_v(sm.vt[buf], sm.vs[buf], a.v + (bh * a.N + c0) * DV, rows);
+        // every load of the chunk first, so that they share one round trip
         const u16* qr = a.q + (bh * a.N + c0) * D;
+        const uint4 vx = fetch_v(a.v + (bh * a.N + c0) * DV, rows);
         bf16x8 qf[4], kf[4];
         load_x(qr, rows, lo, h, qf);
         load_x(a.k + (bh * a.N + c0) * D, rows, lo, h, kf);
+        uint2 dr[2][4], xe[4];
+        fetch_dout(a.dout + (bh * a.N + c0) * DV, rows, lo, h, dr);
+        if (w < 2) fetch_row(qr, rows, lo, h, w, xe);
+        stash_v(sm.vt[buf], sm.vs[buf], vx);
         f32x16 PQ[2], PK[2];
         features2(a, qf, w, fmaf(a.b_norm, sq_norm(qf), a.b_const), live, lo, h, PQ);
         features2(a, kf, w, fmaf(a.b_norm, sq_norm(kf), a.b_const), live, lo, h, PK);
@@ -1314,7 +1362,6 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
 
         // dnum^T [n x t], dden
         const float inv = attn ? 1.f / fmaxf(den, a.eps) : 1.f;
-        const u16* dor = a.dout + (bh * a.N + c0) * DV;
         f32x16 dn[2];
         float dot = 0.f;
 #pragma unroll
@@ -1322,7 +1369,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 float o[4];
-                load4(dor, DV, lo, rows, 32 * nt + 8 * m + 4 * h, o);
+                unpack4(dr[nt][m], o);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     dot = fmaf(o[j], num[nt][4 * m + j], dot);
@@ -1402,7 +1449,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
                 for (int m = 0; m < 4; ++m) {
                     const int c0d = 32 * w + 8 * m + 4 * h;
                     float xv[4], o[4];
-                    load4(qr, D, lo, rows, c0d, xv);
+                    unpack4(xe[m], xv);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) o[j] = a.scale * (s[4 * m + j] - ws * a.scale * xv[j]);
                     store4(a.dx + (bh * a.N + c0) * D, D, lo, c0d, o);
@@ -1492,28 +1539,32 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         const int rows = (int)min<int64_t>(L, t1 - c0);
         const bool live = lo < rows;
         const int buf = cr & 1;
-        stage_v(sm.vt[buf], sm.vs[buf], a.v + (bh * a.N + c0) * DV, rows);
+        // every load of the chunk first, so that they share one round trip
         const u16* kr = a.k + (bh * a.N + c0) * D;
+        const uint4 vx = fetch_v(a.v + (bh * a.N + c0) * DV, rows);
         bf16x8 qf[4], kf[4];
         load_x(a.q + (bh * a.N + c0) * D, rows, lo, h, qf);
         load_x(kr, rows, lo, h, kf);
-        f32x16 PQ[2], PK[2];
-        features2(a, qf, w, fmaf(a.b_norm, sq_norm(qf), a.b_const), live, lo, h, PQ);
-        features2(a, kf, w, fmaf(a.b_norm, sq_norm(kf), a.b_const), live, lo, h, PK);
-        // dnum^T [n x i] = dout^T / D_i and dden_i of the lane's query i = lo
         float inv = 0.f, dden = 0.f;
         if (live) {
             inv = a.tok[2 * (bh * a.N + c0 + lo)];
             dden = a.tok[2 * (bh * a.N + c0 + lo) + 1];
         }
-        const u16* dor = a.dout + (bh * a.N + c0) * DV;
+        uint2 dr[2][4], xe[4];
+        fetch_dout(a.dout + (bh * a.N + c0) * DV, rows, lo, h, dr);
+        if (w >= 2) fetch_row(kr, rows, lo, h, w - 2, xe);
+        stash_v(sm.vt[buf], sm.vs[buf], vx);
+        f32x16 PQ[2], PK[2];
+        features2(a, qf, w, fmaf(a.b_norm, sq_norm(qf), a.b_const), live, lo, h, PQ);
+        features2(a, kf, w, fmaf(a.b_norm, sq_norm(kf), a.b_const), live, lo, h, PK);
+        // dnum^T [n x i] = dout^T / D_i and dden_i of the lane's query i = lo
         f32x16 dn[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 float o[4];
-                load4(dor, DV, lo, rows, 32 * nt + 8 * m + 4 * h, o);
+                unpack4(dr[nt][m], o);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) dn[nt][4 * m + j] = o[j] * inv;
             }
@@ -1633,7 +1684,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
                 for (int m = 0; m < 4; ++m) {
                     const int c0d = 32 * dt + 8 * m + 4 * h;
                     float xv[4], o[4];
-                    load4(kr, D, lo, rows, c0d, xv);
+                    unpack4(xe[m], xv);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) o[j] = a.scale * (s[4 * m + j] - ws * a.scale * xv[j]);
                     store4(a.dx + (bh * a.N + c0) * D, D, lo, c0d, o);

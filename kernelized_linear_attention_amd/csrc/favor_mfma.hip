@@ -33,6 +33,11 @@
 // Modes: SUMS     -- per-segment state increments (no outputs);
 //        CAUSAL   -- chunked recurrence from the carried-in state;
 //        READOUT  -- bidirectional readout against the full summary.
+// The increments also run in k_favor_sums8 (eight symmetric waves), and the
+// backward pass of both forms has matrix-core kernels here too: the
+// bidirectional one with every wave on its own chunks against the totals,
+// the causal one with each workgroup walking its segment and the state
+// split over its waves by feature (see the comments at those kernels).
 #include "launch.hpp"
 
 namespace linattn {

@@ -107,6 +107,22 @@ __device__ __forceinline__ float phi_feature(const Cfg& c, const float* u, float
     }
 }
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
+// every outstanding global load (its fence covers global memory), which
+// drains the prefetches a loop keeps in flight; use this where the waves
+// communicate through LDS alone.
+__device__ __forceinline__ void sync_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(0) as a builtin (expcnt and lgkmcnt at their maxima), so
+// the compiler's load counting sees it, unlike the same instruction in
+// inline asm.  Placed before a loop that uses registers loaded ahead of it:
+// the counting merges the loop entry with the back edge and would otherwise
+// wait for every load in flight, the loop's own prefetches included, at the
+// first use of such a register in every iteration.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);

@@ -28,18 +28,26 @@ template <> struct OmegaRow<bf16_raw> {
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) w[i] = reinterpret_cast<const uint4*>(om + (int64_t)f * D)[i];
     }
-    __device__ __forceinline__ float dot(const float* u) const {
-        float s = 0.f;
+    // omega_f . a and omega_f . b in one pass: each element is unpacked and
+    // used at once, so the unpacked row is never live as a whole (that would
+    // cost 64 registers on top of the state's 64 and halve the occupancy)
+    __device__ __forceinline__ void dot2(const float* a, const float* b, float& da,
+                                         float& db) const {
+        float sa = 0.f, sb = 0.f;
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
             const uint32_t x[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                s = fmaf(__uint_as_float(x[j] << 16), u[8 * i + 2 * j], s);
-                s = fmaf(__uint_as_float(x[j] & 0xffff0000u), u[8 * i + 2 * j + 1], s);
+                const float lo = __uint_as_float(x[j] << 16), hi = __uint_as_float(x[j] & 0xffff0000u);
+                sa = fmaf(lo, a[8 * i + 2 * j], sa);
+                sb = fmaf(lo, b[8 * i + 2 * j], sb);
+                sa = fmaf(hi, a[8 * i + 2 * j + 1], sa);
+                sb = fmaf(hi, b[8 * i + 2 * j + 1], sb);
             }
         }
-        return s;
+        da = sa;
+        db = sb;
     }
 };
 template <> struct OmegaRow<float> {
@@ -48,22 +56,22 @@ template <> struct OmegaRow<float> {
 #pragma unroll
         for (int i = 0; i < D / 4; ++i) w[i] = reinterpret_cast<const float4*>(om + (int64_t)f * D)[i];
     }
-    __device__ __forceinline__ float dot(const float* u) const {
-        float s = 0.f;
+    __device__ __forceinline__ void dot2(const float* a, const float* b, float& da,
+                                         float& db) const {
+        float sa = 0.f, sb = 0.f;
 #pragma unroll
         for (int i = 0; i < D / 4; ++i) {
-            s = fmaf(w[i].x, u[4 * i], s);
-            s = fmaf(w[i].y, u[4 * i + 1], s);
-            s = fmaf(w[i].z, u[4 * i + 2], s);
-            s = fmaf(w[i].w, u[4 * i + 3], s);
+            const float e[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sa = fmaf(e[j], a[4 * i + j], sa);
+                sb = fmaf(e[j], b[4 * i + j], sb);
+            }
         }
-        return s;
+        da = sa;
+        db = sb;
     }
 };
-
-// Barrier for LDS traffic only: __syncthreads() would also wait for the S
-// loads still in flight.
-__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <typename T>
 __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
@@ -94,14 +102,16 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
     if (favor && tid < r) om.load(omega, tid);
 
     // 2. the state stream: float4 e = tid + NT*m is row tid/16 + 16m,
-    //    columns 4*(tid%16) .. +3
+    //    columns 4*(tid%16) .. +3.  Every load is issued unconditionally (rows
+    //    past r re-read the last block of rows, r >= 32 so m_count >= 2): with
+    //    a data-dependent load count the compiler cannot count the loads still
+    //    in flight and waits for the whole stream before the feature map.
     f32x4* S4 = reinterpret_cast<f32x4*>(S + bh * (int64_t)r * DV);
     f32x4 s[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m)
-        if (m < m_count) s[m] = __builtin_nontemporal_load(S4 + tid + NT * m);
-    float zold = 0.f;
-    if (tid < r) zold = __builtin_nontemporal_load(z + bh * r + tid);
+        s[m] = __builtin_nontemporal_load(S4 + tid + NT * (m < m_count ? m : m_count - 1));
+    const float zold = __builtin_nontemporal_load(z + bh * r + (tid < r ? tid : r - 1));
 
     if (tid < D) {
         uq_s[tid] = c.scale * xq;
@@ -124,8 +134,10 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
     if (tid < r) {
         if (favor) {
             // omega . (scale x), from the unscaled row and the scaled input
-            pq = favor_feature(c, om.dot(uq_s), scal_s[0]);
-            pk = favor_feature(c, om.dot(uk_s), scal_s[1]);
+            float dq, dk;
+            om.dot2(uq_s, uk_s, dq, dk);
+            pq = favor_feature(c, dq, scal_s[0]);
+            pk = favor_feature(c, dk, scal_s[1]);
         } else {
             pq = phi_feature<T>(c, uq_s, 0.f, tid, omega);
             pk = phi_feature<T>(c, uk_s, 0.f, tid, omega);

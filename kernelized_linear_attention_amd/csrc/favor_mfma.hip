@@ -98,13 +98,6 @@ __device__ __forceinline__ bool block_segment(const FavorArgs& a, int64_t& bh, i
     return seg >= 0 && g < a.G;
 }
 
-// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
-// every outstanding global load, which would stall on the next chunk's
-// prefetch; here all communication between waves goes through LDS.
-__device__ __forceinline__ void sync_lds() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -749,6 +742,7 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
         vr = load_v(vchunk(0), rows_of(0), tid);
     }
     sync_lds(); // keys of chunk 0 staged
+    wait_all_loads(); // omega's fragments, once, not in every iteration
 
     for (int ci = 0; ci < nck; ++ci) {
         const int rows = rows_of(ci);

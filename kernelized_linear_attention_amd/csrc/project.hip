@@ -45,8 +45,10 @@ __device__ __forceinline__ const bf16_raw* w_row(const ProjArgs& a, int64_t c) {
 
 // Global -> registers: 16-byte piece p of a tile row holds K elements
 // 8p .. 8p+7 of the step; thread t takes pieces t, t + GT, ... of the A tile
-// (row = piece / 8) and of the B tile.  pa / pb: this thread's row starts
-// (NULL for rows past the matrix, which read as zero), fixed for the block.
+// (row = piece / 8) and of the B tile.  pa / pb: this thread's row starts,
+// fixed for the block; rows past the matrix are clamped to its last row (their
+// products are never stored).  Every load is unconditional, so the compiler
+// can count the loads in flight and wait for one K step's alone.
 struct Rows {
     const bf16_raw* pa[AP];
     const bf16_raw* pb[BP];
@@ -56,31 +58,33 @@ __device__ __forceinline__ Rows tile_rows(const ProjArgs& a, int64_t m0, int64_t
     Rows r;
 #pragma unroll
     for (int j = 0; j < AP; ++j) {
-        const int64_t m = m0 + (threadIdx.x + j * GT) / (BK / 8);
-        r.pa[j] = m < a.M ? a.x + m * a.dm + 8 * (threadIdx.x % (BK / 8)) : nullptr;
+        const int64_t m = min<int64_t>(m0 + (threadIdx.x + j * GT) / (BK / 8), a.M - 1);
+        r.pa[j] = a.x + m * a.dm + 8 * (threadIdx.x % (BK / 8));
     }
 #pragma unroll
     for (int j = 0; j < BP; ++j) {
-        const int64_t n = n0 + (threadIdx.x + j * GT) / (BK / 8);
-        r.pb[j] = n < a.cols ? w_row(a, n) + 8 * (threadIdx.x % (BK / 8)) : nullptr;
+        const int64_t n = min<int64_t>(n0 + (threadIdx.x + j * GT) / (BK / 8), a.cols - 1);
+        r.pb[j] = w_row(a, n) + 8 * (threadIdx.x % (BK / 8));
     }
     return r;
 }
 
-__device__ __forceinline__ void fetch(const ProjArgs& a, const Rows& r, int64_t k0,
+// Whether this thread's pieces of K step s lie inside the rows (dm is a
+// multiple of 16, so only the last step can end early); GT is a multiple of
+// BK / 8, so every piece of a thread has the same K.
+__device__ __forceinline__ bool k_inside(const ProjArgs& a, int64_t s) {
+    return s * BK + 8 * (threadIdx.x % (BK / 8)) < a.dm;
+}
+
+// Loads of K step s; pieces past dm read the row start instead (in bounds)
+// and are zeroed before they are stashed.
+__device__ __forceinline__ void fetch(const ProjArgs& a, const Rows& r, int64_t s,
                                       uint4 (&ra)[AP], uint4 (&rb)[BP]) {
-    // GT is a multiple of BK / 8, so every piece of this thread has the same K
-    const bool kin = k0 + 8 * (threadIdx.x % (BK / 8)) < a.dm;
+    const int64_t k0 = k_inside(a, s) ? s * BK : 0;
 #pragma unroll
-    for (int j = 0; j < AP; ++j) {
-        ra[j] = make_uint4(0u, 0u, 0u, 0u);
-        if (kin && r.pa[j]) ra[j] = *reinterpret_cast<const uint4*>(r.pa[j] + k0);
-    }
+    for (int j = 0; j < AP; ++j) ra[j] = *reinterpret_cast<const uint4*>(r.pa[j] + k0);
 #pragma unroll
-    for (int j = 0; j < BP; ++j) {
-        rb[j] = make_uint4(0u, 0u, 0u, 0u);
-        if (kin && r.pb[j]) rb[j] = *reinterpret_cast<const uint4*>(r.pb[j] + k0);
-    }
+    for (int j = 0; j < BP; ++j) rb[j] = *reinterpret_cast<const uint4*>(r.pb[j] + k0);
 }
 
 __device__ __forceinline__ void stash(bf16_raw* st, const uint4 (&ra)[AP], const uint4 (&rb)[BP]) {
@@ -96,6 +100,20 @@ __device__ __forceinline__ void stash(bf16_raw* st, const uint4 (&ra)[AP], const
         const int piece = threadIdx.x + j * GT;
         *reinterpret_cast<uint4*>(Bs + (piece / (BK / 8)) * LDK + 8 * (piece % (BK / 8))) = rb[j];
     }
+}
+
+// Stash of K step s: a last step that ends inside the tile (dm % BK = 16)
+// has its pieces past dm zeroed first (a uniform branch: the masking runs
+// only there).
+__device__ __forceinline__ void stash_step(const ProjArgs& a, int64_t s, int64_t KT, bf16_raw* st,
+                                           uint4 (&ra)[AP], uint4 (&rb)[BP]) {
+    if (s + 1 == KT && a.dm % BK != 0 && !k_inside(a, s)) {
+#pragma unroll
+        for (int j = 0; j < AP; ++j) ra[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < BP; ++j) rb[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    stash(st, ra, rb);
 }
 
 __global__ __launch_bounds__(GT) void k_qkv_project(ProjArgs a) {
@@ -126,12 +144,15 @@ __global__ __launch_bounds__(GT) void k_qkv_project(ProjArgs a) {
     const Rows rows = tile_rows(a, m0, n0);
     // K step s sits in register set (s + 1) % 2 until it is stashed: two steps
     // are in flight while one is multiplied
+    // (steps past the last fetch the last one again: the loads stay the same
+    // in every iteration)
+    auto last = [&](int64_t s) { return s < KT ? s : KT - 1; };
     uint4 ra0[AP], rb0[BP], ra1[AP], rb1[BP];
     fetch(a, rows, 0, ra0, rb0);
-    stash(smem, ra0, rb0);
-    if (KT > 1) fetch(a, rows, BK, ra0, rb0);
-    if (KT > 2) fetch(a, rows, 2 * BK, ra1, rb1);
-    __syncthreads();
+    stash_step(a, 0, KT, smem, ra0, rb0);
+    fetch(a, rows, last(1), ra0, rb0);
+    fetch(a, rows, last(2), ra1, rb1);
+    sync_lds();
     auto mma_step = [&](int64_t kt) {
         const bf16_raw* As = smem + (kt & 1) * STAGE;
         const bf16_raw* Bs = As + BM * LDK;
@@ -156,18 +177,24 @@ __global__ __launch_bounds__(GT) void k_qkv_project(ProjArgs a) {
                                                                         0, 0, 0);
         }
     };
-    for (int64_t kt = 0; kt < KT; kt += 2) {
+    // pairs of steps (no exit between the two halves: the accumulators then
+    // stay in one set of registers), then the last step when KT is odd
+    int64_t kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
         // even step: the next step is in set 0
         mma_step(kt);
-        if (kt + 1 < KT) stash(smem + STAGE, ra0, rb0);
-        if (kt + 3 < KT) fetch(a, rows, (kt + 3) * BK, ra0, rb0);
-        __syncthreads();
-        if (kt + 1 >= KT) break;
+        stash_step(a, kt + 1, KT, smem + STAGE, ra0, rb0);
+        fetch(a, rows, last(kt + 3), ra0, rb0);
+        sync_lds();
         // odd step: the next step is in set 1
         mma_step(kt + 1);
-        if (kt + 2 < KT) stash(smem, ra1, rb1);
-        if (kt + 4 < KT) fetch(a, rows, (kt + 4) * BK, ra1, rb1);
-        __syncthreads();
+        if (kt + 2 < KT) stash_step(a, kt + 2, KT, smem, ra1, rb1);
+        fetch(a, rows, last(kt + 4), ra1, rb1);
+        sync_lds();
+    }
+    if (kt < KT) {
+        mma_step(kt);
+        sync_lds(); // the epilogue reuses the stages
     }
 
     // epilogue: bf16 tile [128][128] through LDS (the A/B buffers are free
@@ -184,7 +211,7 @@ __global__ __launch_bounds__(GT) void k_qkv_project(ProjArgs a) {
                 // the hardware conversion (round to nearest even)
                 Os[row * LDO + col] = __builtin_bit_cast(bf16_raw, (__bf16)acc[i][j][e]);
             }
-    __syncthreads();
+    sync_lds();
     // 128 rows x 2 halves of 64 columns = 256 row pieces of 128 bytes; each
     // thread writes one piece as eight 16-byte stores
     {

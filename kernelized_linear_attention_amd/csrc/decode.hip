@@ -6,18 +6,16 @@
 // The step is a streaming read-modify-write of the float32 state: per head
 // r*dv*4 bytes of S (64 KiB at r = 256) are read and written once, against
 // ~2 flops per byte, so the kernel is bound by HBM bandwidth.  One workgroup
-// per head: every thread issues all of its S loads (16-byte, non-temporal)
-// before it computes its share of phi(q), phi(k), so the feature map runs
-// under the load latency; the new S goes straight back with non-temporal
-// stores and the readout is accumulated from registers.
+// per head (512 or 1024 threads): every thread issues all of its S loads
+// (16-byte, non-temporal) before its share of phi(q), phi(k) is computed, so
+// the feature map runs under the load latency; the new S goes straight back
+// with non-temporal stores and the readout is accumulated from registers.
 #include "launch.hpp"
 
 namespace linattn {
 namespace {
 
-constexpr int NT = 256;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int MAXM = RMAX * DV / 4 / NT; // float4 chunks of S per thread at r = RMAX
 
 // Row f of omega, raw (bfloat16 pairs or float32), loaded early and
 // unpacked only when the feature is computed.
@@ -73,7 +71,10 @@ template <> struct OmegaRow<float> {
     }
 };
 
-template <typename T>
+// NT threads per head (512 or 1024, NT dividing 16 r): the state is split
+// NT ways, 16 r / NT float4 per thread, so few registers hold it and many
+// waves stream it; threads tid < r also compute feature tid.
+template <typename T, int NT>
 __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
                                                const T* __restrict__ k,
                                                const T* __restrict__ v,
@@ -83,11 +84,12 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
     __shared__ float uq_s[D], uk_s[D], v_s[DV];
     __shared__ float pq_s[RMAX], pk_s[RMAX];
     __shared__ float red_s[NT / 64][DV];
-    __shared__ float scal_s[8];
+    constexpr int MAXM = RMAX * DV / 4 / NT; // float4 of S per thread at r = RMAX
+    __shared__ float scal_s[2 + NT / 64]; // |u_q|^2, |u_k|^2, then den per wave
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t bh = blockIdx.x;
     const int r = c.r;
-    const int m_count = r * DV / 4 / NT; // rows of S per thread: r / 16
+    const int m_count = r * DV / 4 / NT; // float4 of S per thread
     const bool favor = c.phi == PHI_FAVOR;
 
     // 1. the feature map's inputs first: vector-memory counters retire in
@@ -101,11 +103,11 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
     OmegaRow<T> om;
     if (favor && tid < r) om.load(omega, tid);
 
-    // 2. the state stream: float4 e = tid + NT*m is row tid/16 + 16m,
-    //    columns 4*(tid%16) .. +3.  Every load is issued unconditionally (rows
-    //    past r re-read the last block of rows, r >= 32 so m_count >= 2): with
-    //    a data-dependent load count the compiler cannot count the loads still
-    //    in flight and waits for the whole stream before the feature map.
+    // 2. the state stream: float4 e = tid + NT*m is row e/16, columns
+    //    4*(tid%16) .. +3.  Every load is issued unconditionally (past m_count
+    //    the last block of rows is read again): with a data-dependent load
+    //    count the compiler cannot count the loads still in flight and waits
+    //    for the whole stream before the feature map.
     f32x4* S4 = reinterpret_cast<f32x4*>(S + bh * (int64_t)r * DV);
     f32x4 s[MAXM];
 #pragma unroll
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
         if (m < m_count) {
-            const int row = tid / 16 + 16 * m;
+            const int row = tid / 16 + (NT / 16) * m;
             const float a = pk_s[row], b = pq_s[row];
             f32x4 x = s[m];
             x.x = fmaf(a, vv.x, x.x);
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
             o.w = fmaf(b, x.w, o.w);
         }
     }
-    // 6. reduce o over the 16 threads sharing columns c4..c4+3: lanes l^16,
+    // 6. reduce o over the threads sharing columns c4..c4+3: lanes l^16,
     //    l^32 within the wave, then the NT/64 waves through LDS.
 #pragma unroll
     for (int off = 16; off < 64; off <<= 1) {
@@ -225,20 +227,31 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
     }
 }
 
-} // namespace
-
-hipError_t launch_decode(const Cfg& c, int dtype, const void* q, const void* k, const void* v,
-                         const void* omega, int64_t BH, float* S, float* z, void* out,
-                         hipStream_t st) {
+template <int NT>
+hipError_t launch_decode_nt(const Cfg& c, int dtype, const void* q, const void* k, const void* v,
+                            const void* omega, int64_t BH, float* S, float* z, void* out,
+                            hipStream_t st) {
     if (dtype == 0)
-        hipLaunchKernelGGL(k_decode<float>, dim3((unsigned)BH), dim3(NT), 0, st, c,
+        hipLaunchKernelGGL((k_decode<float, NT>), dim3((unsigned)BH), dim3(NT), 0, st, c,
                            (const float*)q, (const float*)k, (const float*)v,
                            (const float*)omega, S, z, (float*)out);
     else
-        hipLaunchKernelGGL(k_decode<bf16_raw>, dim3((unsigned)BH), dim3(NT), 0, st, c,
+        hipLaunchKernelGGL((k_decode<bf16_raw, NT>), dim3((unsigned)BH), dim3(NT), 0, st, c,
                            (const bf16_raw*)q, (const bf16_raw*)k, (const bf16_raw*)v,
                            (const bf16_raw*)omega, S, z, (bf16_raw*)out);
     return hipGetLastError();
+}
+
+} // namespace
+
+// 1024 threads per head where they split the state evenly (r a multiple of
+// 64), else 512 (r is a multiple of 32).  Measured at r = 256: 1024 threads
+// stream the state ~10 % faster than 256 (more waves, fewer registers each).
+hipError_t launch_decode(const Cfg& c, int dtype, const void* q, const void* k, const void* v,
+                         const void* omega, int64_t BH, float* S, float* z, void* out,
+                         hipStream_t st) {
+    if (c.r % 64 == 0) return launch_decode_nt<1024>(c, dtype, q, k, v, omega, BH, S, z, out, st);
+    return launch_decode_nt<512>(c, dtype, q, k, v, omega, BH, S, z, out, st);
 }
 
 } // namespace linattn

@@ -94,7 +94,16 @@ def test_causal_from_carried_state(gpu_lib, kind, dtype, r, nu, sum_norm, scale)
     assert_parity(z, rz, tol, "carried z")
 
 
-@pytest.mark.parametrize("kind,dtype,r,nu,sum_norm,scale", MAPS, ids=MAP_IDS)
+# feature widths that are not multiples of 64 take the 512-thread decode kernel
+DECODE_MAPS = MAPS + [
+    ("favor", torch.float32, 96, 1, False, 64 ** -0.25),
+    ("favor", torch.bfloat16, 32, 1, True, 64 ** -0.25),
+    ("favor", torch.bfloat16, 224, 1, False, 64 ** -0.25),
+]
+DECODE_IDS = [f"{k}-{str(dt)[6:]}-r{r}{'-sn' if sn else ''}" for k, dt, r, _, sn, _ in DECODE_MAPS]
+
+
+@pytest.mark.parametrize("kind,dtype,r,nu,sum_norm,scale", DECODE_MAPS, ids=DECODE_IDS)
 def test_decode_step(gpu_lib, kind, dtype, r, nu, sum_norm, scale):
     norm = "none" if kind == "identity" else "attn"
     B, H = 5, 3

@@ -120,52 +120,93 @@ __global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Prefix over segments, one thread per state element, fixed order.  REV: the
-// same over the segments in reverse order (exclusive suffix sums).
+// Prefix over segments, fixed order.  REV: the same over the segments in
+// reverse order (exclusive suffix sums).  The walk is latency-bound (one
+// float per state element and segment, strided by a whole state), so each
+// element's segments are split into P consecutive ranges (P = 1, 2 or 4, by
+// the segment count), one per wave group of the workgroup (NT / P elements
+// per workgroup): every thread loads its range's increments at once and sums
+// them, the ranges' totals are exchanged through LDS, and each thread then
+// writes its range's prefixes from its offset (the totals added in range
+// order: a fixed order).
 // ---------------------------------------------------------------------------
-template <bool REV>
+constexpr int SCAN_BATCH = 16; // increments held in registers per thread
+
+template <bool REV, int P>
 __global__ __launch_bounds__(NT) void k_segment_scan(int r, int64_t G, const float* __restrict__ S0,
                                                      const float* __restrict__ z0,
                                                      float* __restrict__ ws, int prefix_stride,
                                                      float* __restrict__ S_fin,
                                                      float* __restrict__ z_fin,
                                                      float* __restrict__ fin) {
-    constexpr int BATCH = 16;
+    constexpr int EPB = NT / P; // elements per workgroup
+    __shared__ float tot_s[P][EPB];
     const int64_t E = state_elems(r);
-    const int64_t blocks_per_head = (E + NT - 1) / NT;
+    const int64_t blocks_per_head = (E + EPB - 1) / EPB;
     const int64_t bh = blockIdx.x / blocks_per_head;
-    const int64_t e = (blockIdx.x % blocks_per_head) * NT + threadIdx.x;
-    if (e >= E) return;
+    const int el = threadIdx.x % EPB, part = threadIdx.x / EPB;
+    const int64_t e = (blockIdx.x % blocks_per_head) * EPB + el;
+    const bool live = e < E;
+    const int64_t ec = live ? e : E - 1; // in-bounds element for the loads
     const int64_t rdv = (int64_t)r * DV;
-    float run = 0.f;
-    if (S0) run = e < rdv ? S0[bh * rdv + e] : z0[bh * r + (e - rdv)];
-    // REV walks the segments from the last: segment index G-1-i at step i
-    float* p = REV ? ws + (bh * G + G - 1) * E + e : ws + bh * G * E + e;
-    const int64_t step = REV ? -E : E;
-    // batches of independent loads (the scan is latency-bound: one element per
-    // thread), then the fixed-order running sum; the exclusive prefix is
-    // written back only for the segments that read it (every prefix_stride-th;
-    // the stride is a power of two)
+    // this wave's segments [g0, g1) (step i of the walk is segment G-1-i for REV)
+    const int64_t per = (G + P - 1) / P;
+    const int64_t g0 = min<int64_t>(G, part * per), g1 = min<int64_t>(G, g0 + per);
+    auto at = [&](int64_t i) {
+        return REV ? ws + (bh * G + G - 1 - i) * E + ec : ws + (bh * G + i) * E + ec;
+    };
+    // the starting state (any in-bounds value when there is none), then the
+    // first SCAN_BATCH increments of the range, every load unconditional
+    // (clamped to the range's first segment when the range is shorter or
+    // empty; those values are not used)
+    const float* init = S0 ? (ec < rdv ? S0 + bh * rdv + ec : z0 + bh * r + (ec - rdv))
+                           : at(min<int64_t>(g0, G - 1));
+    const float run0 = *init;
+    const int n0 = (int)min<int64_t>(SCAN_BATCH, g1 - g0);
+    float a[SCAN_BATCH];
+#pragma unroll
+    for (int i = 0; i < SCAN_BATCH; ++i) a[i] = *at(min<int64_t>(g0 + (i < n0 ? i : 0), G - 1));
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < SCAN_BATCH; ++i)
+        if (i < n0) tot += a[i];
+    for (int64_t i = g0 + SCAN_BATCH; i < g1; ++i) tot += *at(i);
+    // every load above has landed: the prefix stores below then wait for
+    // nothing (the compiler's counting cannot see that through the
+    // conditional uses, and would wait for each store to complete)
+    wait_all_loads();
+    if (P > 1) {
+        tot_s[part][el] = tot;
+        __syncthreads();
+    }
+    float run = S0 ? run0 : 0.f;
+    for (int u = 0; u < part; ++u) run += tot_s[u][el];
+    // the exclusive prefix is written back only for the segments that read it
+    // (every prefix_stride-th; the stride is a power of two)
     const int64_t pmask = prefix_stride - 1;
-    for (int64_t g0 = 0; g0 < G; g0 += BATCH) {
-        const int n = (int)min<int64_t>(BATCH, G - g0);
-        float a[BATCH];
+    if (live) {
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) a[i] = i < n ? p[(g0 + i) * step] : 0.f;
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            if (i < n) {
-                if (prefix_stride > 0 && ((g0 + i) & pmask) == 0) p[(g0 + i) * step] = run;
+        for (int i = 0; i < SCAN_BATCH; ++i) {
+            if (i < n0) {
+                if (prefix_stride > 0 && ((g0 + i) & pmask) == 0) *at(g0 + i) = run;
                 run += a[i];
             }
         }
+        for (int64_t i = g0 + SCAN_BATCH; i < g1; ++i) {
+            const float x = *at(i);
+            if (prefix_stride > 0 && (i & pmask) == 0) *at(i) = run;
+            run += x;
+        }
     }
-    if (e < rdv) {
-        if (S_fin) S_fin[bh * rdv + e] = run;
-    } else {
-        if (z_fin) z_fin[bh * r + (e - rdv)] = run;
+    // the last range ends with the total
+    if (live && part == P - 1) {
+        if (e < rdv) {
+            if (S_fin) S_fin[bh * rdv + e] = run;
+        } else {
+            if (z_fin) z_fin[bh * r + (e - rdv)] = run;
+        }
+        if (fin) fin[bh * E + e] = run;
     }
-    if (fin) fin[bh * E + e] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -312,6 +353,7 @@ __global__ __launch_bounds__(NT) void k_segment_scan_varlen(int r, int64_t H, in
         float a[BATCH];
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) a[j] = j < n ? p[(gb + j) * E] : 0.f;
+        wait_all_loads(); // else each prefix store below waits for the ones before it
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) {
             if (j < n) {
@@ -381,6 +423,7 @@ __global__ __launch_bounds__(NT) void k_segment_scan_varlen_heads(
         float a[BATCH];
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) a[j] = j < n ? p[(gb + j) * E] : 0.f;
+        wait_all_loads(); // else each prefix store below waits for the ones before it
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) {
             if (j < n && i < num_seqs) {
@@ -640,22 +683,37 @@ hipError_t launch_segment_sums_proj(const Cfg& c, const Proj& P, const void* ome
     return segment_sums_t<bf16_raw, true>(c, nullptr, nullptr, omega, s, sp, ws, P, st);
 }
 
-hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, const float* z0,
-                               float* ws, int prefix_stride, float* S_fin, float* z_fin,
-                               float* fin, hipStream_t st) {
-    const int64_t E = state_elems(r);
-    const dim3 grid((unsigned)(((E + NT - 1) / NT) * s.BH));
-    hipLaunchKernelGGL(k_segment_scan<false>, grid, dim3(NT), 0, st, r, sp.G, S0, z0, ws,
+template <bool REV, int P>
+void segment_scan_p(int r, Shape s, int64_t G, const float* S0, const float* z0, float* ws,
+                    int prefix_stride, float* S_fin, float* z_fin, float* fin, hipStream_t st) {
+    const int64_t epb = NT / P;
+    const dim3 grid((unsigned)(((state_elems(r) + epb - 1) / epb) * s.BH));
+    hipLaunchKernelGGL((k_segment_scan<REV, P>), grid, dim3(NT), 0, st, r, G, S0, z0, ws,
                        prefix_stride, S_fin, z_fin, fin);
+}
+
+// ranges of at most SCAN_BATCH segments where that takes at most 4 of them
+template <bool REV>
+hipError_t segment_scan(int r, Shape s, int64_t G, const float* S0, const float* z0, float* ws,
+                        int prefix_stride, float* S_fin, float* z_fin, float* fin,
+                        hipStream_t st) {
+    if (G > 2 * SCAN_BATCH)
+        segment_scan_p<REV, 4>(r, s, G, S0, z0, ws, prefix_stride, S_fin, z_fin, fin, st);
+    else if (G > SCAN_BATCH)
+        segment_scan_p<REV, 2>(r, s, G, S0, z0, ws, prefix_stride, S_fin, z_fin, fin, st);
+    else
+        segment_scan_p<REV, 1>(r, s, G, S0, z0, ws, prefix_stride, S_fin, z_fin, fin, st);
     return hipGetLastError();
 }
 
+hipError_t launch_segment_scan(int r, Shape s, SegPlan sp, const float* S0, const float* z0,
+                               float* ws, int prefix_stride, float* S_fin, float* z_fin,
+                               float* fin, hipStream_t st) {
+    return segment_scan<false>(r, s, sp.G, S0, z0, ws, prefix_stride, S_fin, z_fin, fin, st);
+}
+
 hipError_t launch_segment_suffix_scan(int r, Shape s, SegPlan sp, float* ws, hipStream_t st) {
-    const int64_t E = state_elems(r);
-    const dim3 grid((unsigned)(((E + NT - 1) / NT) * s.BH));
-    hipLaunchKernelGGL(k_segment_scan<true>, grid, dim3(NT), 0, st, r, sp.G, nullptr, nullptr, ws,
-                       1, nullptr, nullptr, nullptr);
-    return hipGetLastError();
+    return segment_scan<true>(r, s, sp.G, nullptr, nullptr, ws, 1, nullptr, nullptr, nullptr, st);
 }
 
 hipError_t launch_varlen_plan(const int32_t* cu_seqlens, int64_t num_seqs, int64_t total,

@@ -1252,7 +1252,8 @@ __device__ __forceinline__ void features2(const CausalArgs& a, const bf16x8 (&xf
 
 __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
     __shared__ CausalSmem sm;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // wave index, uniform
     const int lo = lane & 31, h = lane >> 5;
     const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
     const int64_t t0 = g * a.seg_len, t1 = min<int64_t>(t0 + a.seg_len, a.N);
@@ -1282,24 +1283,59 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
     for (int f = threadIdx.x; f < R; f += NTC) sm.z[f] = st[(int64_t)R * DV + f];
     __syncthreads(); // omega^T table and z
 
-    for (int ci = 0; ci < nck; ++ci) {
-        const int64_t c0 = t0 + (int64_t)L * ci;
-        const int rows = (int)min<int64_t>(L, t1 - c0);
+    // The chunk's global loads, issued one chunk ahead into one of two
+    // register sets (two chunks per iteration, one per set, so no set is
+    // copied while its loads are in flight); every load is unconditional, at
+    // a row clamped into the chunk, and lanes past the end are zeroed when
+    // the values are used.
+    // (dout and the epilogue's q are loaded at the top of their own chunk,
+    // and used after the first barrier: registers for a second set of them
+    // would spill)
+    struct QueryLoads {
+        uint4 vx;           // V: row threadIdx/8, columns 8 (threadIdx%8) ..
+        bf16x8 qf[4], kf[4];
+    };
+    auto chunk_at = [&](int ci, int64_t& c0, int& rows) {
+        c0 = t0 + (int64_t)L * ci;
+        rows = (int)min<int64_t>(L, t1 - c0);
+    };
+    auto issue = [&](int ci, QueryLoads& ld) {
+        int64_t c0;
+        int rows;
+        chunk_at(min(ci, nck - 1), c0, rows);
+        const int jv = min((int)threadIdx.x >> 3, rows - 1);
+        ld.vx = *reinterpret_cast<const uint4*>(a.v + (bh * a.N + c0 + jv) * DV + (threadIdx.x & 7) * 8);
+        load_x(a.q + (bh * a.N + c0) * D, rows, lo, h, ld.qf);
+        load_x(a.k + (bh * a.N + c0) * D, rows, lo, h, ld.kf);
+    };
+
+    auto body = [&](int ci, QueryLoads& cur, QueryLoads& nxt) {
+        int64_t c0;
+        int rows;
+        chunk_at(ci, c0, rows);
         const bool live = lo < rows;
         const int buf = ci & 1;
-        // every load of the chunk first, so that they share one round trip
-        const u16* qr = a.q + (bh * a.N + c0) * D;
-        const uint4 vx = fetch_v(a.v + (bh * a.N + c0) * DV, rows);
-        bf16x8 qf[4], kf[4];
-        load_x(qr, rows, lo, h, qf);
-        load_x(a.k + (bh * a.N + c0) * D, rows, lo, h, kf);
+        const int t = min(lo, rows - 1);
         uint2 dr[2][4], xe[4];
-        fetch_dout(a.dout + (bh * a.N + c0) * DV, rows, lo, h, dr);
-        if (w < 2) fetch_row(qr, rows, lo, h, w, xe);
-        stash_v(sm.vt[buf], sm.vs[buf], vx);
+        {
+            const u16* dor = a.dout + (bh * a.N + c0 + t) * DV;
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    dr[nt][m] = *reinterpret_cast<const uint2*>(dor + 32 * nt + 8 * m + 4 * h);
+            const u16* xr = a.q + (bh * a.N + c0 + t) * D + 32 * min(w, 1) + 4 * h;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) xe[m] = *reinterpret_cast<const uint2*>(xr + 8 * m);
+        }
+        const bool vlive = ((int)threadIdx.x >> 3) < rows;
+        stash_v(sm.vt[buf], sm.vs[buf], vlive ? cur.vx : make_uint4(0u, 0u, 0u, 0u));
         f32x16 PQ[2], PK[2];
-        features2(a, qf, w, fmaf(a.b_norm, sq_norm(qf), a.b_const), live, lo, h, PQ);
-        features2(a, kf, w, fmaf(a.b_norm, sq_norm(kf), a.b_const), live, lo, h, PK);
+        features2(a, cur.qf, w, fmaf(a.b_norm, sq_norm(cur.qf), a.b_const), live, lo, h, PQ);
+        features2(a, cur.kf, w, fmaf(a.b_norm, sq_norm(cur.kf), a.b_const), live, lo, h, PK);
+        // the next chunk's loads, now that this chunk's are consumed (the
+        // last chunk's are issued again past the end and not used)
+        issue(ci + 1, nxt);
 
         // partial readout num^T [n x t] = S^T phi(Q)^T, den, and A1^T [j x t] = phi(K) phi(Q)^T over F_w
         f32x16 num[2] = {zero16(), zero16()}, a1 = zero16();
@@ -1326,7 +1362,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         }
         den = half_sum(den);
         if (h == 0) sm.tokv[w][0][lo] = den;
-        __syncthreads(); // B1: partials and V tables of the chunk
+        sync_lds(); // B1: partials and V tables of the chunk
 
         // full sums (every wave, redundantly)
         den = 0.f;
@@ -1359,7 +1395,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
                 num[nt] = mfma(lds8(vt + (32 * nt + lo) * LDT + 16 * kk + 8 * h), af, num[nt]);
         }
 
-        // dnum^T [n x t], dden
+        // dnum^T [n x t], dden (zero past the chunk's end)
         const float inv = attn ? 1.f / fmaxf(den, a.eps) : 1.f;
         f32x16 dn[2];
         float dot = 0.f;
@@ -1368,7 +1404,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 float o[4];
-                unpack4(dr[nt][m], o);
+                unpack4(live ? dr[nt][m] : make_uint2(0u, 0u), o);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     dot = fmaf(o[j], num[nt][4 * m + j], dot);
@@ -1432,7 +1468,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
             sm.dpart[w][1][i][lane] = du[1][i];
         }
         if (h == 0) sm.tokv[w][2][lo] = wsum;
-        __syncthreads(); // B2: du partials
+        sync_lds(); // B2: du partials
         if (w < 2) {
             // wave dt sums d-tile dt and stores dq = scale (du - wsum u)
             f32x16 s = zero16();
@@ -1489,6 +1525,15 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
             zs = half_sum(zs);
             if (h == 0) sm.z[64 * w + 32 * ft + lo] += zs;
         }
+    };
+
+    if (nck > 0) {
+        QueryLoads A, B;
+        issue(0, A);
+        for (int ci = 0; ci < nck; ci += 2) {
+            body(ci, A, B);
+            if (ci + 1 < nck) body(ci + 1, B, A);
+        }
     }
     // the segment's backward increments
     float* dst = a.inc + (bh * a.G + g) * state_elems(R);
@@ -1506,7 +1551,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
 
 __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
     __shared__ CausalSmem sm;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // wave index, uniform
     const int lo = lane & 31, h = lane >> 5;
     const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
     const int64_t t0 = g * a.seg_len, t1 = min<int64_t>(t0 + a.seg_len, a.N);
@@ -1532,30 +1578,61 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
     for (int f = threadIdx.x; f < R; f += NTC) sm.z[f] = st[(int64_t)R * DV + f];
     __syncthreads(); // omega^T table and g
 
-    for (int cr = 0; cr < nck; ++cr) {
+    // The chunk's global loads, issued one chunk ahead into one of two
+    // register sets (the loop runs two chunks per iteration, one per set, so
+    // no set is copied while its loads are in flight).  Every load is
+    // unconditional, at a row clamped into the chunk: lanes past the end are
+    // zeroed when the values are used.
+    struct KeyLoads {
+        uint4 vx;           // V: row threadIdx/8, columns 8 (threadIdx%8) ..
+        bf16x8 qf[4], kf[4];
+        float inv, dden;
+        uint2 dr[2][4];     // dout of the lane's query
+        uint2 xe[4];        // k of the lane's key (waves 2, 3), for dk
+    };
+    auto chunk_at = [&](int cr, int64_t& c0, int& rows) {
         const int ci = nck - 1 - cr; // chunks last to first
-        const int64_t c0 = t0 + (int64_t)L * ci;
-        const int rows = (int)min<int64_t>(L, t1 - c0);
+        c0 = t0 + (int64_t)L * ci;
+        rows = (int)min<int64_t>(L, t1 - c0);
+    };
+    auto issue = [&](int cr, KeyLoads& ld) {
+        int64_t c0;
+        int rows;
+        chunk_at(min(cr, nck - 1), c0, rows);
+        const int jv = min((int)threadIdx.x >> 3, rows - 1), t = min(lo, rows - 1);
+        ld.vx = *reinterpret_cast<const uint4*>(a.v + (bh * a.N + c0 + jv) * DV + (threadIdx.x & 7) * 8);
+        load_x(a.q + (bh * a.N + c0) * D, rows, lo, h, ld.qf);
+        load_x(a.k + (bh * a.N + c0) * D, rows, lo, h, ld.kf);
+        ld.inv = a.tok[2 * (bh * a.N + c0 + t)];
+        ld.dden = a.tok[2 * (bh * a.N + c0 + t) + 1];
+        const u16* dor = a.dout + (bh * a.N + c0 + t) * DV;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                ld.dr[nt][m] = *reinterpret_cast<const uint2*>(dor + 32 * nt + 8 * m + 4 * h);
+    };
+    auto issue_xe = [&](int cr, KeyLoads& ld) {
+        int64_t c0;
+        int rows;
+        chunk_at(min(cr, nck - 1), c0, rows);
+        const u16* xr = a.k + (bh * a.N + c0 + min(lo, rows - 1)) * D + 32 * max(w - 2, 0) + 4 * h;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ld.xe[m] = *reinterpret_cast<const uint2*>(xr + 8 * m);
+    };
+
+    auto body = [&](int cr, KeyLoads& cur, KeyLoads& nxt) {
+        int64_t c0;
+        int rows;
+        chunk_at(cr, c0, rows);
         const bool live = lo < rows;
         const int buf = cr & 1;
-        // every load of the chunk first, so that they share one round trip
-        const u16* kr = a.k + (bh * a.N + c0) * D;
-        const uint4 vx = fetch_v(a.v + (bh * a.N + c0) * DV, rows);
-        bf16x8 qf[4], kf[4];
-        load_x(a.q + (bh * a.N + c0) * D, rows, lo, h, qf);
-        load_x(kr, rows, lo, h, kf);
-        float inv = 0.f, dden = 0.f;
-        if (live) {
-            inv = a.tok[2 * (bh * a.N + c0 + lo)];
-            dden = a.tok[2 * (bh * a.N + c0 + lo) + 1];
-        }
-        uint2 dr[2][4], xe[4];
-        fetch_dout(a.dout + (bh * a.N + c0) * DV, rows, lo, h, dr);
-        if (w >= 2) fetch_row(kr, rows, lo, h, w - 2, xe);
-        stash_v(sm.vt[buf], sm.vs[buf], vx);
+        const bool vlive = ((int)threadIdx.x >> 3) < rows;
+        stash_v(sm.vt[buf], sm.vs[buf], vlive ? cur.vx : make_uint4(0u, 0u, 0u, 0u));
         f32x16 PQ[2], PK[2];
-        features2(a, qf, w, fmaf(a.b_norm, sq_norm(qf), a.b_const), live, lo, h, PQ);
-        features2(a, kf, w, fmaf(a.b_norm, sq_norm(kf), a.b_const), live, lo, h, PK);
+        features2(a, cur.qf, w, fmaf(a.b_norm, sq_norm(cur.qf), a.b_const), live, lo, h, PQ);
+        features2(a, cur.kf, w, fmaf(a.b_norm, sq_norm(cur.kf), a.b_const), live, lo, h, PK);
+        const float inv = live ? cur.inv : 0.f, dden = live ? cur.dden : 0.f;
         // dnum^T [n x i] = dout^T / D_i and dden_i of the lane's query i = lo
         f32x16 dn[2];
 #pragma unroll
@@ -1563,10 +1640,13 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 float o[4];
-                unpack4(dr[nt][m], o);
+                unpack4(cur.dr[nt][m], o);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) dn[nt][4 * m + j] = o[j] * inv;
             }
+        // the next chunk's loads, now that this chunk's are consumed (the
+        // last chunk's are issued again past the end and not used)
+        issue(cr + 1, nxt);
         if (h == 0) sm.tokv[w][1][lo] = dden; // this wave's copy, by query
 
         // partials over F_w: dv^T [n x j] = G^T phi(K)^T, B1 [i x j] = phi(Q) phi(K)^T
@@ -1586,35 +1666,42 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
             sm.part[w][1][i][lane] = dvp[1][i];
             sm.part[w][2][i][lane] = b1[i];
         }
-        __syncthreads(); // B1: partials, dden copies and V tables of the chunk
+        sync_lds(); // B1: partials, dden copies and V tables of the chunk
 
         const u16* vs = sm.vs[buf];
         f32x16 dnr[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) dnr[nt] = transpose32(dn[nt], eye); // [i x n]
-        if (w < 2) {
-            // wave nt: dv^T tile nt = sum of partials + dnum^T B1 (masked: query i >= key j)
+        // wave nt < 2: dv^T tile nt = sum of partials + dnum^T B1 (masked:
+        // query i >= key j); the tile index is a constant in each branch (a
+        // runtime index into the register array dnr becomes a select per
+        // element and register)
+        auto dv_tile = [&](const f32x16& dsel, int nt) {
             f32x16 s = zero16();
             f32x16 bm = zero16();
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    s[i] += sm.part[u][w][i][lane];
+                    s[i] += sm.part[u][nt][i][lane];
                     bm[i] += sm.part[u][2][i][lane];
                 }
 #pragma unroll
             for (int i = 0; i < 16; ++i) bm[i] = (8 * (i >> 2) + (i & 3) >= keep_thr) ? bm[i] : 0.f;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) s = mfma(pack8(dnr[w], 8 * kk), pack8(bm, 8 * kk), s);
+            for (int kk = 0; kk < 2; ++kk) s = mfma(pack8(dsel, 8 * kk), pack8(bm, 8 * kk), s);
             if (live) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const float o[4] = {s[4 * m], s[4 * m + 1], s[4 * m + 2], s[4 * m + 3]};
-                    store4(a.dv + (bh * a.N + c0) * DV, DV, lo, 32 * w + 8 * m + 4 * h, o);
+                    store4(a.dv + (bh * a.N + c0) * DV, DV, lo, 32 * nt + 8 * m + 4 * h, o);
                 }
             }
-        }
+        };
+        if (w == 0)
+            dv_tile(dnr[0], 0);
+        else if (w == 1)
+            dv_tile(dnr[1], 1);
         // A3 [i x j] = dnum_i . v_j + dden_i, masked (i >= j)
         f32x16 a3 = zero16();
 #pragma unroll
@@ -1666,7 +1753,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
             sm.dpart[w][1][i][lane] = du[1][i];
         }
         if (h == 0) sm.tokv[w][2][lo] = wsum;
-        __syncthreads(); // B2: du partials
+        sync_lds(); // B2: du partials
         if (w >= 2) {
             // wave 2 + dt: dk tile dt = scale (du - wsum u)
             const int dt = w - 2;
@@ -1683,13 +1770,14 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
                 for (int m = 0; m < 4; ++m) {
                     const int c0d = 32 * dt + 8 * m + 4 * h;
                     float xv[4], o[4];
-                    unpack4(xe[m], xv);
+                    unpack4(cur.xe[m], xv);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) o[j] = a.scale * (s[4 * m + j] - ws * a.scale * xv[j]);
                     store4(a.dx + (bh * a.N + c0) * D, D, lo, c0d, o);
                 }
             }
         }
+        issue_xe(cr + 1, nxt);
         // suffix update for the earlier chunks: G[F_w] += phi(Q)^T dnum, g += phi(Q)^T dden
 #pragma unroll
         for (int ft = 0; ft < 2; ++ft) {
@@ -1705,6 +1793,16 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
                 gsum = fmaf(PQt[ft][i], sm.tokv[w][1][8 * (i >> 2) + 4 * h + (i & 3)], gsum);
             gsum = half_sum(gsum);
             if (h == 0) sm.z[64 * w + 32 * ft + lo] += gsum;
+        }
+    };
+
+    if (nck > 0) {
+        KeyLoads A, B;
+        issue(0, A);
+        issue_xe(0, A);
+        for (int cr = 0; cr < nck; cr += 2) {
+            body(cr, A, B);
+            if (cr + 1 < nck) body(cr + 1, B, A);
         }
     }
 }

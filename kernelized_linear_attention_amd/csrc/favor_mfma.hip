@@ -910,7 +910,8 @@ __device__ __forceinline__ void store_dx(const BwdArgs& a, const u16* xrow0, u16
 
 __global__ __launch_bounds__(NTB) void k_bwd_query_favor(BwdArgs a) {
     __shared__ BwdTables tb;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // wave index, uniform
     const int lo = lane & 31, h = lane >> 5;
     const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
     build_tables(tb, a.st + bh * state_elems(R), a.omega, true);
@@ -1022,7 +1023,8 @@ __global__ __launch_bounds__(NTB) void k_bwd_query_favor(BwdArgs a) {
 
 __global__ __launch_bounds__(NTB) void k_bwd_key_favor(BwdArgs a) {
     __shared__ BwdTables tb;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // wave index, uniform
     const int lo = lane & 31, h = lane >> 5;
     const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
     build_tables(tb, a.st + bh * state_elems(R), a.omega, false);

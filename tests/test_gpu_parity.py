@@ -139,6 +139,30 @@ def test_segment_count_and_chunk_do_not_change_results(gpu_lib):
             assert_parity(S, rS, 2e-2, f"S n_seg={n_seg}")
 
 
+@pytest.mark.parametrize("n_seg", [9, 20, 79])
+def test_many_segments_split_the_scan_into_ranges(gpu_lib, n_seg):
+    """The segment scan splits each element's segments into 1, 2 or 4 ranges
+    by their count (here 18, 40 and 158 half segments on the matrix-core
+    route, the last with ranges longer than the register batch): prefill,
+    final state and the causal backward (suffix scan over 79 segments) against
+    the oracle, and bitwise repeatability."""
+    c = Case(131, 1, 2, 5000, "favor", torch.bfloat16, r=256)
+    kw = c.gkw(scale=64 ** -0.25)
+    ref, rS, rz = oracle.causal(c.qh, c.kh, c.vh, "favor", **c.okw(scale=64 ** -0.25))
+    out, S, z = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, "favor", n_seg=n_seg, **kw)
+    out2, S2, z2 = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, "favor", n_seg=n_seg, **kw)
+    assert torch.equal(out, out2) and torch.equal(S, S2) and torch.equal(z, z2)
+    assert_parity(out, ref, 2e-2, f"out n_seg={n_seg}")
+    assert_parity(S, rS, 2e-2, f"S n_seg={n_seg}")
+    assert_parity(z, rz, 2e-2, f"z n_seg={n_seg}")
+    if n_seg == 79:
+        do = dev(inputs.normal((1, 2, 5000, 64), 131, inputs.T_DOUT), torch.bfloat16)
+        got = gpu_lib.lin_attn_causal_backward(c.q, c.k, c.v, do, "favor", n_seg=n_seg, **kw)
+        gref = oracle.causal_backward(c.qh, c.kh, c.vh, host(do), "favor",
+                                      **c.okw(scale=64 ** -0.25))
+        _assert_grads(got, gref, 2e-2, f"causal backward n_seg={n_seg}")
+
+
 def test_bitwise_deterministic(gpu_lib):
     c = Case(107, 1, 8, 2000, "favor", torch.bfloat16, r=256)
     kw = c.gkw(scale=64 ** -0.25)

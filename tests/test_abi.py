@@ -165,6 +165,20 @@ def test_outside_gpu_coverage_is_unsupported():
     assert decode(params("favor", r=272)) == UNSUPPORTED
 
 
+def test_sizes_past_the_grid_limits_are_unsupported():
+    """Flattened grids stay within 32 bits: more than 2^24 heads in a batch,
+    a B*H product past 2^31 or more than 2^40 tokens is refused before any
+    launch (and B*H = 2^24 exactly is still accepted)."""
+    p = params()
+    assert causal(p, B=1 << 13, H=1 << 12) == UNSUPPORTED        # 2^25 heads
+    assert causal(p, B=1 << 31, H=2) == UNSUPPORTED              # product past 2^31
+    assert bidir(p, B=1, H=1, N=(1 << 40) + 1) == UNSUPPORTED
+    assert decode(p, B=1 << 20, H=1 << 5) == UNSUPPORTED
+    assert varlen(p, num_seqs=1 << 20, H=1 << 5) == UNSUPPORTED
+    # the limit itself is inside the coverage: only the workspace is short
+    assert causal(p, B=1 << 12, H=1 << 12, ws_bytes=0) == WORKSPACE
+
+
 def test_small_workspace_is_rejected():
     p = params()
     need = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 1, 2, 100, 64, 64)

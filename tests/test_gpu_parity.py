@@ -753,3 +753,63 @@ def test_causal_backward_matrix_core_route(gpu_lib, N, n_seg, norm):
         return
     ref = oracle.causal_backward(c.qh, c.kh, c.vh, host(do), "favor", **c.okw(**kw))
     _assert_grads(got, ref, 2e-2, f"causal backward N={N} n_seg={n_seg} {norm}")
+
+
+# ---------------------------------------------------------------------------
+# Randomized configurations: a fixed-seed draw of shapes, maps, dtypes, segment
+# counts and readouts through every forward form, decode and both backwards
+# ---------------------------------------------------------------------------
+
+def _random_configs(n, seed=20261202):
+    import random
+    rng = random.Random(seed)
+    maps = [("favor", 256), ("favor", 128), ("favor", 96), ("favor", 32), ("elu1", 64),
+            ("dpfp", 128), ("dpfp", 256)]
+    out = []
+    for _ in range(n):
+        kind, r = rng.choice(maps)
+        out.append(dict(kind=kind, r=r, nu=r // 128 if kind == "dpfp" else 1,
+                        dtype=rng.choice(["bf16", "f32"]), B=rng.randint(1, 3),
+                        H=rng.randint(1, 3),
+                        N=rng.choice([1, 7, 31, 32, 33, 95, 200, 513, 1500, 3000]),
+                        n_seg=rng.choice([0, 0, 1, 2, 5, 13, 40]),
+                        sum_norm=kind != "favor" and rng.random() < 0.3,
+                        norm=rng.choice(["attn", "attn", "none"])))
+    return out
+
+
+RANDOM_CONFIGS = _random_configs(40)
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM_CONFIGS)))
+def test_random_configuration(gpu_lib, i):
+    cfg = RANDOM_CONFIGS[i]
+    kind, r, nu, N = cfg["kind"], cfg["r"], cfg["nu"], cfg["N"]
+    dtype = DT[cfg["dtype"]]
+    c = Case(3000 + i, cfg["B"], cfg["H"], N, kind, dtype, r=r, nu=nu)
+    kw = dict(scale=64 ** -0.25 if kind == "favor" else 1.0, norm=cfg["norm"],
+              sum_norm=cfg["sum_norm"])
+    tol = TOL[dtype]
+    out, S, z = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, kind, n_seg=cfg["n_seg"],
+                                                **c.gkw(**kw))
+    ro, rS, rz = oracle.causal(c.qh, c.kh, c.vh, kind, **c.okw(**kw))
+    assert_parity(out, ro, tol, f"{cfg} causal out")
+    assert_parity(S, rS, tol, f"{cfg} causal S")
+    assert_parity(z, rz, tol, f"{cfg} causal z")
+    bo = gpu_lib.lin_attn_bidir(c.q, c.k, c.v, kind, n_seg=cfg["n_seg"], **c.gkw(**kw))
+    rb, _, _ = oracle.bidir(c.qh, c.kh, c.vh, kind, **c.okw(**kw))
+    assert_parity(bo, rb, tol, f"{cfg} bidir out")
+    q1, k1, v1 = (t[:, :, 0].contiguous() for t in (c.q, c.k, c.v))
+    S2, z2 = S.clone(), z.clone()
+    o1 = gpu_lib.lin_attn_decode_step(q1, k1, v1, S2, z2, kind, omega=c.omega, nu=nu, **kw)
+    rd, rS2, rz2 = oracle.decode(host(q1), host(k1), host(v1), host(S), host(z), kind,
+                                 omega=c.omega_h, nu=nu, **kw)
+    assert_parity(o1, rd, tol, f"{cfg} decode out")
+    assert_parity(S2, rS2, tol, f"{cfg} decode S")
+    if 1 < N <= 1500:
+        do = dev(inputs.normal((cfg["B"], cfg["H"], N, 64), 3000 + i, inputs.T_DOUT), dtype)
+        for form, fn, ofn in (("causal", gpu_lib.lin_attn_causal_backward, oracle.causal_backward),
+                              ("bidir", gpu_lib.lin_attn_bidir_backward, oracle.bidir_backward)):
+            got = fn(c.q, c.k, c.v, do, kind, n_seg=cfg["n_seg"], **c.gkw(**kw))
+            ref = ofn(c.qh, c.kh, c.vh, host(do), kind, **c.okw(**kw))
+            _assert_grads(got, ref, tol, f"{cfg} {form} backward")

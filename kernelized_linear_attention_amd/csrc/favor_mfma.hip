@@ -167,6 +167,16 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sum over the eight consecutive lanes 8q .. 8q + 7 (every lane of the group
+// gets the same bits): lane ^ 1 and lane ^ 2 within each quad, then the
+// other quad of the group through the half-row mirror (lane i <-> 7 - i).
+__device__ __forceinline__ float row8_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+    return x;
+}
+
 // |x_t|^2 for t = lo from its fragments (the two lane halves hold
 // complementary halves of the row); bf16 products are exact in float32.
 __device__ __forceinline__ float sq_norm(const bf16x8 (&f)[4]) {
@@ -243,7 +253,8 @@ struct Smem {
     float red[2][NW][NW - 1][2][64][4]; // partial numerator blocks [buf][owner][sender slot][j][lane]
     float dint[2][NW][L];          // denominators over F_g (readout + intra block) [buf][g][token]
     float z[R];                    // producer-private: z_{c-1}, by feature
-    float kb[NW][L];               // producer-private: key biases by token
+    float kb[3][L];                // producer-shared: key biases by token, ring by chunk
+    float qb[3][L];                // producer-shared: query biases by token, ring by chunk
     u16 ot[NW][16 * 32];           // consumer-private: finished output block, bf16 rows
 };
 
@@ -300,20 +311,13 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
     auto rows_of = [&](int c) { return (int)min<int64_t>(L, t1 - t0 - (int64_t)L * c); };
 
     // projections of one chunk: P_K (token 8(i/4) + 4h + i%4, feature
-    // f0 + 32 nt + lo) with the key biases in LDS, P_Q^T (feature
-    // f0 + 32 mt + 8(i/4) + 4h + i%4, token lo) with the query bias in bq.
+    // f0 + 32 nt + lo) and P_Q^T (feature f0 + 32 mt + 8(i/4) + 4h + i%4,
+    // token lo); the per-token biases of both come from LDS.
     // Each tile of the next chunk is projected right after this chunk's
     // exponentials have consumed the same tile, so the matrix core runs
     // under the next tile's exponentials.
     bf16x8 qf[4], kf[4], vr;
     f32x16 PK[2], PQ[2];
-    float bq = 0.f;
-    // keys past the end of the segment get bias -inf: exp2 gives exactly 0,
-    // so they add nothing to S, z or the intra-chunk block
-    auto key_bias = [&](int rows) {
-        const float bk = lo < rows ? fmaf(a.b_norm, sq_norm(kf), a.b_const) : -INFINITY;
-        sm.kb[p][lo] = bk; // both lane halves write the same value
-    };
     auto project_k = [&](int nt) {
         f32x16 c = zero16();
 #pragma unroll
@@ -336,9 +340,31 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
         if (HAS_Q) qr = load_block(chunk_ptr(qb, c), rows_of(c), ptid);
         if (HAS_K) kr = load_block(chunk_ptr(kb, c), rows_of(c), ptid);
     };
+    // the per-token biases of a chunk are computed once, as it is staged:
+    // the eight threads of a row sum their squares; keys past the end of the
+    // segment get bias -inf (exp2 gives exactly 0, so they add nothing to S,
+    // z or the intra-chunk block)
+    auto row_sq = [&](const bf16x8& blk) {
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 x = {blk[e], blk[e + 1]};
+            sq = __builtin_amdgcn_fdot2_f32_bf16(x, x, sq, false);
+        }
+        return row8_sum(sq);
+    };
     auto stage_store = [&](int c) {
-        if (HAS_Q) sm.xq[c % 3][ptid] = qr;
-        if (HAS_K) sm.xk[c % 3][ptid] = kr;
+        const int t = ptid >> 3;
+        if (HAS_Q) {
+            sm.xq[c % 3][ptid] = qr;
+            const float sq = row_sq(qr);
+            if ((ptid & 7) == 0) sm.qb[c % 3][t] = fmaf(a.b_norm, sq, a.b_const);
+        }
+        if (HAS_K) {
+            sm.xk[c % 3][ptid] = kr;
+            const float sq = row_sq(kr);
+            if ((ptid & 7) == 0) sm.kb[c % 3][t] = t < rows_of(c) ? fmaf(a.b_norm, sq, a.b_const) : -INFINITY;
+        }
     };
     auto frags = [&](int c) {
         if (HAS_Q) lds_x(sm.xq[c % 3], lo, h, qf);
@@ -359,12 +385,10 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
     if (nck > 0) {
         frags(0);
         if (HAS_K) {
-            key_bias(rows_of(0));
             project_k(0);
             project_k(1);
         }
         if (HAS_Q) {
-            bq = fmaf(a.b_norm, sq_norm(qf), a.b_const);
             project_q(0);
             project_q(1);
         }
@@ -376,6 +400,9 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
             // the next chunk (the last one again after the end: its projections
             // are then unused, and every iteration keeps the same shape)
             const int cn = min(ci + 1, nck - 1);
+            // this chunk's query biases first: in the readout there is no key
+            // phase to hide the read before the exponentials
+            const float bq = HAS_Q ? sm.qb[ci % 3][lo] : 0.f;
             frags(cn);
             if (ci + 2 < nck) stage_store(ci + 2);
             stage_load(min(ci + 3, nck - 1));
@@ -388,8 +415,7 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
                 f32x4 kbias[4]; // biases of the tokens 8 j + 4 h + (0..3)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    kbias[j] = *reinterpret_cast<const f32x4*>(&sm.kb[p][8 * j + 4 * h]);
-                key_bias(rows_of(cn)); // after this chunk's biases are read
+                    kbias[j] = *reinterpret_cast<const f32x4*>(&sm.kb[ci % 3][8 * j + 4 * h]);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     f32x16& c = PK[nt];
@@ -407,7 +433,6 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
 
             // ---- phi(Q) and its denominators against z_{c-1} ------------------------
             if (HAS_Q) {
-                const float bq_next = fmaf(a.b_norm, sq_norm(qf), a.b_const);
                 float den[2] = {0.f, 0.f};
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
@@ -427,7 +452,6 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
                     project_q(mt);
                 }
                 X.den[p][lo] = half_sum(den[0] + den[1]); // both lane halves hold the full sum
-                bq = bq_next;
             }
 
             // ---- z[F_g] += column sums of phi(K_c), after the queries read z_{c-1} ----
@@ -709,7 +733,7 @@ template <bool ZW>
 __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
     __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LDV];
     __shared__ bf16x8 ks_s[2][256];
-    __shared__ __attribute__((aligned(16))) float kb_s[8][L];
+    __shared__ __attribute__((aligned(16))) float kb_s[2][L]; // key biases by chunk parity
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lo = lane & 31, h = lane >> 5;
@@ -735,8 +759,24 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
     // stagers hold the keys of chunk c + 1 and the values of chunk c in
     // registers at the top of iteration c
     bf16x8 kr, vr;
+    // the key bias of a chunk is computed once, by the stagers, from the
+    // blocks they hold: the eight threads of a row sum their squares (keys
+    // past the end of the segment get bias -inf, so exp2 gives 0)
+    auto stage_bias = [&](const bf16x8& blk, int c) {
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 x = {blk[e], blk[e + 1]};
+            sq = __builtin_amdgcn_fdot2_f32_bf16(x, x, sq, false);
+        }
+        sq = row8_sum(sq);
+        const int t = tid >> 3;
+        if ((tid & 7) == 0) kb_s[c & 1][t] = t < rows_of(c) ? fmaf(a.b_norm, sq, a.b_const) : -INFINITY;
+    };
     if (nck > 0 && stager) {
-        ks_s[0][tid] = load_block(kchunk(0), rows_of(0), tid);
+        const bf16x8 k0 = load_block(kchunk(0), rows_of(0), tid);
+        ks_s[0][tid] = k0;
+        stage_bias(k0, 0);
         const int c1 = min(1, nck - 1);
         kr = load_block(kchunk(c1), rows_of(c1), tid);
         vr = load_v(vchunk(0), rows_of(0), tid);
@@ -750,20 +790,19 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
             // past the end: the last chunk again, so every iteration has the same loads
             const int c1 = min(ci + 1, nck - 1), c2 = min(ci + 2, nck - 1);
             ks_s[(ci + 1) & 1][tid] = kr;
+            if (ci + 1 < nck) stage_bias(kr, ci + 1);
             store_vt(vt_s[ci & 1], tid, vr);
             kr = load_block(kchunk(c2), rows_of(c2), tid);
             vr = load_v(vchunk(c1), rows_of(c1), tid);
         }
         bf16x8 kf[4];
         lds_x(ks_s[ci & 1], lo, h, kf);
-        // keys past the end of the segment get bias -inf (exp2 gives 0)
-        kb_s[w][lo] = lo < rows ? fmaf(a.b_norm, sq_norm(kf), a.b_const) : -INFINITY;
         f32x16 c = zero16();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) c = mfma(kf[ks], om[ks], c); // token 8(i/4)+4h+i%4, feature f0+lo
         f32x4 kbias[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kbias[j] = *reinterpret_cast<const f32x4*>(&kb_s[w][8 * j + 4 * h]);
+        for (int j = 0; j < 4; ++j) kbias[j] = *reinterpret_cast<const f32x4*>(&kb_s[ci & 1][8 * j + 4 * h]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
         const bf16x8 fk0 = pack8(c, 0), fk1 = pack8(c, 8);

@@ -256,6 +256,7 @@ struct Smem {
     float kb[3][L];                // producer-shared: key biases by token, ring by chunk
     float qb[3][L];                // producer-shared: query biases by token, ring by chunk
     u16 ot[NW][16 * 32];           // consumer-private: finished output block, bf16 rows
+    float rden[NW][L];             // consumer-private: 1 / max(den, eps) by token
 };
 
 // B operand of a transposition through the matrix core: k-slot e of lane
@@ -489,19 +490,26 @@ __device__ __forceinline__ void finish_block(const FavorArgs& a, Smem& sm, const
     // every LDS read first, then one wait: the partials and denominators were
     // all written before the barrier
     const float(&red)[NW][NW - 1][2][64][4] = sm.red[c & 1];
-    f32x4 part[NW - 1][2], dpart[2][NW];
+    f32x4 part[NW - 1][2];
+    float dg[NW];
 #pragma unroll
     for (int s = 0; s < NW - 1; ++s)
 #pragma unroll
         for (int j = 0; j < 2; ++j) part[s][j] = *reinterpret_cast<const f32x4*>(&red[W][s][j][lane][0]);
     if (a.norm == NORM_ATTN) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) // rows 16 OQ + 8 j + 4 h + (0..3)
-                dpart[j][w2] = *reinterpret_cast<const f32x4*>(&sm.dint[c & 1][w2][16 * OQ + 8 * j + 4 * h]);
+        for (int w2 = 0; w2 < NW; ++w2) dg[w2] = sm.dint[c & 1][w2][lo]; // token lo's four groups
     }
     __builtin_amdgcn_sched_barrier(0);
+    // the denominators: lane lo sums token lo's four groups once, and the
+    // rows this lane finishes (16 OQ + 8 j + 4 h + 0..3) come back from LDS
+    // (the same wave wrote them, so LDS order suffices)
+    f32x4 rd[2];
+    if (a.norm == NORM_ATTN) {
+        if (h == 0) sm.rden[W][lo] = __builtin_amdgcn_rcpf(fmaxf((dg[0] + dg[1]) + (dg[2] + dg[3]), a.eps));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) rd[j] = *reinterpret_cast<const f32x4*>(&sm.rden[W][16 * OQ + 8 * j + 4 * h]);
+    }
     float own[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -511,11 +519,7 @@ __device__ __forceinline__ void finish_block(const FavorArgs& a, Smem& sm, const
     }
     if (a.norm == NORM_ATTN) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float dsum = (dpart[i >> 2][0][i & 3] + dpart[i >> 2][1][i & 3]) +
-                               (dpart[i >> 2][2][i & 3] + dpart[i >> 2][3][i & 3]);
-            own[i] *= __builtin_amdgcn_rcpf(fmaxf(dsum, a.eps));
-        }
+        for (int i = 0; i < 8; ++i) own[i] *= rd[i >> 2][i & 3];
     }
     u16* ot = sm.ot[W];
 #pragma unroll

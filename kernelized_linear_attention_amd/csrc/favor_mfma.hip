@@ -727,9 +727,10 @@ __global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
 // owns the 32 features F_w = [32w, 32w + 32) and, per chunk, projects the
 // keys on its rows of omega, takes the exponentials and adds
 // phi(K)[:, F_w]^T V to its slice of S in MFMA accumulators.  Nothing is
-// reduced across waves; the chunk's keys and V^T are loaded once per
-// workgroup by waves 0..3 and staged in LDS (one barrier per chunk), and
-// every wave has the same mix of matrix-core and vector work.
+// reduced across waves; the chunk's keys, their per-token biases and V^T
+// are loaded (computed) once per workgroup by waves 0..3 and staged in LDS
+// (one barrier per chunk), and every wave has the same mix of matrix-core
+// and vector work.
 constexpr int NT8 = 512;
 // ZW: the z sum weighted per token by a.zw (a separate instantiation, so the
 // plain one keeps its registers).

@@ -78,12 +78,10 @@ int launch_status(hipError_t e) { return e == hipSuccess ? LIN_ATTN_OK : LIN_ATT
 // The kernel family a validated call runs on, and its segmentation.
 bool use_mfma(const lin_attn_params* p) { return favor_mfma_supported(make_cfg(p), p->dtype); }
 
-// The matrix-core increment kernel fits two workgroups per CU while the
-// output kernel fits one: it sums over half segments (32-token multiples).
+// Both matrix-core kernels (increments and outputs) fit two workgroups per
+// CU: the increments are summed over whole segments.
 SegPlan plan_for(const lin_attn_params* p, int64_t BH, int64_t N) {
-    SegPlan sp = plan_segments(BH, N, p->n_seg, use_mfma(p) ? TARGET_BLOCKS_MFMA : TARGET_BLOCKS_VALU);
-    if (use_mfma(p)) sp.sub = 2;
-    return sp;
+    return plan_segments(BH, N, p->n_seg, use_mfma(p) ? TARGET_BLOCKS_MFMA : TARGET_BLOCKS_VALU);
 }
 
 hipError_t segment_sums(const lin_attn_params* p, const Cfg& c, const void* k, const void* v,

@@ -1,43 +1,24 @@
 // favor_mfma.hip -- FAVOR+ attention on the matrix cores (bfloat16 inputs,
 // r = 256 features, d = dv = 64, float32 accumulation and state).
 //
-// One workgroup handles one sequence segment of one head, in chunks of 32
-// tokens (one MFMA tile: the intra-chunk block is a single masked 32 x 32
-// tile).  The 256 features are split into four groups F_g = [64g, 64g + 64),
-// and each group has two waves on the same SIMD:
-//   producer g  (waves 4..7) keeps the rows of omega for F_g in registers and
-//               turns chunk c into its random features, one chunk ahead of
-//               the consumer: the projections and the exponentials
-//                 P_Q^T = omega_g Q_c^T,  P_K = K_c omega_g^T,
-//                 phi   = exp2(P * s*log2(e) + per-token bias)
-//               (the bias holds -s^2 |x|^2 / 2 and -log2(sqrt(r)); x unscaled,
-//               s = scale), the partial denominators phi(Q_c) z_{c-1}[F_g] and
-//               the masked intra-chunk block (phi(Q_c) phi(K_c)^T)|_{F_g};
-//               it also keeps z[F_g] and stages V_c^T in LDS;
-//   consumer g  (waves 0..3) keeps its state slice S[F_g, :] in float32
-//               accumulators and, for chunk c - 1, forms the partial numerator
-//                 phi(Q) S_{c-1}[F_g] + (masked block) V
-//               and the update S[F_g] += phi(K)^T V; the four partial
-//               numerators are summed through LDS and divided by the summed
-//               denominators.
-// Producers are VALU-heavy (two exponentials per token and feature) and
-// consumers MFMA-heavy, so the pair on a SIMD keeps both units busy.  The
-// hand-off buffers in LDS are double-buffered by chunk, which leaves one
-// workgroup barrier per chunk (Kernel Zoo sec. 4.2 / 5.4 map; causal
-// recurrence of sec. 1.3 in chunked form, see generic.hip).
+// Forward outputs (k_favor_fused): one workgroup of four waves handles one
+// sequence segment of one head, in chunks of 32 tokens (one MFMA tile: the
+// intra-chunk block is a single masked 32 x 32 tile), two workgroups per CU.
+// Wave w owns the 64 features F_w = [64w, 64w + 64) and does all of their
+// work: projections and exponentials of the chunk's keys and queries
+// (Kernel Zoo sec. 4.2 / 5.4 map), its share of the masked intra-chunk
+// block, its partial readout against S_{c-1}[F_w] and the update
+// S[F_w] += phi(K_c)^T V_c (sec. 1.3 recurrence in chunked form).  The four
+// partial numerators and denominators are summed through LDS; each wave
+// finishes a quarter of the chunk's output.
+// Segment increments (k_favor_sums8): eight waves of 32 features each.
 // Every contraction is a v_mfma_f32_32x32x16_bf16; the MFMA accumulator
 // layout of one product is reused as an operand of the next where the
 // contraction index allows it (a k-slot permutation applied to both
-// operands).
-//
-// Modes: SUMS     -- per-segment state increments (no outputs);
-//        CAUSAL   -- chunked recurrence from the carried-in state;
-//        READOUT  -- bidirectional readout against the full summary.
-// The increments also run in k_favor_sums8 (eight symmetric waves), and the
-// backward pass of both forms has matrix-core kernels here too: the
-// bidirectional one with every wave on its own chunks against the totals,
-// the causal one with each workgroup walking its segment and the state
-// split over its waves by feature (see the comments at those kernels).
+// operands).  The backward pass of both forms has matrix-core kernels here
+// too: the bidirectional one with every wave on its own chunks against the
+// totals, the causal one with each workgroup walking its segment and the
+// state split over its waves by feature (see the comments at those kernels).
 #include "launch.hpp"
 
 namespace linattn {
@@ -51,13 +32,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NW = 4;         // feature groups of 64: one producer and one consumer wave each
-constexpr int NT = 2 * 64 * NW;
+constexpr int NW = 4;         // feature groups of 64, one wave each
 constexpr int R = 256;
 constexpr int L = 32;         // chunk length: one 32-token MFMA tile
 constexpr int LDV = 40;       // LDS row stride (bf16) of the V^T tile [64 n][32 t]: 80 B
 
-enum { MODE_SUMS = 0, MODE_CAUSAL = 1, MODE_READOUT = 2 };
+enum { MODE_CAUSAL = 1, MODE_READOUT = 2 };
 
 struct FavorArgs {
     const u16* q;
@@ -72,7 +52,7 @@ struct FavorArgs {
     float b_const;  // log2(1 / sqrt(r))
     float eps;
     int norm;
-    float* state;   // SUMS: increments out; CAUSAL: carried-in states; READOUT: summaries
+    float* state;   // increments out (k_favor_sums8); carried-in states (causal); summaries (readout)
     int64_t st_bh;
     int64_t st_g;
     u16* out;
@@ -81,7 +61,7 @@ struct FavorArgs {
     const int64_t* order; // segment-major dispatch order or NULL (see SegPlan)
     int64_t osub;
     int64_t BH;
-    const float* zw;      // SUMS: per-token weights of the z sum [BH, N], or NULL (weight 1)
+    const float* zw;      // k_favor_sums8: per-token weights of the z sum [BH, N], or NULL (weight 1)
 };
 
 // The (head, segment) this workgroup runs; false when it runs nothing.
@@ -236,29 +216,6 @@ __device__ __forceinline__ void lds_x(const bf16x8* xs, int lo, int h, bf16x8 (&
     for (int ks = 0; ks < 4; ++ks) f[ks] = xs[xs_index(lo, 2 * ks + h)];
 }
 
-// One chunk's hand-off from the producers to the consumers, per feature
-// group g; every operand is stored lane-linear, so each side moves it with one
-// 16-byte LDS access per lane.
-struct XBuf {
-    bf16x8 fq[NW][2][2][64]; // phi(Q) as the A operand of the readout [g][feature tile][kk][lane]
-    bf16x8 fk[NW][2][2][64]; // phi(K) as the A operand of the update  [g][feature tile][kk][lane]
-    float den[NW][L];        // phi(Q) z_{c-1} over F_g, by token
-};
-
-struct Smem {
-    XBuf xb[2];                    // double-buffered by chunk
-    bf16x8 xq[3][256];             // producer-shared: swizzled q chunks, three in flight
-    bf16x8 xk[3][256];             // producer-shared: swizzled k chunks
-    u16 vt[2][DV * LDV];           // V^T of the chunk, double-buffered
-    float red[2][NW][NW - 1][2][64][4]; // partial numerator blocks [buf][owner][sender slot][j][lane]
-    float dint[2][NW][L];          // denominators over F_g (readout + intra block) [buf][g][token]
-    float z[R];                    // producer-private: z_{c-1}, by feature
-    float kb[3][L];                // producer-shared: key biases by token, ring by chunk
-    float qb[3][L];                // producer-shared: query biases by token, ring by chunk
-    u16 ot[NW][16 * 32];           // consumer-private: finished output block, bf16 rows
-    float rden[NW][L];             // consumer-private: 1 / max(den, eps) by token
-};
-
 // B operand of a transposition through the matrix core: k-slot e of lane
 // (n, h) is 1 where token 16 kk + 8(e/4) + 4h + e%4 equals n.  With an
 // operand X whose lanes are features and whose k-slots are those tokens,
@@ -271,23 +228,104 @@ __device__ __forceinline__ bf16x8 eye_frag(int kk, int lo, int h) {
     return r;
 }
 
-// Producer of feature group p.  The projections of chunk c + 1 are issued
-// during iteration c, tile by tile between the exponentials of chunk c, so
-// that the exponentials of chunk c + 1 start as soon as the next iteration
-// does.  q and k reach the producers through LDS (loaded once per
-// workgroup, three chunks ahead of their exponentials).  Every global load
-// in the loop is issued unconditionally (past the last chunk it repeats the
-// last one), so the number of loads in flight is the same on every path and
-// each wait covers exactly the loads it needs: a data-dependent load count
-// makes the compiler drain all of them at the top of the loop.
-template <int MODE>
-__device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, int lane, int64_t bh,
-                                         int64_t g, int64_t t0, int64_t t1, int nck) {
-    constexpr bool HAS_K = MODE != MODE_READOUT;
-    constexpr bool HAS_Q = MODE != MODE_SUMS;
+// ---------------------------------------------------------------------------
+// Outputs with symmetric waves: k_favor_fused<MODE> (MODE_CAUSAL, MODE_READOUT).
+//
+// One workgroup of four waves per (head, segment), two workgroups per CU, so
+// that each SIMD runs two independent waves (of different segments).  Wave w
+// owns the 64 features F_w = [64w, 64w + 64) and does all of their work for
+// every 32-token chunk c: the projections P_K = K_c omega_w^T and
+// P_Q^T = omega_w Q_c^T, both exponentials, the partial denominators
+// phi(Q_c) z_{c-1}[F_w], the masked intra-chunk block over F_w, the partial
+// numerator phi(Q_c) S_{c-1}[F_w] + (block) V_c, and the update
+// S[F_w] += phi(K_c)^T V_c (Kernel Zoo sec. 1.3 recurrence in chunked form,
+// the maps of sec. 4.2 / 5.4).  The four partial numerators and
+// denominators meet in LDS; each wave then finishes a quarter of the chunk's
+// output.  q, k and V^T are staged once per workgroup (one 16-byte block of
+// each per thread), one chunk ahead; the partial buffers are double-buffered
+// by chunk, so one workgroup barrier per chunk suffices.
+// Layouts: S[mt][nt] element i is
+// S[f0 + 32 mt + 8 (i/4) + 4 h + i%4][32 nt + lo]; phi(K) leaves the
+// projection with features on lanes (the A operand of the update) and is
+// transposed through the matrix core for the intra-chunk block; phi(Q) leaves
+// it with tokens on lanes (the A operand of the readout).
+// ---------------------------------------------------------------------------
+constexpr int NTF = 64 * NW;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over rows [row0, row0 + rows) of an output [*, DV] in
+// bfloat16: word 3 selects 32-bit raw accesses with range checking, so
+// stores at byte offsets past rows * 2 DV are discarded by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rows(u16* out, int64_t row0, int rows) {
+    return __builtin_amdgcn_make_buffer_rsrc(out + row0 * DV, 0, rows * DV * 2, 0x00020000);
+}
+
+struct SmemF {
+    bf16x8 xq[2][256];                  // swizzled q chunk [chunk parity]
+    bf16x8 xk[2][256];                  // swizzled k chunk
+    u16 vt[2][DV * LDV];                // V^T of the chunk
+    float red[2][NW][NW - 1][2][64][4]; // partial numerator blocks [parity][owner][sender][j][lane]
+    float dpart[2][L][NW];              // partial denominators [parity][token][group]
+    float qb[2][L];                     // query biases by token
+    float kb[2][L];                     // key biases by token (-inf past the segment end)
+    float z[R];                         // z_{c-1} by feature (wave w reads and writes F_w only)
+    bf16x8 eye[2][64];                  // identity operands of the transposition, by lane
+};
+
+// Columns [32 (W%2) + 16 (W/2), +16) of the chunk's output, all 32 tokens,
+// finished by wave W: its own partial (accumulator elements 8 (W/2) .. +7 of
+// tile W%2: token lo, columns 4h + {0..3} and 8 + 4h + {0..3} of the block)
+// plus the three others from LDS, times the reciprocal of token lo's
+// denominator, stored as two 8-byte pieces per lane.
+template <int W, int NORM>
+__device__ __forceinline__ void finish_fused(const FavorArgs& a, SmemF& sm, const f32x16 (&acc)[2],
+                                             int lane, int slot, int64_t bh, int64_t c0, int rows) {
+    constexpr int ON = W & 1, OQ = W >> 1;
     const int lo = lane & 31, h = lane >> 5;
-    const int f0 = 64 * p;
-    const int ptid = 64 * p + lane; // 0 .. 255 over the producers: V^T staging
+    f32x4 part[NW - 1][2];
+#pragma unroll
+    for (int s = 0; s < NW - 1; ++s)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) part[s][j] = *reinterpret_cast<const f32x4*>(&sm.red[slot][W][s][j][lane][0]);
+    f32x4 dg;
+    if (NORM == NORM_ATTN) dg = *reinterpret_cast<const f32x4*>(&sm.dpart[slot][lo][0]);
+    float own[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        own[i] = acc[ON][8 * OQ + i];
+#pragma unroll
+        for (int s = 0; s < NW - 1; ++s) own[i] += part[s][i >> 2][i & 3];
+    }
+    if (NORM == NORM_ATTN) {
+        const float rd = __builtin_amdgcn_rcpf(fmaxf((dg[0] + dg[1]) + (dg[2] + dg[3]), a.eps));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) own[i] *= rd;
+    }
+    // unconditional stores through a buffer resource that covers exactly the
+    // chunk's rows: the hardware drops the rows past the segment end, so no
+    // lane branches around the store and the count of memory operations in
+    // flight stays the same on every path (a branch here makes the next
+    // chunk's wait for its prefetched loads also wait for these stores)
+    const __amdgpu_buffer_rsrc_t orsrc = out_rows(a.out, bh * a.N + c0, rows);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const bf16x2 p0 = {(__bf16)own[4 * j], (__bf16)own[4 * j + 1]};
+        const bf16x2 p1 = {(__bf16)own[4 * j + 2], (__bf16)own[4 * j + 3]};
+        const u32x2 v2 = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+        __builtin_amdgcn_raw_buffer_store_b64(v2, orsrc, lo * (DV * 2) + 2 * (32 * ON + 16 * OQ + 4 * h + 8 * j), 0, 0);
+    }
+}
+
+// The whole segment for wave W (features F_W); every wave-dependent index is
+// a compile-time constant.
+template <int MODE, int NORM, int W>
+__device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int tid, int64_t bh,
+                                           int64_t g, int64_t t0, int64_t t1, int nck) {
+    constexpr bool CAUSAL = MODE == MODE_CAUSAL;
+    constexpr int f0 = 64 * W;
+    const int lane = tid & 63, lo = lane & 31, h = lane >> 5;
+    auto rows_of = [&](int c) { return (int)min<int64_t>(L, t1 - t0 - (int64_t)L * c); };
 
     bf16x8 om[2][4]; // omega[f0 + 32 t + lo][16 ks + 8 h ..]
 #pragma unroll
@@ -295,56 +333,47 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) om[t][ks] = omega_frag(a.omega, f0, t, ks, lo, h);
 
-    float zreg[2] = {0.f, 0.f}; // z[f0 + 32 nt + lo]
-    if (MODE != MODE_SUMS) {
-        const float* st = a.state + bh * a.st_bh + g * a.st_g;
+    // carried-in state (causal) or the summaries (readout)
+    const float* st = a.state + bh * a.st_bh + g * a.st_g;
+    f32x16 S[2][2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) zreg[nt] = st[(int64_t)R * DV + f0 + 32 * nt + lo];
-        if (h == 0) {
-            sm.z[f0 + lo] = zreg[0];
-            sm.z[f0 + 32 + lo] = zreg[1];
-        }
-    }
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int f = f0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+                S[mt][nt][i] = st[(int64_t)f * DV + 32 * nt + lo];
+            }
+    float zreg[2]; // z[f0 + 32 nt + lo]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) zreg[nt] = st[(int64_t)R * DV + f0 + 32 * nt + lo];
+    // both lane halves store the same value at the same address
+    sm.z[f0 + lo] = zreg[0];
+    sm.z[f0 + 32 + lo] = zreg[1];
+    // identity operands of the transposition (read back once per chunk: kept
+    // in LDS rather than in eight registers)
+    if (CAUSAL && W < 2) sm.eye[W][lane] = eye_frag(W, lo, h);
+    // causal mask of the diagonal tile: element i of lane (lo, h) pairs query
+    // lo with key 8(i/4) + 4h + i%4, kept when 8(i/4) + i%4 <= lo - 4h
+    const int keep_thr = lo - 4 * h;
 
-    const u16* qb = a.q + bh * a.N * D;
-    const u16* kb = a.k + bh * a.N * D;
-    const u16* vb = a.v + bh * a.N * DV;
-    auto rows_of = [&](int c) { return (int)min<int64_t>(L, t1 - t0 - (int64_t)L * c); };
-
-    // projections of one chunk: P_K (token 8(i/4) + 4h + i%4, feature
-    // f0 + 32 nt + lo) and P_Q^T (feature f0 + 32 mt + 8(i/4) + 4h + i%4,
-    // token lo); the per-token biases of both come from LDS.
-    // Each tile of the next chunk is projected right after this chunk's
-    // exponentials have consumed the same tile, so the matrix core runs
-    // under the next tile's exponentials.
-    bf16x8 qf[4], kf[4], vr;
-    f32x16 PK[2], PQ[2];
-    auto project_k = [&](int nt) {
-        f32x16 c = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) c = mfma(kf[ks], om[nt][ks], c);
-        PK[nt] = c;
-    };
-    auto project_q = [&](int mt) {
-        f32x16 c = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) c = mfma(om[mt][ks], qf[ks], c);
-        PQ[mt] = c;
-    };
-    // q and k chunks are loaded once for the four producers (one 16-byte
-    // block per thread) into a ring of three swizzled LDS copies: chunk c + 2
-    // is stored during iteration c from registers loaded one iteration
-    // earlier, and the projections of chunk c + 1 read their fragments
-    auto chunk_ptr = [&](const u16* base, int c) { return base + (t0 + (int64_t)L * c) * D; };
-    bf16x8 qr, kr; // staged blocks
+    const u16* qg = a.q + bh * a.N * D;
+    const u16* kg = a.k + bh * a.N * D;
+    const u16* vg = a.v + bh * a.N * DV;
+    auto chunk_ptr = [&](const u16* base, int c, int width) { return base + (t0 + (int64_t)L * c) * width; };
+    // staging: thread tid holds one 16-byte block of the chunk's q, k and v
+    bf16x8 qr, kr, vr;
     auto stage_load = [&](int c) {
-        if (HAS_Q) qr = load_block(chunk_ptr(qb, c), rows_of(c), ptid);
-        if (HAS_K) kr = load_block(chunk_ptr(kb, c), rows_of(c), ptid);
+        qr = load_block(chunk_ptr(qg, c, D), rows_of(c), tid);
+        if (CAUSAL) {
+            kr = load_block(chunk_ptr(kg, c, D), rows_of(c), tid);
+            vr = load_v(chunk_ptr(vg, c, DV), rows_of(c), tid);
+        }
     };
-    // the per-token biases of a chunk are computed once, as it is staged:
-    // the eight threads of a row sum their squares; keys past the end of the
-    // segment get bias -inf (exp2 gives exactly 0, so they add nothing to S,
-    // z or the intra-chunk block)
+    // the per-token biases of a chunk, once per workgroup: the eight threads
+    // of a row sum their squares; keys past the segment end get -inf (exp2
+    // gives 0, so they add nothing to S, z or the intra-chunk block)
     auto row_sq = [&](const bf16x8& blk) {
         float sq = 0.f;
 #pragma unroll
@@ -355,372 +384,232 @@ __device__ __forceinline__ void producer(const FavorArgs& a, Smem& sm, int p, in
         return row8_sum(sq);
     };
     auto stage_store = [&](int c) {
-        const int t = ptid >> 3;
-        if (HAS_Q) {
-            sm.xq[c % 3][ptid] = qr;
-            const float sq = row_sq(qr);
-            if ((ptid & 7) == 0) sm.qb[c % 3][t] = fmaf(a.b_norm, sq, a.b_const);
-        }
-        if (HAS_K) {
-            sm.xk[c % 3][ptid] = kr;
-            const float sq = row_sq(kr);
-            if ((ptid & 7) == 0) sm.kb[c % 3][t] = t < rows_of(c) ? fmaf(a.b_norm, sq, a.b_const) : -INFINITY;
+        const int s = c & 1, t = tid >> 3;
+        sm.xq[s][tid] = qr;
+        const float sq = row_sq(qr);
+        if ((tid & 7) == 0) sm.qb[s][t] = fmaf(a.b_norm, sq, a.b_const);
+        if (CAUSAL) {
+            sm.xk[s][tid] = kr;
+            const float sk = row_sq(kr);
+            if ((tid & 7) == 0) sm.kb[s][t] = t < rows_of(c) ? fmaf(a.b_norm, sk, a.b_const) : -INFINITY;
+            store_vt(sm.vt[s], tid, vr);
         }
     };
-    auto frags = [&](int c) {
-        if (HAS_Q) lds_x(sm.xq[c % 3], lo, h, qf);
-        if (HAS_K) lds_x(sm.xk[c % 3], lo, h, kf);
+
+    // projections of one 32 x 32 tile from the chunk's fragments
+    bf16x8 qf[4], kf[4];
+    auto project_k = [&](int t) {
+        f32x16 c = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) c = mfma(kf[ks], om[t][ks], c);
+        return c;
+    };
+    auto project_q = [&](int t) {
+        f32x16 c = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) c = mfma(om[t][ks], qf[ks], c);
+        return c;
+    };
+    // P0, P1: the first two projection tiles of the chunk about to be
+    // processed (keys when causal, else queries), issued one iteration early
+    f32x16 P0, P1;
+    auto first_tiles = [&](int s) {
+        lds_x(sm.xq[s], lo, h, qf);
+        if (CAUSAL) {
+            lds_x(sm.xk[s], lo, h, kf);
+            P0 = project_k(0);
+            P1 = project_k(1);
+        } else {
+            P0 = project_q(0);
+            P1 = project_q(1);
+        }
     };
 
     if (nck > 0) {
         stage_load(0);
         stage_store(0);
-        if (nck > 1) {
-            stage_load(1);
-            stage_store(1);
-        }
-        stage_load(min(2, nck - 1));
-        if (HAS_K) vr = load_v(vb + t0 * DV, rows_of(0), ptid);
+        stage_load(min(1, nck - 1));
     }
-    sync_lds(); // chunks 0 and 1 staged (the consumers wait here once as well)
-    if (nck > 0) {
-        frags(0);
-        if (HAS_K) {
-            project_k(0);
-            project_k(1);
-        }
-        if (HAS_Q) {
-            project_q(0);
-            project_q(1);
-        }
-    }
+    sync_lds(); // chunk 0 staged, z in LDS
 
+    f32x16 acc[2]; // partial numerator of the chunk, transposed (see below)
     for (int ci = 0; ci < nck; ++ci) {
-        {
-            XBuf& X = sm.xb[ci & 1];
-            // the next chunk (the last one again after the end: its projections
-            // are then unused, and every iteration keeps the same shape)
-            const int cn = min(ci + 1, nck - 1);
-            // this chunk's query biases first: in the readout there is no key
-            // phase to hide the read before the exponentials
-            const float bq = HAS_Q ? sm.qb[ci % 3][lo] : 0.f;
-            frags(cn);
-            if (ci + 2 < nck) stage_store(ci + 2);
-            stage_load(min(ci + 3, nck - 1));
+        const int slot = ci & 1;
+        first_tiles(slot);
+        // the next chunk into the other slot (its readers finished at the last
+        // barrier), then the loads of the one after it (the last chunk again
+        // past the end, so every iteration issues the same loads)
+        if (ci + 1 < nck) stage_store(ci + 1);
+        stage_load(min(ci + 2, nck - 1));
+        // the previous chunk's output, stored here rather than at the end of
+        // its iteration: the loads waited for at the top of the next iteration
+        // then never have a store issued just before their wait (loads and
+        // stores share one in-order counter, and with both in flight every
+        // wait becomes a wait for all of them)
+        if (ci > 0) finish_fused<W, NORM>(a, sm, acc, lane, slot ^ 1, bh, t0 + (int64_t)L * (ci - 1), rows_of(ci - 1));
 
-            // ---- phi(K): exponentials, column sums, hand-off -----------------------
-            float zpart[2] = {0.f, 0.f};
-            if (HAS_K) {
-                store_vt(sm.vt[ci & 1], ptid, vr);
-                vr = load_v(vb + (t0 + (int64_t)L * cn) * DV, rows_of(cn), ptid);
-                f32x4 kbias[4]; // biases of the tokens 8 j + 4 h + (0..3)
+        // ---- exponentials, one 32 x 32 tile at a time: the query tiles are
+        // projected on the matrix core while the key tiles are exponentiated
+        bf16x8 fk[2][2], fq[2][2];
+        float zpart[2] = {0.f, 0.f};
+        float dacc[2] = {0.f, 0.f};
+        const float bq = sm.qb[slot][lo];
+        // phi(K) tile nt: exponentials, bf16 operands, column sums (z sums the
+        // bfloat16 features that also enter S)
+        auto key_tile = [&](f32x16& c, int nt) {
+            f32x4 kbias[4]; // biases of the tokens 8 j + 4 h + (0..3)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    kbias[j] = *reinterpret_cast<const f32x4*>(&sm.kb[ci % 3][8 * j + 4 * h]);
+            for (int j = 0; j < 4; ++j) kbias[j] = *reinterpret_cast<const f32x4*>(&sm.kb[slot][8 * j + 4 * h]);
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x16& c = PK[nt];
+            for (int i = 0; i < 16; ++i) c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
+            fk[nt][0] = pack8(c, 0);
+            fk[nt][1] = pack8(c, 8);
+            zpart[nt] = sum8(fk[nt][0]) + sum8(fk[nt][1]);
+        };
+        // phi(Q) tile mt and its denominators against z_{c-1}
+        auto query_tile = [&](f32x16& c, int mt) {
+            f32x4 zq[4]; // z_{c-1} of the features f0 + 32 mt + 8 j + 4 h + (0..3)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, kbias[i >> 2][i & 3]));
-                    const bf16x8 k0 = pack8(c, 0), k1 = pack8(c, 8);
-                    X.fk[p][nt][0][lane] = k0;
-                    X.fk[p][nt][1][lane] = k1;
-                    // z sums the bfloat16 features that also enter S
-                    zpart[nt] = sum8(k0) + sum8(k1);
-                    project_k(nt);
-                }
+            for (int j = 0; j < 4; ++j) zq[j] = *reinterpret_cast<const f32x4*>(&sm.z[f0 + 32 * mt + 8 * j + 4 * h]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float y = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
+                c[i] = y;
+                if (NORM == NORM_ATTN) dacc[i & 1] = fmaf(y, zq[i >> 2][i & 3], dacc[i & 1]);
             }
-
-            // ---- phi(Q) and its denominators against z_{c-1} ------------------------
-            if (HAS_Q) {
-                float den[2] = {0.f, 0.f};
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    f32x16& c = PQ[mt];
-                    f32x4 zq[4]; // z_{c-1} of the features f0 + 32 mt + 8 j + 4 h + (0..3)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        zq[j] = *reinterpret_cast<const f32x4*>(&sm.z[f0 + 32 * mt + 8 * j + 4 * h]);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float y = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
-                        c[i] = y;
-                        den[i & 1] = fmaf(y, zq[i >> 2][i & 3], den[i & 1]);
-                    }
-                    X.fq[p][mt][0][lane] = pack8(c, 0);
-                    X.fq[p][mt][1][lane] = pack8(c, 8);
-                    project_q(mt);
-                }
-                X.den[p][lo] = half_sum(den[0] + den[1]); // both lane halves hold the full sum
-            }
-
-            // ---- z[F_g] += column sums of phi(K_c), after the queries read z_{c-1} ----
-            if (HAS_K) {
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    zreg[nt] += half_sum(zpart[nt]);
-                    if (MODE == MODE_CAUSAL) sm.z[f0 + 32 * nt + lo] = zreg[nt];
-                }
-            }
-
-
+            fq[mt][0] = pack8(c, 0);
+            fq[mt][1] = pack8(c, 8);
+        };
+        if (CAUSAL) {
+            key_tile(P0, 0);
+            P0 = project_q(0);
+            key_tile(P1, 1);
+            P1 = project_q(1);
         }
-        sync_lds(); // chunk ci handed over; the consumers are done with chunk ci - 1
-    }
-    sync_lds(); // the consumers' last chunk
+        query_tile(P0, 0);
+        query_tile(P1, 1);
+        float den = NORM == NORM_ATTN ? half_sum(dacc[0] + dacc[1]) : 0.f; // token lo, both halves
+        __builtin_amdgcn_sched_barrier(0);
 
-    if (MODE == MODE_SUMS && h == 0) {
-        float* dst = a.state + bh * a.st_bh + g * a.st_g;
-        dst[(int64_t)R * DV + f0 + lo] = zreg[0];
-        dst[(int64_t)R * DV + f0 + 32 + lo] = zreg[1];
-    }
-}
+        // ---- z[F_W] += column sums of phi(K_c), after the queries read z_{c-1} ----
+        if (CAUSAL) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                zreg[nt] += half_sum(zpart[nt]);
+                sm.z[f0 + 32 * nt + lo] = zreg[nt]; // both halves: same value
+            }
+        }
 
-// Output block (ON, OQ) of chunk c -- rows [16 OQ, 16 OQ + 16), columns
-// [32 ON, 32 ON + 32) -- finished by consumer ON + 2 OQ: its own partial
-// (registers 8 OQ .. 8 OQ + 7 of tile ON) plus the other three groups'
-// partials from LDS, divided by the summed denominators, then stored as
-// bfloat16 rows through LDS so that each lane writes 16 contiguous bytes.
-template <int ON, int OQ>
-__device__ __forceinline__ void finish_block(const FavorArgs& a, Smem& sm, const f32x16 (&acc)[2],
-                                             int lane, int c, int64_t bh, int64_t c0, int rows) {
-    constexpr int W = ON + 2 * OQ;
-    const int lo = lane & 31, h = lane >> 5;
-    // every LDS read first, then one wait: the partials and denominators were
-    // all written before the barrier
-    const float(&red)[NW][NW - 1][2][64][4] = sm.red[c & 1];
-    f32x4 part[NW - 1][2];
-    float dg[NW];
-#pragma unroll
-    for (int s = 0; s < NW - 1; ++s)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) part[s][j] = *reinterpret_cast<const f32x4*>(&red[W][s][j][lane][0]);
-    if (a.norm == NORM_ATTN) {
-#pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) dg[w2] = sm.dint[c & 1][w2][lo]; // token lo's four groups
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // the denominators: lane lo sums token lo's four groups once, and the
-    // rows this lane finishes (16 OQ + 8 j + 4 h + 0..3) come back from LDS
-    // (the same wave wrote them, so LDS order suffices)
-    f32x4 rd[2];
-    if (a.norm == NORM_ATTN) {
-        if (h == 0) sm.rden[W][lo] = __builtin_amdgcn_rcpf(fmaxf((dg[0] + dg[1]) + (dg[2] + dg[3]), a.eps));
-#pragma unroll
-        for (int j = 0; j < 2; ++j) rd[j] = *reinterpret_cast<const f32x4*>(&sm.rden[W][16 * OQ + 8 * j + 4 * h]);
-    }
-    float own[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        own[i] = acc[ON][8 * OQ + i];
-#pragma unroll
-        for (int s = 0; s < NW - 1; ++s) own[i] += part[s][i >> 2][i & 3];
-    }
-    if (a.norm == NORM_ATTN) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) own[i] *= rd[i >> 2][i & 3];
-    }
-    u16* ot = sm.ot[W];
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-        const bf16x2 pr = {(__bf16)own[i], (__bf16)own[i + 1]};
-        const uint32_t u = __builtin_bit_cast(uint32_t, pr);
-        const int r = 8 * (i >> 2) + 4 * h + (i & 3); // rows r and r + 1
-        ot[r * 32 + lo] = (u16)(u & 0xffffu);
-        ot[(r + 1) * 32 + lo] = (u16)(u >> 16);
-    }
-    const int orow = lane >> 2, ocol = 8 * (lane & 3); // same wave: LDS keeps its order
-    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&ot[orow * 32 + ocol]);
-    const int t = 16 * OQ + orow;
-    if (t < rows) *reinterpret_cast<bf16x8*>(a.out + (bh * a.N + c0 + t) * DV + 32 * ON + ocol) = ov;
-}
+        const u16* vt = sm.vt[slot];
+        // V^T fragment (kk, nt): lane <-> column 32 nt + lo, k-slot e <-> token
+        // 16 kk + 8 (e/4) + 4 h + e%4
+        auto vfrag = [&](int kk, int nt) {
+            return lds8(vt + (32 * nt + lo) * LDV + vt_col(32 * nt + lo, 16 * kk + 8 * h));
+        };
 
-// Consumer of feature group w: owns S[F_w, :]; for chunk c (one behind the
-// producers) it forms the group's masked intra-chunk block, the partial
-// numerator and the state update, then finishes one quarter of the output.
-template <int MODE>
-__device__ __forceinline__ void consumer(const FavorArgs& a, Smem& sm, int w, int lane, int64_t bh,
-                                         int64_t g, int64_t t0, int64_t t1, int nck) {
-    constexpr bool HAS_K = MODE != MODE_READOUT;
-    constexpr bool HAS_Q = MODE != MODE_SUMS;
-    constexpr bool CAUSAL = MODE == MODE_CAUSAL;
-    const int lo = lane & 31, h = lane >> 5;
-    const int f0 = 64 * w;
+        // ---- masked intra-chunk block over F_W --------------------------------------
+        bf16x8 at[2];
+        if (CAUSAL) {
+            // phi(K) with tokens on lanes: lane (j, h), k-slot e <-> feature
+            // f0 + 32 mt + 16 kk + 8(e/4) + 4h + e%4, as in fq
+            bf16x8 kt[2][2];
+            const bf16x8 eye[2] = {sm.eye[0][lane], sm.eye[1][lane]};
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                f32x16 t = zero16();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) t = mfma(fk[mt][kk], eye[kk], t);
+                kt[mt][0] = pack8(t, 0);
+                kt[mt][1] = pack8(t, 8);
+            }
+            // m[i] = A[lo][j] over F_W, j = 8(i/4) + 4h + i%4
+            f32x16 m = zero16();
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) m = mfma(kt[mt][kk], fq[mt][kk], m);
+            float rs[2] = {0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                m[i] = 8 * (i >> 2) + (i & 3) <= keep_thr ? m[i] : 0.f;
+                rs[i & 1] += m[i];
+            }
+            if (NORM == NORM_ATTN) den += half_sum(rs[0] + rs[1]);
+            at[0] = pack8(m, 0);
+            at[1] = pack8(m, 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 
-    // State slice S[F_g, :] in accumulator layout: element i of S[mt][nt]
-    // is S[f0 + 32 mt + 8 (i/4) + 4 h + i%4][32 nt + lo].
-    f32x16 S[2][2];
-    if (MODE == MODE_SUMS) {
+        // ---- partial numerator, transposed (columns as rows, tokens on lanes):
+        //   acc^T = S_{c-1}[F_W]^T phi(Q)^T + V^T (block)^T
+        // S's accumulator tile packed to bf16 is the A operand of S^T as is.
+        // acc[nt] element i: column 32 nt + 8(i/4) + 4h + i%4, token lo
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int nt = 0; nt < 2; ++nt) {
+            acc[nt] = zero16();
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) S[mt][nt] = zero16();
-    } else {
-        const float* st = a.state + bh * a.st_bh + g * a.st_g;
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+                for (int kk = 0; kk < 2; ++kk) acc[nt] = mfma(pack8(S[mt][nt], 8 * kk), fq[mt][kk], acc[nt]);
+        }
+        if (CAUSAL) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int f = f0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-                    S[mt][nt][i] = st[(int64_t)f * DV + 32 * nt + lo];
-                }
-    }
-    bf16x8 eye[2];
-    if (CAUSAL) {
-        eye[0] = eye_frag(0, lo, h);
-        eye[1] = eye_frag(1, lo, h);
-    }
-    // causal mask of the diagonal tile: element i of lane (lo, h) pairs query
-    // lo with key 8(i/4) + 4h + i%4, kept when 8(i/4) + i%4 <= lo - 4h
-    const int keep_thr = lo - 4 * h;
-
-    sync_lds(); // matches the producers' staging barrier
-    for (int ci = 0; ci <= nck; ++ci) {
-        f32x16 acc[2];    // partial numerator tiles: row 8(i/4) + 4h + i%4, column 32 nt + lo
-        if (ci > 0) {
-            const int c = ci - 1;
-            const XBuf& X = sm.xb[c & 1];
-            const u16* vt = sm.vt[c & 1];
-            // V fragment (kk, nt): k-slot e <-> token 16 kk + 8 (e/4) + 4 h + e%4,
-            // lane <-> column 32 nt + lo
-            auto vfrag = [&](int kk, int nt) {
-                return lds8(vt + (32 * nt + lo) * LDV + vt_col(32 * nt + lo, 16 * kk + 8 * h));
-            };
-            bf16x8 fk[2][2];
-            if (HAS_K) {
+                for (int kk = 0; kk < 2; ++kk) acc[nt] = mfma(vfrag(kk, nt), at[kk], acc[nt]);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- state update: S[F_W] += phi(K)^T V ---------------------------------
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) fk[mt][kk] = X.fk[w][mt][kk][lane];
-            }
-            if (HAS_Q) {
-                bf16x8 fq[2][2];
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) fq[mt][kk] = X.fq[w][mt][kk][lane];
-                float den = X.den[w][lo]; // phi(Q) z_{c-1} over F_g of query lo
-                bf16x8 at[2];
-                if (CAUSAL) {
-                    // phi(K) with tokens on lanes (transposed through the matrix core):
-                    // lane (j, h), k-slot e <-> feature f0 + 32 mt + 16 kk + 8(e/4) + 4h + e%4,
-                    // as in fq
-                    bf16x8 kt[2][2];
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
-                        f32x16 t = zero16();
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) t = mfma(fk[mt][kk], eye[kk], t);
-                        kt[mt][0] = pack8(t, 0);
-                        kt[mt][1] = pack8(t, 8);
-                    }
-                    // masked block over F_g, transposed: m[i] = A[lo][j], j = 8(i/4) + 4h + i%4
-                    f32x16 m = zero16();
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) m = mfma(kt[mt][kk], fq[mt][kk], m);
-                    float rs[2] = {0.f, 0.f};
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        m[i] = 8 * (i >> 2) + (i & 3) <= keep_thr ? m[i] : 0.f;
-                        rs[i & 1] += m[i];
-                    }
-                    den += half_sum(rs[0] + rs[1]);
-                    at[0] = pack8(m, 0);
-                    at[1] = pack8(m, 8);
-                }
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    acc[nt] = zero16();
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) acc[nt] = mfma(fq[mt][kk], pack8(S[mt][nt], 8 * kk), acc[nt]);
-                }
-                if (CAUSAL) {
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) acc[nt] = mfma(at[kk], vfrag(kk, nt), acc[nt]);
-                }
-                sm.dint[c & 1][w][lo] = den; // both lane halves hold the full sum
-                // block (nt, q) belongs to consumer nt + 2 q; this wave keeps its own
-                float(&red)[NW][NW - 1][2][64][4] = sm.red[c & 1];
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int owner = nt + 2 * q;
-                        if (owner == w) continue;
-                        const int slot = w < owner ? w : w - 1;
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const f32x4 x = {acc[nt][8 * q + 4 * j], acc[nt][8 * q + 4 * j + 1],
-                                             acc[nt][8 * q + 4 * j + 2], acc[nt][8 * q + 4 * j + 3]};
-                            *reinterpret_cast<f32x4*>(&red[owner][slot][j][lane][0]) = x;
-                        }
-                    }
-            }
-            // ---- state update: S[F_g] += phi(K)^T V ----------------------------------
-            if (HAS_K) {
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) S[mt][nt] = mfma(fk[mt][kk], vfrag(kk, nt), S[mt][nt]);
-            }
+                    for (int kk = 0; kk < 2; ++kk) S[mt][nt] = mfma(fk[mt][kk], vfrag(kk, nt), S[mt][nt]);
         }
-        sync_lds(); // partial blocks of all consumers in LDS; chunk ci handed over
 
-        if (HAS_Q && ci > 0) {
-            const int c = ci - 1;
-            const int64_t c0 = t0 + (int64_t)L * c;
-            const int rows = (int)min<int64_t>(L, t1 - c0);
-            // block indices as constants: the block's registers are then fixed
-            switch (w) {
-            case 0: finish_block<0, 0>(a, sm, acc, lane, c, bh, c0, rows); break;
-            case 1: finish_block<1, 0>(a, sm, acc, lane, c, bh, c0, rows); break;
-            case 2: finish_block<0, 1>(a, sm, acc, lane, c, bh, c0, rows); break;
-            default: finish_block<1, 1>(a, sm, acc, lane, c, bh, c0, rows); break;
-            }
-        }
-    }
-
-    if (MODE == MODE_SUMS) {
-        float* dst = a.state + bh * a.st_bh + g * a.st_g;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        // ---- exchange: columns [32 nt + 16 q, +16) belong to wave nt + 2 q ---------
+        if (NORM == NORM_ATTN) sm.dpart[slot][lo][W] = den; // both halves: same value
+        {
+            float(&red)[NW][NW - 1][2][64][4] = sm.red[slot];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int f = f0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-                    dst[(int64_t)f * DV + 32 * nt + lo] = S[mt][nt][i];
+                for (int q = 0; q < 2; ++q) {
+                    const int owner = nt + 2 * q;
+                    if (owner == W) continue;
+                    const int sl = W < owner ? W : W - 1;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const f32x4 x = {acc[nt][8 * q + 4 * j], acc[nt][8 * q + 4 * j + 1],
+                                         acc[nt][8 * q + 4 * j + 2], acc[nt][8 * q + 4 * j + 3]};
+                        *reinterpret_cast<f32x4*>(&red[owner][sl][j][lane][0]) = x;
+                    }
                 }
+        }
+        sync_lds(); // partials of chunk ci in LDS; chunk ci + 1 staged
+
+        // the next chunk's first projections run on the matrix core while this
+        // chunk's output is finished
     }
+    if (nck > 0) finish_fused<W, NORM>(a, sm, acc, lane, (nck - 1) & 1, bh, t0 + (int64_t)L * (nck - 1), rows_of(nck - 1));
 }
 
-// Every wave of the workgroup runs nck + 1 iterations with one barrier each
-// (nck is uniform over the workgroup), whichever role it has.
-template <int MODE>
-__global__ __launch_bounds__(NT, 1) void k_favor_mfma(FavorArgs a) {
-    __shared__ Smem sm;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
+template <int MODE, int NORM>
+__global__ __launch_bounds__(NTF, 2) void k_favor_fused(FavorArgs a) {
+    __shared__ SmemF sm;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
     int64_t bh, g;
     if (!block_segment(a, bh, g)) return; // uniform over the workgroup
     int64_t t0, t1;
     seg_range(a.tab, a.tsub, g, a.seg_len, a.N, t0, t1);
     const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
-    if (wv >= NW)
-        producer<MODE>(a, sm, wv - NW, lane, bh, g, t0, t1, nck);
-    else
-        consumer<MODE>(a, sm, wv, lane, bh, g, t0, t1, nck);
+    switch (w) {
+    case 0: fused_wave<MODE, NORM, 0>(a, sm, tid, bh, g, t0, t1, nck); break;
+    case 1: fused_wave<MODE, NORM, 1>(a, sm, tid, bh, g, t0, t1, nck); break;
+    case 2: fused_wave<MODE, NORM, 2>(a, sm, tid, bh, g, t0, t1, nck); break;
+    default: fused_wave<MODE, NORM, 3>(a, sm, tid, bh, g, t0, t1, nck); break;
+    }
 }
 
 // Segment sums (increments of S and z) with eight symmetric waves: wave w
@@ -1184,7 +1073,7 @@ hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const v
 // Causal backward on the matrix cores (FAVOR+, bf16, r = 256).  One workgroup
 // per (head, segment) walks its chunks in order (query pass) or in reverse
 // (key pass); wave w keeps the 64 features F_w = [64w, 64w + 64) of the
-// evolving state in float32 accumulators, as the forward kernel's consumers
+// evolving state in float32 accumulators, as the forward kernel's waves
 // do.  Products over all features (readout, the masked intra-chunk block,
 // du) are summed across the four waves through LDS, two workgroup barriers
 // per chunk.  Tiles are 32 x 32 accumulator tiles; T as an operand is
@@ -1945,10 +1834,15 @@ hipError_t launch_favor_outputs(const Cfg& c, int causal, const void* q, const v
                                 const float* state, int64_t sbh, int64_t sg, void* out,
                                 hipStream_t st) {
     const FavorArgs a = make_args(c, q, k, v, omega, s, sp, const_cast<float*>(state), sbh, sg, out);
-    if (causal)
-        hipLaunchKernelGGL(k_favor_mfma<MODE_CAUSAL>, dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0, st, a);
+    const dim3 grid((unsigned)(sp.G * s.BH));
+    if (causal && c.norm == NORM_ATTN)
+        hipLaunchKernelGGL((k_favor_fused<MODE_CAUSAL, NORM_ATTN>), grid, dim3(NTF), 0, st, a);
+    else if (causal)
+        hipLaunchKernelGGL((k_favor_fused<MODE_CAUSAL, NORM_NONE>), grid, dim3(NTF), 0, st, a);
+    else if (c.norm == NORM_ATTN)
+        hipLaunchKernelGGL((k_favor_fused<MODE_READOUT, NORM_ATTN>), grid, dim3(NTF), 0, st, a);
     else
-        hipLaunchKernelGGL(k_favor_mfma<MODE_READOUT>, dim3((unsigned)(sp.G * s.BH)), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL((k_favor_fused<MODE_READOUT, NORM_NONE>), grid, dim3(NTF), 0, st, a);
     return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ namespace linattn {
 // multiple of SEG_UNIT tokens.
 constexpr int64_t SEG_UNIT = 64;
 constexpr int64_t TARGET_BLOCKS_VALU = 512; // vector kernels: about two workgroups per CU
-constexpr int64_t TARGET_BLOCKS_MFMA = 256; // matrix-core kernels: one workgroup per CU
+constexpr int64_t TARGET_BLOCKS_MFMA = 512; // matrix-core kernels: two workgroups per CU
 
 struct SegPlan {
     int64_t G;       // segments per head (one workgroup each for the outputs)

@@ -201,11 +201,10 @@ def test_empty_inputs_are_noops():
 
 def test_workspace_size_formula():
     """One (S | z) block of r*dv + r floats per head and sequence segment;
-    bidirectional adds one per head for the full summary.  FAVOR+ with
-    bfloat16 inputs and r = 256 runs on the matrix-core kernels, one
-    workgroup per CU: at B=1, H=8, N=65536 that is 32 segments of 2048
-    tokens, whose increments are summed over half segments (64 blocks per
-    head); the float32 vector kernels aim at two per CU (64 segments)."""
+    bidirectional adds one per head for the full summary.  Both kernel
+    families aim at two workgroups per CU: at B=1, H=8, N=65536 that is 64
+    segments of 1024 tokens per head (FAVOR+ with bfloat16 inputs and r = 256
+    on the matrix-core kernels, float32 on the vector kernels)."""
     p = params()
     E = 256 * 64 + 256
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 1, 8, 65536, 64, 64) == \
@@ -216,7 +215,7 @@ def test_workspace_size_formula():
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, pf, 1, 8, 65536, 64, 64) == \
         8 * 64 * E * 4
     p1 = params(n_seg=1)
-    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p1, 2, 3, 1000, 64, 64) == 6 * 2 * E * 4
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p1, 2, 3, 1000, 64, 64) == 6 * 1 * E * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 2, 3, 0, 64, 64) == 0
     assert binding.lin_attn_workspace_bytes(9, p, 2, 3, 10, 64, 64) == 0
 
@@ -242,18 +241,18 @@ def test_varlen_arguments():
 
 def test_varlen_workspace_formula():
     """Increments of every part of every head -- the segments of the uniform
-    plan over all tokens plus one partial segment per sequence, two parts each
-    on the matrix-core path -- then the segment table (two int64 per part,
-    after 256-byte alignment), the first part of every sequence and the
-    dispatch order (one int64 per segment)."""
+    plan over all tokens plus one partial segment per sequence, one part
+    each -- then the segment table (two int64 per part, after 256-byte
+    alignment), the first part of every sequence and the dispatch order (one
+    int64 per segment)."""
     p = params()
     E = 256 * 64 + 256
-    # H = 8, total = 65536: 32 segments of 2048 tokens per head, + 4 sequences
-    parts = (32 + 4) * 2
+    # H = 8, total = 65536: 64 segments of 1024 tokens per head, + 4 sequences
+    parts = 64 + 4
     inc = 8 * parts * E * 4
     assert inc % 256 == 0
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 4, 8, 65536, 64, 64) == \
-        inc + parts * 16 + 5 * 8 + (32 + 4) * 8
+        inc + parts * 16 + 5 * 8 + parts * 8
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 4, 8, 0, 64, 64) == 0
 
 

@@ -125,13 +125,14 @@ def main():
         z = torch.empty((w.B, w.H, w.r), device=dev)
         out = torch.empty((w.B, w.H, w.N, w.dv), device=dev, dtype=torch.bfloat16)
         p = binding.make_params("favor", w.r, dtype=torch.bfloat16, scale=scale, eps=w.eps)
-        wsb = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, w.B, w.H, w.N, w.d, w.dv, 64)
+        chunk = 32  # the intra-chunk block both kernel families run (one 32 x 32 MFMA tile)
+        wsb = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, w.B, w.H, w.N, w.d, w.dv, chunk)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
         def step(i):
             q, k, v = sets[i % 2]
             binding.lin_attn_causal_chunked(q, k, v, "favor", omega=om, scale=scale, eps=w.eps,
-                                            chunk=64, S=S, z=z, out=out, workspace=ws)
+                                            chunk=chunk, S=S, z=z, out=out, workspace=ws)
 
         total_ms, per = timed(step, args.steps, args.warmup)
         ms = total_ms / args.steps
@@ -141,7 +142,7 @@ def main():
         achieved = flops / (call_ms * 1e-3) / 1e12
         result.update(value=toks / (ms * 1e-3), ms_per_step=ms)
         result["config"] = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                            "dv": w.dv, "r": w.r, "phi": "favor", "chunk": 64,
+                            "dv": w.dv, "r": w.r, "phi": "favor", "chunk": chunk,
                             "inputs": "bf16 N(0,1)", "state": "fp32", "eps": w.eps,
                             "scale": scale}
         result["roofline"] = {
@@ -362,7 +363,7 @@ def main():
             y = torch.matmul(psets[i % 2], wcat.t())                 # [B, N, 3 * H * d]
             y = y.view(wp.B, wp.N, 3, wp.H, wp.d).permute(2, 0, 3, 1, 4).contiguous()
             binding.lin_attn_causal_chunked(y[0], y[1], y[2], "favor", omega=om, scale=sp_,
-                                            eps=wp.eps, chunk=64, S=pS, z=pz, out=pout,
+                                            eps=wp.eps, chunk=32, S=pS, z=pz, out=pout,
                                             workspace=uws)
 
         u_total, _ = timed(ustep, args.steps, args.warmup)
@@ -375,7 +376,7 @@ def main():
         def gstep(i):
             binding.lin_attn_qkv_project(psets[i % 2], wq, wk, wv, wp.H, q=gq, k=gk, v=gv)
             binding.lin_attn_causal_chunked(gq, gk, gv, "favor", omega=om, scale=sp_, eps=wp.eps,
-                                            chunk=64, S=pS, z=pz, out=pout, workspace=uws)
+                                            chunk=32, S=pS, z=pz, out=pout, workspace=uws)
 
         g_total, _ = timed(gstep, args.steps, args.warmup)
         g_only, g_per = timed(lambda i: binding.lin_attn_qkv_project(psets[i % 2], wq, wk, wv,

@@ -157,10 +157,12 @@ int lin_attn_bidir(const lin_attn_params* p, const void* q, const void* k, const
  * the state carried in from earlier chunks, and sequence segments are
  * combined by a prefix sum of their state increments; all of these are
  * exact re-associations of the recurrence.
- *   chunk     0, 32, 64 or 128: intra-chunk block length hint.  Each kernel
- *             family has one native block length (64 on the MFMA path, 32
- *             on the float32 path) and uses it; the value never changes the
- *             result beyond rounding.
+ *   chunk     intra-chunk block length: 0 or 32 (one 32 x 32 MFMA tile;
+ *             both kernel families run it, so they round alike).  64 and
+ *             128 are valid lengths (every block length re-associates the
+ *             [KZ] sec. 1.3 recurrence exactly, so the result changes only
+ *             by rounding) that no kernel here runs:
+ *             LIN_ATTN_ERR_UNSUPPORTED.  Other values: LIN_ATTN_ERR_INVALID.
  *   S, z      float32 [B, H, r, dv] / [B, H, r], required, in/out: read
  *             when state_in == 1, always overwritten with the state after
  *             token N (the carried fast-weight memory of [KZ] sec. 9.3; a
@@ -319,8 +321,10 @@ int lin_attn_causal_backward(const lin_attn_params* p, const void* q, const void
  * N = total, lin_attn_causal_varlen (op = LIN_ATTN_OP_CAUSAL_VARLEN), and
  * the backward calls (LIN_ATTN_OP_BIDIR_BACKWARD, LIN_ATTN_OP_CAUSAL_BACKWARD) and
  * the projected calls (LIN_ATTN_OP_CAUSAL_PROJ, LIN_ATTN_OP_BIDIR_PROJ).
+ * `chunk` is checked for LIN_ATTN_OP_CAUSAL as lin_attn_causal_chunked
+ * checks it and ignored for the other operations.
  * Host-only, deterministic in its arguments (independent of the device).
- * Returns 0 for invalid arguments.
+ * Returns 0 for invalid or unsupported arguments.
  */
 size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B, int64_t H,
                                 int64_t N, int64_t d, int64_t dv, int32_t chunk);

@@ -275,6 +275,64 @@ int proj_checks(const lin_attn_params* p, const void* x, const void* w_q, const 
     return LIN_ATTN_OK;
 }
 
+// The intra-chunk block length both kernel families run: one 32 x 32 MFMA
+// tile on the matrix-core path, and the same length on the float32 path so
+// that both round alike.  0 selects it; 64 and 128 are valid lengths of the
+// method that no kernel here runs.
+int check_chunk(int32_t chunk) {
+    if (chunk != 0 && chunk != 32 && chunk != 64 && chunk != 128) return LIN_ATTN_ERR_INVALID;
+    return chunk == 64 || chunk == 128 ? LIN_ATTN_ERR_UNSUPPORTED : LIN_ATTN_OK;
+}
+
+// lin_attn_causal_chunked.
+int causal_call(const lin_attn_params* p, const void* q, const void* k, const void* v, int64_t B,
+                int64_t H, int64_t N, int64_t d, int64_t dv, const void* omega, int32_t chunk,
+                float* S, float* z, int32_t state_in, void* out, void* ws, size_t ws_bytes,
+                void* stream) {
+    int rc = check_params(p, d, dv, omega);
+    if (rc == LIN_ATTN_ERR_INVALID) return rc;
+    const int rs = check_sizes(B, H, N);
+    if (rs == LIN_ATTN_ERR_INVALID) return rs;
+    const int rk = check_chunk(chunk);
+    if (rk == LIN_ATTN_ERR_INVALID) return rk;
+    if (state_in != 0 && state_in != 1) return LIN_ATTN_ERR_INVALID;
+    if (!opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
+    if (B * H > 0 && (!ptr_ok(S) || !ptr_ok(z))) return LIN_ATTN_ERR_INVALID;
+    if (B * H > 0 && N > 0 && (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out)))
+        return LIN_ATTN_ERR_INVALID;
+    if (rc != LIN_ATTN_OK) return rc;
+    if (rs != LIN_ATTN_OK) return rs;
+    if (rk != LIN_ATTN_OK) return rk;
+    if (B * H == 0) return LIN_ATTN_OK;
+    if (N == 0) {
+        // no token: the state after token N is the starting state
+        if (state_in) return LIN_ATTN_OK;
+        hipStream_t st = (hipStream_t)stream;
+        hipError_t e = launch_fill_zero(S, B * H * (int64_t)p->r * DV, st);
+        if (e == hipSuccess) e = launch_fill_zero(z, B * H * (int64_t)p->r, st);
+        return launch_status(e);
+    }
+    const int64_t BH = B * H;
+    const SegPlan sp = plan_for(p, BH, N);
+    const size_t need = ws_floats(LIN_ATTN_OP_CAUSAL, BH, sp, p->r) * sizeof(float);
+    if (ws_bytes < need || !ws) return LIN_ATTN_ERR_WORKSPACE;
+
+    const Cfg c = make_cfg(p);
+    const Shape s{BH, N};
+    hipStream_t st = (hipStream_t)stream;
+    const SegPlan ss = sums_plan(sp);
+    float* inc = (float*)ws;
+    const int64_t E = state_elems(p->r);
+    hipError_t e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
+    if (e == hipSuccess)
+        e = launch_segment_scan(p->r, s, ss, state_in ? S : nullptr, state_in ? z : nullptr, inc,
+                                (int)sp.sub, S, z, nullptr, st);
+    // segment g starts at sub-segment g * sub: its carried-in state is that prefix
+    if (e == hipSuccess)
+        e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, ss.G * E, sp.sub * E, out, st);
+    return launch_status(e);
+}
+
 } // namespace
 
 extern "C" {
@@ -294,8 +352,8 @@ const char* lin_attn_strerror(int32_t code) {
 
 size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B, int64_t H,
                                 int64_t N, int64_t d, int64_t dv, int32_t chunk) {
-    (void)chunk;
     if (op < LIN_ATTN_OP_BIDIR || op > LIN_ATTN_OP_BIDIR_PROJ) return 0;
+    if (op == LIN_ATTN_OP_CAUSAL && check_chunk(chunk) != LIN_ATTN_OK) return 0;
     if (!p || check_sizes(B, H, N) != LIN_ATTN_OK) return 0;
     // omega is not needed to size the workspace: check the rest with a dummy
     const int rc = check_params(p, d, dv, reinterpret_cast<const void*>(uintptr_t(16)));
@@ -370,46 +428,8 @@ int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void*
                             int64_t dv, const void* omega, int32_t chunk, float* S, float* z,
                             int32_t state_in, void* out, void* ws, size_t ws_bytes,
                             void* stream) {
-    int rc = check_params(p, d, dv, omega);
-    if (rc == LIN_ATTN_ERR_INVALID) return rc;
-    const int rs = check_sizes(B, H, N);
-    if (rs == LIN_ATTN_ERR_INVALID) return rs;
-    if (chunk != 0 && chunk != 32 && chunk != 64 && chunk != 128) return LIN_ATTN_ERR_INVALID;
-    if (state_in != 0 && state_in != 1) return LIN_ATTN_ERR_INVALID;
-    if (!opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
-    if (B * H > 0 && (!ptr_ok(S) || !ptr_ok(z))) return LIN_ATTN_ERR_INVALID;
-    if (B * H > 0 && N > 0 && (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out)))
-        return LIN_ATTN_ERR_INVALID;
-    if (rc != LIN_ATTN_OK) return rc;
-    if (rs != LIN_ATTN_OK) return rs;
-    if (B * H == 0) return LIN_ATTN_OK;
-    if (N == 0) {
-        // no token: the state after token N is the starting state
-        if (state_in) return LIN_ATTN_OK;
-        hipStream_t st = (hipStream_t)stream;
-        hipError_t e = launch_fill_zero(S, B * H * (int64_t)p->r * DV, st);
-        if (e == hipSuccess) e = launch_fill_zero(z, B * H * (int64_t)p->r, st);
-        return launch_status(e);
-    }
-    const int64_t BH = B * H;
-    const SegPlan sp = plan_for(p, BH, N);
-    const size_t need = ws_floats(LIN_ATTN_OP_CAUSAL, BH, sp, p->r) * sizeof(float);
-    if (ws_bytes < need || !ws) return LIN_ATTN_ERR_WORKSPACE;
-
-    const Cfg c = make_cfg(p);
-    const Shape s{BH, N};
-    hipStream_t st = (hipStream_t)stream;
-    const SegPlan ss = sums_plan(sp);
-    float* inc = (float*)ws;
-    const int64_t E = state_elems(p->r);
-    hipError_t e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
-    if (e == hipSuccess)
-        e = launch_segment_scan(p->r, s, ss, state_in ? S : nullptr, state_in ? z : nullptr, inc,
-                                (int)sp.sub, S, z, nullptr, st);
-    // segment g starts at sub-segment g * sub: its carried-in state is that prefix
-    if (e == hipSuccess)
-        e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, ss.G * E, sp.sub * E, out, st);
-    return launch_status(e);
+    return causal_call(p, q, k, v, B, H, N, d, dv, omega, chunk, S, z, state_in, out, ws, ws_bytes,
+                       stream);
 }
 
 int lin_attn_causal_varlen(const lin_attn_params* p, const void* q, const void* k,

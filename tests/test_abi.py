@@ -150,6 +150,7 @@ def test_pointers_sizes_and_enums():
     assert bidir(p, N=-1) == INVALID
     assert bidir(p, B=-2) == INVALID
     assert causal(p, chunk=16) == INVALID
+    assert causal(p, chunk=-32) == INVALID
     assert causal(p, state_in=2) == INVALID
     assert causal(p, S=None) == INVALID
     assert decode(p, ptr=None) == INVALID
@@ -163,6 +164,22 @@ def test_outside_gpu_coverage_is_unsupported():
     assert bidir(params("favor", r=48)) == UNSUPPORTED
     assert causal(params("dpfp", r=384, nu=3)) == UNSUPPORTED
     assert decode(params("favor", r=272)) == UNSUPPORTED
+    # 64- and 128-token intra-chunk blocks are valid but run by no kernel
+    assert causal(params(), chunk=64) == UNSUPPORTED
+    assert causal(params(), chunk=128) == UNSUPPORTED
+    assert causal(params("elu1", r=64, dtype=0), chunk=128) == UNSUPPORTED
+
+
+def test_chunk_sizes_the_causal_workspace_only():
+    p = params()
+    args = (p, 1, 8, 4096, 64, 64)
+    need = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, *args, 0)
+    assert need > 0
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, *args, 32) == need
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, *args, 64) == 0
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, *args, 16) == 0
+    assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR, *args, 64) == \
+        binding.lin_attn_workspace_bytes(binding.OP_BIDIR, *args, 0)
 
 
 def test_sizes_past_the_grid_limits_are_unsupported():

@@ -26,8 +26,9 @@
  *   "sampled once and frozen").
  * Ownership.  The caller allocates and owns every buffer, including the
  *   workspace (size from lin_attn_workspace_bytes).  The library never
- *   allocates, frees or keeps a pointer after returning, holds no global
- *   state and is reentrant.
+ *   allocates, frees or keeps a pointer after returning and is reentrant.
+ *   Its only global state is the static scratch array of
+ *   lin_attn_causal_chunked_noalloc (one per GPU, see there).
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  *   stream).  All work is enqueued asynchronously on it; nothing
  *   synchronises.  Buffers must stay valid until that work completes.
@@ -175,6 +176,33 @@ int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void*
                             int64_t dv, const void* omega, int32_t chunk, float* S, float* z,
                             int32_t state_in, void* out, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* Size of the static scratch of lin_attn_causal_chunked_noalloc (64 MiB). */
+#define LIN_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * lin_attn_causal_chunked for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as lin_attn_causal_chunked
+ * without ws / ws_bytes: the workspace is a static array of
+ * LIN_ATTN_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU,
+ * located on the call's first use of a device and held until the process
+ * ends.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).
+ *   The scratch of the current device is used: `stream` must belong to it.
+ *   Calls that overlap in time on one GPU share its scratch and race; the
+ *   caller serialises them (one stream, or events between streams).  Every
+ *   scratch byte a call reads was written earlier in the same call, so
+ *   nothing left by a previous call needs clearing.
+ * Errors as lin_attn_causal_chunked, plus LIN_ATTN_ERR_WORKSPACE when
+ * lin_attn_workspace_bytes(LIN_ATTN_OP_CAUSAL, ...) exceeds the scratch
+ * (B = 1, H = 8, N = 65536, r = 256 needs 34 MB) and LIN_ATTN_ERR_HIP when
+ * the device's copy cannot be located.
+ */
+int lin_attn_causal_chunked_noalloc(const lin_attn_params* p, const void* q, const void* k,
+                                    const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
+                                    int64_t dv, const void* omega, int32_t chunk, float* S,
+                                    float* z, int32_t state_in, void* out, void* stream);
 
 /*
  * Causal prefill of a packed batch: num_seqs independent sequences laid end

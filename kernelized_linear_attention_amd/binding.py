@@ -33,9 +33,11 @@ OP_CAUSAL_BACKWARD = 5
 OP_CAUSAL_PROJ = 6
 OP_BIDIR_PROJ = 7
 ABI_VERSION = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol include/lin_attn.h declares.
 EXPORTS = ("lin_attn_featuremap", "lin_attn_bidir", "lin_attn_causal_chunked",
+           "lin_attn_causal_chunked_noalloc",
            "lin_attn_causal_varlen", "lin_attn_orf_omega", "lin_attn_bidir_backward",
            "lin_attn_causal_backward", "lin_attn_causal_proj", "lin_attn_bidir_proj",
            "lin_attn_qkv_project",
@@ -62,6 +64,9 @@ _lib.lin_attn_bidir.restype = ctypes.c_int
 _lib.lin_attn_causal_chunked.argtypes = [_PP, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I32,
                                          _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]
 _lib.lin_attn_causal_chunked.restype = ctypes.c_int
+_lib.lin_attn_causal_chunked_noalloc.argtypes = [_PP, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
+                                                 _I32, _P, _P, _I32, _P, _P]
+_lib.lin_attn_causal_chunked_noalloc.restype = ctypes.c_int
 _lib.lin_attn_causal_varlen.argtypes = [_PP, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
                                         _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]
 _lib.lin_attn_causal_varlen.restype = ctypes.c_int
@@ -238,6 +243,39 @@ def lin_attn_causal_chunked(q, k, v, kind, *, omega=None, nu=1, sum_norm=False, 
                                       _ptr(om), int(chunk), _ptr(S), _ptr(z), int(bool(state_in)),
                                       _ptr(out), _ptr(ws), ws_bytes, _stream(q.device, stream))
     _check("lin_attn_causal_chunked", rc)
+    return out, S, z
+
+
+def lin_attn_causal_chunked_noalloc(q, k, v, kind, *, omega=None, nu=1, sum_norm=False,
+                                    norm="attn", scale=1.0, eps=1e-6, n_seg=0, chunk=0, S=None,
+                                    z=None, state_in=False, out=None, stream=None):
+    """lin_attn_causal_chunked with the library's static per-GPU scratch as the
+    workspace (the library allocates nothing for the call).  Returns (out, S,
+    z) like lin_attn_causal_chunked; outputs are allocated here only when not
+    given."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t, q.dtype)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    om = _omega(kind, omega, q.dtype)
+    r = feature_width(kind, d, nu, om)
+    p = make_params(kind, r, nu=nu, sum_norm=sum_norm, norm=norm, dtype=q.dtype, scale=scale,
+                    eps=eps, n_seg=n_seg)
+    if S is None:
+        if state_in:
+            raise ValueError("state_in needs S and z")
+        S = torch.empty((B, H, r, dv), dtype=torch.float32, device=q.device)
+        z = torch.empty((B, H, r), dtype=torch.float32, device=q.device)
+    _dev_tensor("S", S, torch.float32)
+    _dev_tensor("z", z, torch.float32)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    _dev_tensor("out", out, q.dtype)
+    rc = _lib.lin_attn_causal_chunked_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), B, H, N,
+                                              d, dv, _ptr(om), int(chunk), _ptr(S), _ptr(z),
+                                              int(bool(state_in)), _ptr(out),
+                                              _stream(q.device, stream))
+    _check("lin_attn_causal_chunked_noalloc", rc)
     return out, S, z
 
 

@@ -3,6 +3,8 @@
 // Validation happens entirely on the host, before anything is enqueued.
 #include <math.h>
 
+#include <atomic>
+
 #include "../../include/lin_attn.h"
 #include "launch.hpp"
 
@@ -284,11 +286,31 @@ int check_chunk(int32_t chunk) {
     return chunk == 64 || chunk == 128 ? LIN_ATTN_ERR_UNSUPPORTED : LIN_ATTN_OK;
 }
 
-// lin_attn_causal_chunked.
+// Static scratch of lin_attn_causal_chunked_noalloc: one copy per GPU, held
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol): each device's
+// copy is located once with hipGetSymbolAddress, with that device current.
+__device__ __align__(256) unsigned char scratch[LIN_ATTN_NOALLOC_SCRATCH_BYTES];
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::atomic<void*> scratch_addr[SCRATCH_MAX_DEVICES];
+
+// This device's copy of `scratch`, or NULL when it cannot be located.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return nullptr;
+    void* ptr = scratch_addr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_addr[dev].store(ptr, std::memory_order_release); // same value if two threads race
+    return ptr;
+}
+
+// lin_attn_causal_chunked, with the workspace either passed in or (noalloc)
+// taken from the current device's static scratch.
 int causal_call(const lin_attn_params* p, const void* q, const void* k, const void* v, int64_t B,
                 int64_t H, int64_t N, int64_t d, int64_t dv, const void* omega, int32_t chunk,
                 float* S, float* z, int32_t state_in, void* out, void* ws, size_t ws_bytes,
-                void* stream) {
+                void* stream, bool noalloc) {
     int rc = check_params(p, d, dv, omega);
     if (rc == LIN_ATTN_ERR_INVALID) return rc;
     const int rs = check_sizes(B, H, N);
@@ -296,7 +318,7 @@ int causal_call(const lin_attn_params* p, const void* q, const void* k, const vo
     const int rk = check_chunk(chunk);
     if (rk == LIN_ATTN_ERR_INVALID) return rk;
     if (state_in != 0 && state_in != 1) return LIN_ATTN_ERR_INVALID;
-    if (!opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
+    if (!noalloc && !opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
     if (B * H > 0 && (!ptr_ok(S) || !ptr_ok(z))) return LIN_ATTN_ERR_INVALID;
     if (B * H > 0 && N > 0 && (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out)))
         return LIN_ATTN_ERR_INVALID;
@@ -315,6 +337,12 @@ int causal_call(const lin_attn_params* p, const void* q, const void* k, const vo
     const int64_t BH = B * H;
     const SegPlan sp = plan_for(p, BH, N);
     const size_t need = ws_floats(LIN_ATTN_OP_CAUSAL, BH, sp, p->r) * sizeof(float);
+    if (noalloc) {
+        if (need > LIN_ATTN_NOALLOC_SCRATCH_BYTES) return LIN_ATTN_ERR_WORKSPACE;
+        ws = device_scratch();
+        if (!ws) return LIN_ATTN_ERR_HIP;
+        ws_bytes = LIN_ATTN_NOALLOC_SCRATCH_BYTES;
+    }
     if (ws_bytes < need || !ws) return LIN_ATTN_ERR_WORKSPACE;
 
     const Cfg c = make_cfg(p);
@@ -429,7 +457,15 @@ int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void*
                             int32_t state_in, void* out, void* ws, size_t ws_bytes,
                             void* stream) {
     return causal_call(p, q, k, v, B, H, N, d, dv, omega, chunk, S, z, state_in, out, ws, ws_bytes,
-                       stream);
+                       stream, false);
+}
+
+int lin_attn_causal_chunked_noalloc(const lin_attn_params* p, const void* q, const void* k,
+                                    const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
+                                    int64_t dv, const void* omega, int32_t chunk, float* S,
+                                    float* z, int32_t state_in, void* out, void* stream) {
+    return causal_call(p, q, k, v, B, H, N, d, dv, omega, chunk, S, z, state_in, out, nullptr, 0,
+                       stream, true);
 }
 
 int lin_attn_causal_varlen(const lin_attn_params* p, const void* q, const void* k,

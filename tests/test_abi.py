@@ -182,6 +182,35 @@ def test_chunk_sizes_the_causal_workspace_only():
         binding.lin_attn_workspace_bytes(binding.OP_BIDIR, *args, 0)
 
 
+def causal_noalloc(p, B=1, H=2, N=100, d=64, dv=64, ptr=FAKE, omega=FAKE, chunk=0, state_in=0,
+                   S=FAKE, z=FAKE):
+    return lib.lin_attn_causal_chunked_noalloc(ctypes.byref(p), ptr, ptr, ptr, B, H, N, d, dv, omega,
+                                               chunk, S, z, state_in, ptr, None)
+
+
+def test_noalloc_arguments():
+    """The allocation-free causal call validates like lin_attn_causal_chunked
+    and refuses problems whose workspace exceeds its static scratch."""
+    p = params()
+    assert causal_noalloc(p, ptr=None) == INVALID
+    assert causal_noalloc(p, chunk=16) == INVALID
+    assert causal_noalloc(p, state_in=2) == INVALID
+    assert causal_noalloc(p, S=None) == INVALID
+    assert causal_noalloc(p, chunk=64) == UNSUPPORTED
+    assert causal_noalloc(params("favor", r=512)) == UNSUPPORTED
+    assert causal_noalloc(p, H=0) == OK
+    # one (S | z) block of 66,560 bytes per head at least: 1024 heads need 68 MB
+    big = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 4, 256, 100, 64, 64, 0)
+    assert big > binding.NOALLOC_SCRATCH_BYTES
+    assert causal_noalloc(p, B=4, H=256) == WORKSPACE
+    assert header_defines_size("LIN_ATTN_NOALLOC_SCRATCH_BYTES") == binding.NOALLOC_SCRATCH_BYTES
+
+
+def header_defines_size(name):
+    m = re.search(r"#define\s+" + name + r"\s+\(\(size_t\)(\d+) << (\d+)\)", header_text())
+    return int(m.group(1)) << int(m.group(2))
+
+
 def test_sizes_past_the_grid_limits_are_unsupported():
     """Flattened grids stay within 32 bits: more than 2^24 heads in a batch,
     a B*H product past 2^31 or more than 2^40 tokens is refused before any

@@ -265,22 +265,26 @@ int lin_attn_orf_omega(const float* gauss, const float* len_gauss, int64_t n_mat
                        int64_t d, int32_t dtype, void* omega, void* stream);
 
 /*
- * Causal prefill and bidirectional attention from the tokens, with the
- * input projection fused into the loads of the kernels ([KZ] sec. 1.2 step
- * 1: k, v, q = W_k x, W_v x, W_q x for every token x): q, k and v are
- * computed in float32 from bfloat16 x and W inside the kernels, chunk by
- * chunk, and never written to memory.  Then exactly lin_attn_causal_chunked
- * (state_in, S, z as there) or lin_attn_bidir (S_out, z_out as there).
+ * Causal prefill and bidirectional attention from the tokens ([KZ] sec.
+ * 1.2 step 1: k, v, q = W_k x, W_v x, W_q x for every token x), then exactly
+ * lin_attn_causal_chunked (state_in, S, z as there) or lin_attn_bidir
+ * (S_out, z_out as there).  Two routes, by configuration:
+ *   FAVOR+ with r = 256 and no sum normalisation (the matrix-core
+ *   configuration): one projection GEMM writes q, k, v (rounded to
+ *   bfloat16, as lin_attn_qkv_project does) into the workspace, then the
+ *   matrix-core kernels run on them;
+ *   every other map: the vector kernels compute q, k and v in float32 from
+ *   x and W inside their loads, chunk by chunk, never writing them out.
  *   x              [B, N, d_model] bfloat16 tokens.
  *   w_q, w_k, w_v  [H * d, d_model] bfloat16 each (out = W x, the layout of a
  *                  linear layer's weight): row h*d + i gives feature i of
  *                  head h.
  *   out            [B, H, N, dv] bfloat16.
  *   d_model        a multiple of 16, at most 65536 (else -2).
- * lin_attn_params.dtype must be LIN_ATTN_BF16 (float32 returns -2).  The
- * float32 vector kernels run these calls for every feature map.
+ * lin_attn_params.dtype must be LIN_ATTN_BF16 (float32 returns -2).
  *   ws   at least lin_attn_workspace_bytes(LIN_ATTN_OP_CAUSAL_PROJ or
- *        LIN_ATTN_OP_BIDIR_PROJ, p, B, H, N, d, dv, 0) bytes.
+ *        LIN_ATTN_OP_BIDIR_PROJ, p, B, H, N, d, dv, 0) bytes (on the
+ *        matrix-core route this includes 3 B H N d bfloat16 for q, k, v).
  * Errors as lin_attn_causal_chunked / lin_attn_bidir; x, w_q, w_k, w_v must
  * be 16-byte aligned.
  */

@@ -252,17 +252,28 @@ int backward_call(bool causal, const lin_attn_params* p, const void* q, const vo
     return launch_status(e);
 }
 
-// Fused input projection: the vector kernels with q, k, v projected from the
-// tokens in their loads.  Workspace as lin_attn_causal_chunked / lin_attn_bidir
-// on the vector plan (no increment halving).
+// Input projection from the tokens.  On the matrix-core configuration
+// (bfloat16 FAVOR+, r = 256) the projection is one GEMM writing q, k, v
+// (bfloat16, head-major) to the front of the workspace, followed by the
+// matrix-core kernels, whose workspace follows (256-byte aligned).  Every
+// other map runs the vector kernels with q, k, v projected in their loads
+// (workspace as lin_attn_causal_chunked / lin_attn_bidir on the vector plan).
 SegPlan proj_plan(const lin_attn_params* p, int64_t BH, int64_t N) {
     return plan_segments(BH, N, p->n_seg, TARGET_BLOCKS_VALU);
 }
 
-size_t proj_ws_floats(bool causal, const lin_attn_params* p, int64_t BH, int64_t N) {
+size_t proj_qkv_bytes(int64_t BH, int64_t N) {
+    return ((size_t)(3 * BH * N * D) * sizeof(bf16_raw) + 255) & ~(size_t)255;
+}
+
+size_t proj_ws_bytes(bool causal, const lin_attn_params* p, int64_t BH, int64_t N) {
+    if (use_mfma(p))
+        return proj_qkv_bytes(BH, N) +
+               ws_floats(causal ? LIN_ATTN_OP_CAUSAL : LIN_ATTN_OP_BIDIR, BH, plan_for(p, BH, N),
+                         p->r) * sizeof(float);
     const SegPlan sp = proj_plan(p, BH, N);
     const int64_t E = state_elems(p->r);
-    return (size_t)(BH * sp.G * E) + (causal ? 0 : (size_t)(BH * E));
+    return ((size_t)(BH * sp.G * E) + (causal ? 0 : (size_t)(BH * E))) * sizeof(float);
 }
 
 // Checks shared by the two projected calls (beyond check_params / check_sizes).
@@ -271,10 +282,54 @@ int proj_checks(const lin_attn_params* p, const void* x, const void* w_q, const 
     if (d_model <= 0) return LIN_ATTN_ERR_INVALID;
     if (any && B * N > 0 && !ptr_ok(x)) return LIN_ATTN_ERR_INVALID;
     if (any && (!ptr_ok(w_q) || !ptr_ok(w_k) || !ptr_ok(w_v))) return LIN_ATTN_ERR_INVALID;
-    (void)H;
     if (p->dtype != LIN_ATTN_BF16) return LIN_ATTN_ERR_UNSUPPORTED;
     if (d_model % 16 != 0 || d_model > 65536) return LIN_ATTN_ERR_UNSUPPORTED;
+    // the projection GEMM's grid (one block per 128 tokens x 128 columns) in range
+    if (B > 0 && N > ((int64_t)1 << 40) / B) return LIN_ATTN_ERR_UNSUPPORTED;
+    const int64_t tiles = ((B * N + 127) / 128) * ((3 * H * D + 127) / 128);
+    if (tiles > ((int64_t)1 << 31)) return LIN_ATTN_ERR_UNSUPPORTED;
     return LIN_ATTN_OK;
+}
+
+// The kernels of lin_attn_bidir on validated arguments: segment increments,
+// their fixed-order total (written to S_out / z_out when given), readout.
+hipError_t bidir_run(const lin_attn_params* p, const void* q, const void* k, const void* v,
+                     int64_t BH, int64_t N, const void* omega, void* out, float* S_out,
+                     float* z_out, float* ws, hipStream_t st) {
+    const Cfg c = make_cfg(p);
+    const Shape s{BH, N};
+    const SegPlan sp = plan_for(p, BH, N);
+    const SegPlan ss = sums_plan(sp);
+    float* inc = ws;
+    float* fin = inc + BH * ss.G * state_elems(p->r);
+    hipError_t e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
+    if (e == hipSuccess)
+        e = launch_segment_scan(p->r, s, ss, nullptr, nullptr, inc, 0, S_out, z_out, fin, st);
+    if (e == hipSuccess)
+        e = segment_outputs(p, c, 0, q, k, v, omega, s, sp, fin, state_elems(p->r), 0, out, st);
+    return e;
+}
+
+// The kernels of lin_attn_causal_chunked on validated arguments: segment
+// increments, their prefix from the starting state (the final state to S,
+// z), the chunked recurrence of every segment from its prefix.
+hipError_t causal_run(const lin_attn_params* p, const void* q, const void* k, const void* v,
+                      int64_t BH, int64_t N, const void* omega, float* S, float* z,
+                      int32_t state_in, void* out, float* ws, hipStream_t st) {
+    const Cfg c = make_cfg(p);
+    const Shape s{BH, N};
+    const SegPlan sp = plan_for(p, BH, N);
+    const SegPlan ss = sums_plan(sp);
+    float* inc = ws;
+    const int64_t E = state_elems(p->r);
+    hipError_t e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
+    if (e == hipSuccess)
+        e = launch_segment_scan(p->r, s, ss, state_in ? S : nullptr, state_in ? z : nullptr, inc,
+                                (int)sp.sub, S, z, nullptr, st);
+    // segment g starts at sub-segment g * sub: its carried-in state is that prefix
+    if (e == hipSuccess)
+        e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, ss.G * E, sp.sub * E, out, st);
+    return e;
 }
 
 // The intra-chunk block length both kernel families run: one 32 x 32 MFMA
@@ -345,20 +400,8 @@ int causal_call(const lin_attn_params* p, const void* q, const void* k, const vo
     }
     if (ws_bytes < need || !ws) return LIN_ATTN_ERR_WORKSPACE;
 
-    const Cfg c = make_cfg(p);
-    const Shape s{BH, N};
-    hipStream_t st = (hipStream_t)stream;
-    const SegPlan ss = sums_plan(sp);
-    float* inc = (float*)ws;
-    const int64_t E = state_elems(p->r);
-    hipError_t e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
-    if (e == hipSuccess)
-        e = launch_segment_scan(p->r, s, ss, state_in ? S : nullptr, state_in ? z : nullptr, inc,
-                                (int)sp.sub, S, z, nullptr, st);
-    // segment g starts at sub-segment g * sub: its carried-in state is that prefix
-    if (e == hipSuccess)
-        e = segment_outputs(p, c, 1, q, k, v, omega, s, sp, inc, ss.G * E, sp.sub * E, out, st);
-    return launch_status(e);
+    return launch_status(causal_run(p, q, k, v, BH, N, omega, S, z, state_in, out, (float*)ws,
+                                    (hipStream_t)stream));
 }
 
 } // namespace
@@ -390,7 +433,7 @@ size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B,
     if (BH == 0 || N == 0) return 0;
     if (op == LIN_ATTN_OP_CAUSAL_VARLEN) return varlen_layout(p, B, H, N).bytes;
     if (op == LIN_ATTN_OP_CAUSAL_PROJ || op == LIN_ATTN_OP_BIDIR_PROJ)
-        return proj_ws_floats(op == LIN_ATTN_OP_CAUSAL_PROJ, p, BH, N) * sizeof(float);
+        return proj_ws_bytes(op == LIN_ATTN_OP_CAUSAL_PROJ, p, BH, N);
     if (op == LIN_ATTN_OP_BIDIR_BACKWARD || op == LIN_ATTN_OP_CAUSAL_BACKWARD)
         return backward_layout(p, op == LIN_ATTN_OP_CAUSAL_BACKWARD, BH, N).floats * sizeof(float);
     return ws_floats(op, BH, plan_for(p, BH, N), p->r) * sizeof(float);
@@ -437,18 +480,8 @@ int lin_attn_bidir(const lin_attn_params* p, const void* q, const void* k, const
     const size_t need = ws_floats(LIN_ATTN_OP_BIDIR, BH, sp, p->r) * sizeof(float);
     if (ws_bytes < need || !ws) return LIN_ATTN_ERR_WORKSPACE;
 
-    const Cfg c = make_cfg(p);
-    const Shape s{BH, N};
-    hipStream_t st = (hipStream_t)stream;
-    const SegPlan ss = sums_plan(sp);
-    float* inc = (float*)ws;
-    float* fin = inc + BH * ss.G * state_elems(p->r);
-    hipError_t e = segment_sums(p, c, k, v, omega, s, ss, inc, st);
-    if (e == hipSuccess)
-        e = launch_segment_scan(p->r, s, ss, nullptr, nullptr, inc, 0, S_out, z_out, fin, st);
-    if (e == hipSuccess)
-        e = segment_outputs(p, c, 0, q, k, v, omega, s, sp, fin, state_elems(p->r), 0, out, st);
-    return launch_status(e);
+    return launch_status(bidir_run(p, q, k, v, BH, N, omega, out, S_out, z_out, (float*)ws,
+                                   (hipStream_t)stream));
 }
 
 int lin_attn_causal_chunked(const lin_attn_params* p, const void* q, const void* k,
@@ -582,8 +615,18 @@ int lin_attn_causal_proj(const lin_attn_params* p, const void* x, const void* w_
         return launch_status(e);
     }
     const int64_t BH = B * H;
-    if (ws_bytes < proj_ws_floats(true, p, BH, N) * sizeof(float) || !ws)
-        return LIN_ATTN_ERR_WORKSPACE;
+    if (ws_bytes < proj_ws_bytes(true, p, BH, N) || !ws) return LIN_ATTN_ERR_WORKSPACE;
+    if (use_mfma(p)) {
+        bf16_raw* qkv = static_cast<bf16_raw*>(ws);
+        const int64_t n = BH * N * D;
+        hipError_t e = launch_qkv_project(x, w_q, w_k, w_v, B, N, d_model, H, qkv, qkv + n,
+                                          qkv + 2 * n, st);
+        if (e == hipSuccess)
+            e = causal_run(p, qkv, qkv + n, qkv + 2 * n, BH, N, omega, S, z, state_in, out,
+                           reinterpret_cast<float*>(static_cast<char*>(ws) + proj_qkv_bytes(BH, N)),
+                           st);
+        return launch_status(e);
+    }
     const Cfg c = make_cfg(p);
     const Shape s{BH, N};
     const SegPlan sp = proj_plan(p, BH, N);
@@ -626,8 +669,18 @@ int lin_attn_bidir_proj(const lin_attn_params* p, const void* x, const void* w_q
         return launch_status(e);
     }
     const int64_t BH = B * H;
-    if (ws_bytes < proj_ws_floats(false, p, BH, N) * sizeof(float) || !ws)
-        return LIN_ATTN_ERR_WORKSPACE;
+    if (ws_bytes < proj_ws_bytes(false, p, BH, N) || !ws) return LIN_ATTN_ERR_WORKSPACE;
+    if (use_mfma(p)) {
+        bf16_raw* qkv = static_cast<bf16_raw*>(ws);
+        const int64_t n = BH * N * D;
+        hipError_t e = launch_qkv_project(x, w_q, w_k, w_v, B, N, d_model, H, qkv, qkv + n,
+                                          qkv + 2 * n, st);
+        if (e == hipSuccess)
+            e = bidir_run(p, qkv, qkv + n, qkv + 2 * n, BH, N, omega, out, S_out, z_out,
+                          reinterpret_cast<float*>(static_cast<char*>(ws) + proj_qkv_bytes(BH, N)),
+                          st);
+        return launch_status(e);
+    }
     const Cfg c = make_cfg(p);
     const Shape s{BH, N};
     const SegPlan sp = proj_plan(p, BH, N);

@@ -403,15 +403,26 @@ def test_projected_call_arguments(call):
 
 
 def test_projected_workspace_formula():
-    """The vector kernels' plan (64 segments per head at H = 8, N = 65536),
-    one (S | z) block per segment, plus the summary per head when
-    bidirectional."""
+    """Matrix-core configuration (bf16 FAVOR+, r = 256): q, k, v in bfloat16
+    (3 B H N d, 256-byte aligned) then the matrix-core workspace (64 segments
+    per head at H = 8, N = 65536; one (S | z) block per segment, plus the
+    summary per head when bidirectional).  Other maps: the vector kernels'
+    plan alone, which at this shape is also 64 segments per head."""
     p = params()
     E = 256 * 64 + 256
+    qkv = 3 * 8 * 65536 * 64 * 2
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_PROJ, p, 1, 8, 65536, 64, 64) == \
-        8 * 64 * E * 4
+        qkv + 8 * 64 * E * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR_PROJ, p, 1, 8, 65536, 64, 64) == \
-        (8 * 64 + 8) * E * 4
+        qkv + (8 * 64 + 8) * E * 4
+    pe = params("elu1", r=64)
+    E64 = 64 * 64 + 64
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_PROJ, pe, 1, 8, 65536, 64, 64) == \
+        8 * 64 * E64 * 4
+    # an odd token count: q, k, v padded to a 256-byte boundary
+    odd = 3 * 1 * 3 * 64 * 2
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_PROJ, params(n_seg=1), 1, 1, 3, 64, 64) \
+        == (odd + 255) // 256 * 256 + E * 4
 
 
 def test_qkv_project_arguments():

@@ -37,9 +37,12 @@
  *   negative code, checks its arguments before enqueueing anything, and on
  *   error enqueues nothing and leaves every buffer untouched.  It never
  *   prints, throws or aborts.  N == 0 or B*H == 0 is a successful no-op.
- * GPU coverage.  d == dv == 64; r a multiple of 32 in [32, 256]; feature
- *   maps identity, ELU+1, FAVOR+, DPFP; float32 and bfloat16.  Other
- *   combinations return LIN_ATTN_ERR_UNSUPPORTED.
+ * GPU coverage.  d == dv == 64; r a multiple of 32 in [32, 512] (the
+ *   backward and the projected calls: [32, 256]); feature maps identity,
+ *   ELU+1, FAVOR+, DPFP; float32 and bfloat16.  Other combinations return
+ *   LIN_ATTN_ERR_UNSUPPORTED.  r = 256 is the Performer's choice for
+ *   d = 64 ([PF] sec. 2) and 384 = d log2 d one reading of its cost
+ *   statement; the pages put the useful range up to r ~ 1024 ([PF] sec. 4).
  */
 #ifndef LIN_ATTN_H
 #define LIN_ATTN_H

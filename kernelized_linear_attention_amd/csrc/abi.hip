@@ -172,6 +172,7 @@ int backward_call(bool causal, const lin_attn_params* p, const void* q, const vo
         return LIN_ATTN_ERR_INVALID;
     if (rc != LIN_ATTN_OK) return rc;
     if (rs != LIN_ATTN_OK) return rs;
+    if (p->r > RMAX_BWD) return LIN_ATTN_ERR_UNSUPPORTED;
     if (B * H == 0 || N == 0) return LIN_ATTN_OK; // no element to write
     const int64_t BH = B * H;
     const BackwardLayout L = backward_layout(p, causal, BH, N);
@@ -282,7 +283,7 @@ int proj_checks(const lin_attn_params* p, const void* x, const void* w_q, const 
     if (d_model <= 0) return LIN_ATTN_ERR_INVALID;
     if (any && B * N > 0 && !ptr_ok(x)) return LIN_ATTN_ERR_INVALID;
     if (any && (!ptr_ok(w_q) || !ptr_ok(w_k) || !ptr_ok(w_v))) return LIN_ATTN_ERR_INVALID;
-    if (p->dtype != LIN_ATTN_BF16) return LIN_ATTN_ERR_UNSUPPORTED;
+    if (p->dtype != LIN_ATTN_BF16 || p->r > RMAX_BWD) return LIN_ATTN_ERR_UNSUPPORTED;
     if (d_model % 16 != 0 || d_model > 65536) return LIN_ATTN_ERR_UNSUPPORTED;
     // the projection GEMM's grid (one block per 128 tokens x 128 columns) in range
     if (B > 0 && N > ((int64_t)1 << 40) / B) return LIN_ATTN_ERR_UNSUPPORTED;
@@ -432,9 +433,11 @@ size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B,
     const int64_t BH = B * H;
     if (BH == 0 || N == 0) return 0;
     if (op == LIN_ATTN_OP_CAUSAL_VARLEN) return varlen_layout(p, B, H, N).bytes;
-    if (op == LIN_ATTN_OP_CAUSAL_PROJ || op == LIN_ATTN_OP_BIDIR_PROJ)
-        return proj_ws_bytes(op == LIN_ATTN_OP_CAUSAL_PROJ, p, BH, N);
-    if (op == LIN_ATTN_OP_BIDIR_BACKWARD || op == LIN_ATTN_OP_CAUSAL_BACKWARD)
+    const bool proj = op == LIN_ATTN_OP_CAUSAL_PROJ || op == LIN_ATTN_OP_BIDIR_PROJ;
+    const bool bwd = op == LIN_ATTN_OP_BIDIR_BACKWARD || op == LIN_ATTN_OP_CAUSAL_BACKWARD;
+    if ((proj || bwd) && p->r > RMAX_BWD) return 0; // unsupported there
+    if (proj) return proj_ws_bytes(op == LIN_ATTN_OP_CAUSAL_PROJ, p, BH, N);
+    if (bwd)
         return backward_layout(p, op == LIN_ATTN_OP_CAUSAL_BACKWARD, BH, N).floats * sizeof(float);
     return ws_floats(op, BH, plan_for(p, BH, N), p->r) * sizeof(float);
 }

@@ -9,7 +9,8 @@ namespace linattn {
 
 constexpr int D = 64;     // query/key width handled by the kernels
 constexpr int DV = 64;    // value width handled by the kernels
-constexpr int RMAX = 256; // largest feature width handled by the kernels
+constexpr int RMAX = 512; // largest feature width of the forward and decode kernels
+constexpr int RMAX_BWD = 256; // largest feature width of the backward and projected calls
 constexpr float LOG2E = 1.4426950408889634f;
 
 enum : int { PHI_IDENTITY = 0, PHI_ELU1 = 1, PHI_FAVOR = 2, PHI_DPFP = 3 };

@@ -73,8 +73,10 @@ template <> struct OmegaRow<float> {
 
 // NT threads per head (512 or 1024, NT dividing 16 r): the state is split
 // NT ways, 16 r / NT float4 per thread, so few registers hold it and many
-// waves stream it; threads tid < r also compute feature tid.
-template <typename T, int NT>
+// waves stream it; threads tid < r also compute feature tid.  RM: the
+// largest r of the instance (256, or RMAX): the register array of the
+// state is sized for it.
+template <typename T, int NT, int RM>
 __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
                                                const T* __restrict__ k,
                                                const T* __restrict__ v,
@@ -82,9 +84,9 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
                                                float* __restrict__ S, float* __restrict__ z,
                                                T* __restrict__ out) {
     __shared__ float uq_s[D], uk_s[D], v_s[DV];
-    __shared__ float pq_s[RMAX], pk_s[RMAX];
+    __shared__ float pq_s[RM], pk_s[RM];
     __shared__ float red_s[NT / 64][DV];
-    constexpr int MAXM = RMAX * DV / 4 / NT; // float4 of S per thread at r = RMAX
+    constexpr int MAXM = RM * DV / 4 / NT; // float4 of S per thread at r = RM
     __shared__ float scal_s[2 + NT / 64]; // |u_q|^2, |u_k|^2, then den per wave
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t bh = blockIdx.x;
@@ -227,16 +229,16 @@ __global__ __launch_bounds__(NT) void k_decode(Cfg c, const T* __restrict__ q,
     }
 }
 
-template <int NT>
+template <int NT, int RM>
 hipError_t launch_decode_nt(const Cfg& c, int dtype, const void* q, const void* k, const void* v,
                             const void* omega, int64_t BH, float* S, float* z, void* out,
                             hipStream_t st) {
     if (dtype == 0)
-        hipLaunchKernelGGL((k_decode<float, NT>), dim3((unsigned)BH), dim3(NT), 0, st, c,
+        hipLaunchKernelGGL((k_decode<float, NT, RM>), dim3((unsigned)BH), dim3(NT), 0, st, c,
                            (const float*)q, (const float*)k, (const float*)v,
                            (const float*)omega, S, z, (float*)out);
     else
-        hipLaunchKernelGGL((k_decode<bf16_raw, NT>), dim3((unsigned)BH), dim3(NT), 0, st, c,
+        hipLaunchKernelGGL((k_decode<bf16_raw, NT, RM>), dim3((unsigned)BH), dim3(NT), 0, st, c,
                            (const bf16_raw*)q, (const bf16_raw*)k, (const bf16_raw*)v,
                            (const bf16_raw*)omega, S, z, (bf16_raw*)out);
     return hipGetLastError();
@@ -250,8 +252,17 @@ hipError_t launch_decode_nt(const Cfg& c, int dtype, const void* q, const void* 
 hipError_t launch_decode(const Cfg& c, int dtype, const void* q, const void* k, const void* v,
                          const void* omega, int64_t BH, float* S, float* z, void* out,
                          hipStream_t st) {
-    if (c.r % 64 == 0) return launch_decode_nt<1024>(c, dtype, q, k, v, omega, BH, S, z, out, st);
-    return launch_decode_nt<512>(c, dtype, q, k, v, omega, BH, S, z, out, st);
+    // widths past 256 get their own instances, so that the r <= 256 ones keep
+    // their register count (a state array sized for r = 512 would issue
+    // twice the loads at r = 256)
+    if (c.r <= 256) {
+        if (c.r % 64 == 0)
+            return launch_decode_nt<1024, 256>(c, dtype, q, k, v, omega, BH, S, z, out, st);
+        return launch_decode_nt<512, 256>(c, dtype, q, k, v, omega, BH, S, z, out, st);
+    }
+    if (c.r % 64 == 0)
+        return launch_decode_nt<1024, RMAX>(c, dtype, q, k, v, omega, BH, S, z, out, st);
+    return launch_decode_nt<512, RMAX>(c, dtype, q, k, v, omega, BH, S, z, out, st);
 }
 
 } // namespace linattn

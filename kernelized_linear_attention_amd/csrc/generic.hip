@@ -62,7 +62,9 @@ __global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict_
                                                      int64_t G, int64_t seg_len,
                                                      const int64_t* __restrict__ tab,
                                                      float* __restrict__ ws, Proj P) {
-    constexpr int L = 64;
+    // 64-token chunks up to r = 256; 16 above, so that the feature tile
+    // (L x (r + 4) floats) stays within LDS
+    constexpr int L = FPT <= 8 ? 64 : 16;
     constexpr int R = 32 * FPT;
     constexpr int OL = R + 4;
     __shared__ float u_s[L * D];
@@ -457,7 +459,11 @@ __global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restri
                                                         const float* __restrict__ state,
                                                         int64_t st_bh, int64_t st_g,
                                                         T* __restrict__ out, Proj P) {
-    constexpr int L = 32;
+    // The state S (r x 64 floats) lives in LDS: 32-token chunks up to
+    // r = 256, 16 up to r = 384 and 4 up to r = 512 keep the state, the two
+    // feature tiles and the chunk within the CU's 160 KB.  The result does
+    // not depend on the chunk length beyond rounding.
+    constexpr int L = FPT <= 8 ? 32 : (FPT <= 12 ? 16 : 4);
     constexpr int R = 32 * FPT;
     constexpr int OL = R + 4;
     constexpr int LC = CAUSAL ? L : 1;
@@ -527,7 +533,8 @@ __global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restri
         }
 
         // readout against the carried-in state, plus the intra-chunk block
-        {
+        // (threads of tokens rt >= L, when L < 32, have no row)
+        if (rt < L) {
             float num[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) num[j] = 0.f;
@@ -602,21 +609,17 @@ void sums_fpt(const Cfg& c, const void* k, const void* v, const void* omega, Sha
                        sp.tab, ws, P);
 }
 
-template <typename T, bool PROJ>
+// The instance for r = 32 f (f = 1 .. 16; the projected kernels stop at 8).
+template <typename T, bool PROJ, int F = 1>
 hipError_t segment_sums_t(const Cfg& c, const void* k, const void* v, const void* omega, Shape s,
                           SegPlan sp, float* ws, const Proj& P, hipStream_t st) {
-    switch (c.r / 32) {
-    case 1: sums_fpt<T, 1, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
-    case 2: sums_fpt<T, 2, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
-    case 3: sums_fpt<T, 3, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
-    case 4: sums_fpt<T, 4, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
-    case 5: sums_fpt<T, 5, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
-    case 6: sums_fpt<T, 6, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
-    case 7: sums_fpt<T, 7, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
-    case 8: sums_fpt<T, 8, PROJ>(c, k, v, omega, s, sp, ws, P, st); break;
-    default: return hipErrorInvalidValue;
+    if constexpr (F > (PROJ ? RMAX_BWD : RMAX) / 32) {
+        return hipErrorInvalidValue;
+    } else {
+        if (c.r != 32 * F) return segment_sums_t<T, PROJ, F + 1>(c, k, v, omega, s, sp, ws, P, st);
+        sums_fpt<T, F, PROJ>(c, k, v, omega, s, sp, ws, P, st);
+        return hipGetLastError();
     }
-    return hipGetLastError();
 }
 
 template <typename T, int FPT, bool PROJ>
@@ -634,21 +637,20 @@ void outputs_fpt(const Cfg& c, int causal, const void* q, const void* k, const v
                            sp.seg_len, sp.tab, sp.sub, state, sbh, sg, (T*)out, P);
 }
 
-template <typename T, bool PROJ>
+template <typename T, bool PROJ, int F = 1>
 hipError_t segment_outputs_t(const Cfg& c, int causal, const void* q, const void* k,
                              const void* v, const void* omega, Shape s, SegPlan sp,
                              const float* state, int64_t sbh, int64_t sg, void* out,
                              const Proj& P, hipStream_t st) {
-#define LINATTN_OUTPUTS(F)                                                                        \
-    case F: outputs_fpt<T, F, PROJ>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, P, st); \
-        break;
-    switch (c.r / 32) {
-        LINATTN_OUTPUTS(1) LINATTN_OUTPUTS(2) LINATTN_OUTPUTS(3) LINATTN_OUTPUTS(4)
-        LINATTN_OUTPUTS(5) LINATTN_OUTPUTS(6) LINATTN_OUTPUTS(7) LINATTN_OUTPUTS(8)
-    default: return hipErrorInvalidValue;
+    if constexpr (F > (PROJ ? RMAX_BWD : RMAX) / 32) {
+        return hipErrorInvalidValue;
+    } else {
+        if (c.r != 32 * F)
+            return segment_outputs_t<T, PROJ, F + 1>(c, causal, q, k, v, omega, s, sp, state, sbh,
+                                                     sg, out, P, st);
+        outputs_fpt<T, F, PROJ>(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, P, st);
+        return hipGetLastError();
     }
-#undef LINATTN_OUTPUTS
-    return hipGetLastError();
 }
 
 __global__ __launch_bounds__(NT) void k_fill_zero(float* __restrict__ p, int64_t n) {

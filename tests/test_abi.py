@@ -160,10 +160,11 @@ def test_pointers_sizes_and_enums():
 def test_outside_gpu_coverage_is_unsupported():
     assert bidir(params("elu1", r=32), d=32, dv=64) == UNSUPPORTED
     assert bidir(params(), dv=32) == UNSUPPORTED
-    assert bidir(params("favor", r=512)) == UNSUPPORTED
-    assert bidir(params("favor", r=48)) == UNSUPPORTED
-    assert causal(params("dpfp", r=384, nu=3)) == UNSUPPORTED
+    assert bidir(params("favor", r=544)) == UNSUPPORTED   # r <= 512 on the forward kernels
+    assert bidir(params("favor", r=48)) == UNSUPPORTED    # a multiple of 32
+    assert causal(params("dpfp", r=640, nu=5)) == UNSUPPORTED
     assert decode(params("favor", r=272)) == UNSUPPORTED
+    assert decode(params("favor", r=576)) == UNSUPPORTED
     # 64- and 128-token intra-chunk blocks are valid but run by no kernel
     assert causal(params(), chunk=64) == UNSUPPORTED
     assert causal(params(), chunk=128) == UNSUPPORTED
@@ -197,7 +198,7 @@ def test_noalloc_arguments():
     assert causal_noalloc(p, state_in=2) == INVALID
     assert causal_noalloc(p, S=None) == INVALID
     assert causal_noalloc(p, chunk=64) == UNSUPPORTED
-    assert causal_noalloc(params("favor", r=512)) == UNSUPPORTED
+    assert causal_noalloc(params("favor", r=544)) == UNSUPPORTED
     assert causal_noalloc(p, H=0) == OK
     # one (S | z) block of 66,560 bytes per head at least: 1024 heads need 68 MB
     big = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, p, 4, 256, 100, 64, 64, 0)
@@ -276,7 +277,7 @@ def test_varlen_arguments():
     assert varlen(p, state_in=2) == INVALID
     assert varlen(p, S=None) == INVALID
     assert varlen(p, ptr=None) == INVALID
-    assert varlen(params("favor", r=512)) == UNSUPPORTED
+    assert varlen(params("favor", r=544)) == UNSUPPORTED
     need = binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_VARLEN, p, 2, 2, 100, 64, 64)
     assert need > 0
     assert varlen(p, ws_bytes=need - 8) == WORKSPACE
@@ -335,7 +336,10 @@ def test_backward_arguments(fn):
     assert backward(p, fn, omega=None) == INVALID
     assert backward(p, fn, ws=FAKE + 4) == INVALID
     assert backward(params(eps=0.0), fn) == INVALID
-    assert backward(params("favor", r=512), fn) == UNSUPPORTED
+    assert backward(params("favor", r=512), fn) == UNSUPPORTED   # r <= 256 for the backward
+    assert backward(params("dpfp", r=384, nu=3), fn) == UNSUPPORTED
+    op_ = binding.OP_BIDIR_BACKWARD if "bidir" in fn else binding.OP_CAUSAL_BACKWARD
+    assert binding.lin_attn_workspace_bytes(op_, params("favor", r=384), 1, 2, 100, 64, 64) == 0
     assert backward(p, fn, d=32) == UNSUPPORTED
     op = binding.OP_BIDIR_BACKWARD if "bidir" in fn else binding.OP_CAUSAL_BACKWARD
     need = binding.lin_attn_workspace_bytes(op, p, 1, 2, 100, 64, 64)
@@ -392,6 +396,7 @@ def test_projected_call_arguments(call):
     assert call(p, dm=520) == UNSUPPORTED               # not a multiple of 16
     assert call(params(dtype=0)) == UNSUPPORTED          # bfloat16 tokens and weights only
     assert call(p, d=32) == UNSUPPORTED
+    assert call(params("favor", r=384)) == UNSUPPORTED   # r <= 256 for the projected calls
     op = binding.OP_CAUSAL_PROJ if call is causal_proj else binding.OP_BIDIR_PROJ
     need = binding.lin_attn_workspace_bytes(op, p, 1, 2, 100, 64, 64)
     assert need > 0

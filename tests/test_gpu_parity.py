@@ -94,6 +94,82 @@ def test_causal_from_carried_state(gpu_lib, kind, dtype, r, nu, sum_norm, scale)
     assert_parity(z, rz, tol, "carried z")
 
 
+# ---------------------------------------------------------------------------
+# Wide feature maps (r = 384 = d log2 d, 480, 512): forward and decode only.
+# The vector kernels keep S in LDS and shorten the chunk as r grows (16 tokens
+# up to r = 384, 4 up to 512), so N = 300 spans many chunks and a ragged tail.
+# ---------------------------------------------------------------------------
+WIDE_MAPS = [
+    ("favor", torch.float32, 384, 1, False, 64 ** -0.25),
+    ("favor", torch.bfloat16, 384, 1, True, 64 ** -0.25),
+    ("favor", torch.bfloat16, 512, 1, False, 64 ** -0.25),
+    ("favor", torch.float32, 480, 1, False, 64 ** -0.25),
+    ("dpfp", torch.float32, 384, 3, True, 1.0),
+    ("dpfp", torch.bfloat16, 512, 4, False, 1.0),
+    ("dpfp", torch.float32, 512, 4, True, 1.0),
+]
+WIDE_IDS = [f"{k}-{str(dt)[6:]}-r{r}{'-sn' if sn else ''}" for k, dt, r, _, sn, _ in WIDE_MAPS]
+
+
+@pytest.mark.parametrize("kind,dtype,r,nu,sum_norm,scale", WIDE_MAPS, ids=WIDE_IDS)
+def test_wide_featuremap(gpu_lib, kind, dtype, r, nu, sum_norm, scale):
+    c = Case(111, 2, 3, 67, kind, dtype, r=r, nu=nu)
+    got = gpu_lib.lin_attn_featuremap(c.q, kind, **c.gkw(sum_norm=sum_norm, scale=scale))
+    ref = oracle.featuremap(c.qh, kind, **c.okw(sum_norm=sum_norm, scale=scale))
+    assert_parity(got, ref, 1e-4, f"featuremap {kind} r={r}")
+
+
+@pytest.mark.parametrize("norm", ["attn", "none"])
+@pytest.mark.parametrize("kind,dtype,r,nu,sum_norm,scale", WIDE_MAPS, ids=WIDE_IDS)
+def test_wide_bidir_and_causal(gpu_lib, kind, dtype, r, nu, sum_norm, scale, norm):
+    c = Case(112, 2, 2, 300, kind, dtype, r=r, nu=nu)
+    kw = dict(sum_norm=sum_norm, scale=scale, norm=norm)
+    tol = TOL[dtype]
+    S = torch.empty((2, 2, r, 64), device="cuda")
+    z = torch.empty((2, 2, r), device="cuda")
+    out = gpu_lib.lin_attn_bidir(c.q, c.k, c.v, kind, S_out=S, z_out=z, **c.gkw(**kw))
+    ro, rS, rz = oracle.bidir(c.qh, c.kh, c.vh, kind, **c.okw(**kw))
+    assert_parity(out, ro, tol, "bidir out")
+    assert_parity(S, rS, tol, "bidir S")
+    assert_parity(z, rz, tol, "bidir z")
+    for n_seg in (0, 3):
+        out, S, z = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, kind, n_seg=n_seg,
+                                                    **c.gkw(**kw))
+        ro, rS, rz = oracle.causal(c.qh, c.kh, c.vh, kind, **c.okw(**kw))
+        assert_parity(out, ro, tol, f"causal out n_seg={n_seg}")
+        assert_parity(S, rS, tol, f"causal S n_seg={n_seg}")
+        assert_parity(z, rz, tol, f"causal z n_seg={n_seg}")
+
+
+@pytest.mark.parametrize("kind,dtype,r,nu,sum_norm,scale", WIDE_MAPS, ids=WIDE_IDS)
+def test_wide_causal_from_carried_state_and_decode(gpu_lib, kind, dtype, r, nu, sum_norm, scale):
+    """A prefill from a carried state, then one decode step from its final
+    state, both against the oracle (r = 480 takes the 512-thread decode)."""
+    pre = Case(113, 2, 3, 40, kind, dtype, r=r, nu=nu, rep=1)
+    c = Case(113, 2, 3, 150, kind, dtype, r=r, nu=nu, rep=2)
+    if kind == "favor":
+        pre.omega, pre.omega_h = c.omega, c.omega_h
+    kw = dict(sum_norm=sum_norm, scale=scale, norm="attn")
+    tol = TOL[dtype]
+    S0, z0 = oracle_prefix_state(pre.qh, pre.kh, pre.vh, kind, **pre.okw(**kw))
+    out, S, z = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, kind, S=torch.from_numpy(S0).cuda(),
+                                                z=torch.from_numpy(z0).cuda(), state_in=True,
+                                                **c.gkw(**kw))
+    ro, rS, rz = oracle.causal(c.qh, c.kh, c.vh, kind, S0=S0, z0=z0, **c.okw(**kw))
+    assert_parity(out, ro, tol, "carried out")
+    assert_parity(S, rS, tol, "carried S")
+    S1, z1 = rS.astype(np.float32), rz.astype(np.float32)
+    tok = Case(113, 2, 3, 1, kind, dtype, r=r, nu=nu, rep=3)
+    q, k, v = (t[:, :, 0].contiguous() for t in (tok.q, tok.k, tok.v))
+    Sd, zd = torch.from_numpy(S1).cuda(), torch.from_numpy(z1).cuda()
+    od = gpu_lib.lin_attn_decode_step(q, k, v, Sd, zd, kind, omega=c.omega, nu=nu, **kw)
+    rd, rSd, rzd = oracle.decode(host(q), host(k), host(v), S1, z1, kind, omega=c.omega_h, nu=nu,
+                                 **kw)
+    assert_parity(od, rd, tol, "decode out")
+    assert_parity(Sd, rSd, tol, "decode S")
+    assert_parity(zd, rzd, tol, "decode z")
+
+
 # feature widths that are not multiples of 64 take the 512-thread decode kernel
 DECODE_MAPS = MAPS + [
     ("favor", torch.float32, 96, 1, False, 64 ** -0.25),

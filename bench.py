@@ -5,11 +5,14 @@ N=65536, d=64, r=256, bf16 inputs, float32 state): feature map, masked
 intra-chunk block, inter-chunk readout and state update, segment carry.
 The same run also times the 12-layer batched decode (B=256, H=8, fp32 state
 read-modify-written in HBM), the bidirectional FAVOR+ pass (B=4, H=8,
-N=4096), the packed prefill, the prefill from 512-wide tokens with the q/k/v
-projection fused in, and the backward passes of the causal and bidirectional
-workloads, and reports each against its roofline.  Inputs are synthetic
-(seeded N(0,1)), resident in HBM before timing starts; two input sets
-alternate so that the 256 MB last-level cache cannot hold a step's inputs.
+N=4096), the small ELU+1 workload (B=1, H=8, N=256, fp32), the DPFP causal
+workload (B=8, H=8, N=2048, nu=2, fp32), the packed prefill, the prefill
+from 512-wide tokens, and the backward passes of the causal and
+bidirectional workloads, and reports each against its roofline; plus a
+device copy (the achievable HBM bandwidth) and the GPU clock sampled under
+the prefill's load.  Inputs are synthetic (seeded N(0,1)), resident in HBM
+before timing starts; enough input sets rotate that a step's inputs are not
+in the 256 MB last-level cache from an earlier step.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
 [--gpus 1] [--no-cpu-baseline]
@@ -39,6 +42,20 @@ def favor_alg_flops_per_tok_head(r=256, d=64, dv=64):
     return 4 * r * d + 4 * r * dv + 3 * r
 
 
+def elu1_alg_flops_per_tok_head(mode, r=64, dv=64):
+    """ELU+1 (r = d): the map (~r ops) and the two contractions phi(K)^T V
+    and phi(Q) S (2 * 2 r dv), denominators and z (~3r); the causal form
+    adds the masked intra-chunk block, which the count leaves out (the
+    reassociated cost, as for FAVOR+)."""
+    return 4 * r * dv + 4 * r
+
+
+def dpfp_alg_flops_per_tok_head(r=256, dv=64):
+    """DPFP with sum normalisation, NONE readout: the r feature products,
+    the sum and the scaling (~3r), phi(K)^T V and phi(Q) S (2 * 2 r dv)."""
+    return 4 * r * dv + 3 * r
+
+
 def backward_alg_flops_per_tok_head(r=256, d=64, dv=64):
     """Algorithmic flops of the backward pass for one token of one head,
     counting each product once (no recomputation): q and k projections
@@ -60,8 +77,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "bidir", "varlen", "backward",
-                                       "proj"],
+    ap.add_argument("--only", choices=["prefill", "decode", "bidir", "elu1", "dpfp", "varlen",
+                                       "backward", "proj", "copy"],
                     default=None,
                     help="run one section only (for profiling)")
     return ap.parse_args()
@@ -151,6 +168,9 @@ def main():
             "kernel": "lin_attn_causal_chunked (whole call)",
             "alg_flops_per_launch": flops, "avg_launch_ms": call_ms,
         }
+        # the GFX clock under this load: amd-smi's reading (through torch),
+        # sampled while ~0.4 s of prefill calls are queued (not timed)
+        result["clock"] = clock_under_load(lambda i: step(i), torch, dev, call_ms)
         del sets, out, ws
 
     # ------------------------------------------------------------------ decode
@@ -221,9 +241,10 @@ def main():
     wb = workloads.FAVOR_BIDIR
     if args.only in (None, "bidir"):
         sb = workloads.scale_of(wb)
+        # 6 input sets of 50 MB: 300 MB rotate through the 256 MB cache
         bsets = []
-        for rep in range(2):
-            q, k, v = (to_dev(inputs.normal((wb.B, wb.H, wb.N, wb.d), wb.wid, t, rep))
+        for rep_ in range(6):
+            q, k, v = (to_dev(inputs.normal((wb.B, wb.H, wb.N, wb.d), wb.wid, t, rep_ % 2))
                        for t in (inputs.T_Q, inputs.T_K, inputs.T_V))
             bsets.append((q, k, v))
         om = to_dev(inputs.orf_omega(wb.r, wb.d, wb.wid))
@@ -233,7 +254,7 @@ def main():
         bws = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
         def bstep(i):
-            q, k, v = bsets[i % 2]
+            q, k, v = bsets[i % 6]
             binding.lin_attn_bidir(q, k, v, "favor", omega=om, scale=sb, eps=wb.eps, out=bout,
                                    workspace=bws)
 
@@ -243,8 +264,108 @@ def main():
         bach = bflops / (float(np.mean(per)) * 1e-3) / 1e12
         result["bidir"] = {"workload": wb.name, "B": wb.B, "H": wb.H, "N": wb.N, "r": wb.r,
                            "ms_per_step": bms, "tokens_per_s": wb.B * wb.N / (bms * 1e-3),
-                           "tflops_alg": bach, "frac_mfma": bach / PEAK_BF16_TFLOPS}
+                           "roofline": {"bound": "mfma", "achieved": bach,
+                                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": bach / PEAK_BF16_TFLOPS,
+                                        "traffic": stored_traffic("bidir"),
+                                        "kernel": "lin_attn_bidir (whole call)",
+                                        "alg_flops_per_launch": bflops,
+                                        "avg_launch_ms": float(np.mean(per))}}
         del bsets
+
+    # ------------------------------------------------------------------ ELU+1, small
+    we = workloads.ELU_SMALL
+    if args.only in (None, "elu1"):
+        eq, ek, ev = (to_dev(inputs.normal((we.B, we.H, we.N, we.d), we.wid, t, 0), torch.float32)
+                      for t in (inputs.T_Q, inputs.T_K, inputs.T_V))
+        pe = binding.make_params("elu1", we.r, dtype=torch.float32, eps=we.eps)
+        eout = torch.empty((we.B, we.H, we.N, we.dv), device=dev)
+        eS = torch.empty((we.B, we.H, we.r, we.dv), device=dev)
+        ez = torch.empty((we.B, we.H, we.r), device=dev)
+        ews = {op: torch.empty(binding.lin_attn_workspace_bytes(op, pe, we.B, we.H, we.N, we.d,
+                                                                we.dv), dtype=torch.uint8,
+                               device=dev) for op in (binding.OP_BIDIR, binding.OP_CAUSAL)}
+        ef = {"bidir": lambda i: binding.lin_attn_bidir(eq, ek, ev, "elu1", eps=we.eps, out=eout,
+                                                        workspace=ews[binding.OP_BIDIR]),
+              "causal": lambda i: binding.lin_attn_causal_chunked(
+                  eq, ek, ev, "elu1", eps=we.eps, S=eS, z=ez, out=eout,
+                  workspace=ews[binding.OP_CAUSAL])}
+        esec = {"workload": we.name, "B": we.B, "H": we.H, "N": we.N, "r": we.r, "dtype": "f32"}
+        for form, fn in ef.items():
+            # device time per call: calls queued behind an untimed GPU-side spin
+            # and timed as a group (one call is shorter than its launch)
+            calls = 50
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for i in range(args.warmup):
+                fn(i)
+            torch.cuda._sleep(4_000_000)
+            e0.record()
+            for i in range(calls):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / calls * 1e3
+            total_ms, per = timed(fn, args.steps, args.warmup)
+            eflops = elu1_alg_flops_per_tok_head(form, we.r, we.dv) * we.B * we.H * we.N
+            ach = eflops / (us * 1e-6) / 1e12
+            esec[form] = {"us_per_call": us, "ms_per_step": total_ms / args.steps,
+                          "roofline": {"bound": "alu", "achieved": ach,
+                                       "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": ach / PEAK_FP32_VALU_TFLOPS,
+                                       "kernel": f"lin_attn_{'bidir' if form == 'bidir' else 'causal_chunked'} (whole call, fp32 vector kernels)",
+                                       "alg_flops_per_launch": eflops,
+                                       "avg_launch_ms": us * 1e-3}}
+        result["elu1"] = esec
+
+    # ------------------------------------------------------------------ DPFP causal
+    wdp = workloads.DPFP_CAUSAL
+    if args.only in (None, "dpfp"):
+        # 3 input sets of 100 MB (fp32): 300 MB rotate through the 256 MB cache
+        dsets = [tuple(to_dev(inputs.normal((wdp.B, wdp.H, wdp.N, wdp.d), wdp.wid, t, rep_ % 2),
+                              torch.float32) for t in (inputs.T_Q, inputs.T_K, inputs.T_V))
+                 for rep_ in range(3)]
+        pdp = binding.make_params("dpfp", wdp.r, nu=wdp.nu, sum_norm=wdp.sum_norm, norm=wdp.norm,
+                                  dtype=torch.float32, eps=wdp.eps)
+        dws = torch.empty(binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, pdp, wdp.B, wdp.H,
+                                                           wdp.N, wdp.d, wdp.dv),
+                          dtype=torch.uint8, device=dev)
+        dout = torch.empty((wdp.B, wdp.H, wdp.N, wdp.dv), device=dev)
+        dS = torch.empty((wdp.B, wdp.H, wdp.r, wdp.dv), device=dev)
+        dz = torch.empty((wdp.B, wdp.H, wdp.r), device=dev)
+
+        def dpstep(i):
+            q, k, v = dsets[i % 3]
+            binding.lin_attn_causal_chunked(q, k, v, "dpfp", nu=wdp.nu, sum_norm=wdp.sum_norm,
+                                            norm=wdp.norm, eps=wdp.eps, S=dS, z=dz, out=dout,
+                                            workspace=dws)
+
+        total_ms, per = timed(dpstep, args.steps, args.warmup)
+        dflops = dpfp_alg_flops_per_tok_head(wdp.r, wdp.dv) * wdp.B * wdp.H * wdp.N
+        dach = dflops / (float(np.mean(per)) * 1e-3) / 1e12
+        result["dpfp"] = {"workload": wdp.name, "B": wdp.B, "H": wdp.H, "N": wdp.N, "r": wdp.r,
+                          "nu": wdp.nu, "sum_norm": wdp.sum_norm, "norm": wdp.norm,
+                          "dtype": "f32", "ms_per_step": total_ms / args.steps,
+                          "tokens_per_s": wdp.B * wdp.N / (total_ms / args.steps * 1e-3),
+                          "roofline": {"bound": "alu", "achieved": dach,
+                                       "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": dach / PEAK_FP32_VALU_TFLOPS,
+                                       "kernel": "lin_attn_causal_chunked (whole call, fp32 vector kernels)",
+                                       "alg_flops_per_launch": dflops,
+                                       "avg_launch_ms": float(np.mean(per))}}
+        del dsets
+
+    # ------------------------------------------------------------------ device copy
+    if args.only in (None, "copy"):
+        # the achievable HBM bandwidth in this run: torch's device-to-device
+        # copy of 2 GiB (read + write), well past the 256 MB cache
+        src = torch.empty(1 << 31, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        cms, cper = timed(lambda i: dst.copy_(src), max(5, args.steps // 2), 2)
+        cbytes = 2 * src.numel()
+        result["hbm_copy"] = {"bytes_per_copy": cbytes, "GBps": cbytes / (float(np.median(cper)) * 1e-3) / 1e9,
+                              "peak": PEAK_HBM_GBPS, "kernel": "torch copy_ (2 GiB)"}
+        del src, dst
 
     # ------------------------------------------------------------------ packed sequences
     wv = workloads.FAVOR_VARLEN
@@ -419,13 +540,40 @@ def stored_traffic(section):
 
 
 def kernel_source_hash():
+    """sha256 over the kernel sources with comments and whitespace removed:
+    an edit to a comment keeps stored counter records valid, any change to
+    the code invalidates all of them."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kernelized_linear_attention_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()
+
+
+def strip_comments(src):
+    """C/C++ source without // and /* */ comments (string and character
+    literals kept) and without whitespace."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "".join("".join(out).split())
 
 
 def cpu_baseline(w, scale):
@@ -450,9 +598,53 @@ def cpu_baseline(w, scale):
         runs.append(time.perf_counter() - t0)
     dt = sorted(runs)[1]
     cores = min(oracle.threads(), w.B * w.H)
+    # one thread (the oracle's OpenMP runs one head per thread): one head,
+    # the first n1 tokens, which is the same arithmetic per token-head
+    n1 = min(n, int(os.environ.get("LINATTN_CPU_SAMPLE_TOKENS_1T", "16384")))
+    t0 = time.perf_counter()
+    oracle.causal(q[:1, :1, :n1].copy(), k[:1, :1, :n1].copy(), v[:1, :1, :n1].copy(), "favor",
+                  omega=om, scale=scale, eps=w.eps)
+    dt1 = time.perf_counter() - t0
     return {"value": w.B * n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"causal FAVOR+ oracle (fp64), B={w.B} H={w.H}, first {n} of {w.N} tokens; "
-                      f"median of 3 runs {dt:.2f} s on {cores} threads (OpenMP over heads)"}
+                      f"median of 3 runs {dt:.2f} s on {cores} threads (OpenMP over heads)",
+            "host_cpu": host_cpu_model(), "host_nproc": os.cpu_count(),
+            "host_cpus_usable": len(os.sched_getaffinity(0)),
+            "one_thread": {"token_heads_per_s": n1 / dt1,
+                           "tokens_per_s_equiv": n1 / dt1 / (w.B * w.H),
+                           "sample": f"1 head, first {n1} tokens, 1 thread, {dt1:.2f} s"}}
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def clock_under_load(step, torch, dev, call_ms):
+    """GFX clock (MHz) read through amd-smi (torch.cuda.clock_rate) while
+    prefill calls are queued on the GPU; None where the reading is not
+    available."""
+    try:
+        calls = max(50, int(400.0 / max(call_ms, 1e-3)))
+        for i in range(calls):
+            step(i)
+        samples = []
+        for _ in range(5):
+            time.sleep(0.03)
+            samples.append(int(torch.cuda.clock_rate(dev)))
+        torch.cuda.synchronize()
+        return {"gfx_mhz_samples": samples, "gfx_mhz_median": float(sorted(samples)[2]),
+                "nominal_mhz": 2400, "source": "amd-smi GFX clock via torch.cuda.clock_rate, "
+                "sampled every 30 ms while 0.4 s of prefill calls run"}
+    except Exception as e:  # the reading is context, never a failure of the bench
+        torch.cuda.synchronize()
+        return {"gfx_mhz_median": None, "error": str(e)[:200]}
 
 
 if __name__ == "__main__":

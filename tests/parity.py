@@ -7,6 +7,9 @@ with tol = 1e-4 for float32 inputs and 2e-2 for bfloat16 inputs (float32
 accumulation).  The oracle always receives the inputs the GPU received,
 after rounding to the compute dtype, upcast exactly to float64.
 """
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -50,8 +53,22 @@ def assert_parity(gpu, ref, tol, what, lead_dims=2):
     assert np.all(np.isfinite(host(gpu) if isinstance(gpu, torch.Tensor) else gpu)), what
     g = host(gpu) if isinstance(gpu, torch.Tensor) else gpu
     e_max, e_fro = slice_errors(g, ref, lead_dims)
+    record_margin(what, e_max, e_fro, tol)
     assert e_max <= tol and e_fro <= tol, f"{what}: max-rel {e_max:.3e}, fro-rel {e_fro:.3e} > {tol}"
     return e_max, e_fro
+
+
+def record_margin(what, e_max, e_fro, tol):
+    """Appends the achieved errors of one comparison to the JSON-lines file
+    named by LINATTN_PARITY_LOG (when set), so that the margins under the
+    tolerance can be summarised after a run."""
+    log = os.environ.get("LINATTN_PARITY_LOG")
+    if not log:
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    with open(log, "a") as f:
+        f.write(json.dumps({"test": test, "what": what, "max_rel": float(e_max),
+                            "fro_rel": float(e_fro), "tol": tol}) + "\n")
 
 
 class Case:

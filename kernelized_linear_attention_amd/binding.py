@@ -16,7 +16,9 @@ import os
 import torch  # loaded first: the library binds to the HIP runtime torch already loaded
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+# LINATTN_LIBRARY names another build of the same library (the host-side
+# sanitizer build of tests/sanitizers.py); there is no other choice of code.
+LIB_PATH = os.environ.get("LINATTN_LIBRARY") or os.path.join(_HERE, "liblinattn.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
                       "`python kernelized_linear_attention_amd/build.py`")

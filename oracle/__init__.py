@@ -32,7 +32,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# LINATTN_ORACLE_LIB names another build of oracle.c (the sanitizer build of
+# tests/sanitizers.py)
+_LIB_PATH = os.environ.get("LINATTN_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _KINDS = {"identity": 0, "elu1": 1, "favor": 2, "dpfp": 3}
 _NORMS = {"attn": 0, "none": 1}

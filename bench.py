@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "causal FAVOR+ prefill tokens/s + % MFMA peak (r=256,d=64); decode GB/s % HBM"
 
 # MI355X published peaks
+SETTLE_S = 0.25  # untimed seconds of each section's own calls before its timing
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # HBM3E
 PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector ALU
@@ -127,6 +128,24 @@ def main():
         torch.cuda.synchronize()
         return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in evs]
 
+    def settle(fn, seconds=SETTLE_S):
+        """Runs fn(i) back to back for about `seconds` (untimed) and returns
+        the number of calls.  On this chip every kernel of a workload runs
+        ~20 % slower for its first ~50 ms of sustained calls (measured on the
+        prefill: outputs kernel 155 -> 127 us, segment sums 64 -> 53 us, over
+        the first ~300 calls), and a copy or matrix-multiply load beforehand
+        does not shorten that; so each section first runs its own calls for
+        this long, then does its W warmup and K timed steps."""
+        torch.cuda.synchronize()
+        t_end = time.time() + seconds
+        n = 0
+        while time.time() < t_end:
+            for _ in range(8):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+        return n
+
     # ------------------------------------------------------------------ prefill
     w = workloads.FAVOR_CAUSAL
     scale = workloads.scale_of(w)
@@ -151,6 +170,13 @@ def main():
             binding.lin_attn_causal_chunked(q, k, v, "favor", omega=om, scale=scale, eps=w.eps,
                                             chunk=chunk, S=S, z=z, out=out, workspace=ws)
 
+        # the device's first K calls of this workload (reported, not the value)
+        cold_ms, cold_per = timed(step, args.steps, args.warmup)
+        # the GFX clock under this load: amd-smi's reading (through torch),
+        # sampled while ~0.4 s of prefill calls are queued (not timed); these
+        # calls also bring the device to its steady state (settle)
+        clock = clock_under_load(lambda i: step(i), torch, dev, float(np.mean(cold_per)))
+        n_settle = settle(step)
         total_ms, per = timed(step, args.steps, args.warmup)
         ms = total_ms / args.steps
         call_ms = float(np.mean(per))
@@ -168,9 +194,15 @@ def main():
             "kernel": "lin_attn_causal_chunked (whole call)",
             "alg_flops_per_launch": flops, "avg_launch_ms": call_ms,
         }
-        # the GFX clock under this load: amd-smi's reading (through torch),
-        # sampled while ~0.4 s of prefill calls are queued (not timed)
-        result["clock"] = clock_under_load(lambda i: step(i), torch, dev, call_ms)
+        result["clock"] = clock
+        result["settle"] = {
+            "seconds_per_section": SETTLE_S, "prefill_calls": n_settle,
+            "cold_ms_per_step": cold_ms / args.steps,
+            "cold_avg_launch_ms": float(np.mean(cold_per)),
+            "note": "each section runs its own calls, untimed, for the seconds above (the "
+                    "prefill: also the 0.4 s of clock sampling) before its W warmup and K timed "
+                    "steps; cold_* are the prefill's first W + K calls on the device, timed the "
+                    "same way"}
         del sets, out, ws
 
     # ------------------------------------------------------------------ decode
@@ -196,6 +228,7 @@ def main():
                 binding.lin_attn_decode_step(q, k, v, S, z, "favor", omega=om, scale=sd,
                                              eps=wd.eps, out=o)
 
+        settle(dstep)
         total_ms, _ = timed(dstep, args.steps, args.warmup)
         dms = total_ms / args.steps
         # Kernel time per launch: the host needs longer to issue a launch through
@@ -258,6 +291,7 @@ def main():
             binding.lin_attn_bidir(q, k, v, "favor", omega=om, scale=sb, eps=wb.eps, out=bout,
                                    workspace=bws)
 
+        settle(bstep)
         total_ms, per = timed(bstep, args.steps, args.warmup)
         bms = total_ms / args.steps
         bflops = favor_alg_flops_per_tok_head(wb.r, wb.d, wb.dv) * wb.B * wb.H * wb.N
@@ -295,7 +329,7 @@ def main():
             # device time per call: calls queued behind an untimed GPU-side spin
             # and timed as a group (one call is shorter than its launch)
             calls = 50
-            torch.cuda.synchronize()
+            settle(fn)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             for i in range(args.warmup):
                 fn(i)
@@ -340,6 +374,7 @@ def main():
                                             norm=wdp.norm, eps=wdp.eps, S=dS, z=dz, out=dout,
                                             workspace=dws)
 
+        settle(dpstep)
         total_ms, per = timed(dpstep, args.steps, args.warmup)
         dflops = dpfp_alg_flops_per_tok_head(wdp.r, wdp.dv) * wdp.B * wdp.H * wdp.N
         dach = dflops / (float(np.mean(per)) * 1e-3) / 1e12
@@ -392,6 +427,7 @@ def main():
             binding.lin_attn_causal_varlen(q, k, v, cu, "favor", omega=om, scale=sv, eps=wv.eps,
                                            S=vS, z=vz, out=vout, workspace=vws)
 
+        settle(vstep)
         total_ms, per = timed(vstep, args.steps, args.warmup)
         vms = total_ms / args.steps
         vflops = favor_alg_flops_per_tok_head(wv.r, wv.d, wv.dv) * wv.H * wv.N
@@ -425,6 +461,7 @@ def main():
                 q, k, v, do = ksets[i % 2]
                 fn(q, k, v, do, "favor", omega=om, scale=sk, eps=wk.eps, workspace=kws)
 
+            settle(kstep)
             total_ms, per = timed(kstep, args.steps, args.warmup)
             kms = total_ms / args.steps
             kflops = backward_alg_flops_per_tok_head(wk.r, wk.d, wk.dv) * wk.B * wk.H * wk.N
@@ -467,11 +504,8 @@ def main():
                                          scale=sp_, eps=wp.eps, S=pS, z=pz, out=pout,
                                          workspace=pws)
 
-        total_ms, per = timed(pstep, args.steps, args.warmup)
-        pms = total_ms / args.steps
         proj_flops = 3 * 2 * dm * wp.d * wp.H * wp.B * wp.N
         att_flops = favor_alg_flops_per_tok_head(wp.r, wp.d, wp.dv) * wp.B * wp.H * wp.N
-        pach = (proj_flops + att_flops) / (float(np.mean(per)) * 1e-3) / 1e12
 
         # the unfused route for comparison: torch's matmul writes q, k, v, then
         # the matrix-core prefill reads them
@@ -487,8 +521,6 @@ def main():
                                             eps=wp.eps, chunk=32, S=pS, z=pz, out=pout,
                                             workspace=uws)
 
-        u_total, _ = timed(ustep, args.steps, args.warmup)
-
         # this library's unfused route: the projection GEMM writes q, k, v
         # head-major, then the matrix-core prefill reads them
         gq = torch.empty((wp.B, wp.H, wp.N, wp.d), device=dev, dtype=torch.bfloat16)
@@ -499,10 +531,22 @@ def main():
             binding.lin_attn_causal_chunked(gq, gk, gv, "favor", omega=om, scale=sp_, eps=wp.eps,
                                             chunk=32, S=pS, z=pz, out=pout, workspace=uws)
 
-        g_total, _ = timed(gstep, args.steps, args.warmup)
-        g_only, g_per = timed(lambda i: binding.lin_attn_qkv_project(psets[i % 2], wq, wk, wv,
-                                                                    wp.H, q=gq, k=gk, v=gv),
-                              args.steps, args.warmup)
+        def gonly(i):
+            binding.lin_attn_qkv_project(psets[i % 2], wq, wk, wv, wp.H, q=gq, k=gk, v=gv)
+
+        # The routes are timed in turn, twice, and the second round is
+        # reported: whichever route is timed first after the set-up runs
+        # ~15 % slow (measured: 0.439 then 0.371 ms for the same calls),
+        # which would otherwise decide the comparison.
+        for fn_ in (pstep, gstep, ustep):
+            settle(fn_)
+        for _round in range(2):
+            total_ms, per = timed(pstep, args.steps, args.warmup)
+            g_total, _ = timed(gstep, args.steps, args.warmup)
+            u_total, _ = timed(ustep, args.steps, args.warmup)
+            g_only, g_per = timed(gonly, args.steps, args.warmup)
+        pms = total_ms / args.steps
+        pach = (proj_flops + att_flops) / (float(np.mean(per)) * 1e-3) / 1e12
         g_ms = float(np.mean(g_per))
         g_tflops = proj_flops / (g_ms * 1e-3) / 1e12
         result["proj"] = {

@@ -35,6 +35,7 @@ SETTLE_S = 0.25  # untimed seconds of each section's own calls before its timing
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # HBM3E
 PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector ALU
+PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA
 
 
 def favor_alg_flops_per_tok_head(r=256, d=64, dv=64):
@@ -344,10 +345,10 @@ def main():
             eflops = elu1_alg_flops_per_tok_head(form, we.r, we.dv) * we.B * we.H * we.N
             ach = eflops / (us * 1e-6) / 1e12
             esec[form] = {"us_per_call": us, "ms_per_step": total_ms / args.steps,
-                          "roofline": {"bound": "alu", "achieved": ach,
-                                       "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": ach / PEAK_FP32_VALU_TFLOPS,
-                                       "kernel": f"lin_attn_{'bidir' if form == 'bidir' else 'causal_chunked'} (whole call, fp32 vector kernels)",
+                          "roofline": {"bound": "mfma", "achieved": ach,
+                                       "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": ach / PEAK_FP32_MFMA_TFLOPS,
+                                       "kernel": f"lin_attn_{'bidir' if form == 'bidir' else 'causal_chunked'} (whole call, fp32 matrix-core kernels)",
                                        "alg_flops_per_launch": eflops,
                                        "avg_launch_ms": us * 1e-3}}
         result["elu1"] = esec
@@ -382,10 +383,11 @@ def main():
                           "nu": wdp.nu, "sum_norm": wdp.sum_norm, "norm": wdp.norm,
                           "dtype": "f32", "ms_per_step": total_ms / args.steps,
                           "tokens_per_s": wdp.B * wdp.N / (total_ms / args.steps * 1e-3),
-                          "roofline": {"bound": "alu", "achieved": dach,
-                                       "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": dach / PEAK_FP32_VALU_TFLOPS,
-                                       "kernel": "lin_attn_causal_chunked (whole call, fp32 vector kernels)",
+                          "roofline": {"bound": "mfma", "achieved": dach,
+                                       "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": dach / PEAK_FP32_MFMA_TFLOPS,
+                                       "traffic": stored_traffic("dpfp"),
+                                       "kernel": "lin_attn_causal_chunked (whole call, fp32 matrix-core kernels)",
                                        "alg_flops_per_launch": dflops,
                                        "avg_launch_ms": float(np.mean(per))}}
         del dsets

@@ -88,17 +88,21 @@ SegPlan plan_for(const lin_attn_params* p, int64_t BH, int64_t N) {
 
 hipError_t segment_sums(const lin_attn_params* p, const Cfg& c, const void* k, const void* v,
                         const void* omega, Shape s, SegPlan sp, float* ws, hipStream_t st) {
-    return use_mfma(p) ? launch_favor_sums(c, k, v, omega, s, sp, ws, st)
-                       : launch_segment_sums(c, p->dtype, k, v, omega, s, sp, ws, st);
+    if (use_mfma(p)) return launch_favor_sums(c, k, v, omega, s, sp, ws, st);
+    if (f32mm_supported(c)) return launch_f32mm_sums(c, p->dtype, k, v, s, sp, ws, st);
+    return launch_segment_sums(c, p->dtype, k, v, omega, s, sp, ws, st);
 }
 
 hipError_t segment_outputs(const lin_attn_params* p, const Cfg& c, int causal, const void* q,
                            const void* k, const void* v, const void* omega, Shape s, SegPlan sp,
                            const float* state, int64_t sbh, int64_t sg, void* out,
                            hipStream_t st) {
-    return use_mfma(p) ? launch_favor_outputs(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st)
-                       : launch_segment_outputs(c, p->dtype, causal, q, k, v, omega, s, sp, state,
-                                                sbh, sg, out, st);
+    if (use_mfma(p))
+        return launch_favor_outputs(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st);
+    if (f32mm_supported(c))
+        return launch_f32mm_outputs(c, p->dtype, causal, q, k, v, s, sp, state, sbh, sg, out, st);
+    return launch_segment_outputs(c, p->dtype, causal, q, k, v, omega, s, sp, state, sbh, sg, out,
+                                  st);
 }
 
 // Packed batch (lin_attn_causal_varlen): the uniform planner over all tokens

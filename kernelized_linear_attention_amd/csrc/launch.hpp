@@ -166,6 +166,14 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 bool favor_mfma_supported(const Cfg& c, int dtype);
 // zw: optional per-token weights [BH, N] of the z sum (z = sum_t w_t phi(k_t));
 // NULL gives the plain sum.
+// float32 matrix-core kernels (mfma_f32.hip): identity and ELU+1 at r = 64,
+// DPFP at r = 128 and 256, float32 or bfloat16 inputs
+bool f32mm_supported(const Cfg& c);
+hipError_t launch_f32mm_sums(const Cfg& c, int dtype, const void* k, const void* v, Shape s,
+                             SegPlan sp, float* ws, hipStream_t st);
+hipError_t launch_f32mm_outputs(const Cfg& c, int dtype, int causal, const void* q, const void* k,
+                                const void* v, Shape s, SegPlan sp, const float* state,
+                                int64_t sbh, int64_t sg, void* out, hipStream_t st);
 hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const void* omega,
                              Shape s, SegPlan sp, float* ws, hipStream_t st,
                              const float* zw = nullptr);

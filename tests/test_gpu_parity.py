@@ -839,6 +839,51 @@ def test_causal_backward_matrix_core_route(gpu_lib, N, n_seg, norm):
     _assert_grads(got, ref, 2e-2, f"causal backward N={N} n_seg={n_seg} {norm}")
 
 
+F32MM_MAPS = [("identity", 64, 1), ("elu1", 64, 1), ("dpfp", 128, 1), ("dpfp", 256, 2)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind,r,nu", F32MM_MAPS, ids=[f"{k}-r{r}" for k, r, _ in F32MM_MAPS])
+def test_f32_matrix_core_route(gpu_lib, kind, r, nu, dtype):
+    """Identity, ELU+1 and DPFP run the increments, the chunked scan and the
+    bidirectional readout on the float32 matrix cores: one token, a chunk
+    less one, several chunks with a ragged tail, segment counts 1, 3, 5 and
+    automatic, both readouts, sum normalisation on and off, bitwise
+    repeatability, then a carried-in state."""
+    dt = DT[dtype]
+    tol = TOL[dt]
+    for i, (N, n_seg) in enumerate([(1, 0), (31, 0), (33, 1), (100, 3), (517, 0), (2000, 5)]):
+        sum_norm = kind != "identity" and i % 2 == 1
+        norm = "none" if kind == "identity" or i % 3 == 0 else "attn"
+        c = Case(140 + i, 2, 3, N, kind, dt, r=r, nu=nu)
+        kw = dict(sum_norm=sum_norm, norm=norm)
+        tag = f"{kind} r={r} {dtype} N={N} n_seg={n_seg} sum_norm={sum_norm} {norm}"
+        out, S, z = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, kind, n_seg=n_seg,
+                                                    **c.gkw(**kw))
+        o2, S2, z2 = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, kind, n_seg=n_seg,
+                                                     **c.gkw(**kw))
+        assert torch.equal(out, o2) and torch.equal(S, S2) and torch.equal(z, z2), tag
+        ro, rS, rz = oracle.causal(c.qh, c.kh, c.vh, kind, **c.okw(**kw))
+        assert_parity(out, ro, tol, f"{tag} causal out")
+        assert_parity(S, rS, tol, f"{tag} causal S")
+        assert_parity(z, rz, tol, f"{tag} causal z")
+        bo = gpu_lib.lin_attn_bidir(c.q, c.k, c.v, kind, n_seg=n_seg, **c.gkw(**kw))
+        rb, _, _ = oracle.bidir(c.qh, c.kh, c.vh, kind, **c.okw(**kw))
+        assert_parity(bo, rb, tol, f"{tag} bidir out")
+    norm = "none" if kind == "identity" else "attn"
+    kw = dict(sum_norm=kind == "dpfp", norm=norm)
+    pre = Case(150, 1, 2, 45, kind, dt, r=r, nu=nu, rep=1)
+    c = Case(150, 1, 2, 130, kind, dt, r=r, nu=nu, rep=2)
+    S0, z0 = oracle_prefix_state(pre.qh, pre.kh, pre.vh, kind, **pre.okw(**kw))
+    out, S, z = gpu_lib.lin_attn_causal_chunked(c.q, c.k, c.v, kind, S=torch.from_numpy(S0).cuda(),
+                                                z=torch.from_numpy(z0).cuda(), state_in=True,
+                                                n_seg=2, **c.gkw(**kw))
+    ro, rS, rz = oracle.causal(c.qh, c.kh, c.vh, kind, S0=S0, z0=z0, **c.okw(**kw))
+    assert_parity(out, ro, tol, f"{kind} carried out")
+    assert_parity(S, rS, tol, f"{kind} carried S")
+    assert_parity(z, rz, tol, f"{kind} carried z")
+
+
 # ---------------------------------------------------------------------------
 # Randomized configurations: a fixed-seed draw of shapes, maps, dtypes, segment
 # counts and readouts through every forward form, decode and both backwards

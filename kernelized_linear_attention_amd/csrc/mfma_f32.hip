@@ -27,7 +27,9 @@
 //   phase 3  (after a barrier) the block's masked row sums complete the
 //            denominators, and the block times V joins the readout.
 // Chunk c's outputs are normalised and stored after the next chunk's first
-// barrier, when all of its denominators are in LDS.
+// barrier, when all of its normalisers are in LDS.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace linattn {
@@ -63,31 +65,41 @@ __device__ __forceinline__ f32x4 mma16(f32x4 a, f32x4 b, f32x4 d) {
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 
-// Eight consecutive elements of one input row, raw (loaded one chunk ahead).
+// One output element through a buffer resource (byte offset; dropped past
+// the resource's range).
+template <typename T> __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t rs, int off, float y);
+template <> __device__ __forceinline__ void store_out<float>(__amdgpu_buffer_rsrc_t rs, int off, float y) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rs, off, 0, 0);
+}
+template <> __device__ __forceinline__ void store_out<bf16_raw>(__amdgpu_buffer_rsrc_t rs, int off, float y) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(y), rs, off, 0, 0);
+}
+
+// Columns 4b .. 4b + 3 and 32 + 4b .. 32 + 4b + 3 of one input row, raw
+// (loaded one chunk ahead).  The eight lanes of a token (b = 0 .. 7) thus
+// cover the row in 16-byte blocks that are adjacent across lanes.
 template <typename T> struct Row8;
 template <> struct Row8<float> {
     float4 a, b;
-    __device__ __forceinline__ void load(const float* p) {
-        a = reinterpret_cast<const float4*>(p)[0];
-        b = reinterpret_cast<const float4*>(p)[1];
+    __device__ __forceinline__ void load(const float* row, int blk) {
+        a = reinterpret_cast<const float4*>(row + 4 * blk)[0];
+        b = reinterpret_cast<const float4*>(row + 32 + 4 * blk)[0];
     }
-    __device__ __forceinline__ float get(int j) const {
-        const float4 x = j < 4 ? a : b;
-        switch (j & 3) {
-        case 0: return x.x;
-        case 1: return x.y;
-        case 2: return x.z;
-        default: return x.w;
-        }
-    }
+    __device__ __forceinline__ f32x4 lo() const { return f32x4{a.x, a.y, a.z, a.w}; }
+    __device__ __forceinline__ f32x4 hi() const { return f32x4{b.x, b.y, b.z, b.w}; }
 };
 template <> struct Row8<bf16_raw> {
-    uint4 a;
-    __device__ __forceinline__ void load(const bf16_raw* p) { a = *reinterpret_cast<const uint4*>(p); }
-    __device__ __forceinline__ float get(int j) const {
-        const uint32_t wd = (j >> 1) == 0 ? a.x : (j >> 1) == 1 ? a.y : (j >> 1) == 2 ? a.z : a.w;
-        return __uint_as_float((j & 1) ? (wd & 0xffff0000u) : (wd << 16));
+    uint2 a, b;
+    __device__ __forceinline__ void load(const bf16_raw* row, int blk) {
+        a = *reinterpret_cast<const uint2*>(row + 4 * blk);
+        b = *reinterpret_cast<const uint2*>(row + 32 + 4 * blk);
     }
+    static __device__ __forceinline__ f32x4 unpack(uint2 x) {
+        return f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                     __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
+    }
+    __device__ __forceinline__ f32x4 lo() const { return unpack(a); }
+    __device__ __forceinline__ f32x4 hi() const { return unpack(b); }
 };
 
 // LDS.  Feature tiles are [32 tokens][r + 4] (the padding keeps the 16-byte
@@ -106,7 +118,7 @@ template <int R, int MODE> struct SmemF32 {
     float vt[MODE == M_READOUT ? 4 : DV * VL];
     float as[MODE == M_CAUSAL ? CL * AL : 4];
     float z[MODE == M_SUMS ? 1 : 2][MODE == M_SUMS ? 4 : R];
-    float den[3][MODE == M_SUMS ? 4 : CL];
+    float den[3][MODE == M_SUMS ? 4 : CL]; // per token: 1 / max(den, eps), or 1
 };
 
 // Float offset of column `col` of token row t in a feature tile of width R.
@@ -115,47 +127,56 @@ __device__ __forceinline__ int fidx(int t, int col) {
     return t * (R + 4) + col;
 }
 
-// phi of token t for features [b r/8, (b + 1) r/8), from its staged (scaled)
-// input in the first 64 floats of row t of tile.  PHI is identity or ELU+1
-// (r = 64) or DPFP-nu (r = 2 d nu): feature f = i + 2d (s - 1) is
-// kt_i kt_{(i + s) mod 2d}, kt = relu([u, -u]) (Kernel Zoo sec. 6.3).
+// Float offset of token t in row `col` of V^T ([64][32]): 4-token blocks are
+// rotated by ((col / 4) mod 8), so that the eight lanes of a token, which
+// write rows 4b + j and 32 + 4b + j, hit distinct banks.
+__device__ __forceinline__ int vidx(int col, int t) {
+    return col * VL + (t ^ (((col >> 2) & 7) << 2));
+}
+
+// phi of token t for features 32 m + 4 b + e (m < r / 32, e < 4) into
+// f[4 m + e], from its staged (scaled) input in the first 64 floats of row t
+// of tile.  PHI is identity or ELU+1 (r = 64) or DPFP-nu (r = 2 d nu):
+// feature f = i + 2d (s - 1) is kt_i kt_{(i + s) mod 2d}, kt = relu([u, -u])
+// (Kernel Zoo sec. 6.3).
 template <int PHI, int R>
 __device__ __forceinline__ void token_features(const float* tile, int t, int b, float (&f)[R / 8]) {
-    constexpr int FB = R / 8;
     if constexpr (PHI == PHI_DPFP) {
-        const int f0 = FB * b;
-        const int s = f0 / (2 * D) + 1;
-        const int i0 = f0 & (2 * D - 1);
-        // kt_{i0 .. i0 + FB + 3}: a block of FB inputs of one sign (FB
-        // divides 64), then four more past it (mod 2d)
-        float kt[FB + 4];
-        {
-            const bool neg = (i0 & D) != 0;
+        constexpr int NU = R / (2 * D);
+        // kt_{32 mu + 4 b .. 32 mu + 4 b + 7} (mod 2d) for mu = 0 .. 3: two
+        // blocks of four inputs, each of one sign
+        float kt[4][8];
 #pragma unroll
-            for (int q4 = 0; q4 < FB / 4; ++q4) {
-                const f32x4 x = lds4(tile + fidx<R>(t, (i0 & (D - 1)) + 4 * q4));
+        for (int mu = 0; mu < 4; ++mu) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) kt[4 * q4 + e] = fmaxf(neg ? -x[e] : x[e], 0.f);
+            for (int h = 0; h < 2; ++h) {
+                const int i = (32 * mu + 4 * b + 4 * h) & (2 * D - 1);
+                const f32x4 x = lds4(tile + fidx<R>(t, i & (D - 1)));
+                const bool neg = (i & D) != 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kt[mu][4 * h + e] = fmaxf(neg ? -x[e] : x[e], 0.f);
             }
-            const int i1 = (i0 + FB) & (2 * D - 1);
-            const bool neg1 = (i1 & D) != 0;
-            const f32x4 x = lds4(tile + fidx<R>(t, i1 & (D - 1)));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kt[FB + e] = fmaxf(neg1 ? -x[e] : x[e], 0.f);
         }
+        // feature 32 m + 4 b + e: block s = m / 4 + 1, i = 32 (m % 4) + 4 b + e
 #pragma unroll
-        for (int j = 0; j < FB; ++j) {
-            const float partner = (R == 2 * D || s == 1) ? kt[j + 1] : kt[j + 2];
-            f[j] = kt[j] * partner;
-        }
+        for (int m = 0; m < 4 * NU; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                f[4 * m + e] = kt[m & 3][e] * kt[m & 3][e + (m >> 2) + 1];
     } else {
 #pragma unroll
-        for (int q4 = 0; q4 < FB / 4; ++q4) {
-            const f32x4 x = lds4(tile + fidx<R>(t, FB * b + 4 * q4));
+        for (int m = 0; m < R / 32; ++m) {
+            const f32x4 x = lds4(tile + fidx<R>(t, 32 * m + 4 * b));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) f[4 * q4 + e] = PHI == PHI_ELU1 ? elu1(x[e]) : x[e];
+            for (int e = 0; e < 4; ++e) f[4 * m + e] = PHI == PHI_ELU1 ? elu1(x[e]) : x[e];
         }
     }
+}
+
+// The factor a token's numerator is multiplied by: 1 / max(den, eps) for
+// attention normalisation, 1 for none.
+__device__ __forceinline__ float normaliser(const Cfg& c, float den) {
+    return c.norm == NORM_ATTN ? 1.f / fmaxf(den, c.eps) : 1.f;
 }
 
 // Sum over the eight lanes of one token (lanes 8a .. 8a + 7).
@@ -166,7 +187,7 @@ __device__ __forceinline__ float sum8(float x) {
     return x;
 }
 
-// Features of token t, block b, for a staged tile: zero past the chunk's
+// Features of token t, lane b, for a staged tile: zero past the chunk's
 // rows, optionally sum-normalised, written over the staged row; returns
 // them in f.  Every read of the staged row precedes every write (the whole
 // wave's, in program order).
@@ -188,9 +209,8 @@ __device__ __forceinline__ void tile_features(const Cfg& c, float* tile, int t, 
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int q4 = 0; q4 < FB / 4; ++q4)
-        st4(tile + fidx<R>(t, FB * b + 4 * q4),
-            f32x4{f[4 * q4], f[4 * q4 + 1], f[4 * q4 + 2], f[4 * q4 + 3]});
+    for (int m = 0; m < FB / 4; ++m)
+        st4(tile + fidx<R>(t, 32 * m + 4 * b), f32x4{f[4 * m], f[4 * m + 1], f[4 * m + 2], f[4 * m + 3]});
 }
 
 // One workgroup per (head, segment).  MODE:
@@ -237,17 +257,18 @@ __global__ __launch_bounds__(FNT, 2) void k_f32mm(Cfg c, const T* __restrict__ q
         sync_lds();
     }
 
-    // chunk inputs, one chunk ahead: lane (ft, fb) loads columns 8 fb .. 8 fb + 7
-    // of token ft (rows clamped into the segment: every load is issued)
+    // chunk inputs, one chunk ahead: lane (ft, fb) loads columns 4 fb .. 4 fb + 3
+    // and 32 + 4 fb .. 32 + 4 fb + 3 of token ft (rows clamped into the
+    // segment: every load is issued)
     Row8<T> xq, xk, xv;
     auto load_chunk = [&](int64_t ci) {
         const int64_t c0 = t0 + ci * CL;
         const int64_t row = min<int64_t>(c0 + ft, t1 - 1);
-        const int64_t off = (bh * N + row) * D + 8 * fb;
-        if (HAS_Q) xq.load(q + off);
+        const int64_t off = (bh * N + row) * D;
+        if (HAS_Q) xq.load(q + off, fb);
         if (HAS_K) {
-            xk.load(k + off);
-            xv.load(v + (bh * N + row) * DV + 8 * fb);
+            xk.load(k + off, fb);
+            xv.load(v + (bh * N + row) * DV, fb);
         }
     };
     if (nck > 0) load_chunk(0);
@@ -256,18 +277,21 @@ __global__ __launch_bounds__(FNT, 2) void k_f32mm(Cfg c, const T* __restrict__ q
     int64_t prev_c0 = 0;
     int prev_rows = 0;
     // normalise and store the outputs of a finished chunk: wave w, lane
-    // (n16, g4), register i of num_ta is token 16 ta + 4 g4 + i, column 16w + n16
+    // (n16, g4), register i of num_ta is token 16 ta + 4 g4 + i, column
+    // 16w + n16.  Stores go through a buffer resource covering the chunk's
+    // rows, whose range check drops the rows past the end.
     auto finish = [&](int64_t pc, int64_t c0, int rows) {
-        const float* den = sm.den[pc % 3];
+        const float* inv = sm.den[pc % 3];
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            out + (bh * N + c0) * DV, 0, rows * DV * (int)sizeof(T), 0x00020000);
 #pragma unroll
         for (int ta = 0; ta < 2; ++ta) {
             const f32x4 nm = ta ? num1 : num0;
-            const f32x4 dn = lds4(den + 16 * ta + 4 * g4);
+            const f32x4 iv = lds4(inv + 16 * ta + 4 * g4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * ta + 4 * g4 + i;
-                const float inv = c.norm == NORM_ATTN ? 1.f / fmaxf(dn[i], c.eps) : 1.f;
-                if (t < rows) Elem<T>::store(out, (bh * N + c0 + t) * DV + 16 * w + n16, nm[i] * inv);
+                store_out<T>(rs, (t * DV + 16 * w + n16) * (int)sizeof(T), nm[i] * iv[i]);
             }
         }
     };
@@ -283,18 +307,19 @@ __global__ __launch_bounds__(FNT, 2) void k_f32mm(Cfg c, const T* __restrict__ q
         // ---- phase 1: stage, prefetch, features
         const float sc = live ? c.scale : 0.f;
         if (HAS_Q) {
-            st4(pq + fidx<R>(ft, 8 * fb),
-                f32x4{sc * xq.get(0), sc * xq.get(1), sc * xq.get(2), sc * xq.get(3)});
-            st4(pq + fidx<R>(ft, 8 * fb + 4),
-                f32x4{sc * xq.get(4), sc * xq.get(5), sc * xq.get(6), sc * xq.get(7)});
+            st4(pq + fidx<R>(ft, 4 * fb), sc * xq.lo());
+            st4(pq + fidx<R>(ft, 32 + 4 * fb), sc * xq.hi());
         }
         if (HAS_K) {
-            st4(pk + fidx<R>(ft, 8 * fb),
-                f32x4{sc * xk.get(0), sc * xk.get(1), sc * xk.get(2), sc * xk.get(3)});
-            st4(pk + fidx<R>(ft, 8 * fb + 4),
-                f32x4{sc * xk.get(4), sc * xk.get(5), sc * xk.get(6), sc * xk.get(7)});
+            st4(pk + fidx<R>(ft, 4 * fb), sc * xk.lo());
+            st4(pk + fidx<R>(ft, 32 + 4 * fb), sc * xk.hi());
+            const f32x4 va = live ? xv.lo() : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 vb = live ? xv.hi() : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sm.vt[(8 * fb + j) * VL + ft] = live ? xv.get(j) : 0.f;
+            for (int j = 0; j < 4; ++j) {
+                sm.vt[vidx(4 * fb + j, ft)] = va[j];
+                sm.vt[vidx(32 + 4 * fb + j, ft)] = vb[j];
+            }
         }
         load_chunk(ci + 1 < nck ? ci + 1 : ci);
         // a token's eight lanes are in one wave: its staged row is complete
@@ -305,15 +330,15 @@ __global__ __launch_bounds__(FNT, 2) void k_f32mm(Cfg c, const T* __restrict__ q
         if (HAS_Q) {
             float f[FB];
             tile_features<PHI, R>(c, pq, ft, fb, live, f);
-            const float* zc = sm.z[MODE == M_READOUT ? 0 : p] + FB * fb;
+            const float* zc = sm.z[MODE == M_READOUT ? 0 : p] + 4 * fb;
 #pragma unroll
-            for (int q4 = 0; q4 < FB / 4; ++q4) {
-                const f32x4 zz = lds4(zc + 4 * q4);
+            for (int m = 0; m < FB / 4; ++m) {
+                const f32x4 zz = lds4(zc + 32 * m);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) den_q = fmaf(f[4 * q4 + e], zz[e], den_q);
+                for (int e = 0; e < 4; ++e) den_q = fmaf(f[4 * m + e], zz[e], den_q);
             }
             den_q = sum8(den_q);
-            if (MODE == M_READOUT && fb == 0) sm.den[ci % 3][ft] = den_q;
+            if (MODE == M_READOUT && fb == 0) sm.den[ci % 3][ft] = normaliser(c, den_q);
         }
         if (HAS_K) {
             float f[FB];
@@ -327,37 +352,70 @@ __global__ __launch_bounds__(FNT, 2) void k_f32mm(Cfg c, const T* __restrict__ q
         f32x4 vb0 = {0.f, 0.f, 0.f, 0.f}, vb1 = vb0;
         if (HAS_K) {
             // V[token 16 tq + 4 g4 + i][column 16w + n16] (B operand)
-            vb0 = lds4(sm.vt + (16 * w + n16) * VL + 4 * g4);
-            vb1 = lds4(sm.vt + (16 * w + n16) * VL + 16 + 4 * g4);
+            vb0 = lds4(sm.vt + vidx(16 * w + n16, 4 * g4));
+            vb1 = lds4(sm.vt + vidx(16 * w + n16, 16 + 4 * g4));
         }
         // the block tile of waves 0-2: rows 16 ta, columns 16 tb
         const int ta = w == 0 ? 0 : 1, tb = w == 2 ? 1 : 0;
         f32x4 blk = {0.f, 0.f, 0.f, 0.f};
         num0 = f32x4{0.f, 0.f, 0.f, 0.f};
         num1 = num0;
-#pragma unroll
-        for (int tt = 0; tt < NT16; ++tt) {
-            if constexpr (HAS_Q) {
-                const f32x4 a0 = lds4(pq + fidx<R>(n16, 16 * tt + 4 * g4));
-                const f32x4 a1 = lds4(pq + fidx<R>(16 + n16, 16 * tt + 4 * g4));
-                num0 = mma16(a0, S[tt], num0);
-                num1 = mma16(a1, S[tt], num1);
-                if (MODE == M_CAUSAL && w < 3) {
-                    const f32x4 bk = lds4(pk + fidx<R>(16 * tb + n16, 16 * tt + 4 * g4));
-                    blk = mma16(ta ? a1 : a0, bk, blk);
+        // One loop per role, chosen once per wave: ROLE 0 has no block tile,
+        // ROLE 1 a tile of rows 0-15, ROLE 2 of rows 16-31.  The operands of
+        // feature tile tt + 1 are read while tile tt is multiplied; the
+        // scheduling barrier keeps each tile's reads in its own step, which
+        // bounds the registers in flight.
+        struct Ops {
+            f32x4 a0, a1, bk;
+        };
+        auto contract = [&](auto role) {
+            constexpr int ROLE = decltype(role)::value;
+            auto load = [&](int tt) {
+                Ops o;
+                if constexpr (HAS_Q) {
+                    o.a0 = lds4(pq + fidx<R>(n16, 16 * tt + 4 * g4));
+                    o.a1 = lds4(pq + fidx<R>(16 + n16, 16 * tt + 4 * g4));
+                    if constexpr (ROLE != 0)
+                        o.bk = lds4(pk + fidx<R>(16 * tb + n16, 16 * tt + 4 * g4));
                 }
-            }
-            if constexpr (HAS_K) {
-                // phi(K)^T[feature 16 tt + n16][token 16 tq + 4 g4 + i]
+                return o;
+            };
+            Ops cur = load(0);
+#pragma unroll
+            for (int tt = 0; tt < NT16; ++tt) {
+                // phi(K)^T[feature 16 tt + n16][token 16 tq + 4 g4 + i], read
+                // at the start of the step and used after the readout
                 f32x4 k0, k1;
+                if constexpr (HAS_K) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    k0[i] = pk[fidx<R>(4 * g4 + i, 16 * tt + n16)];
-                    k1[i] = pk[fidx<R>(16 + 4 * g4 + i, 16 * tt + n16)];
+                    for (int i = 0; i < 4; ++i) {
+                        k0[i] = pk[fidx<R>(4 * g4 + i, 16 * tt + n16)];
+                        k1[i] = pk[fidx<R>(16 + 4 * g4 + i, 16 * tt + n16)];
+                    }
                 }
-                S[tt] = mma16(k0, vb0, S[tt]);
-                S[tt] = mma16(k1, vb1, S[tt]);
+                Ops nxt = cur;
+                if (tt + 1 < NT16) nxt = load(tt + 1);
+                if constexpr (HAS_Q) {
+                    num0 = mma16(cur.a0, S[tt], num0);
+                    num1 = mma16(cur.a1, S[tt], num1);
+                    if constexpr (ROLE == 1) blk = mma16(cur.a0, cur.bk, blk);
+                    if constexpr (ROLE == 2) blk = mma16(cur.a1, cur.bk, blk);
+                }
+                if constexpr (HAS_K) {
+                    S[tt] = mma16(k0, vb0, S[tt]);
+                    S[tt] = mma16(k1, vb1, S[tt]);
+                }
+                cur = nxt;
+                __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        if (MODE == M_CAUSAL && w < 3) {
+            if (w == 0)
+                contract(std::integral_constant<int, 1>{});
+            else
+                contract(std::integral_constant<int, 2>{});
+        } else {
+            contract(std::integral_constant<int, 0>{});
         }
         if constexpr (HAS_K) {
             if (lane < ZF) {
@@ -393,7 +451,7 @@ __global__ __launch_bounds__(FNT, 2) void k_f32mm(Cfg c, const T* __restrict__ q
                     a = (x[0] + x[1]) + (x[2] + x[3]);
                 }
                 a = sum8(a);
-                if (fb == 0) sm.den[ci % 3][ft] = den_q + a;
+                if (fb == 0) sm.den[ci % 3][ft] = normaliser(c, den_q + a);
             }
             num0 = mma16(lds4(sm.as + n16 * AL + 4 * g4), vb0, num0);
             num1 = mma16(lds4(sm.as + (16 + n16) * AL + 4 * g4), vb0, num1);

@@ -161,11 +161,13 @@ int lin_attn_bidir(const lin_attn_params* p, const void* q, const void* k, const
  * the state carried in from earlier chunks, and sequence segments are
  * combined by a prefix sum of their state increments; all of these are
  * exact re-associations of the recurrence.
- *   chunk     intra-chunk block length: 0 or 32 (one 32 x 32 MFMA tile;
- *             both kernel families run it, so they round alike).  64 and
- *             128 are valid lengths (every block length re-associates the
- *             [KZ] sec. 1.3 recurrence exactly, so the result changes only
- *             by rounding) that no kernel here runs:
+ *   chunk     intra-chunk block length.  0: the kernel's own, which is 32
+ *             (one 32 x 32 MFMA tile) for r <= 256 on every kernel family,
+ *             and 16 (r <= 384) or 4 (r <= 512) on the vector kernels that
+ *             run the wider maps.  32: accepted for r <= 256.  Every block
+ *             length re-associates the [KZ] sec. 1.3 recurrence exactly, so
+ *             the result changes only by rounding; 64 and 128 (and 32 past
+ *             r = 256) are valid lengths that no kernel here runs:
  *             LIN_ATTN_ERR_UNSUPPORTED.  Other values: LIN_ATTN_ERR_INVALID.
  *   S, z      float32 [B, H, r, dv] / [B, H, r], required, in/out: read
  *             when state_in == 1, always overwritten with the state after

@@ -341,9 +341,15 @@ hipError_t causal_run(const lin_attn_params* p, const void* q, const void* k, co
 // tile on the matrix-core path, and the same length on the float32 path so
 // that both round alike.  0 selects it; 64 and 128 are valid lengths of the
 // method that no kernel here runs.
-int check_chunk(int32_t chunk) {
+// The intra-chunk block length.  0 selects the kernel's own; 32 is the
+// length every kernel runs up to r = 256 (one 32 x 32 MFMA tile; the vector
+// kernels match it), so it is accepted there.  Past r = 256 the vector
+// kernels run 16 (r <= 384) or 4 tokens (the state and tiles must fit LDS),
+// and 64 and 128 no kernel runs: valid lengths, refused as unsupported.
+int check_chunk(int32_t chunk, int32_t r) {
     if (chunk != 0 && chunk != 32 && chunk != 64 && chunk != 128) return LIN_ATTN_ERR_INVALID;
-    return chunk == 64 || chunk == 128 ? LIN_ATTN_ERR_UNSUPPORTED : LIN_ATTN_OK;
+    if (chunk == 64 || chunk == 128) return LIN_ATTN_ERR_UNSUPPORTED;
+    return chunk == 32 && r > 256 ? LIN_ATTN_ERR_UNSUPPORTED : LIN_ATTN_OK;
 }
 
 // Static scratch of lin_attn_causal_chunked_noalloc: one copy per GPU, held
@@ -375,7 +381,7 @@ int causal_call(const lin_attn_params* p, const void* q, const void* k, const vo
     if (rc == LIN_ATTN_ERR_INVALID) return rc;
     const int rs = check_sizes(B, H, N);
     if (rs == LIN_ATTN_ERR_INVALID) return rs;
-    const int rk = check_chunk(chunk);
+    const int rk = check_chunk(chunk, p->r);
     if (rk == LIN_ATTN_ERR_INVALID) return rk;
     if (state_in != 0 && state_in != 1) return LIN_ATTN_ERR_INVALID;
     if (!noalloc && !opt_ptr_ok(ws)) return LIN_ATTN_ERR_INVALID;
@@ -429,8 +435,8 @@ const char* lin_attn_strerror(int32_t code) {
 size_t lin_attn_workspace_bytes(int32_t op, const lin_attn_params* p, int64_t B, int64_t H,
                                 int64_t N, int64_t d, int64_t dv, int32_t chunk) {
     if (op < LIN_ATTN_OP_BIDIR || op > LIN_ATTN_OP_BIDIR_PROJ) return 0;
-    if (op == LIN_ATTN_OP_CAUSAL && check_chunk(chunk) != LIN_ATTN_OK) return 0;
     if (!p || check_sizes(B, H, N) != LIN_ATTN_OK) return 0;
+    if (op == LIN_ATTN_OP_CAUSAL && check_chunk(chunk, p->r) != LIN_ATTN_OK) return 0;
     // omega is not needed to size the workspace: check the rest with a dummy
     const int rc = check_params(p, d, dv, reinterpret_cast<const void*>(uintptr_t(16)));
     if (rc != LIN_ATTN_OK) return 0;

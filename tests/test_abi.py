@@ -169,6 +169,12 @@ def test_outside_gpu_coverage_is_unsupported():
     assert causal(params(), chunk=64) == UNSUPPORTED
     assert causal(params(), chunk=128) == UNSUPPORTED
     assert causal(params("elu1", r=64, dtype=0), chunk=128) == UNSUPPORTED
+    # past r = 256 the vector kernels run 16- or 4-token blocks: only chunk 0
+    assert causal(params("favor", r=384), chunk=32) == UNSUPPORTED
+    assert causal(params("dpfp", r=512, nu=4, dtype=0), chunk=32) == UNSUPPORTED
+    # accepted by validation (without a GPU the launch itself then fails)
+    assert causal(params("favor", r=384), chunk=0) not in (INVALID, UNSUPPORTED)
+    assert causal(params("favor", r=256), chunk=32) not in (INVALID, UNSUPPORTED)
 
 
 def test_chunk_sizes_the_causal_workspace_only():
@@ -181,6 +187,9 @@ def test_chunk_sizes_the_causal_workspace_only():
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, *args, 16) == 0
     assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR, *args, 64) == \
         binding.lin_attn_workspace_bytes(binding.OP_BIDIR, *args, 0)
+    wide = (params("favor", r=384), 1, 8, 4096, 64, 64)
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, *wide, 0) > 0
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL, *wide, 32) == 0
 
 
 def causal_noalloc(p, B=1, H=2, N=100, d=64, dv=64, ptr=FAKE, omega=FAKE, chunk=0, state_in=0,

@@ -345,6 +345,17 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
                 const int f = f0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
                 S[mt][nt][i] = st[(int64_t)f * DV + 32 * nt + lo];
             }
+    // readout: the summaries never change, so their bf16 operands are packed
+    // once (the float32 copy is then dead)
+    bf16x8 Sp[2][2][2];
+    if (!CAUSAL) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) Sp[mt][nt][kk] = pack8(S[mt][nt], 8 * kk);
+    }
     float zreg[2]; // z[f0 + 32 nt + lo]
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) zreg[nt] = st[(int64_t)R * DV + f0 + 32 * nt + lo];
@@ -550,7 +561,8 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) acc[nt] = mfma(pack8(S[mt][nt], 8 * kk), fq[mt][kk], acc[nt]);
+                for (int kk = 0; kk < 2; ++kk)
+                    acc[nt] = mfma(CAUSAL ? pack8(S[mt][nt], 8 * kk) : Sp[mt][nt][kk], fq[mt][kk], acc[nt]);
         }
         if (CAUSAL) {
 #pragma unroll
@@ -1105,15 +1117,35 @@ struct CausalArgs {
     u16* dv;            // key pass: dv
 };
 
+// A 32 x 32 accumulator tile in LDS, lane by lane: lane l's 16 elements at
+// floats [PS l, PS l + 16), written and read as four 16-byte pieces (the
+// 80-byte lane stride puts the 16 lanes of each access on distinct banks).
+constexpr int PS = 20;
+__device__ __forceinline__ void put_tile(float* base, int lane, const f32x16& t) {
+    float* p = base + PS * lane;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        *reinterpret_cast<f32x4*>(p + 4 * m) = f32x4{t[4 * m], t[4 * m + 1], t[4 * m + 2], t[4 * m + 3]};
+}
+__device__ __forceinline__ void add_tile(const float* base, int lane, f32x16& t) {
+    const float* p = base + PS * lane;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * m);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[4 * m + e] += x[e];
+    }
+}
+
 struct CausalSmem {
     u16 wt[D * LDF];                 // omega^T [d][f'] (swap23 columns)
     u16 vt[2][DV * LDT];             // V^T [n][j'] of the chunk (j in swap23 order)
     u16 vs[2][L * LDN];              // V [j][n'] of the chunk (n in swap23 order)
-    float part[4][3][16][64];        // per wave: partial readout (two tiles) + intra block
-    float dpart[4][2][16][64];       // per wave: partial du^T or dv^T tiles (a second buffer, so
+    float part[4][3][64 * PS];       // per wave: partial readout (two tiles) + intra block
+    float dpart[4][2][64 * PS];      // per wave: partial du^T or dv^T tiles (a second buffer, so
                                      // no wave can overwrite partials another is still reading)
-    float tokv[4][3][L];             // per wave, per token: [0] den / B1 partial sums, [1] dden
-                                     // (own copy), [2] sum_f w partial
+    float tokv[4][4][L];             // per wave, per token: [0] den / B1 partial sums, [1] dden
+                                     // (own copy), [2] sum_f w partial, [3] dout . num partial
     float z[R];                      // z (query pass) or g (key pass)
     float dd[L];                     // dden of the chunk's tokens (key pass)
 };
@@ -1216,7 +1248,6 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
                 S[ft][nt][i] = st[(int64_t)(64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)) * DV + 32 * nt + lo];
         }
     for (int f = threadIdx.x; f < R; f += NTC) sm.z[f] = st[(int64_t)R * DV + f];
-    __syncthreads(); // omega^T table and z
 
     // The chunk's global loads, issued one chunk ahead into one of two
     // register sets (two chunks per iteration, one per set, so no set is
@@ -1263,8 +1294,6 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) xe[m] = *reinterpret_cast<const uint2*>(xr + 8 * m);
         }
-        const bool vlive = ((int)threadIdx.x >> 3) < rows;
-        stash_v(sm.vt[buf], sm.vs[buf], vlive ? cur.vx : make_uint4(0u, 0u, 0u, 0u));
         f32x16 PQ[2], PK[2];
         features2(a, cur.qf, w, fmaf(a.b_norm, sq_norm(cur.qf), a.b_const), live, lo, h, PQ);
         features2(a, cur.kf, w, fmaf(a.b_norm, sq_norm(cur.kf), a.b_const), live, lo, h, PK);
@@ -1272,7 +1301,12 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         // last chunk's are issued again past the end and not used)
         issue(ci + 1, nxt);
 
-        // partial readout num^T [n x t] = S^T phi(Q)^T, den, and A1^T [j x t] = phi(K) phi(Q)^T over F_w
+        // This wave's part of the readout over F_w: num^T [n x t] = S^T phi(Q)^T
+        // plus the masked intra-chunk block A1^T [j x t] = phi(K) phi(Q)^T
+        // (keys j <= query t) times V.  The readout enters the gradient only
+        // through two scalars per token, the denominator and
+        // dot_t = dout_t . num_t, both linear in these parts: each wave folds
+        // its part into them and only the scalars cross waves.
         f32x16 num[2] = {zero16(), zero16()}, a1 = zero16();
         float den = 0.f;
 #pragma unroll
@@ -1291,36 +1325,9 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
                 den = fmaf(PQ[ft][i], sm.z[64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)], den);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            sm.part[w][0][i][lane] = num[0][i];
-            sm.part[w][1][i][lane] = num[1][i];
-            sm.part[w][2][i][lane] = a1[i];
-        }
-        den = half_sum(den);
-        if (h == 0) sm.tokv[w][0][lo] = den;
-        sync_lds(); // B1: partials and V tables of the chunk
-
-        // full sums (every wave, redundantly)
-        den = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) num[0][i] = num[1][i] = a1[i] = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                num[0][i] += sm.part[u][0][i][lane];
-                num[1][i] += sm.part[u][1][i][lane];
-                a1[i] += sm.part[u][2][i][lane];
-            }
-            den += sm.tokv[u][0][lo];
-        }
-        // masked intra-chunk block: keys j <= query t
-        float aden = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
             a1[i] = (8 * (i >> 2) + (i & 3) <= keep_thr) ? a1[i] : 0.f;
-            aden += a1[i];
+            den += a1[i];
         }
-        den += half_sum(aden);
         const u16* vt = sm.vt[buf];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -1329,24 +1336,51 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
             for (int nt = 0; nt < 2; ++nt)
                 num[nt] = mfma(lds8(vt + (32 * nt + lo) * LDT + 16 * kk + 8 * h), af, num[nt]);
         }
-
-        // dnum^T [n x t], dden (zero past the chunk's end)
-        const float inv = attn ? 1.f / fmaxf(den, a.eps) : 1.f;
-        f32x16 dn[2];
+        float o[2][4][4]; // dout of token lo (zero past the chunk's end)
         float dot = 0.f;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                float o[4];
-                unpack4(live ? dr[nt][m] : make_uint2(0u, 0u), o);
+                unpack4(live ? dr[nt][m] : make_uint2(0u, 0u), o[nt][m]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    dot = fmaf(o[j], num[nt][4 * m + j], dot);
-                    dn[nt][4 * m + j] = o[j] * inv;
-                }
+                for (int j = 0; j < 4; ++j) dot = fmaf(o[nt][m][j], num[nt][4 * m + j], dot);
             }
+        den = half_sum(den);
         dot = half_sum(dot);
+        if (h == 0) {
+            sm.tokv[w][0][lo] = den;
+            sm.tokv[w][3][lo] = dot;
+        }
+        sync_lds(); // B1: the waves' scalars
+
+        // the next chunk's V, into the other table pair: every wave has
+        // finished the chunk before this one (its last reader) at B1, and B2
+        // publishes it before the next chunk reads it
+        {
+            int64_t c0n;
+            int rowsn;
+            chunk_at(min(ci + 1, nck - 1), c0n, rowsn);
+            stash_v(sm.vt[buf ^ 1], sm.vs[buf ^ 1],
+                    ((int)threadIdx.x >> 3) < rowsn ? nxt.vx : make_uint4(0u, 0u, 0u, 0u));
+        }
+
+        den = 0.f;
+        dot = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            den += sm.tokv[u][0][lo];
+            dot += sm.tokv[u][3][lo];
+        }
+        // dnum^T [n x t], dden
+        const float inv = attn ? 1.f / fmaxf(den, a.eps) : 1.f;
+        f32x16 dn[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dn[nt][4 * m + j] = o[nt][m][j] * inv;
         const float dden = (attn && den > a.eps) ? -dot * inv * inv : 0.f;
         if (w == 0 && h == 0 && live) {
             a.tok[2 * (bh * a.N + c0 + lo)] = inv;
@@ -1397,11 +1431,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
             }
         }
         wsum = half_sum(wsum);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sm.dpart[w][0][i][lane] = du[0][i];
-            sm.dpart[w][1][i][lane] = du[1][i];
-        }
+        put_tile(sm.dpart[w][0], lane, du[0]);
+        put_tile(sm.dpart[w][1], lane, du[1]);
         if (h == 0) sm.tokv[w][2][lo] = wsum;
         sync_lds(); // B2: du partials
         if (w < 2) {
@@ -1410,8 +1441,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
             float ws = 0.f;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[i] += sm.dpart[u][w][i][lane];
+                add_tile(sm.dpart[u][w], lane, s);
                 ws += sm.tokv[u][2][lo];
             }
             if (live) {
@@ -1462,9 +1492,18 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         }
     };
 
+    // chunk 0's V is staged before the first barrier; every later chunk's
+    // between the two barriers of the chunk before it (see body)
+    QueryLoads A, B;
     if (nck > 0) {
-        QueryLoads A, B;
         issue(0, A);
+        int64_t c0;
+        int rows;
+        chunk_at(0, c0, rows);
+        stash_v(sm.vt[0], sm.vs[0], ((int)threadIdx.x >> 3) < rows ? A.vx : make_uint4(0u, 0u, 0u, 0u));
+    }
+    __syncthreads(); // omega^T table, z and chunk 0's V
+    if (nck > 0) {
         for (int ci = 0; ci < nck; ci += 2) {
             body(ci, A, B);
             if (ci + 1 < nck) body(ci + 1, B, A);
@@ -1595,36 +1634,29 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
                 for (int nt = 0; nt < 2; ++nt) dvp[nt] = mfma(pack8(Gs[ft][nt], 8 * kk), pk, dvp[nt]);
                 b1 = mfma(pack8(PQ[ft], 8 * kk), pk, b1);
             }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sm.part[w][0][i][lane] = dvp[0][i];
-            sm.part[w][1][i][lane] = dvp[1][i];
-            sm.part[w][2][i][lane] = b1[i];
-        }
-        sync_lds(); // B1: partials, dden copies and V tables of the chunk
-
-        const u16* vs = sm.vs[buf];
+        // dv^T = G^T phi(K)^T + dnum^T (B1 masked: query i >= key j) is linear
+        // in the parts over F_w, so each wave adds its own masked block's
+        // term before its part crosses waves
         f32x16 dnr[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) dnr[nt] = transpose32(dn[nt], eye); // [i x n]
-        // wave nt < 2: dv^T tile nt = sum of partials + dnum^T B1 (masked:
-        // query i >= key j); the tile index is a constant in each branch (a
-        // runtime index into the register array dnr becomes a select per
-        // element and register)
-        auto dv_tile = [&](const f32x16& dsel, int nt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b1[i] = (8 * (i >> 2) + (i & 3) >= keep_thr) ? b1[i] : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) dvp[nt] = mfma(pack8(dnr[nt], 8 * kk), pack8(b1, 8 * kk), dvp[nt]);
+        put_tile(sm.part[w][0], lane, dvp[0]);
+        put_tile(sm.part[w][1], lane, dvp[1]);
+        sync_lds(); // B1: partials, dden copies and V tables of the chunk
+
+        const u16* vs = sm.vs[buf];
+        // wave nt < 2: dv^T tile nt = sum of the four parts (the tile index
+        // is a constant in each branch)
+        auto dv_tile = [&](int nt) {
             f32x16 s = zero16();
-            f32x16 bm = zero16();
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    s[i] += sm.part[u][nt][i][lane];
-                    bm[i] += sm.part[u][2][i][lane];
-                }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) bm[i] = (8 * (i >> 2) + (i & 3) >= keep_thr) ? bm[i] : 0.f;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) s = mfma(pack8(dsel, 8 * kk), pack8(bm, 8 * kk), s);
+            for (int u = 0; u < 4; ++u) add_tile(sm.part[u][nt], lane, s);
             if (live) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -1634,9 +1666,9 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
             }
         };
         if (w == 0)
-            dv_tile(dnr[0], 0);
+            dv_tile(0);
         else if (w == 1)
-            dv_tile(dnr[1], 1);
+            dv_tile(1);
         // A3 [i x j] = dnum_i . v_j + dden_i, masked (i >= j)
         f32x16 a3 = zero16();
 #pragma unroll
@@ -1682,11 +1714,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
             }
         }
         wsum = half_sum(wsum);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sm.dpart[w][0][i][lane] = du[0][i];
-            sm.dpart[w][1][i][lane] = du[1][i];
-        }
+        put_tile(sm.dpart[w][0], lane, du[0]);
+        put_tile(sm.dpart[w][1], lane, du[1]);
         if (h == 0) sm.tokv[w][2][lo] = wsum;
         sync_lds(); // B2: du partials
         if (w >= 2) {
@@ -1696,8 +1725,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
             float ws = 0.f;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[i] += sm.dpart[u][dt][i][lane];
+                add_tile(sm.dpart[u][dt], lane, s);
                 ws += sm.tokv[u][2][lo];
             }
             if (live) {

@@ -195,6 +195,13 @@ def main():
             "kernel": "lin_attn_causal_chunked (whole call)",
             "alg_flops_per_launch": flops, "avg_launch_ms": call_ms,
         }
+        # the prefill's algorithmic HBM rate (bf16 q, k, v in, out) and the
+        # spread of the per-call event times
+        alg_bytes = 4 * w.d * 2 * w.B * w.H * w.N
+        result["prefill_hbm"] = {"alg_bytes_per_launch": alg_bytes,
+                                 "GBps": alg_bytes / (call_ms * 1e-3) / 1e9,
+                                 "frac": alg_bytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        result["prefill_call_ms"] = percentiles(per)
         result["clock"] = clock
         result["settle"] = {
             "seconds_per_section": SETTLE_S, "prefill_calls": n_settle,
@@ -247,6 +254,7 @@ def main():
             torch.cuda.synchronize()
             per_layer.append(e0.elapsed_time(e1) / wd.layers)
         launch_ms = float(np.mean(per_layer))
+        decode_pct = percentiles(per_layer)
         heads = wd.B * wd.H
         bytes_layer = decode_alg_bytes_per_head(wd.r, wd.dv, 2) * heads
         gbps_step = bytes_layer * wd.layers / (dms * 1e-3) / 1e9
@@ -261,6 +269,7 @@ def main():
                                 args.warmup)
         result["decode"] = {
             "omega_redraw_us": float(np.median(orf_per)) * 1e3,
+            "layer_ms": decode_pct,
             "workload": wd.name, "B": wd.B, "H": wd.H, "layers": wd.layers, "r": wd.r,
             "ms_per_step": dms, "seq_tokens_per_s": wd.B / (dms * 1e-3),
             "GBps_step": gbps_step,
@@ -299,6 +308,7 @@ def main():
         bach = bflops / (float(np.mean(per)) * 1e-3) / 1e12
         result["bidir"] = {"workload": wb.name, "B": wb.B, "H": wb.H, "N": wb.N, "r": wb.r,
                            "ms_per_step": bms, "tokens_per_s": wb.B * wb.N / (bms * 1e-3),
+                           "call_ms": percentiles(per),
                            "roofline": {"bound": "mfma", "achieved": bach,
                                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                         "frac": bach / PEAK_BF16_TFLOPS,
@@ -569,6 +579,21 @@ def main():
 
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, scale)
+    # every fraction restated against what this run measured: the GFX clock
+    # under the prefill's load and the achievable copy bandwidth
+    ctx = {}
+    mhz = (result.get("clock") or {}).get("gfx_mhz_median")
+    if mhz and "roofline" in result:
+        ctx["prefill_frac_at_measured_clock"] = result["roofline"]["frac"] * 2400.0 / mhz
+    copy_gbps = (result.get("hbm_copy") or {}).get("GBps")
+    if copy_gbps and "decode" in result:
+        ctx["decode_frac_of_copy"] = result["decode"]["roofline"]["achieved"] / copy_gbps
+    if copy_gbps and "prefill_hbm" in result:
+        ctx["prefill_hbm_frac_of_copy"] = result["prefill_hbm"]["GBps"] / copy_gbps
+    if ctx:
+        ctx["note"] = ("fractions against the peaks scaled to the measured clock (2400 MHz "
+                       "nominal) and against the measured 2 GiB device copy")
+        result["context"] = ctx
     print(json.dumps(result), flush=True)
 
 
@@ -659,6 +684,14 @@ def cpu_baseline(w, scale):
             "one_thread": {"token_heads_per_s": n1 / dt1,
                            "tokens_per_s_equiv": n1 / dt1 / (w.B * w.H),
                            "sample": f"1 head, first {n1} tokens, 1 thread, {dt1:.2f} s"}}
+
+
+def percentiles(ms_list):
+    """p10 / p50 / p90 of per-call event times (ms)."""
+    import numpy as np
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "calls": int(a.size)}
 
 
 def host_cpu_model():

@@ -153,7 +153,10 @@ BackwardLayout backward_layout(const lin_attn_params* p, bool causal, int64_t BH
     const size_t inc = (size_t)(BH * L.sp.G * state_elems(p->r));
     L.inc_b = inc;
     L.extra = 2 * inc;
-    L.omega_t = L.extra + (causal ? (size_t)(BH * N * 2)
+    // causal: per token dnum (bf16) and dden on the matrix-core route, two
+    // floats on the vector route; bidirectional: the two totals, then dnum
+    // and dden
+    L.omega_t = L.extra + (causal ? (size_t)(BH * N) * (DV / 2 + 1)
                                   : (size_t)(2 * BH * state_elems(p->r)) +
                                         (size_t)(BH * N) * (DV / 2 + 1));
     L.omega_t = (L.omega_t + 63) & ~(size_t)63; // 256-byte aligned (read as 16-byte pieces)
@@ -199,17 +202,22 @@ int backward_call(bool causal, const lin_attn_params* p, const void* q, const vo
     }
     if (causal && use_mfma(p)) {
         // matrix-core route: each workgroup walks its segment's chunks with the
-        // evolving state in accumulators (forward order, then reverse)
+        // evolving state in accumulators (forward order, then reverse); the
+        // backward increments sum_t phi(q_t) (dnum_t, dden_t) per segment come
+        // from the increment kernel on (q, dnum) with z weights dden
+        void* dnum = extra;                                  // bf16 [BH, N, DV]
+        float* dden = extra + (size_t)BH * N * (DV / 2);     // [BH, N]
         if (e == hipSuccess)
             e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_f, 1, nullptr, nullptr,
                                     nullptr, st);
         if (e == hipSuccess)
             e = launch_favor_causal_bwd_query(c, q, k, v, dout, omega, s, sp, inc_f, sp.G * E, E,
-                                              extra, inc_b, dq, st);
+                                              dnum, dden, dq, st);
+        if (e == hipSuccess) e = launch_favor_sums(c, q, dnum, omega, s, sp, inc_b, st, dden);
         if (e == hipSuccess) e = launch_segment_suffix_scan(p->r, s, sp, inc_b, st);
         if (e == hipSuccess)
-            e = launch_favor_causal_bwd_key(c, q, k, v, dout, omega, s, sp, inc_b, sp.G * E, E,
-                                            extra, dk, dvv, st);
+            e = launch_favor_causal_bwd_key(c, q, k, v, omega, s, sp, inc_b, sp.G * E, E, dnum,
+                                            dden, dk, dvv, st);
     } else if (causal) {
         if (e == hipSuccess)
             e = launch_segment_scan(p->r, s, sp, nullptr, nullptr, inc_f, 1, nullptr, nullptr,

@@ -1083,117 +1083,189 @@ hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const v
 
 // ---------------------------------------------------------------------------
 // Causal backward on the matrix cores (FAVOR+, bf16, r = 256).  One workgroup
-// per (head, segment) walks its chunks in order (query pass) or in reverse
-// (key pass); wave w keeps the 64 features F_w = [64w, 64w + 64) of the
-// evolving state in float32 accumulators, as the forward kernel's waves
-// do.  Products over all features (readout, the masked intra-chunk block,
-// du) are summed across the four waves through LDS, two workgroup barriers
-// per chunk.  Tiles are 32 x 32 accumulator tiles; T as an operand is
-// pack8(T, 8 kk) (k-slots in swap23 order): the B operand of a product over
-// T's rows, or the A operand of T^T.  transpose32 turns a tile into its
-// transpose with the identity operand (exact: one bf16 product by 1 each).
+// of eight waves per (head, segment) walks its chunks in order (query pass)
+// or in reverse (key pass); wave w keeps the 32 features F_w = [32w, 32w + 32)
+// of the evolving state in float32 accumulators (the query pass S^T, the key
+// pass the backward state G).  Two waves share each SIMD.  Each chunk's q, k,
+// V, dout (or dnum), the per-token feature biases and dden are staged once
+// per workgroup in LDS, one chunk ahead.  Products over all features reach
+// the other waves in one of three forms:
+// - the readout enters the query gradient only through two scalars per token,
+//   the denominator and dot_t = dout_t . num_t, and dot_t is
+//   sum_f phi(q_t)_f (S dout_t)_f + sum_j A1[j][t] (v_j . dout_t): both are
+//   linear in the waves' parts over F_w, so only those scalars cross waves;
+// - w = dphi o phi leaves each wave as bfloat16 rows of a [token][feature]
+//   table; wave w then contracts the table with omega over all r features for
+//   one 16 x 16 tile of du^T (16x16x32 products), so no partial du crosses;
+// - the key pass sums the eight waves' parts of dv^T through LDS.
+// The query pass writes dnum_t = dout_t / D_t (in bfloat16, the operand the
+// products take) and dden_t; the segments' backward increments
+// sum_t phi(q_t) (dnum_t, dden_t) come from the increment kernel.
+// Two workgroup barriers per chunk.  32 x 32 tiles are accumulator tiles;
+// T as an operand is pack8(T, 8 kk) (k-slots in swap23 order): the B operand
+// of a product over T's rows, or the A operand of T^T.  transpose32 turns a
+// tile into its transpose with the identity operand (exact: one bf16
+// product by 1 each).
 // ---------------------------------------------------------------------------
-constexpr int NTC = 256; // 4 waves
-constexpr int LDT = 40;  // row length of the per-chunk V tables (bank spread)
+constexpr int NWC = 8;         // waves, 32 features each
+constexpr int NTC = 64 * NWC;
+constexpr int LDT = 40;        // row length of the per-chunk transposed tables (bank spread)
+constexpr int LDW = R + 8;     // row length of the [d][f] omega^T and [t][f] w tables
 
 __device__ __forceinline__ f32x16 transpose32(const f32x16& t, const bf16x8 (&eye)[2]) {
     return mfma(pack8(t, 8), eye[1], mfma(pack8(t, 0), eye[0], zero16()));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 struct CausalArgs {
     const u16* q;
     const u16* k;
     const u16* v;
-    const u16* dout;
+    const u16* dout;    // query pass
     const u16* omega;
     int64_t N, G, seg_len;
     float a_scale, b_norm, b_const, scale, eps;
     int norm;
     const float* state; // query: forward prefix per segment; key: backward suffix per segment
     int64_t st_bh, st_g;
-    float* tok;         // (1 / D_t, dden_t) per token: written by the query pass, read by the key pass
-    float* inc;         // query pass: backward increments per segment [BH][G][E]
+    u16* dnum;          // dnum_t = dout_t / D_t in bfloat16 [BH, N, DV]: written by the query
+                        // pass, read by the key pass
+    float* dden;        // dden_t [BH, N]: likewise
     u16* dx;            // dq or dk
     u16* dv;            // key pass: dv
 };
 
 // A 32 x 32 accumulator tile in LDS, lane by lane: lane l's 16 elements at
-// floats [PS l, PS l + 16), written and read as four 16-byte pieces (the
-// 80-byte lane stride puts the 16 lanes of each access on distinct banks).
-constexpr int PS = 20;
+// floats [16 l, 16 l + 16), as four 16-byte pieces in the order
+// m ^ tile_swz(l), so that the lanes of each piece's access fall on distinct
+// banks.
+__device__ __forceinline__ int tile_swz(int l) { return ((l >> 1) ^ (l >> 3)) & 3; }
 __device__ __forceinline__ void put_tile(float* base, int lane, const f32x16& t) {
-    float* p = base + PS * lane;
+    float* p = base + 16 * lane;
+    const int sw = tile_swz(lane);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-        *reinterpret_cast<f32x4*>(p + 4 * m) = f32x4{t[4 * m], t[4 * m + 1], t[4 * m + 2], t[4 * m + 3]};
+        *reinterpret_cast<f32x4*>(p + 4 * (m ^ sw)) = f32x4{t[4 * m], t[4 * m + 1], t[4 * m + 2], t[4 * m + 3]};
 }
-__device__ __forceinline__ void add_tile(const float* base, int lane, f32x16& t) {
-    const float* p = base + PS * lane;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * m);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[4 * m + e] += x[e];
-    }
+
+// A 32 x 32 tile as the two bf16 operands it feeds (k-slots 0..7 and 8..15
+// of each lane's 16 elements): what is kept of a tile that only ever enters
+// matrix products.
+struct Tile2 {
+    bf16x8 k[2];
+};
+__device__ __forceinline__ Tile2 packt(const f32x16& t) { return Tile2{{pack8(t, 0), pack8(t, 8)}}; }
+__device__ __forceinline__ f32x16 transpose_p(const Tile2& t, const bf16x8 (&eye)[2]) {
+    return mfma(t.k[1], eye[1], mfma(t.k[0], eye[0], zero16()));
 }
+
+constexpr int LDD = DV + 4; // row length (bf16) of the per-chunk dout / dnum table (bank spread)
 
 struct CausalSmem {
-    u16 wt[D * LDF];                 // omega^T [d][f'] (swap23 columns)
-    u16 vt[2][DV * LDT];             // V^T [n][j'] of the chunk (j in swap23 order)
-    u16 vs[2][L * LDN];              // V [j][n'] of the chunk (n in swap23 order)
-    float part[4][3][64 * PS];       // per wave: partial readout (two tiles) + intra block
-    float dpart[4][2][64 * PS];      // per wave: partial du^T or dv^T tiles (a second buffer, so
-                                     // no wave can overwrite partials another is still reading)
-    float tokv[4][4][L];             // per wave, per token: [0] den / B1 partial sums, [1] dden
-                                     // (own copy), [2] sum_f w partial, [3] dout . num partial
-    float z[R];                      // z (query pass) or g (key pass)
-    float dd[L];                     // dden of the chunk's tokens (key pass)
+    u16 wt[D * LDW];               // omega^T [d][f]
+    u16 wq[L * LDW];               // w of the chunk in bfloat16, [token][f]
+    u16 vt[2][DV * LDT];           // V^T [n][j'] of the chunk (j in swap23 order)
+    u16 vs[2][L * LDN];            // V [j][n'] of the chunk (n in swap23 order)
+    bf16x8 xs[2][256];             // q and k of the chunk (swizzled, xs_index)
+    u16 ds[L * LDD];               // dout (query pass) or dnum (key pass) of the chunk, [token][n]
+    float xb[2][L];                // per token of the chunk: the feature map's bias for q and k
+                                   // (-inf past the chunk's end)
+    float wsum[NWC][L];            // per wave, per token: sum_f w over F_w
+    float z[R];                    // z (query pass) or g (key pass)
 };
 
-// V of the chunk: thread t fetches row t/8, columns 8 (t%8) .. +7 (zero past
-// `rows`) with one 16-byte load, then writes them to the two LDS tables.
-__device__ __forceinline__ uint4 fetch_v(const u16* __restrict__ vp, int rows) {
-    const int j = threadIdx.x >> 3, n0 = (threadIdx.x & 7) * 8;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (j < rows) x = *reinterpret_cast<const uint4*>(vp + (int64_t)j * DV + n0);
-    return x;
+struct CausalQuerySmem {
+    CausalSmem c;
+    float red[NWC][2][L];          // per wave, per token: partial denominator and dout . num
+};
+
+struct CausalKeySmem {
+    CausalSmem c;
+    u16 dnt[DV * LDT];             // dnum^T [n][i'] of the chunk (i in swap23 order)
+    float dden[2][L];              // dden of the chunk's queries (by chunk parity)
+    float part[NWC][2][64 * 16];   // per wave: partial dv^T tiles (put_tile)
+};
+
+// The next chunk's global loads, held in registers across the first barrier
+// of the current one: thread th fetches 16-byte block th%256 of q (th < 256)
+// or k, row th/16, columns 4 (th%16) .. +3 of V and of dout (query pass) or
+// dnum (key pass), and (key pass, th < 32) dden of token th, at rows clamped
+// into the chunk.
+struct ChunkLoads {
+    bf16x8 xb;
+    uint2 vx, dx;
+    float dd;
+};
+
+template <bool KEY>
+__device__ __forceinline__ void fetch_chunk(const CausalArgs& a, int64_t row0, int rows,
+                                            ChunkLoads& ld) {
+    const int th = threadIdx.x;
+    ld.xb = load_block((th < 256 ? a.q : a.k) + row0 * D, rows, th & 255);
+    const int64_t j = row0 + min(th >> 4, rows - 1);
+    ld.vx = *reinterpret_cast<const uint2*>(a.v + j * DV + (th & 15) * 4);
+    ld.dx = *reinterpret_cast<const uint2*>((KEY ? a.dnum : a.dout) + j * DV + (th & 15) * 4);
+    if (KEY) ld.dd = a.dden[row0 + min(th & (L - 1), rows - 1)];
 }
 
-__device__ __forceinline__ void stash_v(u16* vt, u16* vs, uint4 x) {
-    const int j = threadIdx.x >> 3, n0 = (threadIdx.x & 7) * 8;
-    const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+// Four bf16 (a row's columns n0 .. n0+3, token j) into a transposed table
+// [n][j'] (j in swap23 order).
+__device__ __forceinline__ void put_transposed4(u16* tt, int j, int n0, uint2 x) {
+    const uint32_t wd[2] = {x.x, x.y};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int n = n0 + e;
+    for (int e = 0; e < 4; ++e) {
         const u16 val = (e & 1) ? (u16)(wd[e >> 1] >> 16) : (u16)(wd[e >> 1] & 0xffffu);
-        vt[n * LDT + (j & ~15) + swap23(j & 15)] = val;
-        vs[j * LDN + (n & ~15) + swap23(n & 15)] = val;
+        tt[(n0 + e) * LDT + (j & ~15) + swap23(j & 15)] = val;
     }
 }
 
-// The lane's dout values of a [n x t] tile pair: dout[lo][32 nt + 8 m + 4h .. +3]
-// as raw bf16 pairs (zero past `rows`).
-__device__ __forceinline__ void fetch_dout(const u16* __restrict__ dor, int rows, int lo, int h,
-                                           uint2 (&r)[2][4]) {
+// ... and their LDS copies (V, dout / dnum zero past `rows`), with the
+// per-token biases of the feature map: the eight threads of a q or k row sum
+// their squares; tokens past the end get -inf (exp2 gives 0).  dnt: the key
+// pass's transposed dnum table, or NULL.
+__device__ __forceinline__ void stash_chunk(const CausalArgs& a, CausalSmem& sm, int buf,
+                                            const ChunkLoads& ld, int rows, u16* dnt) {
+    const int th = threadIdx.x;
+    sm.xs[th >> 8][th & 255] = ld.xb;
+    {
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 x = {ld.xb[e], ld.xb[e + 1]};
+            sq = __builtin_amdgcn_fdot2_f32_bf16(x, x, sq, false);
+        }
+        sq = row8_sum(sq);
+        const int t = (th & 255) >> 3;
+        if ((th & 7) == 0) sm.xb[th >> 8][t] = t < rows ? fmaf(a.b_norm, sq, a.b_const) : -INFINITY;
+    }
+    const int j = th >> 4, n0 = (th & 15) * 4;
+    const bool in = j < rows;
+    const uint2 x = in ? ld.vx : make_uint2(0u, 0u);
+    put_transposed4(sm.vt[buf], j, n0, x);
+    // four consecutive n keep their order under swap23 (bits 0, 1 untouched)
+    *reinterpret_cast<uint2*>(sm.vs[buf] + j * LDN + (n0 & ~15) + swap23(n0 & 15)) = x;
+    const uint2 dx = in ? ld.dx : make_uint2(0u, 0u);
+    *reinterpret_cast<uint2*>(sm.ds + j * LDD + n0) = dx;
+    if (dnt) put_transposed4(dnt, j, n0, dx);
+}
+
+// Row lo of the chunk's dout / dnum table as the lane's pieces
+// [32 nt + 8 m + 4h, +4) (accumulator layout of a [n x t] tile pair).
+__device__ __forceinline__ void read_ds(const CausalSmem& sm, int lo, int h, uint2 (&r)[2][4]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            r[nt][m] = make_uint2(0u, 0u);
-            if (lo < rows)
-                r[nt][m] = *reinterpret_cast<const uint2*>(dor + (int64_t)lo * DV + 32 * nt + 8 * m + 4 * h);
-        }
+        for (int m = 0; m < 4; ++m)
+            r[nt][m] = *reinterpret_cast<const uint2*>(sm.ds + lo * LDD + 32 * nt + 8 * m + 4 * h);
 }
 
-// Row lo of X at columns 32 dt + 8m + 4h .. +3 (the epilogue's u = scale x).
-__device__ __forceinline__ void fetch_row(const u16* __restrict__ xr, int rows, int lo, int h,
-                                          int dt, uint2 (&r)[4]) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        r[m] = make_uint2(0u, 0u);
-        if (lo < rows)
-            r[m] = *reinterpret_cast<const uint2*>(xr + (int64_t)lo * D + 32 * dt + 8 * m + 4 * h);
-    }
+// q or k (xs[x]) at the lane's du_tile position: row t, columns c .. c+3.
+__device__ __forceinline__ uint2 read_xs4(const CausalSmem& sm, int x, int t, int c) {
+    const u16* blk = reinterpret_cast<const u16*>(&sm.xs[x][xs_index(t, c >> 3)]);
+    return *reinterpret_cast<const uint2*>(blk + (c & 7));
 }
 
 __device__ __forceinline__ void unpack4(uint2 w, float (&o)[4]) {
@@ -1203,570 +1275,454 @@ __device__ __forceinline__ void unpack4(uint2 w, float (&o)[4]) {
     o[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
-// phi(X)^T tiles of this wave's two feature tiles: C[f][t], token t = lo.
-__device__ __forceinline__ void features2(const CausalArgs& a, const bf16x8 (&xf)[4], int w,
-                                          float bias, bool live, int lo, int h, f32x16 (&p)[2]) {
+__device__ __forceinline__ uint32_t bf16pair(float a, float b) {
+    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// phi(X)^T tile of this wave's features: C[f][t], f in F_w, token t = lo,
+// from the token's staged bias (zero past the chunk's end).
+__device__ __forceinline__ f32x16 features1(const CausalArgs& a, const bf16x8 (&xf)[4], int w,
+                                            float bias, int lo, int h) {
+    f32x16 c = zero16();
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft) {
-        f32x16 c = zero16();
+    for (int ks = 0; ks < 4; ++ks) c = mfma(omega_frag(a.omega, 32 * w, 0, ks, lo, h), xf[ks], c);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) c = mfma(omega_frag(a.omega, 64 * w, ft, ks, lo, h), xf[ks], c);
+    for (int i = 0; i < 16; ++i) c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bias));
+    return c;
+}
+
+// z (or g) at the lane's 16 rows f = fw + 8 (i/4) + 4h + i%4 of a [f x t] tile.
+__device__ __forceinline__ void read_z(const CausalSmem& sm, int fw, int h, float (&zr)[16]) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) c[i] = live ? __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bias)) : 0.f;
-        p[ft] = c;
+    for (int m = 0; m < 4; ++m) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sm.z + fw + 8 * m + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zr[4 * m + j] = x[j];
+    }
+}
+
+// This wave's rows of w (tile [f x t], f in F_w) into the bfloat16 table.
+__device__ __forceinline__ void put_w(u16* wq, int w, int lo, int h, const f32x16& x) {
+    u16* p = wq + lo * LDW + 32 * w + 4 * h;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        *reinterpret_cast<uint2*>(p + 8 * m) =
+            make_uint2(bf16pair(x[4 * m], x[4 * m + 1]), bf16pair(x[4 * m + 2], x[4 * m + 3]));
+}
+
+// Wave w's 16 x 16 tile of du^T = omega^T w^T over all r features: rows
+// d = 16 (w/2) + 4 (lane/16) + i, column t = 16 (w%2) + lane%16.
+__device__ __forceinline__ f32x4 du_tile(const CausalSmem& sm, int w, int lane) {
+    const int c = lane & 15, g = lane >> 4;
+    const u16* pa = sm.wt + (16 * (w >> 1) + c) * LDW + 8 * g;
+    const u16* pb = sm.wq + (16 * (w & 1) + c) * LDW + 8 * g;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < R / 32; ++s) acc = mfma16(lds8(pa + 32 * s), lds8(pb + 32 * s), acc);
+    return acc;
+}
+
+// The lane's output position of du_tile in the chunk.
+__device__ __forceinline__ int du_token(int w, int lane) { return 16 * (w & 1) + (lane & 15); }
+__device__ __forceinline__ int du_col(int w, int lane) { return 16 * (w >> 1) + 4 * (lane >> 4); }
+
+// dx[t][d .. d+3] = scale (du - wsum_t u), u = scale x, at the lane's
+// du_tile position (nothing past `rows`).
+__device__ __forceinline__ void store_dx(const CausalArgs& a, const CausalSmem& sm, u16* dxc,
+                                         int w, int lane, int rows, const f32x4& du, uint2 xe) {
+    const int t = du_token(w, lane);
+    float ws = 0.f;
+#pragma unroll
+    for (int u = 0; u < NWC; ++u) ws += sm.wsum[u][t];
+    if (t >= rows) return;
+    float xv[4], o[4];
+    unpack4(xe, xv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = a.scale * (du[j] - ws * a.scale * xv[j]);
+    store4(dxc, D, t, du_col(w, lane), o);
+}
+
+// omega^T in LDS, natural f order.
+__device__ __forceinline__ void stage_omega_t(u16* wt, const u16* __restrict__ omega) {
+    for (int e = threadIdx.x; e < R * D; e += NTC) {
+        const int f = e / D, d = e % D;
+        wt[d * LDW + f] = omega[e];
     }
 }
 
 __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
-    __shared__ CausalSmem sm;
+    __shared__ CausalQuerySmem smq;
+    CausalSmem& sm = smq.c;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // wave index, uniform
     const int lo = lane & 31, h = lane >> 5;
     const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
     const int64_t t0 = g * a.seg_len, t1 = min<int64_t>(t0 + a.seg_len, a.N);
     const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
+    if (nck == 0) return; // uniform over the workgroup
     const bool attn = a.norm == NORM_ATTN;
     const bf16x8 eye[2] = {eye_frag(0, lo, h), eye_frag(1, lo, h)};
     // element i of a [row x token] tile pairs token lo with row 8(i/4) + 4h + i%4
     const int keep_thr = lo - 4 * h; // row <= token  <=>  8(i/4) + i%4 <= keep_thr
+    const int fw = 32 * w;           // first feature of this wave
+    const int pn = 32 * (w >> 2) + 8 * (w & 3) + 4 * h; // the dnum piece this wave stores
 
-    for (int e = threadIdx.x; e < R * D; e += NTC) {
-        const int f = e / D, d = e % D;
-        sm.wt[d * LDF + (f & ~15) + swap23(f & 15)] = a.omega[e];
-    }
-    // the forward state carried into the segment: S[F_w] in accumulators, z in LDS
+    stage_omega_t(sm.wt, a.omega);
+    // the forward state carried into the segment, transposed: S^T[n][F_w] in
+    // accumulators (tile nt: rows n = 32 nt + 8(i/4) + 4h + i%4, column
+    // f = fw + lo), z in LDS
     const float* st = a.state + bh * a.st_bh + g * a.st_g;
-    f32x16 S[2][2], Gi[2][2];
-    float gacc[2] = {0.f, 0.f};
+    f32x16 S[2];
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            Gi[ft][nt] = zero16();
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                S[ft][nt][i] = st[(int64_t)(64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)) * DV + 32 * nt + lo];
-        }
+        for (int i = 0; i < 16; ++i)
+            S[nt][i] = st[(int64_t)(fw + lo) * DV + 32 * nt + 8 * (i >> 2) + 4 * h + (i & 3)];
     for (int f = threadIdx.x; f < R; f += NTC) sm.z[f] = st[(int64_t)R * DV + f];
 
-    // The chunk's global loads, issued one chunk ahead into one of two
-    // register sets (two chunks per iteration, one per set, so no set is
-    // copied while its loads are in flight); every load is unconditional, at
-    // a row clamped into the chunk, and lanes past the end are zeroed when
-    // the values are used.
-    // (dout and the epilogue's q are loaded at the top of their own chunk,
-    // and used after the first barrier: registers for a second set of them
-    // would spill)
-    struct QueryLoads {
-        uint4 vx;           // V: row threadIdx/8, columns 8 (threadIdx%8) ..
-        bf16x8 qf[4], kf[4];
-    };
     auto chunk_at = [&](int ci, int64_t& c0, int& rows) {
         c0 = t0 + (int64_t)L * ci;
         rows = (int)min<int64_t>(L, t1 - c0);
     };
-    auto issue = [&](int ci, QueryLoads& ld) {
-        int64_t c0;
-        int rows;
-        chunk_at(min(ci, nck - 1), c0, rows);
-        const int jv = min((int)threadIdx.x >> 3, rows - 1);
-        ld.vx = *reinterpret_cast<const uint4*>(a.v + (bh * a.N + c0 + jv) * DV + (threadIdx.x & 7) * 8);
-        load_x(a.q + (bh * a.N + c0) * D, rows, lo, h, ld.qf);
-        load_x(a.k + (bh * a.N + c0) * D, rows, lo, h, ld.kf);
-    };
+    {
+        ChunkLoads first;
+        fetch_chunk<false>(a, bh * a.N + t0, (int)min<int64_t>(L, t1 - t0), first);
+        stash_chunk(a, sm, 0, first, (int)min<int64_t>(L, t1 - t0), nullptr);
+    }
+    __syncthreads(); // omega^T table, z and chunk 0's tables
 
-    auto body = [&](int ci, QueryLoads& cur, QueryLoads& nxt) {
+    for (int ci = 0; ci < nck; ++ci) {
         int64_t c0;
         int rows;
         chunk_at(ci, c0, rows);
         const bool live = lo < rows;
         const int buf = ci & 1;
-        const int t = min(lo, rows - 1);
-        uint2 dr[2][4], xe[4];
+        bf16x8 qf[4], kf[4];
+        lds_x(sm.xs[0], lo, h, qf);
+        lds_x(sm.xs[1], lo, h, kf);
+        const uint2 xe = read_xs4(sm, 0, du_token(w, lane), du_col(w, lane));
+        // dout of token lo as the B operand of products over n (its raw
+        // bf16 pieces), and this wave's piece of it for the dnum store
+        Tile2 dt[2];
         {
-            const u16* dor = a.dout + (bh * a.N + c0 + t) * DV;
+            uint2 dr[2][4];
+            read_ds(sm, lo, h, dr);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    dr[nt][m] = *reinterpret_cast<const uint2*>(dor + 32 * nt + 8 * m + 4 * h);
-            const u16* xr = a.q + (bh * a.N + c0 + t) * D + 32 * min(w, 1) + 4 * h;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) xe[m] = *reinterpret_cast<const uint2*>(xr + 8 * m);
-        }
-        f32x16 PQ[2], PK[2];
-        features2(a, cur.qf, w, fmaf(a.b_norm, sq_norm(cur.qf), a.b_const), live, lo, h, PQ);
-        features2(a, cur.kf, w, fmaf(a.b_norm, sq_norm(cur.kf), a.b_const), live, lo, h, PK);
-        // the next chunk's loads, now that this chunk's are consumed (the
-        // last chunk's are issued again past the end and not used)
-        issue(ci + 1, nxt);
-
-        // This wave's part of the readout over F_w: num^T [n x t] = S^T phi(Q)^T
-        // plus the masked intra-chunk block A1^T [j x t] = phi(K) phi(Q)^T
-        // (keys j <= query t) times V.  The readout enters the gradient only
-        // through two scalars per token, the denominator and
-        // dot_t = dout_t . num_t, both linear in these parts: each wave folds
-        // its part into them and only the scalars cross waves.
-        f32x16 num[2] = {zero16(), zero16()}, a1 = zero16();
-        float den = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 pq = pack8(PQ[ft], 8 * kk);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) num[nt] = mfma(pack8(S[ft][nt], 8 * kk), pq, num[nt]);
-                a1 = mfma(pack8(PK[ft], 8 * kk), pq, a1);
+            for (int nt = 0; nt < 2; ++nt) {
+                dt[nt].k[0] = __builtin_bit_cast(bf16x8, u32x4{dr[nt][0].x, dr[nt][0].y, dr[nt][1].x, dr[nt][1].y});
+                dt[nt].k[1] = __builtin_bit_cast(bf16x8, u32x4{dr[nt][2].x, dr[nt][2].y, dr[nt][3].x, dr[nt][3].y});
             }
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                den = fmaf(PQ[ft][i], sm.z[64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)], den);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            a1[i] = (8 * (i >> 2) + (i & 3) <= keep_thr) ? a1[i] : 0.f;
-            den += a1[i];
         }
-        const u16* vt = sm.vt[buf];
+        const uint2 dpiece = *reinterpret_cast<const uint2*>(sm.ds + lo * LDD + pn);
+        // the next chunk's loads (the last chunk's again past the end), into
+        // LDS between this chunk's two barriers
+        ChunkLoads nx;
+        int64_t c0n;
+        int rowsn;
+        chunk_at(min(ci + 1, nck - 1), c0n, rowsn);
+        fetch_chunk<false>(a, bh * a.N + c0n, rowsn, nx);
+
+        const f32x16 PQ = features1(a, qf, w, sm.xb[0][lo], lo, h);
+        const Tile2 pk = packt(features1(a, kf, w, sm.xb[1][lo], lo, h));
+
+        // Over F_w: the masked intra-chunk block A1^T [j x t] = phi(K) phi(Q)^T
+        // (keys j <= query t), SD [f x t] = S dout^T and VD [j x t] = V dout^T.
+        // The readout num_t enters the gradient only through the denominator
+        // and dot_t = dout_t . num_t = sum_f phi(Q)[f][t] SD[f][t] +
+        // sum_j A1^T[j][t] VD[j][t]: each wave folds its features' part of
+        // both into the token's two scalars, and only those cross waves.
+        f32x16 a1 = zero16(), SD = zero16(), VD = zero16();
+        {
+            const Tile2 pq = packt(PQ);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 af = pack8(a1, 8 * kk);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                num[nt] = mfma(lds8(vt + (32 * nt + lo) * LDT + 16 * kk + 8 * h), af, num[nt]);
+            for (int kk = 0; kk < 2; ++kk) a1 = mfma(pk.k[kk], pq.k[kk], a1);
         }
-        float o[2][4][4]; // dout of token lo (zero past the chunk's end)
-        float dot = 0.f;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                unpack4(live ? dr[nt][m] : make_uint2(0u, 0u), o[nt][m]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dot = fmaf(o[nt][m][j], num[nt][4 * m + j], dot);
-            }
-        den = half_sum(den);
-        dot = half_sum(dot);
-        if (h == 0) {
-            sm.tokv[w][0][lo] = den;
-            sm.tokv[w][3][lo] = dot;
-        }
-        sync_lds(); // B1: the waves' scalars
-
-        // the next chunk's V, into the other table pair: every wave has
-        // finished the chunk before this one (its last reader) at B1, and B2
-        // publishes it before the next chunk reads it
-        {
-            int64_t c0n;
-            int rowsn;
-            chunk_at(min(ci + 1, nck - 1), c0n, rowsn);
-            stash_v(sm.vt[buf ^ 1], sm.vs[buf ^ 1],
-                    ((int)threadIdx.x >> 3) < rowsn ? nxt.vx : make_uint4(0u, 0u, 0u, 0u));
-        }
-
-        den = 0.f;
-        dot = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            den += sm.tokv[u][0][lo];
-            dot += sm.tokv[u][3][lo];
-        }
-        // dnum^T [n x t], dden
-        const float inv = attn ? 1.f / fmaxf(den, a.eps) : 1.f;
-        f32x16 dn[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dn[nt][4 * m + j] = o[nt][m][j] * inv;
-        const float dden = (attn && den > a.eps) ? -dot * inv * inv : 0.f;
-        if (w == 0 && h == 0 && live) {
-            a.tok[2 * (bh * a.N + c0 + lo)] = inv;
-            a.tok[2 * (bh * a.N + c0 + lo) + 1] = dden;
-        }
-        if (h == 0) sm.tokv[w][1][lo] = dden; // this wave's copy, read back below
-
-        // A2^T [j x t] = V dnum^T + dden_t, masked
-        f32x16 a2 = zero16();
+            for (int kk = 0; kk < 2; ++kk) SD = mfma(pack8(S[nt], 8 * kk), dt[nt].k[kk], SD);
         const u16* vs = sm.vs[buf];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                a2 = mfma(lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), pack8(dn[nt], 8 * kk), a2);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) a2[i] = (8 * (i >> 2) + (i & 3) <= keep_thr) ? a2[i] + dden : 0.f;
-
-        // dphi(Q)^T [f x t] = S dnum^T + z dden + phi(K)^T A2^T, w = dphi o phi, du^T
-        f32x16 du[2] = {zero16(), zero16()}, PKt[2];
-        float wsum = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft) {
-            PKt[ft] = transpose32(PK[ft], eye);
-            f32x16 gq = zero16();
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const f32x16 St = transpose32(S[ft][nt], eye); // [n x f]
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) gq = mfma(pack8(St, 8 * kk), pack8(dn[nt], 8 * kk), gq);
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) gq = mfma(pack8(PKt[ft], 8 * kk), pack8(a2, 8 * kk), gq);
-            f32x16 wq;
+                VD = mfma(lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), dt[nt].k[kk], VD);
+        float den = 0.f, dot = 0.f;
+        {
+            float zr[16];
+            read_z(sm, fw, h, zr);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float gi = fmaf(sm.z[64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)], dden, gq[i]);
-                wq[i] = gi * PQ[ft][i];
-                wsum += wq[i];
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 wf = pack8(wq, 8 * kk);
-#pragma unroll
-                for (int dt = 0; dt < 2; ++dt)
-                    du[dt] = mfma(lds8(sm.wt + (32 * dt + lo) * LDF + 64 * w + 32 * ft + 16 * kk + 8 * h),
-                                  wf, du[dt]);
+                den = fmaf(PQ[i], zr[i], den);
+                dot = fmaf(PQ[i], SD[i], dot);
             }
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            a1[i] = (8 * (i >> 2) + (i & 3) <= keep_thr) ? a1[i] : 0.f;
+            den += a1[i];
+            dot = fmaf(a1[i], VD[i], dot);
+        }
+        den = half_sum(den);
+        dot = half_sum(dot);
+        if (h == 0) {
+            smq.red[w][0][lo] = den;
+            smq.red[w][1][lo] = dot;
+        }
+        sync_lds(); // B1: the waves' scalars; every wave is done with this chunk's q, k, dout
+
+        // the next chunk's tables (V into the other pair: its last reader,
+        // the chunk before this one, finished before B1); B2 publishes them
+        stash_chunk(a, sm, buf ^ 1, nx, rowsn, nullptr);
+
+        den = 0.f;
+        dot = 0.f;
+#pragma unroll
+        for (int u = 0; u < NWC; ++u) {
+            den += smq.red[u][0][lo];
+            dot += smq.red[u][1][lo];
+        }
+        // dnum_t = dout_t / D_t, dden_t (zero past the chunk's end); the key
+        // pass and the increments take dnum in bfloat16
+        const float inv = live ? (attn ? 1.f / fmaxf(den, a.eps) : 1.f) : 0.f;
+        const float dden = (attn && den > a.eps) ? -dot * inv * inv : 0.f;
+        if (live) {
+            float o[4];
+            unpack4(dpiece, o);
+            *reinterpret_cast<uint2*>(a.dnum + (bh * a.N + c0 + lo) * DV + pn) =
+                make_uint2(bf16pair(o[0] * inv, o[1] * inv), bf16pair(o[2] * inv, o[3] * inv));
+            if (w == 0 && h == 0) a.dden[bh * a.N + c0 + lo] = dden;
+        }
+
+        // A2^T [j x t] = V dnum^T + dden_t = VD / D_t + dden_t, masked
+        f32x16 a2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a2[i] = (8 * (i >> 2) + (i & 3) <= keep_thr) ? fmaf(VD[i], inv, dden) : 0.f;
+
+        // dphi(Q)^T [f x t] = SD / D_t + z dden + phi(K)^T A2^T, w = dphi o phi
+        // (phi(K)^T is exact in bf16: a transposition of bf16 values)
+        float zs = 0.f;
+        Tile2 pkt;
+        {
+            const f32x16 t = transpose_p(pk, eye);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) zs += t[i];
+            pkt = packt(t);
+        }
+        {
+            float zr[16];
+            read_z(sm, fw, h, zr);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) SD[i] = fmaf(zr[i], dden, SD[i] * inv);
+        }
+        {
+            const Tile2 a2p = packt(a2);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) SD = mfma(pkt.k[kk], a2p.k[kk], SD);
+        }
+        float wsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            SD[i] *= PQ[i];
+            wsum += SD[i];
+        }
+        put_w(sm.wq, w, lo, h, SD);
         wsum = half_sum(wsum);
-        put_tile(sm.dpart[w][0], lane, du[0]);
-        put_tile(sm.dpart[w][1], lane, du[1]);
-        if (h == 0) sm.tokv[w][2][lo] = wsum;
-        sync_lds(); // B2: du partials
-        if (w < 2) {
-            // wave dt sums d-tile dt and stores dq = scale (du - wsum u)
-            f32x16 s = zero16();
-            float ws = 0.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                add_tile(sm.dpart[u][w], lane, s);
-                ws += sm.tokv[u][2][lo];
-            }
-            if (live) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int c0d = 32 * w + 8 * m + 4 * h;
-                    float xv[4], o[4];
-                    unpack4(xe[m], xv);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) o[j] = a.scale * (s[4 * m + j] - ws * a.scale * xv[j]);
-                    store4(a.dx + (bh * a.N + c0) * D, D, lo, c0d, o);
-                }
-            }
-        }
+        if (h == 0) sm.wsum[w][lo] = wsum;
+        sync_lds(); // B2: the w table, the sums of w and the next chunk's tables
+        store_dx(a, sm, a.dx + (bh * a.N + c0) * D, w, lane, rows, du_tile(sm, w, lane), xe);
 
-        // backward increments: G[F_w] += phi(Q)^T dnum, g[F_w] += phi(Q)^T dden
-        f32x16 dnr[2];
+        // state update: S^T[:, F_w] += V^T phi(K), z[F_w] += phi(K)^T 1
+        const u16* vt = sm.vt[buf];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) dnr[nt] = transpose32(dn[nt], eye); // [t x n]
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int ft = 0; ft < 2; ++ft) {
-            const f32x16 PQt = transpose32(PQ[ft], eye); // [t x f]
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 pf = pack8(PQt, 8 * kk);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) Gi[ft][nt] = mfma(pf, pack8(dnr[nt], 8 * kk), Gi[ft][nt]);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                gacc[ft] = fmaf(PQt[i], sm.tokv[w][1][8 * (i >> 2) + 4 * h + (i & 3)], gacc[ft]);
-        }
-        // state update: S[F_w] += phi(K)^T V, z[F_w] += phi(K)^T 1
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 pk = pack8(PKt[ft], 8 * kk);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    S[ft][nt] = mfma(pk, lds8(vt + (32 * nt + lo) * LDT + 16 * kk + 8 * h), S[ft][nt]);
-            }
-            float zs = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) zs += PKt[ft][i];
-            zs = half_sum(zs);
-            if (h == 0) sm.z[64 * w + 32 * ft + lo] += zs;
-        }
-    };
-
-    // chunk 0's V is staged before the first barrier; every later chunk's
-    // between the two barriers of the chunk before it (see body)
-    QueryLoads A, B;
-    if (nck > 0) {
-        issue(0, A);
-        int64_t c0;
-        int rows;
-        chunk_at(0, c0, rows);
-        stash_v(sm.vt[0], sm.vs[0], ((int)threadIdx.x >> 3) < rows ? A.vx : make_uint4(0u, 0u, 0u, 0u));
-    }
-    __syncthreads(); // omega^T table, z and chunk 0's V
-    if (nck > 0) {
-        for (int ci = 0; ci < nck; ci += 2) {
-            body(ci, A, B);
-            if (ci + 1 < nck) body(ci + 1, B, A);
-        }
-    }
-    // the segment's backward increments
-    float* dst = a.inc + (bh * a.G + g) * state_elems(R);
-#pragma unroll
-    for (int ft = 0; ft < 2; ++ft) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                dst[(int64_t)(64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)) * DV + 32 * nt + lo] = Gi[ft][nt][i];
-        const float gs = half_sum(gacc[ft]);
-        if (h == 0) dst[(int64_t)R * DV + 64 * w + 32 * ft + lo] = gs;
+            for (int nt = 0; nt < 2; ++nt)
+                S[nt] = mfma(lds8(vt + (32 * nt + lo) * LDT + 16 * kk + 8 * h), pkt.k[kk], S[nt]);
+        zs = half_sum(zs);
+        if (h == 0) sm.z[fw + lo] += zs;
     }
 }
 
 __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
-    __shared__ CausalSmem sm;
+    __shared__ CausalKeySmem smk;
+    CausalSmem& sm = smk.c;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // wave index, uniform
     const int lo = lane & 31, h = lane >> 5;
     const int64_t bh = blockIdx.x / a.G, g = blockIdx.x % a.G;
     const int64_t t0 = g * a.seg_len, t1 = min<int64_t>(t0 + a.seg_len, a.N);
     const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
+    if (nck == 0) return; // uniform over the workgroup
     const bf16x8 eye[2] = {eye_frag(0, lo, h), eye_frag(1, lo, h)};
     // element i of a [row x key] tile pairs key lo with row (query) 8(i/4) + 4h + i%4
     const int keep_thr = lo - 4 * h; // query >= key  <=>  8(i/4) + i%4 >= keep_thr
+    const int fw = 32 * w;
 
-    for (int e = threadIdx.x; e < R * D; e += NTC) {
-        const int f = e / D, d = e % D;
-        sm.wt[d * LDF + (f & ~15) + swap23(f & 15)] = a.omega[e];
-    }
+    stage_omega_t(sm.wt, a.omega);
     // the backward state after the segment (suffix): G[F_w] in accumulators, g in LDS
     const float* st = a.state + bh * a.st_bh + g * a.st_g;
-    f32x16 Gs[2][2];
+    f32x16 Gs[2];
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                Gs[ft][nt][i] = st[(int64_t)(64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)) * DV + 32 * nt + lo];
+        for (int i = 0; i < 16; ++i)
+            Gs[nt][i] = st[(int64_t)(fw + 8 * (i >> 2) + 4 * h + (i & 3)) * DV + 32 * nt + lo];
     for (int f = threadIdx.x; f < R; f += NTC) sm.z[f] = st[(int64_t)R * DV + f];
-    __syncthreads(); // omega^T table and g
 
-    // The chunk's global loads, issued one chunk ahead into one of two
-    // register sets (the loop runs two chunks per iteration, one per set, so
-    // no set is copied while its loads are in flight).  Every load is
-    // unconditional, at a row clamped into the chunk: lanes past the end are
-    // zeroed when the values are used.
-    struct KeyLoads {
-        uint4 vx;           // V: row threadIdx/8, columns 8 (threadIdx%8) ..
-        bf16x8 qf[4], kf[4];
-        float inv, dden;
-        uint2 dr[2][4];     // dout of the lane's query
-        uint2 xe[4];        // k of the lane's key (waves 2, 3), for dk
-    };
     auto chunk_at = [&](int cr, int64_t& c0, int& rows) {
         const int ci = nck - 1 - cr; // chunks last to first
         c0 = t0 + (int64_t)L * ci;
         rows = (int)min<int64_t>(L, t1 - c0);
     };
-    auto issue = [&](int cr, KeyLoads& ld) {
+    {
         int64_t c0;
         int rows;
-        chunk_at(min(cr, nck - 1), c0, rows);
-        const int jv = min((int)threadIdx.x >> 3, rows - 1), t = min(lo, rows - 1);
-        ld.vx = *reinterpret_cast<const uint4*>(a.v + (bh * a.N + c0 + jv) * DV + (threadIdx.x & 7) * 8);
-        load_x(a.q + (bh * a.N + c0) * D, rows, lo, h, ld.qf);
-        load_x(a.k + (bh * a.N + c0) * D, rows, lo, h, ld.kf);
-        ld.inv = a.tok[2 * (bh * a.N + c0 + t)];
-        ld.dden = a.tok[2 * (bh * a.N + c0 + t) + 1];
-        const u16* dor = a.dout + (bh * a.N + c0 + t) * DV;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                ld.dr[nt][m] = *reinterpret_cast<const uint2*>(dor + 32 * nt + 8 * m + 4 * h);
-    };
-    auto issue_xe = [&](int cr, KeyLoads& ld) {
-        int64_t c0;
-        int rows;
-        chunk_at(min(cr, nck - 1), c0, rows);
-        const u16* xr = a.k + (bh * a.N + c0 + min(lo, rows - 1)) * D + 32 * max(w - 2, 0) + 4 * h;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) ld.xe[m] = *reinterpret_cast<const uint2*>(xr + 8 * m);
-    };
+        chunk_at(0, c0, rows);
+        ChunkLoads first;
+        fetch_chunk<true>(a, bh * a.N + c0, rows, first);
+        stash_chunk(a, sm, 0, first, rows, smk.dnt);
+        if (threadIdx.x < L) smk.dden[0][threadIdx.x] = (int)threadIdx.x < rows ? first.dd : 0.f;
+    }
+    __syncthreads(); // omega^T table, g and the first chunk's tables
 
-    auto body = [&](int cr, KeyLoads& cur, KeyLoads& nxt) {
+    for (int cr = 0; cr < nck; ++cr) {
         int64_t c0;
         int rows;
         chunk_at(cr, c0, rows);
         const bool live = lo < rows;
         const int buf = cr & 1;
-        const bool vlive = ((int)threadIdx.x >> 3) < rows;
-        stash_v(sm.vt[buf], sm.vs[buf], vlive ? cur.vx : make_uint4(0u, 0u, 0u, 0u));
-        f32x16 PQ[2], PK[2];
-        features2(a, cur.qf, w, fmaf(a.b_norm, sq_norm(cur.qf), a.b_const), live, lo, h, PQ);
-        features2(a, cur.kf, w, fmaf(a.b_norm, sq_norm(cur.kf), a.b_const), live, lo, h, PK);
-        const float inv = live ? cur.inv : 0.f, dden = live ? cur.dden : 0.f;
-        // dnum^T [n x i] = dout^T / D_i and dden_i of the lane's query i = lo
-        f32x16 dn[2];
+        bf16x8 qf[4], kf[4];
+        lds_x(sm.xs[0], lo, h, qf);
+        lds_x(sm.xs[1], lo, h, kf);
+        const uint2 xe = read_xs4(sm, 1, du_token(w, lane), du_col(w, lane));
+        // dnum^T [n x i] of the lane's query i = lo: its bfloat16 pieces are the
+        // operands; and its transpose [i x n] as operands from the transposed table
+        Tile2 dn[2], dnr[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                float o[4];
-                unpack4(cur.dr[nt][m], o);
+            for (int kk = 0; kk < 2; ++kk) dnr[nt].k[kk] = lds8(smk.dnt + (32 * nt + lo) * LDT + 16 * kk + 8 * h);
+        {
+            uint2 dr[2][4];
+            read_ds(sm, lo, h, dr);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dn[nt][4 * m + j] = o[j] * inv;
+            for (int nt = 0; nt < 2; ++nt) {
+                dn[nt].k[0] = __builtin_bit_cast(bf16x8, u32x4{dr[nt][0].x, dr[nt][0].y, dr[nt][1].x, dr[nt][1].y});
+                dn[nt].k[1] = __builtin_bit_cast(bf16x8, u32x4{dr[nt][2].x, dr[nt][2].y, dr[nt][3].x, dr[nt][3].y});
             }
-        // the next chunk's loads, now that this chunk's are consumed (the
-        // last chunk's are issued again past the end and not used)
-        issue(cr + 1, nxt);
-        if (h == 0) sm.tokv[w][1][lo] = dden; // this wave's copy, by query
+        }
+        ChunkLoads nx;
+        int64_t c0n;
+        int rowsn;
+        chunk_at(min(cr + 1, nck - 1), c0n, rowsn);
+        fetch_chunk<true>(a, bh * a.N + c0n, rowsn, nx);
+
+        const Tile2 pq = packt(features1(a, qf, w, sm.xb[0][lo], lo, h));
+        const f32x16 PK = features1(a, kf, w, sm.xb[1][lo], lo, h);
+        const Tile2 pk = packt(PK);
 
         // partials over F_w: dv^T [n x j] = G^T phi(K)^T, B1 [i x j] = phi(Q) phi(K)^T
         f32x16 dvp[2] = {zero16(), zero16()}, b1 = zero16();
 #pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 pk = pack8(PK[ft], 8 * kk);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) dvp[nt] = mfma(pack8(Gs[ft][nt], 8 * kk), pk, dvp[nt]);
-                b1 = mfma(pack8(PQ[ft], 8 * kk), pk, b1);
-            }
+            for (int nt = 0; nt < 2; ++nt) dvp[nt] = mfma(pack8(Gs[nt], 8 * kk), pk.k[kk], dvp[nt]);
+            b1 = mfma(pq.k[kk], pk.k[kk], b1);
+        }
         // dv^T = G^T phi(K)^T + dnum^T (B1 masked: query i >= key j) is linear
         // in the parts over F_w, so each wave adds its own masked block's
         // term before its part crosses waves
-        f32x16 dnr[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) dnr[nt] = transpose32(dn[nt], eye); // [i x n]
 #pragma unroll
         for (int i = 0; i < 16; ++i) b1[i] = (8 * (i >> 2) + (i & 3) >= keep_thr) ? b1[i] : 0.f;
+        {
+            const Tile2 b1p = packt(b1);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) dvp[nt] = mfma(pack8(dnr[nt], 8 * kk), pack8(b1, 8 * kk), dvp[nt]);
-        put_tile(sm.part[w][0], lane, dvp[0]);
-        put_tile(sm.part[w][1], lane, dvp[1]);
-        sync_lds(); // B1: partials, dden copies and V tables of the chunk
+                for (int kk = 0; kk < 2; ++kk) dvp[nt] = mfma(dnr[nt].k[kk], b1p.k[kk], dvp[nt]);
+        }
+        put_tile(smk.part[w][0], lane, dvp[0]);
+        put_tile(smk.part[w][1], lane, dvp[1]);
+        sync_lds(); // B1: partials; every wave is done with this chunk's q, k, dnum
 
-        const u16* vs = sm.vs[buf];
-        // wave nt < 2: dv^T tile nt = sum of the four parts (the tile index
-        // is a constant in each branch)
-        auto dv_tile = [&](int nt) {
-            f32x16 s = zero16();
+        // the next chunk's tables (V and dden into the other pair: their last
+        // reader, the chunk before this one, finished before B1); B2
+        // publishes them
+        stash_chunk(a, sm, buf ^ 1, nx, rowsn, smk.dnt);
+        if (threadIdx.x < L) smk.dden[buf ^ 1][threadIdx.x] = (int)threadIdx.x < rowsn ? nx.dd : 0.f;
+
+        // dv: wave w sums elements 4 (w%4) .. +3 of tile w/4 over the eight
+        // parts: rows n = 32 (w/4) + 8 (w%4) + 4h + e, column j = lo
+        {
+            const int nt = w >> 2, qq = w & 3;
+            const int off = 16 * lane + 4 * (qq ^ tile_swz(lane));
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) add_tile(sm.part[u][nt], lane, s);
+            for (int u = 0; u < NWC; ++u) s += *reinterpret_cast<const f32x4*>(smk.part[u][nt] + off);
             if (live) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float o[4] = {s[4 * m], s[4 * m + 1], s[4 * m + 2], s[4 * m + 3]};
-                    store4(a.dv + (bh * a.N + c0) * DV, DV, lo, 32 * nt + 8 * m + 4 * h, o);
-                }
+                const float o[4] = {s[0], s[1], s[2], s[3]};
+                store4(a.dv + (bh * a.N + c0) * DV, DV, lo, 32 * nt + 8 * qq + 4 * h, o);
             }
-        };
-        if (w == 0)
-            dv_tile(0);
-        else if (w == 1)
-            dv_tile(1);
+        }
         // A3 [i x j] = dnum_i . v_j + dden_i, masked (i >= j)
+        const u16* vs = sm.vs[buf];
+        const float* ddn = smk.dden[buf];
         f32x16 a3 = zero16();
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                a3 = mfma(pack8(dn[nt], 8 * kk), lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), a3);
+                a3 = mfma(dn[nt].k[kk], lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), a3);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            a3[i] = (8 * (i >> 2) + (i & 3) >= keep_thr)
-                        ? a3[i] + sm.tokv[w][1][8 * (i >> 2) + 4 * h + (i & 3)]
-                        : 0.f;
-        // dphi(K)^T [f x j] = G V^T + g + phi(Q)^T A3, w = dphi o phi, du^T
-        f32x16 du[2] = {zero16(), zero16()}, PQt[2];
+            a3[i] = (8 * (i >> 2) + (i & 3) >= keep_thr) ? a3[i] + ddn[8 * (i >> 2) + 4 * h + (i & 3)] : 0.f;
+        // dphi(K)^T [f x j] = G V^T + g + phi(Q)^T A3, w = dphi o phi
+        // (phi(Q)^T is exact in bf16: a transposition of bf16 values)
+        float gsum = 0.f;
+        Tile2 pqt;
+        {
+            const f32x16 t = transpose_p(pq, eye); // [i x f]
+#pragma unroll
+            for (int i = 0; i < 16; ++i) gsum = fmaf(t[i], ddn[8 * (i >> 2) + 4 * h + (i & 3)], gsum);
+            pqt = packt(t);
+        }
+        f32x16 gk = zero16();
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const Tile2 gt = packt(transpose32(Gs[nt], eye)); // [n x f]
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                gk = mfma(gt.k[kk], lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), gk);
+        }
+        {
+            const Tile2 a3p = packt(a3);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) gk = mfma(pqt.k[kk], a3p.k[kk], gk);
+        }
         float wsum = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft) {
-            PQt[ft] = transpose32(PQ[ft], eye); // [i x f]
-            f32x16 gk = zero16();
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const f32x16 Gt = transpose32(Gs[ft][nt], eye); // [n x f]
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    gk = mfma(pack8(Gt, 8 * kk), lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), gk);
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) gk = mfma(pack8(PQt[ft], 8 * kk), pack8(a3, 8 * kk), gk);
-            f32x16 wk;
+        {
+            float zr[16];
+            read_z(sm, fw, h, zr);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float gi = gk[i] + sm.z[64 * w + 32 * ft + 8 * (i >> 2) + 4 * h + (i & 3)];
-                wk[i] = gi * PK[ft][i];
-                wsum += wk[i];
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 wf = pack8(wk, 8 * kk);
-#pragma unroll
-                for (int dt = 0; dt < 2; ++dt)
-                    du[dt] = mfma(lds8(sm.wt + (32 * dt + lo) * LDF + 64 * w + 32 * ft + 16 * kk + 8 * h),
-                                  wf, du[dt]);
+                gk[i] = (gk[i] + zr[i]) * PK[i];
+                wsum += gk[i];
             }
         }
+        put_w(sm.wq, w, lo, h, gk);
         wsum = half_sum(wsum);
-        put_tile(sm.dpart[w][0], lane, du[0]);
-        put_tile(sm.dpart[w][1], lane, du[1]);
-        if (h == 0) sm.tokv[w][2][lo] = wsum;
-        sync_lds(); // B2: du partials
-        if (w >= 2) {
-            // wave 2 + dt: dk tile dt = scale (du - wsum u)
-            const int dt = w - 2;
-            f32x16 s = zero16();
-            float ws = 0.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                add_tile(sm.dpart[u][dt], lane, s);
-                ws += sm.tokv[u][2][lo];
-            }
-            if (live) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int c0d = 32 * dt + 8 * m + 4 * h;
-                    float xv[4], o[4];
-                    unpack4(cur.xe[m], xv);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) o[j] = a.scale * (s[4 * m + j] - ws * a.scale * xv[j]);
-                    store4(a.dx + (bh * a.N + c0) * D, D, lo, c0d, o);
-                }
-            }
-        }
-        issue_xe(cr + 1, nxt);
+        if (h == 0) sm.wsum[w][lo] = wsum;
+        sync_lds(); // B2: the w table, the sums of w and the next chunk's tables
+        store_dx(a, sm, a.dx + (bh * a.N + c0) * D, w, lane, rows, du_tile(sm, w, lane), xe);
+
         // suffix update for the earlier chunks: G[F_w] += phi(Q)^T dnum, g += phi(Q)^T dden
 #pragma unroll
-        for (int ft = 0; ft < 2; ++ft) {
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 pf = pack8(PQt[ft], 8 * kk);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) Gs[ft][nt] = mfma(pf, pack8(dnr[nt], 8 * kk), Gs[ft][nt]);
-            }
-            float gsum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                gsum = fmaf(PQt[ft][i], sm.tokv[w][1][8 * (i >> 2) + 4 * h + (i & 3)], gsum);
-            gsum = half_sum(gsum);
-            if (h == 0) sm.z[64 * w + 32 * ft + lo] += gsum;
-        }
-    };
-
-    if (nck > 0) {
-        KeyLoads A, B;
-        issue(0, A);
-        issue_xe(0, A);
-        for (int cr = 0; cr < nck; cr += 2) {
-            body(cr, A, B);
-            if (cr + 1 < nck) body(cr + 1, B, A);
-        }
+            for (int nt = 0; nt < 2; ++nt) Gs[nt] = mfma(pqt.k[kk], dnr[nt].k[kk], Gs[nt]);
+        gsum = half_sum(gsum);
+        if (h == 0) sm.z[fw + lo] += gsum;
     }
 }
 
@@ -1810,7 +1766,7 @@ hipError_t launch_favor_bwd_key(const Cfg& c, const void* k, const void* v, cons
 
 static CausalArgs causal_args(const Cfg& c, const void* q, const void* k, const void* v,
                               const void* dout, const void* omega, Shape s, SegPlan sp,
-                              const float* state, int64_t sbh, int64_t sg, float* tok, float* inc,
+                              const float* state, int64_t sbh, int64_t sg, void* dnum, float* dden,
                               void* dx, void* dv) {
     CausalArgs a;
     a.q = (const u16*)q;
@@ -1830,8 +1786,8 @@ static CausalArgs causal_args(const Cfg& c, const void* q, const void* k, const 
     a.state = state;
     a.st_bh = sbh;
     a.st_g = sg;
-    a.tok = tok;
-    a.inc = inc;
+    a.dnum = (u16*)dnum;
+    a.dden = dden;
     a.dx = (u16*)dx;
     a.dv = (u16*)dv;
     return a;
@@ -1839,20 +1795,20 @@ static CausalArgs causal_args(const Cfg& c, const void* q, const void* k, const 
 
 hipError_t launch_favor_causal_bwd_query(const Cfg& c, const void* q, const void* k, const void* v,
                                          const void* dout, const void* omega, Shape s, SegPlan sp,
-                                         const float* prefix, int64_t sbh, int64_t sg, float* tok,
-                                         float* inc, void* dq, hipStream_t st) {
+                                         const float* prefix, int64_t sbh, int64_t sg, void* dnum,
+                                         float* dden, void* dq, hipStream_t st) {
     const CausalArgs a =
-        causal_args(c, q, k, v, dout, omega, s, sp, prefix, sbh, sg, tok, inc, dq, nullptr);
+        causal_args(c, q, k, v, dout, omega, s, sp, prefix, sbh, sg, dnum, dden, dq, nullptr);
     hipLaunchKernelGGL(k_bwd_causal_query_favor, dim3((unsigned)(sp.G * s.BH)), dim3(NTC), 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_favor_causal_bwd_key(const Cfg& c, const void* q, const void* k, const void* v,
-                                       const void* dout, const void* omega, Shape s, SegPlan sp,
-                                       const float* suffix, int64_t sbh, int64_t sg,
-                                       const float* tok, void* dk, void* dv, hipStream_t st) {
-    const CausalArgs a = causal_args(c, q, k, v, dout, omega, s, sp, suffix, sbh, sg,
-                                     const_cast<float*>(tok), nullptr, dk, dv);
+                                       const void* omega, Shape s, SegPlan sp, const float* suffix,
+                                       int64_t sbh, int64_t sg, const void* dnum, const float* dden,
+                                       void* dk, void* dv, hipStream_t st) {
+    const CausalArgs a = causal_args(c, q, k, v, nullptr, omega, s, sp, suffix, sbh, sg,
+                                     const_cast<void*>(dnum), const_cast<float*>(dden), dk, dv);
     hipLaunchKernelGGL(k_bwd_causal_key_favor, dim3((unsigned)(sp.G * s.BH)), dim3(NTC), 0, st, a);
     return hipGetLastError();
 }

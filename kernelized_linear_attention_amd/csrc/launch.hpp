@@ -195,17 +195,18 @@ hipError_t launch_favor_bwd_key(const Cfg& c, const void* k, const void* v, cons
                                 hipStream_t st);
 
 // Causal backward on the matrix cores (same configuration): the query pass
-// from each segment's forward prefix writes dq, (1/D, dden) per token and the
-// segment's backward increments; the key pass from each segment's backward
-// suffix writes dk and dv.
+// from each segment's forward prefix writes dq, dnum (bf16 [BH, N, DV]) and
+// dden (float [BH, N]), from which the increment kernel (with z weights dden)
+// forms the segments' backward increments; the key pass from each segment's
+// backward suffix writes dk and dv.
 hipError_t launch_favor_causal_bwd_query(const Cfg& c, const void* q, const void* k, const void* v,
                                          const void* dout, const void* omega, Shape s, SegPlan sp,
-                                         const float* prefix, int64_t sbh, int64_t sg, float* tok,
-                                         float* inc, void* dq, hipStream_t st);
+                                         const float* prefix, int64_t sbh, int64_t sg, void* dnum,
+                                         float* dden, void* dq, hipStream_t st);
 hipError_t launch_favor_causal_bwd_key(const Cfg& c, const void* q, const void* k, const void* v,
-                                       const void* dout, const void* omega, Shape s, SegPlan sp,
-                                       const float* suffix, int64_t sbh, int64_t sg,
-                                       const float* tok, void* dk, void* dv, hipStream_t st);
+                                       const void* omega, Shape s, SegPlan sp, const float* suffix,
+                                       int64_t sbh, int64_t sg, const void* dnum, const float* dden,
+                                       void* dk, void* dv, hipStream_t st);
 
 // Orthogonal random features (orf.hip): n_mat matrices [r, d], d <= 64.
 hipError_t launch_orf(const float* gauss, const float* len_gauss, int64_t n_mat, int64_t r, int d,

@@ -362,10 +362,11 @@ def test_backward_arguments(fn):
 def test_backward_workspace_formula():
     """Forward and backward increments of every segment (the vector kernels'
     plan: two workgroups per CU, 64 segments of 1024 tokens per head at H = 8,
-    N = 65536), then the two full summaries per head (bidirectional) or two
-    floats per token (causal: 1 / max(den, eps) and the denominator's
-    gradient), or the dnum (bf16) and dden of every token (bidirectional),
-    then r * 64 floats for omega^T (used in bfloat16 by FAVOR+)."""
+    N = 65536), then the two full summaries per head (bidirectional only),
+    then the dnum (bf16) and dden of every token (the vector route's causal
+    pass uses two floats per token of that space: 1 / max(den, eps) and the
+    denominator's gradient), then r * 64 floats for omega^T (used in bfloat16
+    by FAVOR+)."""
     p = params()
     E = 256 * 64 + 256
     inc = 2 * 8 * 64 * E * 4
@@ -375,7 +376,7 @@ def test_backward_workspace_formula():
     assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR_BACKWARD, p, 1, 8, 65536, 64, 64) == \
         inc + 2 * 8 * E * 4 + tokens + om_t
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 65536, 64, 64) == \
-        inc + 8 * 65536 * 2 * 4 + om_t
+        inc + tokens + om_t
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 0, 64, 64) == 0
 
 

@@ -640,6 +640,7 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
     __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LDV];
     __shared__ bf16x8 ks_s[2][256];
     __shared__ __attribute__((aligned(16))) float kb_s[2][L]; // key biases by chunk parity
+    __shared__ __attribute__((aligned(16))) float zw_s[ZW ? 2 : 1][L]; // z weights by chunk parity
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lo = lane & 31, h = lane >> 5;
@@ -662,9 +663,17 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
     const u16* vb = a.v + bh * a.N * DV;
     auto kchunk = [&](int c) { return kb + (t0 + (int64_t)L * c) * D; };
     auto vchunk = [&](int c) { return vb + (t0 + (int64_t)L * c) * DV; };
-    // stagers hold the keys of chunk c + 1 and the values of chunk c in
-    // registers at the top of iteration c
+    // stagers hold the keys (and z weights) of chunk c + 1 and the values of
+    // chunk c in registers at the top of iteration c
     bf16x8 kr, vr;
+    float zr = 0.f; // ZW: the weight of token tid / 8 (threads with tid % 8 == 0)
+    const float* zwb = ZW ? a.zw + bh * a.N + t0 : nullptr;
+    auto load_zw = [&](int c) {
+        if (ZW && (tid & 7) == 0) zr = zwb[(int64_t)L * c + min(tid >> 3, rows_of(c) - 1)];
+    };
+    auto stage_zw = [&](int c) {
+        if (ZW && (tid & 7) == 0) zw_s[c & 1][tid >> 3] = (tid >> 3) < rows_of(c) ? zr : 0.f;
+    };
     // the key bias of a chunk is computed once, by the stagers, from the
     // blocks they hold: the eight threads of a row sum their squares (keys
     // past the end of the segment get bias -inf, so exp2 gives 0)
@@ -681,24 +690,30 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
     };
     if (nck > 0 && stager) {
         const bf16x8 k0 = load_block(kchunk(0), rows_of(0), tid);
+        load_zw(0);
         ks_s[0][tid] = k0;
         stage_bias(k0, 0);
+        stage_zw(0);
         const int c1 = min(1, nck - 1);
         kr = load_block(kchunk(c1), rows_of(c1), tid);
+        load_zw(c1);
         vr = load_v(vchunk(0), rows_of(0), tid);
     }
     sync_lds(); // keys of chunk 0 staged
     wait_all_loads(); // omega's fragments, once, not in every iteration
 
     for (int ci = 0; ci < nck; ++ci) {
-        const int rows = rows_of(ci);
         if (stager) {
             // past the end: the last chunk again, so every iteration has the same loads
             const int c1 = min(ci + 1, nck - 1), c2 = min(ci + 2, nck - 1);
             ks_s[(ci + 1) & 1][tid] = kr;
-            if (ci + 1 < nck) stage_bias(kr, ci + 1);
+            if (ci + 1 < nck) {
+                stage_bias(kr, ci + 1);
+                stage_zw(ci + 1);
+            }
             store_vt(vt_s[ci & 1], tid, vr);
             kr = load_block(kchunk(c2), rows_of(c2), tid);
+            load_zw(c2);
             vr = load_v(vchunk(c1), rows_of(c1), tid);
         }
         bf16x8 kf[4];
@@ -715,13 +730,16 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
         if (!ZW) {
             zacc += sum8(fk0) + sum8(fk1); // the bfloat16 features that also enter S
         } else {
-            // weighted: element i is token 8(i/4) + 4h + i%4 of the chunk
-            const float* wt = a.zw + bh * a.N + t0 + (int64_t)L * ci;
+            // weighted: element i is token 8(i/4) + 4h + i%4 of the chunk (the
+            // staged weights are zero past the end)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = 8 * (i >> 2) + 4 * h + (i & 3);
-                const float x = (float)(i < 8 ? fk0[i] : fk1[i - 8]);
-                if (t < rows) zacc = fmaf(x, wt[t], zacc);
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 wz = *reinterpret_cast<const f32x4*>(&zw_s[ci & 1][8 * j + 4 * h]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * j + e;
+                    zacc = fmaf((float)(i < 8 ? fk0[i] : fk1[i - 8]), wz[e], zacc);
+                }
             }
         }
         sync_lds(); // V^T of this chunk and the keys of the next staged
@@ -1384,14 +1402,22 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         c0 = t0 + (int64_t)L * ci;
         rows = (int)min<int64_t>(L, t1 - c0);
     };
+    // Global loads run two chunks ahead: chunk c + 2's are issued at the top
+    // of chunk c into one register set, chunk c + 1's (issued a chunk
+    // earlier, into the other set) are staged between chunk c's barriers.
+    ChunkLoads LA, LB;
     {
         ChunkLoads first;
         fetch_chunk<false>(a, bh * a.N + t0, (int)min<int64_t>(L, t1 - t0), first);
         stash_chunk(a, sm, 0, first, (int)min<int64_t>(L, t1 - t0), nullptr);
+        int64_t c1;
+        int rows1;
+        chunk_at(min(1, nck - 1), c1, rows1);
+        fetch_chunk<false>(a, bh * a.N + c1, rows1, LA);
     }
     __syncthreads(); // omega^T table, z and chunk 0's tables
 
-    for (int ci = 0; ci < nck; ++ci) {
+    auto body = [&](int ci, const ChunkLoads& sl, ChunkLoads& il) {
         int64_t c0;
         int rows;
         chunk_at(ci, c0, rows);
@@ -1414,13 +1440,12 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
             }
         }
         const uint2 dpiece = *reinterpret_cast<const uint2*>(sm.ds + lo * LDD + pn);
-        // the next chunk's loads (the last chunk's again past the end), into
-        // LDS between this chunk's two barriers
-        ChunkLoads nx;
+        // chunk c + 2's loads (the last chunk's again past the end)
         int64_t c0n;
         int rowsn;
+        chunk_at(min(ci + 2, nck - 1), c0n, rowsn);
+        fetch_chunk<false>(a, bh * a.N + c0n, rowsn, il);
         chunk_at(min(ci + 1, nck - 1), c0n, rowsn);
-        fetch_chunk<false>(a, bh * a.N + c0n, rowsn, nx);
 
         const f32x16 PQ = features1(a, qf, w, sm.xb[0][lo], lo, h);
         const Tile2 pk = packt(features1(a, kf, w, sm.xb[1][lo], lo, h));
@@ -1473,7 +1498,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
 
         // the next chunk's tables (V into the other pair: its last reader,
         // the chunk before this one, finished before B1); B2 publishes them
-        stash_chunk(a, sm, buf ^ 1, nx, rowsn, nullptr);
+        stash_chunk(a, sm, buf ^ 1, sl, rowsn, nullptr);
 
         den = 0.f;
         dot = 0.f;
@@ -1541,6 +1566,10 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
                 S[nt] = mfma(lds8(vt + (32 * nt + lo) * LDT + 16 * kk + 8 * h), pkt.k[kk], S[nt]);
         zs = half_sum(zs);
         if (h == 0) sm.z[fw + lo] += zs;
+    };
+    for (int ci = 0; ci < nck; ci += 2) {
+        body(ci, LA, LB);
+        if (ci + 1 < nck) body(ci + 1, LB, LA);
     }
 }
 
@@ -1575,6 +1604,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         c0 = t0 + (int64_t)L * ci;
         rows = (int)min<int64_t>(L, t1 - c0);
     };
+    // Global loads run two chunks ahead (as in the query pass).
+    ChunkLoads LA, LB;
     {
         int64_t c0;
         int rows;
@@ -1583,10 +1614,12 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         fetch_chunk<true>(a, bh * a.N + c0, rows, first);
         stash_chunk(a, sm, 0, first, rows, smk.dnt);
         if (threadIdx.x < L) smk.dden[0][threadIdx.x] = (int)threadIdx.x < rows ? first.dd : 0.f;
+        chunk_at(min(1, nck - 1), c0, rows);
+        fetch_chunk<true>(a, bh * a.N + c0, rows, LA);
     }
     __syncthreads(); // omega^T table, g and the first chunk's tables
 
-    for (int cr = 0; cr < nck; ++cr) {
+    auto body = [&](int cr, const ChunkLoads& sl, ChunkLoads& il) {
         int64_t c0;
         int rows;
         chunk_at(cr, c0, rows);
@@ -1612,11 +1645,11 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
                 dn[nt].k[1] = __builtin_bit_cast(bf16x8, u32x4{dr[nt][2].x, dr[nt][2].y, dr[nt][3].x, dr[nt][3].y});
             }
         }
-        ChunkLoads nx;
         int64_t c0n;
         int rowsn;
+        chunk_at(min(cr + 2, nck - 1), c0n, rowsn);
+        fetch_chunk<true>(a, bh * a.N + c0n, rowsn, il);
         chunk_at(min(cr + 1, nck - 1), c0n, rowsn);
-        fetch_chunk<true>(a, bh * a.N + c0n, rowsn, nx);
 
         const Tile2 pq = packt(features1(a, qf, w, sm.xb[0][lo], lo, h));
         const f32x16 PK = features1(a, kf, w, sm.xb[1][lo], lo, h);
@@ -1649,8 +1682,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         // the next chunk's tables (V and dden into the other pair: their last
         // reader, the chunk before this one, finished before B1); B2
         // publishes them
-        stash_chunk(a, sm, buf ^ 1, nx, rowsn, smk.dnt);
-        if (threadIdx.x < L) smk.dden[buf ^ 1][threadIdx.x] = (int)threadIdx.x < rowsn ? nx.dd : 0.f;
+        stash_chunk(a, sm, buf ^ 1, sl, rowsn, smk.dnt);
+        if (threadIdx.x < L) smk.dden[buf ^ 1][threadIdx.x] = (int)threadIdx.x < rowsn ? sl.dd : 0.f;
 
         // dv: wave w sums elements 4 (w%4) .. +3 of tile w/4 over the eight
         // parts: rows n = 32 (w/4) + 8 (w%4) + 4h + e, column j = lo
@@ -1723,6 +1756,10 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
             for (int nt = 0; nt < 2; ++nt) Gs[nt] = mfma(pqt.k[kk], dnr[nt].k[kk], Gs[nt]);
         gsum = half_sum(gsum);
         if (h == 0) sm.z[fw + lo] += gsum;
+    };
+    for (int cr = 0; cr < nck; cr += 2) {
+        body(cr, LA, LB);
+        if (cr + 1 < nck) body(cr + 1, LB, LA);
     }
 }
 

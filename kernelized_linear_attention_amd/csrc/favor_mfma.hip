@@ -1207,37 +1207,56 @@ struct CausalKeySmem {
     float part[NWC][2][64 * 16];   // per wave: partial dv^T tiles (put_tile)
 };
 
-// The next chunk's global loads, held in registers across the first barrier
-// of the current one: thread th fetches 16-byte block th%256 of q (th < 256)
-// or k, row th/16, columns 4 (th%16) .. +3 of V and of dout (query pass) or
-// dnum (key pass), and (key pass, th < 32) dden of token th, at rows clamped
-// into the chunk.
+// A chunk's global loads, held in registers until they are staged: thread th
+// fetches 16-byte block th%256 of q (th < 256) or k; row vrow(th), columns
+// vcol(th) .. +3 of V and of dout (query pass) or dnum (key pass) (the four
+// lanes of a quad hold four consecutive rows of the same columns); and (key
+// pass, th < 32) dden of token th; at rows clamped into the chunk.
 struct ChunkLoads {
     bf16x8 xb;
     uint2 vx, dx;
     float dd;
 };
 
+__device__ __forceinline__ int vrow(int th) { return 4 * (th >> 6) + (th & 3); }
+__device__ __forceinline__ int vcol(int th) { return 4 * ((th >> 2) & 15); }
+
 template <bool KEY>
 __device__ __forceinline__ void fetch_chunk(const CausalArgs& a, int64_t row0, int rows,
                                             ChunkLoads& ld) {
     const int th = threadIdx.x;
     ld.xb = load_block((th < 256 ? a.q : a.k) + row0 * D, rows, th & 255);
-    const int64_t j = row0 + min(th >> 4, rows - 1);
-    ld.vx = *reinterpret_cast<const uint2*>(a.v + j * DV + (th & 15) * 4);
-    ld.dx = *reinterpret_cast<const uint2*>((KEY ? a.dnum : a.dout) + j * DV + (th & 15) * 4);
+    const int64_t j = row0 + min(vrow(th), rows - 1);
+    ld.vx = *reinterpret_cast<const uint2*>(a.v + j * DV + vcol(th));
+    ld.dx = *reinterpret_cast<const uint2*>((KEY ? a.dnum : a.dout) + j * DV + vcol(th));
     if (KEY) ld.dd = a.dden[row0 + min(th & (L - 1), rows - 1)];
 }
 
-// Four bf16 (a row's columns n0 .. n0+3, token j) into a transposed table
-// [n][j'] (j in swap23 order).
-__device__ __forceinline__ void put_transposed4(u16* tt, int j, int n0, uint2 x) {
-    const uint32_t wd[2] = {x.x, x.y};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const u16 val = (e & 1) ? (u16)(wd[e >> 1] >> 16) : (u16)(wd[e >> 1] & 0xffffu);
-        tt[(n0 + e) * LDT + (j & ~15) + swap23(j & 15)] = val;
+// A quad's 4 x 4 block (lane e: row j0 + e, columns n0 .. n0+3, as two
+// words of bf16 pairs) into a transposed table [n][j'] (j in swap23 order):
+// two DPP exchanges within the quad leave lane e with column n0 + e of the
+// four rows, which it writes as one 8-byte piece (four consecutive j keep
+// their order under swap23).
+__device__ __forceinline__ void put_transposed_quad(u16* tt, int j0, int n0, uint2 x) {
+    const int e = threadIdx.x & 3;
+    // lanes e, e ^ 2 swap the column pairs they do not keep: afterwards P holds
+    // row j0 + e % 2 and Q row j0 + 2 + e % 2, columns 2 (e / 2) and +1
+    const uint32_t send = e < 2 ? x.y : x.x;
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, true);
+    const uint32_t mine = e < 2 ? x.x : x.y;
+    const uint32_t P = e < 2 ? mine : recv, Q = e < 2 ? recv : mine;
+    // lanes e, e ^ 1 swap halves: the even lane keeps the low (first) column
+    const uint32_t pP = (uint32_t)__builtin_amdgcn_mov_dpp((int)P, 0xB1, 0xF, 0xF, true);
+    const uint32_t pQ = (uint32_t)__builtin_amdgcn_mov_dpp((int)Q, 0xB1, 0xF, 0xF, true);
+    uint2 o;
+    if ((e & 1) == 0) {
+        o.x = (P & 0xffffu) | (pP << 16);
+        o.y = (Q & 0xffffu) | (pQ << 16);
+    } else {
+        o.x = (pP >> 16) | (P & 0xffff0000u);
+        o.y = (pQ >> 16) | (Q & 0xffff0000u);
     }
+    *reinterpret_cast<uint2*>(tt + (n0 + e) * LDT + (j0 & ~15) + swap23(j0 & 15)) = o;
 }
 
 // ... and their LDS copies (V, dout / dnum zero past `rows`), with the
@@ -1259,15 +1278,15 @@ __device__ __forceinline__ void stash_chunk(const CausalArgs& a, CausalSmem& sm,
         const int t = (th & 255) >> 3;
         if ((th & 7) == 0) sm.xb[th >> 8][t] = t < rows ? fmaf(a.b_norm, sq, a.b_const) : -INFINITY;
     }
-    const int j = th >> 4, n0 = (th & 15) * 4;
+    const int j = vrow(th), n0 = vcol(th);
     const bool in = j < rows;
     const uint2 x = in ? ld.vx : make_uint2(0u, 0u);
-    put_transposed4(sm.vt[buf], j, n0, x);
+    put_transposed_quad(sm.vt[buf], j & ~3, n0, x);
     // four consecutive n keep their order under swap23 (bits 0, 1 untouched)
     *reinterpret_cast<uint2*>(sm.vs[buf] + j * LDN + (n0 & ~15) + swap23(n0 & 15)) = x;
     const uint2 dx = in ? ld.dx : make_uint2(0u, 0u);
     *reinterpret_cast<uint2*>(sm.ds + j * LDD + n0) = dx;
-    if (dnt) put_transposed4(dnt, j, n0, dx);
+    if (dnt) put_transposed_quad(dnt, j & ~3, n0, dx);
 }
 
 // Row lo of the chunk's dout / dnum table as the lane's pieces

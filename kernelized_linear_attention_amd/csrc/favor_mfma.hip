@@ -171,23 +171,51 @@ __device__ __forceinline__ float sq_norm(const bf16x8 (&f)[4]) {
     return half_sum(s[0] + s[1]);
 }
 
-// Raw V rows of the chunk for the transposed LDS copy: thread th holds
-// V[th/8][8 (th%8) .. +7] (rows past `rows` repeat row rows-1; they only
-// ever meet zero weights).
+// A 4 x 4 block of bf16 held by the four lanes of a quad (lane e: row e,
+// columns 0 .. 3 as two words of pairs) transposed within the quad: lane e
+// gets column e, rows 0 .. 3.  Lanes e and e ^ 2 first swap the column pairs
+// they do not keep, then lanes e and e ^ 1 swap halves (two DPP exchanges).
+// Every lane of the quad must be active.
+__device__ __forceinline__ uint2 quad_transpose4(uint2 x) {
+    const int e = threadIdx.x & 3;
+    // afterwards P holds row e % 2 and Q row 2 + e % 2, columns 2 (e / 2), +1
+    const uint32_t send = e < 2 ? x.y : x.x;
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, true);
+    const uint32_t mine = e < 2 ? x.x : x.y;
+    const uint32_t P = e < 2 ? mine : recv, Q = e < 2 ? recv : mine;
+    // the even lane keeps the first column of its pair, the odd lane the second
+    const uint32_t pP = (uint32_t)__builtin_amdgcn_mov_dpp((int)P, 0xB1, 0xF, 0xF, true);
+    const uint32_t pQ = (uint32_t)__builtin_amdgcn_mov_dpp((int)Q, 0xB1, 0xF, 0xF, true);
+    if ((e & 1) == 0) return make_uint2((P & 0xffffu) | (pP << 16), (Q & 0xffffu) | (pQ << 16));
+    return make_uint2((pP >> 16) | (P & 0xffff0000u), (pQ >> 16) | (Q & 0xffff0000u));
+}
+
+// Raw V rows of the chunk for the transposed LDS copy: thread th (of 256)
+// holds row 4 (th / 32) + th % 4, columns 8 ((th / 4) % 8) .. +7, so the four
+// lanes of a quad hold four consecutive rows of the same columns (rows past
+// `rows` repeat row rows-1; they only ever meet zero weights).
+__device__ __forceinline__ int v_row(int tid) { return 4 * (tid >> 5) + (tid & 3); }
+__device__ __forceinline__ int v_col(int tid) { return 8 * ((tid >> 2) & 7); }
 __device__ __forceinline__ bf16x8 load_v(const u16* __restrict__ V, int rows, int tid) {
-    const int t = min(tid >> 3, rows - 1), n0 = (tid & 7) * 8;
-    return *reinterpret_cast<const bf16x8*>(V + (int64_t)t * DV + n0);
+    return *reinterpret_cast<const bf16x8*>(V + (int64_t)min(v_row(tid), rows - 1) * DV + v_col(tid));
 }
 
 // V^T in LDS: row n holds V[t][n] at column vt_col(n, swap23(t)); the
 // 16-byte chunks of a row are rotated by (n / 8) % 4 so that the transposing
-// stores (eight rows 8 apart at a time) fall on different banks.
+// stores fall on different banks.
 __device__ __forceinline__ int vt_col(int n, int c) { return (((c >> 3) ^ ((n >> 3) & 3)) << 3) | (c & 7); }
 
+// The quad's 4 rows x 8 columns, transposed within the quad as two 4 x 4
+// blocks: lane e writes columns n0 + e and n0 + 4 + e, four rows each, as
+// 8-byte pieces (four consecutive rows from a multiple of 4 keep their order
+// under swap23 and vt_col).  Called by all four lanes of every quad.
 __device__ __forceinline__ void store_vt(u16* vt, int tid, const bf16x8& vr) {
-    const int t = swap23(tid >> 3), n0 = (tid & 7) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vt[(n0 + e) * LDV + vt_col(n0 + e, t)] = bf16_bits(vr, e);
+    const int t = swap23(v_row(tid) & ~3), n0 = v_col(tid), e = tid & 3;
+    const u32x4 w = __builtin_bit_cast(u32x4, vr);
+    const uint2 lo = quad_transpose4(make_uint2(w[0], w[1]));
+    const uint2 hi = quad_transpose4(make_uint2(w[2], w[3]));
+    *reinterpret_cast<uint2*>(vt + (n0 + e) * LDV + vt_col(n0 + e, t)) = lo;
+    *reinterpret_cast<uint2*>(vt + (n0 + 4 + e) * LDV + vt_col(n0 + 4 + e, t)) = hi;
 }
 
 // omega[f0 + 32 t + lo][16 ks + 8 h ..]: A operand of omega X^T (t = feature
@@ -1232,31 +1260,13 @@ __device__ __forceinline__ void fetch_chunk(const CausalArgs& a, int64_t row0, i
     if (KEY) ld.dd = a.dden[row0 + min(th & (L - 1), rows - 1)];
 }
 
-// A quad's 4 x 4 block (lane e: row j0 + e, columns n0 .. n0+3, as two
-// words of bf16 pairs) into a transposed table [n][j'] (j in swap23 order):
-// two DPP exchanges within the quad leave lane e with column n0 + e of the
-// four rows, which it writes as one 8-byte piece (four consecutive j keep
-// their order under swap23).
+// A quad's 4 x 4 block (lane e: row j0 + e, columns n0 .. n0+3) into a
+// transposed table [n][j'] (j in swap23 order): lane e writes column n0 + e
+// of the four rows as one 8-byte piece (four consecutive j from a multiple
+// of 4 keep their order under swap23).  Called by all four lanes of a quad.
 __device__ __forceinline__ void put_transposed_quad(u16* tt, int j0, int n0, uint2 x) {
     const int e = threadIdx.x & 3;
-    // lanes e, e ^ 2 swap the column pairs they do not keep: afterwards P holds
-    // row j0 + e % 2 and Q row j0 + 2 + e % 2, columns 2 (e / 2) and +1
-    const uint32_t send = e < 2 ? x.y : x.x;
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, true);
-    const uint32_t mine = e < 2 ? x.x : x.y;
-    const uint32_t P = e < 2 ? mine : recv, Q = e < 2 ? recv : mine;
-    // lanes e, e ^ 1 swap halves: the even lane keeps the low (first) column
-    const uint32_t pP = (uint32_t)__builtin_amdgcn_mov_dpp((int)P, 0xB1, 0xF, 0xF, true);
-    const uint32_t pQ = (uint32_t)__builtin_amdgcn_mov_dpp((int)Q, 0xB1, 0xF, 0xF, true);
-    uint2 o;
-    if ((e & 1) == 0) {
-        o.x = (P & 0xffffu) | (pP << 16);
-        o.y = (Q & 0xffffu) | (pQ << 16);
-    } else {
-        o.x = (pP >> 16) | (P & 0xffff0000u);
-        o.y = (pQ >> 16) | (Q & 0xffff0000u);
-    }
-    *reinterpret_cast<uint2*>(tt + (n0 + e) * LDT + (j0 & ~15) + swap23(j0 & 15)) = o;
+    *reinterpret_cast<uint2*>(tt + (n0 + e) * LDT + (j0 & ~15) + swap23(j0 & 15)) = quad_transpose4(x);
 }
 
 // ... and their LDS copies (V, dout / dnum zero past `rows`), with the

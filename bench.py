@@ -110,24 +110,32 @@ def main():
               "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
 
     def timed(fn, steps, warmup):
-        """Runs fn() warmup + steps times; returns (total ms of the timed steps,
-        list of per-call event ms)."""
+        """Runs fn() warmup times, then `steps` times back to back between one
+        event pair (the timed region), then `steps` more times with an event
+        pair around each call.  Returns (total ms of the timed region, list of
+        the per-call event ms).  The timed region has no marker between calls:
+        on this stack each event record between two calls holds the stream for
+        a few microseconds, so the per-call times read high and serve only for
+        the spread (percentiles)."""
         for _ in range(warmup):
             fn(0)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         t0.record()
+        for i in range(steps):
+            fn(i)
+        t1.record()
+        torch.cuda.synchronize()
+        total = t0.elapsed_time(t1)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
         for i in range(steps):
             evs[i][0].record()
             fn(i)
             evs[i][1].record()
-        t1.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in evs]
+        return total, [a.elapsed_time(b) for a, b in evs]
 
     def settle(fn, seconds=SETTLE_S):
         """Runs fn(i) back to back for about `seconds` (untimed) and returns
@@ -180,7 +188,7 @@ def main():
         n_settle = settle(step)
         total_ms, per = timed(step, args.steps, args.warmup)
         ms = total_ms / args.steps
-        call_ms = float(np.mean(per))
+        call_ms = ms  # average call duration over the timed region
         toks = w.B * w.N
         flops = favor_alg_flops_per_tok_head(w.r, w.d, w.dv) * w.B * w.H * w.N
         achieved = flops / (call_ms * 1e-3) / 1e12
@@ -206,7 +214,7 @@ def main():
         result["settle"] = {
             "seconds_per_section": SETTLE_S, "prefill_calls": n_settle,
             "cold_ms_per_step": cold_ms / args.steps,
-            "cold_avg_launch_ms": float(np.mean(cold_per)),
+            "cold_avg_launch_ms": cold_ms / args.steps,
             "note": "each section runs its own calls, untimed, for the seconds above (the "
                     "prefill: also the 0.4 s of clock sampling) before its W warmup and K timed "
                     "steps; cold_* are the prefill's first W + K calls on the device, timed the "
@@ -305,7 +313,7 @@ def main():
         total_ms, per = timed(bstep, args.steps, args.warmup)
         bms = total_ms / args.steps
         bflops = favor_alg_flops_per_tok_head(wb.r, wb.d, wb.dv) * wb.B * wb.H * wb.N
-        bach = bflops / (float(np.mean(per)) * 1e-3) / 1e12
+        bach = bflops / (bms * 1e-3) / 1e12
         result["bidir"] = {"workload": wb.name, "B": wb.B, "H": wb.H, "N": wb.N, "r": wb.r,
                            "ms_per_step": bms, "tokens_per_s": wb.B * wb.N / (bms * 1e-3),
                            "call_ms": percentiles(per),
@@ -315,7 +323,7 @@ def main():
                                         "traffic": stored_traffic("bidir"),
                                         "kernel": "lin_attn_bidir (whole call)",
                                         "alg_flops_per_launch": bflops,
-                                        "avg_launch_ms": float(np.mean(per))}}
+                                        "avg_launch_ms": bms}}
         del bsets
 
     # ------------------------------------------------------------------ ELU+1, small
@@ -388,7 +396,7 @@ def main():
         settle(dpstep)
         total_ms, per = timed(dpstep, args.steps, args.warmup)
         dflops = dpfp_alg_flops_per_tok_head(wdp.r, wdp.dv) * wdp.B * wdp.H * wdp.N
-        dach = dflops / (float(np.mean(per)) * 1e-3) / 1e12
+        dach = dflops / (total_ms / args.steps * 1e-3) / 1e12
         result["dpfp"] = {"workload": wdp.name, "B": wdp.B, "H": wdp.H, "N": wdp.N, "r": wdp.r,
                           "nu": wdp.nu, "sum_norm": wdp.sum_norm, "norm": wdp.norm,
                           "dtype": "f32", "ms_per_step": total_ms / args.steps,
@@ -399,7 +407,7 @@ def main():
                                        "traffic": stored_traffic("dpfp"),
                                        "kernel": "lin_attn_causal_chunked (whole call, fp32 matrix-core kernels)",
                                        "alg_flops_per_launch": dflops,
-                                       "avg_launch_ms": float(np.mean(per))}}
+                                       "avg_launch_ms": total_ms / args.steps}}
         del dsets
 
     # ------------------------------------------------------------------ device copy
@@ -443,7 +451,7 @@ def main():
         total_ms, per = timed(vstep, args.steps, args.warmup)
         vms = total_ms / args.steps
         vflops = favor_alg_flops_per_tok_head(wv.r, wv.d, wv.dv) * wv.H * wv.N
-        vach = vflops / (float(np.mean(per)) * 1e-3) / 1e12
+        vach = vflops / (vms * 1e-3) / 1e12
         result["varlen"] = {"workload": wv.name, "sequences": wv.B, "H": wv.H,
                             "tokens": wv.N, "min_len": int(lens.min()), "max_len": int(lens.max()),
                             "ms_per_step": vms, "tokens_per_s": wv.N / (vms * 1e-3),
@@ -477,7 +485,7 @@ def main():
             total_ms, per = timed(kstep, args.steps, args.warmup)
             kms = total_ms / args.steps
             kflops = backward_alg_flops_per_tok_head(wk.r, wk.d, wk.dv) * wk.B * wk.H * wk.N
-            kach = kflops / (float(np.mean(per)) * 1e-3) / 1e12
+            kach = kflops / (kms * 1e-3) / 1e12
             # bf16 FAVOR+ with r = 256: both backward forms run on the matrix cores
             mfma = True
             peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
@@ -488,7 +496,7 @@ def main():
                                      "kernel": "whole call (" + ("bf16 matrix-core kernels"
                                                if mfma else "fp32 vector kernels") + ")",
                                      "alg_flops_per_launch": kflops,
-                                     "avg_launch_ms": float(np.mean(per))}}
+                                     "avg_launch_ms": kms}}
             del ksets
         result["backward"] = bw
 
@@ -556,10 +564,10 @@ def main():
             total_ms, per = timed(pstep, args.steps, args.warmup)
             g_total, _ = timed(gstep, args.steps, args.warmup)
             u_total, _ = timed(ustep, args.steps, args.warmup)
-            g_only, g_per = timed(gonly, args.steps, args.warmup)
+            g_only, _ = timed(gonly, args.steps, args.warmup)
         pms = total_ms / args.steps
-        pach = (proj_flops + att_flops) / (float(np.mean(per)) * 1e-3) / 1e12
-        g_ms = float(np.mean(g_per))
+        pach = (proj_flops + att_flops) / (pms * 1e-3) / 1e12
+        g_ms = g_only / args.steps
         g_tflops = proj_flops / (g_ms * 1e-3) / 1e12
         result["proj"] = {
             "workload": wp.name + "_from_tokens", "B": wp.B, "H": wp.H, "N": wp.N, "d_model": dm,
@@ -574,7 +582,7 @@ def main():
                          "unit": "TFLOP/s", "frac": pach / PEAK_BF16_TFLOPS,
                          "kernel": "whole call (projection GEMM, then the matrix-core prefill)",
                          "alg_flops_per_launch": proj_flops + att_flops,
-                         "avg_launch_ms": float(np.mean(per))}}
+                         "avg_launch_ms": pms}}
         del psets
 
     if args.only in (None, "prefill") and not args.no_cpu_baseline:

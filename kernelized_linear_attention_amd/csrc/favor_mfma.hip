@@ -1231,7 +1231,7 @@ struct CausalQuerySmem {
 struct CausalKeySmem {
     CausalSmem c;
     u16 dnt[DV * LDT];             // dnum^T [n][i'] of the chunk (i in swap23 order)
-    float dden[2][L];              // dden of the chunk's queries (by chunk parity)
+    float dden[2][L] __attribute__((aligned(16))); // dden of the chunk's queries (by chunk parity)
     float part[NWC][2][64 * 16];   // per wave: partial dv^T tiles (put_tile)
 };
 
@@ -1271,8 +1271,11 @@ __device__ __forceinline__ void put_transposed_quad(u16* tt, int j0, int n0, uin
 
 // ... and their LDS copies (V, dout / dnum zero past `rows`), with the
 // per-token biases of the feature map: the eight threads of a q or k row sum
-// their squares; tokens past the end get -inf (exp2 gives 0).  dnt: the key
-// pass's transposed dnum table, or NULL.
+// their squares; tokens past the end get -inf (exp2 gives 0).  The key pass
+// also writes the transposed dnum table dnt.  Per-token values are written
+// by every lane that holds them (the same value to the same address), so
+// that no store needs a branch.
+template <bool KEY>
 __device__ __forceinline__ void stash_chunk(const CausalArgs& a, CausalSmem& sm, int buf,
                                             const ChunkLoads& ld, int rows, u16* dnt) {
     const int th = threadIdx.x;
@@ -1286,7 +1289,7 @@ __device__ __forceinline__ void stash_chunk(const CausalArgs& a, CausalSmem& sm,
         }
         sq = row8_sum(sq);
         const int t = (th & 255) >> 3;
-        if ((th & 7) == 0) sm.xb[th >> 8][t] = t < rows ? fmaf(a.b_norm, sq, a.b_const) : -INFINITY;
+        sm.xb[th >> 8][t] = t < rows ? fmaf(a.b_norm, sq, a.b_const) : -INFINITY;
     }
     const int j = vrow(th), n0 = vcol(th);
     const bool in = j < rows;
@@ -1296,7 +1299,7 @@ __device__ __forceinline__ void stash_chunk(const CausalArgs& a, CausalSmem& sm,
     *reinterpret_cast<uint2*>(sm.vs[buf] + j * LDN + (n0 & ~15) + swap23(n0 & 15)) = x;
     const uint2 dx = in ? ld.dx : make_uint2(0u, 0u);
     *reinterpret_cast<uint2*>(sm.ds + j * LDD + n0) = dx;
-    if (dnt) put_transposed_quad(dnt, j & ~3, n0, dx);
+    if (KEY) put_transposed_quad(dnt, j & ~3, n0, dx);
 }
 
 // Row lo of the chunk's dout / dnum table as the lane's pieces
@@ -1338,14 +1341,20 @@ __device__ __forceinline__ f32x16 features1(const CausalArgs& a, const bf16x8 (&
     return c;
 }
 
-// z (or g) at the lane's 16 rows f = fw + 8 (i/4) + 4h + i%4 of a [f x t] tile.
-__device__ __forceinline__ void read_z(const CausalSmem& sm, int fw, int h, float (&zr)[16]) {
+// p[8 (i/4) + 4h + i%4] for the lane's 16 rows i of an accumulator tile, as
+// four 16-byte reads (p 16-byte aligned).
+__device__ __forceinline__ void read_rows(const float* p, int h, float (&r)[16]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(sm.z + fw + 8 * m + 4 * h);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(p + 8 * m + 4 * h);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) zr[4 * m + j] = x[j];
+        for (int j = 0; j < 4; ++j) r[4 * m + j] = x[j];
     }
+}
+
+// z (or g) at the lane's 16 rows f = fw + 8 (i/4) + 4h + i%4 of a [f x t] tile.
+__device__ __forceinline__ void read_z(const CausalSmem& sm, int fw, int h, float (&zr)[16]) {
+    read_rows(sm.z + fw, h, zr);
 }
 
 // This wave's rows of w (tile [f x t], f in F_w) into the bfloat16 table.
@@ -1373,20 +1382,32 @@ __device__ __forceinline__ f32x4 du_tile(const CausalSmem& sm, int w, int lane) 
 __device__ __forceinline__ int du_token(int w, int lane) { return 16 * (w & 1) + (lane & 15); }
 __device__ __forceinline__ int du_col(int w, int lane) { return 16 * (w >> 1) + 4 * (lane >> 4); }
 
+// Raw buffer resource over the first `rows` rows of width `width` (bf16)
+// at p: stores at byte offsets past the end are dropped by the hardware, so
+// the chunk's stores need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(void* p, int rows, int width) {
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, rows * width * 2, 0x00020000);
+}
+__device__ __forceinline__ void store_b64(__amdgpu_buffer_rsrc_t rs, int byte_off, uint2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, rs, byte_off, 0, 0);
+}
+__device__ __forceinline__ uint2 bf16x4_bits(const float (&o)[4]) {
+    return make_uint2(bf16pair(o[0], o[1]), bf16pair(o[2], o[3]));
+}
+
 // dx[t][d .. d+3] = scale (du - wsum_t u), u = scale x, at the lane's
-// du_tile position (nothing past `rows`).
+// du_tile position (dropped past the chunk's rows).
 __device__ __forceinline__ void store_dx(const CausalArgs& a, const CausalSmem& sm, u16* dxc,
                                          int w, int lane, int rows, const f32x4& du, uint2 xe) {
     const int t = du_token(w, lane);
     float ws = 0.f;
 #pragma unroll
     for (int u = 0; u < NWC; ++u) ws += sm.wsum[u][t];
-    if (t >= rows) return;
     float xv[4], o[4];
     unpack4(xe, xv);
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = a.scale * (du[j] - ws * a.scale * xv[j]);
-    store4(dxc, D, t, du_col(w, lane), o);
+    store_b64(chunk_rsrc(dxc, rows, D), 2 * (t * D + du_col(w, lane)), bf16x4_bits(o));
 }
 
 // omega^T in LDS, natural f order.
@@ -1438,7 +1459,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
     {
         ChunkLoads first;
         fetch_chunk<false>(a, bh * a.N + t0, (int)min<int64_t>(L, t1 - t0), first);
-        stash_chunk(a, sm, 0, first, (int)min<int64_t>(L, t1 - t0), nullptr);
+        stash_chunk<false>(a, sm, 0, first, (int)min<int64_t>(L, t1 - t0), nullptr);
         int64_t c1;
         int rows1;
         chunk_at(min(1, nck - 1), c1, rows1);
@@ -1519,15 +1540,13 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         }
         den = half_sum(den);
         dot = half_sum(dot);
-        if (h == 0) {
-            smq.red[w][0][lo] = den;
-            smq.red[w][1][lo] = dot;
-        }
+        smq.red[w][0][lo] = den; // both halves: the same value
+        smq.red[w][1][lo] = dot;
         sync_lds(); // B1: the waves' scalars; every wave is done with this chunk's q, k, dout
 
         // the next chunk's tables (V into the other pair: its last reader,
         // the chunk before this one, finished before B1); B2 publishes them
-        stash_chunk(a, sm, buf ^ 1, sl, rowsn, nullptr);
+        stash_chunk<false>(a, sm, buf ^ 1, sl, rowsn, nullptr);
 
         den = 0.f;
         dot = 0.f;
@@ -1540,12 +1559,18 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         // pass and the increments take dnum in bfloat16
         const float inv = live ? (attn ? 1.f / fmaxf(den, a.eps) : 1.f) : 0.f;
         const float dden = (attn && den > a.eps) ? -dot * inv * inv : 0.f;
-        if (live) {
+        {
             float o[4];
             unpack4(dpiece, o);
-            *reinterpret_cast<uint2*>(a.dnum + (bh * a.N + c0 + lo) * DV + pn) =
-                make_uint2(bf16pair(o[0] * inv, o[1] * inv), bf16pair(o[2] * inv, o[3] * inv));
-            if (w == 0 && h == 0) a.dden[bh * a.N + c0 + lo] = dden;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] *= inv;
+            store_b64(chunk_rsrc(a.dnum + (bh * a.N + c0) * DV, rows, DV), 2 * (lo * DV + pn),
+                      bf16x4_bits(o));
+            // dden from wave 0's first half (every other lane's offset is past the end)
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc(a.dden + bh * a.N + c0, 0, rows * 4, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dden), rs,
+                                                  (w == 0 && h == 0) ? 4 * lo : 4 * L, 0, 0);
         }
 
         // A2^T [j x t] = V dnum^T + dden_t = VD / D_t + dden_t, masked
@@ -1582,7 +1607,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         }
         put_w(sm.wq, w, lo, h, SD);
         wsum = half_sum(wsum);
-        if (h == 0) sm.wsum[w][lo] = wsum;
+        sm.wsum[w][lo] = wsum; // both halves: the same value
         sync_lds(); // B2: the w table, the sums of w and the next chunk's tables
         store_dx(a, sm, a.dx + (bh * a.N + c0) * D, w, lane, rows, du_tile(sm, w, lane), xe);
 
@@ -1594,7 +1619,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
             for (int nt = 0; nt < 2; ++nt)
                 S[nt] = mfma(lds8(vt + (32 * nt + lo) * LDT + 16 * kk + 8 * h), pkt.k[kk], S[nt]);
         zs = half_sum(zs);
-        if (h == 0) sm.z[fw + lo] += zs;
+        sm.z[fw + lo] += zs; // both halves: the same value
     };
     for (int ci = 0; ci < nck; ci += 2) {
         body(ci, LA, LB);
@@ -1641,8 +1666,9 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         chunk_at(0, c0, rows);
         ChunkLoads first;
         fetch_chunk<true>(a, bh * a.N + c0, rows, first);
-        stash_chunk(a, sm, 0, first, rows, smk.dnt);
-        if (threadIdx.x < L) smk.dden[0][threadIdx.x] = (int)threadIdx.x < rows ? first.dd : 0.f;
+        stash_chunk<true>(a, sm, 0, first, rows, smk.dnt);
+        // every thread holds dden of token th % 32
+        smk.dden[0][threadIdx.x & (L - 1)] = (int)(threadIdx.x & (L - 1)) < rows ? first.dd : 0.f;
         chunk_at(min(1, nck - 1), c0, rows);
         fetch_chunk<true>(a, bh * a.N + c0, rows, LA);
     }
@@ -1711,8 +1737,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         // the next chunk's tables (V and dden into the other pair: their last
         // reader, the chunk before this one, finished before B1); B2
         // publishes them
-        stash_chunk(a, sm, buf ^ 1, sl, rowsn, smk.dnt);
-        if (threadIdx.x < L) smk.dden[buf ^ 1][threadIdx.x] = (int)threadIdx.x < rowsn ? sl.dd : 0.f;
+        stash_chunk<true>(a, sm, buf ^ 1, sl, rowsn, smk.dnt);
+        smk.dden[buf ^ 1][threadIdx.x & (L - 1)] = (int)(threadIdx.x & (L - 1)) < rowsn ? sl.dd : 0.f;
 
         // dv: wave w sums elements 4 (w%4) .. +3 of tile w/4 over the eight
         // parts: rows n = 32 (w/4) + 8 (w%4) + 4h + e, column j = lo
@@ -1722,14 +1748,14 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < NWC; ++u) s += *reinterpret_cast<const f32x4*>(smk.part[u][nt] + off);
-            if (live) {
-                const float o[4] = {s[0], s[1], s[2], s[3]};
-                store4(a.dv + (bh * a.N + c0) * DV, DV, lo, 32 * nt + 8 * qq + 4 * h, o);
-            }
+            const float o[4] = {s[0], s[1], s[2], s[3]};
+            store_b64(chunk_rsrc(a.dv + (bh * a.N + c0) * DV, rows, DV),
+                      2 * (lo * DV + 32 * nt + 8 * qq + 4 * h), bf16x4_bits(o));
         }
         // A3 [i x j] = dnum_i . v_j + dden_i, masked (i >= j)
         const u16* vs = sm.vs[buf];
-        const float* ddn = smk.dden[buf];
+        float ddn[16]; // dden of the lane's 16 query rows
+        read_rows(smk.dden[buf], h, ddn);
         f32x16 a3 = zero16();
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
@@ -1737,8 +1763,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
             for (int kk = 0; kk < 2; ++kk)
                 a3 = mfma(dn[nt].k[kk], lds8(vs + lo * LDN + 32 * nt + 16 * kk + 8 * h), a3);
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            a3[i] = (8 * (i >> 2) + (i & 3) >= keep_thr) ? a3[i] + ddn[8 * (i >> 2) + 4 * h + (i & 3)] : 0.f;
+        for (int i = 0; i < 16; ++i) a3[i] = (8 * (i >> 2) + (i & 3) >= keep_thr) ? a3[i] + ddn[i] : 0.f;
         // dphi(K)^T [f x j] = G V^T + g + phi(Q)^T A3, w = dphi o phi
         // (phi(Q)^T is exact in bf16: a transposition of bf16 values)
         float gsum = 0.f;
@@ -1746,7 +1771,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         {
             const f32x16 t = transpose_p(pq, eye); // [i x f]
 #pragma unroll
-            for (int i = 0; i < 16; ++i) gsum = fmaf(t[i], ddn[8 * (i >> 2) + 4 * h + (i & 3)], gsum);
+            for (int i = 0; i < 16; ++i) gsum = fmaf(t[i], ddn[i], gsum);
             pqt = packt(t);
         }
         f32x16 gk = zero16();
@@ -1774,7 +1799,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         }
         put_w(sm.wq, w, lo, h, gk);
         wsum = half_sum(wsum);
-        if (h == 0) sm.wsum[w][lo] = wsum;
+        sm.wsum[w][lo] = wsum; // both halves: the same value
         sync_lds(); // B2: the w table, the sums of w and the next chunk's tables
         store_dx(a, sm, a.dx + (bh * a.N + c0) * D, w, lane, rows, du_tile(sm, w, lane), xe);
 
@@ -1784,7 +1809,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) Gs[nt] = mfma(pqt.k[kk], dnr[nt].k[kk], Gs[nt]);
         gsum = half_sum(gsum);
-        if (h == 0) sm.z[fw + lo] += gsum;
+        sm.z[fw + lo] += gsum; // both halves: the same value
     };
     for (int cr = 0; cr < nck; cr += 2) {
         body(cr, LA, LB);

@@ -1557,8 +1557,13 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         }
         // dnum_t = dout_t / D_t, dden_t (zero past the chunk's end); the key
         // pass and the increments take dnum in bfloat16
-        const float inv = live ? (attn ? 1.f / fmaxf(den, a.eps) : 1.f) : 0.f;
-        const float dden = (attn && den > a.eps) ? -dot * inv * inv : 0.f;
+        // (both are formed in every lane and then selected: work under a
+        // lane condition would become a branch)
+        float rden = 1.f / fmaxf(den, a.eps);
+        asm volatile("" : "+v"(rden), "+v"(dot));
+        const float inv = live ? (attn ? rden : 1.f) : 0.f;
+        const float dd_all = -dot * inv * inv;
+        const float dden = (attn && den > a.eps) ? dd_all : 0.f;
         {
             float o[4];
             unpack4(dpiece, o);

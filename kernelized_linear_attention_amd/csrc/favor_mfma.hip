@@ -425,12 +425,14 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
     auto stage_store = [&](int c) {
         const int s = c & 1, t = tid >> 3;
         sm.xq[s][tid] = qr;
+        // (all eight threads of the row hold the sum and write the same value:
+        // a write by one of them only would become a branch)
         const float sq = row_sq(qr);
-        if ((tid & 7) == 0) sm.qb[s][t] = fmaf(a.b_norm, sq, a.b_const);
+        sm.qb[s][t] = fmaf(a.b_norm, sq, a.b_const);
         if (CAUSAL) {
             sm.xk[s][tid] = kr;
             const float sk = row_sq(kr);
-            if ((tid & 7) == 0) sm.kb[s][t] = t < rows_of(c) ? fmaf(a.b_norm, sk, a.b_const) : -INFINITY;
+            sm.kb[s][t] = t < rows_of(c) ? fmaf(a.b_norm, sk, a.b_const) : -INFINITY;
             store_vt(sm.vt[s], tid, vr);
         }
     };
@@ -694,17 +696,18 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
     // stagers hold the keys (and z weights) of chunk c + 1 and the values of
     // chunk c in registers at the top of iteration c
     bf16x8 kr, vr;
-    float zr = 0.f; // ZW: the weight of token tid / 8 (threads with tid % 8 == 0)
+    float zr = 0.f; // ZW: the weight of token tid / 8 (the eight threads of a row alike)
     const float* zwb = ZW ? a.zw + bh * a.N + t0 : nullptr;
     auto load_zw = [&](int c) {
-        if (ZW && (tid & 7) == 0) zr = zwb[(int64_t)L * c + min(tid >> 3, rows_of(c) - 1)];
+        if (ZW) zr = zwb[(int64_t)L * c + min(tid >> 3, rows_of(c) - 1)];
     };
     auto stage_zw = [&](int c) {
-        if (ZW && (tid & 7) == 0) zw_s[c & 1][tid >> 3] = (tid >> 3) < rows_of(c) ? zr : 0.f;
+        if (ZW) zw_s[c & 1][tid >> 3] = (tid >> 3) < rows_of(c) ? zr : 0.f;
     };
     // the key bias of a chunk is computed once, by the stagers, from the
     // blocks they hold: the eight threads of a row sum their squares (keys
-    // past the end of the segment get bias -inf, so exp2 gives 0)
+    // past the end of the segment get bias -inf, so exp2 gives 0) and all
+    // eight write it (a write by one of them only would become a branch)
     auto stage_bias = [&](const bf16x8& blk, int c) {
         float sq = 0.f;
 #pragma unroll
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
         }
         sq = row8_sum(sq);
         const int t = tid >> 3;
-        if ((tid & 7) == 0) kb_s[c & 1][t] = t < rows_of(c) ? fmaf(a.b_norm, sq, a.b_const) : -INFINITY;
+        kb_s[c & 1][t] = t < rows_of(c) ? fmaf(a.b_norm, sq, a.b_const) : -INFINITY;
     };
     if (nck > 0 && stager) {
         const bf16x8 k0 = load_block(kchunk(0), rows_of(0), tid);

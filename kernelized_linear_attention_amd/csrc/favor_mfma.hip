@@ -1144,8 +1144,9 @@ hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const v
 //   sum_f phi(q_t)_f (S dout_t)_f + sum_j A1[j][t] (v_j . dout_t): both are
 //   linear in the waves' parts over F_w, so only those scalars cross waves;
 // - w = dphi o phi leaves each wave as bfloat16 rows of a [token][feature]
-//   table; wave w then contracts the table with omega over all r features for
-//   one 16 x 16 tile of du^T (16x16x32 products), so no partial du crosses;
+//   table; waves 0..3 then contract the table with omega over all r features,
+//   two 16 x 16 tiles of du^T each (16x16x32 products), so no partial du
+//   crosses;
 // - the key pass sums the eight waves' parts of dv^T through LDS.
 // The query pass writes dnum_t = dout_t / D_t (in bfloat16, the operand the
 // products take) and dden_t; the segments' backward increments
@@ -1369,21 +1370,29 @@ __device__ __forceinline__ void put_w(u16* wq, int w, int lo, int h, const f32x1
             make_uint2(bf16pair(x[4 * m], x[4 * m + 1]), bf16pair(x[4 * m + 2], x[4 * m + 3]));
 }
 
-// Wave w's 16 x 16 tile of du^T = omega^T w^T over all r features: rows
-// d = 16 (w/2) + 4 (lane/16) + i, column t = 16 (w%2) + lane%16.
-__device__ __forceinline__ f32x4 du_tile(const CausalSmem& sm, int w, int lane) {
+// du^T = omega^T w^T over all r features, by waves 0..3: wave w < 4 forms the
+// two 16 x 16 tiles of rows d = 16 w + 4 (lane/16) + i and columns
+// t = 16 k + lane%16 (k = 0, 1) with 16x16x32 products, one omega^T operand
+// serving both.  (Waves 4..7, on the same SIMDs, have none: each SIMD still
+// runs sixteen of these products per chunk, from three quarters of the LDS
+// reads that one tile per wave would need.)
+__device__ __forceinline__ void du_tiles(const CausalSmem& sm, int w, int lane, f32x4 (&acc)[2]) {
     const int c = lane & 15, g = lane >> 4;
-    const u16* pa = sm.wt + (16 * (w >> 1) + c) * LDW + 8 * g;
-    const u16* pb = sm.wq + (16 * (w & 1) + c) * LDW + 8 * g;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const u16* pa = sm.wt + (16 * w + c) * LDW + 8 * g;
+    const u16* pb = sm.wq + c * LDW + 8 * g;
+    acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[1] = acc[0];
 #pragma unroll
-    for (int s = 0; s < R / 32; ++s) acc = mfma16(lds8(pa + 32 * s), lds8(pb + 32 * s), acc);
-    return acc;
+    for (int s = 0; s < R / 32; ++s) {
+        const bf16x8 af = lds8(pa + 32 * s);
+        acc[0] = mfma16(af, lds8(pb + 32 * s), acc[0]);
+        acc[1] = mfma16(af, lds8(pb + 16 * LDW + 32 * s), acc[1]);
+    }
 }
 
-// The lane's output position of du_tile in the chunk.
-__device__ __forceinline__ int du_token(int w, int lane) { return 16 * (w & 1) + (lane & 15); }
-__device__ __forceinline__ int du_col(int w, int lane) { return 16 * (w >> 1) + 4 * (lane >> 4); }
+// The lane's output positions in the chunk (wave w < 4, tile k).
+__device__ __forceinline__ int du_token(int k, int lane) { return 16 * k + (lane & 15); }
+__device__ __forceinline__ int du_col(int w, int lane) { return 16 * (w & 3) + 4 * (lane >> 4); }
 
 // Raw buffer resource over the first `rows` rows of width `width` (bf16)
 // at p: stores at byte offsets past the end are dropped by the hardware, so
@@ -1398,11 +1407,10 @@ __device__ __forceinline__ uint2 bf16x4_bits(const float (&o)[4]) {
     return make_uint2(bf16pair(o[0], o[1]), bf16pair(o[2], o[3]));
 }
 
-// dx[t][d .. d+3] = scale (du - wsum_t u), u = scale x, at the lane's
-// du_tile position (dropped past the chunk's rows).
+// dx[t][d .. d+3] = scale (du - wsum_t u), u = scale x, at token t and
+// columns d .. d+3 (dropped past the chunk's rows).
 __device__ __forceinline__ void store_dx(const CausalArgs& a, const CausalSmem& sm, u16* dxc,
-                                         int w, int lane, int rows, const f32x4& du, uint2 xe) {
-    const int t = du_token(w, lane);
+                                         int t, int d, int rows, const f32x4& du, uint2 xe) {
     float ws = 0.f;
 #pragma unroll
     for (int u = 0; u < NWC; ++u) ws += sm.wsum[u][t];
@@ -1410,7 +1418,18 @@ __device__ __forceinline__ void store_dx(const CausalArgs& a, const CausalSmem& 
     unpack4(xe, xv);
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = a.scale * (du[j] - ws * a.scale * xv[j]);
-    store_b64(chunk_rsrc(dxc, rows, D), 2 * (t * D + du_col(w, lane)), bf16x4_bits(o));
+    store_b64(chunk_rsrc(dxc, rows, D), 2 * (t * D + d), bf16x4_bits(o));
+}
+
+// dq or dk of the chunk from waves 0..3's du tiles (xe: q or k at the lane's
+// two positions).
+__device__ __forceinline__ void store_du(const CausalArgs& a, const CausalSmem& sm, u16* dxc,
+                                         int w, int lane, int rows, const uint2 (&xe)[2]) {
+    if (w >= 4) return; // uniform over the wave
+    f32x4 acc[2];
+    du_tiles(sm, w, lane, acc);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) store_dx(a, sm, dxc, du_token(k, lane), du_col(w, lane), rows, acc[k], xe[k]);
 }
 
 // omega^T in LDS, natural f order.
@@ -1479,7 +1498,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         bf16x8 qf[4], kf[4];
         lds_x(sm.xs[0], lo, h, qf);
         lds_x(sm.xs[1], lo, h, kf);
-        const uint2 xe = read_xs4(sm, 0, du_token(w, lane), du_col(w, lane));
+        const uint2 xe[2] = {read_xs4(sm, 0, du_token(0, lane), du_col(w, lane)),
+                             read_xs4(sm, 0, du_token(1, lane), du_col(w, lane))};
         // dout of token lo as the B operand of products over n (its raw
         // bf16 pieces), and this wave's piece of it for the dnum store
         Tile2 dt[2];
@@ -1617,7 +1637,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         wsum = half_sum(wsum);
         sm.wsum[w][lo] = wsum; // both halves: the same value
         sync_lds(); // B2: the w table, the sums of w and the next chunk's tables
-        store_dx(a, sm, a.dx + (bh * a.N + c0) * D, w, lane, rows, du_tile(sm, w, lane), xe);
+        store_du(a, sm, a.dx + (bh * a.N + c0) * D, w, lane, rows, xe);
 
         // state update: S^T[:, F_w] += V^T phi(K), z[F_w] += phi(K)^T 1
         const u16* vt = sm.vt[buf];
@@ -1691,7 +1711,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         bf16x8 qf[4], kf[4];
         lds_x(sm.xs[0], lo, h, qf);
         lds_x(sm.xs[1], lo, h, kf);
-        const uint2 xe = read_xs4(sm, 1, du_token(w, lane), du_col(w, lane));
+        const uint2 xe[2] = {read_xs4(sm, 1, du_token(0, lane), du_col(w, lane)),
+                             read_xs4(sm, 1, du_token(1, lane), du_col(w, lane))};
         // dnum^T [n x i] of the lane's query i = lo: its bfloat16 pieces are the
         // operands; and its transpose [i x n] as operands from the transposed table
         Tile2 dn[2], dnr[2];
@@ -1809,7 +1830,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         wsum = half_sum(wsum);
         sm.wsum[w][lo] = wsum; // both halves: the same value
         sync_lds(); // B2: the w table, the sums of w and the next chunk's tables
-        store_dx(a, sm, a.dx + (bh * a.N + c0) * D, w, lane, rows, du_tile(sm, w, lane), xe);
+        store_du(a, sm, a.dx + (bh * a.N + c0) * D, w, lane, rows, xe);
 
         // suffix update for the earlier chunks: G[F_w] += phi(Q)^T dnum, g += phi(Q)^T dden
 #pragma unroll

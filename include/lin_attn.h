@@ -338,7 +338,10 @@ int lin_attn_qkv_project(const void* x, const void* w_q, const void* w_k, const 
  *   sum normalisation when it is on.
  * omega is a constant ([PF] sec. 2: sampled once and frozen): no gradient.
  *   q, k, dq, dk [B, H, N, d]; v, dout, dv [B, H, N, dv]; all of the input
- *   dtype (float32 arithmetic inside).  dq, dk, dv are overwritten.
+ *   dtype.  States and sums are float32; bfloat16 FAVOR+ at r = 256 takes its
+ *   products on the matrix cores with bfloat16 operands (the feature maps,
+ *   dnum, w = dphi o phi, the states rounded once per product), every other
+ *   configuration computes in float32.  dq, dk, dv are overwritten.
  *   ws  at least lin_attn_workspace_bytes(LIN_ATTN_OP_BIDIR_BACKWARD or
  *       LIN_ATTN_OP_CAUSAL_BACKWARD, ...) bytes; contents on entry ignored.
  * Errors as lin_attn_bidir.

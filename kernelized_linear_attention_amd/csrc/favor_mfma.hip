@@ -96,14 +96,6 @@ __device__ __forceinline__ f32x16 zero16() {
     return r;
 }
 
-// Raw bits of element e of a bfloat16 vector (through 32-bit words: a bit
-// cast of a single __bf16 vector element does not lower reliably).
-__device__ __forceinline__ u16 bf16_bits(const bf16x8& v, int e) {
-    const u32x4 u = __builtin_bit_cast(u32x4, v);
-    const uint32_t word = u[e >> 1];
-    return (e & 1) ? (u16)(word >> 16) : (u16)(word & 0xffffu);
-}
-
 // Column order of the LDS tiles that feed MFMA operands.  An accumulator
 // element i of lane half h belongs to index 8(i/4) + 4h + i%4 within a
 // 16-block; the operand built from it holds, in k-slot e, index
@@ -1706,7 +1698,6 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         int64_t c0;
         int rows;
         chunk_at(cr, c0, rows);
-        const bool live = lo < rows;
         const int buf = cr & 1;
         bf16x8 qf[4], kf[4];
         lds_x(sm.xs[0], lo, h, qf);

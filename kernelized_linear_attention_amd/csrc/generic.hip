@@ -87,7 +87,7 @@ __global__ __launch_bounds__(NT) void k_segment_sums(Cfg c, const T* __restrict_
     }
     for (int64_t c0 = t0; c0 < t1; c0 += L) {
         const int rows = (int)min<int64_t>(L, t1 - c0);
-        if (PROJ) {
+        if constexpr (PROJ) {
             project_chunk<L>(P, bh, N, c0, rows, PROJ_K, u_s, c.scale, PROJ_V, v_s, 1.f);
         } else {
             load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, u_s);
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restri
     for (int64_t c0 = t0; c0 < t1; c0 += L) {
         const int rows = (int)min<int64_t>(L, t1 - c0);
         if (CAUSAL) {
-            if (PROJ) {
+            if constexpr (PROJ) {
                 project_chunk<L>(P, bh, N, c0, rows, PROJ_K, u_s, c.scale, PROJ_V, v_s, 1.f);
             } else {
                 load_rows<T, L>(k + (bh * N + c0) * D, rows, c.scale, u_s);
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(NT) void k_segment_outputs(Cfg c, const T* __restri
             __syncthreads();
             phi_tile<T, L>(c, u_s, nrm_s, omega, rows, pk_s, OL, rs_s);
         }
-        if (PROJ)
+        if constexpr (PROJ)
             project_chunk<L>(P, bh, N, c0, rows, PROJ_Q, u_s, c.scale, -1, nullptr, 0.f);
         else
             load_rows<T, L>(q + (bh * N + c0) * D, rows, c.scale, u_s);

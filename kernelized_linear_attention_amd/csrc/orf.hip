@@ -34,6 +34,7 @@ __global__ __launch_bounds__(NT) void k_orf(const float* __restrict__ gauss,
                                             const float* __restrict__ len_gauss, int64_t r, int d_,
                                             int64_t nblk, T* __restrict__ omega) {
     const int d = DC ? DC : d_;
+    constexpr int DCU = DC ? DC : 1; // the unroll count of the dot products
     __shared__ double e_s[DMAX * LD];
     __shared__ double c_s[DMAX];
     const int lane = threadIdx.x;
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(NT) void k_orf(const float* __restrict__ gauss,
             if (lane < i) { // c_j = e_j . e_i
                 const double* ej = e_s + lane * LD;
                 double c[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll(DC ? DC : 1)
+#pragma unroll DCU
                 for (int k = 0; k < d; ++k) c[k & 3] = fma(ej[k], ei[k], c[k & 3]);
                 c_s[lane] = (c[0] + c[1]) + (c[2] + c[3]);
             }

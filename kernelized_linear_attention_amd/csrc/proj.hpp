@@ -66,6 +66,7 @@ __device__ __forceinline__ void project_tile(const Proj& P, const bf16_raw* __re
 template <int L>
 __device__ void project_chunk(const Proj& P, int64_t bh, int64_t N, int64_t t0, int rows, int m0,
                               float* dst0, float s0, int m1, float* dst1, float s1) {
+    static_assert(L % 32 == 0 && L >= 32, "the projection deals whole 32-row tiles");
     constexpr int RB = L / 32;
     const int64_t b = bh / P.H, h = bh % P.H;
     const int nt = (m1 >= 0 ? 2 : 1) * RB * 2;

@@ -182,6 +182,40 @@ __device__ __forceinline__ uint2 quad_transpose4(uint2 x) {
     return make_uint2((pP >> 16) | (P & 0xffff0000u), (pQ >> 16) | (Q & 0xffff0000u));
 }
 
+// Row length (bf16) of a row-major [token][64] table read by tr_operand:
+// 192 bytes, so the four rows one 32-lane read touches (rows r .. r+3 at
+// 48-dword steps) tile the 64 banks.
+constexpr int LDR = 96;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// The operand of a product over 16 tokens with the 32 lanes of each half on
+// columns n0 .. n0+31 of a row-major [token][n] bf16 table (row length LDR),
+// k-slot e holding token 16 kk + 8(e/4) + 4h + e%4 (the order of the
+// operands made from accumulator tiles): two transposing LDS reads.  Within
+// each group of 16 lanes, ds_read_b64_tr_b16 gives lane 4a + b the b-th
+// 16-bit value of what lanes a, a+4, a+8, a+12 address, in that order; so
+// lane r of the group addresses token 16 kk + 4h + r/4 (8 further for the
+// second read) at columns n0 + 16 (group % 2) + 4 (r % 4).
+__device__ __forceinline__ bf16x8 tr_operand(const u16* tab, int n0, int kk, int lane) {
+    const int r = lane & 15, h = lane >> 5;
+    const u16* p = tab + (16 * kk + 4 * h + (r >> 2)) * LDR + n0 + 16 * ((lane >> 4) & 1) + 4 * (r & 3);
+    typedef i16x4 __attribute__((address_space(3))) * lds_i16x4;
+    const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p));
+    const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p + 8 * LDR));
+    const u32x4 w = {(uint32_t)(uint16_t)x0[0] | ((uint32_t)(uint16_t)x0[1] << 16),
+                     (uint32_t)(uint16_t)x0[2] | ((uint32_t)(uint16_t)x0[3] << 16),
+                     (uint32_t)(uint16_t)x1[0] | ((uint32_t)(uint16_t)x1[1] << 16),
+                     (uint32_t)(uint16_t)x1[2] | ((uint32_t)(uint16_t)x1[3] << 16)};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// V of the chunk for a row-major LDS copy: thread th (of 256) holds row
+// th / 8, columns 8 (th % 8) .. +7 (rows past `rows` repeat row rows-1).
+__device__ __forceinline__ bf16x8 load_vrow(const u16* __restrict__ V, int rows, int tid) {
+    return *reinterpret_cast<const bf16x8*>(V + (int64_t)min(tid >> 3, rows - 1) * DV + 8 * (tid & 7));
+}
+
 // Raw V rows of the chunk for the transposed LDS copy: thread th (of 256)
 // holds row 4 (th / 32) + th % 4, columns 8 ((th / 4) % 8) .. +7, so the four
 // lanes of a quad hold four consecutive rows of the same columns (rows past
@@ -659,7 +693,7 @@ constexpr int NT8 = 512;
 // plain one keeps its registers).
 template <bool ZW>
 __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
-    __shared__ __attribute__((aligned(16))) u16 vt_s[2][DV * LDV];
+    __shared__ __attribute__((aligned(16))) u16 vr_s[2][L * LDR]; // V, row-major [token][n]
     __shared__ bf16x8 ks_s[2][256];
     __shared__ __attribute__((aligned(16))) float kb_s[2][L]; // key biases by chunk parity
     __shared__ __attribute__((aligned(16))) float zw_s[ZW ? 2 : 1][L]; // z weights by chunk parity
@@ -720,7 +754,7 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
         const int c1 = min(1, nck - 1);
         kr = load_block(kchunk(c1), rows_of(c1), tid);
         load_zw(c1);
-        vr = load_v(vchunk(0), rows_of(0), tid);
+        vr = load_vrow(vchunk(0), rows_of(0), tid);
     }
     sync_lds(); // keys of chunk 0 staged
     wait_all_loads(); // omega's fragments, once, not in every iteration
@@ -734,10 +768,12 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
                 stage_bias(kr, ci + 1);
                 stage_zw(ci + 1);
             }
-            store_vt(vt_s[ci & 1], tid, vr);
+            // V of this chunk, row-major (rows past the end repeat the last
+            // row; they meet zero features)
+            *reinterpret_cast<bf16x8*>(&vr_s[ci & 1][(tid >> 3) * LDR + 8 * (tid & 7)]) = vr;
             kr = load_block(kchunk(c2), rows_of(c2), tid);
             load_zw(c2);
-            vr = load_v(vchunk(c1), rows_of(c1), tid);
+            vr = load_vrow(vchunk(c1), rows_of(c1), tid);
         }
         bf16x8 kf[4];
         lds_x(ks_s[ci & 1], lo, h, kf);
@@ -766,12 +802,11 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
             }
         }
         sync_lds(); // V^T of this chunk and the keys of the next staged
-        const u16* vt = vt_s[ci & 1];
+        const u16* vr = vr_s[ci & 1];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const int n = 32 * nt + lo;
-            S[nt] = mfma(fk0, lds8(vt + n * LDV + vt_col(n, 8 * h)), S[nt]);
-            S[nt] = mfma(fk1, lds8(vt + n * LDV + vt_col(n, 16 + 8 * h)), S[nt]);
+            S[nt] = mfma(fk0, tr_operand(vr, 32 * nt, 0, lane), S[nt]);
+            S[nt] = mfma(fk1, tr_operand(vr, 32 * nt, 1, lane), S[nt]);
         }
     }
     float* dst = a.state + bh * a.st_bh + g * a.st_g;

@@ -97,8 +97,9 @@ hipError_t segment_outputs(const lin_attn_params* p, const Cfg& c, int causal, c
                            const void* k, const void* v, const void* omega, Shape s, SegPlan sp,
                            const float* state, int64_t sbh, int64_t sg, void* out,
                            hipStream_t st) {
-    if (use_mfma(p))
-        return launch_favor_outputs(c, causal, q, k, v, omega, s, sp, state, sbh, sg, out, st);
+    if (use_mfma(p) && causal)
+        return launch_favor_outputs(c, q, k, v, omega, s, sp, state, sbh, sg, out, st);
+    if (use_mfma(p)) return launch_favor_readout(c, q, omega, s, state, sbh, out, st);
     if (f32mm_supported(c))
         return launch_f32mm_outputs(c, p->dtype, causal, q, k, v, s, sp, state, sbh, sg, out, st);
     return launch_segment_outputs(c, p->dtype, causal, q, k, v, omega, s, sp, state, sbh, sg, out,

@@ -12,6 +12,8 @@
 // partial numerators and denominators are summed through LDS; each wave
 // finishes a quarter of the chunk's output.
 // Segment increments (k_favor_sums8): eight waves of 32 features each.
+// Bidirectional readout (k_favor_readout): the summaries are fixed, so they
+// sit in LDS as operand tables and every wave takes whole chunks on its own.
 // Every contraction is a v_mfma_f32_32x32x16_bf16; the MFMA accumulator
 // layout of one product is reused as an operand of the next where the
 // contraction index allows it (a k-slot permutation applied to both
@@ -37,7 +39,6 @@ constexpr int R = 256;
 constexpr int L = 32;         // chunk length: one 32-token MFMA tile
 constexpr int LDV = 40;       // LDS row stride (bf16) of the V^T tile [64 n][32 t]: 80 B
 
-enum { MODE_CAUSAL = 1, MODE_READOUT = 2 };
 
 struct FavorArgs {
     const u16* q;
@@ -283,7 +284,7 @@ __device__ __forceinline__ bf16x8 eye_frag(int kk, int lo, int h) {
 }
 
 // ---------------------------------------------------------------------------
-// Outputs with symmetric waves: k_favor_fused<MODE> (MODE_CAUSAL, MODE_READOUT).
+// Causal outputs with symmetric waves: k_favor_fused<NORM>.
 //
 // One workgroup of four waves per (head, segment), two workgroups per CU, so
 // that each SIMD runs two independent waves (of different segments).  Wave w
@@ -373,10 +374,9 @@ __device__ __forceinline__ void finish_fused(const FavorArgs& a, SmemF& sm, cons
 
 // The whole segment for wave W (features F_W); every wave-dependent index is
 // a compile-time constant.
-template <int MODE, int NORM, int W>
+template <int NORM, int W>
 __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int tid, int64_t bh,
                                            int64_t g, int64_t t0, int64_t t1, int nck) {
-    constexpr bool CAUSAL = MODE == MODE_CAUSAL;
     constexpr int f0 = 64 * W;
     const int lane = tid & 63, lo = lane & 31, h = lane >> 5;
     auto rows_of = [&](int c) { return (int)min<int64_t>(L, t1 - t0 - (int64_t)L * c); };
@@ -387,7 +387,7 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) om[t][ks] = omega_frag(a.omega, f0, t, ks, lo, h);
 
-    // carried-in state (causal) or the summaries (readout)
+    // carried-in state
     const float* st = a.state + bh * a.st_bh + g * a.st_g;
     f32x16 S[2][2];
 #pragma unroll
@@ -399,17 +399,6 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
                 const int f = f0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
                 S[mt][nt][i] = st[(int64_t)f * DV + 32 * nt + lo];
             }
-    // readout: the summaries never change, so their bf16 operands are packed
-    // once (the float32 copy is then dead)
-    bf16x8 Sp[2][2][2];
-    if (!CAUSAL) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) Sp[mt][nt][kk] = pack8(S[mt][nt], 8 * kk);
-    }
     float zreg[2]; // z[f0 + 32 nt + lo]
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) zreg[nt] = st[(int64_t)R * DV + f0 + 32 * nt + lo];
@@ -418,7 +407,7 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
     sm.z[f0 + 32 + lo] = zreg[1];
     // identity operands of the transposition (read back once per chunk: kept
     // in LDS rather than in eight registers)
-    if (CAUSAL && W < 2) sm.eye[W][lane] = eye_frag(W, lo, h);
+    if (W < 2) sm.eye[W][lane] = eye_frag(W, lo, h);
     // causal mask of the diagonal tile: element i of lane (lo, h) pairs query
     // lo with key 8(i/4) + 4h + i%4, kept when 8(i/4) + i%4 <= lo - 4h
     const int keep_thr = lo - 4 * h;
@@ -431,10 +420,8 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
     bf16x8 qr, kr, vr;
     auto stage_load = [&](int c) {
         qr = load_block(chunk_ptr(qg, c, D), rows_of(c), tid);
-        if (CAUSAL) {
-            kr = load_block(chunk_ptr(kg, c, D), rows_of(c), tid);
-            vr = load_v(chunk_ptr(vg, c, DV), rows_of(c), tid);
-        }
+        kr = load_block(chunk_ptr(kg, c, D), rows_of(c), tid);
+        vr = load_v(chunk_ptr(vg, c, DV), rows_of(c), tid);
     };
     // the per-token biases of a chunk, once per workgroup: the eight threads
     // of a row sum their squares; keys past the segment end get -inf (exp2
@@ -455,12 +442,10 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
         // a write by one of them only would become a branch)
         const float sq = row_sq(qr);
         sm.qb[s][t] = fmaf(a.b_norm, sq, a.b_const);
-        if (CAUSAL) {
-            sm.xk[s][tid] = kr;
-            const float sk = row_sq(kr);
-            sm.kb[s][t] = t < rows_of(c) ? fmaf(a.b_norm, sk, a.b_const) : -INFINITY;
-            store_vt(sm.vt[s], tid, vr);
-        }
+        sm.xk[s][tid] = kr;
+        const float sk = row_sq(kr);
+        sm.kb[s][t] = t < rows_of(c) ? fmaf(a.b_norm, sk, a.b_const) : -INFINITY;
+        store_vt(sm.vt[s], tid, vr);
     };
 
     // projections of one 32 x 32 tile from the chunk's fragments
@@ -477,19 +462,14 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
         for (int ks = 0; ks < 4; ++ks) c = mfma(om[t][ks], qf[ks], c);
         return c;
     };
-    // P0, P1: the first two projection tiles of the chunk about to be
-    // processed (keys when causal, else queries), issued one iteration early
+    // P0, P1: the first two (key) projection tiles of the chunk about to be
+    // processed, issued one iteration early
     f32x16 P0, P1;
     auto first_tiles = [&](int s) {
         lds_x(sm.xq[s], lo, h, qf);
-        if (CAUSAL) {
-            lds_x(sm.xk[s], lo, h, kf);
-            P0 = project_k(0);
-            P1 = project_k(1);
-        } else {
-            P0 = project_q(0);
-            P1 = project_q(1);
-        }
+        lds_x(sm.xk[s], lo, h, kf);
+        P0 = project_k(0);
+        P1 = project_k(1);
     };
 
     if (nck > 0) {
@@ -547,24 +527,20 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
             fq[mt][0] = pack8(c, 0);
             fq[mt][1] = pack8(c, 8);
         };
-        if (CAUSAL) {
-            key_tile(P0, 0);
-            P0 = project_q(0);
-            key_tile(P1, 1);
-            P1 = project_q(1);
-        }
+        key_tile(P0, 0);
+        P0 = project_q(0);
+        key_tile(P1, 1);
+        P1 = project_q(1);
         query_tile(P0, 0);
         query_tile(P1, 1);
         float den = NORM == NORM_ATTN ? half_sum(dacc[0] + dacc[1]) : 0.f; // token lo, both halves
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- z[F_W] += column sums of phi(K_c), after the queries read z_{c-1} ----
-        if (CAUSAL) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                zreg[nt] += half_sum(zpart[nt]);
-                sm.z[f0 + 32 * nt + lo] = zreg[nt]; // both halves: same value
-            }
+        for (int nt = 0; nt < 2; ++nt) {
+            zreg[nt] += half_sum(zpart[nt]);
+            sm.z[f0 + 32 * nt + lo] = zreg[nt]; // both halves: same value
         }
 
         const u16* vt = sm.vt[slot];
@@ -576,7 +552,7 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
 
         // ---- masked intra-chunk block over F_W --------------------------------------
         bf16x8 at[2];
-        if (CAUSAL) {
+        {
             // phi(K) with tokens on lanes: lane (j, h), k-slot e <-> feature
             // f0 + 32 mt + 16 kk + 8(e/4) + 4h + e%4, as in fq
             bf16x8 kt[2][2];
@@ -618,9 +594,9 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    acc[nt] = mfma(CAUSAL ? pack8(S[mt][nt], 8 * kk) : Sp[mt][nt][kk], fq[mt][kk], acc[nt]);
+                    acc[nt] = mfma(pack8(S[mt][nt], 8 * kk), fq[mt][kk], acc[nt]);
         }
-        if (CAUSAL) {
+        {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -662,7 +638,7 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
     if (nck > 0) finish_fused<W, NORM>(a, sm, acc, lane, (nck - 1) & 1, bh, t0 + (int64_t)L * (nck - 1), rows_of(nck - 1));
 }
 
-template <int MODE, int NORM>
+template <int NORM>
 __global__ __launch_bounds__(NTF, 2) void k_favor_fused(FavorArgs a) {
     __shared__ SmemF sm;
     const int tid = threadIdx.x;
@@ -673,10 +649,10 @@ __global__ __launch_bounds__(NTF, 2) void k_favor_fused(FavorArgs a) {
     seg_range(a.tab, a.tsub, g, a.seg_len, a.N, t0, t1);
     const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
     switch (w) {
-    case 0: fused_wave<MODE, NORM, 0>(a, sm, tid, bh, g, t0, t1, nck); break;
-    case 1: fused_wave<MODE, NORM, 1>(a, sm, tid, bh, g, t0, t1, nck); break;
-    case 2: fused_wave<MODE, NORM, 2>(a, sm, tid, bh, g, t0, t1, nck); break;
-    default: fused_wave<MODE, NORM, 3>(a, sm, tid, bh, g, t0, t1, nck); break;
+    case 0: fused_wave<NORM, 0>(a, sm, tid, bh, g, t0, t1, nck); break;
+    case 1: fused_wave<NORM, 1>(a, sm, tid, bh, g, t0, t1, nck); break;
+    case 2: fused_wave<NORM, 2>(a, sm, tid, bh, g, t0, t1, nck); break;
+    default: fused_wave<NORM, 3>(a, sm, tid, bh, g, t0, t1, nck); break;
     }
 }
 
@@ -1107,6 +1083,210 @@ __global__ __launch_bounds__(NTB) void k_bwd_key_favor(BwdArgs a) {
                 }
         }
         store_dx(a, xr, a.dx + (bh * a.N + c0) * D, du, wsum, lo, h, rows);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Bidirectional readout with every wave on its own chunks: k_favor_readout.
+// The summaries S, z do not change along the sequence ("Reassociate a
+// feature-map kernel...", par. 1 and 3: form them once, then read them for
+// every query), so a workgroup of eight waves (one head, one block of its
+// tokens) first puts them in LDS: S^T as a bf16 operand table (the rounding
+// every bf16 product here uses) and z in float32, with omega in the swizzled
+// row layout of the staged chunks.  Then each wave takes whole 32-token
+// chunks of the block, and per 32-feature tile forms phi(Q)^T = exp2(omega
+// Q^T a + b_t) (Kernel Zoo sec. 4.2 / 5.4 map; the token's bias b_t is per
+// lane, as tokens are), adds the tile's part of the denominator phi(q).z and
+// num^T += S^T phi(Q)^T on the matrix core; then out = num / max(den, eps).
+// Nothing crosses waves inside the loop, so it has no barrier, and each
+// chunk's loads are issued one chunk ahead.
+// ---------------------------------------------------------------------------
+constexpr int NTR = 512;
+constexpr int NWR = NTR / 64;
+constexpr int64_t READOUT_BLOCKS = 256;
+
+struct ReadoutArgs {
+    const u16* q;
+    const u16* omega;
+    const float* total;  // (S | z) per head: float32 [R][DV] then [R]
+    int64_t st_bh;       // floats between heads' totals
+    int64_t N;
+    int64_t BH;
+    int64_t blk_len;     // tokens per workgroup (a multiple of 32)
+    float a_scale, b_norm, b_const, eps;
+    int norm;
+    u16* out;
+};
+
+struct ReadoutSmem {
+    u16 mt[DV * LDF];   // S^T [n][f'], f in swap23 order within each 16-block
+    bf16x8 om[R * 8];   // omega rows, 16-byte block j of row f at xs_index(f, j)
+    u16 zb[R];          // z in bf16, by feature
+};
+
+template <int NORM>
+__global__ __launch_bounds__(NTR, 2) void k_favor_readout(ReadoutArgs a) {
+    __shared__ ReadoutSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
+    const int lo = lane & 31, h = lane >> 5;
+    // the workgroups of one head are BH apart in the grid: with BH a
+    // multiple of 8 they run on one XCD and share its L2 copy of the total
+    const int64_t bh = blockIdx.x % a.BH, blk = blockIdx.x / a.BH;
+    const float* tot = a.total + bh * a.st_bh;
+    const int64_t t0 = blk * a.blk_len;
+    const int64_t t1 = min<int64_t>(t0 + a.blk_len, a.N);
+    const int nck = t1 > t0 ? (int)((t1 - t0 + L - 1) / L) : 0;
+    auto rows_of = [&](int ci) { return (int)min<int64_t>(L, t1 - t0 - (int64_t)L * ci); };
+    auto qrow = [&](int ci) { return a.q + (bh * a.N + t0 + (int64_t)L * ci) * D; };
+    // the wave's first queries, then every load of the tables (one round
+    // trip for all of them), then the LDS writes
+    bf16x8 xn[4];
+    if (wv < nck) load_x(qrow(wv), rows_of(wv), lo, h, xn);
+    // S^T: thread (n, q) forms the 16-byte words of row n at positions
+    // 8 q' .. 8 q' + 7 of the swap23-ordered features, q' = q + 8 u: the
+    // features 16 (q' / 2) + swap23(8 (q' % 2) + e); each load instruction
+    // reads 64 consecutive floats of one row of S
+    constexpr int NU = R / 8 / (NTR / DV);
+    const int n = tid & (DV - 1), q = tid / DV;
+    float sv[NU][8];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int qq = q + (NTR / DV) * u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[u][e] = tot[(16 * (qq >> 1) + swap23(8 * (qq & 1) + e)) * DV + n];
+    }
+    constexpr int NO = R * 8 / NTR;
+    bf16x8 ov[NO];
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+        const int b = tid + NTR * u;
+        ov[u] = *reinterpret_cast<const bf16x8*>(a.omega + (int64_t)(b >> 3) * D + 8 * (b & 7));
+    }
+    const f32x4 zv = *reinterpret_cast<const f32x4*>(tot + R * DV + 4 * (tid & (R / 4 - 1)));
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (__bf16)sv[u][e];
+        *reinterpret_cast<bf16x8*>(&sm.mt[n * LDF + 8 * (q + (NTR / DV) * u)]) = w;
+    }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+        const int b = tid + NTR * u;
+        sm.om[xs_index(b >> 3, b & 7)] = ov[u];
+    }
+    if (NORM == NORM_ATTN && tid < R / 4) {
+        const bf16x2 z01 = {(__bf16)zv[0], (__bf16)zv[1]}, z23 = {(__bf16)zv[2], (__bf16)zv[3]};
+        *reinterpret_cast<uint2*>(&sm.zb[4 * tid]) =
+            make_uint2(__builtin_bit_cast(uint32_t, z01), __builtin_bit_cast(uint32_t, z23));
+    }
+    __syncthreads();
+
+    for (int ci = wv; ci < nck; ci += NWR) {
+        const int rows = rows_of(ci);
+        bf16x8 xf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) xf[ks] = xn[ks];
+        // the next chunk's queries (this chunk again past the end, so every
+        // iteration issues the same loads)
+        const int cnx = ci + NWR < nck ? ci + NWR : ci;
+        load_x(qrow(cnx), rows_of(cnx), lo, h, xn);
+        const float bias = fmaf(a.b_norm, sq_norm(xf), a.b_const);
+        f32x16 num[2] = {zero16(), zero16()};
+        float den = 0.f;
+        // LDS operands, read one feature tile ahead of their use: omega rows
+        // 32 b .. +31 (A operand of the projection), S^T for the tile (A
+        // operand of num^T, columns 32 nt + lo) and z (bf16 pairs)
+        auto read_om = [&](int b, bf16x8 (&o)[4]) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) o[ks] = sm.om[xs_index(32 * b + lo, 2 * ks + h)];
+        };
+        auto read_mt = [&](int b, bf16x8 (&o)[4]) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) o[2 * nt + s2] = lds8(sm.mt + (32 * nt + lo) * LDF + 32 * b + 16 * s2 + 8 * h);
+        };
+        auto read_z = [&](int b, uint2 (&o)[4]) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = *reinterpret_cast<const uint2*>(&sm.zb[32 * b + 8 * j + 4 * h]);
+        };
+        auto project = [&](const bf16x8 (&o)[4]) {
+            f32x16 c = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) c = mfma(o[ks], xf[ks], c);
+            return c;
+        };
+        // software pipeline over the 8 feature tiles: region b exponentiates
+        // tile b, projects tile b + 1 on the matrix core and adds tile b to
+        // num; the LDS reads for the next region are issued at the end of
+        // this one (a scheduling barrier ends each region, so they are not
+        // moved next to their uses)
+        bf16x8 om_n[4], mt_n[4];
+        uint2 zb_n[4];
+        read_om(0, om_n);
+        f32x16 cn = project(om_n);
+        read_om(1, om_n);
+        read_mt(0, mt_n);
+        if (NORM == NORM_ATTN) read_z(0, zb_n);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < R / 32; ++b) {
+            f32x16 c = cn;
+            bf16x8 mt_c[4];
+            uint2 zb_c[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mt_c[j] = mt_n[j];
+                zb_c[j] = zb_n[j];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bias));
+            if (b + 1 < R / 32) cn = project(om_n);
+            const bf16x8 p0 = pack8(c, 0), p1 = pack8(c, 8);
+            if (NORM == NORM_ATTN) {
+                // phi . z over the tile's features, in the bf16 roundings the
+                // numerator's products use (S^T and phi are bf16 there): word
+                // m of p0 / p1 holds the features 32 b + 8 (m / 2) + 4 h +
+                // 2 (m % 2) + (0, 1) (+16 for p1), as does zb's word there
+                const u32x4 w0 = __builtin_bit_cast(u32x4, p0), w1 = __builtin_bit_cast(u32x4, p1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t x0 = j < 2 ? w0[2 * j] : w1[2 * j - 4];
+                    const uint32_t x1 = j < 2 ? w0[2 * j + 1] : w1[2 * j - 3];
+                    den = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x0),
+                                                          __builtin_bit_cast(bf16x2, zb_c[j].x), den, false);
+                    den = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x1),
+                                                          __builtin_bit_cast(bf16x2, zb_c[j].y), den, false);
+                }
+            }
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                num[nt] = mfma(mt_c[2 * nt], p0, num[nt]);
+                num[nt] = mfma(mt_c[2 * nt + 1], p1, num[nt]);
+            }
+            if (b + 2 < R / 32) read_om(b + 2, om_n);
+            if (b + 1 < R / 32) {
+                read_mt(b + 1, mt_n);
+                if (NORM == NORM_ATTN) read_z(b + 1, zb_n);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float inv = 1.f;
+        if (NORM == NORM_ATTN) inv = __builtin_amdgcn_rcpf(fmaxf(half_sum(den), a.eps));
+        // token lo, columns 32 nt + 8 m + 4 h + (0..3); rows past the block's
+        // end are dropped by the buffer resource's range
+        const __amdgpu_buffer_rsrc_t orsrc = out_rows(a.out, bh * a.N + t0 + (int64_t)L * ci, rows);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const bf16x2 p0 = {(__bf16)(num[nt][4 * m] * inv), (__bf16)(num[nt][4 * m + 1] * inv)};
+                const bf16x2 p1 = {(__bf16)(num[nt][4 * m + 2] * inv), (__bf16)(num[nt][4 * m + 3] * inv)};
+                const u32x2 v2 = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+                __builtin_amdgcn_raw_buffer_store_b64(v2, orsrc, lo * (DV * 2) + 2 * (32 * nt + 8 * m + 4 * h), 0, 0);
+            }
     }
 }
 
@@ -1959,20 +2139,44 @@ hipError_t launch_favor_causal_bwd_key(const Cfg& c, const void* q, const void* 
     return hipGetLastError();
 }
 
-hipError_t launch_favor_outputs(const Cfg& c, int causal, const void* q, const void* k,
-                                const void* v, const void* omega, Shape s, SegPlan sp,
-                                const float* state, int64_t sbh, int64_t sg, void* out,
-                                hipStream_t st) {
+hipError_t launch_favor_readout(const Cfg& c, const void* q, const void* omega, Shape s,
+                                const float* total, int64_t st_bh, void* out, hipStream_t st) {
+    ReadoutArgs a;
+    a.q = (const u16*)q;
+    a.omega = (const u16*)omega;
+    a.total = total;
+    a.st_bh = st_bh;
+    a.N = s.N;
+    a.BH = s.BH;
+    a.a_scale = c.scale * LOG2E;
+    a.b_norm = -0.5f * c.scale * c.scale * LOG2E;
+    a.b_const = c.favor_log2_bias;
+    a.eps = c.eps;
+    a.norm = c.norm;
+    a.out = (u16*)out;
+    // blocks of whole chunks, about one workgroup per CU (two do not fit
+    // beside each other's registers)
+    const int64_t nblk0 = (READOUT_BLOCKS + s.BH - 1) / s.BH;
+    const int64_t chunks = (s.N + L - 1) / L;
+    a.blk_len = L * ((chunks + nblk0 - 1) / nblk0);
+    const int64_t nblk = (s.N + a.blk_len - 1) / a.blk_len;
+    const dim3 grid((unsigned)(nblk * s.BH));
+    if (c.norm == NORM_ATTN)
+        hipLaunchKernelGGL(k_favor_readout<NORM_ATTN>, grid, dim3(NTR), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_favor_readout<NORM_NONE>, grid, dim3(NTR), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_favor_outputs(const Cfg& c, const void* q, const void* k, const void* v,
+                                const void* omega, Shape s, SegPlan sp, const float* state,
+                                int64_t sbh, int64_t sg, void* out, hipStream_t st) {
     const FavorArgs a = make_args(c, q, k, v, omega, s, sp, const_cast<float*>(state), sbh, sg, out);
     const dim3 grid((unsigned)(sp.G * s.BH));
-    if (causal && c.norm == NORM_ATTN)
-        hipLaunchKernelGGL((k_favor_fused<MODE_CAUSAL, NORM_ATTN>), grid, dim3(NTF), 0, st, a);
-    else if (causal)
-        hipLaunchKernelGGL((k_favor_fused<MODE_CAUSAL, NORM_NONE>), grid, dim3(NTF), 0, st, a);
-    else if (c.norm == NORM_ATTN)
-        hipLaunchKernelGGL((k_favor_fused<MODE_READOUT, NORM_ATTN>), grid, dim3(NTF), 0, st, a);
+    if (c.norm == NORM_ATTN)
+        hipLaunchKernelGGL(k_favor_fused<NORM_ATTN>, grid, dim3(NTF), 0, st, a);
     else
-        hipLaunchKernelGGL((k_favor_fused<MODE_READOUT, NORM_NONE>), grid, dim3(NTF), 0, st, a);
+        hipLaunchKernelGGL(k_favor_fused<NORM_NONE>, grid, dim3(NTF), 0, st, a);
     return hipGetLastError();
 }
 

@@ -177,10 +177,13 @@ hipError_t launch_f32mm_outputs(const Cfg& c, int dtype, int causal, const void*
 hipError_t launch_favor_sums(const Cfg& c, const void* k, const void* v, const void* omega,
                              Shape s, SegPlan sp, float* ws, hipStream_t st,
                              const float* zw = nullptr);
-hipError_t launch_favor_outputs(const Cfg& c, int causal, const void* q, const void* k,
-                                const void* v, const void* omega, Shape s, SegPlan sp,
-                                const float* state, int64_t sbh, int64_t sg, void* out,
-                                hipStream_t st);
+// Bidirectional readout from the per-head totals (S | z) at total + bh * st_bh.
+hipError_t launch_favor_readout(const Cfg& c, const void* q, const void* omega, Shape s,
+                                const float* total, int64_t st_bh, void* out, hipStream_t st);
+// Causal outputs of every segment from its carried-in state.
+hipError_t launch_favor_outputs(const Cfg& c, const void* q, const void* k, const void* v,
+                                const void* omega, Shape s, SegPlan sp, const float* state,
+                                int64_t sbh, int64_t sg, void* out, hipStream_t st);
 
 // Backward of the bidirectional form on the matrix cores (FAVOR+, bfloat16,
 // r = 256): total = the head's (S | z) for the query pass, (G | g) for the key

@@ -21,6 +21,8 @@
 // too: the bidirectional one with every wave on its own chunks against the
 // totals, the causal one with each workgroup walking its segment and the
 // state split over its waves by feature (see the comments at those kernels).
+#include <atomic>
+
 #include "launch.hpp"
 
 namespace linattn {
@@ -63,6 +65,7 @@ struct FavorArgs {
     int64_t osub;
     int64_t BH;
     const float* zw;      // k_favor_sums8: per-token weights of the z sum [BH, N], or NULL (weight 1)
+    int64_t cus;          // compute units of the device (workgroups per dispatch round)
 };
 
 // The (head, segment) this workgroup runs; false when it runs nothing.
@@ -77,6 +80,20 @@ __device__ __forceinline__ bool block_segment(const FavorArgs& a, int64_t& bh, i
     const int64_t seg = a.order[s / a.osub];
     g = seg * a.osub + s % a.osub;
     return seg >= 0 && g < a.G;
+}
+
+// Two workgroups share each CU in the causal outputs kernel, and the
+// hardware issues from the older one's waves first: left alone, the
+// workgroup dispatched second trails by about a third (82 against 109 us at
+// B=1, H=8, N=65536) and ends alone on its CU.  The two dispatch rounds
+// instead take priority in turn, in slots of 1024 ticks (about 10 us) of the
+// constant-rate clock, which keeps them level.  `now` is read before a
+// barrier whose wait also covers it.
+__device__ __forceinline__ void take_turns(uint64_t now, int round) {
+    if ((((now >> 10) + (uint64_t)round) & 1) != 0)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -122,7 +139,9 @@ __device__ __forceinline__ void load_x(const u16* __restrict__ X, int rows, int 
         f[ks] = *reinterpret_cast<const bf16x8*>(X + (int64_t)t * D + 16 * ks + 8 * h);
 }
 
-// Sum of the eight bfloat16 elements, two per v_dot2 against (1, 1).
+// Sum of the eight bfloat16 elements, two per v_dot2 against (1, 1).  The
+// pairs are built from the elements: a bit cast of the vector to 32-bit
+// words was lowered to the same register for different words.
 __device__ __forceinline__ float sum8(const bf16x8& v) {
     const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
     float s0 = 0.f, s1 = 0.f;
@@ -131,6 +150,21 @@ __device__ __forceinline__ float sum8(const bf16x8& v) {
     s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[4], v[5]}, one, s0, false);
     s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[6], v[7]}, one, s1, false);
     return s0 + s1;
+}
+
+// phi . z over the 16 features of a projection tile held as (p0, p1): word m
+// of p0 / p1 (elements 2m, 2m + 1) holds the features 8 (m / 2) + 4 h +
+// 2 (m % 2) + (0, 1) of the tile (+16 for p1), and zq[j] the bf16 z of the
+// features 8 j + 4 h + (0..3); two dot2 chains.
+__device__ __forceinline__ void dot_z(const bf16x8& p0, const bf16x8& p1, const uint2 (&zq)[4],
+                                      float& d0, float& d1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bf16x8& p = j < 2 ? p0 : p1;
+        const int e = 4 * (j & 1);
+        d0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[e], p[e + 1]}, __builtin_bit_cast(bf16x2, zq[j].x), d0, false);
+        d1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[e + 2], p[e + 3]}, __builtin_bit_cast(bf16x2, zq[j].y), d1, false);
+    }
 }
 
 // x[lane] + x[lane ^ 32]: the two lane halves exchanged by one
@@ -324,7 +358,7 @@ struct SmemF {
     float dpart[2][L][NW];              // partial denominators [parity][token][group]
     float qb[2][L];                     // query biases by token
     float kb[2][L];                     // key biases by token (-inf past the segment end)
-    float z[R];                         // z_{c-1} by feature (wave w reads and writes F_w only)
+    u16 zb[R];                          // z_{c-1} by feature in bf16 (wave w reads and writes F_w only)
     bf16x8 eye[2][64];                  // identity operands of the transposition, by lane
 };
 
@@ -403,8 +437,8 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) zreg[nt] = st[(int64_t)R * DV + f0 + 32 * nt + lo];
     // both lane halves store the same value at the same address
-    sm.z[f0 + lo] = zreg[0];
-    sm.z[f0 + 32 + lo] = zreg[1];
+    sm.zb[f0 + lo] = __builtin_bit_cast(u16, (__bf16)zreg[0]);
+    sm.zb[f0 + 32 + lo] = __builtin_bit_cast(u16, (__bf16)zreg[1]);
     // identity operands of the transposition (read back once per chunk: kept
     // in LDS rather than in eight registers)
     if (W < 2) sm.eye[W][lane] = eye_frag(W, lo, h);
@@ -513,19 +547,23 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
             fk[nt][1] = pack8(c, 8);
             zpart[nt] = sum8(fk[nt][0]) + sum8(fk[nt][1]);
         };
-        // phi(Q) tile mt and its denominators against z_{c-1}
+        // phi(Q) tile mt and its denominators against z_{c-1}: phi . z in the
+        // bf16 roundings the numerator's products use (phi and S are bf16
+        // there); word m of fq[mt][0] / [1] holds the features
+        // f0 + 32 mt + 8 (m / 2) + 4 h + 2 (m % 2) + (0, 1) (+16 for [1]), as
+        // does the bf16 z word read at the same features
         auto query_tile = [&](f32x16& c, int mt) {
-            f32x4 zq[4]; // z_{c-1} of the features f0 + 32 mt + 8 j + 4 h + (0..3)
+            // z_{c-1} of the features f0 + 32 mt + 8 j + 4 h + (0..3); read by
+            // memcpy, as the writes are 16-bit: a typed 8-byte load would be
+            // assumed not to alias them and could move past the update below
+            uint2 zq[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) zq[j] = *reinterpret_cast<const f32x4*>(&sm.z[f0 + 32 * mt + 8 * j + 4 * h]);
+            for (int j = 0; j < 4; ++j) __builtin_memcpy(&zq[j], &sm.zb[f0 + 32 * mt + 8 * j + 4 * h], sizeof(uint2));
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float y = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
-                c[i] = y;
-                if (NORM == NORM_ATTN) dacc[i & 1] = fmaf(y, zq[i >> 2][i & 3], dacc[i & 1]);
-            }
+            for (int i = 0; i < 16; ++i) c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bq));
             fq[mt][0] = pack8(c, 0);
             fq[mt][1] = pack8(c, 8);
+            if (NORM == NORM_ATTN) dot_z(fq[mt][0], fq[mt][1], zq, dacc[0], dacc[1]);
         };
         key_tile(P0, 0);
         P0 = project_q(0);
@@ -540,7 +578,7 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             zreg[nt] += half_sum(zpart[nt]);
-            sm.z[f0 + 32 * nt + lo] = zreg[nt]; // both halves: same value
+            sm.zb[f0 + 32 * nt + lo] = __builtin_bit_cast(u16, (__bf16)zreg[nt]); // both halves: same value
         }
 
         const u16* vt = sm.vt[slot];
@@ -571,15 +609,17 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) m = mfma(kt[mt][kk], fq[mt][kk], m);
-            float rs[2] = {0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 m[i] = 8 * (i >> 2) + (i & 3) <= keep_thr ? m[i] : 0.f;
-                rs[i & 1] += m[i];
+                // kept as a float32 select (otherwise the compiler converts
+                // each element alone and masks and repacks the halves)
+                asm volatile("" : "+v"(m[i]));
             }
-            if (NORM == NORM_ATTN) den += half_sum(rs[0] + rs[1]);
             at[0] = pack8(m, 0);
             at[1] = pack8(m, 8);
+            // the block's row sums from the bf16 values its product with V uses
+            if (NORM == NORM_ATTN) den += half_sum(sum8(at[0]) + sum8(at[1]));
         }
         __builtin_amdgcn_sched_barrier(0);
 
@@ -630,7 +670,9 @@ __device__ __forceinline__ void fused_wave(const FavorArgs& a, SmemF& sm, int ti
                     }
                 }
         }
+        const uint64_t now = __builtin_amdgcn_s_memrealtime();
         sync_lds(); // partials of chunk ci in LDS; chunk ci + 1 staged
+        take_turns(now, (int)(blockIdx.x / a.cus));
 
         // the next chunk's first projections run on the matrix core while this
         // chunk's output is finished
@@ -1194,7 +1236,7 @@ __global__ __launch_bounds__(NTR, 2) void k_favor_readout(ReadoutArgs a) {
         load_x(qrow(cnx), rows_of(cnx), lo, h, xn);
         const float bias = fmaf(a.b_norm, sq_norm(xf), a.b_const);
         f32x16 num[2] = {zero16(), zero16()};
-        float den = 0.f;
+        float den = 0.f, den2 = 0.f;
         // LDS operands, read one feature tile ahead of their use: omega rows
         // 32 b .. +31 (A operand of the projection), S^T for the tile (A
         // operand of num^T, columns 32 nt + lo) and z (bf16 pairs)
@@ -1245,22 +1287,9 @@ __global__ __launch_bounds__(NTR, 2) void k_favor_readout(ReadoutArgs a) {
             for (int i = 0; i < 16; ++i) c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bias));
             if (b + 1 < R / 32) cn = project(om_n);
             const bf16x8 p0 = pack8(c, 0), p1 = pack8(c, 8);
-            if (NORM == NORM_ATTN) {
-                // phi . z over the tile's features, in the bf16 roundings the
-                // numerator's products use (S^T and phi are bf16 there): word
-                // m of p0 / p1 holds the features 32 b + 8 (m / 2) + 4 h +
-                // 2 (m % 2) + (0, 1) (+16 for p1), as does zb's word there
-                const u32x4 w0 = __builtin_bit_cast(u32x4, p0), w1 = __builtin_bit_cast(u32x4, p1);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t x0 = j < 2 ? w0[2 * j] : w1[2 * j - 4];
-                    const uint32_t x1 = j < 2 ? w0[2 * j + 1] : w1[2 * j - 3];
-                    den = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x0),
-                                                          __builtin_bit_cast(bf16x2, zb_c[j].x), den, false);
-                    den = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x1),
-                                                          __builtin_bit_cast(bf16x2, zb_c[j].y), den, false);
-                }
-            }
+            // phi . z over the tile's features, in the bf16 roundings the
+            // numerator's products use (S^T and phi are bf16 there)
+            if (NORM == NORM_ATTN) dot_z(p0, p1, zb_c, den, den2);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 num[nt] = mfma(mt_c[2 * nt], p0, num[nt]);
@@ -1274,7 +1303,7 @@ __global__ __launch_bounds__(NTR, 2) void k_favor_readout(ReadoutArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         float inv = 1.f;
-        if (NORM == NORM_ATTN) inv = __builtin_amdgcn_rcpf(fmaxf(half_sum(den), a.eps));
+        if (NORM == NORM_ATTN) inv = __builtin_amdgcn_rcpf(fmaxf(half_sum(den + den2), a.eps));
         // token lo, columns 32 nt + 8 m + 4 h + (0..3); rows past the block's
         // end are dropped by the buffer resource's range
         const __amdgpu_buffer_rsrc_t orsrc = out_rows(a.out, bh * a.N + t0 + (int64_t)L * ci, rows);
@@ -1288,6 +1317,19 @@ __global__ __launch_bounds__(NTR, 2) void k_favor_readout(ReadoutArgs a) {
                 __builtin_amdgcn_raw_buffer_store_b64(v2, orsrc, lo * (DV * 2) + 2 * (32 * nt + 8 * m + 4 * h), 0, 0);
             }
     }
+}
+
+// Compute units of the current device (cached per device; 256 if unknown).
+int64_t device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 FavorArgs make_args(const Cfg& c, const void* q, const void* k, const void* v, const void* omega,
@@ -1315,6 +1357,7 @@ FavorArgs make_args(const Cfg& c, const void* q, const void* k, const void* v, c
     a.osub = sp.osub;
     a.BH = s.BH;
     a.zw = nullptr;
+    a.cus = device_cus();
     return a;
 }
 

@@ -150,7 +150,11 @@ struct BackwardLayout {
 
 BackwardLayout backward_layout(const lin_attn_params* p, bool causal, int64_t BH, int64_t N) {
     BackwardLayout L;
-    L.sp = plan_segments(BH, N, p->n_seg, TARGET_BLOCKS_VALU);
+    // the causal matrix-core passes run one workgroup per CU: about one
+    // segment per CU (at B=1, H=8, N=65536 this beat two per CU, 611 against
+    // 632 us a call: the two scans move half the state)
+    L.sp = plan_segments(BH, N, p->n_seg,
+                         causal && use_mfma(p) ? TARGET_BLOCKS_BWD_CAUSAL_MFMA : TARGET_BLOCKS_VALU);
     const size_t inc = (size_t)(BH * L.sp.G * state_elems(p->r));
     L.inc_b = inc;
     L.extra = 2 * inc;

@@ -18,6 +18,7 @@ namespace linattn {
 constexpr int64_t SEG_UNIT = 64;
 constexpr int64_t TARGET_BLOCKS_VALU = 512; // vector kernels: about two workgroups per CU
 constexpr int64_t TARGET_BLOCKS_MFMA = 512; // matrix-core kernels: two workgroups per CU
+constexpr int64_t TARGET_BLOCKS_BWD_CAUSAL_MFMA = 256; // causal backward passes: one per CU
 
 struct SegPlan {
     int64_t G;       // segments per head (one workgroup each for the outputs)

@@ -375,7 +375,14 @@ def test_backward_workspace_formula():
     tokens = 8 * 65536 * (32 + 1) * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_BIDIR_BACKWARD, p, 1, 8, 65536, 64, 64) == \
         inc + 2 * 8 * E * 4 + tokens + om_t
+    # the causal matrix-core route (these parameters: bf16 FAVOR+, r = 256)
+    # plans one segment per CU: 32 segments of 2048 tokens per head at H = 8
+    inc32 = 2 * 8 * 32 * E * 4
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 65536, 64, 64) == \
+        inc32 + tokens + om_t
+    # ... and the vector route (float32 inputs) two per CU, as above
+    p32 = params(dtype=0)
+    assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p32, 1, 8, 65536, 64, 64) == \
         inc + tokens + om_t
     assert binding.lin_attn_workspace_bytes(binding.OP_CAUSAL_BACKWARD, p, 1, 8, 0, 64, 64) == 0
 

@@ -855,7 +855,8 @@ __global__ __launch_bounds__(NT8, 2) void k_favor_sums8(FavorArgs a) {
 // Tables store the 16-blocks of their contraction index in swap23 order, so
 // an accumulator tile of the previous product is the other operand as is.
 // ---------------------------------------------------------------------------
-constexpr int NTB = 256;          // 4 waves, one chunk each at a time
+constexpr int NTB = 512;          // 8 waves, one chunk each at a time
+constexpr int64_t BWD_BIDIR_BLOCKS = 256; // workgroups of a bidirectional backward pass
 constexpr int LDF = R + 8;        // row length of the [64][R] tables (bank spread)
 constexpr int LDN = DV + 8;       // row length of the [R][64] table
 
@@ -876,26 +877,75 @@ struct BwdTables {
     u16 mt[DV * LDF];   // M^T [n][f']: M[16b + swap23(j)][n] at column 16b + j
     u16 mn[R * LDN];    // query pass: S [f][n'] (n in swap23 order); key pass: G [f][n] natural
     u16 wt[D * LDF];    // omega^T [d][f']: omega[16b + swap23(j)][d] at column 16b + j
+    bf16x8 om[R * 8];   // omega rows, 16-byte block j of row f at xs_index(f, j)
     float m1[R];        // z or g
 };
 
 __device__ __forceinline__ u16 f2bf(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
 
 // Build the tables from the head's state total (float32 [R][DV] then [R])
-// and omega; `swap_n`: store the n index of mn in swap23 order.
+// and omega; `swap_n`: store the n index of mn in swap23 order.  Every
+// global load is issued before the first LDS write (one round trip), and
+// each thread writes whole 16-byte words where the layout allows.
 __device__ void build_tables(BwdTables& tb, const float* __restrict__ st,
                              const u16* __restrict__ omega, bool swap_n) {
-    for (int e = threadIdx.x; e < R * DV; e += NTB) {
-        const int f = e / DV, n = e % DV;
-        const u16 v = f2bf(st[e]);
-        tb.mt[n * LDF + (f & ~15) + swap23(f & 15)] = v;
-        tb.mn[f * LDN + (swap_n ? (n & ~15) + swap23(n & 15) : n)] = v;
+    const int tid = threadIdx.x;
+    // M^T: thread (n, q) forms the words at positions 8 q' .. 8 q' + 7 of
+    // row n, q' = q + 8 u: features 16 (q' / 2) + swap23(8 (q' % 2) + e)
+    constexpr int NU = R / 8 / (NTB / DV);
+    const int n = tid & (DV - 1), q = tid / DV;
+    float sv[NU][8];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int qq = q + (NTB / DV) * u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[u][e] = st[(16 * (qq >> 1) + swap23(8 * (qq & 1) + e)) * DV + n];
     }
-    for (int e = threadIdx.x; e < R * D; e += NTB) {
-        const int f = e / D, d = e % D;
-        tb.wt[d * LDF + (f & ~15) + swap23(f & 15)] = omega[e];
+    // M: thread (f, half) holds 32 consecutive n of row f (8 float4) for
+    // f = tid / 2 (R rows, two threads each)
+    const int fr = tid >> 1, nh = 32 * (tid & 1);
+    f32x4 mv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mv[u] = *reinterpret_cast<const f32x4*>(st + (int64_t)fr * DV + nh + 4 * u);
+    // omega: four 16-byte blocks per thread (as 32-bit words: single bf16
+    // elements are taken by shifts, not vector-element casts)
+    constexpr int NO = R * 8 / NTB;
+    u32x4 ov[NO];
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+        const int b = tid + NTB * u;
+        ov[u] = *reinterpret_cast<const u32x4*>(omega + (int64_t)(b >> 3) * D + 8 * (b & 7));
     }
-    for (int f = threadIdx.x; f < R; f += NTB) tb.m1[f] = st[R * DV + f];
+    const float m1v = st[R * DV + (tid & (R - 1))];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (__bf16)sv[u][e];
+        *reinterpret_cast<bf16x8*>(&tb.mt[n * LDF + 8 * (q + (NTB / DV) * u)]) = w;
+    }
+    // row fr of mn: positions p hold n = swap23 within each 16-block (or n)
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            bf16x8 w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = swap_n ? swap23(8 * half + e) : 8 * half + e; // n within the 16-block
+                w[e] = (__bf16)mv[4 * blk + (j >> 2)][j & 3];
+            }
+            *reinterpret_cast<bf16x8*>(&tb.mn[fr * LDN + nh + 16 * blk + 8 * half]) = w;
+        }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+        const int b = tid + NTB * u, f = b >> 3, d0 = 8 * (b & 7);
+        *reinterpret_cast<u32x4*>(&tb.om[xs_index(f, b & 7)]) = ov[u];
+        const int fc = (f & ~15) + swap23(f & 15);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tb.wt[(d0 + e) * LDF + fc] = (u16)(ov[u][e >> 1] >> (16 * (e & 1)));
+    }
+    if (tid < R) tb.m1[tid] = m1v;
 }
 
 // Loads 4 consecutive bf16 of row `row` of X at column c0 as floats (0 past `rows`).
@@ -918,11 +968,12 @@ __device__ __forceinline__ void store4(u16* __restrict__ X, int ld, int row, int
 
 // phi(X)^T for feature tile b of the chunk: C[f][t] = omega_f . x_t, then
 // exp2(C a_scale + bias_t); tokens past `rows` are zero.
-__device__ __forceinline__ f32x16 feature_tile(const BwdArgs& a, const bf16x8 (&xf)[4], int b,
-                                               float bias, bool live, int lo, int h) {
+__device__ __forceinline__ f32x16 feature_tile(const BwdArgs& a, const BwdTables& tb,
+                                               const bf16x8 (&xf)[4], int b, float bias, bool live,
+                                               int lo, int h) {
     f32x16 c = zero16();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) c = mfma(omega_frag(a.omega, 0, b, ks, lo, h), xf[ks], c);
+    for (int ks = 0; ks < 4; ++ks) c = mfma(tb.om[xs_index(32 * b + lo, 2 * ks + h)], xf[ks], c);
 #pragma unroll
     for (int i = 0; i < 16; ++i) c[i] = live ? __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bias)) : 0.f;
     return c;
@@ -974,7 +1025,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_query_favor(BwdArgs a) {
         float den = 0.f;
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-            const f32x16 c = feature_tile(a, xf, b, bias, live, lo, h);
+            const f32x16 c = feature_tile(a, tb, xf, b, bias, live, lo, h);
             ph[b][0] = pack8(c, 0);
             ph[b][1] = pack8(c, 8);
 #pragma unroll
@@ -1084,7 +1135,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_key_favor(BwdArgs a) {
         float wsum = 0.f;
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-            const f32x16 c = feature_tile(a, xf, b, bias, live, lo, h);
+            const f32x16 c = feature_tile(a, tb, xf, b, bias, live, lo, h);
             const bf16x8 p0 = pack8(c, 0), p1 = pack8(c, 8);
             // dphi(K)^T = G V^T + g
             f32x16 gk = zero16();
@@ -2120,16 +2171,22 @@ static BwdArgs bwd_args(const Cfg& c, const void* x, const void* y, const void* 
 hipError_t launch_favor_bwd_query(const Cfg& c, const void* q, const void* dout, const void* omega,
                                   Shape s, SegPlan sp, const float* total, void* dq, void* dnum,
                                   float* dden, hipStream_t st) {
-    const BwdArgs a = bwd_args(c, q, dout, omega, s, sp, total, dq, dnum, dden);
-    hipLaunchKernelGGL(k_bwd_query_favor, dim3((unsigned)(sp.G * s.BH)), dim3(NTB), 0, st, a);
+    // every token's gradient reads only the totals, so the passes take their
+    // own blocks of tokens: about one workgroup (eight waves) per CU
+    const SegPlan wp = plan_segments(s.BH, s.N, 0, BWD_BIDIR_BLOCKS);
+    (void)sp;
+    const BwdArgs a = bwd_args(c, q, dout, omega, s, wp, total, dq, dnum, dden);
+    hipLaunchKernelGGL(k_bwd_query_favor, dim3((unsigned)(wp.G * s.BH)), dim3(NTB), 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_favor_bwd_key(const Cfg& c, const void* k, const void* v, const void* omega,
                                 Shape s, SegPlan sp, const float* total, void* dk, void* dv,
                                 hipStream_t st) {
-    const BwdArgs a = bwd_args(c, k, v, omega, s, sp, total, dk, dv, nullptr);
-    hipLaunchKernelGGL(k_bwd_key_favor, dim3((unsigned)(sp.G * s.BH)), dim3(NTB), 0, st, a);
+    const SegPlan wp = plan_segments(s.BH, s.N, 0, BWD_BIDIR_BLOCKS);
+    (void)sp;
+    const BwdArgs a = bwd_args(c, k, v, omega, s, wp, total, dk, dv, nullptr);
+    hipLaunchKernelGGL(k_bwd_key_favor, dim3((unsigned)(wp.G * s.BH)), dim3(NTB), 0, st, a);
     return hipGetLastError();
 }
 

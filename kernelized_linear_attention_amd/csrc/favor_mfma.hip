@@ -1531,6 +1531,7 @@ struct CausalSmem {
 struct CausalQuerySmem {
     CausalSmem c;
     float red[NWC][2][L];          // per wave, per token: partial denominator and dout . num
+    bf16x8 om[R * 8];              // omega rows, 16-byte block j of row f at xs_index(f, j)
 };
 
 struct CausalKeySmem {
@@ -1636,11 +1637,18 @@ __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
 
 // phi(X)^T tile of this wave's features: C[f][t], f in F_w, token t = lo,
 // from the token's staged bias (zero past the chunk's end).
-__device__ __forceinline__ f32x16 features1(const CausalArgs& a, const bf16x8 (&xf)[4], int w,
-                                            float bias, int lo, int h) {
+// phi^T of the wave's 32 features, c[f][t] = exp2(omega_f . x_t a + bias_t),
+// with omega's rows read from LDS (xs_index layout; OM_LDS) or from memory
+// (the key pass has no LDS left for them: a copy from omega^T by
+// transposing reads pushed it to 16 spilled registers, 248 -> 319 us)
+template <bool OM_LDS>
+__device__ __forceinline__ f32x16 features1(const CausalArgs& a, const bf16x8* om, const bf16x8 (&xf)[4],
+                                            int w, float bias, int lo, int h) {
     f32x16 c = zero16();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) c = mfma(omega_frag(a.omega, 32 * w, 0, ks, lo, h), xf[ks], c);
+    for (int ks = 0; ks < 4; ++ks)
+        c = mfma(OM_LDS ? om[xs_index(32 * w + lo, 2 * ks + h)] : omega_frag(a.omega, 32 * w, 0, ks, lo, h),
+                 xf[ks], c);
 #pragma unroll
     for (int i = 0; i < 16; ++i) c[i] = __builtin_amdgcn_exp2f(fmaf(c[i], a.a_scale, bias));
     return c;
@@ -1734,10 +1742,23 @@ __device__ __forceinline__ void store_du(const CausalArgs& a, const CausalSmem& 
 }
 
 // omega^T in LDS, natural f order.
-__device__ __forceinline__ void stage_omega_t(u16* wt, const u16* __restrict__ omega) {
-    for (int e = threadIdx.x; e < R * D; e += NTC) {
-        const int f = e / D, d = e % D;
-        wt[d * LDW + f] = omega[e];
+// omega^T [d][f] (row length LDW) and omega's rows in the swizzled layout of
+// the staged chunks: every global load is issued first (one round trip),
+// single bf16 values are taken from 32-bit words by shifts.
+__device__ __forceinline__ void stage_omega_t(u16* wt, bf16x8* rows, const u16* __restrict__ omega) {
+    constexpr int NO = R * 8 / NTC;
+    u32x4 ov[NO];
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+        const int b = threadIdx.x + NTC * u;
+        ov[u] = *reinterpret_cast<const u32x4*>(omega + (int64_t)(b >> 3) * D + 8 * (b & 7));
+    }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+        const int b = threadIdx.x + NTC * u, f = b >> 3, d0 = 8 * (b & 7);
+        *reinterpret_cast<u32x4*>(&rows[xs_index(f, b & 7)]) = ov[u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wt[(d0 + e) * LDW + f] = (u16)(ov[u][e >> 1] >> (16 * (e & 1)));
     }
 }
 
@@ -1758,7 +1779,7 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
     const int fw = 32 * w;           // first feature of this wave
     const int pn = 32 * (w >> 2) + 8 * (w & 3) + 4 * h; // the dnum piece this wave stores
 
-    stage_omega_t(sm.wt, a.omega);
+    stage_omega_t(sm.wt, smq.om, a.omega);
     // the forward state carried into the segment, transposed: S^T[n][F_w] in
     // accumulators (tile nt: rows n = 32 nt + 8(i/4) + 4h + i%4, column
     // f = fw + lo), z in LDS
@@ -1821,8 +1842,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_query_favor(CausalArgs a) {
         fetch_chunk<false>(a, bh * a.N + c0n, rowsn, il);
         chunk_at(min(ci + 1, nck - 1), c0n, rowsn);
 
-        const f32x16 PQ = features1(a, qf, w, sm.xb[0][lo], lo, h);
-        const Tile2 pk = packt(features1(a, kf, w, sm.xb[1][lo], lo, h));
+        const f32x16 PQ = features1<true>(a, smq.om, qf, w, sm.xb[0][lo], lo, h);
+        const Tile2 pk = packt(features1<true>(a, smq.om, kf, w, sm.xb[1][lo], lo, h));
 
         // Over F_w: the masked intra-chunk block A1^T [j x t] = phi(K) phi(Q)^T
         // (keys j <= query t), SD [f x t] = S dout^T and VD [j x t] = V dout^T.
@@ -1971,7 +1992,9 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
     const int keep_thr = lo - 4 * h; // query >= key  <=>  8(i/4) + i%4 >= keep_thr
     const int fw = 32 * w;
 
-    stage_omega_t(sm.wt, a.omega);
+    // (the key pass keeps the element loop: with the batched loads its main
+    // loop ran ~3 % slower at its 256-register limit)
+    for (int e = threadIdx.x; e < R * D; e += NTC) sm.wt[(e % D) * LDW + e / D] = a.omega[e];
     // the backward state after the segment (suffix): G[F_w] in accumulators, g in LDS
     const float* st = a.state + bh * a.st_bh + g * a.st_g;
     f32x16 Gs[2];
@@ -2035,8 +2058,8 @@ __global__ __launch_bounds__(NTC) void k_bwd_causal_key_favor(CausalArgs a) {
         fetch_chunk<true>(a, bh * a.N + c0n, rowsn, il);
         chunk_at(min(cr + 1, nck - 1), c0n, rowsn);
 
-        const Tile2 pq = packt(features1(a, qf, w, sm.xb[0][lo], lo, h));
-        const f32x16 PK = features1(a, kf, w, sm.xb[1][lo], lo, h);
+        const Tile2 pq = packt(features1<false>(a, nullptr, qf, w, sm.xb[0][lo], lo, h));
+        const f32x16 PK = features1<false>(a, nullptr, kf, w, sm.xb[1][lo], lo, h);
         const Tile2 pk = packt(PK);
 
         // partials over F_w: dv^T [n x j] = G^T phi(K)^T, B1 [i x j] = phi(Q) phi(K)^T

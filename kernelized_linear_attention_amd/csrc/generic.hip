@@ -370,78 +370,125 @@ __global__ __launch_bounds__(NT) void k_segment_scan_varlen(int r, int64_t H, in
         z_fin[sh * r + (e - rdv)] = run;
 }
 
-// The same scan with one block per (element block, head) instead of per
-// (element block, head, sequence): the sequence starts first[] are staged in
-// LDS once, and each thread walks all parts of its head in batches of
-// independent loads that span sequences (the carry restarts at every
-// sequence's first part).  For batches of at most MAXS_LDS sequences.
+// The same scan with one block per (64 elements, head) instead of per
+// (element block, head, sequence), for batches of at most MAXS_LDS
+// sequences: the sequence starts first[] are staged in LDS once, and the
+// head's parts are split into P consecutive ranges, one per wave (64
+// elements each, so every branch on the parts is uniform over the wave), so
+// that no thread walks more than a few batches of loads.  A sequence that
+// spans ranges is carried across them as a segmented scan: each range first
+// sums its last sequence's parts within the range (from that sequence's
+// starting state when it starts in the range), the ranges' carries are formed
+// in range order through LDS (a range whose last sequence starts inside it
+// restarts the carry), and each range then writes its prefixes from its
+// carry.  Every sum is taken in a fixed order.
 constexpr int MAXS_LDS = 1024;
-__global__ __launch_bounds__(NT) void k_segment_scan_varlen_heads(
+constexpr int VSCAN_BATCH = 16; // parts held in registers per thread
+constexpr int VSCAN_RANGE = 32; // parts per range the launcher aims at
+
+template <int P>
+__global__ __launch_bounds__(64 * P) void k_segment_scan_varlen_heads(
     int r, int64_t H, int64_t num_seqs, int64_t parts, const int64_t* __restrict__ first,
     const float* __restrict__ S0, const float* __restrict__ z0, float* __restrict__ ws,
     int prefix_stride, float* __restrict__ S_fin, float* __restrict__ z_fin) {
-    constexpr int BATCH = 16;
-    __shared__ int64_t first_s[MAXS_LDS + 1];
-    for (int64_t i = threadIdx.x; i <= num_seqs; i += NT) first_s[i] = first[i];
+    __shared__ int first_s[MAXS_LDS + 1]; // part indices (the host keeps parts below 2^31)
+    __shared__ float tail_s[P][64];
+    __shared__ int restart_s[P];
+    for (int i = threadIdx.x; i <= num_seqs; i += 64 * P) first_s[i] = (int)first[i];
     __syncthreads();
+    const int ns = (int)num_seqs;
     const int64_t E = state_elems(r);
-    const int64_t bpe = (E + NT - 1) / NT;
+    const int64_t bpe = (E + 63) / 64;
     const int64_t h = blockIdx.x / bpe;
-    const int64_t e = (blockIdx.x % bpe) * NT + threadIdx.x;
-    if (e >= E) return;
+    const int el = threadIdx.x & 63;
+    const int part = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t e = (blockIdx.x % bpe) * 64 + el;
+    const bool live = e < E;
+    const int64_t ec = live ? e : E - 1; // in-bounds element for the loads
     const int64_t rdv = (int64_t)r * DV;
-    auto start = [&](int64_t i) -> float {
+    auto start = [&](int i) -> float {
         if (!S0) return 0.f;
-        const int64_t sh = i * H + h;
-        return e < rdv ? S0[sh * rdv + e] : z0[sh * r + (e - rdv)];
+        const int64_t sh = (int64_t)i * H + h;
+        return ec < rdv ? S0[sh * rdv + ec] : z0[sh * r + (ec - rdv)];
     };
-    auto finish = [&](int64_t i, float v) {
-        const int64_t sh = i * H + h;
+    auto finish = [&](int i, float v) {
+        if (!live) return;
+        const int64_t sh = (int64_t)i * H + h;
         if (e < rdv)
             S_fin[sh * rdv + e] = v;
         else
             z_fin[sh * r + (e - rdv)] = v;
     };
-    const int64_t P = min<int64_t>(first_s[num_seqs], parts);
-    float* p = ws + h * parts * E + e;
-    const int64_t pmask = prefix_stride - 1;
-    // sequence i owns parts first[i] .. first[i+1]-1 (empty ones end where they start)
-    int64_t i = 0, seq_first = 0, seq_end = 0;
-    float run = 0.f;
-    auto next_sequence = [&]() {
-        while (i < num_seqs && first_s[i + 1] <= first_s[i]) {
-            finish(i, start(i));
-            ++i;
+    // the sequence whose parts hold part g (the last i with first[i] <= g:
+    // sequences without parts end where they start)
+    auto seq_of = [&](int g) {
+        int lo = 0, hi = ns - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (first_s[mid] <= g) lo = mid; else hi = mid - 1;
         }
-        if (i < num_seqs) {
-            run = start(i);
-            seq_first = first_s[i];
-            seq_end = first_s[i + 1];
-        }
+        return lo;
     };
-    next_sequence();
-    for (int64_t gb = 0; gb < P; gb += BATCH) {
-        const int n = (int)min<int64_t>(BATCH, P - gb);
-        float a[BATCH];
+    const int Pn = (int)min<int64_t>(first_s[ns], parts); // parts in use
+    const int per = (Pn + P - 1) / P;
+    const int g0 = min(Pn, part * per), g1 = min(Pn, g0 + per);
+    const float* base = ws + h * parts * E + ec;
+    auto at = [&](int g) { return base + (int64_t)g * E; };
+    const int n0 = min(VSCAN_BATCH, g1 - g0);
+    // every load unconditional: clamped to the range's first part (part 0
+    // for an empty range); the values past n0 are not used
+    const int gl = g1 > g0 ? g0 : 0;
+    float a[VSCAN_BATCH];
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j) a[j] = j < n ? p[(gb + j) * E] : 0.f;
-        wait_all_loads(); // else each prefix store below waits for the ones before it
+    for (int j = 0; j < VSCAN_BATCH; ++j) a[j] = *at(gl + (j < n0 ? j : 0));
+    // the range's last sequence: its parts within the range, from its
+    // starting state when it starts here
+    float tail = 0.f;
+    int restart = 0;
+    if (g1 > g0) {
+        const int il = seq_of(g1 - 1), fl = first_s[il];
+        restart = fl >= g0;
+        tail = restart ? start(il) : 0.f;
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-            if (j < n && i < num_seqs) {
-                const int64_t g = gb + j;
-                if (prefix_stride > 0 && ((g - seq_first) & pmask) == 0) p[g * E] = run;
-                run += a[j];
-                if (g + 1 >= seq_end) { // last part of sequence i
-                    finish(i, run);
-                    ++i;
-                    next_sequence();
-                }
+        for (int j = 0; j < VSCAN_BATCH; ++j)
+            if (j < n0 && g0 + j >= fl) tail += a[j];
+        for (int g = max(g0 + VSCAN_BATCH, fl); g < g1; ++g) tail += *at(g);
+    }
+    wait_all_loads(); // else each prefix store below waits for the ones before it
+    if (P > 1) {
+        tail_s[part][el] = tail;
+        if (el == 0) restart_s[part] = restart;
+        __syncthreads();
+    }
+    // the carry into this range, ranges in order
+    float carry = 0.f;
+    for (int u = 0; u < part; ++u) carry = restart_s[u] ? tail_s[u][el] : carry + tail_s[u][el];
+    // sequences without parts end with their starting state (a share of them
+    // per range)
+    for (int i = part; i < ns; i += P)
+        if (first_s[i + 1] <= first_s[i]) finish(i, start(i));
+    if (g1 <= g0) return;
+    int i = seq_of(g0), seq_first = first_s[i], seq_end = first_s[i + 1];
+    float run = seq_first == g0 ? start(i) : carry;
+    const int pmask = prefix_stride - 1;
+    auto visit = [&](int g, float x) {
+        if (live && prefix_stride > 0 && ((g - seq_first) & pmask) == 0)
+            *const_cast<float*>(at(g)) = run;
+        run += x;
+        if (g + 1 >= seq_end) { // last part of sequence i
+            finish(i, run);
+            if (g + 1 < g1) { // the next sequence with parts starts at g + 1
+                i = seq_of(g + 1);
+                seq_first = first_s[i];
+                seq_end = first_s[i + 1];
+                run = start(i);
             }
         }
-    }
-    // sequences with parts past the capacity (malformed boundaries only)
-    for (; i < num_seqs; ++i) finish(i, start(i));
+    };
+#pragma unroll
+    for (int j = 0; j < VSCAN_BATCH; ++j)
+        if (j < n0) visit(g0 + j, a[j]);
+    for (int g = g0 + VSCAN_BATCH; g < g1; ++g) visit(g, *at(g));
 }
 
 // ---------------------------------------------------------------------------
@@ -731,10 +778,25 @@ hipError_t launch_segment_scan_varlen(int r, int64_t H, int64_t num_seqs, int64_
                                       float* ws, int prefix_stride, float* S_fin, float* z_fin,
                                       hipStream_t st) {
     const int64_t E = state_elems(r);
-    if (num_seqs <= MAXS_LDS) {
-        const dim3 grid((unsigned)(((E + NT - 1) / NT) * H));
-        hipLaunchKernelGGL(k_segment_scan_varlen_heads, grid, dim3(NT), 0, st, r, H, num_seqs,
-                           parts, first, S0, z0, ws, prefix_stride, S_fin, z_fin);
+    if (num_seqs <= MAXS_LDS && parts < ((int64_t)1 << 30)) {
+        // ranges of at most VSCAN_RANGE parts where that takes at most 16 of them
+        // (shorter ranges measured slower: more waves, each with the same
+        // fixed work)
+        auto go = [&](auto kernel, int p) {
+            const dim3 grid((unsigned)(((E + 63) / 64) * H));
+            hipLaunchKernelGGL(kernel, grid, dim3(64 * p), 0, st, r, H, num_seqs, parts, first, S0,
+                               z0, ws, prefix_stride, S_fin, z_fin);
+        };
+        if (parts > 8 * VSCAN_RANGE)
+            go(k_segment_scan_varlen_heads<16>, 16);
+        else if (parts > 4 * VSCAN_RANGE)
+            go(k_segment_scan_varlen_heads<8>, 8);
+        else if (parts > 2 * VSCAN_RANGE)
+            go(k_segment_scan_varlen_heads<4>, 4);
+        else if (parts > VSCAN_RANGE)
+            go(k_segment_scan_varlen_heads<2>, 2);
+        else
+            go(k_segment_scan_varlen_heads<1>, 1);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)(((E + NT - 1) / NT) * H * num_seqs));

@@ -229,21 +229,29 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int64_t i, int64_t
 }
 
 // Exclusive scan of one value per thread over the workgroup (all threads
-// call it); returns this thread's offset and sets *sum to the total.
+// call it); returns this thread's offset and sets *sum to the total.  Each
+// wave scans its 64 values with lane shuffles; the waves' totals meet in
+// buf[0 .. NT/64) (two barriers per call).
 __device__ int64_t block_exclusive_scan(int64_t x, int64_t* buf, int64_t* sum) {
-    const int tid = threadIdx.x;
-    buf[tid] = x;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-        const int64_t y = tid >= off ? buf[tid - off] : 0;
-        __syncthreads();
-        buf[tid] += y;
-        __syncthreads();
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int64_t incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
     }
-    const int64_t incl = buf[tid];
-    *sum = buf[NT - 1];
+    if (lane == 63) buf[w] = incl;
     __syncthreads();
-    return incl - x;
+    int64_t before = 0, total = 0;
+#pragma unroll
+    for (int u = 0; u < NT / 64; ++u) {
+        const int64_t t = buf[u];
+        if (u < w) before += t;
+        total += t;
+    }
+    *sum = total;
+    __syncthreads(); // buf is written again by the next call
+    return before + incl - x;
 }
 
 __global__ __launch_bounds__(NT) void k_varlen_plan(const int32_t* __restrict__ cu, int64_t num_seqs,
@@ -302,18 +310,21 @@ __global__ __launch_bounds__(NT) void k_varlen_plan(const int32_t* __restrict__ 
     }
     __syncthreads();
     // second walk: full segments in sequence order, partials into their bucket
-    int64_t fbase = 0;
+    // (the parts' offsets scanned again rather than read back from first[])
+    int64_t fbase = 0, pbase = 0;
     for (int64_t i0 = 0; i0 < num_seqs; i0 += NT) {
         const int64_t i = i0 + tid;
-        int64_t s0 = 0, s1 = 0, nf = 0;
+        int64_t s0 = 0, s1 = 0, n = 0, nf = 0;
         if (i < num_seqs) {
             seq_bounds(cu, i, total, s0, s1);
+            n = (s1 - s0 + seg_len - 1) / seg_len * sub;
             nf = (s1 - s0) / seg_len;
         }
-        int64_t fsum;
+        int64_t sum, fsum;
+        const int64_t e0 = pbase + block_exclusive_scan(n, buf, &sum);
         const int64_t f0 = fbase + block_exclusive_scan(nf, buf, &fsum);
         if (i < num_seqs) {
-            const int64_t g0 = first[i] / sub; // the sequence's first segment
+            const int64_t g0 = min<int64_t>(e0, cap) / sub; // the sequence's first segment
             for (int64_t j = 0; j < nf && f0 + j < seg_cap && g0 + j < seg_cap; ++j)
                 order[f0 + j] = g0 + j;
             const int64_t rem = (s1 - s0) % seg_len;
@@ -323,6 +334,7 @@ __global__ __launch_bounds__(NT) void k_varlen_plan(const int32_t* __restrict__ 
             }
         }
         fbase += fsum;
+        pbase += sum;
     }
 }
 

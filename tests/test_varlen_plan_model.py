@@ -98,18 +98,21 @@ def plan(cu, num_seqs, total, seg_len, sub, cap, rng):
     off, _ = block_exclusive_scan(counts)
     for t in range(nb):
         bucket_at[nb - 1 - t] = min(full_base + off[t], seg_cap)
-    fbase = 0
+    fbase = pbase = 0
     for i0 in range(0, num_seqs, NT):
         ids = range(i0, i0 + NT)
         bounds = [seq_bounds(cu, i, total) if i < num_seqs else (0, 0) for i in ids]
+        n = [(s1 - s0 + seg_len - 1) // seg_len * sub if i < num_seqs else 0
+             for i, (s0, s1) in zip(ids, bounds)]
         nf = [(s1 - s0) // seg_len if i < num_seqs else 0 for i, (s0, s1) in zip(ids, bounds)]
+        e0s, tot = block_exclusive_scan(n)
         f0s, ftot = block_exclusive_scan(nf)
         claims = []
         for t, i in enumerate(ids):
             if i >= num_seqs:
                 continue
             s0, s1 = bounds[t]
-            g0 = first[i] // sub
+            g0 = min(pbase + e0s[t], cap) // sub  # the parts' offsets scanned again
             f0 = fbase + f0s[t]
             j = 0
             while j < nf[t] and f0 + j < seg_cap and g0 + j < seg_cap:
@@ -125,6 +128,7 @@ def plan(cu, num_seqs, total, seg_len, sub, cap, rng):
             if pos < seg_cap:
                 order[pos] = g0 + nft if g0 + nft < seg_cap else -1
         fbase += ftot
+        pbase += tot
     return tab, first, order
 
 

@@ -455,12 +455,14 @@ __global__ __launch_bounds__(64 * P) void k_segment_scan_varlen_heads(
     for (int j = 0; j < VSCAN_BATCH; ++j) a[j] = *at(gl + (j < n0 ? j : 0));
     // the range's last sequence: its parts within the range, from its
     // starting state when it starts here
-    float tail = 0.f;
-    int restart = 0;
+    float tail = 0.f, start_last = 0.f;
+    int restart = 0, il = -1;
     if (g1 > g0) {
-        const int il = seq_of(g1 - 1), fl = first_s[il];
+        il = seq_of(g1 - 1);
+        const int fl = first_s[il];
         restart = fl >= g0;
-        tail = restart ? start(il) : 0.f;
+        start_last = restart ? start(il) : 0.f;
+        tail = start_last;
 #pragma unroll
         for (int j = 0; j < VSCAN_BATCH; ++j)
             if (j < n0 && g0 + j >= fl) tail += a[j];
@@ -480,8 +482,15 @@ __global__ __launch_bounds__(64 * P) void k_segment_scan_varlen_heads(
     for (int i = part; i < ns; i += P)
         if (first_s[i + 1] <= first_s[i]) finish(i, start(i));
     if (g1 <= g0) return;
+    // S0 and S_fin may be one buffer (the state updated in place), and a
+    // document's final state is written by the range holding its last part:
+    // so a range takes the starting state of its last document (the only one
+    // that can end in another range) from the read before the barrier; any
+    // other document it starts also ends in it, read before written by this
+    // thread
+    auto start_of = [&](int i) { return i == il ? start_last : start(i); };
     int i = seq_of(g0), seq_first = first_s[i], seq_end = first_s[i + 1];
-    float run = seq_first == g0 ? start(i) : carry;
+    float run = seq_first == g0 ? start_of(i) : carry;
     const int pmask = prefix_stride - 1;
     auto visit = [&](int g, float x) {
         if (live && prefix_stride > 0 && ((g - seq_first) & pmask) == 0)
@@ -493,7 +502,7 @@ __global__ __launch_bounds__(64 * P) void k_segment_scan_varlen_heads(
                 i = seq_of(g + 1);
                 seq_first = first_s[i];
                 seq_end = first_s[i + 1];
-                run = start(i);
+                run = start_of(i);
             }
         }
     };

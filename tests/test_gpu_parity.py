@@ -816,6 +816,38 @@ def test_causal_varlen_thousand_documents(gpu_lib, num_seqs):
     assert_parity(z, rz, 1e-4, "many documents z")
 
 
+def test_causal_varlen_scan_range_counts(gpu_lib):
+    """Packed documents from carried states at segment counts whose part
+    totals put the per-head scan at 1, 2, 4, 8 and 16 ranges: documents
+    spanning range boundaries, empty documents, one output set for every
+    count against one oracle run."""
+    g = np.random.default_rng(150)
+    lens = g.integers(0, 1500, size=24)
+    lens[[2, 9]] = 0
+    c, q, k, v, cu, cu_d = _packed(150, list(lens), "favor", torch.bfloat16, 256, 1, H=2)
+    ns, H, total = len(lens), 2, int(cu[-1])
+    S0 = np.abs(inputs.normal((ns, H, 256, 64), 150, inputs.T_PREFIX)).astype(np.float32) * 0.1
+    z0 = np.abs(inputs.normal((ns, H, 256), 150, inputs.T_PREFIX, 1)).astype(np.float32) + 1.0
+    kw = dict(scale=64 ** -0.25)
+    ro, rS, rz = oracle.causal_varlen(c.qh[0], c.kh[0], c.vh[0], cu, "favor", S0=S0, z0=z0,
+                                      **c.okw(**kw))
+    units = -(-total // 64)
+    seen = set()
+    for n_seg in (1, 12, 80, 150, 300):
+        per = -(-units // min(n_seg, units))
+        parts = -(-units // per) + ns  # the automatic plan's segments plus one partial per document
+        seen.add(next(p for p in (1, 2, 4, 8, 16) if parts <= 32 * p or p == 16))
+        S = torch.from_numpy(S0.copy()).cuda()
+        z = torch.from_numpy(z0.copy()).cuda()
+        out, S, z = gpu_lib.lin_attn_causal_varlen(q, k, v, cu_d, "favor", S=S, z=z, state_in=True,
+                                                   n_seg=n_seg, **c.gkw(**kw))
+        tag = f"varlen n_seg={n_seg} parts={parts}"
+        assert_parity(out, ro, 2e-2, f"{tag} out", lead_dims=1)
+        assert_parity(S, rS, 2e-2, f"{tag} S")
+        assert_parity(z, rz, 2e-2, f"{tag} z")
+    assert seen == {1, 2, 4, 8, 16}, seen
+
+
 @pytest.mark.parametrize("N,n_seg", [(1, 0), (31, 0), (33, 1), (100, 2), (300, 0), (1000, 3)])
 @pytest.mark.parametrize("norm", ["attn", "none"])
 def test_causal_backward_matrix_core_route(gpu_lib, N, n_seg, norm):

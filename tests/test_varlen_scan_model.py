@@ -4,7 +4,11 @@ parts split into P consecutive ranges, each range's last sequence summed
 within the range (from its starting state when it starts there), the
 carries formed in range order (a range whose last sequence starts inside it
 restarts the carry), then each range's prefixes written from its carry.
-Every read and write is bounds-checked.
+Every read and write is bounds-checked.  The starting and final states
+share one array (the library updates the caller's state in place), and the
+ranges' second passes run first to last and last to first: a range must not
+read a starting state that another range has already replaced by a final
+one.
 
 Checked against the plain definition -- each sequence walks its own parts
 from its starting state, writing the exclusive prefix at every
@@ -42,30 +46,40 @@ def seq_of(first, ns, g):
     return lo
 
 
-def model(first, inc, start, P, stride, batch=16):
+def model(first, inc, start0, P, stride, batch=16, order=1):
+    """order: 1 runs the ranges' second passes first to last, -1 last to
+    first (the hardware fixes no order between them)."""
     ns = len(first) - 1
     parts = len(inc)
     ws = Bounded(inc, "ws")
-    fin = [None] * ns
+    # the starting states and the final states share one array, as when the
+    # library updates the caller's state in place
+    state = Bounded(start0, "state")
+    done = [False] * ns
+
+    def start(i):
+        return state[i]
 
     def finish(i, v):
-        assert 0 <= i < ns and fin[i] is None, f"sequence {i} finished twice"
-        fin[i] = v
+        assert 0 <= i < ns and not done[i], f"sequence {i} finished twice"
+        done[i] = True
+        state[i] = v
 
     Pn = min(first[ns], parts)
     per = (Pn + P - 1) // P
     rng = [(min(Pn, k * per), min(Pn, min(Pn, k * per) + per)) for k in range(P)]
-    tails, restarts = [], []
+    tails, restarts, lasts = [], [], []
     for g0, g1 in rng:
         n0 = min(batch, g1 - g0)
         gl = g0 if g1 > g0 else 0
         a = [ws[gl + (j if j < n0 else 0)] for j in range(batch)]
-        tail, restart = 0.0, False
+        tail, restart, il, start_last = 0.0, False, -1, 0.0
         if g1 > g0:
             il = seq_of(first, ns, g1 - 1)
             fl = first[il]
             restart = fl >= g0
-            tail = start[il] if restart else 0.0
+            start_last = start(il) if restart else 0.0
+            tail = start_last
             for j in range(batch):
                 if j < n0 and g0 + j >= fl:
                     tail += a[j]
@@ -73,18 +87,26 @@ def model(first, inc, start, P, stride, batch=16):
                 tail += ws[g]
         tails.append(tail)
         restarts.append(restart)
-    for part, (g0, g1) in enumerate(rng):
+        lasts.append((il, start_last))
+    # (the barrier)
+    for part in range(P)[::order]:
+        g0, g1 = rng[part]
         carry = 0.0
         for u in range(part):
             carry = tails[u] if restarts[u] else carry + tails[u]
         for i in range(part, ns, P):
             if first[i + 1] <= first[i]:
-                finish(i, start[i])
+                finish(i, start(i))
         if g1 <= g0:
             continue
+        il, start_last = lasts[part]
+
+        def start_of(i):
+            return start_last if i == il else start(i)
+
         i = seq_of(first, ns, g0)
         sf, se = first[i], first[i + 1]
-        run = start[i] if sf == g0 else carry
+        run = start_of(i) if sf == g0 else carry
         for g in range(g0, g1):
             x = inc[g]
             if stride > 0 and ((g - sf) & (stride - 1)) == 0:
@@ -95,8 +117,9 @@ def model(first, inc, start, P, stride, batch=16):
                 if g + 1 < g1:
                     i = seq_of(first, ns, g + 1)
                     sf, se = first[i], first[i + 1]
-                    run = start[i]
-    return ws.a, fin
+                    run = start_of(i)
+    assert all(done)
+    return ws.a, list(state.a)
 
 
 def plain(first, inc, start, stride):
@@ -127,6 +150,7 @@ def test_range_split_scan_equals_per_sequence_walk(seed):
         stride = int(g.choice([0, 1, 2, 4]))
         want_ws, want_fin = plain(first, inc, start, stride)
         for P in (1, 2, 4, 8, 16):
-            ws, fin = model(first, inc, start, P, stride)
-            assert np.array_equal(ws, want_ws), (P, first, stride)
-            assert fin == want_fin, (P, first, stride)
+            for order in (1, -1):
+                ws, fin = model(first, inc, start, P, stride, order=order)
+                assert np.array_equal(ws, want_ws), (P, order, first, stride)
+                assert fin == want_fin, (P, order, first, stride)
